@@ -1,0 +1,176 @@
+"""Plain float64 oracle of one DECO MoE feed-forward layer, forward pass.
+
+TEST INFRASTRUCTURE.  Slow and obviously correct on purpose: numpy float64,
+one BLAS matmul per step, no blocking, fusion or reordering.  It shares no
+code with the HIP library; only `tests/`, the smoke check and the benchmark's
+CPU-baseline leg may call it.
+
+Sources (the method's equations section is missing from the available text of
+the DECO paper, so the steps below follow its prose):
+  [P-DECO]  "DECO: Sparse Mixture-of-Experts with Dense-Comparable Performance
+            on End-Side Devices" (arXiv 2605.10933, HTML version):
+            Sec. 1 Introduction; Sec. 2 Related work, paragraphs "Router design"
+            and "Expert design".
+  [W-CN]    Chinese write-up of the same paper (qidianchuan.cn), section 二
+            (core design of DECO): the router part, and the expert-design part
+            on NormSiLU and non-gated experts.
+
+Readings taken where the text is silent (each is listed in the design doc):
+  * router = linear projection with a bias b_r, then ReLU, then a learned
+    per-expert scale lambda_e applied after the ReLU; no softmax / unit-sum;
+  * an expert is active for a token iff its logit is strictly positive
+    (zero or negative scores are ignored) and lambda_e != 0;
+  * NormSiLU mean term uses the mean of ALL routed experts' up-projection
+    weights (fixed at inference, so it cannot depend on the active set);
+    the shared expert is excluded;
+  * intra-expert RMS over the d_ff entries of one (token, expert) row, with
+    epsilon inside the square root and no learnable gain;
+  * experts are non-gated two-matrix MLPs with no biases;
+  * shared expert: non-gated MLP with plain SiLU, weight 1, no lambda;
+  * no residual: the result is the FFN sublayer output only.
+
+Parity against the pages' own numbers is unpinned: the pages print no worked
+example of the layer.  Every function here is pinned by the invariants,
+closed forms, brute force and library cross-checks in tests/test_oracle_pins.py.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+
+def silu(v: np.ndarray) -> np.ndarray:
+    """SiLU(v) = v * sigmoid(v), evaluated without overflow for large |v|."""
+    v = np.asarray(v, dtype=np.float64)
+    out = np.empty_like(v)
+    pos = v >= 0
+    out[pos] = v[pos] / (1.0 + np.exp(-v[pos]))
+    ev = np.exp(v[~pos])
+    out[~pos] = v[~pos] * ev / (1.0 + ev)
+    return out
+
+
+def router(x, W_r, b_r, lam):
+    """ReLU router with expert-wise scaling.
+
+    [P-DECO] Sec. 2 "Router design": a linear projection, an activation, and a
+    post-processing of the scores; DECO uses ReLU as the activation and a
+    learnable per-expert scaling factor in place of a fixed scalar.
+    [W-CN] Sec. 二, router part: an expert with a positive score is used, a
+    zero or negative score is ignored.
+
+    Returns logits z [T,E], the active mask [T,E] (bool) and gates g [T,E]
+    with g = lambda_e * max(z, 0) on active entries and 0 elsewhere.
+    """
+    z = np.asarray(x, np.float64) @ np.asarray(W_r, np.float64) + np.asarray(b_r, np.float64)
+    lam = np.asarray(lam, np.float64)
+    active = (z > 0.0) & (lam != 0.0)[None, :]
+    g = np.where(active, lam[None, :] * np.maximum(z, 0.0), 0.0)
+    return z, active, g
+
+
+def mean_up(W_up) -> np.ndarray:
+    """Inter-expert mean of the up-projection weights, Wbar = (1/E) sum_e W_up[e].
+
+    [W-CN] Sec. 二, expert design: the average over all experts' up-projection
+    weights; at inference the weights are fixed, so this matrix is computed
+    once and stored.  W_up: [E, d, F] -> [d, F].
+    """
+    W_up = np.asarray(W_up, np.float64)
+    return W_up.sum(axis=0) / W_up.shape[0]
+
+
+def normsilu(h, m, eps):
+    """NormSiLU on up-projection rows.
+
+    [W-CN] Sec. 二 and [P-DECO] Sec. 1/2: first subtract the inter-expert mean
+    term m = x . Wbar from the expert's intermediate activation h, then
+    normalise the scale inside the expert (RMS over the F entries of the row),
+    then apply SiLU.  h, m: [n, F].
+    """
+    ht = np.asarray(h, np.float64) - np.asarray(m, np.float64)
+    r = np.sqrt(np.mean(ht * ht, axis=-1, keepdims=True) + eps)
+    return silu(ht / r)
+
+
+def expert_mlp(x_rows, m_rows, W_up_e, W_down_e, eps):
+    """One non-gated routed expert: up-projection -> NormSiLU -> down-projection.
+
+    [W-CN] Sec. 二 (non-gated MLP experts: two matrices, no gate matrix);
+    [P-DECO] Sec. 2 "Expert design".  x_rows [n,d], m_rows [n,F] -> [n,d].
+    """
+    h = np.asarray(x_rows, np.float64) @ np.asarray(W_up_e, np.float64)
+    return normsilu(h, m_rows, eps) @ np.asarray(W_down_e, np.float64)
+
+
+def shared_expert(x, Ws_up, Ws_down):
+    """Always-on shared expert: non-gated MLP with plain SiLU, weight 1.
+
+    [W-CN] Sec. 二 (a shared expert takes part for every token);
+    [P-DECO] Sec. 1.  x [T,d] -> [T,d].
+    """
+    return silu(np.asarray(x, np.float64) @ np.asarray(Ws_up, np.float64)) @ np.asarray(Ws_down, np.float64)
+
+
+@dataclasses.dataclass
+class OracleResult:
+    out: np.ndarray      # [T, d] float64
+    z: np.ndarray        # [T, E] router logits
+    active: np.ndarray   # [T, E] bool
+    g: np.ndarray        # [T, E] gates
+    routed: np.ndarray   # [T, d] routed part of out
+    shared: np.ndarray   # [T, d] shared-expert part of out
+
+
+def forward(x, W_r, b_r, lam, W_up, W_down, Ws_up, Ws_down, eps=1e-6) -> OracleResult:
+    """Sparse evaluation of one DECO layer, expert by expert.
+
+    Steps: router; Wbar and m = x . Wbar; for each expert e the tokens S_e
+    that activate it, in ascending order (per-expert bucketing), the expert
+    MLP on those rows, and out[S_e] += g[S_e, e] * y (gate-weighted combine,
+    [P-DECO] Sec. 2 "Router design": the router assigns a weight to each
+    expert); finally the shared expert is added.
+    """
+    x = np.asarray(x, np.float64)
+    T, d = x.shape
+    W_up = np.asarray(W_up, np.float64)
+    E = W_up.shape[0]
+    z, active, g = router(x, W_r, b_r, lam)
+    m = x @ mean_up(W_up)
+    routed = np.zeros((T, d))
+    for e in range(E):
+        S = np.nonzero(active[:, e])[0]
+        if S.size == 0:
+            continue
+        y = expert_mlp(x[S], m[S], W_up[e], W_down[e], eps)
+        routed[S] += g[S, e][:, None] * y
+    shared = shared_expert(x, Ws_up, Ws_down)
+    return OracleResult(out=routed + shared, z=z, active=active, g=g, routed=routed, shared=shared)
+
+
+def forward_dense_bruteforce(x, W_r, b_r, lam, W_up, W_down, Ws_up, Ws_down, eps=1e-6) -> np.ndarray:
+    """Dense brute force for small inputs: every expert for every token.
+
+    Ignores the mask: each (token, expert) pair is evaluated one at a time,
+    the mean term is rebuilt per token as the average of that token's E
+    up-projections (no precomputed Wbar), and the result is weighted by the
+    gate, which is zero for inactive pairs.  Used only to pin `forward`.
+    """
+    x = np.asarray(x, np.float64)
+    T, d = x.shape
+    W_up = np.asarray(W_up, np.float64)
+    W_down = np.asarray(W_down, np.float64)
+    E = W_up.shape[0]
+    _, _, g = router(x, W_r, b_r, lam)
+    out = np.zeros((T, d))
+    for t in range(T):
+        h_all = np.stack([x[t] @ W_up[e] for e in range(E)])      # [E, F]
+        m_t = h_all.sum(axis=0) / E
+        for e in range(E):
+            ht = h_all[e] - m_t
+            r = np.sqrt(np.mean(ht * ht) + eps)
+            a = silu(ht / r)
+            out[t] += g[t, e] * (a @ W_down[e])
+        out[t] += silu(x[t] @ np.asarray(Ws_up, np.float64)) @ np.asarray(Ws_down, np.float64)
+    return out

@@ -1,0 +1,270 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle itself.
+
+Each test targets a plausible mistake: a dropped term (bias, lambda, mean term,
+shared expert), a wrong sign, a wrong reduction axis, a transposed operand, a
+wrong tie rule at zero, or broken bucketing/combine.  CPU only.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synthetic import make_custom, make_layer, round_to_bf16, bf16_bits
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _fw(L, **over):
+    x = over.pop("x", L.x)
+    w = L.weights()
+    w.update(over)
+    return oracle.forward(x, **w, eps=L.eps)
+
+
+def _rms(a):
+    return float(np.sqrt(np.mean(np.asarray(a) ** 2)))
+
+
+def _torch_shared(x, Ws_up, Ws_down):
+    """Shared expert through torch library routines (a second, independent evaluation)."""
+    xt = torch.from_numpy(np.ascontiguousarray(x))
+    return (torch.nn.functional.silu(xt @ torch.from_numpy(Ws_up)) @ torch.from_numpy(Ws_down)).numpy()
+
+
+# 1. brute force --------------------------------------------------------------
+@pytest.mark.parametrize("case", ["c1", "c2slice", "skewed"])
+def test_sparse_dispatch_equals_dense_bruteforce(case):
+    if case == "c1":
+        L = make_layer(1)
+    elif case == "c2slice":
+        # d=2048 layer of the decode workload, first 8 experts, 6 tokens
+        L = make_custom(2048, 8, 128, 256, 6, "bf16", seed=3)
+    else:
+        L = make_custom(128, 12, 64, 96, 24, "f32", seed=5, skew_var=0.3, ratio=0.3)
+    r = _fw(L)
+    bf = oracle.forward_dense_bruteforce(L.x, **L.weights(), eps=L.eps)
+    assert r.active.any() and not r.active.all()
+    assert np.max(np.abs(r.out - bf)) <= 1e-12 * _rms(bf)
+
+
+# 2./3. collapses to the shared expert ----------------------------------------
+def test_all_negative_logits_give_shared_only():
+    L = make_layer(1)
+    r = _fw(L, b_r=np.full(L.E, -1e4))
+    assert not r.active.any()
+    assert np.array_equal(r.routed, np.zeros_like(r.routed))
+    ref = _torch_shared(L.x, L.Ws_up, L.Ws_down)
+    assert np.max(np.abs(r.out - ref)) <= 1e-13 * _rms(ref)
+
+
+def test_lambda_zero_gives_shared_only_and_inactive():
+    L = make_layer(1)
+    r = _fw(L, lam=np.zeros(L.E))
+    assert not r.active.any()
+    ref = _torch_shared(L.x, L.Ws_up, L.Ws_down)
+    assert np.max(np.abs(r.out - ref)) <= 1e-13 * _rms(ref)
+
+
+def test_single_lambda_zero_only_drops_that_expert():
+    L = make_layer(1)
+    lam = L.lam.copy()
+    lam[3] = 0.0
+    r0 = _fw(L)
+    r1 = _fw(L, lam=lam)
+    assert r0.active[:, 3].any() and not r1.active[:, 3].any()
+    # expert 3's contribution, rebuilt from the brute-force pieces
+    m = L.x @ oracle.mean_up(L.W_up)
+    S = np.nonzero(r0.active[:, 3])[0]
+    y3 = oracle.expert_mlp(L.x[S], m[S], L.W_up[3], L.W_down[3], L.eps) * r0.g[S, 3][:, None]
+    diff = r0.out.copy()
+    diff[S] -= y3
+    assert np.max(np.abs(diff - r1.out)) <= 1e-12 * _rms(r0.out)
+
+
+def test_gate_is_linear_in_lambda():
+    L = make_layer(1)
+    r1 = _fw(L)
+    r3 = _fw(L, lam=2.5 * L.lam)
+    assert np.array_equal(r1.active, r3.active)
+    assert np.max(np.abs(r3.routed - 2.5 * r1.routed)) <= 1e-12 * _rms(r1.routed)
+    # and the gate equals lambda * logit on active entries (ReLU then scale)
+    assert np.allclose(r1.g[r1.active], (L.lam[None, :] * r1.z)[r1.active], rtol=0, atol=0)
+
+
+# 4./5. mean term ---------------------------------------------------------------
+def test_mean_term_is_mean_of_expert_projections():
+    L = make_layer(1)
+    m = L.x @ oracle.mean_up(L.W_up)
+    per = np.stack([L.x @ L.W_up[e] for e in range(L.E)])     # [E,T,F]
+    assert np.max(np.abs(m - per.mean(axis=0))) <= 1e-12 * np.max(np.abs(per))
+
+
+def test_mean_subtracted_activations_sum_to_zero_over_experts():
+    # NormSiLU step 1 over the right set: sum_e (h_e - m) == 0 for every token
+    L = make_custom(96, 7, 48, 32, 9, "f32", seed=11)
+    m = L.x @ oracle.mean_up(L.W_up)
+    ht = np.stack([L.x @ L.W_up[e] - m for e in range(L.E)])
+    scale = np.max(np.abs(ht))
+    assert np.max(np.abs(ht.sum(axis=0))) <= 1e-12 * scale
+    # the wrong sign (adding m) would not sum to zero
+    assert np.max(np.abs(np.stack([L.x @ L.W_up[e] + m for e in range(L.E)]).sum(0))) > 1e-3 * scale
+
+
+def test_mean_includes_inactive_experts():
+    # Wbar is fixed at load time: deactivating experts must not change the
+    # routed output of the experts that stay active.
+    L = make_layer(1)
+    b = L.b_r.copy()
+    b[[0, 5]] = -1e4
+    r0 = _fw(L)
+    r1 = _fw(L, b_r=b)
+    keep = [e for e in range(L.E) if e not in (0, 5)]
+    m = L.x @ oracle.mean_up(L.W_up)
+    ref = np.zeros_like(r1.routed)
+    for e in keep:
+        S = np.nonzero(r0.active[:, e])[0]
+        if S.size:
+            ref[S] += r0.g[S, e][:, None] * oracle.expert_mlp(L.x[S], m[S], L.W_up[e], L.W_down[e], L.eps)
+    assert np.max(np.abs(r1.routed - ref)) <= 1e-12 * _rms(ref)
+
+
+# 6./8. RMS step -----------------------------------------------------------------
+def test_up_projection_scale_invariance_at_eps0():
+    L = make_layer(1)
+    w = L.weights()
+    a = oracle.forward(L.x, **w, eps=0.0)
+    w["W_up"] = 7.25 * L.W_up
+    b = oracle.forward(L.x, **w, eps=0.0)
+    assert np.max(np.abs(a.out - b.out)) <= 1e-10 * _rms(a.out)
+
+
+def test_pre_silu_rows_have_mean_square_ms_over_ms_plus_eps():
+    rng = np.random.default_rng(0)
+    h = rng.standard_normal((10, 32)) * 1e-3
+    m = rng.standard_normal((10, 32)) * 1e-4
+    eps = 1e-6
+    ht = h - m
+    ms = np.mean(ht * ht, axis=1)
+    r = np.sqrt(ms + eps)
+    u = ht / r[:, None]
+    # invert SiLU numerically to check what normsilu fed it
+    a = oracle.normsilu(h, m, eps)
+    # u*sigmoid(u) is monotone for u > -1.278; check the relation on reconstructed u
+    assert np.allclose(a, u / (1 + np.exp(-u)), rtol=1e-14, atol=0)
+    assert np.allclose(np.mean(u * u, axis=1), ms / (ms + eps), rtol=1e-12)
+
+
+def test_rms_axis_is_per_row():
+    # rows with very different scales normalise independently (wrong axis fails)
+    h = np.array([[1.0, -2.0, 3.0, 0.5], [100.0, 200.0, -50.0, 10.0]])
+    a = oracle.normsilu(h, np.zeros_like(h), 0.0)
+    a_row0 = oracle.normsilu(h[:1], np.zeros((1, 4)), 0.0)
+    a_row1_scaled = oracle.normsilu(h[1:] / 100.0, np.zeros((1, 4)), 0.0)
+    assert np.allclose(a[0], a_row0[0], rtol=1e-15)
+    assert np.allclose(a[1], a_row1_scaled[0], rtol=1e-13)
+
+
+# 7. E = 1 -----------------------------------------------------------------------
+def test_single_expert_routed_contribution_vanishes():
+    L = make_custom(64, 1, 32, 48, 12, "f32", seed=2, ratio=0.9)
+    r = _fw(L)
+    assert r.active.any()
+    assert np.max(np.abs(r.routed)) <= 1e-12 * _rms(r.shared)
+
+
+# 9. F = 1 closed form -------------------------------------------------------------
+def test_f1_closed_form():
+    with open(os.path.join(GOLDEN, "closed_forms.json")) as f:
+        cf = json.load(f)
+    h = np.array([[3.7], [-0.02], [1e-2]])
+    a = oracle.normsilu(h, np.zeros_like(h), 1e-12)
+    assert abs(a[0, 0] - cf["silu_of_plus_one"]) < 1e-6
+    assert abs(a[1, 0] - cf["silu_of_minus_one"]) < 1e-6
+    assert abs(a[2, 0] - cf["silu_of_plus_one"]) < 1e-6
+
+
+# 10. single expert with Wbar = 0 vs torch rms_norm / silu ----------------------------
+def test_single_active_expert_with_zero_mean_matches_torch_rmsnorm_silu():
+    d, F, Fs, T = 64, 24, 16, 10
+    L = make_custom(d, 2, F, Fs, T, "f32", seed=4)
+    W_up = L.W_up.copy()
+    W_up[1] = -W_up[0]                      # Wbar == 0 exactly
+    b = np.array([1e4, -1e4])               # expert 0 always on, expert 1 never
+    r = _fw(L, W_up=W_up, b_r=b)
+    assert r.active[:, 0].all() and not r.active[:, 1].any()
+    eps = L.eps
+    h = torch.from_numpy(L.x @ W_up[0])
+    a = torch.nn.functional.silu(torch.nn.functional.rms_norm(h, (F,), eps=eps))
+    y = (a @ torch.from_numpy(L.W_down[0])).numpy() * r.g[:, :1]
+    assert np.max(np.abs(r.routed - y)) <= 1e-12 * _rms(y)
+
+
+# 11. token independence, expert permutation -----------------------------------------
+def test_token_independence():
+    L = make_layer(1)
+    full = _fw(L).out
+    rows = np.concatenate([_fw(L, x=L.x[t:t + 1]).out for t in range(L.T)])
+    assert np.max(np.abs(full - rows)) <= 1e-12 * _rms(full)
+
+
+def test_expert_permutation_equivariance():
+    L = make_layer(1)
+    perm = np.random.default_rng(1).permutation(L.E)
+    r0 = _fw(L)
+    r1 = _fw(L, W_r=L.W_r[:, perm], b_r=L.b_r[perm], lam=L.lam[perm],
+             W_up=L.W_up[perm], W_down=L.W_down[perm])
+    assert np.array_equal(r1.active, r0.active[:, perm])
+    assert np.max(np.abs(r0.out - r1.out)) <= 1e-12 * _rms(r0.out)
+
+
+def test_transposed_down_projection_is_detected():
+    # non-square F != d: feeding W_down transposed would not even conform
+    L = make_layer(1)
+    with pytest.raises(ValueError):
+        oracle.forward(L.x, L.W_r, L.b_r, L.lam, L.W_up, np.swapaxes(L.W_down, 1, 2),
+                       L.Ws_up, L.Ws_down, eps=L.eps)
+
+
+# zero tie ---------------------------------------------------------------------------
+def test_zero_logit_is_inactive_and_positive_is_active():
+    L = make_layer(1)
+    x0 = np.zeros((3, L.d))
+    b = np.zeros(L.E)
+    b[2] = 1e-30
+    b[4] = -1e-30
+    r = _fw(L, x=x0, b_r=b)
+    expect = np.zeros((3, L.E), bool)
+    expect[:, 2] = True
+    assert np.array_equal(r.active, expect)
+    assert np.all(r.g[:, 2] == L.lam[2] * 1e-30)
+
+
+# 12. realised ratio ---------------------------------------------------------------
+@pytest.mark.parametrize("ratio", [0.05, 0.10, 0.20, 0.40])
+def test_realised_activation_ratio_in_binomial_band(ratio):
+    L = make_custom(512, 32, 32, 32, 512, "bf16", seed=7, ratio=ratio)
+    _, active, _ = oracle.router(L.x, L.W_r, L.b_r, L.lam)
+    n = active.size
+    p_hat = active.mean()
+    # per-token count is variable (ReLU routing), the mean is the target
+    assert abs(p_hat - ratio) <= 5 * math.sqrt(ratio * (1 - ratio) / n) + 0.01
+    per_tok = active.sum(axis=1)
+    assert per_tok.min() < per_tok.max()
+
+
+def test_generator_bf16_rounding_is_single_rne_cast():
+    # halfway cases round to even; exact values stay; bits round-trip
+    one = 1.0
+    ulp = 2.0 ** -7
+    v = np.array([one + ulp / 2, one + 3 * ulp / 2, one + ulp / 2 + 1e-12, -2.5, 0.0])
+    r = round_to_bf16(v)
+    assert r[0] == one and r[1] == one + 2 * ulp and r[2] == one + ulp
+    assert r[3] == -2.5 and r[4] == 0.0
+    bits = bf16_bits(r)
+    assert bits[0] == 0x3F80 and bits[3] == 0xC020
+    t = torch.tensor(v[:2], dtype=torch.float64).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(t, r[:2])
