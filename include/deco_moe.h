@@ -1,0 +1,144 @@
+/*
+ * deco_moe.h - C ABI of the MI355X (gfx950) DECO sparse-MoE feed-forward layer.
+ *
+ * The layer (forward pass only), in the notation of the DECO paper
+ * ("DECO: Sparse Mixture-of-Experts with Dense-Comparable Performance on
+ * End-Side Devices", Sec. 1 Introduction and Sec. 2 Related work, paragraphs
+ * "Router design" and "Expert design"; and the Chinese write-up of the same
+ * paper on qidianchuan.cn, section 二, router and expert-design parts):
+ *
+ *   z      = x W_r + b_r                          router logits       [T, E]
+ *   g      = lambda_e * max(z, 0)                 gates (ReLU routing with a
+ *                                                 learned per-expert scale)
+ *   active = (z > 0) and (lambda_e != 0)          variable experts per token
+ *   Wbar   = (1/E) sum_e W_up[e]                  inter-expert mean, fixed at load
+ *   for each active (t, e):
+ *     h~   = x_t W_up[e] - x_t Wbar               NormSiLU step 1 (mean term)
+ *     r    = sqrt(mean_f h~_f^2 + eps)            NormSiLU step 2 (RMS inside
+ *     a    = SiLU(h~ / r)                         the expert), then SiLU
+ *     out_t += g_te * a W_down[e]                 non-gated expert, weighted sum
+ *   out_t += SiLU(x_t Ws_up) Ws_down               always-on shared expert
+ *
+ * Memory: every pointer argument of the compute calls is DEVICE memory,
+ * row-major and contiguous, owned by the caller; `stream` is a hipStream_t
+ * passed as void* (NULL = the default stream).  Weights and activations share
+ * one element type (`dtype`); b_r and lambda are always float32.
+ *
+ * Errors: every call returns a deco_status (0 = OK, negative = error) and
+ * launches nothing when it fails validation; output buffers are then left
+ * untouched.  No C++ exception crosses this interface.  Non-finite inputs are
+ * not detected.  A layer may be used by one stream at a time: calls that
+ * overlap on one layer race on its workspace.
+ */
+#ifndef DECO_MOE_H
+#define DECO_MOE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct deco_moe_layer deco_moe_layer;   /* opaque, owns all its device buffers */
+
+typedef enum {
+  DECO_OK = 0,
+  DECO_ERR_INVALID_ARG = -1,     /* null pointer, T < 0, T > max_tokens, E < 1, ... */
+  DECO_ERR_UNSUPPORTED = -2,     /* shape or dtype outside the supported set      */
+  DECO_ERR_OUT_OF_MEMORY = -3,   /* device allocation failed                      */
+  DECO_ERR_HIP = -4              /* a HIP runtime call or a launch failed         */
+} deco_status;
+
+typedef enum { DECO_DT_BF16 = 0, DECO_DT_F32 = 1 } deco_dtype;
+
+typedef enum {
+  DECO_PATH_AUTO = 0,     /* decode path for T <= DECO_DECODE_MAX_T, else prefill */
+  DECO_PATH_DECODE = 1,   /* weight-streaming path; requires T <= DECO_DECODE_MAX_T */
+  DECO_PATH_PREFILL = 2   /* bucketed grouped-MFMA path; any T                      */
+} deco_path;
+
+#define DECO_DECODE_MAX_T 16
+
+typedef struct {
+  int32_t d_model;      /* d  : multiple of 64                                  */
+  int32_t n_experts;    /* E  : 1 .. 256 routed experts                         */
+  int32_t d_ff;         /* F  : routed expert width, one of 32, 64, 128, 256    */
+  int32_t d_ff_shared;  /* Fs : shared expert width, multiple of 32, 32..16384  */
+  int32_t max_tokens;   /* largest T passed to deco_moe_forward (>= 1)          */
+  deco_dtype dtype;     /* element type of x, out and all weight matrices       */
+  float rms_eps;        /* epsilon inside the NormSiLU RMS (e.g. 1e-6), >= 0    */
+} deco_moe_config;
+
+/* Check a configuration without touching the GPU.  Returns DECO_OK,
+ * DECO_ERR_INVALID_ARG (null, non-positive sizes, negative eps) or
+ * DECO_ERR_UNSUPPORTED (shape outside the set documented in the struct). */
+int deco_moe_check_config(const deco_moe_config* cfg);
+
+/* Copy, pack and preprocess one layer's weights into library-owned device
+ * buffers, and size the layer's workspace for cfg->max_tokens tokens.
+ *   W_r     [d, E]      dtype     router projection
+ *   b_r     [E]         float32   router bias
+ *   lambda  [E]         float32   expert-wise router scaling
+ *   W_up    [E, d, F]   dtype     routed up-projections
+ *   W_down  [E, F, d]   dtype     routed down-projections
+ *   Ws_up   [d, Fs]     dtype     shared-expert up-projection
+ *   Ws_down [Fs, d]     dtype     shared-expert down-projection
+ * Computes Wbar = mean over all E routed experts of W_up (the NormSiLU mean
+ * term is precomputable because inference weights are fixed: qidianchuan.cn
+ * write-up, section 二, expert design) in fp32 and folds it into the packed
+ * up-projections (W_up[e] - Wbar).  Runs on `stream` and synchronizes it
+ * before returning, so the sources may be freed afterwards.  On success
+ * *out_layer receives the new layer; on failure it is set to NULL and nothing
+ * stays allocated. */
+int deco_moe_load_weights(const deco_moe_config* cfg,
+                          const void* W_r, const float* b_r, const float* lambda,
+                          const void* W_up, const void* W_down,
+                          const void* Ws_up, const void* Ws_down,
+                          void* stream, deco_moe_layer** out_layer);
+
+/* One forward pass: out [T, d] = DECO layer(x [T, d]), both of the layer's
+ * dtype, on device.  x and out must not overlap.  Asynchronous on `stream`;
+ * allocates nothing and never waits on the host.  T == 0 returns DECO_OK and
+ * launches nothing.  Same as deco_moe_forward_path(..., DECO_PATH_AUTO). */
+int deco_moe_forward(const deco_moe_layer* L, const void* x, int64_t T, void* out, void* stream);
+
+/* As deco_moe_forward, with the kernel family chosen explicitly (both give
+ * the same result up to fp32 summation order).  DECO_PATH_DECODE with
+ * T > DECO_DECODE_MAX_T returns DECO_ERR_INVALID_ARG. */
+int deco_moe_forward_path(const deco_moe_layer* L, const void* x, int64_t T, void* out,
+                          void* stream, int path);
+
+/* Routing state of the most recent forward on L, for the same T:
+ *   mask   [T, ceil(E/64)] uint64 (device): bit e%64 of word e/64 of row t is
+ *          set iff expert e was active for token t (z > 0 and lambda_e != 0);
+ *   logits [T, E] float32 (device, may be NULL): router logits z as computed
+ *          on the GPU (fp32 accumulation of the dtype products, plus b_r).
+ * T must equal the T of that forward (not checked beyond 0 <= T <= max). */
+int deco_moe_copy_routing(const deco_moe_layer* L, int64_t T, uint64_t* mask, float* logits,
+                          void* stream);
+
+/* Copy the inter-expert mean Wbar [d, F] (float32, device) built at load. */
+int deco_moe_copy_mean_up(const deco_moe_layer* L, float* wbar, void* stream);
+
+/* Release every device buffer of L (NULL is a no-op).  The caller must make
+ * sure no work using L is still pending on any stream. */
+void deco_moe_free(deco_moe_layer* L);
+
+/* Static English description of a status code. */
+const char* deco_moe_status_string(int status);
+
+/* Per-kernel timing with HIP events, for measurement.  While enabled, every
+ * forward records a start/stop event pair around each kernel it launches, on
+ * the launch stream.  deco_moe_timing_read waits for those events and returns
+ * for kernel slot `idx` its name, the summed elapsed milliseconds and the
+ * number of launches since the last reset; it returns DECO_ERR_INVALID_ARG
+ * once idx passes the last slot.  Not thread-safe; global to the library. */
+int deco_moe_timing_enable(int enable);
+int deco_moe_timing_reset(void);
+int deco_moe_timing_read(int idx, const char** name, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DECO_MOE_H */

@@ -1,0 +1,235 @@
+"""Python binding of libdeco_moe.so: the MI355X DECO sparse-MoE FFN layer.
+
+Argument marshalling only: every step of the forward pass runs in the HIP
+kernels of the library.  torch provides device memory and streams.  There is
+no fallback: if the library is missing the import of `load_library()` fails
+loudly (build it with ``python -m sparse_moe_relu_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+# torch first: its HIP runtime (soname libamdhip64.so.7) must be the one the
+# library binds to, so tensors and kernels share one runtime.
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdeco_moe.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "deco_moe.h")
+
+DECO_OK = 0
+DECO_ERR_INVALID_ARG = -1
+DECO_ERR_UNSUPPORTED = -2
+DECO_ERR_OUT_OF_MEMORY = -3
+DECO_ERR_HIP = -4
+DECO_DT_BF16 = 0
+DECO_DT_F32 = 1
+DECO_PATH_AUTO = 0
+DECO_PATH_DECODE = 1
+DECO_PATH_PREFILL = 2
+DECODE_MAX_T = 16
+
+EXPORTS = ("deco_moe_check_config", "deco_moe_load_weights", "deco_moe_forward",
+           "deco_moe_forward_path", "deco_moe_copy_routing", "deco_moe_copy_mean_up",
+           "deco_moe_free", "deco_moe_status_string", "deco_moe_timing_enable",
+           "deco_moe_timing_reset", "deco_moe_timing_read")
+
+
+class DecoConfig(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int32), ("n_experts", ctypes.c_int32),
+                ("d_ff", ctypes.c_int32), ("d_ff_shared", ctypes.c_int32),
+                ("max_tokens", ctypes.c_int32), ("dtype", ctypes.c_int),
+                ("rms_eps", ctypes.c_float)]
+
+
+class DecoError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load (once) and type the C ABI.  Raises if the library is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"libdeco_moe.so not found at {path}; build it with "
+                           "`python -m sparse_moe_relu_amd.build` (no fallback path exists)")
+    lib = ctypes.CDLL(path)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.deco_moe_check_config.argtypes = [ctypes.POINTER(DecoConfig)]
+    lib.deco_moe_check_config.restype = i32
+    lib.deco_moe_load_weights.argtypes = [ctypes.POINTER(DecoConfig), vp, vp, vp, vp, vp, vp, vp, vp,
+                                          ctypes.POINTER(vp)]
+    lib.deco_moe_load_weights.restype = i32
+    lib.deco_moe_forward.argtypes = [vp, vp, i64, vp, vp]
+    lib.deco_moe_forward.restype = i32
+    lib.deco_moe_forward_path.argtypes = [vp, vp, i64, vp, vp, i32]
+    lib.deco_moe_forward_path.restype = i32
+    lib.deco_moe_copy_routing.argtypes = [vp, i64, vp, vp, vp]
+    lib.deco_moe_copy_routing.restype = i32
+    lib.deco_moe_copy_mean_up.argtypes = [vp, vp, vp]
+    lib.deco_moe_copy_mean_up.restype = i32
+    lib.deco_moe_free.argtypes = [vp]
+    lib.deco_moe_free.restype = None
+    lib.deco_moe_status_string.argtypes = [i32]
+    lib.deco_moe_status_string.restype = ctypes.c_char_p
+    lib.deco_moe_timing_enable.argtypes = [i32]
+    lib.deco_moe_timing_enable.restype = i32
+    lib.deco_moe_timing_reset.argtypes = []
+    lib.deco_moe_timing_reset.restype = i32
+    lib.deco_moe_timing_read.argtypes = [i32, ctypes.POINTER(ctypes.c_char_p),
+                                         ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+    lib.deco_moe_timing_read.restype = i32
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().deco_moe_status_string(int(status)).decode()
+
+
+def make_config(d: int, E: int, F: int, Fs: int, max_tokens: int, dtype: str = "bf16",
+                eps: float = 1e-6) -> DecoConfig:
+    dt = {"bf16": DECO_DT_BF16, "f32": DECO_DT_F32}[dtype]
+    return DecoConfig(d, E, F, Fs, max_tokens, dt, eps)
+
+
+def check_config(cfg: DecoConfig) -> int:
+    return int(load_library().deco_moe_check_config(ctypes.byref(cfg)))
+
+
+def _stream_handle(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+_TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+class Layer:
+    """One DECO MoE FFN layer whose weights live in library-owned device buffers.
+
+    Weights are device tensors of the layer dtype (b_r and lam: float32):
+    W_r [d,E], b_r [E], lam [E], W_up [E,d,F], W_down [E,F,d], Ws_up [d,Fs],
+    Ws_down [Fs,d].  They are packed at construction and may be freed after.
+    """
+
+    def __init__(self, W_r, b_r, lam, W_up, W_down, Ws_up, Ws_down, *, max_tokens: int,
+                 eps: float = 1e-6, stream=None):
+        lib = load_library()
+        dtype = {torch.bfloat16: "bf16", torch.float32: "f32"}.get(W_up.dtype)
+        if dtype is None:
+            raise TypeError(f"unsupported weight dtype {W_up.dtype}")
+        E, d, F = W_up.shape
+        Fs = Ws_up.shape[1]
+        shapes = {"W_r": (W_r, (d, E)), "W_up": (W_up, (E, d, F)), "W_down": (W_down, (E, F, d)),
+                  "Ws_up": (Ws_up, (d, Fs)), "Ws_down": (Ws_down, (Fs, d))}
+        for name, (t, shp) in shapes.items():
+            if tuple(t.shape) != shp or t.dtype != W_up.dtype or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name}: expected contiguous device {shp} {W_up.dtype}, got "
+                                 f"{tuple(t.shape)} {t.dtype} {t.device}")
+        for name, t in (("b_r", b_r), ("lam", lam)):
+            if tuple(t.shape) != (E,) or t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name}: expected contiguous device float32 ({E},)")
+        self.cfg = make_config(d, E, F, Fs, max_tokens, dtype, eps)
+        self.d, self.E, self.F, self.Fs, self.dtype = d, E, F, Fs, dtype
+        self.max_tokens = max_tokens
+        self.W = (E + 63) // 64
+        h = ctypes.c_void_p()
+        st = lib.deco_moe_load_weights(ctypes.byref(self.cfg), W_r.data_ptr(), b_r.data_ptr(),
+                                       lam.data_ptr(), W_up.data_ptr(), W_down.data_ptr(),
+                                       Ws_up.data_ptr(), Ws_down.data_ptr(), _stream_handle(stream),
+                                       ctypes.byref(h))
+        if st != DECO_OK:
+            raise DecoError(st, "deco_moe_load_weights")
+        self._h = h
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        if self._h is None:
+            raise RuntimeError("layer was freed")
+        return self._h
+
+    def forward(self, x: torch.Tensor, out: torch.Tensor | None = None, *, path: int = DECO_PATH_AUTO,
+                stream=None) -> torch.Tensor:
+        T = x.shape[0]
+        if x.dim() != 2 or x.shape[1] != self.d or x.dtype != _TORCH_DT[self.dtype] or not x.is_cuda \
+                or not x.is_contiguous():
+            raise ValueError(f"x: expected contiguous device [T,{self.d}] {_TORCH_DT[self.dtype]}")
+        if out is None:
+            out = torch.empty_like(x)
+        st = load_library().deco_moe_forward_path(self.handle, x.data_ptr(), T, out.data_ptr(),
+                                                  _stream_handle(stream), int(path))
+        if st != DECO_OK:
+            raise DecoError(st, "deco_moe_forward")
+        return out
+
+    __call__ = forward
+
+    def routing(self, T: int, stream=None):
+        """(mask [T, ceil(E/64)] int64 bit words, logits [T, E] float32) of the last forward."""
+        mask = torch.empty((T, self.W), dtype=torch.int64, device="cuda")
+        logits = torch.empty((T, self.E), dtype=torch.float32, device="cuda")
+        st = load_library().deco_moe_copy_routing(self.handle, T, mask.data_ptr(), logits.data_ptr(),
+                                                  _stream_handle(stream))
+        if st != DECO_OK:
+            raise DecoError(st, "deco_moe_copy_routing")
+        return mask, logits
+
+    def active_mask(self, T: int, stream=None) -> torch.Tensor:
+        """Boolean [T, E] active-expert mask of the last forward (on the host)."""
+        mask, _ = self.routing(T, stream)
+        words = mask.cpu().numpy().view("uint64")
+        import numpy as np
+        bits = np.unpackbits(words.view(np.uint8).reshape(T, self.W, 8), axis=2, bitorder="little")
+        return torch.from_numpy(bits.reshape(T, self.W * 64)[:, :self.E].astype(bool))
+
+    def mean_up(self, stream=None) -> torch.Tensor:
+        wbar = torch.empty((self.d, self.F), dtype=torch.float32, device="cuda")
+        st = load_library().deco_moe_copy_mean_up(self.handle, wbar.data_ptr(), _stream_handle(stream))
+        if st != DECO_OK:
+            raise DecoError(st, "deco_moe_copy_mean_up")
+        return wbar
+
+    def free(self):
+        if getattr(self, "_h", None) is not None:
+            load_library().deco_moe_free(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+def timing_enable(on: bool = True):
+    load_library().deco_moe_timing_enable(1 if on else 0)
+
+
+def timing_reset():
+    load_library().deco_moe_timing_reset()
+
+
+def timing_read() -> dict:
+    """{kernel name: (total_ms, launches)} accumulated since the last reset."""
+    lib = load_library()
+    out = {}
+    i = 0
+    while True:
+        name = ctypes.c_char_p()
+        ms = ctypes.c_double()
+        n = ctypes.c_int64()
+        if lib.deco_moe_timing_read(i, ctypes.byref(name), ctypes.byref(ms), ctypes.byref(n)) != DECO_OK:
+            break
+        if n.value:
+            out[name.value.decode()] = (ms.value, n.value)
+        i += 1
+    return out

@@ -1,0 +1,139 @@
+// deco_common.h - shared device helpers of the DECO MoE HIP library (gfx950).
+//
+// Fragment convention used by every kernel.  A "k-block" is KB consecutive
+// reduction indices; one 16-byte vector per lane of a 64-lane wave (1 KiB)
+// holds a 16 x KB operand tile of an MFMA 16x16 product:
+//   lane l serves row/column (l & 15) and lane group g = l >> 4;
+//   bf16 (KB = 32): element j (0..7) of the lane is k = 8 g + j, consumed by
+//                   one v_mfma_f32_16x16x32_bf16;
+//   fp32 (KB = 16): element j (0..3) of the lane is k = 4 j + g, consumed by
+//                   the j-th of four v_mfma_f32_16x16x4_f32.
+// The 16x16 fp32 result of a lane holds rows 4 g + i (i = 0..3) of column
+// (l & 15).  Weights are packed once, at load, into this layout so each lane
+// fetches its operand with one 16-byte load (a wave reads 1 KiB contiguous).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace deco {
+
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4_t;
+
+constexpr int WAVE = 64;
+constexpr int FRAG_BYTES = 1024;   // one k-block x 16 columns, all 64 lanes
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// round-to-nearest-even float -> bf16 bits (inputs are finite)
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+struct BF16 {
+  using elem = uint16_t;
+  static constexpr int KB = 32;    // k per fragment
+  static constexpr int EPL = 8;    // elements per lane
+  // gated expert activations enter the down-projection as hi + lo bf16 parts
+  static constexpr bool SPLIT = true;
+  // per-(token, expert) outputs kept between the expert and combine kernels
+  using pair = _Float16;
+  __host__ __device__ static constexpr int frag_k(int g, int j) { return 8 * g + j; }
+  __device__ static float to_f32(elem v) { return bf16_to_f32(v); }
+  __device__ static elem from_f32(float f) { return (elem)f32_to_bf16(f); }
+  // lane group / element index holding in-block k index `w` (inverse of frag_k)
+  __host__ __device__ static constexpr int frag_g(int w) { return w >> 3; }
+  __host__ __device__ static constexpr int frag_j(int w) { return w & 7; }
+  __device__ static float lane_elem(const i32x4_t& v, int j) {
+    uint32_t w = (uint32_t)v[j >> 1];
+    return bf16_to_f32((j & 1) ? (w >> 16) : (w & 0xFFFFu));
+  }
+  // acc(16x16) += A(16 x 32) * B(32 x 16)
+  __device__ static void mma(f32x4_t& acc, const i32x4_t& a, const i32x4_t& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                  __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+  }
+  // pack 8 floats (j order) into one lane vector
+  __device__ static i32x4_t pack(const float* f) {
+    i32x4_t v;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      v[q] = (int)(f32_to_bf16(f[2 * q]) | (f32_to_bf16(f[2 * q + 1]) << 16));
+    return v;
+  }
+};
+
+struct F32 {
+  using elem = float;
+  static constexpr int KB = 16;
+  static constexpr int EPL = 4;
+  static constexpr bool SPLIT = false;
+  using pair = float;
+  __host__ __device__ static constexpr int frag_k(int g, int j) { return 4 * j + g; }
+  __host__ __device__ static constexpr int frag_g(int w) { return w & 3; }
+  __host__ __device__ static constexpr int frag_j(int w) { return w >> 2; }
+  __device__ static float to_f32(elem v) { return v; }
+  __device__ static elem from_f32(float f) { return f; }
+  __device__ static float lane_elem(const i32x4_t& v, int j) { return __int_as_float(v[j]); }
+  __device__ static void mma(f32x4_t& acc, const i32x4_t& a, const i32x4_t& b) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__int_as_float(a[j]), __int_as_float(b[j]), acc, 0, 0, 0);
+  }
+  __device__ static i32x4_t pack(const float* f) {
+    i32x4_t v;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = __float_as_int(f[q]);
+    return v;
+  }
+};
+
+__device__ __forceinline__ i32x4_t ld16(const void* p) { return *reinterpret_cast<const i32x4_t*>(p); }
+__device__ __forceinline__ void st16(void* p, const i32x4_t& v) { *reinterpret_cast<i32x4_t*>(p) = v; }
+__device__ __forceinline__ i32x4_t zero16() { i32x4_t z = {0, 0, 0, 0}; return z; }
+
+__device__ __forceinline__ float silu_f(float v) { return v / (1.0f + __expf(-v)); }
+
+// v = hi + lo with hi = dtype(v), lo = dtype(v - hi): two bf16 products then
+// carry v to ~16 significant bits.  For fp32, lo is 0 and unused.
+template <class DT>
+__device__ __forceinline__ void split_hi_lo(float v, typename DT::elem& hi, typename DT::elem& lo) {
+  hi = DT::from_f32(v);
+  lo = DT::from_f32(v - DT::to_f32(hi));
+}
+
+// Operand fragment of row-major data: lane (c = l & 15, g) of k-block kb of
+// row `row` (elements kb*KB + frag_k(g, j)).
+template <class DT>
+__device__ __forceinline__ i32x4_t load_row_frag(const typename DT::elem* row, int kb, int g);
+template <>
+__device__ __forceinline__ i32x4_t load_row_frag<BF16>(const uint16_t* row, int kb, int g) {
+  return ld16(row + kb * 32 + 8 * g);
+}
+template <>
+__device__ __forceinline__ i32x4_t load_row_frag<F32>(const float* row, int kb, int g) {
+  i32x4_t v;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) v[j] = __float_as_int(row[kb * 16 + 4 * j + g]);
+  return v;
+}
+
+// Byte offset, inside an array of [k-block][64 lanes][16 B] fragments, of the
+// element at operand row `row` (0..15) and reduction index k.
+template <class DT>
+__host__ __device__ __forceinline__ size_t frag_elem_off(int row, int k) {
+  const int kb = k / DT::KB, w = k % DT::KB;
+  return (size_t)kb * FRAG_BYTES + (size_t)(row + 16 * DT::frag_g(w)) * 16 +
+         (size_t)DT::frag_j(w) * sizeof(typename DT::elem);
+}
+
+// Offset (bytes) of k-block kb of 16-column panel p in a packed matrix with nkb k-blocks.
+__host__ __device__ __forceinline__ size_t frag_off(int p, int kb, int nkb) {
+  return ((size_t)p * nkb + kb) * FRAG_BYTES;
+}
+
+}  // namespace deco

@@ -1,0 +1,88 @@
+// deco_internal.h - layer object, workspace layout and kernel launchers (host side).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/deco_moe.h"
+
+struct deco_moe_layer {
+  deco_moe_config cfg;
+  int device;
+  int d, E, F, Fs, maxT;
+  int esz;                 // bytes per element (2 bf16, 4 fp32)
+  int KB;                  // k per fragment (32 bf16, 16 fp32)
+  int nkb_d, nkb_F, nkb_Fs;
+  int pR;                  // router panels (E padded to a multiple of 64, /16)
+  int pF, pD, pFs;         // 16-column panels of F, d, Fs
+  int W;                   // mask words per token = ceil(E/64)
+  int n_groups;            // d / 64 output column groups (decode down kernel)
+  int dec_q;               // K-split factor of the decode down kernel
+  int pre_grid;            // persistent grid of the prefill expert kernel
+
+  // packed weights (one allocation)
+  char* wmem;
+  size_t wmem_bytes;
+  char* Wr_p;              // router  [pR][nkb_d] frags
+  char* Wup_p;             // per expert [pF][nkb_d] frags of W_up[e]
+  char* Wbar_p;            // [pF][nkb_d] frags of Wbar (layer dtype)
+  char* Wdn_p;             // per expert [pD][nkb_F] frags
+  char* Wsu_p;             // [pFs][nkb_d]
+  char* Wsd_p;             // [pD][nkb_Fs]
+  size_t up_stride, dn_stride;   // bytes per expert
+  float* b_r;
+  float* lam;
+  float* wbar;             // [d][F] fp32
+
+  // workspace (one allocation, sized for max(maxT, 16) tokens)
+  char* ws;
+  size_t ws_bytes;
+  float* z;                // [Tcap][E] router logits
+  float* g;                // [Tcap][E] gates
+  uint64_t* mask;          // [Tcap][W]
+  // decode
+  float* mbuf;             // [Tcap][F]    x . Wbar (NormSiLU mean term)
+  float* hbuf;             // [E][16][F]   raw up-projection rows
+  char* actf;              // [E][nkb_F][hi, lo] frags  gated NormSiLU output (A operand)
+  char* sactf;             // [nkb_Fs] frags      shared SiLU output
+  int* eact;               // [E] expert touched by the batch
+  unsigned* cnt_up;        // [E] arrival counters (reset by the down kernel)
+  unsigned* cnt_dn;        // [n_groups] arrival counters
+  float* part;             // [dec_q][n_groups][16][64] partial outputs
+  // prefill
+  int* tok_off;            // [Tcap + 1]
+  int* ecnt;               // [E]
+  int* list_tok;           // [E][Tcap]
+  int* list_slot;          // [E][Tcap]
+  char* sbuf;              // [Tcap][Fs] shared activations (dtype)
+  char* ybuf;              // [Tcap * E][d] gated expert outputs, token-major (dtype)
+};
+
+namespace deco_host {
+
+struct Timer;  // per-kernel event timing (host.cpp)
+void timing_begin(hipStream_t s, int slot);
+void timing_end(hipStream_t s, int slot);
+
+// kernel slots for timing
+enum {
+  KS_PACK = 0,
+  KS_DEC_UP,
+  KS_DEC_DOWN,
+  KS_PRE_ROUTER_SHARED,
+  KS_PRE_DISPATCH,
+  KS_PRE_EXPERT,
+  KS_PRE_SHARED_DOWN,
+  KS_COUNT
+};
+const char* kernel_slot_name(int slot);
+
+// launchers (return hipSuccess or the launch error)
+hipError_t launch_pack_all(deco_moe_layer* L, const void* W_r, const void* W_up, const void* W_down,
+                           const void* Ws_up, const void* Ws_down, hipStream_t s);
+hipError_t launch_decode(const deco_moe_layer* L, const void* x, int T, void* out, hipStream_t s);
+hipError_t launch_prefill(const deco_moe_layer* L, const void* x, int T, void* out, hipStream_t s);
+hipError_t launch_copy_mask(const deco_moe_layer* L, int T, uint64_t* mask, hipStream_t s);
+
+}  // namespace deco_host

@@ -1,0 +1,338 @@
+// host.hip - the C ABI of include/deco_moe.h: validation, layer object,
+// device buffers, path choice and per-kernel event timing.
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+#include <vector>
+
+#include "deco_internal.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int validate_cfg(const deco_moe_config* c) {
+  if (!c) return DECO_ERR_INVALID_ARG;
+  if (c->d_model <= 0 || c->n_experts < 1 || c->d_ff <= 0 || c->d_ff_shared <= 0 || c->max_tokens < 1)
+    return DECO_ERR_INVALID_ARG;
+  if (!(c->rms_eps >= 0.0f) || !isfinite(c->rms_eps)) return DECO_ERR_INVALID_ARG;
+  if (c->dtype != DECO_DT_BF16 && c->dtype != DECO_DT_F32) return DECO_ERR_UNSUPPORTED;
+  if (c->d_model % 64 != 0 || c->d_model > 32768) return DECO_ERR_UNSUPPORTED;
+  if (c->n_experts > 256) return DECO_ERR_UNSUPPORTED;
+  if (c->d_ff != 32 && c->d_ff != 64 && c->d_ff != 128 && c->d_ff != 256) return DECO_ERR_UNSUPPORTED;
+  if (c->d_ff_shared % 32 != 0 || c->d_ff_shared > 16384) return DECO_ERR_UNSUPPORTED;
+  if (c->max_tokens > (1 << 20)) return DECO_ERR_UNSUPPORTED;
+  return DECO_OK;
+}
+
+// derived sizes (no allocation)
+void derive(deco_moe_layer* L) {
+  const deco_moe_config& c = L->cfg;
+  L->d = c.d_model;
+  L->E = c.n_experts;
+  L->F = c.d_ff;
+  L->Fs = c.d_ff_shared;
+  L->maxT = c.max_tokens;
+  L->esz = c.dtype == DECO_DT_BF16 ? 2 : 4;
+  L->KB = c.dtype == DECO_DT_BF16 ? 32 : 16;
+  L->nkb_d = L->d / L->KB;
+  L->nkb_F = L->F / L->KB;
+  L->nkb_Fs = L->Fs / L->KB;
+  L->pR = (L->E + 63) / 64 * 4;
+  L->pF = L->F / 16;
+  L->pD = L->d / 16;
+  L->pFs = L->Fs / 16;
+  L->W = (L->E + 63) / 64;
+  L->n_groups = L->d / 64;
+  int q = (512 + L->n_groups - 1) / L->n_groups;
+  L->dec_q = q < 1 ? 1 : (q > 32 ? 32 : q);
+  L->pre_grid = 1024;
+}
+
+struct Carve {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    size_t o = off;
+    off += align_up(bytes);
+    return o;
+  }
+};
+
+// ---- per-kernel event timing ----------------------------------------------
+struct PendingPair {
+  hipEvent_t a, b;
+  int slot;
+};
+bool g_timing = false;
+std::vector<hipEvent_t> g_pool;
+std::vector<PendingPair> g_pending;
+hipEvent_t g_open[deco_host::KS_COUNT];
+double g_total_ms[deco_host::KS_COUNT];
+int64_t g_count[deco_host::KS_COUNT];
+
+hipEvent_t get_event() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+void drain_pending() {
+  for (const PendingPair& p : g_pending) {
+    float ms = 0.f;
+    if (hipEventSynchronize(p.b) == hipSuccess && hipEventElapsedTime(&ms, p.a, p.b) == hipSuccess) {
+      g_total_ms[p.slot] += ms;
+      g_count[p.slot] += 1;
+    }
+    g_pool.push_back(p.a);
+    g_pool.push_back(p.b);
+  }
+  g_pending.clear();
+}
+
+}  // namespace
+
+namespace deco_host {
+
+const char* kernel_slot_name(int slot) {
+  switch (slot) {
+    case KS_PACK: return "load_pack";
+    case KS_DEC_UP: return "k_dec_up";
+    case KS_DEC_DOWN: return "k_dec_down";
+    case KS_PRE_ROUTER_SHARED: return "k_pre_router_shared";
+    case KS_PRE_DISPATCH: return "k_pre_dispatch";
+    case KS_PRE_EXPERT: return "k_pre_expert";
+    case KS_PRE_SHARED_DOWN: return "k_pre_shared_down";
+    default: return "?";
+  }
+}
+
+void timing_begin(hipStream_t s, int slot) {
+  if (!g_timing) return;
+  hipEvent_t e = get_event();
+  g_open[slot] = e;
+  if (e) (void)hipEventRecord(e, s);
+}
+
+void timing_end(hipStream_t s, int slot) {
+  if (!g_timing || !g_open[slot]) return;
+  hipEvent_t e = get_event();
+  if (!e) return;
+  (void)hipEventRecord(e, s);
+  g_pending.push_back(PendingPair{g_open[slot], e, slot});
+  g_open[slot] = nullptr;
+  if (g_pending.size() > 8192) drain_pending();
+}
+
+}  // namespace deco_host
+
+extern "C" {
+
+int deco_moe_check_config(const deco_moe_config* cfg) { return validate_cfg(cfg); }
+
+const char* deco_moe_status_string(int status) {
+  switch (status) {
+    case DECO_OK: return "ok";
+    case DECO_ERR_INVALID_ARG: return "invalid argument";
+    case DECO_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case DECO_ERR_OUT_OF_MEMORY: return "device out of memory";
+    case DECO_ERR_HIP: return "HIP runtime or launch error";
+    default: return "unknown status";
+  }
+}
+
+void deco_moe_free(deco_moe_layer* L) {
+  if (!L) return;
+  if (L->wmem) (void)hipFree(L->wmem);
+  if (L->ws) (void)hipFree(L->ws);
+  delete L;
+}
+
+int deco_moe_load_weights(const deco_moe_config* cfg, const void* W_r, const float* b_r,
+                          const float* lambda, const void* W_up, const void* W_down, const void* Ws_up,
+                          const void* Ws_down, void* stream, deco_moe_layer** out_layer) {
+  if (!out_layer) return DECO_ERR_INVALID_ARG;
+  *out_layer = nullptr;
+  int st = validate_cfg(cfg);
+  if (st != DECO_OK) return st;
+  if (!W_r || !b_r || !lambda || !W_up || !W_down || !Ws_up || !Ws_down) return DECO_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+
+  deco_moe_layer* L = new (std::nothrow) deco_moe_layer();
+  if (!L) return DECO_ERR_OUT_OF_MEMORY;
+  memset(L, 0, sizeof(*L));
+  L->cfg = *cfg;
+  derive(L);
+  if (hipGetDevice(&L->device) != hipSuccess) {
+    delete L;
+    return DECO_ERR_HIP;
+  }
+  const size_t KBy = 1024;
+  const int E = L->E;
+  // packed weights
+  Carve w;
+  size_t o_wr = w.take((size_t)L->pR * L->nkb_d * KBy);
+  L->up_stride = (size_t)L->pF * L->nkb_d * KBy;
+  L->dn_stride = (size_t)L->pD * L->nkb_F * KBy;
+  size_t o_up = w.take(L->up_stride * E);
+  size_t o_wbp = w.take((size_t)L->pF * L->nkb_d * KBy);
+  size_t o_dn = w.take(L->dn_stride * E);
+  size_t o_su = w.take((size_t)L->pFs * L->nkb_d * KBy);
+  size_t o_sd = w.take((size_t)L->pD * L->nkb_Fs * KBy);
+  size_t o_b = w.take(sizeof(float) * E);
+  size_t o_l = w.take(sizeof(float) * E);
+  size_t o_wb = w.take(sizeof(float) * (size_t)L->d * L->F);
+  L->wmem_bytes = w.off;
+  // workspace
+  const size_t Tcap = (size_t)(L->maxT < 16 ? 16 : L->maxT);
+  Carve k;
+  size_t o_z = k.take(sizeof(float) * Tcap * E);
+  size_t o_g = k.take(sizeof(float) * Tcap * E);
+  size_t o_m = k.take(sizeof(uint64_t) * Tcap * L->W);
+  size_t o_mb = k.take(sizeof(float) * Tcap * L->F);
+  size_t o_h = k.take(sizeof(float) * (size_t)E * 16 * L->F);
+  size_t o_af = k.take((size_t)E * L->nkb_F * KBy * (L->cfg.dtype == DECO_DT_BF16 ? 2 : 1));
+  size_t o_sf = k.take((size_t)L->nkb_Fs * KBy);
+  size_t o_ea = k.take(sizeof(int) * E);
+  size_t o_cu = k.take(sizeof(unsigned) * E);
+  size_t o_cd = k.take(sizeof(unsigned) * L->n_groups);
+  size_t o_pt = k.take(sizeof(float) * (size_t)L->dec_q * L->n_groups * 1024);
+  size_t o_to = k.take(sizeof(int) * (Tcap + 1));
+  size_t o_ec = k.take(sizeof(int) * E);
+  size_t o_lt = k.take(sizeof(int) * (size_t)E * Tcap);
+  size_t o_ls = k.take(sizeof(int) * (size_t)E * Tcap);
+  size_t o_sb = k.take((size_t)L->esz * Tcap * L->Fs);
+  size_t o_yb = k.take((size_t)L->esz * Tcap * E * L->d);
+  L->ws_bytes = k.off;
+
+  if (hipMalloc((void**)&L->wmem, L->wmem_bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    deco_moe_free(L);
+    return DECO_ERR_OUT_OF_MEMORY;
+  }
+  if (hipMalloc((void**)&L->ws, L->ws_bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    deco_moe_free(L);
+    return DECO_ERR_OUT_OF_MEMORY;
+  }
+  L->Wr_p = L->wmem + o_wr;
+  L->Wup_p = L->wmem + o_up;
+  L->Wbar_p = L->wmem + o_wbp;
+  L->Wdn_p = L->wmem + o_dn;
+  L->Wsu_p = L->wmem + o_su;
+  L->Wsd_p = L->wmem + o_sd;
+  L->b_r = (float*)(L->wmem + o_b);
+  L->lam = (float*)(L->wmem + o_l);
+  L->wbar = (float*)(L->wmem + o_wb);
+  L->z = (float*)(L->ws + o_z);
+  L->g = (float*)(L->ws + o_g);
+  L->mask = (uint64_t*)(L->ws + o_m);
+  L->mbuf = (float*)(L->ws + o_mb);
+  L->hbuf = (float*)(L->ws + o_h);
+  L->actf = L->ws + o_af;
+  L->sactf = L->ws + o_sf;
+  L->eact = (int*)(L->ws + o_ea);
+  L->cnt_up = (unsigned*)(L->ws + o_cu);
+  L->cnt_dn = (unsigned*)(L->ws + o_cd);
+  L->part = (float*)(L->ws + o_pt);
+  L->tok_off = (int*)(L->ws + o_to);
+  L->ecnt = (int*)(L->ws + o_ec);
+  L->list_tok = (int*)(L->ws + o_lt);
+  L->list_slot = (int*)(L->ws + o_ls);
+  L->sbuf = L->ws + o_sb;
+  L->ybuf = L->ws + o_yb;
+
+  hipError_t err = hipSuccess;
+  // counters, flags and activation fragments start at zero; the rest of the
+  // workspace is always written before it is read
+  size_t zero_end = o_to;
+  err = hipMemsetAsync(L->ws, 0, zero_end, s);
+  if (err == hipSuccess) err = hipMemcpyAsync(L->b_r, b_r, sizeof(float) * E, hipMemcpyDeviceToDevice, s);
+  if (err == hipSuccess) err = hipMemcpyAsync(L->lam, lambda, sizeof(float) * E, hipMemcpyDeviceToDevice, s);
+  if (err == hipSuccess) {
+    deco_host::timing_begin(s, deco_host::KS_PACK);
+    err = deco_host::launch_pack_all(L, W_r, W_up, W_down, Ws_up, Ws_down, s);
+    deco_host::timing_end(s, deco_host::KS_PACK);
+  }
+  if (err == hipSuccess) err = hipStreamSynchronize(s);
+  if (err != hipSuccess) {
+    (void)hipGetLastError();
+    deco_moe_free(L);
+    return DECO_ERR_HIP;
+  }
+  *out_layer = L;
+  return DECO_OK;
+}
+
+int deco_moe_forward_path(const deco_moe_layer* L, const void* x, int64_t T, void* out, void* stream,
+                          int path) {
+  if (!L || T < 0 || T > L->maxT) return DECO_ERR_INVALID_ARG;
+  if (path != DECO_PATH_AUTO && path != DECO_PATH_DECODE && path != DECO_PATH_PREFILL)
+    return DECO_ERR_INVALID_ARG;
+  if (T == 0) return DECO_OK;
+  if (!x || !out) return DECO_ERR_INVALID_ARG;
+  if (((uintptr_t)x % 16) != 0 || ((uintptr_t)out % 16) != 0) return DECO_ERR_INVALID_ARG;
+  const size_t bytes = (size_t)T * L->d * L->esz;
+  const char* xb = (const char*)x;
+  const char* ob = (const char*)out;
+  if (xb < ob + bytes && ob < xb + bytes) return DECO_ERR_INVALID_ARG;   // x and out overlap
+  if (path == DECO_PATH_AUTO) path = T <= DECO_DECODE_MAX_T ? DECO_PATH_DECODE : DECO_PATH_PREFILL;
+  if (path == DECO_PATH_DECODE && T > DECO_DECODE_MAX_T) return DECO_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t err = path == DECO_PATH_DECODE ? deco_host::launch_decode(L, x, (int)T, out, s)
+                                            : deco_host::launch_prefill(L, x, (int)T, out, s);
+  return err == hipSuccess ? DECO_OK : DECO_ERR_HIP;
+}
+
+int deco_moe_forward(const deco_moe_layer* L, const void* x, int64_t T, void* out, void* stream) {
+  return deco_moe_forward_path(L, x, T, out, stream, DECO_PATH_AUTO);
+}
+
+int deco_moe_copy_routing(const deco_moe_layer* L, int64_t T, uint64_t* mask, float* logits, void* stream) {
+  if (!L || T < 0 || T > L->maxT || !mask) return DECO_ERR_INVALID_ARG;
+  if (T == 0) return DECO_OK;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t err = deco_host::launch_copy_mask(L, (int)T, mask, s);
+  if (err == hipSuccess && logits)
+    err = hipMemcpyAsync(logits, L->z, sizeof(float) * (size_t)T * L->E, hipMemcpyDeviceToDevice, s);
+  return err == hipSuccess ? DECO_OK : DECO_ERR_HIP;
+}
+
+int deco_moe_copy_mean_up(const deco_moe_layer* L, float* wbar, void* stream) {
+  if (!L || !wbar) return DECO_ERR_INVALID_ARG;
+  hipError_t err = hipMemcpyAsync(wbar, L->wbar, sizeof(float) * (size_t)L->d * L->F, hipMemcpyDeviceToDevice,
+                                  (hipStream_t)stream);
+  return err == hipSuccess ? DECO_OK : DECO_ERR_HIP;
+}
+
+int deco_moe_timing_enable(int enable) {
+  g_timing = enable != 0;
+  return DECO_OK;
+}
+
+int deco_moe_timing_reset(void) {
+  drain_pending();
+  for (int i = 0; i < deco_host::KS_COUNT; ++i) {
+    g_total_ms[i] = 0.0;
+    g_count[i] = 0;
+  }
+  return DECO_OK;
+}
+
+int deco_moe_timing_read(int idx, const char** name, double* total_ms, int64_t* launches) {
+  if (idx < 0 || idx >= deco_host::KS_COUNT) return DECO_ERR_INVALID_ARG;
+  drain_pending();
+  if (name) *name = deco_host::kernel_slot_name(idx);
+  if (total_ms) *total_ms = g_total_ms[idx];
+  if (launches) *launches = g_count[idx];
+  return DECO_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,109 @@
+"""C-ABI library: loads, exports every symbol the header declares, and rejects
+bad arguments on the host before any HIP call.  CPU only (no compute calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_moe_relu_amd as dm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dm.LIB_PATH):
+        from sparse_moe_relu_amd.build import build_library
+        build_library(verbose=False)
+    return dm.load_library()
+
+
+def _declared_functions():
+    with open(os.path.join(ROOT, "include", "deco_moe.h")) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(deco_moe_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_binding_exports():
+    assert _declared_functions() == sorted(dm.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+        assert isinstance(getattr(lib, name), ctypes._CFuncPtr)
+
+
+def test_status_strings(lib):
+    for st in (dm.DECO_OK, dm.DECO_ERR_INVALID_ARG, dm.DECO_ERR_UNSUPPORTED, dm.DECO_ERR_OUT_OF_MEMORY,
+               dm.DECO_ERR_HIP):
+        assert dm.status_string(st) and dm.status_string(st) != "unknown status"
+    assert dm.status_string(12345) == "unknown status"
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(), dm.DECO_OK),
+    (dict(d=2048, E=56, F=128, Fs=1024), dm.DECO_OK),
+    (dict(d=4096, E=112, F=128, Fs=2048), dm.DECO_OK),
+    (dict(E=256), dm.DECO_OK),
+    (dict(F=256, Fs=32), dm.DECO_OK),
+    (dict(d=0), dm.DECO_ERR_INVALID_ARG),
+    (dict(E=0), dm.DECO_ERR_INVALID_ARG),
+    (dict(T=0), dm.DECO_ERR_INVALID_ARG),
+    (dict(eps=-1.0), dm.DECO_ERR_INVALID_ARG),
+    (dict(eps=float("nan")), dm.DECO_ERR_INVALID_ARG),
+    (dict(d=96), dm.DECO_ERR_UNSUPPORTED),
+    (dict(E=257), dm.DECO_ERR_UNSUPPORTED),
+    (dict(F=48), dm.DECO_ERR_UNSUPPORTED),
+    (dict(F=512), dm.DECO_ERR_UNSUPPORTED),
+    (dict(Fs=48), dm.DECO_ERR_UNSUPPORTED),
+    (dict(T=(1 << 20) + 1), dm.DECO_ERR_UNSUPPORTED),
+])
+def test_check_config(lib, kw, expect):
+    a = dict(d=64, E=8, F=32, Fs=64, T=16, dtype="f32", eps=1e-6)
+    a.update(kw)
+    cfg = dm.make_config(a["d"], a["E"], a["F"], a["Fs"], a["T"], a["dtype"], a["eps"])
+    assert dm.check_config(cfg) == expect
+
+
+def test_bad_dtype_is_unsupported(lib):
+    cfg = dm.make_config(64, 8, 32, 64, 16, "f32")
+    cfg.dtype = 7
+    assert dm.check_config(cfg) == dm.DECO_ERR_UNSUPPORTED
+    assert lib.deco_moe_check_config(None) == dm.DECO_ERR_INVALID_ARG
+
+
+def test_host_side_rejections_touch_no_device(lib):
+    cfg = dm.make_config(64, 8, 32, 64, 16, "f32")
+    h = ctypes.c_void_p(1234)
+    # null weight pointer: rejected before any HIP call, *out_layer cleared
+    st = lib.deco_moe_load_weights(ctypes.byref(cfg), None, None, None, None, None, None, None, None,
+                                   ctypes.byref(h))
+    assert st == dm.DECO_ERR_INVALID_ARG and not h.value
+    # invalid config is reported before the pointer checks
+    bad = dm.make_config(96, 8, 32, 64, 16, "f32")
+    assert lib.deco_moe_load_weights(ctypes.byref(bad), None, None, None, None, None, None, None, None,
+                                     ctypes.byref(h)) == dm.DECO_ERR_UNSUPPORTED
+    assert lib.deco_moe_load_weights(ctypes.byref(cfg), None, None, None, None, None, None, None, None,
+                                     None) == dm.DECO_ERR_INVALID_ARG
+    # null layer
+    assert lib.deco_moe_forward(None, None, 0, None, None) == dm.DECO_ERR_INVALID_ARG
+    assert lib.deco_moe_forward_path(None, None, 4, None, None, 1) == dm.DECO_ERR_INVALID_ARG
+    assert lib.deco_moe_copy_routing(None, 1, None, None, None) == dm.DECO_ERR_INVALID_ARG
+    assert lib.deco_moe_copy_mean_up(None, None, None) == dm.DECO_ERR_INVALID_ARG
+    lib.deco_moe_free(None)
+    assert lib.deco_moe_timing_read(-1, None, None, None) == dm.DECO_ERR_INVALID_ARG
+
+
+def test_product_path_has_no_oracle_dependency():
+    # the binding and the HIP sources never reference the oracle package
+    pkg = os.path.join(ROOT, "sparse_moe_relu_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".h", ".cpp")):
+                with open(os.path.join(dirpath, fn), encoding="utf-8") as f:
+                    src = f.read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", src, re.M), fn
+                assert "oracle/" not in src, fn
