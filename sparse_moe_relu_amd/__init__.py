@@ -15,7 +15,8 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libdeco_moe.so")
+# DECO_MOE_LIB selects another build of the library (e.g. other launch shapes)
+LIB_PATH = os.environ.get("DECO_MOE_LIB") or os.path.join(_PKG, "libdeco_moe.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "deco_moe.h")
 
 DECO_OK = 0

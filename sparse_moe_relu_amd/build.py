@@ -30,9 +30,9 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, build_dir: str, extra: list) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(line for line in (r.stdout + r.stderr).splitlines()
                      if "packed-fp32-ops" not in line and line.strip())
@@ -43,23 +43,32 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build_library(verbose: bool = True) -> str:
+def build_library(verbose: bool = True, out: str = LIB, defines: list | None = None) -> str:
+    """Compile every source and link `out`.  `defines` (NAME=VALUE strings)
+    override the kernels' compile-time launch parameters."""
     if not os.path.exists(HIPCC):
         raise RuntimeError(f"hipcc not found at {HIPCC}")
-    os.makedirs(BUILD_DIR, exist_ok=True)
+    extra = [f"-D{d}" for d in (defines or [])]
+    build_dir = BUILD_DIR if out == LIB else out + ".build"
+    os.makedirs(build_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda src: _compile(src, build_dir, extra), SOURCES))
+    tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
-    shutil.rmtree(BUILD_DIR, ignore_errors=True)
+    os.replace(tmp, out)
+    shutil.rmtree(build_dir, ignore_errors=True)
     if verbose:
-        print(f"[build] wrote {LIB}")
-    return LIB
+        print(f"[build] wrote {out}")
+    return out
 
 
 if __name__ == "__main__":
-    build_library()
+    import argparse
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--out", default=LIB)
+    ap.add_argument("-D", dest="defines", action="append", default=[])
+    a = ap.parse_args()
+    build_library(out=a.out, defines=a.defines)

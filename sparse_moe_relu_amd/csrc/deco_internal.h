@@ -1,11 +1,12 @@
 // deco_internal.h - layer object, workspace layout and kernel launchers (host side).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/deco_moe.h"
+#include "deco_moe.h"
 
 struct deco_moe_layer {
   deco_moe_config cfg;
@@ -61,9 +62,19 @@ struct deco_moe_layer {
 
 namespace deco_host {
 
-struct Timer;  // per-kernel event timing (host.cpp)
-void timing_begin(hipStream_t s, int slot);
-void timing_end(hipStream_t s, int slot);
+// Per-kernel timing: when enabled, returns a start/stop event pair that the
+// launch itself records (hipExtLaunchKernel stamps the kernel's own dispatch,
+// so the elapsed time matches a profiler's kernel duration); else nulls.
+void timing_events(int slot, hipEvent_t* start, hipEvent_t* stop);
+
+template <typename... KArgs, typename... Args>
+inline hipError_t launch(int slot, void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t s,
+                         Args... args) {
+  hipEvent_t a = nullptr, b = nullptr;
+  timing_events(slot, &a, &b);
+  hipExtLaunchKernelGGL(kernel, grid, block, 0, s, a, b, 0, static_cast<KArgs>(args)...);
+  return hipGetLastError();
+}
 
 // kernel slots for timing
 enum {

@@ -62,49 +62,81 @@ struct DecArgs {
   float* part;
 };
 
-constexpr int DEC_NW = 8;   // waves per workgroup
-constexpr int DEC_NP = 2;   // 16-column panels per up-projection workgroup
-constexpr int DEC_CH = 8;   // k-blocks held in registers per wave at a time
+#ifndef DECO_DEC_NW
+#define DECO_DEC_NW 8
+#endif
+#ifndef DECO_DEC_NP
+#define DECO_DEC_NP 2
+#endif
+#ifndef DECO_DEC_CH
+#define DECO_DEC_CH 8
+#endif
+constexpr int DEC_NW = DECO_DEC_NW;   // waves per workgroup
+constexpr int DEC_NP = DECO_DEC_NP;   // 16-column panels per up-projection workgroup
+constexpr int DEC_CH = DECO_DEC_CH;   // k-blocks held in registers per wave at a time
+constexpr int DEC_QMAX = 32;          // largest K-split of the down kernel (host clamps dec_q)
 
-// NormSiLU of the 16 (padded) token rows of expert e, times the gate, stored as
-// down-projection operand fragments (hi, then lo for bf16).  Called by the one
-// workgroup that saw the expert's arrival count reach its target.
+// NormSiLU of the 16 (padded) token rows of each expert in `list`, times the
+// gate, stored as down-projection operand fragments (hi, then lo for bf16).
+// Called by the workgroup that saw the experts' arrival counts reach their
+// target.  Rows are processed RB at a time per wave so their loads overlap.
 template <class DT, int NW>
-__device__ void dec_finalize(const DecArgs& a, int e) {
+__device__ void dec_finalize(const DecArgs& a, const int* list, int n) {
   using elem = typename DT::elem;
+  constexpr int RB = 4;
+  constexpr int NPART = DT::SPLIT ? 2 : 1;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const float invF = 1.0f / (float)a.F;
-  constexpr int NPART = DT::SPLIT ? 2 : 1;
-  char* act_e = a.actf + (size_t)e * a.nkb_F * NPART * FRAG_BYTES;
-  for (int t = w; t < 16; t += NW) {
-    // inactive pairs have g == 0; rows past T are padding
-    const float gate = t < a.T ? a.g[(size_t)t * a.E + e] : 0.f;
-    float hv[4];
-    float ss = 0.f;
+  const int nrows = n * 16;
+  const __amdgpu_buffer_rsrc_t rg = dev_rsrc(a.g), rh = dev_rsrc(a.hbuf), rm = dev_rsrc(a.mbuf);
+  for (int r0 = w * RB; r0 < nrows; r0 += NW * RB) {
+    float hv[RB][4], mv[RB][4], gate[RB];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int f = l + 64 * q;
-      hv[q] = f < a.F ? a.hbuf[((size_t)e * 16 + t) * a.F + f] - a.mbuf[(size_t)t * a.F + f] : 0.f;
-      ss += hv[q] * hv[q];
+    for (int rr = 0; rr < RB; ++rr) {
+      const int r = r0 + rr;
+      const int e = r < nrows ? list[r >> 4] : 0, t = r & 15;
+      const bool ok = r < nrows;
+      // inactive pairs have g == 0; rows past T are padding
+      gate[rr] = (ok && t < a.T) ? ld_dev_buf(rg, 4u * (unsigned)(t * a.E + e)) : 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int f = l + 64 * q;
+        const bool okf = ok && f < a.F;
+        hv[rr][q] = okf ? ld_dev_buf(rh, 4u * (unsigned)((e * 16 + t) * a.F + f)) : 0.f;
+        mv[rr][q] = okf ? ld_dev_buf(rm, 4u * (unsigned)(t * a.F + f)) : 0.f;
+      }
     }
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
-    const float inv_r = 1.0f / sqrtf(ss * invF + a.eps);
+    for (int rr = 0; rr < RB; ++rr)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int f = l + 64 * q;
-      if (f < a.F) {
-        const float v = gate != 0.f ? silu_f(hv[q] * inv_r) * gate : 0.f;
-        const int kb = f / DT::KB;
-        char* frag = act_e + (size_t)kb * NPART * FRAG_BYTES + frag_elem_off<DT>(t, f % DT::KB);
-        elem hi, lo;
-        split_hi_lo<DT>(v, hi, lo);
-        *reinterpret_cast<elem*>(frag) = hi;
-        if (DT::SPLIT) *reinterpret_cast<elem*>(frag + FRAG_BYTES) = lo;
+      for (int q = 0; q < 4; ++q) hv[rr][q] -= mv[rr][q];
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) {
+      const int r = r0 + rr;
+      if (r >= nrows) break;
+      const int e = list[r >> 4], t = r & 15;
+      float ss = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) ss += hv[rr][q] * hv[rr][q];
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+      const float inv_r = 1.0f / sqrtf(ss * invF + a.eps);
+      char* act_e = a.actf + (size_t)e * a.nkb_F * NPART * FRAG_BYTES;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int f = l + 64 * q;
+        if (f < a.F) {
+          const float v = gate[rr] != 0.f ? silu_f(hv[rr][q] * inv_r) * gate[rr] : 0.f;
+          char* frag = act_e + (size_t)(f / DT::KB) * NPART * FRAG_BYTES + frag_elem_off<DT>(t, f % DT::KB);
+          elem hi, lo;
+          split_hi_lo<DT>(v, hi, lo);
+          *reinterpret_cast<elem*>(frag) = hi;
+          if (DT::SPLIT) *reinterpret_cast<elem*>(frag + FRAG_BYTES) = lo;
+        }
       }
     }
   }
-  if (tid == 0) a.eact[e] = 1;
+  for (int k = tid; k < n; k += NW * 64) a.eact[list[k]] = 1;
 }
 
 template <class DT, int NW, int NP>
@@ -113,22 +145,22 @@ __global__ void __launch_bounds__(NW * 64) k_dec_up(DecArgs a) {
   constexpr int CH = DEC_CH;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, c = l & 15;
   const int wg_per_e = a.pF / NP;        // workgroups per routed expert
-  const int n_routed = a.E * wg_per_e;
   const int n_wbar = a.pF / NP;          // workgroups of the mean term
   const unsigned target = (unsigned)(wg_per_e + n_wbar);
+  // grid order: mean-term slices, shared-expert slices, then routed slices
+  // (the first two need no router result, so they stream from the start)
+  const int n_shared = a.pFs / NP;
   const int bid = blockIdx.x;
-  const int kind = bid < n_routed ? 0 : (bid < n_routed + n_wbar ? 1 : 2);   // routed / mean / shared
-  const int e = kind == 0 ? bid / wg_per_e : 0;
-  const int p0 = kind == 0 ? (bid % wg_per_e) * NP
-               : (kind == 1 ? (bid - n_routed) * NP : (bid - n_routed - n_wbar) * NP);
+  const int kind = bid < n_wbar ? 1 : (bid < n_wbar + n_shared ? 2 : 0);   // routed / mean / shared
+  const int rb = bid - n_wbar - n_shared;
+  const int e = kind == 0 ? rb / wg_per_e : 0;
+  const int p0 = kind == 0 ? (rb % wg_per_e) * NP : (kind == 1 ? bid * NP : (bid - n_wbar) * NP);
   const int nkb = a.nkb_d;
   const int kb_lo = (w * nkb) / NW, kb_hi = ((w + 1) * nkb) / NW;
   const elem* xrow = (const elem*)a.x + (size_t)c * a.d;
   const bool row_ok = c < a.T;
 
   __shared__ float s_zred[NW][16];
-  __shared__ float s_z[16];
-  __shared__ int s_any;
   __shared__ int s_last;
   __shared__ int s_nfin;
   __shared__ int s_fin[256];
@@ -138,48 +170,45 @@ __global__ void __launch_bounds__(NW * 64) k_dec_up(DecArgs a) {
   if (kind == 0) {
     // router logits of expert e for the 16 (padded) token rows
     const float lam_e = a.lam[e];
+    const float b_e = a.b_r[e];
     float zp = 0.f;
     const char* wr = a.Wr_p + frag_off(e >> 4, 0, nkb) + (size_t)((e & 15) + 16 * g) * 16;
     for (int kb0 = kb_lo; kb0 < kb_hi; kb0 += CH) {
+      i32x4_t wv[CH];
 #pragma unroll
       for (int u = 0; u < CH; ++u) {
         const int kb = kb0 + u;
         xf[u] = (kb < kb_hi && row_ok) ? load_row_frag<DT>(xrow, kb, g) : zero16();
+        wv[u] = kb < kb_hi ? ld16(wr + (size_t)kb * FRAG_BYTES) : zero16();
       }
 #pragma unroll
       for (int u = 0; u < CH; ++u) {
-        const int kb = kb0 + u;
-        if (kb < kb_hi) {
-          const i32x4_t wv = ld16(wr + (size_t)kb * FRAG_BYTES);
 #pragma unroll
-          for (int j = 0; j < DT::EPL; ++j) zp += DT::lane_elem(xf[u], j) * DT::lane_elem(wv, j);
-        }
+        for (int j = 0; j < DT::EPL; ++j) zp += DT::lane_elem(xf[u], j) * DT::lane_elem(wv[u], j);
       }
     }
     zp += __shfl_xor(zp, 16);
     zp += __shfl_xor(zp, 32);
     if (g == 0) s_zred[w][c] = zp;
     __syncthreads();
-    if (tid < 16) {
+    // every thread forms the T logits itself (same order everywhere), so the
+    // activity decision needs no further barrier
+    bool any = false;
+    float z_mine = 0.f;
+    for (int t = 0; t < a.T; ++t) {
       float zz = 0.f;
 #pragma unroll
-      for (int ww = 0; ww < NW; ++ww) zz += s_zred[ww][tid];
-      s_z[tid] = zz + a.b_r[e];
+      for (int ww = 0; ww < NW; ++ww) zz += s_zred[ww][t];
+      zz += b_e;
+      any |= zz > 0.f && lam_e != 0.f;
+      if (t == tid) z_mine = zz;
     }
-    __syncthreads();
-    if (tid == 0) {
-      int any = 0;
-      for (int t = 0; t < a.T; ++t) any |= (s_z[t] > 0.f && lam_e != 0.f) ? 1 : 0;
-      s_any = any;
-    }
-    __syncthreads();
     if (p0 == 0 && tid < a.T) {
-      const float zz = s_z[tid];
-      const bool act = zz > 0.f && lam_e != 0.f;
-      a.z[(size_t)tid * a.E + e] = zz;
-      a.g[(size_t)tid * a.E + e] = act ? lam_e * zz : 0.f;
+      const bool act = z_mine > 0.f && lam_e != 0.f;
+      a.z[(size_t)tid * a.E + e] = z_mine;
+      st_dev(&a.g[(size_t)tid * a.E + e], act ? lam_e * z_mine : 0.f);
     }
-    if (!s_any) {
+    if (!any) {
       if (p0 == 0 && tid == 0) a.eact[e] = 0;
       return;  // inactive expert: none of its weights are read
     }
@@ -225,9 +254,9 @@ __global__ void __launch_bounds__(NW * 64) k_dec_up(DecArgs a) {
     for (int ww = 0; ww < NW; ++ww) v += s_red[ww][p][ll][i];
     const int row = 4 * (ll >> 4) + i, col = (p0 + p) * 16 + (ll & 15);
     if (kind == 0) {
-      a.hbuf[((size_t)e * 16 + row) * a.F + col] = v;
+      st_dev(&a.hbuf[((size_t)e * 16 + row) * a.F + col], v);
     } else if (kind == 1) {
-      a.mbuf[(size_t)row * a.F + col] = v;
+      st_dev(&a.mbuf[(size_t)row * a.F + col], v);
     } else {
       // shared expert: plain SiLU, stored as down-projection operand fragments
       *reinterpret_cast<elem*>(a.sactf + frag_elem_off<DT>(row, col)) = DT::from_f32(silu_f(v));
@@ -237,25 +266,25 @@ __global__ void __launch_bounds__(NW * 64) k_dec_up(DecArgs a) {
 
   // arrival counting: each expert finishes once its own slices and all the
   // mean-term slices are written; that last workgroup applies NormSiLU
-  __threadfence();
+  wait_all_mem();
   __syncthreads();
   if (kind == 0) {
-    if (tid == 0) s_last = (atomicAdd(&a.cnt_up[e], 1u) == target - 1u) ? 1 : 0;
+    if (tid == 0) {
+      s_last = (arrive(&a.cnt_up[e]) == target - 1u) ? 1 : 0;
+      s_fin[0] = e;
+    }
     __syncthreads();
     if (!s_last) return;
-    __threadfence();
-    dec_finalize<DT, NW>(a, e);
+    dec_finalize<DT, NW>(a, s_fin, 1);
   } else {
     if (tid == 0) s_nfin = 0;
     __syncthreads();
     for (int ee = tid; ee < a.E; ee += NW * 64) {
-      if (atomicAdd(&a.cnt_up[ee], 1u) == target - 1u) s_fin[atomicAdd(&s_nfin, 1)] = ee;
+      if (arrive(&a.cnt_up[ee]) == target - 1u) s_fin[atomicAdd(&s_nfin, 1)] = ee;
     }
     __syncthreads();
     const int nfin = s_nfin;
-    if (nfin == 0) return;
-    __threadfence();
-    for (int k = 0; k < nfin; ++k) dec_finalize<DT, NW>(a, s_fin[k]);
+    if (nfin > 0) dec_finalize<DT, NW>(a, s_fin, nfin);
   }
 }
 
@@ -268,7 +297,7 @@ __global__ void __launch_bounds__(NW * 64) k_dec_down(DecArgs a) {
   constexpr int NPART = DT::SPLIT ? 2 : 1;
   // the up kernel has completed: clear its per-expert arrival counters
   if (blockIdx.x == 0)
-    for (int e = tid; e < a.E; e += NW * 64) a.cnt_up[e] = 0u;
+    for (int e = tid; e < a.E; e += NW * 64) st_dev_u32(&a.cnt_up[e], 0u);
 
   __shared__ int s_ulist[256];
   __shared__ int s_wcnt[4];
@@ -357,22 +386,27 @@ __global__ void __launch_bounds__(NW * 64) k_dec_down(DecArgs a) {
 #pragma unroll
     for (int ww = 0; ww < NW; ++ww) v += s_red[ww][p][ll][i];
     const int row = 4 * (ll >> 4) + i, col = p * 16 + (ll & 15);
-    mypart[row * 64 + col] = v;
+    st_dev(&mypart[row * 64 + col], v);
   }
-  __threadfence();
+  wait_all_mem();
   __syncthreads();
-  if (tid == 0) s_last = (atomicAdd(&a.cnt_dn[grp], 1u) == (unsigned)(a.Q - 1)) ? 1 : 0;
+  if (tid == 0) s_last = (arrive(&a.cnt_dn[grp]) == (unsigned)(a.Q - 1)) ? 1 : 0;
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
   elem* out = (elem*)a.out;
+  const __amdgpu_buffer_rsrc_t rp = dev_rsrc(a.part);
   for (int idx = tid; idx < a.T * 64; idx += NW * 64) {
     const int row = idx >> 6, col = idx & 63;
+    float pv[DEC_QMAX];
+#pragma unroll
+    for (int qq = 0; qq < DEC_QMAX; ++qq)
+      pv[qq] = qq < a.Q ? ld_dev_buf(rp, 4u * (unsigned)(((qq * a.n_groups + grp) << 10) + row * 64 + col)) : 0.f;
     float v = 0.f;
-    for (int qq = 0; qq < a.Q; ++qq) v += a.part[((size_t)qq * a.n_groups + grp) * 1024 + row * 64 + col];
+#pragma unroll
+    for (int qq = 0; qq < DEC_QMAX; ++qq) v += pv[qq];   // fixed order: deterministic
     out[(size_t)row * a.d + grp * 64 + col] = DT::from_f32(v);
   }
-  if (tid == 0) a.cnt_dn[grp] = 0u;
+  if (tid == 0) st_dev_u32(&a.cnt_dn[grp], 0u);
 }
 
 template <class DT>
@@ -414,13 +448,12 @@ hipError_t decode(const deco_moe_layer* L, const void* x, int T, void* out, hipS
   a.cnt_dn = L->cnt_dn;
   a.part = L->part;
   const unsigned grid_up = (unsigned)((L->E + 1) * (L->pF / DEC_NP) + L->pFs / DEC_NP);
-  deco_host::timing_begin(s, deco_host::KS_DEC_UP);
-  k_dec_up<DT, DEC_NW, DEC_NP><<<grid_up, DEC_NW * 64, 0, s>>>(a);
-  deco_host::timing_end(s, deco_host::KS_DEC_UP);
+  hipError_t err = deco_host::launch(deco_host::KS_DEC_UP, k_dec_up<DT, DEC_NW, DEC_NP>, dim3(grid_up),
+                                     dim3(DEC_NW * 64), s, a);
+  if (err != hipSuccess) return err;
   const unsigned grid_dn = (unsigned)(L->n_groups * L->dec_q);
-  deco_host::timing_begin(s, deco_host::KS_DEC_DOWN);
-  k_dec_down<DT, DEC_NW><<<grid_dn, DEC_NW * 64, 0, s>>>(a);
-  deco_host::timing_end(s, deco_host::KS_DEC_DOWN);
+  err = deco_host::launch(deco_host::KS_DEC_DOWN, k_dec_down<DT, DEC_NW>, dim3(grid_dn), dim3(DEC_NW * 64), s, a);
+  if (err != hipSuccess) return err;
   return hipGetLastError();
 }
 

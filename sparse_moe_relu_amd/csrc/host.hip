@@ -47,7 +47,10 @@ void derive(deco_moe_layer* L) {
   L->pFs = L->Fs / 16;
   L->W = (L->E + 63) / 64;
   L->n_groups = L->d / 64;
-  int q = (512 + L->n_groups - 1) / L->n_groups;
+#ifndef DECO_DEC_DOWN_WGS
+#define DECO_DEC_DOWN_WGS 512
+#endif
+  int q = (DECO_DEC_DOWN_WGS + L->n_groups - 1) / L->n_groups;
   L->dec_q = q < 1 ? 1 : (q > 32 ? 32 : q);
   L->pre_grid = 1024;
 }
@@ -69,7 +72,6 @@ struct PendingPair {
 bool g_timing = false;
 std::vector<hipEvent_t> g_pool;
 std::vector<PendingPair> g_pending;
-hipEvent_t g_open[deco_host::KS_COUNT];
 double g_total_ms[deco_host::KS_COUNT];
 int64_t g_count[deco_host::KS_COUNT];
 
@@ -114,20 +116,18 @@ const char* kernel_slot_name(int slot) {
   }
 }
 
-void timing_begin(hipStream_t s, int slot) {
+void timing_events(int slot, hipEvent_t* start, hipEvent_t* stop) {
+  *start = *stop = nullptr;
   if (!g_timing) return;
-  hipEvent_t e = get_event();
-  g_open[slot] = e;
-  if (e) (void)hipEventRecord(e, s);
-}
-
-void timing_end(hipStream_t s, int slot) {
-  if (!g_timing || !g_open[slot]) return;
-  hipEvent_t e = get_event();
-  if (!e) return;
-  (void)hipEventRecord(e, s);
-  g_pending.push_back(PendingPair{g_open[slot], e, slot});
-  g_open[slot] = nullptr;
+  hipEvent_t a = get_event();
+  hipEvent_t b = a ? get_event() : nullptr;
+  if (!a || !b) {
+    if (a) g_pool.push_back(a);
+    return;
+  }
+  *start = a;
+  *stop = b;
+  g_pending.push_back(PendingPair{a, b, slot});
   if (g_pending.size() > 8192) drain_pending();
 }
 
@@ -256,11 +256,7 @@ int deco_moe_load_weights(const deco_moe_config* cfg, const void* W_r, const flo
   err = hipMemsetAsync(L->ws, 0, zero_end, s);
   if (err == hipSuccess) err = hipMemcpyAsync(L->b_r, b_r, sizeof(float) * E, hipMemcpyDeviceToDevice, s);
   if (err == hipSuccess) err = hipMemcpyAsync(L->lam, lambda, sizeof(float) * E, hipMemcpyDeviceToDevice, s);
-  if (err == hipSuccess) {
-    deco_host::timing_begin(s, deco_host::KS_PACK);
-    err = deco_host::launch_pack_all(L, W_r, W_up, W_down, Ws_up, Ws_down, s);
-    deco_host::timing_end(s, deco_host::KS_PACK);
-  }
+  if (err == hipSuccess) err = deco_host::launch_pack_all(L, W_r, W_up, W_down, Ws_up, Ws_down, s);
   if (err == hipSuccess) err = hipStreamSynchronize(s);
   if (err != hipSuccess) {
     (void)hipGetLastError();

@@ -468,23 +468,20 @@ hipError_t prefill(const deco_moe_layer* L, const void* x, int T, void* out, hip
   a.ybuf = L->ybuf;
   const unsigned mtiles = (unsigned)((T + BM - 1) / BM);
   const unsigned ntiles = (unsigned)(L->pR / 4 + (L->pF + 3) / 4 + (L->pFs + 3) / 4);
-  deco_host::timing_begin(s, deco_host::KS_PRE_ROUTER_SHARED);
-  k_pre_router_shared<DT><<<dim3(mtiles, ntiles), 256, 0, s>>>(a);
-  deco_host::timing_end(s, deco_host::KS_PRE_ROUTER_SHARED);
-  deco_host::timing_begin(s, deco_host::KS_PRE_DISPATCH);
-  k_pre_dispatch<<<(unsigned)L->E, 256, 0, s>>>(a);
-  deco_host::timing_end(s, deco_host::KS_PRE_DISPATCH);
-  deco_host::timing_begin(s, deco_host::KS_PRE_EXPERT);
-  switch (L->pF) {
-    case 2: k_pre_expert<DT, 2><<<(unsigned)L->pre_grid, 256, 0, s>>>(a); break;
-    case 4: k_pre_expert<DT, 4><<<(unsigned)L->pre_grid, 256, 0, s>>>(a); break;
-    case 8: k_pre_expert<DT, 8><<<(unsigned)L->pre_grid, 256, 0, s>>>(a); break;
-    default: k_pre_expert<DT, 16><<<(unsigned)L->pre_grid, 256, 0, s>>>(a); break;
+  using deco_host::launch;
+  hipError_t err = launch(deco_host::KS_PRE_ROUTER_SHARED, k_pre_router_shared<DT>, dim3(mtiles, ntiles),
+                          dim3(256), s, a);
+  if (err == hipSuccess) err = launch(deco_host::KS_PRE_DISPATCH, k_pre_dispatch, dim3(L->E), dim3(256), s, a);
+  if (err == hipSuccess) {
+    void (*kx)(PreArgs) = L->pF == 2 ? k_pre_expert<DT, 2>
+                        : L->pF == 4 ? k_pre_expert<DT, 4>
+                        : L->pF == 8 ? k_pre_expert<DT, 8> : k_pre_expert<DT, 16>;
+    err = launch(deco_host::KS_PRE_EXPERT, kx, dim3(L->pre_grid), dim3(256), s, a);
   }
-  deco_host::timing_end(s, deco_host::KS_PRE_EXPERT);
-  deco_host::timing_begin(s, deco_host::KS_PRE_SHARED_DOWN);
-  k_pre_shared_down<DT><<<dim3(mtiles, (unsigned)(L->pD / 4)), 256, 0, s>>>(a);
-  deco_host::timing_end(s, deco_host::KS_PRE_SHARED_DOWN);
+  if (err == hipSuccess)
+    err = launch(deco_host::KS_PRE_SHARED_DOWN, k_pre_shared_down<DT>, dim3(mtiles, (unsigned)(L->pD / 4)),
+                 dim3(256), s, a);
+  if (err != hipSuccess) return err;
   return hipGetLastError();
 }
 
