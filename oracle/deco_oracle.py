@@ -15,7 +15,7 @@ the DECO paper, so the steps below follow its prose):
             (core design of DECO): the router part, and the expert-design part
             on NormSiLU and non-gated experts.
 
-Readings taken where the text is silent (each is listed in the design doc):
+Readings taken where the text is silent:
   * router = linear projection with a bias b_r, then ReLU, then a learned
     per-expert scale lambda_e applied after the ReLU; no softmax / unit-sum;
   * an expert is active for a token iff its logit is strictly positive
@@ -29,9 +29,10 @@ Readings taken where the text is silent (each is listed in the design doc):
   * shared expert: non-gated MLP with plain SiLU, weight 1, no lambda;
   * no residual: the result is the FFN sublayer output only.
 
-Parity against the pages' own numbers is unpinned: the pages print no worked
-example of the layer.  Every function here is pinned by the invariants,
-closed forms, brute force and library cross-checks in tests/test_oracle_pins.py.
+The pages print no worked numeric example of the layer, so no value here is
+compared with a printed one; every function is pinned instead by invariants,
+closed forms, dense brute force and library cross-checks
+(tests/test_oracle_pins.py).
 """
 from __future__ import annotations
 
