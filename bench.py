@@ -75,9 +75,10 @@ def traffic_from_profiles(kernel: str, workload: str):
 
 # workload accounting -----------------------------------------------------------
 def decode_bytes(L, n_union: int, T: int) -> dict:
-    """Algorithmic HBM bytes per launch, per kernel: weights the method must
-    read (router, the active experts' two matrices, the shared expert) plus
-    x in and out.  The mean-term matrix is not counted (it could be folded)."""
+    """Algorithmic HBM bytes per launch, per decode kernel: the weights the
+    method must read (router, bias and scale, the two matrices of each expert
+    touched by the batch, the shared expert) plus x in and out.  The
+    mean-term matrix is not counted (it could be folded into the experts)."""
     s = 2 if L.dtype == "bf16" else 4
     up = L.d * L.E * s + 8 * L.E + n_union * L.d * L.F * s + L.d * L.Fs * s + T * L.d * s
     down = n_union * L.F * L.d * s + L.Fs * L.d * s + T * L.d * s

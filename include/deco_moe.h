@@ -52,7 +52,7 @@ typedef enum {
 typedef enum { DECO_DT_BF16 = 0, DECO_DT_F32 = 1 } deco_dtype;
 
 typedef enum {
-  DECO_PATH_AUTO = 0,     /* decode path for T <= DECO_DECODE_MAX_T, else prefill */
+  DECO_PATH_AUTO = 0,     /* decode path for T <= DECO_DECODE_MAX_T, else prefill   */
   DECO_PATH_DECODE = 1,   /* weight-streaming path; requires T <= DECO_DECODE_MAX_T */
   DECO_PATH_PREFILL = 2   /* bucketed grouped-MFMA path; any T                      */
 } deco_path;
@@ -85,8 +85,10 @@ int deco_moe_check_config(const deco_moe_config* cfg);
  *   Ws_down [Fs, d]     dtype     shared-expert down-projection
  * Computes Wbar = mean over all E routed experts of W_up (the NormSiLU mean
  * term is precomputable because inference weights are fixed: qidianchuan.cn
- * write-up, section 二, expert design) in fp32 and folds it into the packed
- * up-projections (W_up[e] - Wbar).  Runs on `stream` and synchronizes it
+ * write-up, section 二, expert design) in fp32 and packs it, in the layer
+ * dtype, next to the experts' weights; the forward pass forms x.Wbar once per
+ * token and subtracts it from every expert's up-projection.  Runs on
+ * `stream` and synchronizes it
  * before returning, so the sources may be freed afterwards.  On success
  * *out_layer receives the new layer; on failure it is set to NULL and nothing
  * stays allocated. */
@@ -119,6 +121,13 @@ int deco_moe_copy_routing(const deco_moe_layer* L, int64_t T, uint64_t* mask, fl
 
 /* Copy the inter-expert mean Wbar [d, F] (float32, device) built at load. */
 int deco_moe_copy_mean_up(const deco_moe_layer* L, float* wbar, void* stream);
+
+/* Health flags of L's device-side work, read synchronously (waits for all
+ * work on the device) and cleared by the read.  Bit 0: an in-kernel
+ * hand-off between workgroups timed out (the output of that call is not
+ * valid).  The current kernels never wait on other workgroups, so the flags
+ * stay 0.  Returns DECO_ERR_INVALID_ARG on NULL arguments. */
+int deco_moe_read_error_flags(const deco_moe_layer* L, uint32_t* flags);
 
 /* Release every device buffer of L (NULL is a no-op).  The caller must make
  * sure no work using L is still pending on any stream. */

@@ -33,7 +33,7 @@ DECODE_MAX_T = 16
 
 EXPORTS = ("deco_moe_check_config", "deco_moe_load_weights", "deco_moe_forward",
            "deco_moe_forward_path", "deco_moe_copy_routing", "deco_moe_copy_mean_up",
-           "deco_moe_free", "deco_moe_status_string", "deco_moe_timing_enable",
+           "deco_moe_free", "deco_moe_status_string", "deco_moe_read_error_flags", "deco_moe_timing_enable",
            "deco_moe_timing_reset", "deco_moe_timing_read")
 
 
@@ -76,6 +76,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.deco_moe_copy_routing.restype = i32
     lib.deco_moe_copy_mean_up.argtypes = [vp, vp, vp]
     lib.deco_moe_copy_mean_up.restype = i32
+    lib.deco_moe_read_error_flags.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32)]
+    lib.deco_moe_read_error_flags.restype = i32
     lib.deco_moe_free.argtypes = [vp]
     lib.deco_moe_free.restype = None
     lib.deco_moe_status_string.argtypes = [i32]
@@ -198,6 +200,14 @@ class Layer:
         if st != DECO_OK:
             raise DecoError(st, "deco_moe_copy_mean_up")
         return wbar
+
+    def error_flags(self) -> int:
+        """Device-side health flags (bit 0: a decode wait timed out); clears them."""
+        f = ctypes.c_uint32()
+        st = load_library().deco_moe_read_error_flags(self.handle, ctypes.byref(f))
+        if st != DECO_OK:
+            raise DecoError(st, "deco_moe_read_error_flags")
+        return int(f.value)
 
     def free(self):
         if getattr(self, "_h", None) is not None:

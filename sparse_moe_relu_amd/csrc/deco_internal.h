@@ -19,7 +19,8 @@ struct deco_moe_layer {
   int pF, pD, pFs;         // 16-column panels of F, d, Fs
   int W;                   // mask words per token = ceil(E/64)
   int n_groups;            // d / 64 output column groups (decode down kernel)
-  int dec_q;               // K-split factor of the decode down kernel
+  int dec_q;               // reduction split of the decode down role
+  int dec_ok;              // the decode path is available for this layer
   int pre_grid;            // persistent grid of the prefill expert kernel
 
   // packed weights (one allocation)
@@ -47,8 +48,9 @@ struct deco_moe_layer {
   float* hbuf;             // [E][16][F]   raw up-projection rows
   char* actf;              // [E][nkb_F][hi, lo] frags  gated NormSiLU output (A operand)
   char* sactf;             // [nkb_Fs] frags      shared SiLU output
-  int* eact;               // [E] expert touched by the batch
-  unsigned* cnt_up;        // [E] arrival counters (reset by the down kernel)
+  unsigned* eact;          // [E] expert touched by the batch
+  unsigned* cnt_up;        // [E] arrival counters (cleared by the down kernel)
+  unsigned* dec_err;       // [1] device-side error flags
   unsigned* cnt_dn;        // [n_groups] arrival counters
   float* part;             // [dec_q][n_groups][16][64] partial outputs
   // prefill
@@ -92,6 +94,7 @@ const char* kernel_slot_name(int slot);
 // launchers (return hipSuccess or the launch error)
 hipError_t launch_pack_all(deco_moe_layer* L, const void* W_r, const void* W_up, const void* W_down,
                            const void* Ws_up, const void* Ws_down, hipStream_t s);
+hipError_t plan_decode(deco_moe_layer* L);   // decode launch shape (load time)
 hipError_t launch_decode(const deco_moe_layer* L, const void* x, int T, void* out, hipStream_t s);
 hipError_t launch_prefill(const deco_moe_layer* L, const void* x, int T, void* out, hipStream_t s);
 hipError_t launch_copy_mask(const deco_moe_layer* L, int T, uint64_t* mask, hipStream_t s);

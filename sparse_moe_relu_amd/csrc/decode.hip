@@ -56,7 +56,7 @@ struct DecArgs {
   float* hbuf;
   char* actf;
   char* sactf;
-  int* eact;
+  unsigned* eact;
   unsigned* cnt_up;
   unsigned* cnt_dn;
   float* part;
@@ -136,7 +136,7 @@ __device__ void dec_finalize(const DecArgs& a, const int* list, int n) {
       }
     }
   }
-  for (int k = tid; k < n; k += NW * 64) a.eact[list[k]] = 1;
+  for (int k = tid; k < n; k += NW * 64) a.eact[list[k]] = 1u;
 }
 
 template <class DT, int NW, int NP>
@@ -209,7 +209,7 @@ __global__ void __launch_bounds__(NW * 64) k_dec_up(DecArgs a) {
       st_dev(&a.g[(size_t)tid * a.E + e], act ? lam_e * z_mine : 0.f);
     }
     if (!any) {
-      if (p0 == 0 && tid == 0) a.eact[e] = 0;
+      if (p0 == 0 && tid == 0) a.eact[e] = 0u;
       return;  // inactive expert: none of its weights are read
     }
   }
@@ -308,7 +308,7 @@ __global__ void __launch_bounds__(NW * 64) k_dec_down(DecArgs a) {
   // ascending list of the experts that at least one token activated
   const int nwE = (a.E + 63) >> 6;
   const int e_ = w * 64 + l;
-  const bool act = (w < nwE) && (e_ < a.E) && (a.eact[e_] != 0);
+  const bool act = (w < nwE) && (e_ < a.E) && (a.eact[e_] != 0u);
   const unsigned long long bal = __ballot(act);
   if (w < nwE && l == 0) s_wcnt[w] = __popcll(bal);
   __syncthreads();
@@ -460,6 +460,15 @@ hipError_t decode(const deco_moe_layer* L, const void* x, int T, void* out, hipS
 }  // namespace
 
 namespace deco_host {
+
+// Decode launch shape: the down kernel splits its reduction Q ways so that
+// about 512 workgroups stream the down-projection weights.
+hipError_t plan_decode(deco_moe_layer* L) {
+  int q = (512 + L->n_groups - 1) / L->n_groups;
+  L->dec_q = q < 1 ? 1 : (q > DEC_QMAX ? DEC_QMAX : q);
+  L->dec_ok = 1;
+  return hipSuccess;
+}
 
 hipError_t launch_decode(const deco_moe_layer* L, const void* x, int T, void* out, hipStream_t s) {
   if (L->cfg.dtype == DECO_DT_BF16) return decode<BF16>(L, x, T, out, s);

@@ -47,11 +47,7 @@ void derive(deco_moe_layer* L) {
   L->pFs = L->Fs / 16;
   L->W = (L->E + 63) / 64;
   L->n_groups = L->d / 64;
-#ifndef DECO_DEC_DOWN_WGS
-#define DECO_DEC_DOWN_WGS 512
-#endif
-  int q = (DECO_DEC_DOWN_WGS + L->n_groups - 1) / L->n_groups;
-  L->dec_q = q < 1 ? 1 : (q > 32 ? 32 : q);
+  L->dec_q = 32;   // upper bound for the workspace; the decode plan picks the value at load
   L->pre_grid = 1024;
 }
 
@@ -200,8 +196,9 @@ int deco_moe_load_weights(const deco_moe_config* cfg, const void* W_r, const flo
   size_t o_h = k.take(sizeof(float) * (size_t)E * 16 * L->F);
   size_t o_af = k.take((size_t)E * L->nkb_F * KBy * (L->cfg.dtype == DECO_DT_BF16 ? 2 : 1));
   size_t o_sf = k.take((size_t)L->nkb_Fs * KBy);
-  size_t o_ea = k.take(sizeof(int) * E);
+  size_t o_ea = k.take(sizeof(unsigned) * E);
   size_t o_cu = k.take(sizeof(unsigned) * E);
+  size_t o_er = k.take(sizeof(unsigned));
   size_t o_cd = k.take(sizeof(unsigned) * L->n_groups);
   size_t o_pt = k.take(sizeof(float) * (size_t)L->dec_q * L->n_groups * 1024);
   size_t o_to = k.take(sizeof(int) * (Tcap + 1));
@@ -238,8 +235,9 @@ int deco_moe_load_weights(const deco_moe_config* cfg, const void* W_r, const flo
   L->hbuf = (float*)(L->ws + o_h);
   L->actf = L->ws + o_af;
   L->sactf = L->ws + o_sf;
-  L->eact = (int*)(L->ws + o_ea);
+  L->eact = (unsigned*)(L->ws + o_ea);
   L->cnt_up = (unsigned*)(L->ws + o_cu);
+  L->dec_err = (unsigned*)(L->ws + o_er);
   L->cnt_dn = (unsigned*)(L->ws + o_cd);
   L->part = (float*)(L->ws + o_pt);
   L->tok_off = (int*)(L->ws + o_to);
@@ -257,6 +255,7 @@ int deco_moe_load_weights(const deco_moe_config* cfg, const void* W_r, const flo
   if (err == hipSuccess) err = hipMemcpyAsync(L->b_r, b_r, sizeof(float) * E, hipMemcpyDeviceToDevice, s);
   if (err == hipSuccess) err = hipMemcpyAsync(L->lam, lambda, sizeof(float) * E, hipMemcpyDeviceToDevice, s);
   if (err == hipSuccess) err = deco_host::launch_pack_all(L, W_r, W_up, W_down, Ws_up, Ws_down, s);
+  if (err == hipSuccess) err = deco_host::plan_decode(L);
   if (err == hipSuccess) err = hipStreamSynchronize(s);
   if (err != hipSuccess) {
     (void)hipGetLastError();
@@ -279,8 +278,10 @@ int deco_moe_forward_path(const deco_moe_layer* L, const void* x, int64_t T, voi
   const char* xb = (const char*)x;
   const char* ob = (const char*)out;
   if (xb < ob + bytes && ob < xb + bytes) return DECO_ERR_INVALID_ARG;   // x and out overlap
-  if (path == DECO_PATH_AUTO) path = T <= DECO_DECODE_MAX_T ? DECO_PATH_DECODE : DECO_PATH_PREFILL;
+  if (path == DECO_PATH_AUTO)
+    path = (T <= DECO_DECODE_MAX_T && L->dec_ok) ? DECO_PATH_DECODE : DECO_PATH_PREFILL;
   if (path == DECO_PATH_DECODE && T > DECO_DECODE_MAX_T) return DECO_ERR_INVALID_ARG;
+  if (path == DECO_PATH_DECODE && !L->dec_ok) return DECO_ERR_UNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
   hipError_t err = path == DECO_PATH_DECODE ? deco_host::launch_decode(L, x, (int)T, out, s)
                                             : deco_host::launch_prefill(L, x, (int)T, out, s);
@@ -305,6 +306,16 @@ int deco_moe_copy_mean_up(const deco_moe_layer* L, float* wbar, void* stream) {
   if (!L || !wbar) return DECO_ERR_INVALID_ARG;
   hipError_t err = hipMemcpyAsync(wbar, L->wbar, sizeof(float) * (size_t)L->d * L->F, hipMemcpyDeviceToDevice,
                                   (hipStream_t)stream);
+  return err == hipSuccess ? DECO_OK : DECO_ERR_HIP;
+}
+
+int deco_moe_read_error_flags(const deco_moe_layer* L, uint32_t* flags) {
+  if (!L || !flags) return DECO_ERR_INVALID_ARG;
+  unsigned v = 0;
+  hipError_t err = hipDeviceSynchronize();
+  if (err == hipSuccess) err = hipMemcpy(&v, L->dec_err, sizeof(v), hipMemcpyDeviceToHost);
+  if (err == hipSuccess && v) err = hipMemset(L->dec_err, 0, sizeof(v));
+  *flags = v;
   return err == hipSuccess ? DECO_OK : DECO_ERR_HIP;
 }
 

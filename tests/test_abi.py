@@ -93,6 +93,7 @@ def test_host_side_rejections_touch_no_device(lib):
     assert lib.deco_moe_forward_path(None, None, 4, None, None, 1) == dm.DECO_ERR_INVALID_ARG
     assert lib.deco_moe_copy_routing(None, 1, None, None, None) == dm.DECO_ERR_INVALID_ARG
     assert lib.deco_moe_copy_mean_up(None, None, None) == dm.DECO_ERR_INVALID_ARG
+    assert lib.deco_moe_read_error_flags(None, None) == dm.DECO_ERR_INVALID_ARG
     lib.deco_moe_free(None)
     assert lib.deco_moe_timing_read(-1, None, None, None) == dm.DECO_ERR_INVALID_ARG
 

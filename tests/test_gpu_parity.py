@@ -71,6 +71,7 @@ def check(L, ref, layer, path=None, *, T=None, label=""):
     mism = act != ref.active[:T]
     near = np.abs(ref.z[:T]) < NEAR
     assert not np.any(mism & ~near), f"{label}: {int(np.sum(mism & ~near))} mask mismatches outside band"
+    assert layer.error_flags() == 0, f"{label}: a device-side wait timed out"
     _, logits = layer.routing(T)
     zerr = float(np.max(np.abs(logits.cpu().numpy().astype(np.float64) - ref.z[:T])))
     _say(f"  ok: excess/rms={excess / rms:.2e} literal err/rms={err / rms:.2e} mask_mismatch_in_band={int(mism.sum())} near_zero={int(near.sum())} "
