@@ -45,7 +45,7 @@ KERNEL_SOURCES = {
     "k_pre_router_shared": "sparse_moe_relu_amd/csrc/prefill.hip",
     "k_pre_dispatch": "sparse_moe_relu_amd/csrc/prefill.hip",
     "k_pre_expert": "sparse_moe_relu_amd/csrc/prefill.hip",
-    "k_pre_shared_down": "sparse_moe_relu_amd/csrc/prefill.hip",
+    "k_pre_combine": "sparse_moe_relu_amd/csrc/prefill.hip",
 }
 
 
@@ -86,12 +86,14 @@ def decode_bytes(L, n_union: int, T: int) -> dict:
 
 
 def prefill_flops(L, P: int, T: int) -> dict:
-    """Algorithmic flops per launch, per kernel (router + shared up; routed
-    up + down over the P active pairs; shared down)."""
+    """Algorithmic flops per launch, per kernel: router and shared up-projection
+    (the x.Wbar mean term is not counted); routed up + down over the P active
+    (token, expert) pairs plus the shared down-projection; the dispatch and the
+    combine (a sum of pair rows) do no matrix work."""
     return {"k_pre_router_shared": 2 * T * L.d * L.E + 2 * T * L.d * L.Fs,
             "k_pre_dispatch": 0,
-            "k_pre_expert": 4 * P * L.d * L.F,
-            "k_pre_shared_down": 2 * T * L.d * L.Fs}
+            "k_pre_expert": 4 * P * L.d * L.F + 2 * T * L.d * L.Fs,
+            "k_pre_combine": 0}
 
 
 def layer_weight_bytes(L) -> int:

@@ -3,14 +3,17 @@
 // Fragment convention used by every kernel.  A "k-block" is KB consecutive
 // reduction indices; one 16-byte vector per lane of a 64-lane wave (1 KiB)
 // holds a 16 x KB operand tile of an MFMA 16x16 product:
-//   lane l serves row/column (l & 15) and lane group g = l >> 4;
-//   bf16 (KB = 32): element j (0..7) of the lane is k = 8 g + j, consumed by
-//                   one v_mfma_f32_16x16x32_bf16;
-//   fp32 (KB = 16): element j (0..3) of the lane is k = 4 j + g, consumed by
-//                   the j-th of four v_mfma_f32_16x16x4_f32.
+//   lane l serves row/column (l & 15) and lane group g = l >> 4, and holds
+//   the EPL consecutive reduction indices k = EPL g + j (j = 0 .. EPL - 1);
+//   bf16 (KB = 32, EPL = 8): consumed by one v_mfma_f32_16x16x32_bf16;
+//   fp32 (KB = 16, EPL = 4): element j feeds the j-th of four
+//                   v_mfma_f32_16x16x4_f32 (that MFMA sums k = 4 g + j over
+//                   the four lane groups; the four together cover the block).
 // The 16x16 fp32 result of a lane holds rows 4 g + i (i = 0..3) of column
 // (l & 15).  Weights are packed once, at load, into this layout so each lane
-// fetches its operand with one 16-byte load (a wave reads 1 KiB contiguous).
+// fetches its operand with one 16-byte load (a wave reads 1 KiB contiguous),
+// and a row-major activation row supplies a fragment lane with one 16-byte
+// load as well.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -34,6 +37,33 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return u >> 16;
 }
 
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8_t;
+
+// fp16 operands (same fragment layout as bf16).  Used for the prefill
+// down-projection of bf16 layers: W_down is packed once more in fp16 (every
+// bf16 value within fp16's normal range converts exactly) and the NormSiLU
+// activations are rounded to fp16 (11-bit significand) instead of being split
+// into two bf16 parts, which halves that projection's MFMA work.
+struct FP16 {
+  using elem = uint16_t;           // storage bits
+  static constexpr int KB = 32;
+  static constexpr int EPL = 8;
+  __host__ __device__ static constexpr int frag_k(int g, int j) { return 8 * g + j; }
+  __host__ __device__ static constexpr int frag_g(int w) { return w >> 3; }
+  __host__ __device__ static constexpr int frag_j(int w) { return w & 7; }
+  __device__ static void mma(f32x4_t& acc, const i32x4_t& a, const i32x4_t& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                 __builtin_bit_cast(f16x8_t, b), acc, 0, 0, 0);
+  }
+  __device__ static uint32_t bits(float f) { return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f); }
+  __device__ static i32x4_t pack(const float* f) {
+    i32x4_t v;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = (int)(bits(f[2 * q]) | (bits(f[2 * q + 1]) << 16));
+    return v;
+  }
+};
+
 struct BF16 {
   using elem = uint16_t;
   static constexpr int KB = 32;    // k per fragment
@@ -42,6 +72,8 @@ struct BF16 {
   static constexpr bool SPLIT = true;
   // per-(token, expert) outputs kept between the expert and combine kernels
   using pair = _Float16;
+  // operand type of the prefill down-projection
+  using Down = FP16;
   __host__ __device__ static constexpr int frag_k(int g, int j) { return 8 * g + j; }
   __device__ static float to_f32(elem v) { return bf16_to_f32(v); }
   __device__ static elem from_f32(float f) { return (elem)f32_to_bf16(f); }
@@ -73,9 +105,10 @@ struct F32 {
   static constexpr int EPL = 4;
   static constexpr bool SPLIT = false;
   using pair = float;
-  __host__ __device__ static constexpr int frag_k(int g, int j) { return 4 * j + g; }
-  __host__ __device__ static constexpr int frag_g(int w) { return w & 3; }
-  __host__ __device__ static constexpr int frag_j(int w) { return w >> 2; }
+  using Down = F32;
+  __host__ __device__ static constexpr int frag_k(int g, int j) { return 4 * g + j; }
+  __host__ __device__ static constexpr int frag_g(int w) { return w >> 2; }
+  __host__ __device__ static constexpr int frag_j(int w) { return w & 3; }
   __device__ static float to_f32(elem v) { return v; }
   __device__ static elem from_f32(float f) { return f; }
   __device__ static float lane_elem(const i32x4_t& v, int j) { return __int_as_float(v[j]); }
@@ -116,10 +149,7 @@ __device__ __forceinline__ i32x4_t load_row_frag<BF16>(const uint16_t* row, int 
 }
 template <>
 __device__ __forceinline__ i32x4_t load_row_frag<F32>(const float* row, int kb, int g) {
-  i32x4_t v;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) v[j] = __float_as_int(row[kb * 16 + 4 * j + g]);
-  return v;
+  return ld16(row + kb * 16 + 4 * g);
 }
 
 // Byte offset, inside an array of [k-block][64 lanes][16 B] fragments, of the

@@ -30,6 +30,7 @@ struct deco_moe_layer {
   char* Wup_p;             // per expert [pF][nkb_d] frags of W_up[e]
   char* Wbar_p;            // [pF][nkb_d] frags of Wbar (layer dtype)
   char* Wdn_p;             // per expert [pD][nkb_F] frags
+  char* Wdn16_p;           // bf16 layers: W_down again, in fp16 (prefill); fp32 layers: = Wdn_p
   char* Wsu_p;             // [pFs][nkb_d]
   char* Wsd_p;             // [pD][nkb_Fs]
   size_t up_stride, dn_stride;   // bytes per expert
@@ -57,9 +58,11 @@ struct deco_moe_layer {
   int* tok_off;            // [Tcap + 1]
   int* ecnt;               // [E]
   int* list_tok;           // [E][Tcap]
-  int* list_slot;          // [E][Tcap]
   char* sbuf;              // [Tcap][Fs] shared activations (dtype)
-  char* ybuf;              // [Tcap * E][d] gated expert outputs, token-major (dtype)
+  char* ybuf;              // [Tcap * (E + 1)][d] pair buffer, token-major: per token its
+                           // shared-expert output, then gate * expert output for each
+                           // active expert in ascending order (fp16 for bf16 layers,
+                           // fp32 for fp32 layers)
 };
 
 namespace deco_host {
@@ -86,7 +89,7 @@ enum {
   KS_PRE_ROUTER_SHARED,
   KS_PRE_DISPATCH,
   KS_PRE_EXPERT,
-  KS_PRE_SHARED_DOWN,
+  KS_PRE_COMBINE,
   KS_COUNT
 };
 const char* kernel_slot_name(int slot);
@@ -95,6 +98,7 @@ const char* kernel_slot_name(int slot);
 hipError_t launch_pack_all(deco_moe_layer* L, const void* W_r, const void* W_up, const void* W_down,
                            const void* Ws_up, const void* Ws_down, hipStream_t s);
 hipError_t plan_decode(deco_moe_layer* L);   // decode launch shape (load time)
+hipError_t plan_prefill(deco_moe_layer* L);  // prefill launch shape (load time)
 hipError_t launch_decode(const deco_moe_layer* L, const void* x, int T, void* out, hipStream_t s);
 hipError_t launch_prefill(const deco_moe_layer* L, const void* x, int T, void* out, hipStream_t s);
 hipError_t launch_copy_mask(const deco_moe_layer* L, int T, uint64_t* mask, hipStream_t s);

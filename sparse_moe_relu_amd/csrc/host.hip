@@ -107,7 +107,7 @@ const char* kernel_slot_name(int slot) {
     case KS_PRE_ROUTER_SHARED: return "k_pre_router_shared";
     case KS_PRE_DISPATCH: return "k_pre_dispatch";
     case KS_PRE_EXPERT: return "k_pre_expert";
-    case KS_PRE_SHARED_DOWN: return "k_pre_shared_down";
+    case KS_PRE_COMBINE: return "k_pre_combine";
     default: return "?";
   }
 }
@@ -180,6 +180,7 @@ int deco_moe_load_weights(const deco_moe_config* cfg, const void* W_r, const flo
   size_t o_up = w.take(L->up_stride * E);
   size_t o_wbp = w.take((size_t)L->pF * L->nkb_d * KBy);
   size_t o_dn = w.take(L->dn_stride * E);
+  size_t o_dn16 = L->cfg.dtype == DECO_DT_BF16 ? w.take(L->dn_stride * E) : o_dn;
   size_t o_su = w.take((size_t)L->pFs * L->nkb_d * KBy);
   size_t o_sd = w.take((size_t)L->pD * L->nkb_Fs * KBy);
   size_t o_b = w.take(sizeof(float) * E);
@@ -204,9 +205,8 @@ int deco_moe_load_weights(const deco_moe_config* cfg, const void* W_r, const flo
   size_t o_to = k.take(sizeof(int) * (Tcap + 1));
   size_t o_ec = k.take(sizeof(int) * E);
   size_t o_lt = k.take(sizeof(int) * (size_t)E * Tcap);
-  size_t o_ls = k.take(sizeof(int) * (size_t)E * Tcap);
   size_t o_sb = k.take((size_t)L->esz * Tcap * L->Fs);
-  size_t o_yb = k.take((size_t)L->esz * Tcap * E * L->d);
+  size_t o_yb = k.take((size_t)L->esz * Tcap * (E + 1) * L->d);
   L->ws_bytes = k.off;
 
   if (hipMalloc((void**)&L->wmem, L->wmem_bytes) != hipSuccess) {
@@ -223,6 +223,7 @@ int deco_moe_load_weights(const deco_moe_config* cfg, const void* W_r, const flo
   L->Wup_p = L->wmem + o_up;
   L->Wbar_p = L->wmem + o_wbp;
   L->Wdn_p = L->wmem + o_dn;
+  L->Wdn16_p = L->wmem + o_dn16;
   L->Wsu_p = L->wmem + o_su;
   L->Wsd_p = L->wmem + o_sd;
   L->b_r = (float*)(L->wmem + o_b);
@@ -243,7 +244,6 @@ int deco_moe_load_weights(const deco_moe_config* cfg, const void* W_r, const flo
   L->tok_off = (int*)(L->ws + o_to);
   L->ecnt = (int*)(L->ws + o_ec);
   L->list_tok = (int*)(L->ws + o_lt);
-  L->list_slot = (int*)(L->ws + o_ls);
   L->sbuf = L->ws + o_sb;
   L->ybuf = L->ws + o_yb;
 
@@ -256,6 +256,7 @@ int deco_moe_load_weights(const deco_moe_config* cfg, const void* W_r, const flo
   if (err == hipSuccess) err = hipMemcpyAsync(L->lam, lambda, sizeof(float) * E, hipMemcpyDeviceToDevice, s);
   if (err == hipSuccess) err = deco_host::launch_pack_all(L, W_r, W_up, W_down, Ws_up, Ws_down, s);
   if (err == hipSuccess) err = deco_host::plan_decode(L);
+  if (err == hipSuccess) err = deco_host::plan_prefill(L);
   if (err == hipSuccess) err = hipStreamSynchronize(s);
   if (err != hipSuccess) {
     (void)hipGetLastError();

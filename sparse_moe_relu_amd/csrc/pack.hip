@@ -78,6 +78,10 @@ hipError_t pack_all(deco_moe_layer* L, const void* W_r, const void* W_up, const 
   // routed down: K = F, N = d
   k_pack<DT, E_t><<<grid(L->pD, L->nkb_F, E), 256, 0, s>>>((const E_t*)W_down, dF, F, d, d, L->pD, L->nkb_F,
                                                            L->Wdn_p, L->dn_stride);
+  // routed down again in fp16 for the prefill path of bf16 layers
+  if constexpr (sizeof(E_t) == 2)
+    k_pack<FP16, E_t><<<grid(L->pD, L->nkb_F, E), 256, 0, s>>>((const E_t*)W_down, dF, F, d, d, L->pD,
+                                                               L->nkb_F, L->Wdn16_p, L->dn_stride);
   // shared up: K = d, N = Fs
   k_pack<DT, E_t><<<grid(L->pFs, L->nkb_d, 1), 256, 0, s>>>((const E_t*)Ws_up, 0, d, Fs, Fs, L->pFs,
                                                             L->nkb_d, L->Wsu_p, 0);

@@ -1,32 +1,37 @@
 // prefill.hip - bucketed forward path for large batches.
 //
-//   k_pre_router_shared  one GEMM over x for the router columns, the columns
-//                        of the inter-expert mean Wbar and the shared expert's
-//                        up-projection.  Router epilogue: logits + b_r, gates
-//                        lambda_e * ReLU(z), active-expert bit masks (DECO
-//                        paper Sec. 2 "Router design"; zero or negative scores
-//                        are ignored: qidianchuan.cn write-up, section 二,
-//                        router).  Mean epilogue: m = x.Wbar in fp32 (the
-//                        NormSiLU mean term, same for every expert).  Shared
-//                        epilogue: SiLU, stored for the shared down-projection.
-//   k_pre_dispatch       per-expert token buckets ("expert batching"), built
-//                        with wave ballots and a workgroup prefix scan:
-//                        ascending token lists, and for every (token, expert)
-//                        pair its slot in a token-major pair buffer.
-//   k_pre_expert         persistent grouped kernel over (expert, 64-token
-//                        tile): gathered x rows . W_up[e] on MFMA, minus the
-//                        mean term, NormSiLU on the F-wide rows in registers,
-//                        then the down-projection (activations as a hi + lo
-//                        bf16 pair), written ungated to the token's pair slot
-//                        in fp16 (11-bit significand; a bf16 pair buffer
-//                        costs up to 4 % of RMS(out) on heavy-tailed gates).
-//   k_pre_shared_down    shared down-projection GEMM whose epilogue adds each
-//                        token's expert outputs times their gates in fp32
-//                        (the weighted combine; DECO paper Sec. 2 "Router
-//                        design": the router assigns each expert a weight), in
-//                        ascending expert order, then rounds to the dtype.
+//   k_pre_router_shared  one GEMM of x against the concatenated column panels
+//                        [router | inter-expert mean Wbar | shared up-proj].
+//                        Router epilogue: logits + b_r, gates lambda_e*ReLU(z)
+//                        and active-expert bit masks (DECO paper Sec. 2
+//                        "Router design"; zero or negative scores are ignored:
+//                        qidianchuan.cn write-up, section 二, router).  Mean
+//                        epilogue: m = x.Wbar in fp32 (the NormSiLU mean term,
+//                        the same for every expert).  Shared epilogue: SiLU,
+//                        stored for the shared down-projection.
+//   k_pre_dispatch       per-expert token buckets ("expert batching") from a
+//                        workgroup prefix scan: ascending token lists per
+//                        expert, and per token the offset of its slots in a
+//                        token-major pair buffer (slot 0: shared expert, then
+//                        one slot per active expert in ascending order).
+//   k_pre_expert         persistent grouped kernel.  Expert tiles (expert e,
+//                        up to 128 of its tokens): gathered x rows . W_up[e] on
+//                        MFMA, minus the mean term, NormSiLU (RMS over the F
+//                        columns of a row, then SiLU), . W_down[e] in fp16,
+//                        times the gate (DECO paper Sec. 2 "Router design": the
+//                        router gives every expert a weight), stored in fp16
+//                        to the pair slot.  Shared tiles: SiLU(x Ws_up) .
+//                        Ws_down into slot 0.
+//   k_pre_combine        out[t] = sum of token t's pair rows in slot order, in
+//                        fp32, rounded once to the dtype.
+//
+// All GEMMs run on the LDS-staged tile of gemm_tile.h with swapped operands,
+// so an accumulator lane holds 4 consecutive columns of one row.  Pair values
+// are fp16 (11-bit significand): a bf16 pair buffer costs up to 4 % of
+// RMS(out) on heavy-tailed gates.
 #include "deco_common.h"
 #include "deco_internal.h"
+#include "gemm_tile.h"
 
 using namespace deco;
 
@@ -37,10 +42,13 @@ struct PreArgs {
   void* out;
   int T, Tcap, d, E, F, Fs, W;
   int nkb_d, nkb_F, nkb_Fs, pR, pF, pD, pFs;
+  int pF4, pFs4;       // panel counts of the mean and shared sections, padded to 4
+  int rs_nt;           // 8-panel column tiles of the router/mean/shared GEMM
   const char* Wr_p;
   const char* Wup_p;
   const char* Wbar_p;
   const char* Wdn_p;
+  const char* Wdn16_p;     // down-projection operand of the prefill path (fp16 or fp32)
   const char* Wsu_p;
   const char* Wsd_p;
   size_t up_stride, dn_stride;
@@ -54,107 +62,152 @@ struct PreArgs {
   int* tok_off;
   int* ecnt;
   int* list_tok;
-  int* list_slot;
   void* sbuf;
   void* ybuf;
 };
 
-constexpr int BM = 64;   // token rows per tile (4 waves x 16)
+#ifndef DECO_PRE_KS
+#define DECO_PRE_KS 1     // k-blocks per pipeline step
+#endif
+#ifndef DECO_PRE_NS
+#define DECO_PRE_NS 4     // pipeline stages in LDS
+#endif
+
+constexpr int NXCD = 8;
+constexpr int GM = 128;   // rows of the dense GEMM tiles
+constexpr int GP = 8;     // 16-column panels of the dense GEMM tiles
+template <class DT>
+using DenseTile = Tile<DT, GM, GP, DECO_PRE_KS, DECO_PRE_NS>;
+
+// Workgroups are handed to the 8 XCDs round-robin (workgroup b runs on XCD
+// b % 8).  Renumber them so each XCD works on one contiguous range of tiles:
+// tiles next to each other share operands, and each XCD has its own L2.
+__device__ __forceinline__ int xcd_tile(int b, int n) {
+  const int per = n / NXCD, rem = n % NXCD, x = b % NXCD, i = b / NXCD;
+  return x * per + (x < rem ? x : rem) + i;
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// 4 consecutive values of one row, stored as the dtype (8 bytes bf16, 16 fp32)
+template <class DT>
+__device__ __forceinline__ void store4(typename DT::elem* p, float v0, float v1, float v2, float v3) {
+  if constexpr (sizeof(typename DT::elem) == 2) {
+    uint2 u;
+    u.x = f32_to_bf16(v0) | (f32_to_bf16(v1) << 16);
+    u.y = f32_to_bf16(v2) | (f32_to_bf16(v3) << 16);
+    *reinterpret_cast<uint2*>(p) = u;
+  } else {
+    *reinterpret_cast<float4*>(p) = make_float4(v0, v1, v2, v3);
+  }
+}
+
+template <class PT>
+__device__ __forceinline__ void store4_pair(PT* p, const f32x4_t& v) {
+  if constexpr (sizeof(PT) == 2) {
+    typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 h4;
+    h4 h = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+    *reinterpret_cast<h4*>(p) = h;
+  } else {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+}
 
 // --------------------------------------------------------------------------
 template <class DT>
-__global__ void __launch_bounds__(256) k_pre_router_shared(PreArgs a) {
+__global__ void __launch_bounds__(256, 2) k_pre_router_shared(PreArgs a) {
   using elem = typename DT::elem;
-  constexpr int CH = 4;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, c = l & 15;
-  const int mt = blockIdx.x, nt = blockIdx.y;
-  const int nRt = a.pR / 4, nMt = (a.pF + 3) / 4;
-  const int kind = nt < nRt ? 0 : (nt < nRt + nMt ? 1 : 2);    // router / mean / shared
-  const bool is_router = kind == 0;
-  const int pbase = kind == 0 ? nt * 4 : (kind == 1 ? (nt - nRt) * 4 : (nt - nRt - nMt) * 4);
-  const int np = kind == 0 ? 4 : min(4, (kind == 1 ? a.pF : a.pFs) - pbase);
-  const char* Wb = kind == 0 ? a.Wr_p : (kind == 1 ? a.Wbar_p : a.Wsu_p);
-  const int row = mt * BM + w * 16 + c;
-  const bool row_ok = row < a.T;
-  const elem* xrow = (const elem*)a.x + (size_t)row * a.d;
+  using TC = DenseTile<DT>;
+  __shared__ i32x4_t lds[TC::LDS_V];
+  const int tid = threadIdx.x, w = tid >> 6, wm = w >> 1, wn = w & 1, l = tid & 63, g = l >> 4, c = l & 15;
+  const int t = xcd_tile(blockIdx.x, gridDim.x);
+  const int m0 = (t / a.rs_nt) * GM, p0 = (t % a.rs_nt) * GP;
+  const elem* x = (const elem*)a.x;
+  // rows past T and padding panels read valid memory; those outputs are dropped
+  auto row = [&](int r) -> const elem* {
+    const int rr = m0 + r;
+    return x + (size_t)(rr < a.T ? rr : a.T - 1) * a.d;
+  };
+  auto panel = [&](int p) -> const char* {
+    int q = p0 + p;
+    if (q < a.pR) return a.Wr_p + frag_off(q, 0, a.nkb_d);
+    q -= a.pR;
+    if (q < a.pF4) return a.Wbar_p + frag_off(q < a.pF ? q : 0, 0, a.nkb_d);
+    q -= a.pF4;
+    return a.Wsu_p + frag_off(q < a.pFs ? q : 0, 0, a.nkb_d);
+  };
+  f32x4_t acc[TC::MB][TC::NBW];
+#pragma unroll
+  for (int i = 0; i < TC::MB; ++i)
+#pragma unroll
+    for (int j = 0; j < TC::NBW; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  tile_gemm<DT, TC, true>(lds, row, panel, a.nkb_d, acc);
 
-  f32x4_t acc[4];
+  // lane: row m0 + wm*64 + 16 i + c, columns 16 (q0 + j) + 4 g + ii
+  const int q0 = p0 + wn * TC::NBW;   // a multiple of 4: one section per wave
+  if (q0 < a.pR) {
+    float be[TC::NBW][4], le[TC::NBW][4];
 #pragma unroll
-  for (int p = 0; p < 4; ++p) acc[p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int kb0 = 0; kb0 < a.nkb_d; kb0 += CH) {
-    i32x4_t xf[CH], wf[CH][4];
+    for (int j = 0; j < TC::NBW; ++j)
 #pragma unroll
-    for (int u = 0; u < CH; ++u) {
-      const int kb = kb0 + u;
-      xf[u] = (kb < a.nkb_d && row_ok) ? load_row_frag<DT>(xrow, kb, g) : zero16();
-#pragma unroll
-      for (int p = 0; p < 4; ++p)
-        wf[u][p] = (kb < a.nkb_d && p < np) ? ld16(Wb + frag_off(pbase + p, kb, a.nkb_d) + (size_t)l * 16)
-                                            : zero16();
-    }
-#pragma unroll
-    for (int u = 0; u < CH; ++u)
-#pragma unroll
-      for (int p = 0; p < 4; ++p) DT::mma(acc[p], xf[u], wf[u][p]);
-  }
-
-  const int rbase = mt * BM + w * 16 + 4 * g;
-  if (is_router) {
-    uint32_t bits[4][4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int e = nt * 64 + p * 16 + c;
-      const bool e_ok = e < a.E;
-      const float be = e_ok ? a.b_r[e] : 0.f;
-      const float le = e_ok ? a.lam[e] : 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = rbase + i;
-        const bool ok = e_ok && r < a.T;
-        const float zv = acc[p][i] + be;
-        const bool act = ok && zv > 0.f && le != 0.f;
-        if (ok) {
-          a.z[(size_t)r * a.E + e] = zv;
-          a.g[(size_t)r * a.E + e] = act ? le * zv : 0.f;
-        }
-        const unsigned long long bal = __ballot(act);
-        bits[p][i] = (uint32_t)((bal >> (16 * g)) & 0xFFFFull);
+      for (int ii = 0; ii < 4; ++ii) {
+        const int e = (q0 + j) * 16 + 4 * g + ii;
+        be[j][ii] = e < a.E ? a.b_r[e] : 0.f;
+        le[j][ii] = e < a.E ? a.lam[e] : 0.f;
       }
-    }
-    if (c == 0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = rbase + i;
-        if (r < a.T) {
-          uint64_t word = 0;
+    for (int i = 0; i < TC::MB; ++i) {
+      const int r = m0 + wm * (GM / 2) + 16 * i + c;
+      uint64_t bits = 0;
 #pragma unroll
-          for (int p = 0; p < 4; ++p) word |= (uint64_t)bits[p][i] << (16 * p);
-          a.mask[(size_t)r * a.W + nt] = word;
+      for (int j = 0; j < TC::NBW; ++j)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int e = (q0 + j) * 16 + 4 * g + ii;
+          const float zv = acc[i][j][ii] + be[j][ii];
+          const bool act = e < a.E && zv > 0.f && le[j][ii] != 0.f;
+          if (act) bits |= 1ull << (16 * j + 4 * g + ii);
+          if (r < a.T && e < a.E) {
+            a.z[(size_t)r * a.E + e] = zv;
+            a.g[(size_t)r * a.E + e] = act ? le[j][ii] * zv : 0.f;
+          }
         }
-      }
+      bits |= shfl_xor_u64(bits, 16);
+      bits |= shfl_xor_u64(bits, 32);
+      if (g == 0 && r < a.T) a.mask[(size_t)r * a.W + q0 / 4] = bits;
     }
-  } else if (kind == 1) {
+  } else if (q0 - a.pR < a.pF4) {
+    const int q = q0 - a.pR;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      if (p < np) {
-        const int col = (pbase + p) * 16 + c;
+    for (int j = 0; j < TC::NBW; ++j) {
+      if (q + j < a.pF) {
+        const int f0 = (q + j) * 16 + 4 * g;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = rbase + i;
-          if (r < a.T) a.mbuf[(size_t)r * a.F + col] = acc[p][i];
+        for (int i = 0; i < TC::MB; ++i) {
+          const int r = m0 + wm * (GM / 2) + 16 * i + c;
+          if (r < a.T)
+            *reinterpret_cast<float4*>(a.mbuf + (size_t)r * a.F + f0) =
+                make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
         }
       }
     }
   } else {
+    const int q = q0 - a.pR - a.pF4;
     elem* sb = (elem*)a.sbuf;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      if (p < np) {
-        const int col = (pbase + p) * 16 + c;
+    for (int j = 0; j < TC::NBW; ++j) {
+      if (q + j < a.pFs) {
+        const int c0 = (q + j) * 16 + 4 * g;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = rbase + i;
-          if (r < a.T) sb[(size_t)r * a.Fs + col] = DT::from_f32(silu_f(acc[p][i]));
+        for (int i = 0; i < TC::MB; ++i) {
+          const int r = m0 + wm * (GM / 2) + 16 * i + c;
+          if (r < a.T)
+            store4<DT>(sb + (size_t)r * a.Fs + c0, silu_f(acc[i][j][0]), silu_f(acc[i][j][1]),
+                       silu_f(acc[i][j][2]), silu_f(acc[i][j][3]));
         }
       }
     }
@@ -162,8 +215,10 @@ __global__ void __launch_bounds__(256) k_pre_router_shared(PreArgs a) {
 }
 
 // --------------------------------------------------------------------------
-// Exclusive scan of one int per thread over a 256-thread workgroup.
-__device__ int block_excl_scan(int v, int* s_tmp, int* total) {
+// Exclusive scan of one int per thread over a workgroup of NW waves; *total
+// receives the sum.  s_tmp holds NW ints.
+template <int NW>
+__device__ __forceinline__ int block_excl_scan(int v, int* s_tmp, int* total) {
   const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
   int incl = v;
 #pragma unroll
@@ -175,7 +230,7 @@ __device__ int block_excl_scan(int v, int* s_tmp, int* total) {
   __syncthreads();
   int base = 0, tot = 0;
 #pragma unroll
-  for (int ww = 0; ww < 4; ++ww) {
+  for (int ww = 0; ww < NW; ++ww) {
     const int t = s_tmp[ww];
     if (ww < w) base += t;
     tot += t;
@@ -185,67 +240,162 @@ __device__ int block_excl_scan(int v, int* s_tmp, int* total) {
   return base + incl - v;
 }
 
-__global__ void __launch_bounds__(256) k_pre_dispatch(PreArgs a) {
-  __shared__ int s_tmp1[4], s_tmp2[4];
+// Workgroup e < E: the ascending token list of expert e and its size.
+// Workgroup E: per token, the offset of its pair slots (exclusive prefix of
+// 1 + the token's active-expert count): slot 0 for the shared expert, then
+// one per active expert in ascending e.
+constexpr int DISP_NT = 1024, DISP_TPT = 4;
+
+__global__ void __launch_bounds__(DISP_NT) k_pre_dispatch(PreArgs a) {
+  __shared__ int s_tmp[DISP_NT / 64];
   const int e = blockIdx.x, tid = threadIdx.x;
+  const bool offsets = e == a.E;
   const int wi = e >> 6, bit = e & 63;
-  int run_tok = 0, run_e = 0;
-  for (int t0 = 0; t0 < a.T; t0 += 256) {
-    const int t = t0 + tid;
-    const bool valid = t < a.T;
-    int cnt = 0, below = 0;
-    bool act = false;
-    if (valid) {
-      for (int ww = 0; ww < a.W; ++ww) {
-        const uint64_t m = a.mask[(size_t)t * a.W + ww];
-        cnt += __popcll(m);
-        if (ww < wi) below += __popcll(m);
-        if (ww == wi) {
-          below += __popcll(m & ((1ull << bit) - 1ull));
-          act = (m >> bit) & 1ull;
+  int run = 0;
+  for (int t0 = 0; t0 < a.T; t0 += DISP_NT * DISP_TPT) {
+    const int tb = t0 + tid * DISP_TPT;
+    int v[DISP_TPT], local = 0;
+#pragma unroll
+    for (int k = 0; k < DISP_TPT; ++k) {
+      const int t = tb + k;
+      v[k] = 0;
+      if (t < a.T) {
+        if (offsets) {
+          v[k] = 1;   // slot 0: the shared expert
+          for (int ww = 0; ww < a.W; ++ww) v[k] += __popcll(a.mask[(size_t)t * a.W + ww]);
+        } else {
+          v[k] = (int)((a.mask[(size_t)t * a.W + wi] >> bit) & 1ull);
         }
       }
+      local += v[k];
     }
-    int tot_tok, tot_e;
-    const int off_t = run_tok + block_excl_scan(cnt, s_tmp1, &tot_tok);
-    const int rank = run_e + block_excl_scan(act ? 1 : 0, s_tmp2, &tot_e);
-    if (valid && e == 0) a.tok_off[t] = off_t;
-    if (act) {
-      a.list_tok[(size_t)e * a.Tcap + rank] = t;
-      a.list_slot[(size_t)e * a.Tcap + rank] = off_t + below;
+    int tot;
+    int pos = run + block_excl_scan<DISP_NT / 64>(local, s_tmp, &tot);
+#pragma unroll
+    for (int k = 0; k < DISP_TPT; ++k) {
+      const int t = tb + k;
+      if (offsets) {
+        if (t < a.T) a.tok_off[t] = pos;
+      } else if (v[k]) {
+        a.list_tok[(size_t)e * a.Tcap + pos] = t;
+      }
+      pos += v[k];
     }
-    run_tok += tot_tok;
-    run_e += tot_e;
+    run += tot;
   }
   if (tid == 0) {
-    a.ecnt[e] = run_e;
-    if (e == 0) a.tok_off[a.T] = run_tok;
+    if (offsets) a.tok_off[a.T] = run;
+    else a.ecnt[e] = run;
   }
 }
 
 // --------------------------------------------------------------------------
-template <class DT, int NPF>
-__global__ void __launch_bounds__(256) k_pre_expert(PreArgs a) {
-  using elem = typename DT::elem;
-  constexpr int F = NPF * 16;
-  constexpr int CH = 4;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, c = l & 15;
-  constexpr int NPART = DT::SPLIT ? 2 : 1;
-  __shared__ int s_toff[257];
-  __shared__ elem s_a[NPART][4][16][F];
+template <class DT, int BNP>
+struct ExpertShape {
+  using DN = typename DT::Down;                      // down-projection operand type
+  static constexpr int BM = BNP >= 16 ? 64 : 128;    // token rows per tile
+  // up-projection ring: one k-block per step (two for F = 32, so that the
+  // 2 panels' fragments divide over the 4 waves)
+  using TC = Tile<DT, BM, BNP, (BNP == 2 ? 2 : 1), (BNP == 2 || BNP >= 16 ? 3 : 4)>;
+  static constexpr int F = BNP * 16;
+  static constexpr int NKF = F / DN::KB;             // k-blocks of the down-projection
+  static constexpr int RB = BM / 16;                 // 16-row blocks of the tile
+  static constexpr int MB = BM / 32;                 // 16-row blocks per wave
+  static constexpr int ACT_V = RB * NKF * 64;        // 16-byte LDS slots of the activations
+  static constexpr int DP = NKF >= 8 ? 2 : 4;        // W_down panels per ring stage
+  static constexpr int DSTAGE_V = DP * NKF * 64;
+  static constexpr int DNS = DSTAGE_V <= 1024 ? 4 : 2;   // ring stages (16 KiB stages: 4)
+  static constexpr int DLPW = DP * NKF / 4;          // ring loads per wave per stage
+  static constexpr int OCC = sizeof(typename DT::elem) == 2 ? 2 : 1;   // workgroups per CU
+  static constexpr int cmax(int x, int y) { return x > y ? x : y; }
+  static constexpr int LDS_V = cmax(cmax(TC::LDS_V, ACT_V), cmax(DNS * DSTAGE_V, DenseTile<DT>::LDS_V));
+  static_assert((DP * NKF) % 4 == 0, "ring fragments must divide over the 4 waves");
+};
 
-  if (tid == 0) {
-    int acc = 0;
-    for (int e = 0; e < a.E; ++e) {
-      s_toff[e] = acc;
-      acc += (a.ecnt[e] + BM - 1) / BM;
-    }
-    s_toff[a.E] = acc;
+// One persistent kernel for all grouped work after the dispatch:
+//   expert tiles  (expert e, up to BM of its tokens): gathered x . W_up[e],
+//                 NormSiLU, then . W_down[e], scaled by the gates and written
+//                 to the tokens' pair slots;
+//   shared tiles  (128 tokens x 128 columns): SiLU(x Ws_up) . Ws_down, written
+//                 to slot 0 of each token's pairs.
+// Expert tiles come first (they are the longer ones); each XCD works through
+// its own contiguous range of both lists.
+template <class DT, int BNP>
+__global__ void __launch_bounds__(256, (ExpertShape<DT, BNP>::OCC)) k_pre_expert(PreArgs a) {
+  using elem = typename DT::elem;
+  using S = ExpertShape<DT, BNP>;
+  using TC = typename S::TC;
+  using DN = typename S::DN;
+  using PT = typename DT::pair;
+  constexpr int BM = S::BM, MB = S::MB, NBW = TC::NBW, F = S::F, NKF = S::NKF, DP = S::DP;
+  __shared__ i32x4_t lds[S::LDS_V];
+  __shared__ int s_toff[257];
+  __shared__ int s_tmp[4];
+  __shared__ int s_tok[BM];
+  __shared__ int s_slot[BM];
+  __shared__ float s_gate[BM];
+  __shared__ float s_ss[2][BM];
+  const int tid = threadIdx.x, w = tid >> 6, wm = w >> 1, wn = w & 1, l = tid & 63, g = l >> 4, c = l & 15;
+
+  // expert e owns tiles s_toff[e] .. s_toff[e + 1] - 1
+  {
+    const int n = tid < a.E ? (a.ecnt[tid] + BM - 1) / BM : 0;
+    int tot;
+    const int ex = block_excl_scan<4>(n, s_tmp, &tot);
+    if (tid < a.E) s_toff[tid] = ex;
+    if (tid == 0) s_toff[a.E] = tot;
   }
   __syncthreads();
-  const int NT = s_toff[a.E];
+  const int n_et = s_toff[a.E];
+  const int nsp = (a.pD + GP - 1) / GP;                      // shared tiles per 128 rows
+  const int n_st = ((a.T + GM - 1) / GM) * nsp;
+  const int xg = blockIdx.x % NXCD, lb = blockIdx.x / NXCD;
+  const int gx = ((int)gridDim.x - xg + NXCD - 1) / NXCD;    // workgroups on this XCD
+  const int e_beg = (int)((long long)n_et * xg / NXCD), e_end = (int)((long long)n_et * (xg + 1) / NXCD);
+  const int s_beg = (int)((long long)n_st * xg / NXCD), s_end = (int)((long long)n_st * (xg + 1) / NXCD);
+  const int n_mine = (e_end - e_beg) + (s_end - s_beg);
   const float invF = 1.0f / (float)F;
-  for (int tile = blockIdx.x; tile < NT; tile += gridDim.x) {
+  const elem* x = (const elem*)a.x;
+  PT* yb = (PT*)a.ybuf;
+
+  for (int k = lb; k < n_mine; k += gx) {
+    __syncthreads();   // the previous tile no longer reads LDS
+    if (k >= e_end - e_beg) {
+      // ---- shared tile: rows m0.., panels p0.. of SiLU(x Ws_up) . Ws_down
+      using TD = DenseTile<DT>;
+      const int ts = s_beg + k - (e_end - e_beg);
+      const int m0 = (ts / nsp) * GM, p0 = (ts % nsp) * GP;
+      const elem* sbuf = (const elem*)a.sbuf;
+      auto row = [&](int r) -> const elem* {
+        const int rr = m0 + r;
+        return sbuf + (size_t)(rr < a.T ? rr : a.T - 1) * a.Fs;
+      };
+      auto panel = [&](int p) -> const char* {
+        return a.Wsd_p + frag_off(p0 + p < a.pD ? p0 + p : 0, 0, a.nkb_Fs);
+      };
+      f32x4_t acc[TD::MB][TD::NBW];
+#pragma unroll
+      for (int i = 0; i < TD::MB; ++i)
+#pragma unroll
+        for (int j = 0; j < TD::NBW; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      tile_gemm<DT, TD, true>(lds, row, panel, a.nkb_Fs, acc);
+      const int q0 = p0 + wn * TD::NBW;
+      if (q0 < a.pD) {   // pD is a multiple of 4: a wave's 4 panels are all valid or all padding
+#pragma unroll
+        for (int i = 0; i < TD::MB; ++i) {
+          const int r = m0 + wm * (GM / 2) + 16 * i + c;
+          if (r < a.T) {
+            PT* dst = yb + (size_t)a.tok_off[r] * a.d + q0 * 16 + 4 * g;
+#pragma unroll
+            for (int j = 0; j < TD::NBW; ++j) store4_pair(dst + j * 16, acc[i][j]);
+          }
+        }
+      }
+      continue;
+    }
+
+    // ---- expert tile
+    const int tile = e_beg + k;
     int lo = 0, hi = a.E;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
@@ -253,163 +403,213 @@ __global__ void __launch_bounds__(256) k_pre_expert(PreArgs a) {
     }
     const int e = lo;
     const int n_e = a.ecnt[e];
-    const int r0 = (tile - s_toff[e]) * BM + w * 16;
-    const int* ltok = a.list_tok + (size_t)e * a.Tcap;
-    const int* lslot = a.list_slot + (size_t)e * a.Tcap;
+    const int r0 = (tile - s_toff[e]) * BM;
+    if (tid < BM) {
+      const int rank = r0 + tid;
+      int tok = -1, slot = -1;
+      float gate = 0.f;
+      if (rank < n_e) {
+        tok = a.list_tok[(size_t)e * a.Tcap + rank];
+        const uint64_t* mrow = a.mask + (size_t)tok * a.W;
+        int below = 0;
+        for (int ww = 0; ww < (e >> 6); ++ww) below += __popcll(mrow[ww]);
+        below += __popcll(mrow[e >> 6] & ((1ull << (e & 63)) - 1ull));
+        slot = a.tok_off[tok] + 1 + below;   // slot 0 of the token holds the shared expert
+        gate = a.g[(size_t)tok * a.E + e];
+      }
+      s_tok[tid] = tok;
+      s_slot[tid] = slot;
+      s_gate[tid] = gate;
+    }
+    __syncthreads();
 
     // up-projection of the gathered rows, all F columns
-    const int myrow = r0 + c;
-    const int tok = myrow < n_e ? ltok[myrow] : -1;
-    const elem* xrow = (const elem*)a.x + (size_t)(tok < 0 ? 0 : tok) * a.d;
     const char* Wu = a.Wup_p + (size_t)e * a.up_stride;
-    f32x4_t acc[NPF];
+    auto row = [&](int r) -> const elem* {
+      const int tk = s_tok[r];   // padding rows read token 0; their outputs are dropped
+      return x + (size_t)(tk >= 0 ? tk : 0) * a.d;
+    };
+    auto panel = [&](int p) -> const char* { return Wu + frag_off(p, 0, a.nkb_d); };
+    f32x4_t acc[MB][NBW];
 #pragma unroll
-    for (int p = 0; p < NPF; ++p) acc[p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int kb0 = 0; kb0 < a.nkb_d; kb0 += CH) {
-      i32x4_t xf[CH];
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
-      for (int u = 0; u < CH; ++u) {
-        const int kb = kb0 + u;
-        xf[u] = (kb < a.nkb_d && tok >= 0) ? load_row_frag<DT>(xrow, kb, g) : zero16();
+      for (int j = 0; j < NBW; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    tile_gemm<DT, TC, true>(lds, row, panel, a.nkb_d, acc);
+
+    // NormSiLU.  Lane: local row R = wm*BM/2 + 16 i + c, columns
+    // f = 16 (wn*NBW + j) + 4 g + ii.  Subtract the mean term, then the sum
+    // of squares over the row's F columns: in-lane, over the 4 lane groups,
+    // then over the two column halves (waves wn = 0, 1) through LDS.
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      const int R = wm * (BM / 2) + 16 * i + c;
+      const int tk = s_tok[R];
+      const float* mrow = a.mbuf + (size_t)(tk < 0 ? 0 : tk) * F;
+      float ss = 0.f;
+#pragma unroll
+      for (int j = 0; j < NBW; ++j) {
+        const float4 m = *reinterpret_cast<const float4*>(mrow + 16 * (wn * NBW + j) + 4 * g);
+        acc[i][j][0] -= m.x;
+        acc[i][j][1] -= m.y;
+        acc[i][j][2] -= m.z;
+        acc[i][j][3] -= m.w;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) ss += acc[i][j][ii] * acc[i][j][ii];
+      }
+      ss += __shfl_xor(ss, 16);
+      ss += __shfl_xor(ss, 32);
+      if (g == 0) s_ss[wn][R] = ss;
+    }
+    __syncthreads();
+    // activations into LDS in the fragment order of the down-projection's
+    // token operand (rounded once to the operand type)
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      const int R = wm * (BM / 2) + 16 * i + c;
+      const bool ok = s_tok[R] >= 0;
+      const float inv_r = ok ? 1.0f / sqrtf((s_ss[0][R] + s_ss[1][R]) * invF + a.eps) : 0.f;
+#pragma unroll
+      for (int j = 0; j < NBW; ++j) {
+        const int p = wn * NBW + j;
+        float v[4];
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) v[ii] = ok ? silu_f(acc[i][j][ii] * inv_r) : 0.f;
+        if constexpr (DN::KB == 32) {
+          // f = 16 p + 4 g + ii: k-block p / 2, lane group 2 (p % 2) + g / 2,
+          // elements 4 (g % 2) + ii of the lane
+          const int slot = ((R >> 4) * NKF + (p >> 1)) * 64 + (R & 15) + 16 * (2 * (p & 1) + (g >> 1));
+          *reinterpret_cast<uint2*>(reinterpret_cast<char*>(lds + slot) + 8 * (g & 1)) =
+              make_uint2(DN::bits(v[0]) | (DN::bits(v[1]) << 16), DN::bits(v[2]) | (DN::bits(v[3]) << 16));
+        } else {
+          // fp32: f = 16 p + 4 g + ii: k-block p, lane group g, elements ii
+          *reinterpret_cast<float4*>(lds + ((R >> 4) * NKF + p) * 64 + (R & 15) + 16 * g) =
+              make_float4(v[0], v[1], v[2], v[3]);
+        }
+      }
+    }
+    __syncthreads();
+    // each wave keeps the activations of its token blocks in registers
+    i32x4_t act[MB][NKF];
+#pragma unroll
+    for (int jt = 0; jt < MB; ++jt)
+#pragma unroll
+      for (int kb = 0; kb < NKF; ++kb) act[jt][kb] = lds[((wm * MB + jt) * NKF + kb) * 64 + l];
+    float gt[MB];
+    int sl[MB];
+#pragma unroll
+    for (int jt = 0; jt < MB; ++jt) {
+      gt[jt] = s_gate[wm * (BM / 2) + 16 * jt + c];
+      sl[jt] = s_slot[wm * (BM / 2) + 16 * jt + c];
+    }
+    __syncthreads();   // every wave holds its activations: the LDS becomes the W_down ring
+
+    // down-projection through a ring of DP-panel stages of W_down[e] (all
+    // NKF k-blocks of each panel); wave (wm, wn) takes its token blocks and
+    // panels wn*DP/2 .. of each stage.  Operands swapped (W_down as the row
+    // operand): a lane holds 4 consecutive output columns of one token.
+    const char* Wd = a.Wdn16_p + (size_t)e * a.dn_stride;
+    const int nds = a.pD / DP;
+    auto issue = [&](int st) {
+      i32x4_t* ring = lds + (st % S::DNS) * S::DSTAGE_V;
+#pragma unroll
+      for (int i = 0; i < S::DLPW; ++i) {
+        const int f = w * S::DLPW + i;   // panel f / NKF of the stage, k-block f % NKF
+        load_lds16(Wd + frag_off(st * DP + f / NKF, f % NKF, NKF) + l * 16, ring + f * 64);
+      }
+    };
+#pragma unroll
+    for (int st = 0; st < S::DNS - 1; ++st)
+      if (st < nds) issue(st);
+    for (int st = 0; st < nds; ++st) {
+      if (st + S::DNS - 2 < nds) wait_vmcnt<(S::DNS - 2) * S::DLPW>();
+      else wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      if (st + S::DNS - 1 < nds) issue(st + S::DNS - 1);
+      const i32x4_t* ring = lds + (st % S::DNS) * S::DSTAGE_V;
+      f32x4_t y[MB][DP / 2];
+#pragma unroll
+      for (int jt = 0; jt < MB; ++jt)
+#pragma unroll
+        for (int q = 0; q < DP / 2; ++q) y[jt][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < NKF; ++kb) {
+        i32x4_t bv[DP / 2];
+#pragma unroll
+        for (int q = 0; q < DP / 2; ++q) bv[q] = ring[((wn * (DP / 2) + q) * NKF + kb) * 64 + l];
+#pragma unroll
+        for (int jt = 0; jt < MB; ++jt)
+#pragma unroll
+          for (int q = 0; q < DP / 2; ++q) DN::mma(y[jt][q], bv[q], act[jt][kb]);
       }
 #pragma unroll
-      for (int u = 0; u < CH; ++u) {
-        const int kb = kb0 + u;
-        if (kb < a.nkb_d) {
+      for (int jt = 0; jt < MB; ++jt) {
+        if (sl[jt] >= 0) {
+          PT* dst = yb + (size_t)sl[jt] * a.d + (st * DP + wn * (DP / 2)) * 16 + 4 * g;
 #pragma unroll
-          for (int p = 0; p < NPF; ++p) {
-            const i32x4_t wv = ld16(Wu + frag_off(p, kb, a.nkb_d) + (size_t)l * 16);
-            DT::mma(acc[p], xf[u], wv);
+          for (int q = 0; q < DP / 2; ++q) {
+            f32x4_t v = y[jt][q];
+            v[0] *= gt[jt];
+            v[1] *= gt[jt];
+            v[2] *= gt[jt];
+            v[3] *= gt[jt];
+            store4_pair(dst + q * 16, v);
           }
         }
       }
     }
-
-    // NormSiLU: subtract the mean term, RMS over the F columns of the row
-    // (spread over the 16 lanes of a lane group and the NPF panels), SiLU,
-    // times the gate; stored to LDS as hi (+ lo) parts
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rr = r0 + 4 * g + i;
-      const int tk = rr < n_e ? ltok[rr] : -1;
-      const float* mrow = a.mbuf + (size_t)(tk < 0 ? 0 : tk) * F;
-      float ss = 0.f;
-#pragma unroll
-      for (int p = 0; p < NPF; ++p) {
-        const float hv = tk >= 0 ? acc[p][i] - mrow[p * 16 + c] : 0.f;
-        acc[p][i] = hv;
-        ss += hv * hv;
-      }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) ss += __shfl_xor(ss, o);
-      const float inv_r = 1.0f / sqrtf(ss * invF + a.eps);
-#pragma unroll
-      for (int p = 0; p < NPF; ++p) {
-        const float v = tk >= 0 ? silu_f(acc[p][i] * inv_r) : 0.f;
-        elem hi, lo;
-        split_hi_lo<DT>(v, hi, lo);
-        s_a[0][w][4 * g + i][p * 16 + c] = hi;
-        if (DT::SPLIT) s_a[NPART - 1][w][4 * g + i][p * 16 + c] = lo;
-      }
-    }
-    __syncthreads();
-
-    // down-projection, 64 output columns at a time, into the pair slots
-    i32x4_t af[F / DT::KB], alo[F / DT::KB];
-#pragma unroll
-    for (int kb = 0; kb < F / DT::KB; ++kb) {
-      af[kb] = load_row_frag<DT>(&s_a[0][w][c][0], kb, g);
-      alo[kb] = DT::SPLIT ? load_row_frag<DT>(&s_a[NPART - 1][w][c][0], kb, g) : zero16();
-    }
-    const char* Wd = a.Wdn_p + (size_t)e * a.dn_stride;
-    typename DT::pair* yb = (typename DT::pair*)a.ybuf;
-    int slot[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rr = r0 + 4 * g + i;
-      slot[i] = rr < n_e ? lslot[rr] : -1;
-    }
-    for (int n4 = 0; n4 < a.pD / 4; ++n4) {
-      f32x4_t y[4];
-#pragma unroll
-      for (int p = 0; p < 4; ++p) y[p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < F / DT::KB; ++kb) {
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const i32x4_t wv = ld16(Wd + frag_off(n4 * 4 + p, kb, a.nkb_F) + (size_t)l * 16);
-          DT::mma(y[p], af[kb], wv);
-          if (DT::SPLIT) DT::mma(y[p], alo[kb], wv);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (slot[i] >= 0) {
-#pragma unroll
-          for (int p = 0; p < 4; ++p)
-            yb[(size_t)slot[i] * a.d + (n4 * 4 + p) * 16 + c] = (typename DT::pair)y[p][i];
-        }
-      }
-    }
-    __syncthreads();
   }
 }
 
 // --------------------------------------------------------------------------
+// out[t] = sum of token t's pair rows (its shared-expert output, then its
+// gated expert outputs in ascending expert order), in fp32, rounded once.
+// One thread per 8 output columns; loads batched four pair rows at a time.
 template <class DT>
-__global__ void __launch_bounds__(256) k_pre_shared_down(PreArgs a) {
+__global__ void __launch_bounds__(256) k_pre_combine(PreArgs a) {
   using elem = typename DT::elem;
-  constexpr int CH = 4;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, c = l & 15;
-  const int mt = blockIdx.x, nt = blockIdx.y;
-  const int row = mt * BM + w * 16 + c;
-  const bool row_ok = row < a.T;
-  const elem* srow = (const elem*)a.sbuf + (size_t)row * a.Fs;
-  f32x4_t acc[4];
+  using PT = typename DT::pair;
+  const int cpr = a.d / 8;
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  const int r = (int)(idx / cpr), col = (int)(idx % cpr) * 8;
+  if (r >= a.T) return;
+  const int s0 = a.tok_off[r], s1 = a.tok_off[r + 1];
+  const PT* yb = (const PT*)a.ybuf + col;
+  float v[8];
 #pragma unroll
-  for (int p = 0; p < 4; ++p) acc[p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int kb0 = 0; kb0 < a.nkb_Fs; kb0 += CH) {
-    i32x4_t sf[CH], wf[CH][4];
+  for (int k = 0; k < 8; ++k) v[k] = 0.f;
+  auto add = [&](const PT* p) {
+    if constexpr (sizeof(PT) == 2) {
+      const f16x8_t y = *reinterpret_cast<const f16x8_t*>(p);
 #pragma unroll
-    for (int u = 0; u < CH; ++u) {
-      const int kb = kb0 + u;
-      sf[u] = (kb < a.nkb_Fs && row_ok) ? load_row_frag<DT>(srow, kb, g) : zero16();
-#pragma unroll
-      for (int p = 0; p < 4; ++p)
-        wf[u][p] = kb < a.nkb_Fs ? ld16(a.Wsd_p + frag_off(nt * 4 + p, kb, a.nkb_Fs) + (size_t)l * 16) : zero16();
+      for (int k = 0; k < 8; ++k) v[k] += (float)y[k];
+    } else {
+      const float4 y0 = *reinterpret_cast<const float4*>(p);
+      const float4 y1 = *reinterpret_cast<const float4*>(p + 4);
+      v[0] += y0.x; v[1] += y0.y; v[2] += y0.z; v[3] += y0.w;
+      v[4] += y1.x; v[5] += y1.y; v[6] += y1.z; v[7] += y1.w;
     }
+  };
+  int s = s0;
+  for (; s + 4 <= s1; s += 4) {
+    // four independent loads in flight, added in slot order
+    if constexpr (sizeof(PT) == 2) {
+      f16x8_t y[4];
 #pragma unroll
-    for (int u = 0; u < CH; ++u)
+      for (int u = 0; u < 4; ++u) y[u] = *reinterpret_cast<const f16x8_t*>(yb + (size_t)(s + u) * a.d);
 #pragma unroll
-      for (int p = 0; p < 4; ++p) DT::mma(acc[p], sf[u], wf[u][p]);
-  }
-  const typename DT::pair* yb = (const typename DT::pair*)a.ybuf;
-  elem* out = (elem*)a.out;
+      for (int u = 0; u < 4; ++u)
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = mt * BM + w * 16 + 4 * g + i;
-    if (r < a.T) {
-      float v[4];
+        for (int k = 0; k < 8; ++k) v[k] += (float)y[u][k];
+    } else {
 #pragma unroll
-      for (int p = 0; p < 4; ++p) v[p] = acc[p][i];
-      // the token's pair slots hold its active experts in ascending order
-      int sl = a.tok_off[r];
-      for (int wi = 0; wi < a.W; ++wi) {
-        uint64_t m = a.mask[(size_t)r * a.W + wi];
-        while (m) {
-          const int e = wi * 64 + __ffsll((unsigned long long)m) - 1;
-          m &= m - 1;
-          const float gate = a.g[(size_t)r * a.E + e];
-          const typename DT::pair* yrow = yb + (size_t)sl * a.d + nt * 64 + c;
-#pragma unroll
-          for (int p = 0; p < 4; ++p) v[p] += gate * (float)yrow[p * 16];
-          ++sl;
-        }
-      }
-#pragma unroll
-      for (int p = 0; p < 4; ++p) out[(size_t)r * a.d + (nt * 4 + p) * 16 + c] = DT::from_f32(v[p]);
+      for (int u = 0; u < 4; ++u) add(yb + (size_t)(s + u) * a.d);
     }
   }
+  for (; s < s1; ++s) add(yb + (size_t)s * a.d);
+  elem* orow = (elem*)a.out + (size_t)r * a.d + col;
+  store4<DT>(orow, v[0], v[1], v[2], v[3]);
+  store4<DT>(orow + 4, v[4], v[5], v[6], v[7]);
 }
 
 // --------------------------------------------------------------------------
@@ -425,6 +625,15 @@ __global__ void __launch_bounds__(256) k_copy_mask(const float* __restrict__ z, 
   }
   mask[idx] = word;
 }
+
+template <class DT>
+void (*expert_kernel(int pF))(PreArgs) {
+  return pF == 2 ? k_pre_expert<DT, 2>
+       : pF == 4 ? k_pre_expert<DT, 4>
+       : pF == 8 ? k_pre_expert<DT, 8> : k_pre_expert<DT, 16>;
+}
+
+int round4(int v) { return (v + 3) / 4 * 4; }
 
 template <class DT>
 hipError_t prefill(const deco_moe_layer* L, const void* x, int T, void* out, hipStream_t s) {
@@ -445,6 +654,9 @@ hipError_t prefill(const deco_moe_layer* L, const void* x, int T, void* out, hip
   a.pF = L->pF;
   a.pD = L->pD;
   a.pFs = L->pFs;
+  a.pF4 = round4(L->pF);
+  a.pFs4 = round4(L->pFs);
+  a.rs_nt = (a.pR + a.pF4 + a.pFs4 + GP - 1) / GP;
   a.Wr_p = L->Wr_p;
   a.Wup_p = L->Wup_p;
   a.Wbar_p = L->Wbar_p;
@@ -463,24 +675,20 @@ hipError_t prefill(const deco_moe_layer* L, const void* x, int T, void* out, hip
   a.tok_off = L->tok_off;
   a.ecnt = L->ecnt;
   a.list_tok = L->list_tok;
-  a.list_slot = L->list_slot;
+  a.Wdn16_p = L->Wdn16_p;
   a.sbuf = L->sbuf;
   a.ybuf = L->ybuf;
-  const unsigned mtiles = (unsigned)((T + BM - 1) / BM);
-  const unsigned ntiles = (unsigned)(L->pR / 4 + (L->pF + 3) / 4 + (L->pFs + 3) / 4);
+  const unsigned mtiles = (unsigned)((T + GM - 1) / GM);
   using deco_host::launch;
-  hipError_t err = launch(deco_host::KS_PRE_ROUTER_SHARED, k_pre_router_shared<DT>, dim3(mtiles, ntiles),
+  hipError_t err = launch(deco_host::KS_PRE_ROUTER_SHARED, k_pre_router_shared<DT>, dim3(mtiles * a.rs_nt),
                           dim3(256), s, a);
-  if (err == hipSuccess) err = launch(deco_host::KS_PRE_DISPATCH, k_pre_dispatch, dim3(L->E), dim3(256), s, a);
-  if (err == hipSuccess) {
-    void (*kx)(PreArgs) = L->pF == 2 ? k_pre_expert<DT, 2>
-                        : L->pF == 4 ? k_pre_expert<DT, 4>
-                        : L->pF == 8 ? k_pre_expert<DT, 8> : k_pre_expert<DT, 16>;
-    err = launch(deco_host::KS_PRE_EXPERT, kx, dim3(L->pre_grid), dim3(256), s, a);
-  }
   if (err == hipSuccess)
-    err = launch(deco_host::KS_PRE_SHARED_DOWN, k_pre_shared_down<DT>, dim3(mtiles, (unsigned)(L->pD / 4)),
-                 dim3(256), s, a);
+    err = launch(deco_host::KS_PRE_DISPATCH, k_pre_dispatch, dim3(L->E + 1), dim3(DISP_NT), s, a);
+  if (err == hipSuccess)
+    err = launch(deco_host::KS_PRE_EXPERT, expert_kernel<DT>(L->pF), dim3(L->pre_grid), dim3(256), s, a);
+  if (err == hipSuccess)
+    err = launch(deco_host::KS_PRE_COMBINE, k_pre_combine<DT>,
+                 dim3((unsigned)(((long long)T * (L->d / 8) + 255) / 256)), dim3(256), s, a);
   if (err != hipSuccess) return err;
   return hipGetLastError();
 }
@@ -492,6 +700,20 @@ namespace deco_host {
 hipError_t launch_prefill(const deco_moe_layer* L, const void* x, int T, void* out, hipStream_t s) {
   if (L->cfg.dtype == DECO_DT_BF16) return prefill<BF16>(L, x, T, out, s);
   return prefill<F32>(L, x, T, out, s);
+}
+
+// Persistent grid of the expert kernel: as many workgroups as fit on the
+// device at once, a multiple of the 8 XCDs.
+hipError_t plan_prefill(deco_moe_layer* L) {
+  void (*kx)(PreArgs) = L->cfg.dtype == DECO_DT_BF16 ? expert_kernel<BF16>(L->pF) : expert_kernel<F32>(L->pF);
+  int occ = 0, cus = 0;
+  hipError_t err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kx, 256, 0);
+  if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, L->device);
+  if (err != hipSuccess) return err;
+  int grid = (occ < 1 ? 1 : occ) * (cus < 1 ? 1 : cus);
+  grid = (grid + NXCD - 1) / NXCD * NXCD;
+  L->pre_grid = grid;
+  return hipSuccess;
 }
 
 hipError_t launch_copy_mask(const deco_moe_layer* L, int T, uint64_t* mask, hipStream_t s) {
