@@ -59,10 +59,10 @@ struct deco_moe_layer {
   int* ecnt;               // [E]
   int* list_tok;           // [E][Tcap]
   char* sbuf;              // [Tcap][Fs] shared activations (dtype)
-  char* ybuf;              // [Tcap * (E + 1)][d] pair buffer, token-major: per token its
+  char* ybuf;              // [Tcap * (E + 1) + 1][d] pair buffer, token-major: per token its
                            // shared-expert output, then gate * expert output for each
                            // active expert in ascending order (fp16 for bf16 layers,
-                           // fp32 for fp32 layers)
+                           // fp32 for fp32 layers); the last row is scratch
 };
 
 namespace deco_host {

@@ -2,19 +2,23 @@
 //
 // A workgroup of 4 waves computes a BM x (16*BNP) tile of C += A.B, with the
 // waves in a 2 x 2 grid (each wave: BM/2 rows x BNP/2 panels).  K advances in
-// steps of KS k-blocks through a ring of NS stages in LDS.  Operands go from
-// global memory straight into LDS (global_load_lds_dwordx4: each lane's 16
-// bytes land at its own 16-byte slot of a 1 KiB block), already in MFMA
-// fragment order (the layout of deco_common.h):
-//   A: row-major rows (any row addresses: gathered or strided); the lane that
-//      serves row r and lane group g of a fragment loads the EPL consecutive
-//      elements k = EPL g .. of row r of that k-block;
-//   B: weights packed in fragment order (16-column panels of 1 KiB k-blocks),
-//      copied as is.
-// So no operand passes through registers on its way in, every LDS read is a
-// conflict-free 16-byte ds_read over 1 KiB, and NS - 1 steps of loads are in
-// flight while one step computes.  Waits are explicit vmcnt counts (each wave
-// issues the same number of loads per step) followed by a plain s_barrier.
+// steps of 2 k-blocks (128 bytes of each A row) through a ring of NS stages
+// in LDS.  Operands go from global memory straight into LDS
+// (global_load_lds_dwordx4: lane l's 16 bytes land at 16-byte slot l of a
+// 1 KiB block):
+//   A: row-major rows (any row addresses: gathered or strided).  One block
+//      holds 8 rows x 128 bytes, so each load instruction reads 8 whole
+//      128-byte lines.  Slot 8 r + s of a block holds 16-byte chunk s ^ r of
+//      row r (an XOR swizzle): the 8 lanes that read chunk j of 8 different
+//      rows hit 8 different bank groups.
+//   B: weights packed in MFMA fragment order (16-column panels of 1 KiB
+//      k-blocks, deco_common.h), copied as is.
+// No operand passes through registers on its way in, and NS - 1 steps of
+// loads are in flight while one step computes.  Waits are explicit vmcnt
+// counts (each wave issues the same number of loads per step) followed by an
+// LDS-only barrier.  A kernel using the tile keeps all its LDS in one array:
+// the compiler cannot tell the LDS-DMA writes of one array from reads of
+// another and would otherwise wait for every DMA before every LDS read.
 #pragma once
 
 #include "deco_common.h"
@@ -23,13 +27,13 @@ namespace deco {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-template <class DT, int BM_, int BNP_, int KS_, int NS_>
+template <class DT, int BM_, int BNP_, int NS_>
 struct Tile {
   static constexpr int NT = 256;                  // threads per workgroup
-  static constexpr int BM = BM_, BNP = BNP_, KS = KS_, NS = NS_;
+  static constexpr int BM = BM_, BNP = BNP_, KS = 2, NS = NS_;
   static constexpr int MB = BM / 32;              // 16-row blocks per wave
   static constexpr int NBW = BNP / 2;             // panels per wave
-  static constexpr int NA = (BM / 16) * KS;       // A fragments per step
+  static constexpr int NA = BM / 8;               // A blocks (8 rows x 128 bytes) per step
   static constexpr int NB = BNP * KS;             // B fragments per step
   static constexpr int NAW = NA / 4, NBL = NB / 4;   // per wave
   static constexpr int LPW = NAW + NBL;           // loads per wave per step
@@ -38,7 +42,8 @@ struct Tile {
   static constexpr int STAGE_V = A_V + B_V;
   static constexpr int LDS_V = NS * STAGE_V;      // slots of the whole ring
   static_assert(BM % 32 == 0 && BNP % 2 == 0, "tile shape");
-  static_assert(NA % 4 == 0 && NB % 4 == 0, "fragments must divide over the 4 waves");
+  static_assert(NA % 4 == 0 && NB % 4 == 0, "blocks must divide over the 4 waves");
+  static_assert(KS * DT::KB * sizeof(typename DT::elem) == 128, "a step covers 128 bytes of an A row");
   static_assert(NS >= 2, "at least two stages");
 };
 
@@ -48,6 +53,20 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for LDS hand-offs.  It waits for this wave's LDS reads
+// and writes (lgkmcnt 0) but not for its global loads, stores or LDS-DMA
+// loads: a memory fence (__syncthreads(), or even an LDS-only fence, since
+// DMA loads in flight are pending LDS writes) would wait for all of those
+// and empty every prefetch ring at every barrier.  Where a DMA stage must
+// have landed, the caller waits for it with wait_vmcnt first.  The empty asm
+// statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt unconstrained
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
 }
 
 __device__ __forceinline__ void load_lds16(const void* src, i32x4_t* lds_block) {
@@ -69,7 +88,12 @@ __device__ __forceinline__ void tile_mma(const i32x4_t* lds_a, const i32x4_t* ld
     if (kb < kb_lim) {
       i32x4_t av[TC::MB], bv[TC::NBW];
 #pragma unroll
-      for (int i = 0; i < TC::MB; ++i) av[i] = lds_a[((wm * TC::MB + i) * TC::KS + kb) * 64 + l];
+      for (int i = 0; i < TC::MB; ++i) {
+        // row 16 (wm*MB + i) + c lives in block 2 (wm*MB + i) + c / 8 at row c % 8;
+        // this lane's chunk is k-block kb, quarter g
+        const int c = l & 15, rl = c & 7;
+        av[i] = lds_a[(2 * (wm * TC::MB + i) + (c >> 3)) * 64 + rl * 8 + ((kb * 4 + (l >> 4)) ^ rl)];
+      }
 #pragma unroll
       for (int j = 0; j < TC::NBW; ++j) bv[j] = lds_b[((wn * TC::NBW + j) * TC::KS + kb) * 64 + l];
 #pragma unroll
@@ -97,13 +121,15 @@ __device__ __forceinline__ void tile_gemm(i32x4_t* lds, RowF row, PanelF panel, 
   using elem = typename DT::elem;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63, wm = w >> 1, wn = w & 1;
   const int nsteps = (nkb + TC::KS - 1) / TC::KS;
-  // this wave's fragments: A fa = w*NAW + i (row block fa / KS, k-block fa % KS),
-  // B fb = w*NBL + i (panel fb / KS, k-block fb % KS)
+  // this wave's loads: A blocks fa = w*NAW + i (rows 8 fa ..; lane l loads
+  // row 8 fa + l / 8, chunk ch = (l % 8) ^ (l / 8)), B fragments fb = w*NBL + i
+  // (panel fb / KS, k-block fb % KS)
+  const int ch = (l & 7) ^ (l >> 3);
   const elem* rp[TC::NAW];
 #pragma unroll
   for (int i = 0; i < TC::NAW; ++i) {
     const int fa = w * TC::NAW + i;
-    rp[i] = row((fa / TC::KS) * 16 + (l & 15)) + DT::EPL * (l >> 4);
+    rp[i] = row(8 * fa + (l >> 3)) + (ch & 3) * DT::EPL;
   }
   const char* pp[TC::NBL];
 #pragma unroll
@@ -113,13 +139,10 @@ __device__ __forceinline__ void tile_gemm(i32x4_t* lds, RowF row, PanelF panel, 
   }
   auto issue = [&](int s) {
     i32x4_t* st = lds + (s % TC::NS) * TC::STAGE_V;
+    int kba = s * TC::KS + (ch >> 2);
+    kba = kba < nkb ? kba : nkb - 1;   // past the end: a valid block, its MFMAs are skipped
 #pragma unroll
-    for (int i = 0; i < TC::NAW; ++i) {
-      const int fa = w * TC::NAW + i;
-      int kb = s * TC::KS + fa % TC::KS;
-      kb = kb < nkb ? kb : nkb - 1;   // past the end: a valid block, its MFMAs are skipped
-      load_lds16(rp[i] + kb * DT::KB, st + fa * 64);
-    }
+    for (int i = 0; i < TC::NAW; ++i) load_lds16(rp[i] + kba * DT::KB, st + (w * TC::NAW + i) * 64);
 #pragma unroll
     for (int i = 0; i < TC::NBL; ++i) {
       const int fb = w * TC::NBL + i;
@@ -137,12 +160,12 @@ __device__ __forceinline__ void tile_gemm(i32x4_t* lds, RowF row, PanelF panel, 
     // and shows that every wave has finished reading step s - 1's stage
     if (s + TC::NS - 2 < nsteps) wait_vmcnt<(TC::NS - 2) * TC::LPW>();
     else wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
+    lds_barrier();
     if (s + TC::NS - 1 < nsteps) issue(s + TC::NS - 1);
     const i32x4_t* st = lds + (s % TC::NS) * TC::STAGE_V;
     tile_mma<DT, TC, SWAP>(st, st + TC::A_V, acc, wm, wn, nkb - s * TC::KS);
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 }  // namespace deco

@@ -206,7 +206,8 @@ int deco_moe_load_weights(const deco_moe_config* cfg, const void* W_r, const flo
   size_t o_ec = k.take(sizeof(int) * E);
   size_t o_lt = k.take(sizeof(int) * (size_t)E * Tcap);
   size_t o_sb = k.take((size_t)L->esz * Tcap * L->Fs);
-  size_t o_yb = k.take((size_t)L->esz * Tcap * (E + 1) * L->d);
+  // pair buffer plus one scratch row that takes the stores of padding rows
+  size_t o_yb = k.take((size_t)L->esz * (Tcap * (E + 1) + 1) * L->d);
   L->ws_bytes = k.off;
 
   if (hipMalloc((void**)&L->wmem, L->wmem_bytes) != hipSuccess) {

@@ -66,18 +66,15 @@ struct PreArgs {
   void* ybuf;
 };
 
-#ifndef DECO_PRE_KS
-#define DECO_PRE_KS 1     // k-blocks per pipeline step
-#endif
 #ifndef DECO_PRE_NS
-#define DECO_PRE_NS 4     // pipeline stages in LDS
+#define DECO_PRE_NS 2     // pipeline stages in LDS (32 KiB each for the dense tiles)
 #endif
 
 constexpr int NXCD = 8;
 constexpr int GM = 128;   // rows of the dense GEMM tiles
 constexpr int GP = 8;     // 16-column panels of the dense GEMM tiles
 template <class DT>
-using DenseTile = Tile<DT, GM, GP, DECO_PRE_KS, DECO_PRE_NS>;
+using DenseTile = Tile<DT, GM, GP, DECO_PRE_NS>;
 
 // Workgroups are handed to the 8 XCDs round-robin (workgroup b runs on XCD
 // b % 8).  Renumber them so each XCD works on one contiguous range of tiles:
@@ -294,9 +291,7 @@ template <class DT, int BNP>
 struct ExpertShape {
   using DN = typename DT::Down;                      // down-projection operand type
   static constexpr int BM = BNP >= 16 ? 64 : 128;    // token rows per tile
-  // up-projection ring: one k-block per step (two for F = 32, so that the
-  // 2 panels' fragments divide over the 4 waves)
-  using TC = Tile<DT, BM, BNP, (BNP == 2 ? 2 : 1), (BNP == 2 || BNP >= 16 ? 3 : 4)>;
+  using TC = Tile<DT, BM, BNP, DECO_PRE_NS>;          // up-projection ring
   static constexpr int F = BNP * 16;
   static constexpr int NKF = F / DN::KB;             // k-blocks of the down-projection
   static constexpr int RB = BM / 16;                 // 16-row blocks of the tile
@@ -304,11 +299,24 @@ struct ExpertShape {
   static constexpr int ACT_V = RB * NKF * 64;        // 16-byte LDS slots of the activations
   static constexpr int DP = NKF >= 8 ? 2 : 4;        // W_down panels per ring stage
   static constexpr int DSTAGE_V = DP * NKF * 64;
-  static constexpr int DNS = DSTAGE_V <= 1024 ? 4 : 2;   // ring stages (16 KiB stages: 4)
+  static constexpr int DNS = 3;                      // ring stages
   static constexpr int DLPW = DP * NKF / 4;          // ring loads per wave per stage
+  // output staging: the gated pair values of one ring stage (BM tokens x
+  // 16 DP columns) go through LDS so that global stores write whole rows.
+  // 16-byte chunk q of staged row R sits at slot R*OCH + (q ^ (R % OCH)).
+  using PT = typename DT::pair;
+  static constexpr int OROW = DP * 16 * (int)sizeof(PT);   // bytes of one staged row
+  static constexpr int OCH = OROW / 16;                    // 16-byte chunks per staged row
+  static constexpr int OBUF_V = BM * OCH;
+  static constexpr int FPT = BM * OCH / 256;               // staged-row stores per thread
+  static_assert(BM * OCH % 256 == 0 && (OCH & (OCH - 1)) == 0, "staged rows must divide over the workgroup");
   static constexpr int OCC = sizeof(typename DT::elem) == 2 ? 2 : 1;   // workgroups per CU
   static constexpr int cmax(int x, int y) { return x > y ? x : y; }
-  static constexpr int LDS_V = cmax(cmax(TC::LDS_V, ACT_V), cmax(DNS * DSTAGE_V, DenseTile<DT>::LDS_V));
+  // shared tiles stage their 128 x 128 output the same way
+  static constexpr int SPITCH_V = GP * 16 * (int)sizeof(PT) / 16 + 1;
+  static constexpr int LDS_V = cmax(cmax(TC::LDS_V, ACT_V),
+                                    cmax(DNS * DSTAGE_V + OBUF_V,
+                                         cmax(DenseTile<DT>::LDS_V, GM * SPITCH_V)));
   static_assert((DP * NKF) % 4 == 0, "ring fragments must divide over the 4 waves");
 };
 
@@ -328,13 +336,17 @@ __global__ void __launch_bounds__(256, (ExpertShape<DT, BNP>::OCC)) k_pre_expert
   using DN = typename S::DN;
   using PT = typename DT::pair;
   constexpr int BM = S::BM, MB = S::MB, NBW = TC::NBW, F = S::F, NKF = S::NKF, DP = S::DP;
-  __shared__ i32x4_t lds[S::LDS_V];
-  __shared__ int s_toff[257];
-  __shared__ int s_tmp[4];
-  __shared__ int s_tok[BM];
-  __shared__ int s_slot[BM];
-  __shared__ float s_gate[BM];
-  __shared__ float s_ss[2][BM];
+  // one LDS array for everything (the operand rings, the activations, the
+  // staging buffer and the per-tile tables), carved below
+  constexpr int SMALL_V = (257 + 4 + 3 * BM + 2 * BM + 3) / 4;
+  __shared__ i32x4_t lds_all[S::LDS_V + SMALL_V];
+  i32x4_t* lds = lds_all;
+  int* s_toff = reinterpret_cast<int*>(lds_all + S::LDS_V);
+  int* s_tmp = s_toff + 257;
+  int* s_tok = s_tmp + 4;
+  int* s_slot = s_tok + BM;
+  float* s_gate = reinterpret_cast<float*>(s_slot + BM);
+  float (*s_ss)[BM] = reinterpret_cast<float (*)[BM]>(s_gate + BM);
   const int tid = threadIdx.x, w = tid >> 6, wm = w >> 1, wn = w & 1, l = tid & 63, g = l >> 4, c = l & 15;
 
   // expert e owns tiles s_toff[e] .. s_toff[e + 1] - 1
@@ -359,7 +371,7 @@ __global__ void __launch_bounds__(256, (ExpertShape<DT, BNP>::OCC)) k_pre_expert
   PT* yb = (PT*)a.ybuf;
 
   for (int k = lb; k < n_mine; k += gx) {
-    __syncthreads();   // the previous tile no longer reads LDS
+    lds_barrier();   // the previous tile no longer reads LDS
     if (k >= e_end - e_beg) {
       // ---- shared tile: rows m0.., panels p0.. of SiLU(x Ws_up) . Ws_down
       using TD = DenseTile<DT>;
@@ -379,17 +391,22 @@ __global__ void __launch_bounds__(256, (ExpertShape<DT, BNP>::OCC)) k_pre_expert
 #pragma unroll
         for (int j = 0; j < TD::NBW; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       tile_gemm<DT, TD, true>(lds, row, panel, a.nkb_Fs, acc);
-      const int q0 = p0 + wn * TD::NBW;
-      if (q0 < a.pD) {   // pD is a multiple of 4: a wave's 4 panels are all valid or all padding
+      // stage the tile (pair type) in LDS, then store whole rows
+      constexpr int SP = S::SPITCH_V;
 #pragma unroll
-        for (int i = 0; i < TD::MB; ++i) {
-          const int r = m0 + wm * (GM / 2) + 16 * i + c;
-          if (r < a.T) {
-            PT* dst = yb + (size_t)a.tok_off[r] * a.d + q0 * 16 + 4 * g;
+      for (int i = 0; i < TD::MB; ++i) {
+        const int R = wm * (GM / 2) + 16 * i + c;
 #pragma unroll
-            for (int j = 0; j < TD::NBW; ++j) store4_pair(dst + j * 16, acc[i][j]);
-          }
-        }
+        for (int j = 0; j < TD::NBW; ++j)
+          store4_pair(reinterpret_cast<PT*>(lds + R * SP) + (wn * TD::NBW + j) * 16 + 4 * g, acc[i][j]);
+      }
+      lds_barrier();
+      constexpr int CPR = GP * 16 * (int)sizeof(PT) / 16;   // 16-byte chunks per row
+      const int ncol_ch = (a.pD - p0 < GP ? a.pD - p0 : GP) * 16 * (int)sizeof(PT) / 16;
+      for (int idx = tid; idx < GM * CPR; idx += 256) {
+        const int R = idx / CPR, q = idx % CPR, r = m0 + R;
+        if (r < a.T && q < ncol_ch)
+          st16(reinterpret_cast<char*>(yb + (size_t)a.tok_off[r] * a.d + p0 * 16) + q * 16, lds[R * SP + q]);
       }
       continue;
     }
@@ -421,7 +438,7 @@ __global__ void __launch_bounds__(256, (ExpertShape<DT, BNP>::OCC)) k_pre_expert
       s_slot[tid] = slot;
       s_gate[tid] = gate;
     }
-    __syncthreads();
+    lds_barrier();
 
     // up-projection of the gathered rows, all F columns
     const char* Wu = a.Wup_p + (size_t)e * a.up_stride;
@@ -461,7 +478,7 @@ __global__ void __launch_bounds__(256, (ExpertShape<DT, BNP>::OCC)) k_pre_expert
       ss += __shfl_xor(ss, 32);
       if (g == 0) s_ss[wn][R] = ss;
     }
-    __syncthreads();
+    lds_barrier();
     // activations into LDS in the fragment order of the down-projection's
     // token operand (rounded once to the operand type)
 #pragma unroll
@@ -488,7 +505,7 @@ __global__ void __launch_bounds__(256, (ExpertShape<DT, BNP>::OCC)) k_pre_expert
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
     // each wave keeps the activations of its token blocks in registers
     i32x4_t act[MB][NKF];
 #pragma unroll
@@ -496,13 +513,9 @@ __global__ void __launch_bounds__(256, (ExpertShape<DT, BNP>::OCC)) k_pre_expert
 #pragma unroll
       for (int kb = 0; kb < NKF; ++kb) act[jt][kb] = lds[((wm * MB + jt) * NKF + kb) * 64 + l];
     float gt[MB];
-    int sl[MB];
 #pragma unroll
-    for (int jt = 0; jt < MB; ++jt) {
-      gt[jt] = s_gate[wm * (BM / 2) + 16 * jt + c];
-      sl[jt] = s_slot[wm * (BM / 2) + 16 * jt + c];
-    }
-    __syncthreads();   // every wave holds its activations: the LDS becomes the W_down ring
+    for (int jt = 0; jt < MB; ++jt) gt[jt] = s_gate[wm * (BM / 2) + 16 * jt + c];
+    lds_barrier();   // every wave holds its activations: the LDS becomes the W_down ring
 
     // down-projection through a ring of DP-panel stages of W_down[e] (all
     // NKF k-blocks of each panel); wave (wm, wn) takes its token blocks and
@@ -510,6 +523,8 @@ __global__ void __launch_bounds__(256, (ExpertShape<DT, BNP>::OCC)) k_pre_expert
     // operand): a lane holds 4 consecutive output columns of one token.
     const char* Wd = a.Wdn16_p + (size_t)e * a.dn_stride;
     const int nds = a.pD / DP;
+    i32x4_t* obuf = lds + S::DNS * S::DSTAGE_V;   // staging buffer after the ring
+    constexpr int OCH = S::OCH;
     auto issue = [&](int st) {
       i32x4_t* ring = lds + (st % S::DNS) * S::DSTAGE_V;
 #pragma unroll
@@ -518,14 +533,39 @@ __global__ void __launch_bounds__(256, (ExpertShape<DT, BNP>::OCC)) k_pre_expert
         load_lds16(Wd + frag_off(st * DP + f / NKF, f % NKF, NKF) + l * 16, ring + f * 64);
       }
     };
+    // copy the staged stage `st` (BM rows x OROW bytes) to the tokens' pair
+    // rows.  Exactly FPT stores per thread, none skipped (padding rows go to
+    // the scratch row after the pair buffer), so the vmcnt waits below can
+    // leave the latest stores in flight.
+    const size_t trash = (size_t)a.Tcap * (a.E + 1);
+    auto flush = [&](int st) {
 #pragma unroll
-    for (int st = 0; st < S::DNS - 1; ++st)
-      if (st < nds) issue(st);
+      for (int u = 0; u < S::FPT; ++u) {
+        const int idx = tid + 256 * u, R = idx / OCH, q = idx % OCH, slot = s_slot[R];
+        st16(reinterpret_cast<char*>(yb + (slot >= 0 ? (size_t)slot : trash) * a.d + st * DP * 16) + q * 16,
+             obuf[R * OCH + (q ^ (R & (OCH - 1)))]);
+      }
+    };
+    static_assert(S::DNS == 3, "the vmcnt counts below assume a 3-stage ring");
+    // Per iteration st the memory operations are: flush(st - 1) (FPT stores),
+    // then the loads of stage st + 2.  So after the loads of stage st come:
+    // st = 0: stage 1's loads; st = 1: stage 2's; st >= 2: the stores of
+    // flush(st - 2) and stage st + 1's loads (those that exist).
+    auto wait_stage = [&](int st) {
+      const bool next = st + 1 < nds;
+      if (st < 2) {
+        if (next) wait_vmcnt<S::DLPW>(); else wait_vmcnt<0>();
+      } else {
+        if (next) wait_vmcnt<S::FPT + S::DLPW>(); else wait_vmcnt<S::FPT>();
+      }
+    };
+    if (nds > 0) issue(0);
+    if (nds > 1) issue(1);
     for (int st = 0; st < nds; ++st) {
-      if (st + S::DNS - 2 < nds) wait_vmcnt<(S::DNS - 2) * S::DLPW>();
-      else wait_vmcnt<0>();
-      __builtin_amdgcn_s_barrier();
-      if (st + S::DNS - 1 < nds) issue(st + S::DNS - 1);
+      wait_stage(st);
+      lds_barrier();   // stage st landed; staged st - 1 complete; ring stage st - 1 free
+      if (st > 0) flush(st - 1);
+      if (st + 2 < nds) issue(st + 2);
       const i32x4_t* ring = lds + (st % S::DNS) * S::DSTAGE_V;
       f32x4_t y[MB][DP / 2];
 #pragma unroll
@@ -542,22 +582,27 @@ __global__ void __launch_bounds__(256, (ExpertShape<DT, BNP>::OCC)) k_pre_expert
 #pragma unroll
           for (int q = 0; q < DP / 2; ++q) DN::mma(y[jt][q], bv[q], act[jt][kb]);
       }
+      lds_barrier();   // flush(st - 1) has read the staging buffer
+      // gate, round to the pair type, stage: token R, columns (wn*DP/2 + q)*16 + 4 g ..
 #pragma unroll
       for (int jt = 0; jt < MB; ++jt) {
-        if (sl[jt] >= 0) {
-          PT* dst = yb + (size_t)sl[jt] * a.d + (st * DP + wn * (DP / 2)) * 16 + 4 * g;
+        const int R = wm * (BM / 2) + 16 * jt + c;
 #pragma unroll
-          for (int q = 0; q < DP / 2; ++q) {
-            f32x4_t v = y[jt][q];
-            v[0] *= gt[jt];
-            v[1] *= gt[jt];
-            v[2] *= gt[jt];
-            v[3] *= gt[jt];
-            store4_pair(dst + q * 16, v);
-          }
+        for (int q = 0; q < DP / 2; ++q) {
+          f32x4_t v = y[jt][q];
+          v[0] *= gt[jt];
+          v[1] *= gt[jt];
+          v[2] *= gt[jt];
+          v[3] *= gt[jt];
+          const int b = ((wn * (DP / 2) + q) * 16 + 4 * g) * (int)sizeof(PT);   // byte in the staged row
+          store4_pair(reinterpret_cast<PT*>(reinterpret_cast<char*>(obuf + R * OCH + ((b >> 4) ^ (R & (OCH - 1)))) +
+                                            (b & 15)),
+                      v);
         }
       }
     }
+    lds_barrier();
+    if (nds > 0) flush(nds - 1);
   }
 }
 
