@@ -190,6 +190,54 @@ def write_profile_summary(db: str, out: str, command: str):
     print("\n".join(lines))
 
 
+def write_pmc_summary(fetch_csv: str, write_csv: str, workload: str, cmd_fetch: str, cmd_write: str,
+                      calib_mib: int):
+    """HBM bytes per launch of each library kernel from two rocprofv3 --pmc
+    runs (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled by what
+    the same counter reads for a device copy of calib_mib MiB (read calib_mib,
+    write calib_mib) in the same run.  Writes profiles/<kernel>_<workload>_pmc.txt."""
+    import csv
+    import collections
+
+    def load(path, counter):
+        vals = collections.defaultdict(list)
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    vals[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return vals
+
+    fetch, write = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
+    calib_kib = calib_mib * 1024.0
+
+    def calib(vals):
+        copies = [v for k, vs in vals.items() if "copyBuffer" in k for v in vs]
+        return calib_kib / max(copies) if copies else None
+
+    ff, fw = calib(fetch), calib(write)
+    for k in KERNEL_SOURCES:
+        fk = [v for name, vs in fetch.items() if k in name for v in vs]
+        wk = [v for name, vs in write.items() if k in name for v in vs]
+        if not fk or not wk or ff is None or fw is None:
+            continue
+        f_kib, w_kib = sum(fk) / len(fk), sum(wk) / len(wk)
+        hbm = (f_kib * ff + w_kib * fw) * 1024.0
+        out = os.path.join(PROFILE_DIR, f"{k}_{workload}_pmc.txt")
+        lines = [f"# rocprofv3 PMC summary: HBM traffic of {k}, {workload} workload",
+                 f"command (FETCH_SIZE pass): {cmd_fetch}",
+                 f"command (WRITE_SIZE pass): {cmd_write}",
+                 f"calibration: device copy of {calib_mib} MiB in the same runs; "
+                 f"scale FETCH x{ff:.4f}, WRITE x{fw:.4f}",
+                 f"dispatches: {len(fk)} (fetch pass), {len(wk)} (write pass)",
+                 f"fetch_kib_per_dispatch_raw: {f_kib:.1f}",
+                 f"write_kib_per_dispatch_raw: {w_kib:.1f}",
+                 f"hbm_bytes_per_launch: {hbm:.0f}",
+                 f"source_sha256_16: {source_hash(k)}"]
+        with open(out, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -203,10 +251,19 @@ def main():
                     help="profiler mode: GPU loop of --workload only, no JSON")
     ap.add_argument("--profile-summary", nargs=3, metavar=("DB", "OUT", "COMMAND"),
                     help="write a text summary of a rocprofv3 kernel-trace database (no GPU needed)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="profiler mode: first copy this many MiB device to device (PMC calibration)")
+    ap.add_argument("--pmc-summary", nargs=6,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "WORKLOAD", "CMD_FETCH", "CMD_WRITE", "CALIB_MIB"),
+                    help="write profiles/<kernel>_<workload>_pmc.txt from two rocprofv3 --pmc runs")
     args = ap.parse_args()
 
     if args.profile_summary:
         write_profile_summary(*args.profile_summary)
+        return
+    if args.pmc_summary:
+        fc, wc, wl, cf, cw, mib = args.pmc_summary
+        write_pmc_summary(fc, wc, wl, cf, cw, int(mib))
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -223,6 +280,13 @@ def main():
     dm.load_library()
 
     if args.only_gpu_loop:
+        if args.calib_copy_mib:
+            src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            del src, dst
         L = make_layer(2) if args.workload == "decode" else make_layer(3)
         r = run_workload(L, args.steps, args.warmup)
         log(f"{args.workload}: {r['elapsed'] / args.steps * 1e6:.2f} us/step kernels={r['kernels']}")
