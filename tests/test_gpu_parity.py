@@ -21,6 +21,7 @@ import torch
 
 import oracle
 from synthetic import make_custom, make_layer
+from synthetic.gen import round_to_bf16
 from synthetic.device import layer_tensors, x_tensor
 
 pytestmark = pytest.mark.gpu
@@ -202,6 +203,25 @@ def test_shapes(shape, path):
     layer = _layer_obj(L, 80)
     check(L, ref, layer, dm.DECO_PATH_DECODE if path == "decode" else dm.DECO_PATH_PREFILL,
           label=f"shape{shape}")
+    layer.free()
+
+
+def test_changing_inputs_between_calls():
+    """Alternate different batches (and sizes) through one layer on both paths:
+    each call must match the oracle on its own input, so no value a kernel
+    hands from one workgroup to another can be left over from an earlier call
+    (the benchmark repeats one input, which would hide that)."""
+    base = make_custom(512, 24, 128, 256, 16, "bf16", seed=31, ratio=0.3)
+    rng = np.random.default_rng(77)
+    xb = round_to_bf16(rng.standard_normal((16, base.d)))
+    layer = _layer_obj(base, 64)
+    plan = [(base.x, 16, dm.DECO_PATH_DECODE), (xb, 9, dm.DECO_PATH_DECODE), (base.x, 16, dm.DECO_PATH_DECODE),
+            (xb, 16, dm.DECO_PATH_PREFILL), (base.x, 5, dm.DECO_PATH_PREFILL), (xb, 3, dm.DECO_PATH_DECODE),
+            (base.x, 16, dm.DECO_PATH_PREFILL)]
+    for k, (x, T, path) in enumerate(plan):
+        L = base.with_x(x[:T])
+        ref = oracle.forward(L.x, **L.weights(), eps=L.eps)
+        check(L, ref, layer, path, label=f"alternate-{k}")
     layer.free()
 
 
