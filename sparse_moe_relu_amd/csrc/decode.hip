@@ -462,9 +462,14 @@ hipError_t decode(const deco_moe_layer* L, const void* x, int T, void* out, hipS
 namespace deco_host {
 
 // Decode launch shape: the down kernel splits its reduction Q ways so that
-// about 512 workgroups stream the down-projection weights.
+// about DECO_DEC_DOWN_WG workgroups stream the down-projection weights (256
+// measured best on the d = 2048 layer among 128 .. 1024: fewer partials to
+// sum at the end, still one workgroup per CU streaming).
+#ifndef DECO_DEC_DOWN_WG
+#define DECO_DEC_DOWN_WG 256
+#endif
 hipError_t plan_decode(deco_moe_layer* L) {
-  int q = (512 + L->n_groups - 1) / L->n_groups;
+  int q = (DECO_DEC_DOWN_WG + L->n_groups - 1) / L->n_groups;
   L->dec_q = q < 1 ? 1 : (q > DEC_QMAX ? DEC_QMAX : q);
   L->dec_ok = 1;
   return hipSuccess;
