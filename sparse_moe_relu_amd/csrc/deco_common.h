@@ -68,8 +68,6 @@ struct BF16 {
   using elem = uint16_t;
   static constexpr int KB = 32;    // k per fragment
   static constexpr int EPL = 8;    // elements per lane
-  // gated expert activations enter the down-projection as hi + lo bf16 parts
-  static constexpr bool SPLIT = true;
   // per-(token, expert) outputs kept between the expert and combine kernels
   using pair = _Float16;
   // operand type of the prefill down-projection
@@ -103,7 +101,6 @@ struct F32 {
   using elem = float;
   static constexpr int KB = 16;
   static constexpr int EPL = 4;
-  static constexpr bool SPLIT = false;
   using pair = float;
   using Down = F32;
   __host__ __device__ static constexpr int frag_k(int g, int j) { return 4 * g + j; }
@@ -130,14 +127,6 @@ __device__ __forceinline__ void st16(void* p, const i32x4_t& v) { *reinterpret_c
 __device__ __forceinline__ i32x4_t zero16() { i32x4_t z = {0, 0, 0, 0}; return z; }
 
 __device__ __forceinline__ float silu_f(float v) { return v / (1.0f + __expf(-v)); }
-
-// v = hi + lo with hi = dtype(v), lo = dtype(v - hi): two bf16 products then
-// carry v to ~16 significant bits.  For fp32, lo is 0 and unused.
-template <class DT>
-__device__ __forceinline__ void split_hi_lo(float v, typename DT::elem& hi, typename DT::elem& lo) {
-  hi = DT::from_f32(v);
-  lo = DT::from_f32(v - DT::to_f32(hi));
-}
 
 // Operand fragment of row-major data: lane (c = l & 15, g) of k-block kb of
 // row `row` (elements kb*KB + frag_k(g, j)).

@@ -18,8 +18,9 @@ struct deco_moe_layer {
   int pR;                  // router panels (E padded to a multiple of 64, /16)
   int pF, pD, pFs;         // 16-column panels of F, d, Fs
   int W;                   // mask words per token = ceil(E/64)
-  int n_groups;            // d / 64 output column groups (decode down kernel)
-  int dec_q;               // reduction split of the decode down role
+  int n_groups;            // ceil(d / 128) output column groups (decode down kernel)
+  int dec_q;               // reduction split of the decode down kernel
+  int dec_multi;           // decode down kernel needs more than one chunk of units per wave
   int dec_ok;              // the decode path is available for this layer
   int pre_grid;            // persistent grid of the prefill expert kernel
 
@@ -46,14 +47,13 @@ struct deco_moe_layer {
   uint64_t* mask;          // [Tcap][W]
   // decode
   float* mbuf;             // [Tcap][F]    x . Wbar (NormSiLU mean term)
-  float* hbuf;             // [E][16][F]   raw up-projection rows
-  char* actf;              // [E][nkb_F][hi, lo] frags  gated NormSiLU output (A operand)
+  float* hbuf;             // [E][16][F]   h - m rows of each routed expert (decode)
+  float* sspart;           // [E][16][16]  per-slice sums of squares of h - m (decode)
   char* sactf;             // [nkb_Fs] frags      shared SiLU output
-  unsigned* eact;          // [E] expert touched by the batch
-  unsigned* cnt_up;        // [E] arrival counters (cleared by the down kernel)
+  unsigned* rflag;         // [E] routing of the last decode call (1 no token, 2 some token routed to e)
   unsigned* dec_err;       // [1] device-side error flags
-  unsigned* cnt_dn;        // [n_groups] arrival counters
-  float* part;             // [dec_q][n_groups][16][64] partial outputs
+  unsigned* cnt_dn;        // [n_groups] arrival counters of the decode down kernel
+  float* part;             // [dec_q][n_groups][16][128] partial outputs of the decode down kernel
   // prefill
   int* tok_off;            // [Tcap + 1]
   int* ecnt;               // [E]

@@ -5,31 +5,36 @@
 // point of ReLU routing with sparse experts is that inactive routed experts
 // cost nothing: the DECO paper (Sec. 1 and the Sec. 4 acceleration paragraph
 // with Table 4) attributes its speedup to skipping the memory traffic of
-// inactive experts.  Two kernels:
+// inactive experts.  Two kernels, with no workgroup waiting on another
+// except for the final sum of partial outputs:
 //
-//   k_dec_up   one workgroup per (routed expert, 32 columns of F), per 32
-//              columns of the inter-expert mean Wbar, and per 32 columns of
-//              the shared expert.  A routed workgroup first computes its
-//              expert's router logits for the batch (router: linear
+//   k_dec_up   one workgroup per 32 columns of the shared expert, and per
+//              (routed expert, 32 columns of F).  A routed workgroup computes
+//              its expert's router logits for the batch (router: linear
 //              projection + bias, ReLU, per-expert scale; DECO paper Sec. 2
-//              "Router design") and exits before touching any expert weight
-//              when no token activates the expert.  Otherwise it streams its
-//              slice of W_up[e] through v_mfma 16x16 products (tokens padded
-//              to 16 rows).  The Wbar workgroups compute the mean term
-//              m = x.Wbar once for all experts.  The last workgroup to finish
-//              the rows of an expert (counted per expert, the Wbar workgroups
-//              included) applies NormSiLU to the full F-wide rows
-//              (qidianchuan.cn write-up, section 二: subtract the mean term,
-//              RMS inside the expert, then SiLU), multiplies by the gate and
-//              stores the result as down-projection operand fragments, as a
-//              hi + lo pair of bf16 values.
-//   k_dec_down one workgroup per (64 output columns, 1/Q of the reduction).
-//              The reduction runs over the k-blocks of the experts that at
-//              least one token activated, then the shared expert; the last
-//              workgroup of a column group sums the Q partials in a fixed
-//              order (deterministic) and writes out.
+//              "Router design") while its slice of the inter-expert mean Wbar
+//              loads (one matrix shared by all experts, so it stays in L2),
+//              and exits without reading any expert weight when no token
+//              activated the expert.  Otherwise it streams its slice of
+//              W_up[e] through v_mfma 16x16 products (tokens padded to 16 rows)
+//              into the accumulator that already holds -x.Wbar: h - m, the
+//              mean-subtracted pre-activation of NormSiLU (qidianchuan.cn
+//              write-up, section 二: subtract the mean term, RMS inside the
+//              expert, then SiLU).  It stores h - m and the per-row sums of
+//              squares of its slice; the expert's first slice also stores the
+//              logits, the gates and the expert's routing flag.  Shared-expert
+//              workgroups store SiLU(x.Ws_up) as down-projection operands.
+//   k_dec_down one workgroup per (128 output columns, 1/Q of the reduction).
+//              It lists the experts at least one token activated, loads its
+//              share of their down-projection weights (and of the shared
+//              expert's), completes each row's RMS from the slices' sums of
+//              squares, applies SiLU and the gate while building the MFMA
+//              operands, multiplies, and the last workgroup of a column group
+//              sums the Q partials in a fixed order (deterministic) and
+//              writes out.
 #include "deco_common.h"
 #include "deco_internal.h"
+#include "gemm_tile.h"
 
 using namespace deco;
 
@@ -39,11 +44,12 @@ struct DecArgs {
   const void* x;
   void* out;
   int T, d, E, F, Fs;
-  int nkb_d, nkb_F, nkb_Fs, pF, pFs, n_groups, Q;
+  int nkb_d, nkb_F, nkb_Fs, pF, pFs, pD, n_groups, Q;
+  int n_shared, wg_per_e;   // up workgroups of the shared expert; per routed expert
   const char* Wr_p;
   const char* Wup_p;
   const char* Wbar_p;
-  const char* Wdn_p;
+  const char* Wdn_p;        // W_down in the operand type of the routed down-projection
   const char* Wsu_p;
   const char* Wsd_p;
   size_t up_stride, dn_stride;
@@ -52,13 +58,11 @@ struct DecArgs {
   float eps;
   float* z;
   float* g;
-  float* mbuf;
-  float* hbuf;
-  char* actf;
-  char* sactf;
-  unsigned* eact;
-  unsigned* cnt_up;
-  unsigned* cnt_dn;
+  float* hbuf;              // [E][16][F] h - m of each token row
+  float* sspart;            // [E][wg_per_e][16] sums of squares of h - m over each slice
+  char* sactf;              // shared-expert activations as down-projection operand fragments
+  unsigned* rflag;          // [E] 1 no token routed to e, 2 some token did
+  unsigned* cnt_dn;         // [n_groups] arrivals of a column group's workgroups
   float* part;
 };
 
@@ -72,170 +76,76 @@ struct DecArgs {
 #define DECO_DEC_CH 8
 #endif
 constexpr int DEC_NW = DECO_DEC_NW;   // waves per workgroup
-constexpr int DEC_NP = DECO_DEC_NP;   // 16-column panels per up-projection workgroup
+constexpr int DEC_NP = DECO_DEC_NP;   // 16-column panels per up workgroup
 constexpr int DEC_CH = DECO_DEC_CH;   // k-blocks held in registers per wave at a time
-constexpr int DEC_QMAX = 32;          // largest K-split of the down kernel (host clamps dec_q)
+constexpr int DEC_QMAX = 64;          // largest K-split of the down kernel (host clamps dec_q)
+constexpr int DEC_WGMAX = 8;          // largest number of up slices per routed expert
+constexpr int DEC_UB = 2;             // down-kernel units (k-blocks) in flight per wave
+constexpr int DEC_DP = 8;             // 16-column output panels per down workgroup
+constexpr int DEC_XMAX = 64;          // routed experts one down workgroup may touch (host plan)
+// A buffer-load offset past the resource's range: the load returns zeros
+// without touching memory (used to mask loads without branching).
+constexpr unsigned OOB = 0xFFFFFF00u;
 
-// NormSiLU of the 16 (padded) token rows of each expert in `list`, times the
-// gate, stored as down-projection operand fragments (hi, then lo for bf16).
-// Called by the workgroup that saw the experts' arrival counts reach their
-// target.  Rows are processed RB at a time per wave so their loads overlap.
-template <class DT, int NW>
-__device__ void dec_finalize(const DecArgs& a, const int* list, int n) {
-  using elem = typename DT::elem;
-  constexpr int RB = 4;
-  constexpr int NPART = DT::SPLIT ? 2 : 1;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const float invF = 1.0f / (float)a.F;
-  const int nrows = n * 16;
-  const __amdgpu_buffer_rsrc_t rg = dev_rsrc(a.g), rh = dev_rsrc(a.hbuf), rm = dev_rsrc(a.mbuf);
-  for (int r0 = w * RB; r0 < nrows; r0 += NW * RB) {
-    float hv[RB][4], mv[RB][4], gate[RB];
-#pragma unroll
-    for (int rr = 0; rr < RB; ++rr) {
-      const int r = r0 + rr;
-      const int e = r < nrows ? list[r >> 4] : 0, t = r & 15;
-      const bool ok = r < nrows;
-      // inactive pairs have g == 0; rows past T are padding
-      gate[rr] = (ok && t < a.T) ? ld_dev_buf(rg, 4u * (unsigned)(t * a.E + e)) : 0.f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int f = l + 64 * q;
-        const bool okf = ok && f < a.F;
-        hv[rr][q] = okf ? ld_dev_buf(rh, 4u * (unsigned)((e * 16 + t) * a.F + f)) : 0.f;
-        mv[rr][q] = okf ? ld_dev_buf(rm, 4u * (unsigned)(t * a.F + f)) : 0.f;
-      }
-    }
-#pragma unroll
-    for (int rr = 0; rr < RB; ++rr)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) hv[rr][q] -= mv[rr][q];
-#pragma unroll
-    for (int rr = 0; rr < RB; ++rr) {
-      const int r = r0 + rr;
-      if (r >= nrows) break;
-      const int e = list[r >> 4], t = r & 15;
-      float ss = 0.f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) ss += hv[rr][q] * hv[rr][q];
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
-      const float inv_r = 1.0f / sqrtf(ss * invF + a.eps);
-      char* act_e = a.actf + (size_t)e * a.nkb_F * NPART * FRAG_BYTES;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int f = l + 64 * q;
-        if (f < a.F) {
-          const float v = gate[rr] != 0.f ? silu_f(hv[rr][q] * inv_r) * gate[rr] : 0.f;
-          char* frag = act_e + (size_t)(f / DT::KB) * NPART * FRAG_BYTES + frag_elem_off<DT>(t, f % DT::KB);
-          elem hi, lo;
-          split_hi_lo<DT>(v, hi, lo);
-          *reinterpret_cast<elem*>(frag) = hi;
-          if (DT::SPLIT) *reinterpret_cast<elem*>(frag + FRAG_BYTES) = lo;
-        }
-      }
-    }
-  }
-  for (int k = tid; k < n; k += NW * 64) a.eact[list[k]] = 1u;
+// 16 bytes through a buffer resource: `soff` is wave-uniform (an SGPR), so a
+// run of such loads needs one VGPR for all its addresses
+__device__ __forceinline__ i32x4_t ld16_buf(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+  return __builtin_bit_cast(i32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+__device__ __forceinline__ float ld_buf(__amdgpu_buffer_rsrc_t r, unsigned voff) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, 0));
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7FFFFFFF, 0x00020000);
 }
 
 template <class DT, int NW, int NP>
 __global__ void __launch_bounds__(NW * 64) k_dec_up(DecArgs a) {
   using elem = typename DT::elem;
   constexpr int CH = DEC_CH;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, c = l & 15;
-  const int wg_per_e = a.pF / NP;        // workgroups per routed expert
-  const int n_wbar = a.pF / NP;          // workgroups of the mean term
-  const unsigned target = (unsigned)(wg_per_e + n_wbar);
-  // grid order: mean-term slices, shared-expert slices, then routed slices
-  // (the first two need no router result, so they stream from the start)
-  const int n_shared = a.pFs / NP;
+  static_assert(NP * 256 <= NW * 64, "one output entry per thread");
+  static_assert(NP <= 4, "s_red holds 4 panels per wave");
+  __shared__ float s_zred[NW][16];
+  __shared__ float s_ss[NP][16];
+  __shared__ f32x4_t s_red[NW][4][64];
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 4, c = l & 15;
+  // grid order: shared-expert slices (they need no router result, so they
+  // stream from the start), then (routed expert, slice)
   const int bid = blockIdx.x;
-  const int kind = bid < n_wbar ? 1 : (bid < n_wbar + n_shared ? 2 : 0);   // routed / mean / shared
-  const int rb = bid - n_wbar - n_shared;
-  const int e = kind == 0 ? rb / wg_per_e : 0;
-  const int p0 = kind == 0 ? (rb % wg_per_e) * NP : (kind == 1 ? bid * NP : (bid - n_wbar) * NP);
+  const bool routed = bid >= a.n_shared;
+  const int rb = bid - a.n_shared;
+  const int e = routed ? rb / a.wg_per_e : 0;
+  const int wgi = routed ? rb % a.wg_per_e : 0;
+  const int p0 = routed ? wgi * NP : bid * NP;
   const int nkb = a.nkb_d;
   const int kb_lo = (w * nkb) / NW, kb_hi = ((w + 1) * nkb) / NW;
   const elem* xrow = (const elem*)a.x + (size_t)c * a.d;
   const bool row_ok = c < a.T;
-
-  __shared__ float s_zred[NW][16];
-  __shared__ int s_last;
-  __shared__ int s_nfin;
-  __shared__ int s_fin[256];
-  __shared__ f32x4_t s_red[NW][NP][64];
+  const bool x_fits = kb_hi - kb_lo <= CH;   // the wave's x fragments fit in registers at once
 
   i32x4_t xf[CH];
-  if (kind == 0) {
-    // router logits of expert e for the 16 (padded) token rows
-    const float lam_e = a.lam[e];
-    const float b_e = a.b_r[e];
-    float zp = 0.f;
-    const char* wr = a.Wr_p + frag_off(e >> 4, 0, nkb) + (size_t)((e & 15) + 16 * g) * 16;
-    for (int kb0 = kb_lo; kb0 < kb_hi; kb0 += CH) {
-      i32x4_t wv[CH];
+  i32x4_t wf[CH][NP];
+  auto load_x = [&](int kb0) {
 #pragma unroll
-      for (int u = 0; u < CH; ++u) {
-        const int kb = kb0 + u;
-        xf[u] = (kb < kb_hi && row_ok) ? load_row_frag<DT>(xrow, kb, g) : zero16();
-        wv[u] = kb < kb_hi ? ld16(wr + (size_t)kb * FRAG_BYTES) : zero16();
-      }
-#pragma unroll
-      for (int u = 0; u < CH; ++u) {
-#pragma unroll
-        for (int j = 0; j < DT::EPL; ++j) zp += DT::lane_elem(xf[u], j) * DT::lane_elem(wv[u], j);
-      }
+    for (int u = 0; u < CH; ++u) {
+      const int kb = kb0 + u;
+      xf[u] = (kb < kb_hi && row_ok) ? load_row_frag<DT>(xrow, kb, g) : zero16();
     }
-    zp += __shfl_xor(zp, 16);
-    zp += __shfl_xor(zp, 32);
-    if (g == 0) s_zred[w][c] = zp;
-    __syncthreads();
-    // every thread forms the T logits itself (same order everywhere), so the
-    // activity decision needs no further barrier
-    bool any = false;
-    float z_mine = 0.f;
-    for (int t = 0; t < a.T; ++t) {
-      float zz = 0.f;
-#pragma unroll
-      for (int ww = 0; ww < NW; ++ww) zz += s_zred[ww][t];
-      zz += b_e;
-      any |= zz > 0.f && lam_e != 0.f;
-      if (t == tid) z_mine = zz;
-    }
-    if (p0 == 0 && tid < a.T) {
-      const bool act = z_mine > 0.f && lam_e != 0.f;
-      a.z[(size_t)tid * a.E + e] = z_mine;
-      st_dev(&a.g[(size_t)tid * a.E + e], act ? lam_e * z_mine : 0.f);
-    }
-    if (!any) {
-      if (p0 == 0 && tid == 0) a.eact[e] = 0u;
-      return;  // inactive expert: none of its weights are read
-    }
-  }
-
-  // h[16 x (NP*16)] = x[16 x d] . Wslice[d x (NP*16)]
-  const char* wbase = kind == 0 ? a.Wup_p + (size_t)e * a.up_stride : (kind == 1 ? a.Wbar_p : a.Wsu_p);
-  const bool xf_valid = kind == 0 && (kb_hi - kb_lo <= CH);
-  f32x4_t acc[NP];
-#pragma unroll
-  for (int p = 0; p < NP; ++p) acc[p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int kb0 = kb_lo; kb0 < kb_hi; kb0 += CH) {
-    if (!xf_valid) {
-#pragma unroll
-      for (int u = 0; u < CH; ++u) {
-        const int kb = kb0 + u;
-        xf[u] = (kb < kb_hi && row_ok) ? load_row_frag<DT>(xrow, kb, g) : zero16();
-      }
-    }
-    i32x4_t wf[CH][NP];
+  };
+  auto load_w = [&](const char* wbase, int kb0) {
+    const __amdgpu_buffer_rsrc_t rw = buf_rsrc(wbase);
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
       const int kb = kb0 + u;
 #pragma unroll
       for (int p = 0; p < NP; ++p)
-        wf[u][p] = kb < kb_hi ? ld16(wbase + frag_off(p0 + p, kb, nkb) + (size_t)l * 16) : zero16();
+        wf[u][p] = kb < kb_hi ? ld16_buf(rw, 16u * l, (unsigned)frag_off(p0 + p, kb, nkb)) : zero16();
     }
+  };
+  f32x4_t acc[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) acc[p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto mma_chunk = [&](int kb0) {
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
       if (kb0 + u < kb_hi) {
@@ -243,72 +153,130 @@ __global__ void __launch_bounds__(NW * 64) k_dec_up(DecArgs a) {
         for (int p = 0; p < NP; ++p) DT::mma(acc[p], xf[u], wf[u][p]);
       }
     }
+  };
+  // acc += x . (the NP panels at p0 of wbase) over this wave's k-range; xf
+  // and wf may already hold the first chunk's operands
+  auto stream = [&](const char* wbase, bool w0_loaded, bool x0_loaded) {
+    for (int kb0 = kb_lo; kb0 < kb_hi; kb0 += CH) {
+      if (!(x0_loaded && kb0 == kb_lo)) load_x(kb0);
+      if (!(w0_loaded && kb0 == kb_lo)) load_w(wbase, kb0);
+      mma_chunk(kb0);
+    }
+  };
+
+  if (routed) {
+    // router logits of expert e for the 16 (padded) token rows
+    const float lam_e = a.lam[e];
+    const float b_e = a.b_r[e];
+    float zp = 0.f;
+    const char* wr = a.Wr_p + frag_off(e >> 4, 0, nkb) + (size_t)((e & 15) + 16 * g) * 16;
+    for (int kb0 = kb_lo; kb0 < kb_hi; kb0 += CH) {
+      load_x(kb0);
+      i32x4_t wv[CH];
+#pragma unroll
+      for (int u = 0; u < CH; ++u) wv[u] = kb0 + u < kb_hi ? ld16(wr + (size_t)(kb0 + u) * FRAG_BYTES) : zero16();
+#pragma unroll
+      for (int u = 0; u < CH; ++u) {
+#pragma unroll
+        for (int j = 0; j < DT::EPL; ++j) zp += DT::lane_elem(xf[u], j) * DT::lane_elem(wv[u], j);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);   // keep the router's registers apart from the weights'
+    if (!x_fits) load_x(kb_lo);
+    // the mean-term weights load while the waves combine their logits
+    load_w(a.Wbar_p, kb_lo);
+    zp += __shfl_xor(zp, 16);
+    zp += __shfl_xor(zp, 32);
+    if (g == 0) s_zred[w][c] = zp;
+    lds_barrier();   // LDS only: the weight loads stay in flight
+    // every wave forms the logits itself (lane: token row c, same order
+    // everywhere), so the activity decision needs no further barrier
+    float zz = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) zz += s_zred[ww][c];
+    zz += b_e;
+    const bool act = c < a.T && zz > 0.f && lam_e != 0.f;
+    const bool any = __ballot(act) != 0ull;
+    if (wgi == 0 && w == 0) {
+      if (l == 0) a.rflag[e] = any ? 2u : 1u;
+      if (l < a.T) {
+        a.z[(size_t)l * a.E + e] = zz;
+        a.g[(size_t)l * a.E + e] = act ? lam_e * zz : 0.f;
+      }
+    }
+    if (!any) {
+      wait_all_mem();
+      return;  // inactive expert: none of its weights are read
+    }
+    // acc = -(x . Wbar) + x . W_up[e]: the NormSiLU mean term and the expert
+    // in one fp32 accumulator
+    stream(a.Wbar_p, true, true);
+    __builtin_amdgcn_sched_barrier(0);   // keep the two streams' registers apart
+#pragma unroll
+    for (int p = 0; p < NP; ++p) acc[p] = -acc[p];
+    // (with a single chunk per wave xf still holds it)
+    stream(a.Wup_p + (size_t)e * a.up_stride, false, x_fits);
+  } else {
+    stream(a.Wsu_p, false, false);
   }
+
+  // sum the waves' partial products: one (row, column) entry per thread
 #pragma unroll
   for (int p = 0; p < NP; ++p) s_red[w][p][l] = acc[p];
   __syncthreads();
-  for (int idx = tid; idx < NP * 64 * 4; idx += NW * 64) {
-    const int p = idx >> 8, ll = (idx >> 2) & 63, i = idx & 3;
-    float v = 0.f;
+  const bool mine = tid < NP * 256;
+  const int pp = tid >> 8, ll = (tid >> 2) & 63, i = tid & 3;
+  const int row = 4 * (ll >> 4) + i, col = (p0 + pp) * 16 + (ll & 15);
+  float v = 0.f;
+  if (mine) {
 #pragma unroll
-    for (int ww = 0; ww < NW; ++ww) v += s_red[ww][p][ll][i];
-    const int row = 4 * (ll >> 4) + i, col = (p0 + p) * 16 + (ll & 15);
-    if (kind == 0) {
-      st_dev(&a.hbuf[((size_t)e * 16 + row) * a.F + col], v);
-    } else if (kind == 1) {
-      st_dev(&a.mbuf[(size_t)row * a.F + col], v);
-    } else {
-      // shared expert: plain SiLU, stored as down-projection operand fragments
-      *reinterpret_cast<elem*>(a.sactf + frag_elem_off<DT>(row, col)) = DT::from_f32(silu_f(v));
-    }
+    for (int ww = 0; ww < NW; ++ww) v += s_red[ww][pp][ll][i];
   }
-  if (kind == 2) return;
-
-  // arrival counting: each expert finishes once its own slices and all the
-  // mean-term slices are written; that last workgroup applies NormSiLU
-  wait_all_mem();
+  if (!routed) {
+    // shared expert: plain SiLU, stored as down-projection operand fragments
+    if (mine) *reinterpret_cast<elem*>(a.sactf + frag_elem_off<DT>(row, col)) = DT::from_f32(silu_f(v));
+    return;
+  }
+  if (mine && row < a.T) a.hbuf[((size_t)e * 16 + row) * a.F + col] = v;
+  // per-row sum of squares over this slice: lanes with equal l & 3 of a wave
+  // hold one row (4 (w & 3) + (l & 3)) of panel w >> 2, columns l >> 2
+  float sq = v * v;
+  sq += __shfl_xor(sq, 4);
+  sq += __shfl_xor(sq, 8);
+  sq += __shfl_xor(sq, 16);
+  sq += __shfl_xor(sq, 32);
+  if (mine && l < 4) s_ss[pp][row] = sq;
   __syncthreads();
-  if (kind == 0) {
-    if (tid == 0) {
-      s_last = (arrive(&a.cnt_up[e]) == target - 1u) ? 1 : 0;
-      s_fin[0] = e;
-    }
-    __syncthreads();
-    if (!s_last) return;
-    dec_finalize<DT, NW>(a, s_fin, 1);
-  } else {
-    if (tid == 0) s_nfin = 0;
-    __syncthreads();
-    for (int ee = tid; ee < a.E; ee += NW * 64) {
-      if (arrive(&a.cnt_up[ee]) == target - 1u) s_fin[atomicAdd(&s_nfin, 1)] = ee;
-    }
-    __syncthreads();
-    const int nfin = s_nfin;
-    if (nfin > 0) dec_finalize<DT, NW>(a, s_fin, nfin);
+  if (tid < a.T) {
+    float ss = 0.f;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) ss += s_ss[p][tid];
+    a.sspart[((size_t)e * a.wg_per_e + wgi) * 16 + tid] = ss;
   }
 }
 
-template <class DT, int NW>
+template <class DT, int NW, bool MULTI>
 __global__ void __launch_bounds__(NW * 64) k_dec_down(DecArgs a) {
   using elem = typename DT::elem;
-  constexpr int UB = 4;  // units (k-blocks) in flight per wave
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const int grp = blockIdx.x % a.n_groups, q = blockIdx.x / a.n_groups;
-  constexpr int NPART = DT::SPLIT ? 2 : 1;
-  // the up kernel has completed: clear its per-expert arrival counters
-  if (blockIdx.x == 0)
-    for (int e = tid; e < a.E; e += NW * 64) st_dev_u32(&a.cnt_up[e], 0u);
-
+  using DN = typename DT::Down;   // operand type of the routed down-projection
+  constexpr int UB = DEC_UB;
+  constexpr int DP = DEC_DP;
+  constexpr int EPL = DT::EPL;
+  constexpr int NCOL = DP * 16;
   __shared__ int s_ulist[256];
   __shared__ int s_wcnt[4];
   __shared__ int s_nu;
   __shared__ int s_last;
+  __shared__ float s_rinv[DEC_XMAX * 16];
+  __shared__ float s_gate[DEC_XMAX * 16];
   __shared__ f32x4_t s_red[NW][4][64];
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, c = l & 15, g = l >> 4;
+  const int grp = blockIdx.x % a.n_groups, q = blockIdx.x / a.n_groups;
 
   // ascending list of the experts that at least one token activated
   const int nwE = (a.E + 63) >> 6;
   const int e_ = w * 64 + l;
-  const bool act = (w < nwE) && (e_ < a.E) && (a.eact[e_] != 0u);
+  const bool act = (w < nwE) && (e_ < a.E) && (a.rflag[e_] == 2u);
   const unsigned long long bal = __ballot(act);
   if (w < nwE && l == 0) s_wcnt[w] = __popcll(bal);
   __syncthreads();
@@ -327,67 +295,149 @@ __global__ void __launch_bounds__(NW * 64) k_dec_down(DecArgs a) {
   const int n_routed_units = nu * a.nkb_F;
   const int C = n_routed_units + a.nkb_Fs;
   const int lo = (int)(((long long)q * C) / a.Q), hi = (int)(((long long)(q + 1) * C) / a.Q);
+  // routed experts with units in [lo, hi): list entries i0 .. i0 + nx - 1
+  const int rhi = hi < n_routed_units ? hi : n_routed_units;
+  const int i0 = lo < rhi ? lo / a.nkb_F : 0;
+  const int nx = lo < rhi ? (rhi - 1) / a.nkb_F - i0 + 1 : 0;
 
-  f32x4_t acc[4];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) acc[p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int u0 = lo + w; u0 < hi; u0 += NW * UB) {
-    i32x4_t af[UB], al[UB], bfr[UB][4];
+  // weights of one chunk of this wave's units (k-blocks), straight to
+  // registers.  Panels past the last output column (d not a multiple of
+  // NCOL) read the last panel again and their results are dropped.
+  i32x4_t bfr[UB][DP];
+  auto load_b = [&](int u0) {
 #pragma unroll
     for (int ub = 0; ub < UB; ++ub) {
-      const int u = u0 + ub * NW;
-      if (u < hi) {
-        const char* A;
-        const char* B;
-        int kb, nkb;
-        if (u < n_routed_units) {
-          const int e = s_ulist[u / a.nkb_F];
-          kb = u % a.nkb_F;
-          nkb = a.nkb_F;
-          A = a.actf + ((size_t)e * a.nkb_F + kb) * NPART * FRAG_BYTES;
-          B = a.Wdn_p + (size_t)e * a.dn_stride;
-        } else {
-          kb = u - n_routed_units;
-          nkb = a.nkb_Fs;
-          A = a.sactf + (size_t)kb * FRAG_BYTES;
-          B = a.Wsd_p;
-        }
-        af[ub] = ld16(A + (size_t)l * 16);
-        al[ub] = (DT::SPLIT && u < n_routed_units) ? ld16(A + FRAG_BYTES + (size_t)l * 16) : zero16();
-#pragma unroll
-        for (int p = 0; p < 4; ++p) bfr[ub][p] = ld16(B + frag_off(grp * 4 + p, kb, nkb) + (size_t)l * 16);
+      const int u = u0 + ub * NW;   // wave-uniform
+      const char* B;
+      int kb, nkb;
+      if (u < rhi) {
+        kb = u % a.nkb_F;
+        nkb = a.nkb_F;
+        B = a.Wdn_p + (size_t)__builtin_amdgcn_readfirstlane(s_ulist[u / a.nkb_F]) * a.dn_stride;
       } else {
-        af[ub] = zero16();
-        al[ub] = zero16();
+        kb = u < hi ? u - n_routed_units : 0;
+        nkb = a.nkb_Fs;
+        B = a.Wsd_p;
+      }
+      const __amdgpu_buffer_rsrc_t rb = buf_rsrc(B);
 #pragma unroll
-        for (int p = 0; p < 4; ++p) bfr[ub][p] = zero16();
+      for (int p = 0; p < DP; ++p) {
+        int pan = grp * DP + p;
+        pan = pan < a.pD ? pan : a.pD - 1;
+        bfr[ub][p] = u < hi ? ld16_buf(rb, 16u * l, (unsigned)frag_off(pan, kb, nkb)) : zero16();
       }
     }
+  };
+  // raw activation operands of a chunk: for a routed unit (expert e, k-block
+  // kb) lane (c, g) takes h - m of token row c at the EPL columns its
+  // fragment holds (rows past T read nothing: the buffer range check returns
+  // zeros); for a shared unit, the stored fragment
+  const __amdgpu_buffer_rsrc_t rh = buf_rsrc(a.hbuf), rs = buf_rsrc(a.sactf);
+  float hv[UB][EPL];
+  auto load_a = [&](int u0) {
 #pragma unroll
     for (int ub = 0; ub < UB; ++ub) {
       const int u = u0 + ub * NW;
+      i32x4_t r[EPL / 4];
+      if (u < rhi) {
+        const int e = s_ulist[u / a.nkb_F], kb = u % a.nkb_F;
+        const unsigned off = c < a.T ? 4u * (unsigned)((e * 16 + c) * a.F + kb * DT::KB + EPL * g) : OOB;
+#pragma unroll
+        for (int k = 0; k < EPL / 4; ++k) r[k] = ld16_buf(rh, off + 16u * k, 0u);
+      } else {   // a shared unit, or past the range (reads nothing)
+        const unsigned off = u < hi ? (unsigned)((u - n_routed_units) * FRAG_BYTES) + 16u * l : OOB;
+        r[0] = ld16_buf(rs, off, 0u);
+#pragma unroll
+        for (int k = 1; k < EPL / 4; ++k) r[k] = zero16();
+      }
+#pragma unroll
+      for (int k = 0; k < EPL / 4; ++k)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) hv[ub][4 * k + j] = __int_as_float(r[k][j]);
+    }
+  };
+  load_b(lo + w);
+  load_a(lo + w);
+  // 1 / RMS (NormSiLU) and gate of each (expert in range, token row)
+  {
+    const __amdgpu_buffer_rsrc_t rsp = buf_rsrc(a.sspart), rg = buf_rsrc(a.g);
+    const float invF = 1.0f / (float)a.F;
+    for (int k = tid; k < nx * 16; k += NW * 64) {
+      const int e = s_ulist[i0 + (k >> 4)], t = k & 15;
+      float rinv = 0.f, gt = 0.f;
+      if (t < a.T) {
+        float part_ss[DEC_WGMAX];
+#pragma unroll
+        for (int wi = 0; wi < DEC_WGMAX; ++wi)   // issued together; slices past wg_per_e read 0
+          part_ss[wi] = ld_buf(rsp, wi < a.wg_per_e ? 4u * (unsigned)((e * a.wg_per_e + wi) * 16 + t) : OOB);
+        float ss = 0.f;
+#pragma unroll
+        for (int wi = 0; wi < DEC_WGMAX; ++wi) ss += part_ss[wi];
+        rinv = 1.0f / sqrtf(ss * invF + a.eps);
+        gt = ld_buf(rg, 4u * (unsigned)(t * a.E + e));   // 0 for an inactive pair
+      }
+      s_rinv[k] = rinv;
+      s_gate[k] = gt;
+    }
+  }
+  __syncthreads();
+
+  f32x4_t acc[DP];
+#pragma unroll
+  for (int p = 0; p < DP; ++p) acc[p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int u0) {
+#pragma unroll
+    for (int ub = 0; ub < UB; ++ub) {
+      const int u = u0 + ub * NW;
+      __builtin_amdgcn_sched_barrier(0);   // one unit's temporaries at a time
       if (u < hi) {
+        if (u < n_routed_units) {
+          // gated NormSiLU, rounded once to the down-projection operand type
+          const int k = (u / a.nkb_F - i0) * 16 + c;
+          const float rinv = s_rinv[k], gt = s_gate[k];
 #pragma unroll
-        for (int p = 0; p < 4; ++p) DT::mma(acc[p], af[ub], bfr[ub][p]);
-        if (DT::SPLIT && u < n_routed_units) {
+          for (int j = 0; j < EPL; ++j) hv[ub][j] = gt != 0.f ? silu_f(hv[ub][j] * rinv) * gt : 0.f;
+          const i32x4_t af = DN::pack(hv[ub]);
 #pragma unroll
-          for (int p = 0; p < 4; ++p) DT::mma(acc[p], al[ub], bfr[ub][p]);
+          for (int p = 0; p < DP; ++p) DN::mma(acc[p], af, bfr[ub][p]);
+        } else {
+          i32x4_t af;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) af[j] = __float_as_int(hv[ub][j]);
+#pragma unroll
+          for (int p = 0; p < DP; ++p) DT::mma(acc[p], af, bfr[ub][p]);
         }
       }
     }
+  };
+  compute(lo + w);
+  if constexpr (MULTI) {
+    for (int u0 = lo + w + NW * UB; u0 < hi; u0 += NW * UB) {
+      load_b(u0);
+      load_a(u0);
+      compute(u0);
+    }
   }
+  // sum the waves' partial products, 4 panels at a time through LDS
+  float* mypart = a.part + ((size_t)q * a.n_groups + grp) * (16 * NCOL);
 #pragma unroll
-  for (int p = 0; p < 4; ++p) s_red[w][p][l] = acc[p];
-  __syncthreads();
-  float* mypart = a.part + ((size_t)q * a.n_groups + grp) * 1024;
-  for (int idx = tid; idx < 1024; idx += NW * 64) {
-    const int p = idx >> 8, ll = (idx >> 2) & 63, i = idx & 3;
-    float v = 0.f;
+  for (int h = 0; h < DP / 4; ++h) {
 #pragma unroll
-    for (int ww = 0; ww < NW; ++ww) v += s_red[ww][p][ll][i];
-    const int row = 4 * (ll >> 4) + i, col = p * 16 + (ll & 15);
-    st_dev(&mypart[row * 64 + col], v);
+    for (int p = 0; p < 4; ++p) s_red[w][p][l] = acc[4 * h + p];
+    __syncthreads();
+    for (int idx = tid; idx < 1024; idx += NW * 64) {
+      const int p = idx >> 8, ll = (idx >> 2) & 63, i = idx & 3;
+      const int row = 4 * (ll >> 4) + i, col = (4 * h + p) * 16 + (ll & 15);
+      if (row < a.T) {
+        float v = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) v += s_red[ww][p][ll][i];
+        st_dev(&mypart[row * NCOL + col], v);
+      }
+    }
+    __syncthreads();
   }
+  // the last workgroup of the column group to finish sums the Q partials
   wait_all_mem();
   __syncthreads();
   if (tid == 0) s_last = (arrive(&a.cnt_dn[grp]) == (unsigned)(a.Q - 1)) ? 1 : 0;
@@ -395,16 +445,21 @@ __global__ void __launch_bounds__(NW * 64) k_dec_down(DecArgs a) {
   if (!s_last) return;
   elem* out = (elem*)a.out;
   const __amdgpu_buffer_rsrc_t rp = dev_rsrc(a.part);
-  for (int idx = tid; idx < a.T * 64; idx += NW * 64) {
-    const int row = idx >> 6, col = idx & 63;
-    float pv[DEC_QMAX];
-#pragma unroll
-    for (int qq = 0; qq < DEC_QMAX; ++qq)
-      pv[qq] = qq < a.Q ? ld_dev_buf(rp, 4u * (unsigned)(((qq * a.n_groups + grp) << 10) + row * 64 + col)) : 0.f;
+  const int ncol = a.d - grp * NCOL < NCOL ? a.d - grp * NCOL : NCOL;
+  for (int idx = tid; idx < a.T * NCOL; idx += NW * 64) {
+    const int row = idx / NCOL, col = idx % NCOL;
     float v = 0.f;
+    for (int q0 = 0; q0 < a.Q; q0 += 16) {
+      float pv[16];
 #pragma unroll
-    for (int qq = 0; qq < DEC_QMAX; ++qq) v += pv[qq];   // fixed order: deterministic
-    out[(size_t)row * a.d + grp * 64 + col] = DT::from_f32(v);
+      for (int qq = 0; qq < 16; ++qq)   // issued together; splits past Q read 0
+        pv[qq] = ld_dev_buf(rp, q0 + qq < a.Q ? 4u * (unsigned)(((q0 + qq) * a.n_groups + grp) * (16 * NCOL) +
+                                                                 row * NCOL + col)
+                                              : OOB);
+#pragma unroll
+      for (int qq = 0; qq < 16; ++qq) v += pv[qq];   // fixed order: deterministic
+    }
+    if (col < ncol) out[(size_t)row * a.d + grp * NCOL + col] = DT::from_f32(v);
   }
   if (tid == 0) st_dev_u32(&a.cnt_dn[grp], 0u);
 }
@@ -424,12 +479,15 @@ hipError_t decode(const deco_moe_layer* L, const void* x, int T, void* out, hipS
   a.nkb_Fs = L->nkb_Fs;
   a.pF = L->pF;
   a.pFs = L->pFs;
+  a.pD = L->pD;
   a.n_groups = L->n_groups;
   a.Q = L->dec_q;
+  a.n_shared = L->pFs / DEC_NP;
+  a.wg_per_e = L->pF / DEC_NP;
   a.Wr_p = L->Wr_p;
   a.Wup_p = L->Wup_p;
   a.Wbar_p = L->Wbar_p;
-  a.Wdn_p = L->Wdn_p;
+  a.Wdn_p = L->Wdn16_p;   // fp16 copy for bf16 layers, W_down itself for fp32 layers
   a.Wsu_p = L->Wsu_p;
   a.Wsd_p = L->Wsd_p;
   a.up_stride = L->up_stride;
@@ -439,20 +497,20 @@ hipError_t decode(const deco_moe_layer* L, const void* x, int T, void* out, hipS
   a.eps = L->cfg.rms_eps;
   a.z = L->z;
   a.g = L->g;
-  a.mbuf = L->mbuf;
   a.hbuf = L->hbuf;
-  a.actf = L->actf;
+  a.sspart = L->sspart;
   a.sactf = L->sactf;
-  a.eact = L->eact;
-  a.cnt_up = L->cnt_up;
+  a.rflag = L->rflag;
   a.cnt_dn = L->cnt_dn;
   a.part = L->part;
-  const unsigned grid_up = (unsigned)((L->E + 1) * (L->pF / DEC_NP) + L->pFs / DEC_NP);
+  const unsigned grid_up = (unsigned)(a.n_shared + L->E * a.wg_per_e);
   hipError_t err = deco_host::launch(deco_host::KS_DEC_UP, k_dec_up<DT, DEC_NW, DEC_NP>, dim3(grid_up),
                                      dim3(DEC_NW * 64), s, a);
   if (err != hipSuccess) return err;
   const unsigned grid_dn = (unsigned)(L->n_groups * L->dec_q);
-  err = deco_host::launch(deco_host::KS_DEC_DOWN, k_dec_down<DT, DEC_NW>, dim3(grid_dn), dim3(DEC_NW * 64), s, a);
+  err = L->dec_multi
+      ? deco_host::launch(deco_host::KS_DEC_DOWN, k_dec_down<DT, DEC_NW, true>, dim3(grid_dn), dim3(DEC_NW * 64), s, a)
+      : deco_host::launch(deco_host::KS_DEC_DOWN, k_dec_down<DT, DEC_NW, false>, dim3(grid_dn), dim3(DEC_NW * 64), s, a);
   if (err != hipSuccess) return err;
   return hipGetLastError();
 }
@@ -462,15 +520,28 @@ hipError_t decode(const deco_moe_layer* L, const void* x, int T, void* out, hipS
 namespace deco_host {
 
 // Decode launch shape: the down kernel splits its reduction Q ways so that
-// about DECO_DEC_DOWN_WG workgroups stream the down-projection weights (256
-// measured best on the d = 2048 layer among 128 .. 1024: fewer partials to
-// sum at the end, still one workgroup per CU streaming).
+// about DECO_DEC_DOWN_WG workgroups stream the down-projection weights.
 #ifndef DECO_DEC_DOWN_WG
 #define DECO_DEC_DOWN_WG 256
 #endif
 hipError_t plan_decode(deco_moe_layer* L) {
   int q = (DECO_DEC_DOWN_WG + L->n_groups - 1) / L->n_groups;
-  L->dec_q = q < 1 ? 1 : (q > DEC_QMAX ? DEC_QMAX : q);
+  q = q < 1 ? 1 : (q > DEC_QMAX ? DEC_QMAX : q);
+  // With every expert active the reduction has C units.  A down workgroup
+  // takes ceil(C / q) of them: one chunk of DEC_UB units per wave when that
+  // fits (the kernel without a reload loop, which needs fewer registers), and
+  // at most DEC_XMAX experts (1/RMS and gates in LDS; a range of n units spans
+  // at most n / nkb_F + 2 experts).
+  const int C = L->E * L->nkb_F + L->nkb_Fs;
+  auto span = [&](int qq) { return (C + qq - 1) / qq; };
+  auto xmax = [&](int qq) {
+    const int x = span(qq) / L->nkb_F + 2;
+    return x < L->E ? x : L->E;
+  };
+  while (q < DEC_QMAX && (span(q) > DEC_NW * DEC_UB || xmax(q) > DEC_XMAX)) ++q;
+  if (xmax(q) > DEC_XMAX || L->pF / DEC_NP > DEC_WGMAX) return hipErrorInvalidValue;
+  L->dec_q = q;
+  L->dec_multi = span(q) > DEC_NW * DEC_UB;
   L->dec_ok = 1;
   return hipSuccess;
 }

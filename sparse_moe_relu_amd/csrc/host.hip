@@ -46,8 +46,8 @@ void derive(deco_moe_layer* L) {
   L->pD = L->d / 16;
   L->pFs = L->Fs / 16;
   L->W = (L->E + 63) / 64;
-  L->n_groups = L->d / 64;
-  L->dec_q = 32;   // upper bound for the workspace; the decode plan picks the value at load
+  L->n_groups = (L->pD + 7) / 8;   // 128-column groups of the decode down role
+  L->dec_q = 64;   // upper bound for the workspace; the decode plan picks the value at load
   L->pre_grid = 1024;
 }
 
@@ -195,13 +195,12 @@ int deco_moe_load_weights(const deco_moe_config* cfg, const void* W_r, const flo
   size_t o_m = k.take(sizeof(uint64_t) * Tcap * L->W);
   size_t o_mb = k.take(sizeof(float) * Tcap * L->F);
   size_t o_h = k.take(sizeof(float) * (size_t)E * 16 * L->F);
-  size_t o_af = k.take((size_t)E * L->nkb_F * KBy * (L->cfg.dtype == DECO_DT_BF16 ? 2 : 1));
+  size_t o_ss = k.take(sizeof(float) * (size_t)E * 16 * 16);
   size_t o_sf = k.take((size_t)L->nkb_Fs * KBy);
-  size_t o_ea = k.take(sizeof(unsigned) * E);
-  size_t o_cu = k.take(sizeof(unsigned) * E);
+  size_t o_rf = k.take(sizeof(unsigned) * E);
   size_t o_er = k.take(sizeof(unsigned));
   size_t o_cd = k.take(sizeof(unsigned) * L->n_groups);
-  size_t o_pt = k.take(sizeof(float) * (size_t)L->dec_q * L->n_groups * 1024);
+  size_t o_pt = k.take(sizeof(float) * (size_t)L->dec_q * L->n_groups * 16 * 128);
   size_t o_to = k.take(sizeof(int) * (Tcap + 1));
   size_t o_ec = k.take(sizeof(int) * E);
   size_t o_lt = k.take(sizeof(int) * (size_t)E * Tcap);
@@ -235,10 +234,9 @@ int deco_moe_load_weights(const deco_moe_config* cfg, const void* W_r, const flo
   L->mask = (uint64_t*)(L->ws + o_m);
   L->mbuf = (float*)(L->ws + o_mb);
   L->hbuf = (float*)(L->ws + o_h);
-  L->actf = L->ws + o_af;
+  L->sspart = (float*)(L->ws + o_ss);
   L->sactf = L->ws + o_sf;
-  L->eact = (unsigned*)(L->ws + o_ea);
-  L->cnt_up = (unsigned*)(L->ws + o_cu);
+  L->rflag = (unsigned*)(L->ws + o_rf);
   L->dec_err = (unsigned*)(L->ws + o_er);
   L->cnt_dn = (unsigned*)(L->ws + o_cd);
   L->part = (float*)(L->ws + o_pt);
