@@ -86,6 +86,7 @@ enum {
   KS_PACK = 0,
   KS_DEC_UP,
   KS_DEC_DOWN,
+  KS_DEC_SUM,
   KS_PRE_ROUTER_SHARED,
   KS_PRE_DISPATCH,
   KS_PRE_EXPERT,

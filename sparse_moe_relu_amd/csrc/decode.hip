@@ -83,6 +83,9 @@ constexpr int DEC_WGMAX = 8;          // largest number of up slices per routed 
 constexpr int DEC_UB = 2;             // down-kernel units (k-blocks) in flight per wave
 constexpr int DEC_DP = 8;             // 16-column output panels per down workgroup
 constexpr int DEC_XMAX = 64;          // routed experts one down workgroup may touch (host plan)
+#ifndef DECO_DEC_SUM
+#define DECO_DEC_SUM 1
+#endif
 // A buffer-load offset past the resource's range: the load returns zeros
 // without touching memory (used to mask loads without branching).
 constexpr unsigned OOB = 0xFFFFFF00u;
@@ -432,11 +435,18 @@ __global__ void __launch_bounds__(NW * 64) k_dec_down(DecArgs a) {
         float v = 0.f;
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww) v += s_red[ww][p][ll][i];
+#if DECO_DEC_SUM
+        mypart[row * NCOL + col] = v;
+#else
         st_dev(&mypart[row * NCOL + col], v);
+#endif
       }
     }
     __syncthreads();
   }
+#if DECO_DEC_SUM
+  return;   // k_dec_sum adds the Q partials
+#endif
   // the last workgroup of the column group to finish sums the Q partials
   wait_all_mem();
   __syncthreads();
@@ -462,6 +472,32 @@ __global__ void __launch_bounds__(NW * 64) k_dec_down(DecArgs a) {
     if (col < ncol) out[(size_t)row * a.d + grp * NCOL + col] = DT::from_f32(v);
   }
   if (tid == 0) st_dev_u32(&a.cnt_dn[grp], 0u);
+}
+
+// out[t][c] = sum over the Q reduction splits of the down kernel's partial
+// products, in split order (deterministic); 4 consecutive columns per thread.
+template <class DT>
+__global__ void __launch_bounds__(256) k_dec_sum(DecArgs a) {
+  constexpr int NCOL = DEC_DP * 16;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx * 4 >= a.T * a.d) return;
+  const int row = (idx * 4) / a.d, col = (idx * 4) % a.d;
+  const int grp = col / NCOL, cin = col % NCOL;
+  f32x4_t v = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int q0 = 0; q0 < a.Q; q0 += 16) {
+    f32x4_t pv[16];
+#pragma unroll
+    for (int qq = 0; qq < 16; ++qq)   // issued together
+      pv[qq] = q0 + qq < a.Q
+                   ? *reinterpret_cast<const f32x4_t*>(
+                         a.part + ((((size_t)(q0 + qq) * a.n_groups + grp) * 16 + row) * NCOL + cin))
+                   : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int qq = 0; qq < 16; ++qq) v += pv[qq];
+  }
+  typename DT::elem* o = (typename DT::elem*)a.out + (size_t)row * a.d + col;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) o[j] = DT::from_f32(v[j]);
 }
 
 template <class DT>
@@ -512,6 +548,11 @@ hipError_t decode(const deco_moe_layer* L, const void* x, int T, void* out, hipS
       ? deco_host::launch(deco_host::KS_DEC_DOWN, k_dec_down<DT, DEC_NW, true>, dim3(grid_dn), dim3(DEC_NW * 64), s, a)
       : deco_host::launch(deco_host::KS_DEC_DOWN, k_dec_down<DT, DEC_NW, false>, dim3(grid_dn), dim3(DEC_NW * 64), s, a);
   if (err != hipSuccess) return err;
+#if DECO_DEC_SUM
+  const unsigned grid_sum = (unsigned)((T * L->d / 4 + 255) / 256);
+  err = deco_host::launch(deco_host::KS_DEC_SUM, k_dec_sum<DT>, dim3(grid_sum), dim3(256), s, a);
+  if (err != hipSuccess) return err;
+#endif
   return hipGetLastError();
 }
 

@@ -104,6 +104,7 @@ const char* kernel_slot_name(int slot) {
     case KS_PACK: return "load_pack";
     case KS_DEC_UP: return "k_dec_up";
     case KS_DEC_DOWN: return "k_dec_down";
+    case KS_DEC_SUM: return "k_dec_sum";
     case KS_PRE_ROUTER_SHARED: return "k_pre_router_shared";
     case KS_PRE_DISPATCH: return "k_pre_dispatch";
     case KS_PRE_EXPERT: return "k_pre_expert";
