@@ -42,6 +42,7 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "k_dec_up": "sparse_moe_relu_amd/csrc/decode.hip",
     "k_dec_down": "sparse_moe_relu_amd/csrc/decode.hip",
+    "k_dec_sum": "sparse_moe_relu_amd/csrc/decode.hip",
     "k_pre_router_shared": "sparse_moe_relu_amd/csrc/prefill.hip",
     "k_pre_dispatch": "sparse_moe_relu_amd/csrc/prefill.hip",
     "k_pre_expert": "sparse_moe_relu_amd/csrc/prefill.hip",
@@ -78,11 +79,12 @@ def decode_bytes(L, n_union: int, T: int) -> dict:
     """Algorithmic HBM bytes per launch, per decode kernel: the weights the
     method must read (router, bias and scale, the two matrices of each expert
     touched by the batch, the shared expert) plus x in and out.  The
-    mean-term matrix is not counted (it could be folded into the experts)."""
+    mean-term matrix and the hand-off buffers between the kernels are not
+    counted."""
     s = 2 if L.dtype == "bf16" else 4
     up = L.d * L.E * s + 8 * L.E + n_union * L.d * L.F * s + L.d * L.Fs * s + T * L.d * s
-    down = n_union * L.F * L.d * s + L.Fs * L.d * s + T * L.d * s
-    return {"k_dec_up": up, "k_dec_down": down}
+    down = n_union * L.F * L.d * s + L.Fs * L.d * s
+    return {"k_dec_up": up, "k_dec_down": down, "k_dec_sum": T * L.d * s}
 
 
 def prefill_flops(L, P: int, T: int) -> dict:

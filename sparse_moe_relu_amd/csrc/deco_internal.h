@@ -52,7 +52,6 @@ struct deco_moe_layer {
   char* sactf;             // [nkb_Fs] frags      shared SiLU output
   unsigned* rflag;         // [E] routing of the last decode call (1 no token, 2 some token routed to e)
   unsigned* dec_err;       // [1] device-side error flags
-  unsigned* cnt_dn;        // [n_groups] arrival counters of the decode down kernel
   float* part;             // [dec_q][n_groups][16][128] partial outputs of the decode down kernel
   // prefill
   int* tok_off;            // [Tcap + 1]

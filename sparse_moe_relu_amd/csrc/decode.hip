@@ -5,8 +5,7 @@
 // point of ReLU routing with sparse experts is that inactive routed experts
 // cost nothing: the DECO paper (Sec. 1 and the Sec. 4 acceleration paragraph
 // with Table 4) attributes its speedup to skipping the memory traffic of
-// inactive experts.  Two kernels, with no workgroup waiting on another
-// except for the final sum of partial outputs:
+// inactive experts.  Three kernels, no workgroup waiting on another:
 //
 //   k_dec_up   one workgroup per 32 columns of the shared expert, and per
 //              (routed expert, 32 columns of F).  A routed workgroup computes
@@ -29,9 +28,9 @@
 //              share of their down-projection weights (and of the shared
 //              expert's), completes each row's RMS from the slices' sums of
 //              squares, applies SiLU and the gate while building the MFMA
-//              operands, multiplies, and the last workgroup of a column group
-//              sums the Q partials in a fixed order (deterministic) and
-//              writes out.
+//              operands, multiplies, and stores its partial product.
+//   k_dec_sum  adds the Q partial products of each output in split order
+//              (deterministic) and writes out.
 #include "deco_common.h"
 #include "deco_internal.h"
 #include "gemm_tile.h"
@@ -62,7 +61,6 @@ struct DecArgs {
   float* sspart;            // [E][wg_per_e][16] sums of squares of h - m over each slice
   char* sactf;              // shared-expert activations as down-projection operand fragments
   unsigned* rflag;          // [E] 1 no token routed to e, 2 some token did
-  unsigned* cnt_dn;         // [n_groups] arrivals of a column group's workgroups
   float* part;
 };
 
@@ -83,9 +81,6 @@ constexpr int DEC_WGMAX = 8;          // largest number of up slices per routed 
 constexpr int DEC_UB = 2;             // down-kernel units (k-blocks) in flight per wave
 constexpr int DEC_DP = 8;             // 16-column output panels per down workgroup
 constexpr int DEC_XMAX = 64;          // routed experts one down workgroup may touch (host plan)
-#ifndef DECO_DEC_SUM
-#define DECO_DEC_SUM 1
-#endif
 // A buffer-load offset past the resource's range: the load returns zeros
 // without touching memory (used to mask loads without branching).
 constexpr unsigned OOB = 0xFFFFFF00u;
@@ -269,7 +264,6 @@ __global__ void __launch_bounds__(NW * 64) k_dec_down(DecArgs a) {
   __shared__ int s_ulist[256];
   __shared__ int s_wcnt[4];
   __shared__ int s_nu;
-  __shared__ int s_last;
   __shared__ float s_rinv[DEC_XMAX * 16];
   __shared__ float s_gate[DEC_XMAX * 16];
   __shared__ f32x4_t s_red[NW][4][64];
@@ -435,43 +429,11 @@ __global__ void __launch_bounds__(NW * 64) k_dec_down(DecArgs a) {
         float v = 0.f;
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww) v += s_red[ww][p][ll][i];
-#if DECO_DEC_SUM
         mypart[row * NCOL + col] = v;
-#else
-        st_dev(&mypart[row * NCOL + col], v);
-#endif
       }
     }
     __syncthreads();
   }
-#if DECO_DEC_SUM
-  return;   // k_dec_sum adds the Q partials
-#endif
-  // the last workgroup of the column group to finish sums the Q partials
-  wait_all_mem();
-  __syncthreads();
-  if (tid == 0) s_last = (arrive(&a.cnt_dn[grp]) == (unsigned)(a.Q - 1)) ? 1 : 0;
-  __syncthreads();
-  if (!s_last) return;
-  elem* out = (elem*)a.out;
-  const __amdgpu_buffer_rsrc_t rp = dev_rsrc(a.part);
-  const int ncol = a.d - grp * NCOL < NCOL ? a.d - grp * NCOL : NCOL;
-  for (int idx = tid; idx < a.T * NCOL; idx += NW * 64) {
-    const int row = idx / NCOL, col = idx % NCOL;
-    float v = 0.f;
-    for (int q0 = 0; q0 < a.Q; q0 += 16) {
-      float pv[16];
-#pragma unroll
-      for (int qq = 0; qq < 16; ++qq)   // issued together; splits past Q read 0
-        pv[qq] = ld_dev_buf(rp, q0 + qq < a.Q ? 4u * (unsigned)(((q0 + qq) * a.n_groups + grp) * (16 * NCOL) +
-                                                                 row * NCOL + col)
-                                              : OOB);
-#pragma unroll
-      for (int qq = 0; qq < 16; ++qq) v += pv[qq];   // fixed order: deterministic
-    }
-    if (col < ncol) out[(size_t)row * a.d + grp * NCOL + col] = DT::from_f32(v);
-  }
-  if (tid == 0) st_dev_u32(&a.cnt_dn[grp], 0u);
 }
 
 // out[t][c] = sum over the Q reduction splits of the down kernel's partial
@@ -537,7 +499,6 @@ hipError_t decode(const deco_moe_layer* L, const void* x, int T, void* out, hipS
   a.sspart = L->sspart;
   a.sactf = L->sactf;
   a.rflag = L->rflag;
-  a.cnt_dn = L->cnt_dn;
   a.part = L->part;
   const unsigned grid_up = (unsigned)(a.n_shared + L->E * a.wg_per_e);
   hipError_t err = deco_host::launch(deco_host::KS_DEC_UP, k_dec_up<DT, DEC_NW, DEC_NP>, dim3(grid_up),
@@ -548,11 +509,9 @@ hipError_t decode(const deco_moe_layer* L, const void* x, int T, void* out, hipS
       ? deco_host::launch(deco_host::KS_DEC_DOWN, k_dec_down<DT, DEC_NW, true>, dim3(grid_dn), dim3(DEC_NW * 64), s, a)
       : deco_host::launch(deco_host::KS_DEC_DOWN, k_dec_down<DT, DEC_NW, false>, dim3(grid_dn), dim3(DEC_NW * 64), s, a);
   if (err != hipSuccess) return err;
-#if DECO_DEC_SUM
   const unsigned grid_sum = (unsigned)((T * L->d / 4 + 255) / 256);
   err = deco_host::launch(deco_host::KS_DEC_SUM, k_dec_sum<DT>, dim3(grid_sum), dim3(256), s, a);
   if (err != hipSuccess) return err;
-#endif
   return hipGetLastError();
 }
 

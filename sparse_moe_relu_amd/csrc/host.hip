@@ -200,7 +200,6 @@ int deco_moe_load_weights(const deco_moe_config* cfg, const void* W_r, const flo
   size_t o_sf = k.take((size_t)L->nkb_Fs * KBy);
   size_t o_rf = k.take(sizeof(unsigned) * E);
   size_t o_er = k.take(sizeof(unsigned));
-  size_t o_cd = k.take(sizeof(unsigned) * L->n_groups);
   size_t o_pt = k.take(sizeof(float) * (size_t)L->dec_q * L->n_groups * 16 * 128);
   size_t o_to = k.take(sizeof(int) * (Tcap + 1));
   size_t o_ec = k.take(sizeof(int) * E);
@@ -239,7 +238,6 @@ int deco_moe_load_weights(const deco_moe_config* cfg, const void* W_r, const flo
   L->sactf = L->ws + o_sf;
   L->rflag = (unsigned*)(L->ws + o_rf);
   L->dec_err = (unsigned*)(L->ws + o_er);
-  L->cnt_dn = (unsigned*)(L->ws + o_cd);
   L->part = (float*)(L->ws + o_pt);
   L->tok_off = (int*)(L->ws + o_to);
   L->ecnt = (int*)(L->ws + o_ec);
