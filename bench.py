@@ -98,6 +98,62 @@ def prefill_flops(L, P: int, T: int) -> dict:
             "k_pre_combine": 0}
 
 
+def layer_flops(L, P: int, T: int) -> int:
+    """Algorithmic flops of one call: router, routed up + down over the P
+    active pairs, shared expert (mean term, NormSiLU, SiLU not counted)."""
+    return T * 2 * L.d * L.E + P * 4 * L.d * L.F + T * 4 * L.d * L.Fs
+
+
+def dense_ffn_time(d: int, dff: int, T: int, steps: int = 20) -> float:
+    """Seconds per call of the dense-equivalent non-gated FFN, SiLU(x W1) W2,
+    on torch (hipBLASLt) in bf16, cycling weight copies past the Infinity Cache."""
+    import torch
+    n = max(1, math.ceil(CACHE_DEFEAT_BYTES / (2 * d * dff * 2)))
+    g = torch.Generator(device="cuda").manual_seed(0)
+    W1 = [torch.randn(d, dff, device="cuda", dtype=torch.bfloat16, generator=g) * d ** -0.5 for _ in range(n)]
+    W2 = [torch.randn(dff, d, device="cuda", dtype=torch.bfloat16, generator=g) * dff ** -0.5 for _ in range(n)]
+    x = torch.randn(T, d, device="cuda", dtype=torch.bfloat16, generator=g)
+    for k in range(5):
+        torch.nn.functional.silu(x @ W1[k % n]) @ W2[k % n]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        torch.nn.functional.silu(x @ W1[k % n]) @ W2[k % n]
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def sweep():
+    """The d=4096 layer over T in {1, 16, 256, 2048} and the d=2048 layer at
+    T=1024 over activation ratios 5..40 % (with the dense-equivalent FFN):
+    tokens/s and the fraction of the attainable roofline, max(B/BW, F/MFMA)/t,
+    with B the decode byte count (weights touched + x in and out) and F the
+    algorithmic flops.  Prints a table; no JSON line."""
+    from synthetic import make_layer
+    rows = []
+    cases = [(4, T, None) for T in (1, 16, 256, 2048)] + [(5, 1024, r) for r in (0.05, 0.10, 0.20, 0.40)]
+    for cfg, T, ratio in cases:
+        L = make_layer(cfg, T=T, ratio=ratio)
+        steps = 400 if T <= 16 else (100 if T <= 256 else 30)
+        r = run_workload(L, steps, max(5, steps // 10))
+        t = r["elapsed"] / steps
+        B = decode_bytes(L, r["n_union"], T)
+        Bt = sum(B.values()) + T * L.d * (2 if L.dtype == "bf16" else 4)
+        Fl = layer_flops(L, r["P"], T)
+        fb, ff = Bt / t / (HBM_PEAK_GBS * 1e9), Fl / t / (BF16_PEAK_TFLOPS * 1e12)
+        row = dict(cfg=f"c{cfg}", T=T, ratio=round(r["ratio"], 4), experts_touched=r["n_union"], pairs=r["P"],
+                   us_per_call=round(t * 1e6, 2), tokens_per_s=round(T / t, 1),
+                   hbm_frac=round(fb, 4), mfma_frac=round(ff, 4), attainable_frac=round(max(fb, ff), 4),
+                   kernels_us={k: round(v * 1e3, 2) for k, v in r["kernels"].items()})
+        if cfg == 5:
+            td = dense_ffn_time(L.d, L.E * L.F + L.Fs, T)
+            row["dense_ffn_us"] = round(td * 1e6, 2)
+            row["speedup_vs_dense"] = round(td / t, 3)
+        log(json.dumps(row))
+        rows.append(row)
+    print(json.dumps({"sweep": rows}), flush=True)
+
+
 def layer_weight_bytes(L) -> int:
     s = 2 if L.dtype == "bf16" else 4
     return s * (L.d * L.E + 2 * L.E * L.d * L.F + 2 * L.d * L.Fs + L.d * L.F)
@@ -249,6 +305,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--workload", choices=["decode", "prefill"], default="decode",
                     help="run only this workload's GPU loop (for profiler runs)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="T sweep of the d=4096 layer and ratio sweep against the dense FFN (table, no JSON)")
     ap.add_argument("--only-gpu-loop", action="store_true",
                     help="profiler mode: GPU loop of --workload only, no JSON")
     ap.add_argument("--profile-summary", nargs=3, metavar=("DB", "OUT", "COMMAND"),
@@ -280,6 +338,10 @@ def main():
     torch.cuda.set_device(0)
     import sparse_moe_relu_amd as dm
     dm.load_library()
+
+    if args.sweep:
+        sweep()
+        return
 
     if args.only_gpu_loop:
         if args.calib_copy_mib:
