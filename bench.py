@@ -124,14 +124,16 @@ def dense_ffn_time(d: int, dff: int, T: int, steps: int = 20) -> float:
 
 
 def sweep():
-    """The d=4096 layer over T in {1, 16, 256, 2048} and the d=2048 layer at
-    T=1024 over activation ratios 5..40 % (with the dense-equivalent FFN):
+    """The decode layer at T in {1, 8}, the d=4096 layer over T in
+    {1, 16, 256, 2048} and the d=2048 layer at T=1024 over activation ratios
+    5..40 % (the d=2048 cases beside the dense-equivalent FFN):
     tokens/s and the fraction of the attainable roofline, max(B/BW, F/MFMA)/t,
     with B the decode byte count (weights touched + x in and out) and F the
     algorithmic flops.  Prints a table; no JSON line."""
     from synthetic import make_layer
     rows = []
-    cases = [(4, T, None) for T in (1, 16, 256, 2048)] + [(5, 1024, r) for r in (0.05, 0.10, 0.20, 0.40)]
+    cases = ([(2, T, None) for T in (1, 8)] + [(4, T, None) for T in (1, 16, 256, 2048)]
+             + [(5, 1024, r) for r in (0.05, 0.10, 0.20, 0.40)])
     for cfg, T, ratio in cases:
         L = make_layer(cfg, T=T, ratio=ratio)
         steps = 400 if T <= 16 else (100 if T <= 256 else 30)
@@ -145,8 +147,8 @@ def sweep():
                    us_per_call=round(t * 1e6, 2), tokens_per_s=round(T / t, 1),
                    hbm_frac=round(fb, 4), mfma_frac=round(ff, 4), attainable_frac=round(max(fb, ff), 4),
                    kernels_us={k: round(v * 1e3, 2) for k, v in r["kernels"].items()})
-        if cfg == 5:
-            td = dense_ffn_time(L.d, L.E * L.F + L.Fs, T)
+        if cfg in (2, 5):
+            td = dense_ffn_time(L.d, L.E * L.F + L.Fs, T, steps=200 if T <= 16 else 20)
             row["dense_ffn_us"] = round(td * 1e6, 2)
             row["speedup_vs_dense"] = round(td / t, 3)
         log(json.dumps(row))

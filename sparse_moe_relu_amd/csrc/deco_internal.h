@@ -23,6 +23,7 @@ struct deco_moe_layer {
   int dec_multi;           // decode down kernel needs more than one chunk of units per wave
   int dec_ok;              // the decode path is available for this layer
   int pre_grid;            // persistent grid of the prefill expert kernel
+  int n_cu;                // compute units of the device
 
   // packed weights (one allocation)
   char* wmem;

@@ -115,10 +115,13 @@ __device__ __forceinline__ void store4_pair(PT* p, const f32x4_t& v) {
 }
 
 // --------------------------------------------------------------------------
-template <class DT>
+// NS pipeline stages in LDS: 2 (64 KiB, two workgroups per CU) when the grid
+// exceeds the CUs, 4 (128 KiB, one per CU, three steps of loads in flight)
+// when it does not, which is the case below a few thousand tokens.
+template <class DT, int NS>
 __global__ void __launch_bounds__(256, 2) k_pre_router_shared(PreArgs a) {
   using elem = typename DT::elem;
-  using TC = DenseTile<DT>;
+  using TC = Tile<DT, GM, GP, NS>;
   __shared__ i32x4_t lds[TC::LDS_V];
   const int tid = threadIdx.x, w = tid >> 6, wm = w >> 1, wn = w & 1, l = tid & 63, g = l >> 4, c = l & 15;
   const int t = xcd_tile(blockIdx.x, gridDim.x);
@@ -725,8 +728,10 @@ hipError_t prefill(const deco_moe_layer* L, const void* x, int T, void* out, hip
   a.ybuf = L->ybuf;
   const unsigned mtiles = (unsigned)((T + GM - 1) / GM);
   using deco_host::launch;
-  hipError_t err = launch(deco_host::KS_PRE_ROUTER_SHARED, k_pre_router_shared<DT>, dim3(mtiles * a.rs_nt),
-                          dim3(256), s, a);
+  const unsigned rs_grid = mtiles * a.rs_nt;
+  hipError_t err = rs_grid <= (unsigned)L->n_cu
+      ? launch(deco_host::KS_PRE_ROUTER_SHARED, k_pre_router_shared<DT, 4>, dim3(rs_grid), dim3(256), s, a)
+      : launch(deco_host::KS_PRE_ROUTER_SHARED, k_pre_router_shared<DT, DECO_PRE_NS>, dim3(rs_grid), dim3(256), s, a);
   if (err == hipSuccess)
     err = launch(deco_host::KS_PRE_DISPATCH, k_pre_dispatch, dim3(L->E + 1), dim3(DISP_NT), s, a);
   if (err == hipSuccess)
@@ -758,6 +763,7 @@ hipError_t plan_prefill(deco_moe_layer* L) {
   int grid = (occ < 1 ? 1 : occ) * (cus < 1 ? 1 : cus);
   grid = (grid + NXCD - 1) / NXCD * NXCD;
   L->pre_grid = grid;
+  L->n_cu = cus < 1 ? 1 : cus;
   return hipSuccess;
 }
 
