@@ -14,6 +14,9 @@ the DECO paper, so the steps below follow its prose):
   [W-CN]    Chinese write-up of the same paper (qidianchuan.cn), section 二
             (core design of DECO): the router part, and the expert-design part
             on NormSiLU and non-gated experts.
+  The TopK variant follows the baseline of [P-DECO] Sec. 4 (the acceleration
+  paragraph and its Table 4), which replaces the ReLU routing by conventional
+  TopK at the same average activation ratio.
 
 Readings taken where the text is silent:
   * router = linear projection with a bias b_r, then ReLU, then a learned
@@ -28,6 +31,11 @@ Readings taken where the text is silent:
   * experts are non-gated two-matrix MLPs with no biases;
   * shared expert: non-gated MLP with plain SiLU, weight 1, no lambda;
   * no residual: the result is the FFN sublayer output only.
+  * TopK variant (top_k = k > 0): the same router projection; each token keeps
+    the k experts with the largest logits, ties going to the lower expert
+    index; gates are the softmax of the kept logits (conventional TopK
+    gating); no expert-wise scale (lambda belongs to the ReLU routing it
+    replaces); experts and shared expert unchanged.
 
 The pages print no worked numeric example of the layer, so no value here is
 compared with a printed one; every function is pinned instead by invariants,
@@ -68,6 +76,29 @@ def router(x, W_r, b_r, lam):
     lam = np.asarray(lam, np.float64)
     active = (z > 0.0) & (lam != 0.0)[None, :]
     g = np.where(active, lam[None, :] * np.maximum(z, 0.0), 0.0)
+    return z, active, g
+
+
+def router_topk(x, W_r, b_r, k: int):
+    """TopK routing variant, the baseline of [P-DECO] Sec. 4 (acceleration
+    paragraph, Table 4): conventional TopK in place of the ReLU routing.
+
+    z = x . W_r + b_r as in `router`; per token the k largest logits are kept
+    (a stable descending sort, so equal logits go to the lower expert index),
+    and their gates are the softmax of the kept logits; every other gate is 0.
+    Returns z [T,E], the active mask [T,E] (bool, exactly k per row) and g.
+    """
+    z = np.asarray(x, np.float64) @ np.asarray(W_r, np.float64) + np.asarray(b_r, np.float64)
+    T, E = z.shape
+    if not 1 <= k <= E:
+        raise ValueError(f"top_k must be in 1..{E}")
+    active = np.zeros((T, E), dtype=bool)
+    g = np.zeros((T, E))
+    for t in range(T):
+        keep = np.argsort(-z[t], kind="stable")[:k]
+        active[t, keep] = True
+        w = np.exp(z[t, keep] - z[t, keep].max())
+        g[t, keep] = w / w.sum()
     return z, active, g
 
 
@@ -124,20 +155,21 @@ class OracleResult:
     shared: np.ndarray   # [T, d] shared-expert part of out
 
 
-def forward(x, W_r, b_r, lam, W_up, W_down, Ws_up, Ws_down, eps=1e-6) -> OracleResult:
+def forward(x, W_r, b_r, lam, W_up, W_down, Ws_up, Ws_down, eps=1e-6, top_k: int = 0) -> OracleResult:
     """Sparse evaluation of one DECO layer, expert by expert.
 
-    Steps: router; Wbar and m = x . Wbar; for each expert e the tokens S_e
-    that activate it, in ascending order (per-expert bucketing), the expert
-    MLP on those rows, and out[S_e] += g[S_e, e] * y (gate-weighted combine,
-    [P-DECO] Sec. 2 "Router design": the router assigns a weight to each
-    expert); finally the shared expert is added.
+    Steps: router (the ReLU router, or with top_k > 0 the TopK variant);
+    Wbar and m = x . Wbar; for each expert e the tokens S_e that activate it,
+    in ascending order (per-expert bucketing), the expert MLP on those rows,
+    and out[S_e] += g[S_e, e] * y (gate-weighted combine, [P-DECO] Sec. 2
+    "Router design": the router assigns a weight to each expert); finally the
+    shared expert is added.
     """
     x = np.asarray(x, np.float64)
     T, d = x.shape
     W_up = np.asarray(W_up, np.float64)
     E = W_up.shape[0]
-    z, active, g = router(x, W_r, b_r, lam)
+    z, active, g = router_topk(x, W_r, b_r, top_k) if top_k > 0 else router(x, W_r, b_r, lam)
     m = x @ mean_up(W_up)
     routed = np.zeros((T, d))
     for e in range(E):
@@ -150,20 +182,44 @@ def forward(x, W_r, b_r, lam, W_up, W_down, Ws_up, Ws_down, eps=1e-6) -> OracleR
     return OracleResult(out=routed + shared, z=z, active=active, g=g, routed=routed, shared=shared)
 
 
-def forward_dense_bruteforce(x, W_r, b_r, lam, W_up, W_down, Ws_up, Ws_down, eps=1e-6) -> np.ndarray:
+def _topk_gates_by_subsets(z_row: np.ndarray, k: int) -> np.ndarray:
+    """TopK gates of one token found by enumerating every k-subset of the
+    experts: the subset with the largest logit sum (first in lexicographic
+    order among equal sums), softmax-weighted.  Exponential; tiny E only."""
+    import itertools
+    E = z_row.shape[0]
+    best, best_sum = None, -np.inf
+    for sub in itertools.combinations(range(E), k):
+        s = float(sum(z_row[list(sub)]))
+        if s > best_sum:
+            best, best_sum = sub, s
+    g = np.zeros(E)
+    w = np.array([np.exp(z_row[e] - max(z_row[list(best)])) for e in best])
+    g[list(best)] = w / w.sum()
+    return g
+
+
+def forward_dense_bruteforce(x, W_r, b_r, lam, W_up, W_down, Ws_up, Ws_down, eps=1e-6,
+                             top_k: int = 0) -> np.ndarray:
     """Dense brute force for small inputs: every expert for every token.
 
     Ignores the mask: each (token, expert) pair is evaluated one at a time,
     the mean term is rebuilt per token as the average of that token's E
     up-projections (no precomputed Wbar), and the result is weighted by the
-    gate, which is zero for inactive pairs.  Used only to pin `forward`.
+    gate, which is zero for inactive pairs.  With top_k > 0 the gates come
+    from an enumeration of expert subsets instead of a sort.  Used only to
+    pin `forward`.
     """
     x = np.asarray(x, np.float64)
     T, d = x.shape
     W_up = np.asarray(W_up, np.float64)
     W_down = np.asarray(W_down, np.float64)
     E = W_up.shape[0]
-    _, _, g = router(x, W_r, b_r, lam)
+    if top_k > 0:
+        zz = x @ np.asarray(W_r, np.float64) + np.asarray(b_r, np.float64)
+        g = np.stack([_topk_gates_by_subsets(zz[t], top_k) for t in range(T)])
+    else:
+        _, _, g = router(x, W_r, b_r, lam)
     out = np.zeros((T, d))
     for t in range(T):
         h_all = np.stack([x[t] @ W_up[e] for e in range(E)])      # [E, F]

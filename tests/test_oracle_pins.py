@@ -268,3 +268,77 @@ def test_generator_bf16_rounding_is_single_rne_cast():
     assert bits[0] == 0x3F80 and bits[3] == 0xC020
     t = torch.tensor(v[:2], dtype=torch.float64).to(torch.bfloat16).double().numpy()
     assert np.array_equal(t, r[:2])
+
+
+# TopK routing variant --------------------------------------------------------
+def _fw_topk(L, k, **over):
+    x = over.pop("x", L.x)
+    w = L.weights()
+    w.update(over)
+    return oracle.forward(x, **w, eps=L.eps, top_k=k)
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 5])
+def test_topk_selection_equals_best_subset_and_softmax_gates(k):
+    # selection pinned by enumerating every k-subset (largest logit sum) and
+    # by the order statistics of the logits; gates by their defining ratios
+    L = make_custom(64, 7, 32, 64, 12, "f32", seed=11)
+    z, active, g = oracle.router_topk(L.x, L.W_r, L.b_r, k)
+    for t in range(L.T):
+        import itertools
+        best = max(itertools.combinations(range(L.E), k), key=lambda s: sum(z[t, list(s)]))
+        assert set(np.nonzero(active[t])[0]) == set(best)
+        kept, dropped = z[t, active[t]], z[t, ~active[t]]
+        assert dropped.size == 0 or kept.min() > dropped.max()
+        assert math.isclose(g[t].sum(), 1.0, rel_tol=1e-12)
+        assert np.all(g[t, ~active[t]] == 0.0) and np.all(g[t, active[t]] > 0.0)
+        a = np.nonzero(active[t])[0]
+        for i in a:
+            for j in a:
+                assert math.isclose(g[t, i] / g[t, j], math.exp(z[t, i] - z[t, j]), rel_tol=1e-9)
+
+
+def test_topk_ties_go_to_lower_expert_index():
+    x = np.eye(5)                              # token t reads row t of W_r
+    W_r = np.array([[1.0, 3.0, 3.0, 0.0, 3.0]] * 5)
+    z, active, g = oracle.router_topk(x, W_r, np.zeros(5), 2)
+    assert np.array_equal(np.nonzero(active[0])[0], [1, 2])
+    assert np.allclose(g[0, [1, 2]], 0.5)
+    z, active, _ = oracle.router_topk(x, W_r, np.zeros(5), 4)
+    assert np.array_equal(np.nonzero(active[0])[0], [0, 1, 2, 4])
+
+
+def test_topk_k1_is_argmax_with_gate_one():
+    L = make_custom(64, 8, 32, 64, 10, "f32", seed=12)
+    z, active, g = oracle.router_topk(L.x, L.W_r, L.b_r, 1)
+    assert np.array_equal(np.nonzero(active)[1], np.argmax(z, axis=1))
+    assert np.array_equal(g[active], np.ones(L.T))
+
+
+def test_topk_full_k_is_softmax_over_all_experts():
+    L = make_custom(64, 8, 32, 64, 6, "f32", seed=13)
+    z, active, g = oracle.router_topk(L.x, L.W_r, L.b_r, L.E)
+    assert active.all()
+    ref = torch.softmax(torch.from_numpy(z), dim=1).numpy()   # library routine
+    assert np.max(np.abs(g - ref)) <= 1e-15
+
+
+def test_topk_ignores_lambda_and_ratio_bias_sign():
+    # the TopK variant has no expert-wise scale and keeps k experts whatever
+    # the sign of the logits (a negative bias does not empty the selection)
+    L = make_custom(64, 8, 32, 64, 6, "f32", seed=14)
+    a = _fw_topk(L, 2)
+    b = _fw_topk(L, 2, lam=np.zeros(L.E))
+    c = _fw_topk(L, 2, b_r=L.b_r - 100.0)
+    assert np.array_equal(a.out, b.out)
+    assert np.all(c.active.sum(axis=1) == 2)
+    assert np.max(np.abs(a.out - c.out)) <= 1e-12 * _rms(a.out)   # a shift of every logit changes nothing
+
+
+@pytest.mark.parametrize("k", [1, 3])
+def test_topk_sparse_forward_equals_subset_bruteforce(k):
+    L = make_custom(128, 6, 64, 96, 9, "f32", seed=15)
+    r = _fw_topk(L, k)
+    bf = oracle.forward_dense_bruteforce(L.x, **L.weights(), eps=L.eps, top_k=k)
+    assert np.all(r.active.sum(axis=1) == k)
+    assert np.max(np.abs(r.out - bf)) <= 1e-12 * _rms(bf)
