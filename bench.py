@@ -125,29 +125,32 @@ def dense_ffn_time(d: int, dff: int, T: int, steps: int = 20) -> float:
 
 def sweep():
     """The decode layer at T in {1, 8}, the d=4096 layer over T in
-    {1, 16, 256, 2048} and the d=2048 layer at T=1024 over activation ratios
-    5..40 % (the d=2048 cases beside the dense-equivalent FFN):
+    {1, 16, 256, 2048}, the d=2048 layer at T=1024 over activation ratios
+    5..40 % (the d=2048 cases beside the dense-equivalent FFN), and the TopK
+    routing variant (k = 11 of 56 experts, 20 %) beside the ReLU routing at
+    T = 1, 8 and 4096:
     tokens/s and the fraction of the attainable roofline, max(B/BW, F/MFMA)/t,
     with B the decode byte count (weights touched + x in and out) and F the
     algorithmic flops.  Prints a table; no JSON line."""
     from synthetic import make_layer
     rows = []
-    cases = ([(2, T, None) for T in (1, 8)] + [(4, T, None) for T in (1, 16, 256, 2048)]
-             + [(5, 1024, r) for r in (0.05, 0.10, 0.20, 0.40)])
-    for cfg, T, ratio in cases:
+    cases = ([(2, T, None, 0) for T in (1, 8)] + [(4, T, None, 0) for T in (1, 16, 256, 2048)]
+             + [(5, 1024, r, 0) for r in (0.05, 0.10, 0.20, 0.40)]
+             + [(2, 1, None, 11), (2, 8, None, 11), (3, 4096, None, 0), (3, 4096, None, 11)])
+    for cfg, T, ratio, k in cases:
         L = make_layer(cfg, T=T, ratio=ratio)
         steps = 400 if T <= 16 else (100 if T <= 256 else 30)
-        r = run_workload(L, steps, max(5, steps // 10))
+        r = run_workload(L, steps, max(5, steps // 10), top_k=k)
         t = r["elapsed"] / steps
         B = decode_bytes(L, r["n_union"], T)
         Bt = sum(B.values()) + T * L.d * (2 if L.dtype == "bf16" else 4)
         Fl = layer_flops(L, r["P"], T)
         fb, ff = Bt / t / (HBM_PEAK_GBS * 1e9), Fl / t / (BF16_PEAK_TFLOPS * 1e12)
-        row = dict(cfg=f"c{cfg}", T=T, ratio=round(r["ratio"], 4), experts_touched=r["n_union"], pairs=r["P"],
+        row = dict(cfg=f"c{cfg}", T=T, routing=f"top{k}" if k else "relu", ratio=round(r["ratio"], 4), experts_touched=r["n_union"], pairs=r["P"],
                    us_per_call=round(t * 1e6, 2), tokens_per_s=round(T / t, 1),
                    hbm_frac=round(fb, 4), mfma_frac=round(ff, 4), attainable_frac=round(max(fb, ff), 4),
                    kernels_us={k: round(v * 1e3, 2) for k, v in r["kernels"].items()})
-        if cfg in (2, 5):
+        if cfg in (2, 5) and k == 0:
             td = dense_ffn_time(L.d, L.E * L.F + L.Fs, T, steps=200 if T <= 16 else 20)
             row["dense_ffn_us"] = round(td * 1e6, 2)
             row["speedup_vs_dense"] = round(td / t, 3)
@@ -162,7 +165,7 @@ def layer_weight_bytes(L) -> int:
 
 
 # GPU measurement ---------------------------------------------------------------
-def run_workload(L, steps: int, warmup: int, n_layers: int | None = None):
+def run_workload(L, steps: int, warmup: int, n_layers: int | None = None, top_k: int = 0):
     import numpy as np
     import torch
 
@@ -172,7 +175,7 @@ def run_workload(L, steps: int, warmup: int, n_layers: int | None = None):
     W = layer_tensors(L)
     if n_layers is None:
         n_layers = max(1, math.ceil(CACHE_DEFEAT_BYTES / layer_weight_bytes(L)))
-    layers = [dm.Layer(**W, max_tokens=L.T, eps=L.eps) for _ in range(n_layers)]
+    layers = [dm.Layer(**W, max_tokens=L.T, eps=L.eps, top_k=top_k) for _ in range(n_layers)]
     del W
     torch.cuda.synchronize()
     x = x_tensor(L)

@@ -67,11 +67,18 @@ typedef struct {
   int32_t max_tokens;   /* largest T passed to deco_moe_forward (>= 1)          */
   deco_dtype dtype;     /* element type of x, out and all weight matrices       */
   float rms_eps;        /* epsilon inside the NormSiLU RMS (e.g. 1e-6), >= 0    */
+  int32_t top_k;        /* 0: DECO's ReLU routing (above).  1..E: the TopK      */
+                        /* routing variant, the baseline of the DECO paper's    */
+                        /* Sec. 4 acceleration experiment (Table 4): each token */
+                        /* keeps the top_k largest logits z (ties to the lower  */
+                        /* expert index), gates = softmax of the kept logits,   */
+                        /* lambda unused; experts and shared expert unchanged.  */
 } deco_moe_config;
 
 /* Check a configuration without touching the GPU.  Returns DECO_OK,
- * DECO_ERR_INVALID_ARG (null, non-positive sizes, negative eps) or
- * DECO_ERR_UNSUPPORTED (shape outside the set documented in the struct). */
+ * DECO_ERR_INVALID_ARG (null, non-positive sizes, negative eps, top_k outside
+ * 0..n_experts) or DECO_ERR_UNSUPPORTED (shape outside the set documented in
+ * the struct). */
 int deco_moe_check_config(const deco_moe_config* cfg);
 
 /* Copy, pack and preprocess one layer's weights into library-owned device
@@ -112,7 +119,8 @@ int deco_moe_forward_path(const deco_moe_layer* L, const void* x, int64_t T, voi
 
 /* Routing state of the most recent forward on L, for the same T:
  *   mask   [T, ceil(E/64)] uint64 (device): bit e%64 of word e/64 of row t is
- *          set iff expert e was active for token t (z > 0 and lambda_e != 0);
+ *          set iff expert e was active for token t (z > 0 and lambda_e != 0;
+ *          with top_k > 0: e among the token's top_k logits);
  *   logits [T, E] float32 (device, may be NULL): router logits z as computed
  *          on the GPU (fp32 accumulation of the dtype products, plus b_r).
  * T must equal the T of that forward (not checked beyond 0 <= T <= max). */

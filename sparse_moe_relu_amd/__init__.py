@@ -41,7 +41,7 @@ class DecoConfig(ctypes.Structure):
     _fields_ = [("d_model", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("d_ff", ctypes.c_int32), ("d_ff_shared", ctypes.c_int32),
                 ("max_tokens", ctypes.c_int32), ("dtype", ctypes.c_int),
-                ("rms_eps", ctypes.c_float)]
+                ("rms_eps", ctypes.c_float), ("top_k", ctypes.c_int32)]
 
 
 class DecoError(RuntimeError):
@@ -98,9 +98,10 @@ def status_string(status: int) -> str:
 
 
 def make_config(d: int, E: int, F: int, Fs: int, max_tokens: int, dtype: str = "bf16",
-                eps: float = 1e-6) -> DecoConfig:
+                eps: float = 1e-6, top_k: int = 0) -> DecoConfig:
+    """top_k = 0: DECO's ReLU routing; 1..E: the TopK routing variant."""
     dt = {"bf16": DECO_DT_BF16, "f32": DECO_DT_F32}[dtype]
-    return DecoConfig(d, E, F, Fs, max_tokens, dt, eps)
+    return DecoConfig(d, E, F, Fs, max_tokens, dt, eps, top_k)
 
 
 def check_config(cfg: DecoConfig) -> int:
@@ -125,7 +126,7 @@ class Layer:
     """
 
     def __init__(self, W_r, b_r, lam, W_up, W_down, Ws_up, Ws_down, *, max_tokens: int,
-                 eps: float = 1e-6, stream=None):
+                 eps: float = 1e-6, top_k: int = 0, stream=None):
         lib = load_library()
         dtype = {torch.bfloat16: "bf16", torch.float32: "f32"}.get(W_up.dtype)
         if dtype is None:
@@ -141,7 +142,8 @@ class Layer:
         for name, t in (("b_r", b_r), ("lam", lam)):
             if tuple(t.shape) != (E,) or t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
                 raise ValueError(f"{name}: expected contiguous device float32 ({E},)")
-        self.cfg = make_config(d, E, F, Fs, max_tokens, dtype, eps)
+        self.cfg = make_config(d, E, F, Fs, max_tokens, dtype, eps, top_k)
+        self.top_k = top_k
         self.d, self.E, self.F, self.Fs, self.dtype = d, E, F, Fs, dtype
         self.max_tokens = max_tokens
         self.W = (E + 63) // 64

@@ -180,6 +180,60 @@ __device__ __forceinline__ unsigned arrive(unsigned* counter) {
   return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// TopK selection over one token's logits held by a wave: lane l holds
+// v[j] = z[64 j + l] (-inf past the last expert).  k rounds of a wave-wide
+// argmax (ties to the lower expert index) mark the kept experts in sel[j];
+// gates are the softmax of the kept logits: gate[j] = exp(z - zmax) / sum
+// (0 where not kept).  Every lane ends with the same selection.
+template <int NJ>
+__device__ __forceinline__ void topk_wave(const float (&z)[NJ], int k, bool (&sel)[NJ], float (&gate)[NJ]) {
+  const int l = threadIdx.x & 63;
+  float v[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    v[j] = z[j];
+    sel[j] = false;
+  }
+  float zmax = -__builtin_inff();
+  for (int r = 0; r < k; ++r) {
+    float bv = -__builtin_inff();
+    int bi = 1 << 30;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      if (v[j] > bv) {   // ascending j: on equal values the lower index stays
+        bv = v[j];
+        bi = 64 * j + l;
+      }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(bv, o);
+      const int oi = __shfl_xor(bi, o);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (r == 0) zmax = bv;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      if (bi == 64 * j + l) {
+        sel[j] = true;
+        v[j] = -__builtin_inff();
+      }
+  }
+  float part = 0.f;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    gate[j] = sel[j] ? expf(z[j] - zmax) : 0.f;
+    part += gate[j];
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o);
+  const float inv = 1.0f / part;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) gate[j] *= inv;
+}
+
 // Offset (bytes) of k-block kb of 16-column panel p in a packed matrix with nkb k-blocks.
 __host__ __device__ __forceinline__ size_t frag_off(int p, int kb, int nkb) {
   return ((size_t)p * nkb + kb) * FRAG_BYTES;

@@ -87,6 +87,8 @@ enum {
   KS_DEC_UP,
   KS_DEC_DOWN,
   KS_DEC_SUM,
+  KS_DEC_TOPK,
+  KS_PRE_TOPK,
   KS_PRE_ROUTER_SHARED,
   KS_PRE_DISPATCH,
   KS_PRE_EXPERT,

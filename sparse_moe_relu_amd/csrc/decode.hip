@@ -45,6 +45,7 @@ struct DecArgs {
   int T, d, E, F, Fs;
   int nkb_d, nkb_F, nkb_Fs, pF, pFs, pD, n_groups, Q;
   int n_shared, wg_per_e;   // up workgroups of the shared expert; per routed expert
+  int top_k, pR, W;         // TopK variant (0: ReLU routing); router panels; mask words
   const char* Wr_p;
   const char* Wup_p;
   const char* Wbar_p;
@@ -61,6 +62,7 @@ struct DecArgs {
   float* sspart;            // [E][wg_per_e][16] sums of squares of h - m over each slice
   char* sactf;              // shared-expert activations as down-projection operand fragments
   unsigned* rflag;          // [E] 1 no token routed to e, 2 some token did
+  uint64_t* mask;           // [T][W] routing masks (stored by the TopK router)
   float* part;
 };
 
@@ -95,6 +97,89 @@ __device__ __forceinline__ float ld_buf(__amdgpu_buffer_rsrc_t r, unsigned voff)
 }
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7FFFFFFF, 0x00020000);
+}
+
+// TopK routing variant (the baseline of the DECO paper's Sec. 4 acceleration
+// experiment, Table 4): one workgroup computes the logits of all experts for
+// the batch (MFMA, 16 padded rows; the waves split d, then add their
+// products in a fixed order), keeps each token's top_k experts (ties to the
+// lower index), stores logits, gates (softmax of the kept logits) and masks,
+// and publishes each expert's flag for the up and down kernels.
+template <class DT, int NW>
+__global__ void __launch_bounds__(NW * 64) k_dec_topk(DecArgs a) {
+  using elem = typename DT::elem;
+  constexpr int CH = 4, PG = 4;   // k-blocks and router panels per load batch
+  constexpr int PMAX = 16;        // router panels (E <= 256)
+  __shared__ f32x4_t s_red[NW][PG][64];
+  __shared__ float s_z[16][PMAX * 16];
+  __shared__ int s_act[PMAX * 16];
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 4, c = l & 15;
+  const int nkb = a.nkb_d;
+  const int kb_lo = (w * nkb) / NW, kb_hi = ((w + 1) * nkb) / NW;
+  const elem* xrow = (const elem*)a.x + (size_t)c * a.d;
+  const bool row_ok = c < a.T;
+  const __amdgpu_buffer_rsrc_t rw = buf_rsrc(a.Wr_p);
+  for (int e = tid; e < PMAX * 16; e += NW * 64) s_act[e] = 0;
+  for (int pg = 0; pg < a.pR; pg += PG) {
+    f32x4_t acc[PG];
+#pragma unroll
+    for (int p = 0; p < PG; ++p) acc[p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int kb0 = kb_lo; kb0 < kb_hi; kb0 += CH) {
+      i32x4_t xf[CH], wf[CH][PG];
+#pragma unroll
+      for (int u = 0; u < CH; ++u) {
+        const int kb = kb0 + u;
+        xf[u] = (kb < kb_hi && row_ok) ? load_row_frag<DT>(xrow, kb, g) : zero16();
+#pragma unroll
+        for (int p = 0; p < PG; ++p)
+          wf[u][p] = (kb < kb_hi && pg + p < a.pR) ? ld16_buf(rw, 16u * l, (unsigned)frag_off(pg + p, kb, nkb)) : zero16();
+      }
+#pragma unroll
+      for (int u = 0; u < CH; ++u)
+        if (kb0 + u < kb_hi) {
+#pragma unroll
+          for (int p = 0; p < PG; ++p) DT::mma(acc[p], xf[u], wf[u][p]);
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < PG; ++p) s_red[w][p][l] = acc[p];
+    __syncthreads();
+    // lane (c, g) of panel p holds rows 4 g + i of expert 16 p + c
+    for (int idx = tid; idx < PG * 256; idx += NW * 64) {
+      const int p = idx >> 8, ll = (idx >> 2) & 63, i = idx & 3;
+      float v = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) v += s_red[ww][p][ll][i];
+      s_z[4 * (ll >> 4) + i][(pg + p) * 16 + (ll & 15)] = v;
+    }
+    __syncthreads();
+  }
+  // one wave per token: keep the top_k logits
+  if (w < a.T) {
+    const int t = w;
+    float zv[4];
+    bool sel[4];
+    float gate[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = 64 * j + l;
+      zv[j] = e < a.E ? s_z[t][e] + a.b_r[e] : -__builtin_inff();
+    }
+    topk_wave<4>(zv, a.top_k, sel, gate);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = 64 * j + l;
+      if (e < a.E) {
+        a.z[(size_t)t * a.E + e] = zv[j];
+        a.g[(size_t)t * a.E + e] = gate[j];
+        if (sel[j]) s_act[e] = 1;
+      }
+      const unsigned long long word = __ballot(sel[j]);
+      if (l == 0 && j < a.W) a.mask[(size_t)t * a.W + j] = word;
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < a.E; e += NW * 64) a.rflag[e] = s_act[e] ? 2u : 1u;
 }
 
 template <class DT, int NW, int NP>
@@ -162,7 +247,21 @@ __global__ void __launch_bounds__(NW * 64) k_dec_up(DecArgs a) {
     }
   };
 
-  if (routed) {
+  if (routed && a.top_k > 0) {
+    // TopK variant: k_dec_topk has routed the batch; x and the mean-term
+    // weights load while the expert's flag is read
+    load_x(kb_lo);
+    load_w(a.Wbar_p, kb_lo);
+    if (a.rflag[e] != 2u) {
+      wait_all_mem();
+      return;  // no token keeps expert e: none of its weights are read
+    }
+    stream(a.Wbar_p, true, true);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) acc[p] = -acc[p];
+    stream(a.Wup_p + (size_t)e * a.up_stride, false, x_fits);
+  } else if (routed) {
     // router logits of expert e for the 16 (padded) token rows
     const float lam_e = a.lam[e];
     const float b_e = a.b_r[e];
@@ -482,6 +581,10 @@ hipError_t decode(const deco_moe_layer* L, const void* x, int T, void* out, hipS
   a.Q = L->dec_q;
   a.n_shared = L->pFs / DEC_NP;
   a.wg_per_e = L->pF / DEC_NP;
+  a.top_k = L->cfg.top_k;
+  a.pR = L->pR;
+  a.W = L->W;
+  a.mask = L->mask;
   a.Wr_p = L->Wr_p;
   a.Wup_p = L->Wup_p;
   a.Wbar_p = L->Wbar_p;
@@ -500,8 +603,13 @@ hipError_t decode(const deco_moe_layer* L, const void* x, int T, void* out, hipS
   a.sactf = L->sactf;
   a.rflag = L->rflag;
   a.part = L->part;
+  hipError_t err = hipSuccess;
+  if (a.top_k > 0) {
+    err = deco_host::launch(deco_host::KS_DEC_TOPK, k_dec_topk<DT, 16>, dim3(1), dim3(16 * 64), s, a);
+    if (err != hipSuccess) return err;
+  }
   const unsigned grid_up = (unsigned)(a.n_shared + L->E * a.wg_per_e);
-  hipError_t err = deco_host::launch(deco_host::KS_DEC_UP, k_dec_up<DT, DEC_NW, DEC_NP>, dim3(grid_up),
+  err = deco_host::launch(deco_host::KS_DEC_UP, k_dec_up<DT, DEC_NW, DEC_NP>, dim3(grid_up),
                                      dim3(DEC_NW * 64), s, a);
   if (err != hipSuccess) return err;
   const unsigned grid_dn = (unsigned)(L->n_groups * L->dec_q);

@@ -19,6 +19,7 @@ int validate_cfg(const deco_moe_config* c) {
   if (c->d_model <= 0 || c->n_experts < 1 || c->d_ff <= 0 || c->d_ff_shared <= 0 || c->max_tokens < 1)
     return DECO_ERR_INVALID_ARG;
   if (!(c->rms_eps >= 0.0f) || !isfinite(c->rms_eps)) return DECO_ERR_INVALID_ARG;
+  if (c->top_k < 0 || c->top_k > c->n_experts) return DECO_ERR_INVALID_ARG;
   if (c->dtype != DECO_DT_BF16 && c->dtype != DECO_DT_F32) return DECO_ERR_UNSUPPORTED;
   if (c->d_model % 64 != 0 || c->d_model > 32768) return DECO_ERR_UNSUPPORTED;
   if (c->n_experts > 256) return DECO_ERR_UNSUPPORTED;
@@ -105,6 +106,8 @@ const char* kernel_slot_name(int slot) {
     case KS_DEC_UP: return "k_dec_up";
     case KS_DEC_DOWN: return "k_dec_down";
     case KS_DEC_SUM: return "k_dec_sum";
+    case KS_DEC_TOPK: return "k_dec_topk";
+    case KS_PRE_TOPK: return "k_pre_topk";
     case KS_PRE_ROUTER_SHARED: return "k_pre_router_shared";
     case KS_PRE_DISPATCH: return "k_pre_dispatch";
     case KS_PRE_EXPERT: return "k_pre_expert";
@@ -295,7 +298,11 @@ int deco_moe_copy_routing(const deco_moe_layer* L, int64_t T, uint64_t* mask, fl
   if (!L || T < 0 || T > L->maxT || !mask) return DECO_ERR_INVALID_ARG;
   if (T == 0) return DECO_OK;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t err = deco_host::launch_copy_mask(L, (int)T, mask, s);
+  // ReLU routing: the mask follows from the logits and lambda; TopK: the
+  // routing kernels stored it
+  hipError_t err = L->cfg.top_k > 0
+      ? hipMemcpyAsync(mask, L->mask, sizeof(uint64_t) * (size_t)T * L->W, hipMemcpyDeviceToDevice, s)
+      : deco_host::launch_copy_mask(L, (int)T, mask, s);
   if (err == hipSuccess && logits)
     err = hipMemcpyAsync(logits, L->z, sizeof(float) * (size_t)T * L->E, hipMemcpyDeviceToDevice, s);
   return err == hipSuccess ? DECO_OK : DECO_ERR_HIP;

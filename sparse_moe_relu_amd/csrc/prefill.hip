@@ -41,6 +41,7 @@ struct PreArgs {
   const void* x;
   void* out;
   int T, Tcap, d, E, F, Fs, W;
+  int top_k;           // TopK routing variant (0: ReLU routing)
   int nkb_d, nkb_F, nkb_Fs, pR, pF, pD, pFs;
   int pF4, pFs4;       // panel counts of the mean and shared sections, padded to 4
   int rs_nt;           // 8-panel column tiles of the router/mean/shared GEMM
@@ -211,6 +212,32 @@ __global__ void __launch_bounds__(256, 2) k_pre_router_shared(PreArgs a) {
         }
       }
     }
+  }
+}
+
+// --------------------------------------------------------------------------
+// TopK routing variant (the baseline of the DECO paper's Sec. 4 acceleration
+// experiment, Table 4): one wave per token keeps the top_k largest of the
+// logits the router GEMM stored (ties to the lower expert index) and
+// replaces the token's gates (softmax of the kept logits) and mask words.
+__global__ void __launch_bounds__(256) k_pre_topk(PreArgs a) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6), l = threadIdx.x & 63;
+  if (t >= a.T) return;
+  float zv[4];
+  bool sel[4];
+  float gate[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = 64 * j + l;
+    zv[j] = e < a.E ? a.z[(size_t)t * a.E + e] : -__builtin_inff();
+  }
+  topk_wave<4>(zv, a.top_k, sel, gate);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = 64 * j + l;
+    if (e < a.E) a.g[(size_t)t * a.E + e] = gate[j];
+    const unsigned long long word = __ballot(sel[j]);
+    if (l == 0 && j < a.W) a.mask[(size_t)t * a.W + j] = word;
   }
 }
 
@@ -695,6 +722,7 @@ hipError_t prefill(const deco_moe_layer* L, const void* x, int T, void* out, hip
   a.F = L->F;
   a.Fs = L->Fs;
   a.W = L->W;
+  a.top_k = L->cfg.top_k;
   a.nkb_d = L->nkb_d;
   a.nkb_F = L->nkb_F;
   a.nkb_Fs = L->nkb_Fs;
@@ -732,6 +760,8 @@ hipError_t prefill(const deco_moe_layer* L, const void* x, int T, void* out, hip
   hipError_t err = rs_grid <= (unsigned)L->n_cu
       ? launch(deco_host::KS_PRE_ROUTER_SHARED, k_pre_router_shared<DT, 4>, dim3(rs_grid), dim3(256), s, a)
       : launch(deco_host::KS_PRE_ROUTER_SHARED, k_pre_router_shared<DT, DECO_PRE_NS>, dim3(rs_grid), dim3(256), s, a);
+  if (err == hipSuccess && a.top_k > 0)
+    err = launch(deco_host::KS_PRE_TOPK, k_pre_topk, dim3((unsigned)((T + 3) / 4)), dim3(256), s, a);
   if (err == hipSuccess)
     err = launch(deco_host::KS_PRE_DISPATCH, k_pre_dispatch, dim3(L->E + 1), dim3(DISP_NT), s, a);
   if (err == hipSuccess)

@@ -60,11 +60,15 @@ def test_status_strings(lib):
     (dict(F=512), dm.DECO_ERR_UNSUPPORTED),
     (dict(Fs=48), dm.DECO_ERR_UNSUPPORTED),
     (dict(T=(1 << 20) + 1), dm.DECO_ERR_UNSUPPORTED),
+    (dict(top_k=1), dm.DECO_OK),
+    (dict(top_k=8), dm.DECO_OK),
+    (dict(top_k=9), dm.DECO_ERR_INVALID_ARG),
+    (dict(top_k=-1), dm.DECO_ERR_INVALID_ARG),
 ])
 def test_check_config(lib, kw, expect):
-    a = dict(d=64, E=8, F=32, Fs=64, T=16, dtype="f32", eps=1e-6)
+    a = dict(d=64, E=8, F=32, Fs=64, T=16, dtype="f32", eps=1e-6, top_k=0)
     a.update(kw)
-    cfg = dm.make_config(a["d"], a["E"], a["F"], a["Fs"], a["T"], a["dtype"], a["eps"])
+    cfg = dm.make_config(a["d"], a["E"], a["F"], a["Fs"], a["T"], a["dtype"], a["eps"], a["top_k"])
     assert dm.check_config(cfg) == expect
 
 
