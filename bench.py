@@ -316,6 +316,8 @@ def main():
                     help="profiler mode: GPU loop of --workload only, no JSON")
     ap.add_argument("--profile-summary", nargs=3, metavar=("DB", "OUT", "COMMAND"),
                     help="write a text summary of a rocprofv3 kernel-trace database (no GPU needed)")
+    ap.add_argument("--top-k", type=int, default=0,
+                    help="profiler mode: run the TopK routing variant with this k")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="profiler mode: first copy this many MiB device to device (PMC calibration)")
     ap.add_argument("--pmc-summary", nargs=6,
@@ -357,7 +359,7 @@ def main():
             torch.cuda.synchronize()
             del src, dst
         L = make_layer(2) if args.workload == "decode" else make_layer(3)
-        r = run_workload(L, args.steps, args.warmup)
+        r = run_workload(L, args.steps, args.warmup, top_k=args.top_k)
         log(f"{args.workload}: {r['elapsed'] / args.steps * 1e6:.2f} us/step kernels={r['kernels']}")
         return
 

@@ -180,47 +180,59 @@ __device__ __forceinline__ unsigned arrive(unsigned* counter) {
   return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// TopK selection over one token's logits held by a wave: lane l holds
-// v[j] = z[64 j + l] (-inf past the last expert).  k rounds of a wave-wide
-// argmax (ties to the lower expert index) mark the kept experts in sel[j];
-// gates are the softmax of the kept logits: gate[j] = exp(z - zmax) / sum
-// (0 where not kept).  Every lane ends with the same selection.
+// TopK selection over one token's logits, by a wave: lane l holds
+// z[j] = logit of expert 64 j + l (-inf past the last expert).  Logits map to
+// unsigned keys in the same order; a bitwise binary search with ballots and
+// popcounts finds the k-th largest key (32 steps, no cross-lane data
+// movement), every expert above it is kept, and experts equal to it are kept
+// in ascending index order until k are kept (ties to the lower index).  The
+// largest key is found the same way.  Gates are the softmax of the kept
+// logits: gate[j] = exp(z - zmax) / sum over kept (0 where not kept).
+__device__ __forceinline__ unsigned order_key(float v) {
+  const unsigned u = __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <int NJ>
+__device__ __forceinline__ unsigned kth_largest_key(const unsigned (&key)[NJ], int k) {
+  unsigned prefix = 0u;
+  for (int bit = 31; bit >= 0; --bit) {
+    const unsigned cand = prefix | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) cnt += __popcll(__ballot(key[j] >= cand));
+    if (cnt >= k) prefix = cand;
+  }
+  return prefix;
+}
+
 template <int NJ>
 __device__ __forceinline__ void topk_wave(const float (&z)[NJ], int k, bool (&sel)[NJ], float (&gate)[NJ]) {
   const int l = threadIdx.x & 63;
-  float v[NJ];
+  unsigned key[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) key[j] = order_key(z[j]);
+  const unsigned kth = kth_largest_key<NJ>(key, k);
+  const unsigned kmax = kth_largest_key<NJ>(key, 1);
+  int above = 0;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    v[j] = z[j];
-    sel[j] = false;
+    sel[j] = key[j] > kth;
+    above += __popcll(__ballot(sel[j]));
   }
-  float zmax = -__builtin_inff();
-  for (int r = 0; r < k; ++r) {
-    float bv = -__builtin_inff();
-    int bi = 1 << 30;
+  int need = k - above;   // >= 1: at least one key equals the k-th largest
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      if (v[j] > bv) {   // ascending j: on equal values the lower index stays
-        bv = v[j];
-        bi = 64 * j + l;
-      }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(bv, o);
-      const int oi = __shfl_xor(bi, o);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
+  for (int j = 0; j < NJ; ++j) {
+    unsigned long long tie = __ballot(key[j] == kth);
+    while (need > 0 && tie != 0ull) {
+      const int b = __builtin_ctzll(tie);
+      if (l == b) sel[j] = true;
+      tie &= tie - 1ull;
+      --need;
     }
-    if (r == 0) zmax = bv;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      if (bi == 64 * j + l) {
-        sel[j] = true;
-        v[j] = -__builtin_inff();
-      }
   }
+  // the largest logit, from its key (the map is invertible)
+  const float zmax = __uint_as_float((kmax & 0x80000000u) ? (kmax & 0x7FFFFFFFu) : ~kmax);
   float part = 0.f;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {

@@ -150,7 +150,8 @@ __global__ void __launch_bounds__(NW * 64) k_dec_topk(DecArgs a) {
       float v = 0.f;
 #pragma unroll
       for (int ww = 0; ww < NW; ++ww) v += s_red[ww][p][ll][i];
-      s_z[4 * (ll >> 4) + i][(pg + p) * 16 + (ll & 15)] = v;
+      const int e = (pg + p) * 16 + (ll & 15);
+      s_z[4 * (ll >> 4) + i][e] = v + (e < a.E ? a.b_r[e] : 0.f);
     }
     __syncthreads();
   }
@@ -163,7 +164,7 @@ __global__ void __launch_bounds__(NW * 64) k_dec_topk(DecArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = 64 * j + l;
-      zv[j] = e < a.E ? s_z[t][e] + a.b_r[e] : -__builtin_inff();
+      zv[j] = e < a.E ? s_z[t][e] : -__builtin_inff();
     }
     topk_wave<4>(zv, a.top_k, sel, gate);
 #pragma unroll
