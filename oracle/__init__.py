@@ -4,8 +4,8 @@ Only the tests, the smoke check and the benchmark's CPU-baseline leg use this
 package.  The product path (the HIP library and its binding) never imports
 it, and it imports nothing from the product path.
 """
-from .deco_oracle import (router, router_topk, mean_up, normsilu, silu, expert_mlp, shared_expert,
+from .deco_oracle import (router, router_topk, mean_up, normsilu, silu, expert_mlp, expert_mlp_gated, shared_expert,
                           forward, forward_dense_bruteforce, OracleResult)
 
-__all__ = ["router", "router_topk", "mean_up", "normsilu", "silu", "expert_mlp", "shared_expert",
+__all__ = ["router", "router_topk", "mean_up", "normsilu", "silu", "expert_mlp", "expert_mlp_gated", "shared_expert",
            "forward", "forward_dense_bruteforce", "OracleResult"]

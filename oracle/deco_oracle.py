@@ -31,6 +31,13 @@ Readings taken where the text is silent:
   * experts are non-gated two-matrix MLPs with no biases;
   * shared expert: non-gated MLP with plain SiLU, weight 1, no lambda;
   * no residual: the result is the FFN sublayer output only.
+  * gated variant ("DECO (gated)", [W-CN] 二 and [P-DECO] Sec. 2 "Expert
+    design", which compare it with the non-gated experts): a routed expert
+    has a gate projection W_gate[e] next to W_up[e]; NormSiLU acts on the gate
+    projection (its mean term from the mean of ALL experts' gate projections,
+    its RMS over the gate row) and multiplies the up projection elementwise:
+    a = NormSiLU(x.W_gate[e]) * (x.W_up[e]), y = a.W_down[e]; the shared
+    expert is unchanged;
   * TopK variant (top_k = k > 0): the same router projection; each token keeps
     the k experts with the largest logits, ties going to the lower expert
     index; gates are the softmax of the kept logits (conventional TopK
@@ -136,6 +143,20 @@ def expert_mlp(x_rows, m_rows, W_up_e, W_down_e, eps):
     return normsilu(h, m_rows, eps) @ np.asarray(W_down_e, np.float64)
 
 
+def expert_mlp_gated(x_rows, m_rows, W_gate_e, W_up_e, W_down_e, eps):
+    """One gated routed expert ("DECO (gated)"): NormSiLU of the gate
+    projection times the up projection, then the down-projection.
+
+    [W-CN] Sec. 二 (gated MLP experts carry an extra multiplicative
+    interaction); [P-DECO] Sec. 2 "Expert design".  m_rows is x . Wbar with
+    Wbar the mean of the gate projections.  x_rows [n,d] -> [n,d].
+    """
+    x_rows = np.asarray(x_rows, np.float64)
+    hg = x_rows @ np.asarray(W_gate_e, np.float64)
+    u = x_rows @ np.asarray(W_up_e, np.float64)
+    return (normsilu(hg, m_rows, eps) * u) @ np.asarray(W_down_e, np.float64)
+
+
 def shared_expert(x, Ws_up, Ws_down):
     """Always-on shared expert: non-gated MLP with plain SiLU, weight 1.
 
@@ -155,7 +176,8 @@ class OracleResult:
     shared: np.ndarray   # [T, d] shared-expert part of out
 
 
-def forward(x, W_r, b_r, lam, W_up, W_down, Ws_up, Ws_down, eps=1e-6, top_k: int = 0) -> OracleResult:
+def forward(x, W_r, b_r, lam, W_up, W_down, Ws_up, Ws_down, eps=1e-6, top_k: int = 0,
+            W_gate=None) -> OracleResult:
     """Sparse evaluation of one DECO layer, expert by expert.
 
     Steps: router (the ReLU router, or with top_k > 0 the TopK variant);
@@ -163,20 +185,24 @@ def forward(x, W_r, b_r, lam, W_up, W_down, Ws_up, Ws_down, eps=1e-6, top_k: int
     in ascending order (per-expert bucketing), the expert MLP on those rows,
     and out[S_e] += g[S_e, e] * y (gate-weighted combine, [P-DECO] Sec. 2
     "Router design": the router assigns a weight to each expert); finally the
-    shared expert is added.
+    shared expert is added.  With W_gate [E,d,F] the routed experts are the
+    gated variant (`expert_mlp_gated`) and the mean term comes from W_gate.
     """
     x = np.asarray(x, np.float64)
     T, d = x.shape
     W_up = np.asarray(W_up, np.float64)
     E = W_up.shape[0]
     z, active, g = router_topk(x, W_r, b_r, top_k) if top_k > 0 else router(x, W_r, b_r, lam)
-    m = x @ mean_up(W_up)
+    m = x @ mean_up(W_up if W_gate is None else W_gate)
     routed = np.zeros((T, d))
     for e in range(E):
         S = np.nonzero(active[:, e])[0]
         if S.size == 0:
             continue
-        y = expert_mlp(x[S], m[S], W_up[e], W_down[e], eps)
+        if W_gate is None:
+            y = expert_mlp(x[S], m[S], W_up[e], W_down[e], eps)
+        else:
+            y = expert_mlp_gated(x[S], m[S], np.asarray(W_gate, np.float64)[e], W_up[e], W_down[e], eps)
         routed[S] += g[S, e][:, None] * y
     shared = shared_expert(x, Ws_up, Ws_down)
     return OracleResult(out=routed + shared, z=z, active=active, g=g, routed=routed, shared=shared)
@@ -200,7 +226,7 @@ def _topk_gates_by_subsets(z_row: np.ndarray, k: int) -> np.ndarray:
 
 
 def forward_dense_bruteforce(x, W_r, b_r, lam, W_up, W_down, Ws_up, Ws_down, eps=1e-6,
-                             top_k: int = 0) -> np.ndarray:
+                             top_k: int = 0, W_gate=None) -> np.ndarray:
     """Dense brute force for small inputs: every expert for every token.
 
     Ignores the mask: each (token, expert) pair is evaluated one at a time,
@@ -221,13 +247,16 @@ def forward_dense_bruteforce(x, W_r, b_r, lam, W_up, W_down, Ws_up, Ws_down, eps
     else:
         _, _, g = router(x, W_r, b_r, lam)
     out = np.zeros((T, d))
+    Wn = W_up if W_gate is None else np.asarray(W_gate, np.float64)   # NormSiLU input
     for t in range(T):
-        h_all = np.stack([x[t] @ W_up[e] for e in range(E)])      # [E, F]
+        h_all = np.stack([x[t] @ Wn[e] for e in range(E)])      # [E, F]
         m_t = h_all.sum(axis=0) / E
         for e in range(E):
             ht = h_all[e] - m_t
             r = np.sqrt(np.mean(ht * ht) + eps)
             a = silu(ht / r)
+            if W_gate is not None:
+                a = a * (x[t] @ W_up[e])
             out[t] += g[t, e] * (a @ W_down[e])
         out[t] += silu(x[t] @ np.asarray(Ws_up, np.float64)) @ np.asarray(Ws_down, np.float64)
     return out

@@ -102,10 +102,14 @@ class LayerInputs:
     Ws_up: np.ndarray    # [d, Fs]
     Ws_down: np.ndarray  # [Fs, d]
     name: str = ""
+    W_gate: np.ndarray | None = None   # [E, d, F], gated-expert layers only
 
     def weights(self) -> dict:
-        return dict(W_r=self.W_r, b_r=self.b_r, lam=self.lam, W_up=self.W_up,
-                    W_down=self.W_down, Ws_up=self.Ws_up, Ws_down=self.Ws_down)
+        w = dict(W_r=self.W_r, b_r=self.b_r, lam=self.lam, W_up=self.W_up,
+                 W_down=self.W_down, Ws_up=self.Ws_up, Ws_down=self.Ws_down)
+        if self.W_gate is not None:
+            w["W_gate"] = self.W_gate
+        return w
 
     def with_x(self, x: np.ndarray) -> "LayerInputs":
         return dataclasses.replace(self, x=np.asarray(x, dtype=np.float64), T=int(x.shape[0]))
@@ -113,9 +117,12 @@ class LayerInputs:
 
 def make_custom(d: int, E: int, F: int, Fs: int, T: int, dtype: str = "bf16", *,
                 seed: int = 0, ratio: float = 0.20, lam: str = "lognormal-var0.5",
-                skew_var: float = 0.0, eps: float = 1e-6, name: str = "custom") -> LayerInputs:
-    """Draw one layer of the given shape with the recipe in the module docstring."""
-    ss = np.random.SeedSequence(seed).spawn(8)
+                skew_var: float = 0.0, eps: float = 1e-6, name: str = "custom",
+                gated: bool = False) -> LayerInputs:
+    """Draw one layer of the given shape with the recipe in the module docstring.
+    gated: also a gate projection W_gate [E,d,F] ~ N(0, 1/d) from a ninth
+    sub-stream (the first eight, and so the other weights, are unchanged)."""
+    ss = np.random.SeedSequence(seed).spawn(9 if gated else 8)
     rng = [np.random.Generator(np.random.PCG64(s)) for s in ss]
     x = _cast(rng[0].standard_normal((T, d)), dtype)
     W_r = _cast(rng[1].standard_normal((d, E)) / math.sqrt(d), dtype)
@@ -136,17 +143,20 @@ def make_custom(d: int, E: int, F: int, Fs: int, T: int, dtype: str = "bf16", *,
     if skew_var > 0.0:
         b = b + math.sqrt(skew_var) * rng[7].standard_normal(E)
     f32 = lambda a: np.asarray(a, dtype=np.float32).astype(np.float64)
+    W_gate = None
+    if gated:
+        W_gate = _cast(np.random.Generator(np.random.PCG64(ss[8])).standard_normal((E, d, F)) / math.sqrt(d), dtype)
     return LayerInputs(d=d, E=E, F=F, Fs=Fs, T=T, dtype=dtype, eps=eps, x=x, W_r=W_r,
                        b_r=f32(b), lam=f32(lam_v), W_up=W_up, W_down=W_down,
-                       Ws_up=Ws_up, Ws_down=Ws_down, name=name)
+                       Ws_up=Ws_up, Ws_down=Ws_down, name=name, W_gate=W_gate)
 
 
 def make_layer(cfg_id: int, seed: int = 0, *, T: int | None = None,
-               ratio: float | None = None) -> LayerInputs:
+               ratio: float | None = None, gated: bool = False) -> LayerInputs:
     """The synthetic workload `cfg_id` (1..5).  `T` overrides the token count
     (the d=4096 layer is swept over T), `ratio` the target activation ratio
     (the ratio-sweep workload)."""
     c = CONFIGS[cfg_id]
     return make_custom(c["d"], c["E"], c["F"], c["Fs"], c["T"] if T is None else T,
                        c["dtype"], seed=seed, ratio=c["ratio"] if ratio is None else ratio,
-                       lam=c["lam"], skew_var=c["skew_var"], name=c["name"])
+                       lam=c["lam"], skew_var=c["skew_var"], name=c["name"], gated=gated)

@@ -342,3 +342,49 @@ def test_topk_sparse_forward_equals_subset_bruteforce(k):
     bf = oracle.forward_dense_bruteforce(L.x, **L.weights(), eps=L.eps, top_k=k)
     assert np.all(r.active.sum(axis=1) == k)
     assert np.max(np.abs(r.out - bf)) <= 1e-12 * _rms(bf)
+
+
+# gated-expert variant --------------------------------------------------------
+def test_gated_sparse_forward_equals_dense_bruteforce():
+    L = make_custom(128, 7, 64, 96, 10, "f32", seed=21, gated=True, ratio=0.3)
+    r = oracle.forward(L.x, **L.weights(), eps=L.eps)
+    bf = oracle.forward_dense_bruteforce(L.x, **L.weights(), eps=L.eps)
+    assert r.active.any() and not r.active.all()
+    assert np.max(np.abs(r.out - bf)) <= 1e-12 * _rms(bf)
+
+
+def test_gated_with_unit_up_projection_is_the_nongated_layer_on_the_gate():
+    # x carries a constant-1 feature and W_up reads only it, so x.W_up = 1:
+    # the gated expert must reduce to the non-gated one whose up-projection
+    # is W_gate (catches swapped gate/up roles and a mean term on the wrong
+    # projection)
+    L = make_custom(64, 6, 32, 64, 9, "f32", seed=22, gated=True, ratio=0.4)
+    x = L.x.copy()
+    x[:, -1] = 1.0
+    W_one = np.zeros_like(L.W_up)
+    W_one[:, -1, :] = 1.0
+    w = L.weights()
+    gated = oracle.forward(x, **dict(w, W_up=W_one), eps=L.eps)
+    w.pop("W_gate")
+    plain = oracle.forward(x, **dict(w, W_up=L.W_gate), eps=L.eps)
+    assert gated.active.any()
+    assert np.max(np.abs(gated.out - plain.out)) <= 1e-12 * _rms(plain.out)
+
+
+def test_gated_routed_part_is_linear_in_the_up_projection():
+    L = make_custom(64, 6, 32, 64, 9, "f32", seed=23, gated=True, ratio=0.4)
+    a = oracle.forward(L.x, **L.weights(), eps=L.eps)
+    b = oracle.forward(L.x, **dict(L.weights(), W_up=-3.0 * L.W_up), eps=L.eps)
+    assert np.max(np.abs(b.routed + 3.0 * a.routed)) <= 1e-12 * _rms(a.routed)
+    assert np.array_equal(a.shared, b.shared)
+
+
+def test_gated_mean_term_is_the_mean_gate_projection():
+    # shifting every expert's gate projection by the same matrix leaves the
+    # mean-subtracted gate rows, and so the layer, unchanged
+    L = make_custom(64, 6, 32, 64, 9, "f32", seed=24, gated=True, ratio=0.4)
+    rng = np.random.default_rng(5)
+    shift = rng.standard_normal((L.d, L.F))
+    a = oracle.forward(L.x, **L.weights(), eps=L.eps)
+    b = oracle.forward(L.x, **dict(L.weights(), W_gate=L.W_gate + shift[None]), eps=L.eps)
+    assert np.max(np.abs(a.out - b.out)) <= 1e-10 * _rms(a.out)
