@@ -105,6 +105,27 @@ int deco_moe_load_weights(const deco_moe_config* cfg,
                           const void* Ws_up, const void* Ws_down,
                           void* stream, deco_moe_layer** out_layer);
 
+/* The gated-expert variant ("DECO (gated)" in the DECO paper's Sec. 2
+ * "Expert design" comparison, which the paper sets against its non-gated
+ * experts; the qidianchuan.cn write-up, section 二, describes gated MLPs as
+ * carrying an extra multiplicative interaction).  Each routed expert has a
+ * gate projection next to its up-projection, and NormSiLU acts on the gate
+ * projection:
+ *   Wbar    = (1/E) sum_e W_gate[e]               mean term from the gates
+ *   h~      = x_t W_gate[e] - x_t Wbar,  r = sqrt(mean_f h~_f^2 + eps)
+ *   out_t  += g_te * (SiLU(h~ / r) * (x_t W_up[e])) W_down[e]
+ * Router, routing variants and shared expert are as in deco_moe_load_weights.
+ *   W_gate  [E, d, F]   dtype     routed gate projections (NormSiLU input)
+ *   W_up    [E, d, F]   dtype     routed up-projections (multiplied in)
+ * Every other argument, the ownership and the error behaviour are those of
+ * deco_moe_load_weights; deco_moe_copy_mean_up returns the mean of W_gate.
+ * The forward calls below take either kind of layer. */
+int deco_moe_load_weights_gated(const deco_moe_config* cfg,
+                                const void* W_r, const float* b_r, const float* lambda,
+                                const void* W_gate, const void* W_up, const void* W_down,
+                                const void* Ws_up, const void* Ws_down,
+                                void* stream, deco_moe_layer** out_layer);
+
 /* One forward pass: out [T, d] = DECO layer(x [T, d]), both of the layer's
  * dtype, on device.  x and out must not overlap.  Asynchronous on `stream`;
  * allocates nothing and never waits on the host.  T == 0 returns DECO_OK and
@@ -127,7 +148,8 @@ int deco_moe_forward_path(const deco_moe_layer* L, const void* x, int64_t T, voi
 int deco_moe_copy_routing(const deco_moe_layer* L, int64_t T, uint64_t* mask, float* logits,
                           void* stream);
 
-/* Copy the inter-expert mean Wbar [d, F] (float32, device) built at load. */
+/* Copy the inter-expert mean Wbar [d, F] (float32, device) built at load
+ * (of W_up, or of W_gate for a gated layer). */
 int deco_moe_copy_mean_up(const deco_moe_layer* L, float* wbar, void* stream);
 
 /* Health flags of L's device-side work, read synchronously (waits for all

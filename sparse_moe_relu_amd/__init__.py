@@ -31,7 +31,7 @@ DECO_PATH_DECODE = 1
 DECO_PATH_PREFILL = 2
 DECODE_MAX_T = 16
 
-EXPORTS = ("deco_moe_check_config", "deco_moe_load_weights", "deco_moe_forward",
+EXPORTS = ("deco_moe_check_config", "deco_moe_load_weights", "deco_moe_load_weights_gated", "deco_moe_forward",
            "deco_moe_forward_path", "deco_moe_copy_routing", "deco_moe_copy_mean_up",
            "deco_moe_free", "deco_moe_status_string", "deco_moe_read_error_flags", "deco_moe_timing_enable",
            "deco_moe_timing_reset", "deco_moe_timing_read")
@@ -68,6 +68,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.deco_moe_load_weights.argtypes = [ctypes.POINTER(DecoConfig), vp, vp, vp, vp, vp, vp, vp, vp,
                                           ctypes.POINTER(vp)]
     lib.deco_moe_load_weights.restype = i32
+    lib.deco_moe_load_weights_gated.argtypes = [ctypes.POINTER(DecoConfig), vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                ctypes.POINTER(vp)]
+    lib.deco_moe_load_weights_gated.restype = i32
     lib.deco_moe_forward.argtypes = [vp, vp, i64, vp, vp]
     lib.deco_moe_forward.restype = i32
     lib.deco_moe_forward_path.argtypes = [vp, vp, i64, vp, vp, i32]
@@ -123,10 +126,13 @@ class Layer:
     Weights are device tensors of the layer dtype (b_r and lam: float32):
     W_r [d,E], b_r [E], lam [E], W_up [E,d,F], W_down [E,F,d], Ws_up [d,Fs],
     Ws_down [Fs,d].  They are packed at construction and may be freed after.
+    W_gate [E,d,F] (optional) selects the gated-expert variant
+    (deco_moe_load_weights_gated): NormSiLU acts on x.W_gate[e] and the
+    result multiplies x.W_up[e].
     """
 
     def __init__(self, W_r, b_r, lam, W_up, W_down, Ws_up, Ws_down, *, max_tokens: int,
-                 eps: float = 1e-6, top_k: int = 0, stream=None):
+                 eps: float = 1e-6, top_k: int = 0, W_gate=None, stream=None):
         lib = load_library()
         dtype = {torch.bfloat16: "bf16", torch.float32: "f32"}.get(W_up.dtype)
         if dtype is None:
@@ -135,6 +141,8 @@ class Layer:
         Fs = Ws_up.shape[1]
         shapes = {"W_r": (W_r, (d, E)), "W_up": (W_up, (E, d, F)), "W_down": (W_down, (E, F, d)),
                   "Ws_up": (Ws_up, (d, Fs)), "Ws_down": (Ws_down, (Fs, d))}
+        if W_gate is not None:
+            shapes["W_gate"] = (W_gate, (E, d, F))
         for name, (t, shp) in shapes.items():
             if tuple(t.shape) != shp or t.dtype != W_up.dtype or not t.is_cuda or not t.is_contiguous():
                 raise ValueError(f"{name}: expected contiguous device {shp} {W_up.dtype}, got "
@@ -144,16 +152,25 @@ class Layer:
                 raise ValueError(f"{name}: expected contiguous device float32 ({E},)")
         self.cfg = make_config(d, E, F, Fs, max_tokens, dtype, eps, top_k)
         self.top_k = top_k
+        self.gated = W_gate is not None
         self.d, self.E, self.F, self.Fs, self.dtype = d, E, F, Fs, dtype
         self.max_tokens = max_tokens
         self.W = (E + 63) // 64
         h = ctypes.c_void_p()
-        st = lib.deco_moe_load_weights(ctypes.byref(self.cfg), W_r.data_ptr(), b_r.data_ptr(),
-                                       lam.data_ptr(), W_up.data_ptr(), W_down.data_ptr(),
-                                       Ws_up.data_ptr(), Ws_down.data_ptr(), _stream_handle(stream),
-                                       ctypes.byref(h))
+        if W_gate is None:
+            st = lib.deco_moe_load_weights(ctypes.byref(self.cfg), W_r.data_ptr(), b_r.data_ptr(),
+                                           lam.data_ptr(), W_up.data_ptr(), W_down.data_ptr(),
+                                           Ws_up.data_ptr(), Ws_down.data_ptr(), _stream_handle(stream),
+                                           ctypes.byref(h))
+            what = "deco_moe_load_weights"
+        else:
+            st = lib.deco_moe_load_weights_gated(ctypes.byref(self.cfg), W_r.data_ptr(), b_r.data_ptr(),
+                                                 lam.data_ptr(), W_gate.data_ptr(), W_up.data_ptr(),
+                                                 W_down.data_ptr(), Ws_up.data_ptr(), Ws_down.data_ptr(),
+                                                 _stream_handle(stream), ctypes.byref(h))
+            what = "deco_moe_load_weights_gated"
         if st != DECO_OK:
-            raise DecoError(st, "deco_moe_load_weights")
+            raise DecoError(st, what)
         self._h = h
 
     @property

@@ -24,13 +24,16 @@ struct deco_moe_layer {
   int dec_ok;              // the decode path is available for this layer
   int pre_grid;            // persistent grid of the prefill expert kernel
   int n_cu;                // compute units of the device
+  int gated;               // gated routed experts: NormSiLU(x.W_gate[e]) * (x.W_up[e])
 
   // packed weights (one allocation)
   char* wmem;
   size_t wmem_bytes;
   char* Wr_p;              // router  [pR][nkb_d] frags
-  char* Wup_p;             // per expert [pF][nkb_d] frags of W_up[e]
-  char* Wbar_p;            // [pF][nkb_d] frags of Wbar (layer dtype)
+  char* Wup_p;             // per expert [pF][nkb_d] frags of the NormSiLU input projection
+                           // (W_up[e]; W_gate[e] for gated experts)
+  char* Wlin_p;            // gated experts: per expert [pF][nkb_d] frags of W_up[e]; else null
+  char* Wbar_p;            // [pF][nkb_d] frags of Wbar, the mean of the Wup_p matrices (layer dtype)
   char* Wdn_p;             // per expert [pD][nkb_F] frags
   char* Wdn16_p;           // bf16 layers: W_down again, in fp16 (prefill); fp32 layers: = Wdn_p
   char* Wsu_p;             // [pFs][nkb_d]
@@ -49,6 +52,7 @@ struct deco_moe_layer {
   // decode
   float* mbuf;             // [Tcap][F]    x . Wbar (NormSiLU mean term)
   float* hbuf;             // [E][16][F]   h - m rows of each routed expert (decode)
+  float* ubuf;             // [E][16][F]   gated experts: x . W_up[e] rows (decode); else null
   float* sspart;           // [E][16][16]  per-slice sums of squares of h - m (decode)
   char* sactf;             // [nkb_Fs] frags      shared SiLU output
   unsigned* rflag;         // [E] routing of the last decode call (1 no token, 2 some token routed to e)
@@ -98,8 +102,10 @@ enum {
 const char* kernel_slot_name(int slot);
 
 // launchers (return hipSuccess or the launch error)
-hipError_t launch_pack_all(deco_moe_layer* L, const void* W_r, const void* W_up, const void* W_down,
-                           const void* Ws_up, const void* Ws_down, hipStream_t s);
+// W_norm: the projection NormSiLU acts on (W_up, or W_gate for gated
+// experts); W_lin: gated experts' W_up (null otherwise)
+hipError_t launch_pack_all(deco_moe_layer* L, const void* W_r, const void* W_norm, const void* W_lin,
+                           const void* W_down, const void* Ws_up, const void* Ws_down, hipStream_t s);
 hipError_t plan_decode(deco_moe_layer* L);   // decode launch shape (load time)
 hipError_t plan_prefill(deco_moe_layer* L);  // prefill launch shape (load time)
 hipError_t launch_decode(const deco_moe_layer* L, const void* x, int T, void* out, hipStream_t s);

@@ -46,8 +46,10 @@ struct DecArgs {
   int nkb_d, nkb_F, nkb_Fs, pF, pFs, pD, n_groups, Q;
   int n_shared, wg_per_e;   // up workgroups of the shared expert; per routed expert
   int top_k, pR, W;         // TopK variant (0: ReLU routing); router panels; mask words
+  int gated;                // 1: gated experts (up workgroups for W_up[e] follow each expert's own)
   const char* Wr_p;
-  const char* Wup_p;
+  const char* Wup_p;        // NormSiLU input projection (a gated expert's gate projection)
+  const char* Wlin_p;       // gated experts' up-projection
   const char* Wbar_p;
   const char* Wdn_p;        // W_down in the operand type of the routed down-projection
   const char* Wsu_p;
@@ -59,6 +61,7 @@ struct DecArgs {
   float* z;
   float* g;
   float* hbuf;              // [E][16][F] h - m of each token row
+  float* ubuf;              // [E][16][F] gated experts: x . W_up[e] of each token row
   float* sspart;            // [E][wg_per_e][16] sums of squares of h - m over each slice
   char* sactf;              // shared-expert activations as down-projection operand fragments
   unsigned* rflag;          // [E] 1 no token routed to e, 2 some token did
@@ -194,13 +197,19 @@ __global__ void __launch_bounds__(NW * 64) k_dec_up(DecArgs a) {
   __shared__ f32x4_t s_red[NW][4][64];
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 4, c = l & 15;
   // grid order: shared-expert slices (they need no router result, so they
-  // stream from the start), then (routed expert, slice)
+  // stream from the start), then (routed expert, slice); a gated expert's
+  // slices of its NormSiLU input come first, then those of its W_up
   const int bid = blockIdx.x;
   const bool routed = bid >= a.n_shared;
   const int rb = bid - a.n_shared;
-  const int e = routed ? rb / a.wg_per_e : 0;
-  const int wgi = routed ? rb % a.wg_per_e : 0;
+  const int spe = a.wg_per_e << a.gated;
+  const int e = routed ? rb / spe : 0;
+  const int rs = routed ? rb % spe : 0;
+  const bool lin = rs >= a.wg_per_e;   // W_up slice of a gated expert: no mean term, no RMS
+  const int wgi = lin ? rs - a.wg_per_e : rs;
   const int p0 = routed ? wgi * NP : bid * NP;
+  // what the first stream reads: the mean term, or a gated expert's W_up
+  const char* w_first = lin ? a.Wlin_p + (size_t)e * a.up_stride : a.Wbar_p;
   const int nkb = a.nkb_d;
   const int kb_lo = (w * nkb) / NW, kb_hi = ((w + 1) * nkb) / NW;
   const elem* xrow = (const elem*)a.x + (size_t)c * a.d;
@@ -249,19 +258,21 @@ __global__ void __launch_bounds__(NW * 64) k_dec_up(DecArgs a) {
   };
 
   if (routed && a.top_k > 0) {
-    // TopK variant: k_dec_topk has routed the batch; x and the mean-term
+    // TopK variant: k_dec_topk has routed the batch; x and the first
     // weights load while the expert's flag is read
     load_x(kb_lo);
-    load_w(a.Wbar_p, kb_lo);
+    load_w(w_first, kb_lo);
     if (a.rflag[e] != 2u) {
       wait_all_mem();
       return;  // no token keeps expert e: none of its weights are read
     }
-    stream(a.Wbar_p, true, true);
-    __builtin_amdgcn_sched_barrier(0);
+    stream(w_first, true, true);
+    if (!lin) {
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int p = 0; p < NP; ++p) acc[p] = -acc[p];
-    stream(a.Wup_p + (size_t)e * a.up_stride, false, x_fits);
+      for (int p = 0; p < NP; ++p) acc[p] = -acc[p];
+      stream(a.Wup_p + (size_t)e * a.up_stride, false, x_fits);
+    }
   } else if (routed) {
     // router logits of expert e for the 16 (padded) token rows
     const float lam_e = a.lam[e];
@@ -281,8 +292,8 @@ __global__ void __launch_bounds__(NW * 64) k_dec_up(DecArgs a) {
     }
     __builtin_amdgcn_sched_barrier(0);   // keep the router's registers apart from the weights'
     if (!x_fits) load_x(kb_lo);
-    // the mean-term weights load while the waves combine their logits
-    load_w(a.Wbar_p, kb_lo);
+    // the first weights load while the waves combine their logits
+    load_w(w_first, kb_lo);
     zp += __shfl_xor(zp, 16);
     zp += __shfl_xor(zp, 32);
     if (g == 0) s_zred[w][c] = zp;
@@ -295,7 +306,7 @@ __global__ void __launch_bounds__(NW * 64) k_dec_up(DecArgs a) {
     zz += b_e;
     const bool act = c < a.T && zz > 0.f && lam_e != 0.f;
     const bool any = __ballot(act) != 0ull;
-    if (wgi == 0 && w == 0) {
+    if (rs == 0 && w == 0) {
       if (l == 0) a.rflag[e] = any ? 2u : 1u;
       if (l < a.T) {
         a.z[(size_t)l * a.E + e] = zz;
@@ -307,13 +318,15 @@ __global__ void __launch_bounds__(NW * 64) k_dec_up(DecArgs a) {
       return;  // inactive expert: none of its weights are read
     }
     // acc = -(x . Wbar) + x . W_up[e]: the NormSiLU mean term and the expert
-    // in one fp32 accumulator
-    stream(a.Wbar_p, true, true);
-    __builtin_amdgcn_sched_barrier(0);   // keep the two streams' registers apart
+    // in one fp32 accumulator (a gated expert's W_up slice: acc = x . W_up[e])
+    stream(w_first, true, true);
+    if (!lin) {
+      __builtin_amdgcn_sched_barrier(0);   // keep the two streams' registers apart
 #pragma unroll
-    for (int p = 0; p < NP; ++p) acc[p] = -acc[p];
-    // (with a single chunk per wave xf still holds it)
-    stream(a.Wup_p + (size_t)e * a.up_stride, false, x_fits);
+      for (int p = 0; p < NP; ++p) acc[p] = -acc[p];
+      // (with a single chunk per wave xf still holds it)
+      stream(a.Wup_p + (size_t)e * a.up_stride, false, x_fits);
+    }
   } else {
     stream(a.Wsu_p, false, false);
   }
@@ -335,7 +348,8 @@ __global__ void __launch_bounds__(NW * 64) k_dec_up(DecArgs a) {
     if (mine) *reinterpret_cast<elem*>(a.sactf + frag_elem_off<DT>(row, col)) = DT::from_f32(silu_f(v));
     return;
   }
-  if (mine && row < a.T) a.hbuf[((size_t)e * 16 + row) * a.F + col] = v;
+  if (mine && row < a.T) (lin ? a.ubuf : a.hbuf)[((size_t)e * 16 + row) * a.F + col] = v;
+  if (lin) return;
   // per-row sum of squares over this slice: lanes with equal l & 3 of a wave
   // hold one row (4 (w & 3) + (l & 3)) of panel w >> 2, columns l >> 2
   float sq = v * v;
@@ -353,7 +367,7 @@ __global__ void __launch_bounds__(NW * 64) k_dec_up(DecArgs a) {
   }
 }
 
-template <class DT, int NW, bool MULTI>
+template <class DT, int NW, bool MULTI, bool GATED>
 __global__ void __launch_bounds__(NW * 64) k_dec_down(DecArgs a) {
   using elem = typename DT::elem;
   using DN = typename DT::Down;   // operand type of the routed down-projection
@@ -428,29 +442,43 @@ __global__ void __launch_bounds__(NW * 64) k_dec_down(DecArgs a) {
   // raw activation operands of a chunk: for a routed unit (expert e, k-block
   // kb) lane (c, g) takes h - m of token row c at the EPL columns its
   // fragment holds (rows past T read nothing: the buffer range check returns
-  // zeros); for a shared unit, the stored fragment
+  // zeros), and for gated experts x . W_up[e] at the same place; for a
+  // shared unit, the stored fragment
   const __amdgpu_buffer_rsrc_t rh = buf_rsrc(a.hbuf), rs = buf_rsrc(a.sactf);
+  const __amdgpu_buffer_rsrc_t ru = buf_rsrc(GATED ? a.ubuf : a.hbuf);
   float hv[UB][EPL];
+  float uv[UB][GATED ? EPL : 1];
   auto load_a = [&](int u0) {
 #pragma unroll
     for (int ub = 0; ub < UB; ++ub) {
       const int u = u0 + ub * NW;
-      i32x4_t r[EPL / 4];
+      i32x4_t r[EPL / 4], r2[EPL / 4];
       if (u < rhi) {
         const int e = s_ulist[u / a.nkb_F], kb = u % a.nkb_F;
         const unsigned off = c < a.T ? 4u * (unsigned)((e * 16 + c) * a.F + kb * DT::KB + EPL * g) : OOB;
 #pragma unroll
         for (int k = 0; k < EPL / 4; ++k) r[k] = ld16_buf(rh, off + 16u * k, 0u);
+        if constexpr (GATED) {
+#pragma unroll
+          for (int k = 0; k < EPL / 4; ++k) r2[k] = ld16_buf(ru, off + 16u * k, 0u);
+        }
       } else {   // a shared unit, or past the range (reads nothing)
         const unsigned off = u < hi ? (unsigned)((u - n_routed_units) * FRAG_BYTES) + 16u * l : OOB;
         r[0] = ld16_buf(rs, off, 0u);
 #pragma unroll
         for (int k = 1; k < EPL / 4; ++k) r[k] = zero16();
+        if constexpr (GATED) {
+#pragma unroll
+          for (int k = 0; k < EPL / 4; ++k) r2[k] = zero16();
+        }
       }
 #pragma unroll
       for (int k = 0; k < EPL / 4; ++k)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) hv[ub][4 * k + j] = __int_as_float(r[k][j]);
+        for (int j = 0; j < 4; ++j) {
+          hv[ub][4 * k + j] = __int_as_float(r[k][j]);
+          if constexpr (GATED) uv[ub][4 * k + j] = __int_as_float(r2[k][j]);
+        }
     }
   };
   load_b(lo + w);
@@ -489,11 +517,16 @@ __global__ void __launch_bounds__(NW * 64) k_dec_down(DecArgs a) {
       __builtin_amdgcn_sched_barrier(0);   // one unit's temporaries at a time
       if (u < hi) {
         if (u < n_routed_units) {
-          // gated NormSiLU, rounded once to the down-projection operand type
+          // NormSiLU times the router gate (and, for gated experts, times
+          // x . W_up[e]), rounded once to the down-projection operand type
           const int k = (u / a.nkb_F - i0) * 16 + c;
           const float rinv = s_rinv[k], gt = s_gate[k];
 #pragma unroll
-          for (int j = 0; j < EPL; ++j) hv[ub][j] = gt != 0.f ? silu_f(hv[ub][j] * rinv) * gt : 0.f;
+          for (int j = 0; j < EPL; ++j) {
+            float v = silu_f(hv[ub][j] * rinv) * gt;
+            if constexpr (GATED) v *= uv[ub][j];
+            hv[ub][j] = gt != 0.f ? v : 0.f;
+          }
           const i32x4_t af = DN::pack(hv[ub]);
 #pragma unroll
           for (int p = 0; p < DP; ++p) DN::mma(acc[p], af, bfr[ub][p]);
@@ -583,6 +616,9 @@ hipError_t decode(const deco_moe_layer* L, const void* x, int T, void* out, hipS
   a.n_shared = L->pFs / DEC_NP;
   a.wg_per_e = L->pF / DEC_NP;
   a.top_k = L->cfg.top_k;
+  a.gated = L->gated;
+  a.Wlin_p = L->Wlin_p;
+  a.ubuf = L->ubuf;
   a.pR = L->pR;
   a.W = L->W;
   a.mask = L->mask;
@@ -609,14 +645,14 @@ hipError_t decode(const deco_moe_layer* L, const void* x, int T, void* out, hipS
     err = deco_host::launch(deco_host::KS_DEC_TOPK, k_dec_topk<DT, 16>, dim3(1), dim3(16 * 64), s, a);
     if (err != hipSuccess) return err;
   }
-  const unsigned grid_up = (unsigned)(a.n_shared + L->E * a.wg_per_e);
+  const unsigned grid_up = (unsigned)(a.n_shared + L->E * (a.wg_per_e << a.gated));
   err = deco_host::launch(deco_host::KS_DEC_UP, k_dec_up<DT, DEC_NW, DEC_NP>, dim3(grid_up),
                                      dim3(DEC_NW * 64), s, a);
   if (err != hipSuccess) return err;
   const unsigned grid_dn = (unsigned)(L->n_groups * L->dec_q);
-  err = L->dec_multi
-      ? deco_host::launch(deco_host::KS_DEC_DOWN, k_dec_down<DT, DEC_NW, true>, dim3(grid_dn), dim3(DEC_NW * 64), s, a)
-      : deco_host::launch(deco_host::KS_DEC_DOWN, k_dec_down<DT, DEC_NW, false>, dim3(grid_dn), dim3(DEC_NW * 64), s, a);
+  auto down = L->dec_multi ? (a.gated ? k_dec_down<DT, DEC_NW, true, true> : k_dec_down<DT, DEC_NW, true, false>)
+                           : (a.gated ? k_dec_down<DT, DEC_NW, false, true> : k_dec_down<DT, DEC_NW, false, false>);
+  err = deco_host::launch(deco_host::KS_DEC_DOWN, down, dim3(grid_dn), dim3(DEC_NW * 64), s, a);
   if (err != hipSuccess) return err;
   const unsigned grid_sum = (unsigned)((T * L->d / 4 + 255) / 256);
   err = deco_host::launch(deco_host::KS_DEC_SUM, k_dec_sum<DT>, dim3(grid_sum), dim3(256), s, a);

@@ -155,20 +155,24 @@ void deco_moe_free(deco_moe_layer* L) {
   delete L;
 }
 
-int deco_moe_load_weights(const deco_moe_config* cfg, const void* W_r, const float* b_r,
-                          const float* lambda, const void* W_up, const void* W_down, const void* Ws_up,
-                          const void* Ws_down, void* stream, deco_moe_layer** out_layer) {
+// Both loaders.  W_norm is the projection NormSiLU acts on (W_up, or W_gate
+// of gated experts) and the one Wbar averages; W_lin is gated experts' W_up.
+static int load_layer(const deco_moe_config* cfg, const void* W_r, const float* b_r, const float* lambda,
+                      const void* W_norm, bool gated, const void* W_lin, const void* W_down,
+                      const void* Ws_up, const void* Ws_down, void* stream, deco_moe_layer** out_layer) {
   if (!out_layer) return DECO_ERR_INVALID_ARG;
   *out_layer = nullptr;
   int st = validate_cfg(cfg);
   if (st != DECO_OK) return st;
-  if (!W_r || !b_r || !lambda || !W_up || !W_down || !Ws_up || !Ws_down) return DECO_ERR_INVALID_ARG;
+  if (!W_r || !b_r || !lambda || !W_norm || !W_down || !Ws_up || !Ws_down) return DECO_ERR_INVALID_ARG;
+  if (gated && !W_lin) return DECO_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
 
   deco_moe_layer* L = new (std::nothrow) deco_moe_layer();
   if (!L) return DECO_ERR_OUT_OF_MEMORY;
   memset(L, 0, sizeof(*L));
   L->cfg = *cfg;
+  L->gated = gated;
   derive(L);
   if (hipGetDevice(&L->device) != hipSuccess) {
     delete L;
@@ -182,6 +186,7 @@ int deco_moe_load_weights(const deco_moe_config* cfg, const void* W_r, const flo
   L->up_stride = (size_t)L->pF * L->nkb_d * KBy;
   L->dn_stride = (size_t)L->pD * L->nkb_F * KBy;
   size_t o_up = w.take(L->up_stride * E);
+  size_t o_lin = L->gated ? w.take(L->up_stride * E) : 0;
   size_t o_wbp = w.take((size_t)L->pF * L->nkb_d * KBy);
   size_t o_dn = w.take(L->dn_stride * E);
   size_t o_dn16 = L->cfg.dtype == DECO_DT_BF16 ? w.take(L->dn_stride * E) : o_dn;
@@ -199,6 +204,7 @@ int deco_moe_load_weights(const deco_moe_config* cfg, const void* W_r, const flo
   size_t o_m = k.take(sizeof(uint64_t) * Tcap * L->W);
   size_t o_mb = k.take(sizeof(float) * Tcap * L->F);
   size_t o_h = k.take(sizeof(float) * (size_t)E * 16 * L->F);
+  size_t o_u = L->gated ? k.take(sizeof(float) * (size_t)E * 16 * L->F) : 0;
   size_t o_ss = k.take(sizeof(float) * (size_t)E * 16 * 16);
   size_t o_sf = k.take((size_t)L->nkb_Fs * KBy);
   size_t o_rf = k.take(sizeof(unsigned) * E);
@@ -224,6 +230,7 @@ int deco_moe_load_weights(const deco_moe_config* cfg, const void* W_r, const flo
   }
   L->Wr_p = L->wmem + o_wr;
   L->Wup_p = L->wmem + o_up;
+  L->Wlin_p = L->gated ? L->wmem + o_lin : nullptr;
   L->Wbar_p = L->wmem + o_wbp;
   L->Wdn_p = L->wmem + o_dn;
   L->Wdn16_p = L->wmem + o_dn16;
@@ -237,6 +244,7 @@ int deco_moe_load_weights(const deco_moe_config* cfg, const void* W_r, const flo
   L->mask = (uint64_t*)(L->ws + o_m);
   L->mbuf = (float*)(L->ws + o_mb);
   L->hbuf = (float*)(L->ws + o_h);
+  L->ubuf = L->gated ? (float*)(L->ws + o_u) : nullptr;
   L->sspart = (float*)(L->ws + o_ss);
   L->sactf = L->ws + o_sf;
   L->rflag = (unsigned*)(L->ws + o_rf);
@@ -255,7 +263,7 @@ int deco_moe_load_weights(const deco_moe_config* cfg, const void* W_r, const flo
   err = hipMemsetAsync(L->ws, 0, zero_end, s);
   if (err == hipSuccess) err = hipMemcpyAsync(L->b_r, b_r, sizeof(float) * E, hipMemcpyDeviceToDevice, s);
   if (err == hipSuccess) err = hipMemcpyAsync(L->lam, lambda, sizeof(float) * E, hipMemcpyDeviceToDevice, s);
-  if (err == hipSuccess) err = deco_host::launch_pack_all(L, W_r, W_up, W_down, Ws_up, Ws_down, s);
+  if (err == hipSuccess) err = deco_host::launch_pack_all(L, W_r, W_norm, W_lin, W_down, Ws_up, Ws_down, s);
   if (err == hipSuccess) err = deco_host::plan_decode(L);
   if (err == hipSuccess) err = deco_host::plan_prefill(L);
   if (err == hipSuccess) err = hipStreamSynchronize(s);
@@ -266,6 +274,19 @@ int deco_moe_load_weights(const deco_moe_config* cfg, const void* W_r, const flo
   }
   *out_layer = L;
   return DECO_OK;
+}
+
+int deco_moe_load_weights(const deco_moe_config* cfg, const void* W_r, const float* b_r,
+                          const float* lambda, const void* W_up, const void* W_down, const void* Ws_up,
+                          const void* Ws_down, void* stream, deco_moe_layer** out_layer) {
+  return load_layer(cfg, W_r, b_r, lambda, W_up, false, nullptr, W_down, Ws_up, Ws_down, stream, out_layer);
+}
+
+int deco_moe_load_weights_gated(const deco_moe_config* cfg, const void* W_r, const float* b_r,
+                                const float* lambda, const void* W_gate, const void* W_up,
+                                const void* W_down, const void* Ws_up, const void* Ws_down, void* stream,
+                                deco_moe_layer** out_layer) {
+  return load_layer(cfg, W_r, b_r, lambda, W_gate, true, W_up, W_down, Ws_up, Ws_down, stream, out_layer);
 }
 
 int deco_moe_forward_path(const deco_moe_layer* L, const void* x, int64_t T, void* out, void* stream,

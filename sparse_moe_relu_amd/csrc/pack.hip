@@ -55,9 +55,11 @@ __global__ void __launch_bounds__(256) k_pack(const SRC* __restrict__ src, size_
   st16(dst + (size_t)b * dst_bstride + frag_off(p, kb, nkb) + (size_t)l * 16, DT::pack(f));
 }
 
+// W_up here is the projection NormSiLU acts on (a gated expert's gate
+// projection); W_lin, when given, is a gated expert's up-projection.
 template <class DT>
-hipError_t pack_all(deco_moe_layer* L, const void* W_r, const void* W_up, const void* W_down,
-                    const void* Ws_up, const void* Ws_down, hipStream_t s) {
+hipError_t pack_all(deco_moe_layer* L, const void* W_r, const void* W_up, const void* W_lin,
+                    const void* W_down, const void* Ws_up, const void* Ws_down, hipStream_t s) {
   using E_t = typename DT::elem;
   const int d = L->d, E = L->E, F = L->F, Fs = L->Fs;
   const size_t dF = (size_t)d * F;
@@ -72,6 +74,9 @@ hipError_t pack_all(deco_moe_layer* L, const void* W_r, const void* W_up, const 
   // routed up: K = d, N = F
   k_pack<DT, E_t><<<grid(L->pF, L->nkb_d, E), 256, 0, s>>>((const E_t*)W_up, dF, d, F, F, L->pF, L->nkb_d,
                                                            L->Wup_p, L->up_stride);
+  if (W_lin)
+    k_pack<DT, E_t><<<grid(L->pF, L->nkb_d, E), 256, 0, s>>>((const E_t*)W_lin, dF, d, F, F, L->pF, L->nkb_d,
+                                                             L->Wlin_p, L->up_stride);
   // inter-expert mean, in the layer dtype: K = d, N = F
   k_pack<DT, float><<<grid(L->pF, L->nkb_d, 1), 256, 0, s>>>(L->wbar, 0, d, F, F, L->pF, L->nkb_d,
                                                             L->Wbar_p, 0);
@@ -95,10 +100,10 @@ hipError_t pack_all(deco_moe_layer* L, const void* W_r, const void* W_up, const 
 
 namespace deco_host {
 
-hipError_t launch_pack_all(deco_moe_layer* L, const void* W_r, const void* W_up, const void* W_down,
-                           const void* Ws_up, const void* Ws_down, hipStream_t s) {
-  if (L->cfg.dtype == DECO_DT_BF16) return pack_all<BF16>(L, W_r, W_up, W_down, Ws_up, Ws_down, s);
-  return pack_all<F32>(L, W_r, W_up, W_down, Ws_up, Ws_down, s);
+hipError_t launch_pack_all(deco_moe_layer* L, const void* W_r, const void* W_norm, const void* W_lin,
+                           const void* W_down, const void* Ws_up, const void* Ws_down, hipStream_t s) {
+  if (L->cfg.dtype == DECO_DT_BF16) return pack_all<BF16>(L, W_r, W_norm, W_lin, W_down, Ws_up, Ws_down, s);
+  return pack_all<F32>(L, W_r, W_norm, W_lin, W_down, Ws_up, Ws_down, s);
 }
 
 }  // namespace deco_host

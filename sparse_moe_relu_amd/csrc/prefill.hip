@@ -46,7 +46,8 @@ struct PreArgs {
   int pF4, pFs4;       // panel counts of the mean and shared sections, padded to 4
   int rs_nt;           // 8-panel column tiles of the router/mean/shared GEMM
   const char* Wr_p;
-  const char* Wup_p;
+  const char* Wup_p;       // NormSiLU input projection (a gated expert's gate projection)
+  const char* Wlin_p;      // gated experts' up-projection
   const char* Wbar_p;
   const char* Wdn_p;
   const char* Wdn16_p;     // down-projection operand of the prefill path (fp16 or fp32)
@@ -317,10 +318,12 @@ __global__ void __launch_bounds__(DISP_NT) k_pre_dispatch(PreArgs a) {
 }
 
 // --------------------------------------------------------------------------
-template <class DT, int BNP>
+template <class DT, int BNP, bool GATED>
 struct ExpertShape {
   using DN = typename DT::Down;                      // down-projection operand type
-  static constexpr int BM = BNP >= 16 ? 64 : 128;    // token rows per tile
+  // token rows per tile (gated experts hold a second up-projection
+  // accumulator, so their tiles have half the rows)
+  static constexpr int BM = (BNP >= 16 || GATED) ? 64 : 128;
   using TC = Tile<DT, BM, BNP, DECO_PRE_NS>;          // up-projection ring
   static constexpr int F = BNP * 16;
   static constexpr int NKF = F / DN::KB;             // k-blocks of the down-projection
@@ -358,10 +361,14 @@ struct ExpertShape {
 //                 to slot 0 of each token's pairs.
 // Expert tiles come first (they are the longer ones); each XCD works through
 // its own contiguous range of both lists.
-template <class DT, int BNP>
-__global__ void __launch_bounds__(256, (ExpertShape<DT, BNP>::OCC)) k_pre_expert(PreArgs a) {
+//
+// GATED: a routed expert's NormSiLU output is multiplied, element by
+// element, by x . W_up[e] (a second pass of the tile over W_lin before the
+// NormSiLU input's pass; its accumulators wait in registers).
+template <class DT, int BNP, bool GATED>
+__global__ void __launch_bounds__(256, (ExpertShape<DT, BNP, GATED>::OCC)) k_pre_expert(PreArgs a) {
   using elem = typename DT::elem;
-  using S = ExpertShape<DT, BNP>;
+  using S = ExpertShape<DT, BNP, GATED>;
   using TC = typename S::TC;
   using DN = typename S::DN;
   using PT = typename DT::pair;
@@ -477,11 +484,16 @@ __global__ void __launch_bounds__(256, (ExpertShape<DT, BNP>::OCC)) k_pre_expert
       return x + (size_t)(tk >= 0 ? tk : 0) * a.d;
     };
     auto panel = [&](int p) -> const char* { return Wu + frag_off(p, 0, a.nkb_d); };
-    f32x4_t acc[MB][NBW];
+    f32x4_t acc[MB][NBW], accu[MB][NBW];
 #pragma unroll
     for (int i = 0; i < MB; ++i)
 #pragma unroll
-      for (int j = 0; j < NBW; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < NBW; ++j) acc[i][j] = accu[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if constexpr (GATED) {
+      const char* Wl = a.Wlin_p + (size_t)e * a.up_stride;
+      auto panel_lin = [&](int p) -> const char* { return Wl + frag_off(p, 0, a.nkb_d); };
+      tile_gemm<DT, TC, true>(lds, row, panel_lin, a.nkb_d, accu);
+    }
     tile_gemm<DT, TC, true>(lds, row, panel, a.nkb_d, acc);
 
     // NormSiLU.  Lane: local row R = wm*BM/2 + 16 i + c, columns
@@ -521,7 +533,10 @@ __global__ void __launch_bounds__(256, (ExpertShape<DT, BNP>::OCC)) k_pre_expert
         const int p = wn * NBW + j;
         float v[4];
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) v[ii] = ok ? silu_f(acc[i][j][ii] * inv_r) : 0.f;
+        for (int ii = 0; ii < 4; ++ii) {
+          v[ii] = ok ? silu_f(acc[i][j][ii] * inv_r) : 0.f;
+          if constexpr (GATED) v[ii] *= accu[i][j][ii];
+        }
         if constexpr (DN::KB == 32) {
           // f = 16 p + 4 g + ii: k-block p / 2, lane group 2 (p % 2) + g / 2,
           // elements 4 (g % 2) + ii of the lane
@@ -701,11 +716,15 @@ __global__ void __launch_bounds__(256) k_copy_mask(const float* __restrict__ z, 
   mask[idx] = word;
 }
 
+template <class DT, bool GATED>
+void (*expert_kernel_g(int pF))(PreArgs) {
+  return pF == 2 ? k_pre_expert<DT, 2, GATED>
+       : pF == 4 ? k_pre_expert<DT, 4, GATED>
+       : pF == 8 ? k_pre_expert<DT, 8, GATED> : k_pre_expert<DT, 16, GATED>;
+}
 template <class DT>
-void (*expert_kernel(int pF))(PreArgs) {
-  return pF == 2 ? k_pre_expert<DT, 2>
-       : pF == 4 ? k_pre_expert<DT, 4>
-       : pF == 8 ? k_pre_expert<DT, 8> : k_pre_expert<DT, 16>;
+void (*expert_kernel(int pF, bool gated))(PreArgs) {
+  return gated ? expert_kernel_g<DT, true>(pF) : expert_kernel_g<DT, false>(pF);
 }
 
 int round4(int v) { return (v + 3) / 4 * 4; }
@@ -735,6 +754,7 @@ hipError_t prefill(const deco_moe_layer* L, const void* x, int T, void* out, hip
   a.rs_nt = (a.pR + a.pF4 + a.pFs4 + GP - 1) / GP;
   a.Wr_p = L->Wr_p;
   a.Wup_p = L->Wup_p;
+  a.Wlin_p = L->Wlin_p;
   a.Wbar_p = L->Wbar_p;
   a.Wdn_p = L->Wdn_p;
   a.Wsu_p = L->Wsu_p;
@@ -765,7 +785,7 @@ hipError_t prefill(const deco_moe_layer* L, const void* x, int T, void* out, hip
   if (err == hipSuccess)
     err = launch(deco_host::KS_PRE_DISPATCH, k_pre_dispatch, dim3(L->E + 1), dim3(DISP_NT), s, a);
   if (err == hipSuccess)
-    err = launch(deco_host::KS_PRE_EXPERT, expert_kernel<DT>(L->pF), dim3(L->pre_grid), dim3(256), s, a);
+    err = launch(deco_host::KS_PRE_EXPERT, expert_kernel<DT>(L->pF, L->gated), dim3(L->pre_grid), dim3(256), s, a);
   if (err == hipSuccess)
     err = launch(deco_host::KS_PRE_COMBINE, k_pre_combine<DT>,
                  dim3((unsigned)(((long long)T * (L->d / 8) + 255) / 256)), dim3(256), s, a);
@@ -785,7 +805,8 @@ hipError_t launch_prefill(const deco_moe_layer* L, const void* x, int T, void* o
 // Persistent grid of the expert kernel: as many workgroups as fit on the
 // device at once, a multiple of the 8 XCDs.
 hipError_t plan_prefill(deco_moe_layer* L) {
-  void (*kx)(PreArgs) = L->cfg.dtype == DECO_DT_BF16 ? expert_kernel<BF16>(L->pF) : expert_kernel<F32>(L->pF);
+  void (*kx)(PreArgs) = L->cfg.dtype == DECO_DT_BF16 ? expert_kernel<BF16>(L->pF, L->gated)
+                                                    : expert_kernel<F32>(L->pF, L->gated);
   int occ = 0, cus = 0;
   hipError_t err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kx, 256, 0);
   if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, L->device);

@@ -92,6 +92,13 @@ def test_host_side_rejections_touch_no_device(lib):
                                      ctypes.byref(h)) == dm.DECO_ERR_UNSUPPORTED
     assert lib.deco_moe_load_weights(ctypes.byref(cfg), None, None, None, None, None, None, None, None,
                                      None) == dm.DECO_ERR_INVALID_ARG
+    # gated loader: same order of checks; a missing up-projection is rejected too
+    st = lib.deco_moe_load_weights_gated(ctypes.byref(cfg), *([None] * 9), ctypes.byref(h))
+    assert st == dm.DECO_ERR_INVALID_ARG and not h.value
+    h.value = 1234
+    assert lib.deco_moe_load_weights_gated(ctypes.byref(bad), *([None] * 9),
+                                           ctypes.byref(h)) == dm.DECO_ERR_UNSUPPORTED and not h.value
+    assert lib.deco_moe_load_weights_gated(ctypes.byref(cfg), *([None] * 9), None) == dm.DECO_ERR_INVALID_ARG
     # null layer
     assert lib.deco_moe_forward(None, None, 0, None, None) == dm.DECO_ERR_INVALID_ARG
     assert lib.deco_moe_forward_path(None, None, 4, None, None, 1) == dm.DECO_ERR_INVALID_ARG
