@@ -80,9 +80,10 @@ def decode_bytes(L, n_union: int, T: int) -> dict:
     method must read (router, bias and scale, the two matrices of each expert
     touched by the batch, the shared expert) plus x in and out.  The
     mean-term matrix and the hand-off buffers between the kernels are not
-    counted."""
+    counted.  Gated experts add their W_up to the up kernel's bytes."""
     s = 2 if L.dtype == "bf16" else 4
-    up = L.d * L.E * s + 8 * L.E + n_union * L.d * L.F * s + L.d * L.Fs * s + T * L.d * s
+    n_up = 2 if L.W_gate is not None else 1
+    up = L.d * L.E * s + 8 * L.E + n_up * n_union * L.d * L.F * s + L.d * L.Fs * s + T * L.d * s
     down = n_union * L.F * L.d * s + L.Fs * L.d * s
     return {"k_dec_up": up, "k_dec_down": down, "k_dec_sum": T * L.d * s}
 
@@ -91,17 +92,21 @@ def prefill_flops(L, P: int, T: int) -> dict:
     """Algorithmic flops per launch, per kernel: router and shared up-projection
     (the x.Wbar mean term is not counted); routed up + down over the P active
     (token, expert) pairs plus the shared down-projection; the dispatch and the
-    combine (a sum of pair rows) do no matrix work."""
+    combine (a sum of pair rows) do no matrix work.  Gated experts have
+    three matrices per pair instead of two."""
+    n_mat = 3 if L.W_gate is not None else 2
     return {"k_pre_router_shared": 2 * T * L.d * L.E + 2 * T * L.d * L.Fs,
             "k_pre_dispatch": 0,
-            "k_pre_expert": 4 * P * L.d * L.F + 2 * T * L.d * L.Fs,
+            "k_pre_expert": 2 * n_mat * P * L.d * L.F + 2 * T * L.d * L.Fs,
             "k_pre_combine": 0}
 
 
 def layer_flops(L, P: int, T: int) -> int:
     """Algorithmic flops of one call: router, routed up + down over the P
-    active pairs, shared expert (mean term, NormSiLU, SiLU not counted)."""
-    return T * 2 * L.d * L.E + P * 4 * L.d * L.F + T * 4 * L.d * L.Fs
+    active pairs (three matrices per pair for gated experts), shared expert
+    (mean term, NormSiLU, SiLU not counted)."""
+    n_mat = 3 if L.W_gate is not None else 2
+    return T * 2 * L.d * L.E + P * 2 * n_mat * L.d * L.F + T * 4 * L.d * L.Fs
 
 
 def dense_ffn_time(d: int, dff: int, T: int, steps: int = 20) -> float:
@@ -126,19 +131,21 @@ def dense_ffn_time(d: int, dff: int, T: int, steps: int = 20) -> float:
 def sweep():
     """The decode layer at T in {1, 8}, the d=4096 layer over T in
     {1, 16, 256, 2048}, the d=2048 layer at T=1024 over activation ratios
-    5..40 % (the d=2048 cases beside the dense-equivalent FFN), and the TopK
+    5..40 % (the d=2048 cases beside the dense-equivalent FFN), the TopK
     routing variant (k = 11 of 56 experts, 20 %) beside the ReLU routing at
-    T = 1, 8 and 4096:
+    T = 1, 8 and 4096, and the gated-expert variant at T = 1, 8 and 4096:
     tokens/s and the fraction of the attainable roofline, max(B/BW, F/MFMA)/t,
     with B the decode byte count (weights touched + x in and out) and F the
     algorithmic flops.  Prints a table; no JSON line."""
     from synthetic import make_layer
     rows = []
-    cases = ([(2, T, None, 0) for T in (1, 8)] + [(4, T, None, 0) for T in (1, 16, 256, 2048)]
-             + [(5, 1024, r, 0) for r in (0.05, 0.10, 0.20, 0.40)]
-             + [(2, 1, None, 11), (2, 8, None, 11), (3, 4096, None, 0), (3, 4096, None, 11)])
-    for cfg, T, ratio, k in cases:
-        L = make_layer(cfg, T=T, ratio=ratio)
+    cases = ([(2, T, None, 0, False) for T in (1, 8)] + [(4, T, None, 0, False) for T in (1, 16, 256, 2048)]
+             + [(5, 1024, r, 0, False) for r in (0.05, 0.10, 0.20, 0.40)]
+             + [(2, 1, None, 11, False), (2, 8, None, 11, False), (3, 4096, None, 0, False),
+                (3, 4096, None, 11, False)]
+             + [(2, 1, None, 0, True), (2, 8, None, 0, True), (3, 4096, None, 0, True)])
+    for cfg, T, ratio, k, gated in cases:
+        L = make_layer(cfg, T=T, ratio=ratio, gated=gated)
         steps = 400 if T <= 16 else (100 if T <= 256 else 30)
         r = run_workload(L, steps, max(5, steps // 10), top_k=k)
         t = r["elapsed"] / steps
@@ -146,11 +153,12 @@ def sweep():
         Bt = sum(B.values()) + T * L.d * (2 if L.dtype == "bf16" else 4)
         Fl = layer_flops(L, r["P"], T)
         fb, ff = Bt / t / (HBM_PEAK_GBS * 1e9), Fl / t / (BF16_PEAK_TFLOPS * 1e12)
-        row = dict(cfg=f"c{cfg}", T=T, routing=f"top{k}" if k else "relu", ratio=round(r["ratio"], 4), experts_touched=r["n_union"], pairs=r["P"],
+        row = dict(cfg=f"c{cfg}", T=T, routing=f"top{k}" if k else "relu",
+                   experts="gated" if gated else "non-gated", ratio=round(r["ratio"], 4), experts_touched=r["n_union"], pairs=r["P"],
                    us_per_call=round(t * 1e6, 2), tokens_per_s=round(T / t, 1),
                    hbm_frac=round(fb, 4), mfma_frac=round(ff, 4), attainable_frac=round(max(fb, ff), 4),
                    kernels_us={k: round(v * 1e3, 2) for k, v in r["kernels"].items()})
-        if cfg in (2, 5) and k == 0:
+        if cfg in (2, 5) and k == 0 and not gated:
             td = dense_ffn_time(L.d, L.E * L.F + L.Fs, T, steps=200 if T <= 16 else 20)
             row["dense_ffn_us"] = round(td * 1e6, 2)
             row["speedup_vs_dense"] = round(td / t, 3)
@@ -161,7 +169,8 @@ def sweep():
 
 def layer_weight_bytes(L) -> int:
     s = 2 if L.dtype == "bf16" else 4
-    return s * (L.d * L.E + 2 * L.E * L.d * L.F + 2 * L.d * L.Fs + L.d * L.F)
+    n_mat = 3 if L.W_gate is not None else 2
+    return s * (L.d * L.E + n_mat * L.E * L.d * L.F + 2 * L.d * L.Fs + L.d * L.F)
 
 
 # GPU measurement ---------------------------------------------------------------
@@ -316,6 +325,8 @@ def main():
                     help="profiler mode: GPU loop of --workload only, no JSON")
     ap.add_argument("--profile-summary", nargs=3, metavar=("DB", "OUT", "COMMAND"),
                     help="write a text summary of a rocprofv3 kernel-trace database (no GPU needed)")
+    ap.add_argument("--gated", action="store_true",
+                    help="with --only-gpu-loop: the gated-expert variant (for profiler runs)")
     ap.add_argument("--top-k", type=int, default=0,
                     help="profiler mode: run the TopK routing variant with this k")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -358,7 +369,7 @@ def main():
                 dst.copy_(src)
             torch.cuda.synchronize()
             del src, dst
-        L = make_layer(2) if args.workload == "decode" else make_layer(3)
+        L = make_layer(2, gated=args.gated) if args.workload == "decode" else make_layer(3, gated=args.gated)
         r = run_workload(L, args.steps, args.warmup, top_k=args.top_k)
         log(f"{args.workload}: {r['elapsed'] / args.steps * 1e6:.2f} us/step kernels={r['kernels']}")
         return
