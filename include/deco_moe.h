@@ -73,12 +73,15 @@ typedef struct {
                         /* keeps the top_k largest logits z (ties to the lower  */
                         /* expert index), gates = softmax of the kept logits,   */
                         /* lambda unused; experts and shared expert unchanged.  */
+  int32_t backward;     /* 0: inference only.  1: also keep the transposed      */
+                        /* weight copies and the workspace deco_moe_backward    */
+                        /* needs (non-gated experts only)                       */
 } deco_moe_config;
 
 /* Check a configuration without touching the GPU.  Returns DECO_OK,
  * DECO_ERR_INVALID_ARG (null, non-positive sizes, negative eps, top_k outside
- * 0..n_experts) or DECO_ERR_UNSUPPORTED (shape outside the set documented in
- * the struct). */
+ * 0..n_experts, backward not 0 or 1) or DECO_ERR_UNSUPPORTED (shape outside
+ * the set documented in the struct). */
 int deco_moe_check_config(const deco_moe_config* cfg);
 
 /* Copy, pack and preprocess one layer's weights into library-owned device
@@ -151,6 +154,49 @@ int deco_moe_copy_routing(const deco_moe_layer* L, int64_t T, uint64_t* mask, fl
 /* Copy the inter-expert mean Wbar [d, F] (float32, device) built at load
  * (of W_up, or of W_gate for a gated layer). */
 int deco_moe_copy_mean_up(const deco_moe_layer* L, float* wbar, void* stream);
+
+/* Gradients written by deco_moe_backward: float32 device buffers owned by
+ * the caller, row-major, shaped like the weights (every one is overwritten,
+ * none is accumulated into).  n_active_pairs may be NULL. */
+typedef struct {
+  float* dx;              /* [T, d]      */
+  float* dW_r;            /* [d, E]      */
+  float* db_r;            /* [E]         */
+  float* dlambda;         /* [E]         */
+  float* dW_up;           /* [E, d, F]   */
+  float* dW_down;         /* [E, F, d]   */
+  float* dWs_up;          /* [d, Fs]     */
+  float* dWs_down;        /* [Fs, d]     */
+  int32_t* n_active_pairs;/* [1] active (token, expert) pairs of the call    */
+} deco_moe_grads;
+
+/* Backward pass of the layer (the training side of the DECO paper: Sec. 2
+ * "Router design", "Expert design" and "Auxiliary training objective";
+ * qidianchuan.cn write-up, sections 二 and 三).  Gradients, with respect to
+ * x and every weight, of
+ *   Loss = sum(dout * layer(x)) + reg_coef * (1/T) sum_t H_t,
+ * dout [T, d] (layer dtype, device) being the upstream gradient of the
+ * output and H_t the router entropy of token t: the entropy of the token's
+ * gates normalised over its active experts (0 without any; the pages name the
+ * entropy penalty but print no formula, so this is a stated reading).  The
+ * inter-expert mean Wbar is treated as the function of W_up it is during
+ * training, so every expert's W_up receives (1/E) x^T dm.  The ReLU's
+ * derivative at z = 0 is 0; experts with lambda_e = 0 get no gradient.  TopK
+ * layers differentiate the softmax over the kept logits (reg_coef must be 0).
+ * The routing is recomputed from x (the forward's kernels), so no state of a
+ * previous forward call is needed.  Requires a layer loaded with
+ * cfg.backward = 1 and non-gated experts (else DECO_ERR_UNSUPPORTED); T in
+ * 1..max_tokens; asynchronous on `stream`; allocates nothing.  Overwrites the
+ * layer's routing state (deco_moe_copy_routing then describes x). */
+int deco_moe_backward(const deco_moe_layer* L, const void* x, const void* dout, int64_t T,
+                      float reg_coef, const deco_moe_grads* grads, void* stream);
+
+/* The adaptive sparsity-regularisation coefficient (qidianchuan.cn write-up,
+ * section 三; DECO paper Sec. 2 "Auxiliary training objective"), one step,
+ * meant to run after every training iteration: returns coef * factor when the
+ * measured activation ratio is above the target, coef / factor when below
+ * (the pages' example factor is 1.002), coef when equal.  Host only. */
+float deco_moe_sparsity_coef_update(float coef, float active_ratio, float target_ratio, float factor);
 
 /* Health flags of L's device-side work, read synchronously (waits for all
  * work on the device) and cleared by the read.  Bit 0: an in-kernel

@@ -34,14 +34,20 @@ DECODE_MAX_T = 16
 EXPORTS = ("deco_moe_check_config", "deco_moe_load_weights", "deco_moe_load_weights_gated", "deco_moe_forward",
            "deco_moe_forward_path", "deco_moe_copy_routing", "deco_moe_copy_mean_up",
            "deco_moe_free", "deco_moe_status_string", "deco_moe_read_error_flags", "deco_moe_timing_enable",
-           "deco_moe_timing_reset", "deco_moe_timing_read")
+           "deco_moe_timing_reset", "deco_moe_timing_read", "deco_moe_backward",
+           "deco_moe_sparsity_coef_update")
 
 
 class DecoConfig(ctypes.Structure):
     _fields_ = [("d_model", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("d_ff", ctypes.c_int32), ("d_ff_shared", ctypes.c_int32),
                 ("max_tokens", ctypes.c_int32), ("dtype", ctypes.c_int),
-                ("rms_eps", ctypes.c_float), ("top_k", ctypes.c_int32)]
+                ("rms_eps", ctypes.c_float), ("top_k", ctypes.c_int32), ("backward", ctypes.c_int32)]
+
+
+class DecoGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("dx", "dW_r", "db_r", "dlambda", "dW_up", "dW_down", "dWs_up",
+                                                 "dWs_down", "n_active_pairs")]
 
 
 class DecoError(RuntimeError):
@@ -92,6 +98,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.deco_moe_timing_read.argtypes = [i32, ctypes.POINTER(ctypes.c_char_p),
                                          ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     lib.deco_moe_timing_read.restype = i32
+    lib.deco_moe_backward.argtypes = [vp, vp, vp, i64, ctypes.c_float, ctypes.POINTER(DecoGrads), vp]
+    lib.deco_moe_backward.restype = i32
+    lib.deco_moe_sparsity_coef_update.argtypes = [ctypes.c_float] * 4
+    lib.deco_moe_sparsity_coef_update.restype = ctypes.c_float
     _lib = lib
     return lib
 
@@ -101,10 +111,16 @@ def status_string(status: int) -> str:
 
 
 def make_config(d: int, E: int, F: int, Fs: int, max_tokens: int, dtype: str = "bf16",
-                eps: float = 1e-6, top_k: int = 0) -> DecoConfig:
-    """top_k = 0: DECO's ReLU routing; 1..E: the TopK routing variant."""
+                eps: float = 1e-6, top_k: int = 0, backward: bool = False) -> DecoConfig:
+    """top_k = 0: DECO's ReLU routing; 1..E: the TopK routing variant.
+    backward: keep what deco_moe_backward needs."""
     dt = {"bf16": DECO_DT_BF16, "f32": DECO_DT_F32}[dtype]
-    return DecoConfig(d, E, F, Fs, max_tokens, dt, eps, top_k)
+    return DecoConfig(d, E, F, Fs, max_tokens, dt, eps, top_k, 1 if backward else 0)
+
+
+def sparsity_coef_update(coef: float, active_ratio: float, target_ratio: float, factor: float = 1.002) -> float:
+    """One step of the adaptive sparsity coefficient (deco_moe_sparsity_coef_update)."""
+    return float(load_library().deco_moe_sparsity_coef_update(coef, active_ratio, target_ratio, factor))
 
 
 def check_config(cfg: DecoConfig) -> int:
@@ -132,7 +148,7 @@ class Layer:
     """
 
     def __init__(self, W_r, b_r, lam, W_up, W_down, Ws_up, Ws_down, *, max_tokens: int,
-                 eps: float = 1e-6, top_k: int = 0, W_gate=None, stream=None):
+                 eps: float = 1e-6, top_k: int = 0, W_gate=None, backward: bool = False, stream=None):
         lib = load_library()
         dtype = {torch.bfloat16: "bf16", torch.float32: "f32"}.get(W_up.dtype)
         if dtype is None:
@@ -150,7 +166,7 @@ class Layer:
         for name, t in (("b_r", b_r), ("lam", lam)):
             if tuple(t.shape) != (E,) or t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
                 raise ValueError(f"{name}: expected contiguous device float32 ({E},)")
-        self.cfg = make_config(d, E, F, Fs, max_tokens, dtype, eps, top_k)
+        self.cfg = make_config(d, E, F, Fs, max_tokens, dtype, eps, top_k, backward)
         self.top_k = top_k
         self.gated = W_gate is not None
         self.d, self.E, self.F, self.Fs, self.dtype = d, E, F, Fs, dtype
@@ -194,6 +210,29 @@ class Layer:
         return out
 
     __call__ = forward
+
+    def backward(self, x: torch.Tensor, dout: torch.Tensor, *, reg_coef: float = 0.0, stream=None) -> dict:
+        """Gradients of sum(dout * layer(x)) + reg_coef * mean router entropy
+        (deco_moe_backward): float32 device tensors dx, dW_r, db_r, dlambda,
+        dW_up, dW_down, dWs_up, dWs_down, and n_active_pairs (int32 [1])."""
+        T = x.shape[0]
+        for name, t in (("x", x), ("dout", dout)):
+            if t.dim() != 2 or tuple(t.shape) != (T, self.d) or t.dtype != _TORCH_DT[self.dtype] or not t.is_cuda \
+                    or not t.is_contiguous():
+                raise ValueError(f"{name}: expected contiguous device [T,{self.d}] {_TORCH_DT[self.dtype]}")
+        f32 = dict(dtype=torch.float32, device=x.device)
+        d, E, F, Fs = self.d, self.E, self.F, self.Fs
+        g = dict(dx=torch.empty((T, d), **f32), dW_r=torch.empty((d, E), **f32), db_r=torch.empty(E, **f32),
+                 dlambda=torch.empty(E, **f32), dW_up=torch.empty((E, d, F), **f32),
+                 dW_down=torch.empty((E, F, d), **f32), dWs_up=torch.empty((d, Fs), **f32),
+                 dWs_down=torch.empty((Fs, d), **f32),
+                 n_active_pairs=torch.empty(1, dtype=torch.int32, device=x.device))
+        gs = DecoGrads(*[g[n].data_ptr() for n, _ in DecoGrads._fields_])
+        st = load_library().deco_moe_backward(self.handle, x.data_ptr(), dout.data_ptr(), T, float(reg_coef),
+                                              ctypes.byref(gs), _stream_handle(stream))
+        if st != DECO_OK:
+            raise DecoError(st, "deco_moe_backward")
+        return g
 
     def routing(self, T: int, stream=None):
         """(mask [T, ceil(E/64)] int64 bit words, logits [T, E] float32) of the last forward."""

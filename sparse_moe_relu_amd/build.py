@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libdeco_moe.so")
 BUILD_DIR = os.path.join(PKG, "_build")
-SOURCES = ["host.hip", "pack.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["host.hip", "pack.hip", "decode.hip", "prefill.hip", "backward.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -54,7 +54,7 @@ def build_library(verbose: bool = True, out: str = LIB, defines: list | None = N
     with cf.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
         objs = list(ex.map(lambda src: _compile(src, build_dir, extra), SOURCES))
     tmp = out + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)

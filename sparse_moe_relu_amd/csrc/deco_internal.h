@@ -24,6 +24,7 @@ struct deco_moe_layer {
   int dec_ok;              // the decode path is available for this layer
   int pre_grid;            // persistent grid of the prefill expert kernel
   int n_cu;                // compute units of the device
+  int bwd_grid;            // persistent grid of the backward expert kernel
   int gated;               // gated routed experts: NormSiLU(x.W_gate[e]) * (x.W_up[e])
 
   // packed weights (one allocation)
@@ -42,6 +43,13 @@ struct deco_moe_layer {
   float* b_r;
   float* lam;
   float* wbar;             // [d][F] fp32
+  // backward (cfg.backward = 1; null otherwise)
+  int Fp, Ep, Fsp;         // F, E, Fs rounded up to 64: sections of the dense backward operand
+  int nkb_cat;             // k-blocks of Fp + Ep + Fsp
+  char* WdnT_p;            // per expert [pF][nkb_d] frags of W_down[e]^T (K = d, N = F), layer dtype
+  char* WupT_p;            // per expert [pD][nkb_F] frags of W_up[e]^T (K = F, N = d), down operand type
+  char* WsdT_p;            // [pFs][nkb_d] frags of Ws_down^T (K = d, N = Fs)
+  char* Bcat_p;            // [pD][nkb_cat] frags of [Wbar^T; W_r^T; Ws_up^T] (K = Fp + Ep + Fsp, N = d)
 
   // workspace (one allocation, sized for max(maxT, 16) tokens)
   char* ws;
@@ -63,6 +71,21 @@ struct deco_moe_layer {
   int* ecnt;               // [E]
   int* list_tok;           // [E][Tcap]
   char* sbuf;              // [Tcap][Fs] shared activations (dtype)
+  // backward workspace
+  float* dgbuf;            // [Tcap][E] dLoss/dg of the active pairs
+  char* dhbuf;             // [pair slots][F] dLoss/dh~ of each pair (layer dtype; bf16: high part)
+  char* agbuf;             // [pair slots][F] g * a of each pair (likewise)
+  char* dhbuf_lo;          // bf16 layers: low parts (v - high part) of dhbuf, agbuf, dcat; else null
+  char* agbuf_lo;
+  char* dcat_lo;
+  char* sb_hi;             // [Tcap][Fs] s = SiLU(x Ws_up) recomputed in fp32 (bf16 layers: high part)
+  char* sb_lo;             // bf16 layers: its low part
+  int* slot_list;          // [E][Tcap] pair slot of each entry of an expert's token list
+  char* dcat;              // [Tcap][Fp + Ep + Fsp] rows dm | dz | du_s (layer dtype)
+  float* dzbuf;            // [Tcap][E] dLoss/dz
+  float* dlz;              // [Tcap][E] ReLU(z) * dLoss/dg
+  float* gbuf;             // [d][F] x^T dm (gradient of Wbar)
+  float* colpart;          // [2][ceil(Tcap / 64)][E] partial column sums (db_r, dlambda)
   char* ybuf;              // [Tcap * (E + 1) + 1][d] pair buffer, token-major: per token its
                            // shared-expert output, then gate * expert output for each
                            // active expert in ascending order (fp16 for bf16 layers,
@@ -97,6 +120,13 @@ enum {
   KS_PRE_DISPATCH,
   KS_PRE_EXPERT,
   KS_PRE_COMBINE,
+  KS_BWD_SHARED,
+  KS_BWD_EXPERT,
+  KS_BWD_TOKEN,
+  KS_BWD_COLSUM,
+  KS_BWD_DENSE_DX,
+  KS_BWD_COMBINE,
+  KS_BWD_WGRAD,
   KS_COUNT
 };
 const char* kernel_slot_name(int slot);
@@ -108,8 +138,11 @@ hipError_t launch_pack_all(deco_moe_layer* L, const void* W_r, const void* W_nor
                            const void* W_down, const void* Ws_up, const void* Ws_down, hipStream_t s);
 hipError_t plan_decode(deco_moe_layer* L);   // decode launch shape (load time)
 hipError_t plan_prefill(deco_moe_layer* L);  // prefill launch shape (load time)
+hipError_t plan_backward(deco_moe_layer* L); // backward launch shape (load time, after plan_prefill)
 hipError_t launch_decode(const deco_moe_layer* L, const void* x, int T, void* out, hipStream_t s);
 hipError_t launch_prefill(const deco_moe_layer* L, const void* x, int T, void* out, hipStream_t s);
 hipError_t launch_copy_mask(const deco_moe_layer* L, int T, uint64_t* mask, hipStream_t s);
+hipError_t launch_backward(const deco_moe_layer* L, const void* x, const void* dout, int T, float reg_coef,
+                           const deco_moe_grads* gr, hipStream_t s);
 
 }  // namespace deco_host

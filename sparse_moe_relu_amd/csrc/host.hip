@@ -26,6 +26,7 @@ int validate_cfg(const deco_moe_config* c) {
   if (c->d_ff != 32 && c->d_ff != 64 && c->d_ff != 128 && c->d_ff != 256) return DECO_ERR_UNSUPPORTED;
   if (c->d_ff_shared % 32 != 0 || c->d_ff_shared > 16384) return DECO_ERR_UNSUPPORTED;
   if (c->max_tokens > (1 << 20)) return DECO_ERR_UNSUPPORTED;
+  if (c->backward != 0 && c->backward != 1) return DECO_ERR_INVALID_ARG;
   return DECO_OK;
 }
 
@@ -50,6 +51,11 @@ void derive(deco_moe_layer* L) {
   L->n_groups = (L->pD + 7) / 8;   // 128-column groups of the decode down role
   L->dec_q = 64;   // upper bound for the workspace; the decode plan picks the value at load
   L->pre_grid = 1024;
+  auto r64 = [](int v) { return (v + 63) / 64 * 64; };
+  L->Fp = r64(L->F);
+  L->Ep = r64(L->E);
+  L->Fsp = r64(L->Fs);
+  L->nkb_cat = (L->Fp + L->Ep + L->Fsp) / L->KB;
 }
 
 struct Carve {
@@ -112,6 +118,13 @@ const char* kernel_slot_name(int slot) {
     case KS_PRE_DISPATCH: return "k_pre_dispatch";
     case KS_PRE_EXPERT: return "k_pre_expert";
     case KS_PRE_COMBINE: return "k_pre_combine";
+    case KS_BWD_SHARED: return "k_bwd_shared";
+    case KS_BWD_EXPERT: return "k_bwd_expert";
+    case KS_BWD_TOKEN: return "k_bwd_token";
+    case KS_BWD_COLSUM: return "k_bwd_colsum";
+    case KS_BWD_DENSE_DX: return "k_bwd_dense_dx";
+    case KS_BWD_COMBINE: return "k_bwd_combine";
+    case KS_BWD_WGRAD: return "k_bwd_wgrad";
     default: return "?";
   }
 }
@@ -166,6 +179,7 @@ static int load_layer(const deco_moe_config* cfg, const void* W_r, const float* 
   if (st != DECO_OK) return st;
   if (!W_r || !b_r || !lambda || !W_norm || !W_down || !Ws_up || !Ws_down) return DECO_ERR_INVALID_ARG;
   if (gated && !W_lin) return DECO_ERR_INVALID_ARG;
+  if (gated && cfg->backward) return DECO_ERR_UNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
 
   deco_moe_layer* L = new (std::nothrow) deco_moe_layer();
@@ -195,6 +209,11 @@ static int load_layer(const deco_moe_config* cfg, const void* W_r, const float* 
   size_t o_b = w.take(sizeof(float) * E);
   size_t o_l = w.take(sizeof(float) * E);
   size_t o_wb = w.take(sizeof(float) * (size_t)L->d * L->F);
+  const bool bwd = L->cfg.backward != 0;
+  size_t o_dnT = bwd ? w.take(L->up_stride * E) : 0;
+  size_t o_upT = bwd ? w.take(L->dn_stride * E) : 0;
+  size_t o_sdT = bwd ? w.take((size_t)L->pFs * L->nkb_d * KBy) : 0;
+  size_t o_cat = bwd ? w.take((size_t)L->pD * L->nkb_cat * KBy) : 0;
   L->wmem_bytes = w.off;
   // workspace
   const size_t Tcap = (size_t)(L->maxT < 16 ? 16 : L->maxT);
@@ -216,6 +235,22 @@ static int load_layer(const deco_moe_config* cfg, const void* W_r, const float* 
   size_t o_sb = k.take((size_t)L->esz * Tcap * L->Fs);
   // pair buffer plus one scratch row that takes the stores of padding rows
   size_t o_yb = k.take((size_t)L->esz * (Tcap * (E + 1) + 1) * L->d);
+  const size_t n_slots = Tcap * (E + 1) + 1;
+  size_t o_dg = bwd ? k.take(sizeof(float) * Tcap * E) : 0;
+  size_t o_dh = bwd ? k.take((size_t)L->esz * n_slots * L->F) : 0;
+  size_t o_ag = bwd ? k.take((size_t)L->esz * n_slots * L->F) : 0;
+  size_t o_sl = bwd ? k.take(sizeof(int) * (size_t)E * Tcap) : 0;
+  size_t o_dc = bwd ? k.take((size_t)L->esz * Tcap * (L->Fp + L->Ep + L->Fsp)) : 0;
+  size_t o_dz = bwd ? k.take(sizeof(float) * Tcap * E) : 0;
+  size_t o_dl = bwd ? k.take(sizeof(float) * Tcap * E) : 0;
+  size_t o_gb = bwd ? k.take(sizeof(float) * (size_t)L->d * L->F) : 0;
+  size_t o_cp = bwd ? k.take(sizeof(float) * 2 * ((Tcap + 63) / 64) * E) : 0;
+  const bool split = bwd && L->esz == 2;   // low parts of the backward's bf16 operands
+  size_t o_dhl = split ? k.take((size_t)L->esz * n_slots * L->F) : 0;
+  size_t o_agl = split ? k.take((size_t)L->esz * n_slots * L->F) : 0;
+  size_t o_dcl = split ? k.take((size_t)L->esz * Tcap * (L->Fp + L->Ep + L->Fsp)) : 0;
+  size_t o_sbh = bwd ? k.take((size_t)L->esz * Tcap * L->Fs) : 0;
+  size_t o_sbl = split ? k.take((size_t)L->esz * Tcap * L->Fs) : 0;
   L->ws_bytes = k.off;
 
   if (hipMalloc((void**)&L->wmem, L->wmem_bytes) != hipSuccess) {
@@ -239,6 +274,12 @@ static int load_layer(const deco_moe_config* cfg, const void* W_r, const float* 
   L->b_r = (float*)(L->wmem + o_b);
   L->lam = (float*)(L->wmem + o_l);
   L->wbar = (float*)(L->wmem + o_wb);
+  if (bwd) {
+    L->WdnT_p = L->wmem + o_dnT;
+    L->WupT_p = L->wmem + o_upT;
+    L->WsdT_p = L->wmem + o_sdT;
+    L->Bcat_p = L->wmem + o_cat;
+  }
   L->z = (float*)(L->ws + o_z);
   L->g = (float*)(L->ws + o_g);
   L->mask = (uint64_t*)(L->ws + o_m);
@@ -255,6 +296,24 @@ static int load_layer(const deco_moe_config* cfg, const void* W_r, const float* 
   L->list_tok = (int*)(L->ws + o_lt);
   L->sbuf = L->ws + o_sb;
   L->ybuf = L->ws + o_yb;
+  if (bwd) {
+    L->dgbuf = (float*)(L->ws + o_dg);
+    L->dhbuf = L->ws + o_dh;
+    L->agbuf = L->ws + o_ag;
+    L->slot_list = (int*)(L->ws + o_sl);
+    L->dcat = L->ws + o_dc;
+    L->dzbuf = (float*)(L->ws + o_dz);
+    L->dlz = (float*)(L->ws + o_dl);
+    L->gbuf = (float*)(L->ws + o_gb);
+    L->colpart = (float*)(L->ws + o_cp);
+    L->sb_hi = L->ws + o_sbh;
+    if (split) {
+      L->dhbuf_lo = L->ws + o_dhl;
+      L->agbuf_lo = L->ws + o_agl;
+      L->dcat_lo = L->ws + o_dcl;
+      L->sb_lo = L->ws + o_sbl;
+    }
+  }
 
   hipError_t err = hipSuccess;
   // counters, flags and activation fragments start at zero; the rest of the
@@ -266,6 +325,7 @@ static int load_layer(const deco_moe_config* cfg, const void* W_r, const float* 
   if (err == hipSuccess) err = deco_host::launch_pack_all(L, W_r, W_norm, W_lin, W_down, Ws_up, Ws_down, s);
   if (err == hipSuccess) err = deco_host::plan_decode(L);
   if (err == hipSuccess) err = deco_host::plan_prefill(L);
+  if (err == hipSuccess && bwd) err = deco_host::plan_backward(L);
   if (err == hipSuccess) err = hipStreamSynchronize(s);
   if (err != hipSuccess) {
     (void)hipGetLastError();
@@ -334,6 +394,26 @@ int deco_moe_copy_mean_up(const deco_moe_layer* L, float* wbar, void* stream) {
   hipError_t err = hipMemcpyAsync(wbar, L->wbar, sizeof(float) * (size_t)L->d * L->F, hipMemcpyDeviceToDevice,
                                   (hipStream_t)stream);
   return err == hipSuccess ? DECO_OK : DECO_ERR_HIP;
+}
+
+int deco_moe_backward(const deco_moe_layer* L, const void* x, const void* dout, int64_t T, float reg_coef,
+                      const deco_moe_grads* gr, void* stream) {
+  if (!L || !x || !dout || !gr || T < 1 || T > L->maxT) return DECO_ERR_INVALID_ARG;
+  if (!gr->dx || !gr->dW_r || !gr->db_r || !gr->dlambda || !gr->dW_up || !gr->dW_down || !gr->dWs_up ||
+      !gr->dWs_down)
+    return DECO_ERR_INVALID_ARG;
+  if (!isfinite(reg_coef) || (L->cfg.top_k > 0 && reg_coef != 0.0f)) return DECO_ERR_INVALID_ARG;
+  if (!L->cfg.backward || L->gated) return DECO_ERR_UNSUPPORTED;
+  if (((uintptr_t)x % 16) != 0 || ((uintptr_t)dout % 16) != 0 || ((uintptr_t)gr->dx % 16) != 0)
+    return DECO_ERR_INVALID_ARG;
+  hipError_t err = deco_host::launch_backward(L, x, dout, (int)T, reg_coef, gr, (hipStream_t)stream);
+  return err == hipSuccess ? DECO_OK : DECO_ERR_HIP;
+}
+
+float deco_moe_sparsity_coef_update(float coef, float active_ratio, float target_ratio, float factor) {
+  if (active_ratio > target_ratio) return coef * factor;
+  if (active_ratio < target_ratio) return coef / factor;
+  return coef;
 }
 
 int deco_moe_read_error_flags(const deco_moe_layer* L, uint32_t* flags) {

@@ -26,15 +26,19 @@ __global__ void __launch_bounds__(256) k_mean_up(const typename DT::elem* __rest
   wbar[i] = s / (float)E;
 }
 
-// Pack src [K][N] (row stride ld; `batch` matrices `src_bstride` elements
-// apart) into fragments: panel p (16 columns), k-block kb, lane l.  Entries
-// outside K x N are zero.  Values are rounded once to the element type.
+// Pack the K x N matrix src(k, n) = src[k*sk + n*sn] (`batch` matrices
+// `src_bstride` elements apart; sk = ld, sn = 1 for a row-major [K][N]
+// matrix, sk = 1, sn = ld for the transpose of a row-major [N][K] one) into
+// fragments: panel p (16 columns), k-block kb_off + kb of a layout with
+// nkb_tot k-blocks, lane l.  Entries outside K x N are zero.  Values are
+// rounded once to the element type.
 __device__ __forceinline__ float src_f32(const uint16_t* p, size_t i) { return bf16_to_f32(p[i]); }
 __device__ __forceinline__ float src_f32(const float* p, size_t i) { return p[i]; }
 
 template <class DT, class SRC>
 __global__ void __launch_bounds__(256) k_pack(const SRC* __restrict__ src, size_t src_bstride,
-                                              int K, int N, int ld, int P, int nkb,
+                                              int K, int N, size_t sk, size_t sn, int P, int nkb,
+                                              int kb_off, int nkb_tot,
                                               char* __restrict__ dst, size_t dst_bstride) {
   const int b = blockIdx.y;
   const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -50,9 +54,31 @@ __global__ void __launch_bounds__(256) k_pack(const SRC* __restrict__ src, size_
 #pragma unroll
   for (int j = 0; j < DT::EPL; ++j) {
     const int k = kb * DT::KB + DT::frag_k(g, j);
-    f[j] = (k < K && n < N) ? src_f32(s, (size_t)k * ld + n) : 0.f;
+    f[j] = (k < K && n < N) ? src_f32(s, (size_t)k * sk + (size_t)n * sn) : 0.f;
   }
-  st16(dst + (size_t)b * dst_bstride + frag_off(p, kb, nkb) + (size_t)l * 16, DT::pack(f));
+  st16(dst + (size_t)b * dst_bstride + frag_off(p, kb_off + kb, nkb_tot) + (size_t)l * 16, DT::pack(f));
+}
+
+dim3 pack_grid(int P, int nkb, int batch) {
+  size_t thr = (size_t)P * nkb * WAVE;
+  return dim3((unsigned)((thr + 255) / 256), (unsigned)batch);
+}
+
+// row-major [K][N] source, whole layout
+template <class DT, class SRC>
+void pack_rm(const void* src, size_t bstride, int K, int N, int P, int nkb, char* dst, size_t dstride, int batch,
+             hipStream_t s) {
+  k_pack<DT, SRC><<<pack_grid(P, nkb, batch), 256, 0, s>>>((const SRC*)src, bstride, K, N, (size_t)N, 1, P, nkb, 0,
+                                                           nkb, dst, dstride);
+}
+
+// transpose of a row-major [N][K] source (element (k, n) = src[n*K + k]),
+// written to k-blocks kb_off .. of a layout with nkb_tot k-blocks
+template <class DT, class SRC>
+void pack_tr(const void* src, size_t bstride, int K, int N, int P, int nkb, int kb_off, int nkb_tot, char* dst,
+             size_t dstride, int batch, hipStream_t s) {
+  k_pack<DT, SRC><<<pack_grid(P, nkb, batch), 256, 0, s>>>((const SRC*)src, bstride, K, N, 1, (size_t)K, P, nkb,
+                                                           kb_off, nkb_tot, dst, dstride);
 }
 
 // W_up here is the projection NormSiLU acts on (a gated expert's gate
@@ -61,38 +87,38 @@ template <class DT>
 hipError_t pack_all(deco_moe_layer* L, const void* W_r, const void* W_up, const void* W_lin,
                     const void* W_down, const void* Ws_up, const void* Ws_down, hipStream_t s) {
   using E_t = typename DT::elem;
+  using DN = typename DT::Down;
   const int d = L->d, E = L->E, F = L->F, Fs = L->Fs;
   const size_t dF = (size_t)d * F;
   k_mean_up<DT><<<(unsigned)((dF + 255) / 256), 256, 0, s>>>((const E_t*)W_up, E, dF, L->wbar);
-  auto grid = [](int P, int nkb, int batch) {
-    size_t thr = (size_t)P * nkb * WAVE;
-    return dim3((unsigned)((thr + 255) / 256), (unsigned)batch);
-  };
   // router: K = d, N = E (padded to multiples of 64 columns)
-  k_pack<DT, E_t><<<grid(L->pR, L->nkb_d, 1), 256, 0, s>>>((const E_t*)W_r, 0, d, E, E, L->pR, L->nkb_d,
-                                                           L->Wr_p, 0);
+  pack_rm<DT, E_t>(W_r, 0, d, E, L->pR, L->nkb_d, L->Wr_p, 0, 1, s);
   // routed up: K = d, N = F
-  k_pack<DT, E_t><<<grid(L->pF, L->nkb_d, E), 256, 0, s>>>((const E_t*)W_up, dF, d, F, F, L->pF, L->nkb_d,
-                                                           L->Wup_p, L->up_stride);
-  if (W_lin)
-    k_pack<DT, E_t><<<grid(L->pF, L->nkb_d, E), 256, 0, s>>>((const E_t*)W_lin, dF, d, F, F, L->pF, L->nkb_d,
-                                                             L->Wlin_p, L->up_stride);
+  pack_rm<DT, E_t>(W_up, dF, d, F, L->pF, L->nkb_d, L->Wup_p, L->up_stride, E, s);
+  if (W_lin) pack_rm<DT, E_t>(W_lin, dF, d, F, L->pF, L->nkb_d, L->Wlin_p, L->up_stride, E, s);
   // inter-expert mean, in the layer dtype: K = d, N = F
-  k_pack<DT, float><<<grid(L->pF, L->nkb_d, 1), 256, 0, s>>>(L->wbar, 0, d, F, F, L->pF, L->nkb_d,
-                                                            L->Wbar_p, 0);
+  pack_rm<DT, float>(L->wbar, 0, d, F, L->pF, L->nkb_d, L->Wbar_p, 0, 1, s);
   // routed down: K = F, N = d
-  k_pack<DT, E_t><<<grid(L->pD, L->nkb_F, E), 256, 0, s>>>((const E_t*)W_down, dF, F, d, d, L->pD, L->nkb_F,
-                                                           L->Wdn_p, L->dn_stride);
-  // routed down again in fp16 for the prefill path of bf16 layers
+  pack_rm<DT, E_t>(W_down, dF, F, d, L->pD, L->nkb_F, L->Wdn_p, L->dn_stride, E, s);
+  // routed down again in fp16 for bf16 layers (the down-projection operand)
   if constexpr (sizeof(E_t) == 2)
-    k_pack<FP16, E_t><<<grid(L->pD, L->nkb_F, E), 256, 0, s>>>((const E_t*)W_down, dF, F, d, d, L->pD,
-                                                               L->nkb_F, L->Wdn16_p, L->dn_stride);
-  // shared up: K = d, N = Fs
-  k_pack<DT, E_t><<<grid(L->pFs, L->nkb_d, 1), 256, 0, s>>>((const E_t*)Ws_up, 0, d, Fs, Fs, L->pFs,
-                                                            L->nkb_d, L->Wsu_p, 0);
-  // shared down: K = Fs, N = d
-  k_pack<DT, E_t><<<grid(L->pD, L->nkb_Fs, 1), 256, 0, s>>>((const E_t*)Ws_down, 0, Fs, d, d, L->pD,
-                                                            L->nkb_Fs, L->Wsd_p, 0);
+    pack_rm<FP16, E_t>(W_down, dF, F, d, L->pD, L->nkb_F, L->Wdn16_p, L->dn_stride, E, s);
+  // shared up: K = d, N = Fs; shared down: K = Fs, N = d
+  pack_rm<DT, E_t>(Ws_up, 0, d, Fs, L->pFs, L->nkb_d, L->Wsu_p, 0, 1, s);
+  pack_rm<DT, E_t>(Ws_down, 0, Fs, d, L->pD, L->nkb_Fs, L->Wsd_p, 0, 1, s);
+  if (L->cfg.backward) {
+    // W_down[e]^T: K = d, N = F (the ungated output gradient times W_down^T)
+    pack_tr<DT, E_t>(W_down, dF, d, F, L->pF, L->nkb_d, 0, L->nkb_d, L->WdnT_p, L->up_stride, E, s);
+    // W_up[e]^T: K = F, N = d, in the down-projection operand type
+    pack_tr<DN, E_t>(W_up, dF, F, d, L->pD, L->nkb_F, 0, L->nkb_F, L->WupT_p, L->dn_stride, E, s);
+    // Ws_down^T: K = d, N = Fs
+    pack_tr<DT, E_t>(Ws_down, 0, d, Fs, L->pFs, L->nkb_d, 0, L->nkb_d, L->WsdT_p, 0, 1, s);
+    // [Wbar^T; W_r^T; Ws_up^T]: K = Fp + Ep + Fsp, N = d (sections zero-padded)
+    const int KB = DT::KB;
+    pack_tr<DT, float>(L->wbar, 0, F, d, L->pD, L->Fp / KB, 0, L->nkb_cat, L->Bcat_p, 0, 1, s);
+    pack_tr<DT, E_t>(W_r, 0, E, d, L->pD, L->Ep / KB, L->Fp / KB, L->nkb_cat, L->Bcat_p, 0, 1, s);
+    pack_tr<DT, E_t>(Ws_up, 0, Fs, d, L->pD, L->Fsp / KB, (L->Fp + L->Ep) / KB, L->nkb_cat, L->Bcat_p, 0, 1, s);
+  }
   return hipGetLastError();
 }
 

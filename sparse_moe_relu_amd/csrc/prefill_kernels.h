@@ -1,0 +1,910 @@
+// prefill_kernels.h - device code of the bucketed large-batch path, shared
+// by the forward launchers (prefill.hip) and the backward pass
+// (backward.hip), which reuses the router, dispatch and expert-tile kernels.
+// Included by exactly those two translation units; everything here has
+// internal linkage.
+//
+//   k_pre_router_shared  one GEMM of x against the concatenated column panels
+//                        [router | inter-expert mean Wbar | shared up-proj].
+//                        Router epilogue: logits + b_r, gates lambda_e*ReLU(z)
+//                        and active-expert bit masks (DECO paper Sec. 2
+//                        "Router design"; zero or negative scores are ignored:
+//                        qidianchuan.cn write-up, section 二, router).  Mean
+//                        epilogue: m = x.Wbar in fp32 (the NormSiLU mean term,
+//                        the same for every expert).  Shared epilogue: SiLU,
+//                        stored for the shared down-projection.
+//   k_pre_dispatch       per-expert token buckets ("expert batching") from a
+//                        workgroup prefix scan: ascending token lists per
+//                        expert, and per token the offset of its slots in a
+//                        token-major pair buffer (slot 0: shared expert, then
+//                        one slot per active expert in ascending order).
+//   k_pre_expert         persistent grouped kernel.  Expert tiles (expert e,
+//                        up to 128 of its tokens): gathered x rows . W_up[e] on
+//                        MFMA, minus the mean term, NormSiLU (RMS over the F
+//                        columns of a row, then SiLU), . W_down[e] in fp16,
+//                        times the gate (DECO paper Sec. 2 "Router design": the
+//                        router gives every expert a weight), stored in fp16
+//                        to the pair slot.  Shared tiles: SiLU(x Ws_up) .
+//                        Ws_down into slot 0.
+//   k_pre_combine        out[t] = sum of token t's pair rows in slot order, in
+//                        fp32, rounded once to the dtype.
+//
+// All GEMMs run on the LDS-staged tile of gemm_tile.h with swapped operands,
+// so an accumulator lane holds 4 consecutive columns of one row.  Pair values
+// are fp16 (11-bit significand): a bf16 pair buffer costs up to 4 % of
+// RMS(out) on heavy-tailed gates.
+#pragma once
+
+#include <string.h>
+
+#include "deco_common.h"
+#include "deco_internal.h"
+#include "gemm_tile.h"
+
+using namespace deco;
+
+namespace {
+
+struct PreArgs {
+  const void* x;
+  void* out;
+  int T, Tcap, d, E, F, Fs, W;
+  int top_k;           // TopK routing variant (0: ReLU routing)
+  int nkb_d, nkb_F, nkb_Fs, pR, pF, pD, pFs;
+  int pF4, pFs4;       // panel counts of the mean and shared sections, padded to 4
+  int rs_nt;           // 8-panel column tiles of the router/mean/shared GEMM
+  const char* Wr_p;
+  const char* Wup_p;       // NormSiLU input projection (a gated expert's gate projection)
+  const char* Wlin_p;      // gated experts' up-projection
+  const char* Wbar_p;
+  const char* Wdn_p;
+  const char* Wdn16_p;     // down-projection operand of the prefill path (fp16 or fp32)
+  const char* Wsu_p;
+  const char* Wsd_p;
+  size_t up_stride, dn_stride;
+  const float* b_r;
+  const float* lam;
+  float eps;
+  float* z;
+  float* g;
+  float* mbuf;
+  uint64_t* mask;
+  int* tok_off;
+  int* ecnt;
+  int* list_tok;
+  void* sbuf;
+  void* ybuf;
+  // backward pass
+  const void* dout;        // [T][d] upstream gradient of the layer output
+  const char* WdnT_p;      // W_down[e]^T frags (K = d, N = F)
+  const char* WupT_p;      // W_up[e]^T frags (K = F, N = d), down operand type
+  float* dgbuf;            // [Tcap][E] dLoss/dg
+  void* dhbuf;             // [pair slots][F] dLoss/dh~ (layer dtype; bf16 layers: the high part)
+  void* agbuf;             // [pair slots][F] g * a (likewise)
+  void* dhbuf_lo;          // bf16 layers: the low parts (value - high part, rounded), else null
+  void* agbuf_lo;
+  int* slot_list;          // [E][Tcap] pair slot of each list entry
+};
+
+// what an expert tile computes
+constexpr int XM_FWD = 0;     // NormSiLU(x.W_up[e] - m) . W_down[e], times the gate
+constexpr int XM_GATED = 1;   // (NormSiLU(x.W_gate[e] - m) * x.W_up[e]) . W_down[e], times the gate
+constexpr int XM_BWD = 2;     // backward of XM_FWD: dLoss/dh~ . W_up[e]^T and the pair rows
+
+__device__ __forceinline__ float dsilu_f(float u) {
+  const float sg = 1.0f / (1.0f + __expf(-u));
+  return sg * (1.0f + u * (1.0f - sg));
+}
+
+#ifndef DECO_PRE_NS
+#define DECO_PRE_NS 2     // pipeline stages in LDS (32 KiB each for the dense tiles)
+#endif
+
+constexpr int NXCD = 8;
+constexpr int GM = 128;   // rows of the dense GEMM tiles
+constexpr int GP = 8;     // 16-column panels of the dense GEMM tiles
+template <class DT>
+using DenseTile = Tile<DT, GM, GP, DECO_PRE_NS>;
+
+// Workgroups are handed to the 8 XCDs round-robin (workgroup b runs on XCD
+// b % 8).  Renumber them so each XCD works on one contiguous range of tiles:
+// tiles next to each other share operands, and each XCD has its own L2.
+__device__ __forceinline__ int xcd_tile(int b, int n) {
+  const int per = n / NXCD, rem = n % NXCD, x = b % NXCD, i = b / NXCD;
+  return x * per + (x < rem ? x : rem) + i;
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// 4 consecutive values of one row, stored as the dtype (8 bytes bf16, 16 fp32)
+template <class DT>
+__device__ __forceinline__ void store4(typename DT::elem* p, float v0, float v1, float v2, float v3) {
+  if constexpr (sizeof(typename DT::elem) == 2) {
+    uint2 u;
+    u.x = f32_to_bf16(v0) | (f32_to_bf16(v1) << 16);
+    u.y = f32_to_bf16(v2) | (f32_to_bf16(v3) << 16);
+    *reinterpret_cast<uint2*>(p) = u;
+  } else {
+    *reinterpret_cast<float4*>(p) = make_float4(v0, v1, v2, v3);
+  }
+}
+
+// v = hi + lo to about 16 significant bits, both bf16 (for fp32 layers the
+// value itself, lo unused)
+template <class DT>
+__device__ __forceinline__ void store4_split(typename DT::elem* hi, typename DT::elem* lo, const float* v) {
+  store4<DT>(hi, v[0], v[1], v[2], v[3]);
+  if constexpr (sizeof(typename DT::elem) == 2) {
+    float r[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = v[i] - bf16_to_f32(f32_to_bf16(v[i]));
+    store4<DT>(lo, r[0], r[1], r[2], r[3]);
+  }
+}
+
+template <class PT>
+__device__ __forceinline__ void store4_pair(PT* p, const f32x4_t& v) {
+  if constexpr (sizeof(PT) == 2) {
+    typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 h4;
+    h4 h = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+    *reinterpret_cast<h4*>(p) = h;
+  } else {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+}
+
+// --------------------------------------------------------------------------
+// NS pipeline stages in LDS: 2 (64 KiB, two workgroups per CU) when the grid
+// exceeds the CUs, 4 (128 KiB, one per CU, three steps of loads in flight)
+// when it does not, which is the case below a few thousand tokens.
+template <class DT, int NS>
+__global__ void __launch_bounds__(256, 2) k_pre_router_shared(PreArgs a) {
+  using elem = typename DT::elem;
+  using TC = Tile<DT, GM, GP, NS>;
+  __shared__ i32x4_t lds[TC::LDS_V];
+  const int tid = threadIdx.x, w = tid >> 6, wm = w >> 1, wn = w & 1, l = tid & 63, g = l >> 4, c = l & 15;
+  const int t = xcd_tile(blockIdx.x, gridDim.x);
+  const int m0 = (t / a.rs_nt) * GM, p0 = (t % a.rs_nt) * GP;
+  const elem* x = (const elem*)a.x;
+  // rows past T and padding panels read valid memory; those outputs are dropped
+  auto row = [&](int r) -> const elem* {
+    const int rr = m0 + r;
+    return x + (size_t)(rr < a.T ? rr : a.T - 1) * a.d;
+  };
+  auto panel = [&](int p) -> const char* {
+    int q = p0 + p;
+    if (q < a.pR) return a.Wr_p + frag_off(q, 0, a.nkb_d);
+    q -= a.pR;
+    if (q < a.pF4) return a.Wbar_p + frag_off(q < a.pF ? q : 0, 0, a.nkb_d);
+    q -= a.pF4;
+    return a.Wsu_p + frag_off(q < a.pFs ? q : 0, 0, a.nkb_d);
+  };
+  f32x4_t acc[TC::MB][TC::NBW];
+#pragma unroll
+  for (int i = 0; i < TC::MB; ++i)
+#pragma unroll
+    for (int j = 0; j < TC::NBW; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  tile_gemm<DT, TC, true>(lds, row, panel, a.nkb_d, acc);
+
+  // lane: row m0 + wm*64 + 16 i + c, columns 16 (q0 + j) + 4 g + ii
+  const int q0 = p0 + wn * TC::NBW;   // a multiple of 4: one section per wave
+  if (q0 < a.pR) {
+    float be[TC::NBW][4], le[TC::NBW][4];
+#pragma unroll
+    for (int j = 0; j < TC::NBW; ++j)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int e = (q0 + j) * 16 + 4 * g + ii;
+        be[j][ii] = e < a.E ? a.b_r[e] : 0.f;
+        le[j][ii] = e < a.E ? a.lam[e] : 0.f;
+      }
+#pragma unroll
+    for (int i = 0; i < TC::MB; ++i) {
+      const int r = m0 + wm * (GM / 2) + 16 * i + c;
+      uint64_t bits = 0;
+#pragma unroll
+      for (int j = 0; j < TC::NBW; ++j)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int e = (q0 + j) * 16 + 4 * g + ii;
+          const float zv = acc[i][j][ii] + be[j][ii];
+          const bool act = e < a.E && zv > 0.f && le[j][ii] != 0.f;
+          if (act) bits |= 1ull << (16 * j + 4 * g + ii);
+          if (r < a.T && e < a.E) {
+            a.z[(size_t)r * a.E + e] = zv;
+            a.g[(size_t)r * a.E + e] = act ? le[j][ii] * zv : 0.f;
+          }
+        }
+      bits |= shfl_xor_u64(bits, 16);
+      bits |= shfl_xor_u64(bits, 32);
+      if (g == 0 && r < a.T) a.mask[(size_t)r * a.W + q0 / 4] = bits;
+    }
+  } else if (q0 - a.pR < a.pF4) {
+    const int q = q0 - a.pR;
+#pragma unroll
+    for (int j = 0; j < TC::NBW; ++j) {
+      if (q + j < a.pF) {
+        const int f0 = (q + j) * 16 + 4 * g;
+#pragma unroll
+        for (int i = 0; i < TC::MB; ++i) {
+          const int r = m0 + wm * (GM / 2) + 16 * i + c;
+          if (r < a.T)
+            *reinterpret_cast<float4*>(a.mbuf + (size_t)r * a.F + f0) =
+                make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+        }
+      }
+    }
+  } else {
+    const int q = q0 - a.pR - a.pF4;
+    elem* sb = (elem*)a.sbuf;
+#pragma unroll
+    for (int j = 0; j < TC::NBW; ++j) {
+      if (q + j < a.pFs) {
+        const int c0 = (q + j) * 16 + 4 * g;
+#pragma unroll
+        for (int i = 0; i < TC::MB; ++i) {
+          const int r = m0 + wm * (GM / 2) + 16 * i + c;
+          if (r < a.T)
+            store4<DT>(sb + (size_t)r * a.Fs + c0, silu_f(acc[i][j][0]), silu_f(acc[i][j][1]),
+                       silu_f(acc[i][j][2]), silu_f(acc[i][j][3]));
+        }
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// TopK routing variant (the baseline of the DECO paper's Sec. 4 acceleration
+// experiment, Table 4): one wave per token keeps the top_k largest of the
+// logits the router GEMM stored (ties to the lower expert index) and
+// replaces the token's gates (softmax of the kept logits) and mask words.
+__global__ void __launch_bounds__(256) k_pre_topk(PreArgs a) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6), l = threadIdx.x & 63;
+  if (t >= a.T) return;
+  float zv[4];
+  bool sel[4];
+  float gate[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = 64 * j + l;
+    zv[j] = e < a.E ? a.z[(size_t)t * a.E + e] : -__builtin_inff();
+  }
+  topk_wave<4>(zv, a.top_k, sel, gate);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = 64 * j + l;
+    if (e < a.E) a.g[(size_t)t * a.E + e] = gate[j];
+    const unsigned long long word = __ballot(sel[j]);
+    if (l == 0 && j < a.W) a.mask[(size_t)t * a.W + j] = word;
+  }
+}
+
+// --------------------------------------------------------------------------
+// Exclusive scan of one int per thread over a workgroup of NW waves; *total
+// receives the sum.  s_tmp holds NW ints.
+template <int NW>
+__device__ __forceinline__ int block_excl_scan(int v, int* s_tmp, int* total) {
+  const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (l >= o) incl += y;
+  }
+  if (l == 63) s_tmp[w] = incl;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int ww = 0; ww < NW; ++ww) {
+    const int t = s_tmp[ww];
+    if (ww < w) base += t;
+    tot += t;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + incl - v;
+}
+
+// Workgroup e < E: the ascending token list of expert e and its size.
+// Workgroup E: per token, the offset of its pair slots (exclusive prefix of
+// 1 + the token's active-expert count): slot 0 for the shared expert, then
+// one per active expert in ascending e.
+constexpr int DISP_NT = 1024, DISP_TPT = 4;
+
+__global__ void __launch_bounds__(DISP_NT) k_pre_dispatch(PreArgs a) {
+  __shared__ int s_tmp[DISP_NT / 64];
+  const int e = blockIdx.x, tid = threadIdx.x;
+  const bool offsets = e == a.E;
+  const int wi = e >> 6, bit = e & 63;
+  int run = 0;
+  for (int t0 = 0; t0 < a.T; t0 += DISP_NT * DISP_TPT) {
+    const int tb = t0 + tid * DISP_TPT;
+    int v[DISP_TPT], local = 0;
+#pragma unroll
+    for (int k = 0; k < DISP_TPT; ++k) {
+      const int t = tb + k;
+      v[k] = 0;
+      if (t < a.T) {
+        if (offsets) {
+          v[k] = 1;   // slot 0: the shared expert
+          for (int ww = 0; ww < a.W; ++ww) v[k] += __popcll(a.mask[(size_t)t * a.W + ww]);
+        } else {
+          v[k] = (int)((a.mask[(size_t)t * a.W + wi] >> bit) & 1ull);
+        }
+      }
+      local += v[k];
+    }
+    int tot;
+    int pos = run + block_excl_scan<DISP_NT / 64>(local, s_tmp, &tot);
+#pragma unroll
+    for (int k = 0; k < DISP_TPT; ++k) {
+      const int t = tb + k;
+      if (offsets) {
+        if (t < a.T) a.tok_off[t] = pos;
+      } else if (v[k]) {
+        a.list_tok[(size_t)e * a.Tcap + pos] = t;
+      }
+      pos += v[k];
+    }
+    run += tot;
+  }
+  if (tid == 0) {
+    if (offsets) a.tok_off[a.T] = run;
+    else a.ecnt[e] = run;
+  }
+}
+
+// --------------------------------------------------------------------------
+template <class DT, int BNP, int MODE>
+struct ExpertShape {
+  using DN = typename DT::Down;                      // down-projection operand type
+  // token rows per tile (gated experts and the backward hold a second
+  // K = d accumulator, so their tiles have half the rows)
+  static constexpr int BM = (BNP >= 16 || MODE != XM_FWD) ? 64 : 128;
+  using TC = Tile<DT, BM, BNP, DECO_PRE_NS>;          // up-projection ring
+  static constexpr int F = BNP * 16;
+  static constexpr int NKF = F / DN::KB;             // k-blocks of the down-projection
+  static constexpr int RB = BM / 16;                 // 16-row blocks of the tile
+  static constexpr int MB = BM / 32;                 // 16-row blocks per wave
+  static constexpr int ACT_V = RB * NKF * 64;        // 16-byte LDS slots of the activations
+  static constexpr int DP = NKF >= 8 ? 2 : 4;        // W_down panels per ring stage
+  static constexpr int DSTAGE_V = DP * NKF * 64;
+  static constexpr int DNS = 3;                      // ring stages
+  static constexpr int DLPW = DP * NKF / 4;          // ring loads per wave per stage
+  // output staging: the gated pair values of one ring stage (BM tokens x
+  // 16 DP columns) go through LDS so that global stores write whole rows.
+  // 16-byte chunk q of staged row R sits at slot R*OCH + (q ^ (R % OCH)).
+  using PT = typename DT::pair;
+  static constexpr int OROW = DP * 16 * (int)sizeof(PT);   // bytes of one staged row
+  static constexpr int OCH = OROW / 16;                    // 16-byte chunks per staged row
+  static constexpr int OBUF_V = BM * OCH;
+  static constexpr int FPT = BM * OCH / 256;               // staged-row stores per thread
+  static_assert(BM * OCH % 256 == 0 && (OCH & (OCH - 1)) == 0, "staged rows must divide over the workgroup");
+  static constexpr int OCC = sizeof(typename DT::elem) == 2 ? 2 : 1;   // workgroups per CU
+  static constexpr int cmax(int x, int y) { return x > y ? x : y; }
+  // shared tiles stage their 128 x 128 output the same way
+  static constexpr int SPITCH_V = GP * 16 * (int)sizeof(PT) / 16 + 1;
+  static constexpr int LDS_V = cmax(cmax(TC::LDS_V, ACT_V),
+                                    cmax(DNS * DSTAGE_V + OBUF_V,
+                                         cmax(DenseTile<DT>::LDS_V, GM * SPITCH_V)));
+  static_assert((DP * NKF) % 4 == 0, "ring fragments must divide over the 4 waves");
+};
+
+// One persistent kernel for all grouped work after the dispatch:
+//   expert tiles  (expert e, up to BM of its tokens): gathered x . W_up[e],
+//                 NormSiLU, then . W_down[e], scaled by the gates and written
+//                 to the tokens' pair slots;
+//   shared tiles  (128 tokens x 128 columns): SiLU(x Ws_up) . Ws_down, written
+//                 to slot 0 of each token's pairs.
+// Expert tiles come first (they are the longer ones); each XCD works through
+// its own contiguous range of both lists.
+//
+// XM_GATED: a routed expert's NormSiLU output is multiplied, element by
+// element, by x . W_up[e] (a second pass of the tile over W_lin before the
+// NormSiLU input's pass; its accumulators wait in registers).
+//
+// XM_BWD (backward pass; expert tiles only): with q = dout . W_down[e]^T
+// (the ungated output gradient, a second pass of the tile), u = h~ / r and
+// a = SiLU(u) recomputed as in the forward pass, per row
+//   dg  = sum_f a_f q_f                               (gradient of the gate)
+//   du  = g q SiLU'(u)
+//   dh~ = du / r - h~ (sum_f du_f h~_f) / (F r^3)     (through NormSiLU step 2)
+// dg goes to dgbuf, dh~ and g*a to the pair-slot rows of dhbuf and agbuf
+// (operands of the weight gradients), the slot to slot_list, and
+// dh~ . W_up[e]^T (this pair's part of dLoss/dx) to the pair buffer.
+template <class DT, int BNP, int MODE>
+__global__ void __launch_bounds__(256, (ExpertShape<DT, BNP, MODE>::OCC)) k_pre_expert(PreArgs a) {
+  using elem = typename DT::elem;
+  using S = ExpertShape<DT, BNP, MODE>;
+  using TC = typename S::TC;
+  using DN = typename S::DN;
+  using PT = typename DT::pair;
+  constexpr int BM = S::BM, MB = S::MB, NBW = TC::NBW, F = S::F, NKF = S::NKF, DP = S::DP;
+  // one LDS array for everything (the operand rings, the activations, the
+  // staging buffer and the per-tile tables), carved below
+  constexpr int SMALL_V = (257 + 4 + 3 * BM + 2 * BM + (MODE == XM_BWD ? 4 * BM : 0) + 3) / 4;
+  __shared__ i32x4_t lds_all[S::LDS_V + SMALL_V];
+  i32x4_t* lds = lds_all;
+  int* s_toff = reinterpret_cast<int*>(lds_all + S::LDS_V);
+  int* s_tmp = s_toff + 257;
+  int* s_tok = s_tmp + 4;
+  int* s_slot = s_tok + BM;
+  float* s_gate = reinterpret_cast<float*>(s_slot + BM);
+  float (*s_ss)[BM] = reinterpret_cast<float (*)[BM]>(s_gate + BM);
+  float (*s_bw)[2][BM] = reinterpret_cast<float (*)[2][BM]>(s_gate + 3 * BM);   // XM_BWD: [dg, dot][wn][row]
+  const int tid = threadIdx.x, w = tid >> 6, wm = w >> 1, wn = w & 1, l = tid & 63, g = l >> 4, c = l & 15;
+
+  // expert e owns tiles s_toff[e] .. s_toff[e + 1] - 1
+  {
+    const int n = tid < a.E ? (a.ecnt[tid] + BM - 1) / BM : 0;
+    int tot;
+    const int ex = block_excl_scan<4>(n, s_tmp, &tot);
+    if (tid < a.E) s_toff[tid] = ex;
+    if (tid == 0) s_toff[a.E] = tot;
+  }
+  __syncthreads();
+  const int n_et = s_toff[a.E];
+  const int nsp = (a.pD + GP - 1) / GP;                      // shared tiles per 128 rows
+  const int n_st = MODE == XM_BWD ? 0 : ((a.T + GM - 1) / GM) * nsp;   // the backward has no shared tiles
+  const int xg = blockIdx.x % NXCD, lb = blockIdx.x / NXCD;
+  const int gx = ((int)gridDim.x - xg + NXCD - 1) / NXCD;    // workgroups on this XCD
+  const int e_beg = (int)((long long)n_et * xg / NXCD), e_end = (int)((long long)n_et * (xg + 1) / NXCD);
+  const int s_beg = (int)((long long)n_st * xg / NXCD), s_end = (int)((long long)n_st * (xg + 1) / NXCD);
+  const int n_mine = (e_end - e_beg) + (s_end - s_beg);
+  const float invF = 1.0f / (float)F;
+  const elem* x = (const elem*)a.x;
+  PT* yb = (PT*)a.ybuf;
+
+  for (int k = lb; k < n_mine; k += gx) {
+    lds_barrier();   // the previous tile no longer reads LDS
+    if (k >= e_end - e_beg) {
+      // ---- shared tile: rows m0.., panels p0.. of SiLU(x Ws_up) . Ws_down
+      using TD = DenseTile<DT>;
+      const int ts = s_beg + k - (e_end - e_beg);
+      const int m0 = (ts / nsp) * GM, p0 = (ts % nsp) * GP;
+      const elem* sbuf = (const elem*)a.sbuf;
+      auto row = [&](int r) -> const elem* {
+        const int rr = m0 + r;
+        return sbuf + (size_t)(rr < a.T ? rr : a.T - 1) * a.Fs;
+      };
+      auto panel = [&](int p) -> const char* {
+        return a.Wsd_p + frag_off(p0 + p < a.pD ? p0 + p : 0, 0, a.nkb_Fs);
+      };
+      f32x4_t acc[TD::MB][TD::NBW];
+#pragma unroll
+      for (int i = 0; i < TD::MB; ++i)
+#pragma unroll
+        for (int j = 0; j < TD::NBW; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      tile_gemm<DT, TD, true>(lds, row, panel, a.nkb_Fs, acc);
+      // stage the tile (pair type) in LDS, then store whole rows
+      constexpr int SP = S::SPITCH_V;
+#pragma unroll
+      for (int i = 0; i < TD::MB; ++i) {
+        const int R = wm * (GM / 2) + 16 * i + c;
+#pragma unroll
+        for (int j = 0; j < TD::NBW; ++j)
+          store4_pair(reinterpret_cast<PT*>(lds + R * SP) + (wn * TD::NBW + j) * 16 + 4 * g, acc[i][j]);
+      }
+      lds_barrier();
+      constexpr int CPR = GP * 16 * (int)sizeof(PT) / 16;   // 16-byte chunks per row
+      const int ncol_ch = (a.pD - p0 < GP ? a.pD - p0 : GP) * 16 * (int)sizeof(PT) / 16;
+      for (int idx = tid; idx < GM * CPR; idx += 256) {
+        const int R = idx / CPR, q = idx % CPR, r = m0 + R;
+        if (r < a.T && q < ncol_ch)
+          st16(reinterpret_cast<char*>(yb + (size_t)a.tok_off[r] * a.d + p0 * 16) + q * 16, lds[R * SP + q]);
+      }
+      continue;
+    }
+
+    // ---- expert tile
+    const int tile = e_beg + k;
+    int lo = 0, hi = a.E;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_toff[mid] <= tile) lo = mid; else hi = mid;
+    }
+    const int e = lo;
+    const int n_e = a.ecnt[e];
+    const int r0 = (tile - s_toff[e]) * BM;
+    if (tid < BM) {
+      const int rank = r0 + tid;
+      int tok = -1, slot = -1;
+      float gate = 0.f;
+      if (rank < n_e) {
+        tok = a.list_tok[(size_t)e * a.Tcap + rank];
+        const uint64_t* mrow = a.mask + (size_t)tok * a.W;
+        int below = 0;
+        for (int ww = 0; ww < (e >> 6); ++ww) below += __popcll(mrow[ww]);
+        below += __popcll(mrow[e >> 6] & ((1ull << (e & 63)) - 1ull));
+        slot = a.tok_off[tok] + 1 + below;   // slot 0 of the token holds the shared expert
+        gate = a.g[(size_t)tok * a.E + e];
+        if constexpr (MODE == XM_BWD) a.slot_list[(size_t)e * a.Tcap + rank] = slot;
+      }
+      s_tok[tid] = tok;
+      s_slot[tid] = slot;
+      s_gate[tid] = gate;
+    }
+    lds_barrier();
+
+    // up-projection of the gathered rows, all F columns
+    const char* Wu = a.Wup_p + (size_t)e * a.up_stride;
+    auto row = [&](int r) -> const elem* {
+      const int tk = s_tok[r];   // padding rows read token 0; their outputs are dropped
+      return x + (size_t)(tk >= 0 ? tk : 0) * a.d;
+    };
+    auto panel = [&](int p) -> const char* { return Wu + frag_off(p, 0, a.nkb_d); };
+    f32x4_t acc[MB][NBW], accu[MB][NBW];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NBW; ++j) acc[i][j] = accu[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if constexpr (MODE == XM_GATED) {
+      const char* Wl = a.Wlin_p + (size_t)e * a.up_stride;
+      auto panel_lin = [&](int p) -> const char* { return Wl + frag_off(p, 0, a.nkb_d); };
+      tile_gemm<DT, TC, true>(lds, row, panel_lin, a.nkb_d, accu);
+    }
+    if constexpr (MODE == XM_BWD) {
+      // q = dout . W_down[e]^T over the gathered rows
+      const char* Wt = a.WdnT_p + (size_t)e * a.up_stride;
+      const elem* dout = (const elem*)a.dout;
+      auto row_d = [&](int r) -> const elem* {
+        const int tk = s_tok[r];
+        return dout + (size_t)(tk >= 0 ? tk : 0) * a.d;
+      };
+      auto panel_t = [&](int p) -> const char* { return Wt + frag_off(p, 0, a.nkb_d); };
+      tile_gemm<DT, TC, true>(lds, row_d, panel_t, a.nkb_d, accu);
+    }
+    tile_gemm<DT, TC, true>(lds, row, panel, a.nkb_d, acc);
+
+    // NormSiLU.  Lane: local row R = wm*BM/2 + 16 i + c, columns
+    // f = 16 (wn*NBW + j) + 4 g + ii.  Subtract the mean term, then the sum
+    // of squares over the row's F columns: in-lane, over the 4 lane groups,
+    // then over the two column halves (waves wn = 0, 1) through LDS.
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      const int R = wm * (BM / 2) + 16 * i + c;
+      const int tk = s_tok[R];
+      const float* mrow = a.mbuf + (size_t)(tk < 0 ? 0 : tk) * F;
+      float ss = 0.f;
+#pragma unroll
+      for (int j = 0; j < NBW; ++j) {
+        const float4 m = *reinterpret_cast<const float4*>(mrow + 16 * (wn * NBW + j) + 4 * g);
+        acc[i][j][0] -= m.x;
+        acc[i][j][1] -= m.y;
+        acc[i][j][2] -= m.z;
+        acc[i][j][3] -= m.w;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) ss += acc[i][j][ii] * acc[i][j][ii];
+      }
+      ss += __shfl_xor(ss, 16);
+      ss += __shfl_xor(ss, 32);
+      if (g == 0) s_ss[wn][R] = ss;
+    }
+    lds_barrier();
+    if constexpr (MODE == XM_BWD) {
+      // per-row sums of a * q and du * h~ (same reduction path as the sums of squares)
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        const int R = wm * (BM / 2) + 16 * i + c;
+        const bool ok = s_tok[R] >= 0;
+        const float inv_r = ok ? 1.0f / sqrtf((s_ss[0][R] + s_ss[1][R]) * invF + a.eps) : 0.f;
+        const float gr = s_gate[R];
+        float sdg = 0.f, sdot = 0.f;
+#pragma unroll
+        for (int j = 0; j < NBW; ++j)
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            const float u = acc[i][j][ii] * inv_r, q = accu[i][j][ii];
+            sdg += silu_f(u) * q;
+            sdot += gr * q * dsilu_f(u) * acc[i][j][ii];
+          }
+        sdg += __shfl_xor(sdg, 16);
+        sdg += __shfl_xor(sdg, 32);
+        sdot += __shfl_xor(sdot, 16);
+        sdot += __shfl_xor(sdot, 32);
+        if (g == 0) {
+          s_bw[0][wn][R] = sdg;
+          s_bw[1][wn][R] = sdot;
+        }
+      }
+      lds_barrier();
+    }
+    // activations into LDS in the fragment order of the down-projection's
+    // token operand (rounded once to the operand type); the backward puts
+    // dh~ there and stores its pair rows
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      const int R = wm * (BM / 2) + 16 * i + c;
+      const bool ok = s_tok[R] >= 0;
+      const float inv_r = ok ? 1.0f / sqrtf((s_ss[0][R] + s_ss[1][R]) * invF + a.eps) : 0.f;
+      float gr = 0.f, dot_r = 0.f;
+      size_t prow = 0;
+      if constexpr (MODE == XM_BWD) {
+        gr = s_gate[R];
+        dot_r = (s_bw[1][0][R] + s_bw[1][1][R]) * inv_r * inv_r * inv_r * invF;
+        prow = (size_t)(ok ? s_slot[R] : 0) * F;
+        if (ok && wn == 0 && g == 0) a.dgbuf[(size_t)s_tok[R] * a.E + e] = s_bw[0][0][R] + s_bw[0][1][R];
+      }
+#pragma unroll
+      for (int j = 0; j < NBW; ++j) {
+        const int p = wn * NBW + j;
+        float v[4];
+        if constexpr (MODE == XM_BWD) {
+          float ag[4];
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            const float ht = acc[i][j][ii], u = ht * inv_r, q = accu[i][j][ii];
+            v[ii] = ok ? gr * q * dsilu_f(u) * inv_r - ht * dot_r : 0.f;   // dh~
+            ag[ii] = ok ? gr * silu_f(u) : 0.f;
+          }
+          if (ok) {
+            const int f = 16 * p + 4 * g;
+            store4_split<DT>((elem*)a.dhbuf + prow + f, (elem*)a.dhbuf_lo + prow + f, v);
+            store4_split<DT>((elem*)a.agbuf + prow + f, (elem*)a.agbuf_lo + prow + f, ag);
+          }
+        } else {
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            v[ii] = ok ? silu_f(acc[i][j][ii] * inv_r) : 0.f;
+            if constexpr (MODE == XM_GATED) v[ii] *= accu[i][j][ii];
+          }
+        }
+        if constexpr (DN::KB == 32) {
+          // f = 16 p + 4 g + ii: k-block p / 2, lane group 2 (p % 2) + g / 2,
+          // elements 4 (g % 2) + ii of the lane
+          const int slot = ((R >> 4) * NKF + (p >> 1)) * 64 + (R & 15) + 16 * (2 * (p & 1) + (g >> 1));
+          *reinterpret_cast<uint2*>(reinterpret_cast<char*>(lds + slot) + 8 * (g & 1)) =
+              make_uint2(DN::bits(v[0]) | (DN::bits(v[1]) << 16), DN::bits(v[2]) | (DN::bits(v[3]) << 16));
+        } else {
+          // fp32: f = 16 p + 4 g + ii: k-block p, lane group g, elements ii
+          *reinterpret_cast<float4*>(lds + ((R >> 4) * NKF + p) * 64 + (R & 15) + 16 * g) =
+              make_float4(v[0], v[1], v[2], v[3]);
+        }
+      }
+    }
+    lds_barrier();
+    // each wave keeps the activations of its token blocks in registers
+    i32x4_t act[MB][NKF];
+#pragma unroll
+    for (int jt = 0; jt < MB; ++jt)
+#pragma unroll
+      for (int kb = 0; kb < NKF; ++kb) act[jt][kb] = lds[((wm * MB + jt) * NKF + kb) * 64 + l];
+    float gt[MB];   // the backward's pair rows are not gated
+#pragma unroll
+    for (int jt = 0; jt < MB; ++jt) gt[jt] = MODE == XM_BWD ? 1.0f : s_gate[wm * (BM / 2) + 16 * jt + c];
+    lds_barrier();   // every wave holds its activations: the LDS becomes the W_down ring
+
+    // down-projection through a ring of DP-panel stages of W_down[e] (all
+    // NKF k-blocks of each panel); wave (wm, wn) takes its token blocks and
+    // panels wn*DP/2 .. of each stage.  Operands swapped (W_down as the row
+    // operand): a lane holds 4 consecutive output columns of one token.
+    const char* Wd = (MODE == XM_BWD ? a.WupT_p : a.Wdn16_p) + (size_t)e * a.dn_stride;
+    const int nds = a.pD / DP;
+    i32x4_t* obuf = lds + S::DNS * S::DSTAGE_V;   // staging buffer after the ring
+    constexpr int OCH = S::OCH;
+    auto issue = [&](int st) {
+      i32x4_t* ring = lds + (st % S::DNS) * S::DSTAGE_V;
+#pragma unroll
+      for (int i = 0; i < S::DLPW; ++i) {
+        const int f = w * S::DLPW + i;   // panel f / NKF of the stage, k-block f % NKF
+        load_lds16(Wd + frag_off(st * DP + f / NKF, f % NKF, NKF) + l * 16, ring + f * 64);
+      }
+    };
+    // copy the staged stage `st` (BM rows x OROW bytes) to the tokens' pair
+    // rows.  Exactly FPT stores per thread, none skipped (padding rows go to
+    // the scratch row after the pair buffer), so the vmcnt waits below can
+    // leave the latest stores in flight.
+    const size_t trash = (size_t)a.Tcap * (a.E + 1);
+    auto flush = [&](int st) {
+#pragma unroll
+      for (int u = 0; u < S::FPT; ++u) {
+        const int idx = tid + 256 * u, R = idx / OCH, q = idx % OCH, slot = s_slot[R];
+        st16(reinterpret_cast<char*>(yb + (slot >= 0 ? (size_t)slot : trash) * a.d + st * DP * 16) + q * 16,
+             obuf[R * OCH + (q ^ (R & (OCH - 1)))]);
+      }
+    };
+    static_assert(S::DNS == 3, "the vmcnt counts below assume a 3-stage ring");
+    // Per iteration st the memory operations are: flush(st - 1) (FPT stores),
+    // then the loads of stage st + 2.  So after the loads of stage st come:
+    // st = 0: stage 1's loads; st = 1: stage 2's; st >= 2: the stores of
+    // flush(st - 2) and stage st + 1's loads (those that exist).
+    auto wait_stage = [&](int st) {
+      const bool next = st + 1 < nds;
+      if (st < 2) {
+        if (next) wait_vmcnt<S::DLPW>(); else wait_vmcnt<0>();
+      } else {
+        if (next) wait_vmcnt<S::FPT + S::DLPW>(); else wait_vmcnt<S::FPT>();
+      }
+    };
+    if (nds > 0) issue(0);
+    if (nds > 1) issue(1);
+    for (int st = 0; st < nds; ++st) {
+      wait_stage(st);
+      lds_barrier();   // stage st landed; staged st - 1 complete; ring stage st - 1 free
+      if (st > 0) flush(st - 1);
+      if (st + 2 < nds) issue(st + 2);
+      const i32x4_t* ring = lds + (st % S::DNS) * S::DSTAGE_V;
+      f32x4_t y[MB][DP / 2];
+#pragma unroll
+      for (int jt = 0; jt < MB; ++jt)
+#pragma unroll
+        for (int q = 0; q < DP / 2; ++q) y[jt][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < NKF; ++kb) {
+        i32x4_t bv[DP / 2];
+#pragma unroll
+        for (int q = 0; q < DP / 2; ++q) bv[q] = ring[((wn * (DP / 2) + q) * NKF + kb) * 64 + l];
+#pragma unroll
+        for (int jt = 0; jt < MB; ++jt)
+#pragma unroll
+          for (int q = 0; q < DP / 2; ++q) DN::mma(y[jt][q], bv[q], act[jt][kb]);
+      }
+      lds_barrier();   // flush(st - 1) has read the staging buffer
+      // gate, round to the pair type, stage: token R, columns (wn*DP/2 + q)*16 + 4 g ..
+#pragma unroll
+      for (int jt = 0; jt < MB; ++jt) {
+        const int R = wm * (BM / 2) + 16 * jt + c;
+#pragma unroll
+        for (int q = 0; q < DP / 2; ++q) {
+          f32x4_t v = y[jt][q];
+          v[0] *= gt[jt];
+          v[1] *= gt[jt];
+          v[2] *= gt[jt];
+          v[3] *= gt[jt];
+          const int b = ((wn * (DP / 2) + q) * 16 + 4 * g) * (int)sizeof(PT);   // byte in the staged row
+          store4_pair(reinterpret_cast<PT*>(reinterpret_cast<char*>(obuf + R * OCH + ((b >> 4) ^ (R & (OCH - 1)))) +
+                                            (b & 15)),
+                      v);
+        }
+      }
+    }
+    lds_barrier();
+    if (nds > 0) flush(nds - 1);
+  }
+}
+
+// --------------------------------------------------------------------------
+// out[t] = sum of token t's pair rows (its shared-expert output, then its
+// gated expert outputs in ascending expert order), in fp32, rounded once.
+// One thread per 8 output columns; loads batched four pair rows at a time.
+// F32OUT: the sum is written in fp32 (the backward's dLoss/dx).
+template <class DT, bool F32OUT = false>
+__global__ void __launch_bounds__(256) k_pre_combine(PreArgs a) {
+  using elem = typename DT::elem;
+  using PT = typename DT::pair;
+  const int cpr = a.d / 8;
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  const int r = (int)(idx / cpr), col = (int)(idx % cpr) * 8;
+  if (r >= a.T) return;
+  const int s0 = a.tok_off[r], s1 = a.tok_off[r + 1];
+  const PT* yb = (const PT*)a.ybuf + col;
+  float v[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) v[k] = 0.f;
+  auto add = [&](const PT* p) {
+    if constexpr (sizeof(PT) == 2) {
+      const f16x8_t y = *reinterpret_cast<const f16x8_t*>(p);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] += (float)y[k];
+    } else {
+      const float4 y0 = *reinterpret_cast<const float4*>(p);
+      const float4 y1 = *reinterpret_cast<const float4*>(p + 4);
+      v[0] += y0.x; v[1] += y0.y; v[2] += y0.z; v[3] += y0.w;
+      v[4] += y1.x; v[5] += y1.y; v[6] += y1.z; v[7] += y1.w;
+    }
+  };
+  int s = s0;
+  for (; s + 4 <= s1; s += 4) {
+    // four independent loads in flight, added in slot order
+    if constexpr (sizeof(PT) == 2) {
+      f16x8_t y[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) y[u] = *reinterpret_cast<const f16x8_t*>(yb + (size_t)(s + u) * a.d);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] += (float)y[u][k];
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) add(yb + (size_t)(s + u) * a.d);
+    }
+  }
+  for (; s < s1; ++s) add(yb + (size_t)s * a.d);
+  if constexpr (F32OUT) {
+    float* orow = (float*)a.out + (size_t)r * a.d + col;
+    *reinterpret_cast<float4*>(orow) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(orow + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  } else {
+    elem* orow = (elem*)a.out + (size_t)r * a.d + col;
+    store4<DT>(orow, v[0], v[1], v[2], v[3]);
+    store4<DT>(orow + 4, v[4], v[5], v[6], v[7]);
+  }
+}
+
+// --------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) k_copy_mask(const float* __restrict__ z, const float* __restrict__ lam,
+                                                   int T, int E, int W, uint64_t* __restrict__ mask) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= T * W) return;
+  const int t = idx / W, wi = idx % W;
+  uint64_t word = 0;
+  for (int b = 0; b < 64; ++b) {
+    const int e = wi * 64 + b;
+    if (e < E && z[(size_t)t * E + e] > 0.f && lam[e] != 0.f) word |= 1ull << b;
+  }
+  mask[idx] = word;
+}
+
+int round4(int v) { return (v + 3) / 4 * 4; }
+
+// launch arguments shared by the forward and backward launchers
+PreArgs fill_pre_args(const deco_moe_layer* L, const void* x, int T, void* out) {
+  PreArgs a;
+  memset(&a, 0, sizeof(a));
+  a.x = x;
+  a.out = out;
+  a.T = T;
+  a.Tcap = L->maxT < 16 ? 16 : L->maxT;
+  a.d = L->d;
+  a.E = L->E;
+  a.F = L->F;
+  a.Fs = L->Fs;
+  a.W = L->W;
+  a.top_k = L->cfg.top_k;
+  a.nkb_d = L->nkb_d;
+  a.nkb_F = L->nkb_F;
+  a.nkb_Fs = L->nkb_Fs;
+  a.pR = L->pR;
+  a.pF = L->pF;
+  a.pD = L->pD;
+  a.pFs = L->pFs;
+  a.pF4 = round4(L->pF);
+  a.pFs4 = round4(L->pFs);
+  a.rs_nt = (a.pR + a.pF4 + a.pFs4 + GP - 1) / GP;
+  a.Wr_p = L->Wr_p;
+  a.Wup_p = L->Wup_p;
+  a.Wlin_p = L->Wlin_p;
+  a.Wbar_p = L->Wbar_p;
+  a.Wdn_p = L->Wdn_p;
+  a.Wsu_p = L->Wsu_p;
+  a.Wsd_p = L->Wsd_p;
+  a.up_stride = L->up_stride;
+  a.dn_stride = L->dn_stride;
+  a.b_r = L->b_r;
+  a.lam = L->lam;
+  a.eps = L->cfg.rms_eps;
+  a.z = L->z;
+  a.g = L->g;
+  a.mbuf = L->mbuf;
+  a.mask = L->mask;
+  a.tok_off = L->tok_off;
+  a.ecnt = L->ecnt;
+  a.list_tok = L->list_tok;
+  a.Wdn16_p = L->Wdn16_p;
+  a.sbuf = L->sbuf;
+  a.ybuf = L->ybuf;
+  return a;
+}
+
+// the routing steps shared by the forward and backward launchers: router
+// (and the mean and shared up-projection), TopK selection, dispatch
+template <class DT>
+hipError_t launch_routing(const deco_moe_layer* L, const PreArgs& a, int T, hipStream_t s) {
+  using deco_host::launch;
+  const unsigned mtiles = (unsigned)((T + GM - 1) / GM);
+  const unsigned rs_grid = mtiles * a.rs_nt;
+  hipError_t err = rs_grid <= (unsigned)L->n_cu
+      ? launch(deco_host::KS_PRE_ROUTER_SHARED, k_pre_router_shared<DT, 4>, dim3(rs_grid), dim3(256), s, a)
+      : launch(deco_host::KS_PRE_ROUTER_SHARED, k_pre_router_shared<DT, DECO_PRE_NS>, dim3(rs_grid), dim3(256), s, a);
+  if (err == hipSuccess && a.top_k > 0)
+    err = launch(deco_host::KS_PRE_TOPK, k_pre_topk, dim3((unsigned)((T + 3) / 4)), dim3(256), s, a);
+  if (err == hipSuccess)
+    err = launch(deco_host::KS_PRE_DISPATCH, k_pre_dispatch, dim3(L->E + 1), dim3(DISP_NT), s, a);
+  return err;
+}
+
+}  // namespace

@@ -5,8 +5,8 @@ It holds none of the layer's arithmetic, so both the fp64 oracle (through the
 tests) and the HIP library (through the tests and the benchmark) can be fed
 from it without sharing any computation.
 """
-from .gen import (CONFIGS, LayerInputs, make_layer, make_custom, round_to_bf16,
+from .gen import (CONFIGS, LayerInputs, make_layer, make_custom, make_dout, round_to_bf16,
                   bf16_bits, dense_equivalent_dff)
 
-__all__ = ["CONFIGS", "LayerInputs", "make_layer", "make_custom", "round_to_bf16",
+__all__ = ["CONFIGS", "LayerInputs", "make_layer", "make_custom", "make_dout", "round_to_bf16",
            "bf16_bits", "dense_equivalent_dff"]

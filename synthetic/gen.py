@@ -160,3 +160,10 @@ def make_layer(cfg_id: int, seed: int = 0, *, T: int | None = None,
     return make_custom(c["d"], c["E"], c["F"], c["Fs"], c["T"] if T is None else T,
                        c["dtype"], seed=seed, ratio=c["ratio"] if ratio is None else ratio,
                        lam=c["lam"], skew_var=c["skew_var"], name=c["name"], gated=gated)
+
+
+def make_dout(L: LayerInputs, seed: int = 1) -> np.ndarray:
+    """An upstream gradient of the layer output for the backward pass:
+    [T, d] ~ N(0, 1), cast once to the layer dtype (float64 values)."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 0xD0])))
+    return _cast(rng.standard_normal((L.T, L.d)), L.dtype)

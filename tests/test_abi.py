@@ -4,6 +4,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import sparse_moe_relu_amd as dm
@@ -119,3 +120,24 @@ def test_product_path_has_no_oracle_dependency():
                     src = f.read()
                 assert not re.search(r"^\s*(import|from)\s+oracle\b", src, re.M), fn
                 assert "oracle/" not in src, fn
+
+
+def test_backward_flag_and_host_side_backward_calls(lib):
+    cfg = dm.make_config(64, 8, 32, 64, 16, "f32", backward=True)
+    assert dm.check_config(cfg) == dm.DECO_OK
+    cfg.backward = 2
+    assert dm.check_config(cfg) == dm.DECO_ERR_INVALID_ARG
+    # null layer / grads: rejected before any HIP call
+    g = dm.DecoGrads()
+    assert lib.deco_moe_backward(None, None, None, 4, 0.0, ctypes.byref(g), None) == dm.DECO_ERR_INVALID_ARG
+    assert lib.deco_moe_backward(None, None, None, 4, 0.0, None, None) == dm.DECO_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("ratio,target", [(0.25, 0.2), (0.15, 0.2), (0.2, 0.2), (0.0, 0.05)])
+def test_sparsity_coef_update_matches_the_oracle_rule(lib, ratio, target):
+    import oracle
+    for coef in (1.0, 0.37, 3e-3):
+        got = dm.sparsity_coef_update(coef, ratio, target, 1.002)
+        want = oracle.sparsity_coef_update(np.float32(coef), np.float32(ratio), np.float32(target),
+                                           np.float32(1.002))
+        assert np.float32(got) == np.float32(want)
