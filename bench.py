@@ -43,10 +43,15 @@ KERNEL_SOURCES = {
     "k_dec_up": "sparse_moe_relu_amd/csrc/decode.hip",
     "k_dec_down": "sparse_moe_relu_amd/csrc/decode.hip",
     "k_dec_sum": "sparse_moe_relu_amd/csrc/decode.hip",
-    "k_pre_router_shared": "sparse_moe_relu_amd/csrc/prefill.hip",
-    "k_pre_dispatch": "sparse_moe_relu_amd/csrc/prefill.hip",
-    "k_pre_expert": "sparse_moe_relu_amd/csrc/prefill.hip",
-    "k_pre_combine": "sparse_moe_relu_amd/csrc/prefill.hip",
+    "k_pre_router_shared": "sparse_moe_relu_amd/csrc/prefill_kernels.h",
+    "k_pre_dispatch": "sparse_moe_relu_amd/csrc/prefill_kernels.h",
+    "k_pre_expert": "sparse_moe_relu_amd/csrc/prefill_kernels.h",
+    "k_pre_combine": "sparse_moe_relu_amd/csrc/prefill_kernels.h",
+    "k_bwd_shared": "sparse_moe_relu_amd/csrc/backward.hip",
+    "k_bwd_token": "sparse_moe_relu_amd/csrc/backward.hip",
+    "k_bwd_colsum": "sparse_moe_relu_amd/csrc/backward.hip",
+    "k_bwd_dense_dx": "sparse_moe_relu_amd/csrc/backward.hip",
+    "k_bwd_wgrad": "sparse_moe_relu_amd/csrc/backward.hip",
 }
 
 
@@ -109,6 +114,16 @@ def layer_flops(L, P: int, T: int) -> int:
     return T * 2 * L.d * L.E + P * 2 * n_mat * L.d * L.F + T * 4 * L.d * L.Fs
 
 
+def backward_flops(L, P: int, T: int) -> int:
+    """Algorithmic flops of the backward pass: for every product Y = X W of
+    the forward (router, mean term, routed up and down over the P active
+    pairs, shared up and down) the two products dX = dY W^T and dW = X^T dY.
+    The forward quantities the backward recomputes (routing, h, s) are not
+    counted."""
+    fwd = T * 2 * L.d * L.E + T * 2 * L.d * L.F + P * 4 * L.d * L.F + T * 4 * L.d * L.Fs
+    return 2 * fwd
+
+
 def dense_ffn_time(d: int, dff: int, T: int, steps: int = 20) -> float:
     """Seconds per call of the dense-equivalent non-gated FFN, SiLU(x W1) W2,
     on torch (hipBLASLt) in bf16, cycling weight copies past the Infinity Cache."""
@@ -133,7 +148,9 @@ def sweep():
     {1, 16, 256, 2048}, the d=2048 layer at T=1024 over activation ratios
     5..40 % (the d=2048 cases beside the dense-equivalent FFN), the TopK
     routing variant (k = 11 of 56 experts, 20 %) beside the ReLU routing at
-    T = 1, 8 and 4096, and the gated-expert variant at T = 1, 8 and 4096:
+    T = 1, 8 and 4096, the gated-expert variant at T = 1, 8 and 4096, and the
+    backward pass at T = 1024 and 4096 (its MFMA fraction on
+    `backward_flops`):
     tokens/s and the fraction of the attainable roofline, max(B/BW, F/MFMA)/t,
     with B the decode byte count (weights touched + x in and out) and F the
     algorithmic flops.  Prints a table; no JSON line."""
@@ -162,6 +179,18 @@ def sweep():
             td = dense_ffn_time(L.d, L.E * L.F + L.Fs, T, steps=200 if T <= 16 else 20)
             row["dense_ffn_us"] = round(td * 1e6, 2)
             row["speedup_vs_dense"] = round(td / t, 3)
+        log(json.dumps(row))
+        rows.append(row)
+    for cfg, T in ((5, 1024), (3, 4096)):
+        L = make_layer(cfg, T=T)
+        steps = 30
+        r = run_backward(L, steps, 5)
+        t = r["elapsed"] / steps
+        Fl = backward_flops(L, r["P"], T)
+        row = dict(cfg=f"c{cfg}", T=T, pass_="backward", ratio=round(r["ratio"], 4), pairs=r["P"],
+                   us_per_call=round(t * 1e6, 2), tokens_per_s=round(T / t, 1),
+                   mfma_frac=round(Fl / t / (BF16_PEAK_TFLOPS * 1e12), 4),
+                   kernels_us={k: round(v * 1e3, 2) for k, v in r["kernels"].items()})
         log(json.dumps(row))
         rows.append(row)
     print(json.dumps({"sweep": rows}), flush=True)
@@ -213,6 +242,46 @@ def run_workload(L, steps: int, warmup: int, n_layers: int | None = None, top_k:
     torch.cuda.synchronize()
     return dict(elapsed=elapsed, n_layers=n_layers, kernels={k: v[0] / v[1] for k, v in kt.items()},
                 n_union=int(act.any(axis=0).sum()), P=int(act.sum()), ratio=float(act.mean()))
+
+
+def run_backward(L, steps: int, warmup: int):
+    """Time deco_moe_backward (dout ~ N(0, 1)) over `steps` calls cycling
+    layer copies like run_workload; per-kernel averages from the launches'
+    HIP events in a second pass."""
+    import torch
+
+    import sparse_moe_relu_amd as dm
+    from synthetic import make_dout
+    from synthetic.device import layer_tensors, to_tensor, x_tensor
+
+    W = layer_tensors(L)
+    n_layers = max(1, math.ceil(CACHE_DEFEAT_BYTES / layer_weight_bytes(L)))
+    layers = [dm.Layer(**W, max_tokens=L.T, eps=L.eps, backward=True) for _ in range(n_layers)]
+    del W
+    x = x_tensor(L)
+    dout = to_tensor(make_dout(L), L.dtype)
+    for k in range(warmup):
+        g = layers[k % n_layers].backward(x, dout)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        g = layers[k % n_layers].backward(x, dout)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    dm.timing_reset()
+    dm.timing_enable(True)
+    for k in range(steps):
+        g = layers[k % n_layers].backward(x, dout)
+    torch.cuda.synchronize()
+    kt = dm.timing_read()
+    dm.timing_enable(False)
+    dm.timing_reset()
+    P = int(g["n_active_pairs"].item())
+    for ly in layers:
+        ly.free()
+    torch.cuda.synchronize()
+    return dict(elapsed=elapsed, n_layers=n_layers, kernels={k: v[0] / v[1] for k, v in kt.items()},
+                P=P, ratio=P / (L.T * L.E))
 
 
 def cpu_baseline(L, budget_s: float = 12.0):
@@ -317,7 +386,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--no-secondary", action="store_true", help="skip the prefill measurement")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
-    ap.add_argument("--workload", choices=["decode", "prefill"], default="decode",
+    ap.add_argument("--workload", choices=["decode", "prefill", "backward"], default="decode",
                     help="run only this workload's GPU loop (for profiler runs)")
     ap.add_argument("--sweep", action="store_true",
                     help="T sweep of the d=4096 layer and ratio sweep against the dense FFN (table, no JSON)")
@@ -370,6 +439,12 @@ def main():
             torch.cuda.synchronize()
             del src, dst
         L = make_layer(2, gated=args.gated) if args.workload == "decode" else make_layer(3, gated=args.gated)
+        if args.workload == "backward":
+            r = run_backward(L, args.steps, args.warmup)
+            Fl = backward_flops(L, r["P"], L.T)
+            t = r["elapsed"] / args.steps
+            log(f"backward: {t * 1e6:.2f} us/step {Fl / t / 1e12:.1f} TFLOP/s kernels={r['kernels']}")
+            return
         r = run_workload(L, args.steps, args.warmup, top_k=args.top_k)
         log(f"{args.workload}: {r['elapsed'] / args.steps * 1e6:.2f} us/step kernels={r['kernels']}")
         return

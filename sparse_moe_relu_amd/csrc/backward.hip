@@ -34,6 +34,8 @@
 // and lo = bf16(v - hi), and multiplied as hi and lo passes: one bf16
 // rounding of such an operand costs up to 2^-9 of the largest terms, which on
 // heavy-tailed gates reaches several percent of a gradient's RMS.
+#include <initializer_list>
+
 #include "prefill_kernels.h"
 
 namespace {
@@ -284,10 +286,16 @@ __global__ void __launch_bounds__(256) k_bwd_dense_dx(BwdArgs a) {
 // Weight gradients: C[M][N] = sum over K rows of A_k^T B_k, A_k and B_k rows
 // of row-major layer-dtype matrices (a token's row, or a pair slot's row).
 // A workgroup owns one 128 x 128 tile of C (of one expert, for per-expert
-// jobs) over the whole K, so every element is written once.  Each step
-// stages 32 rows of A and of B in LDS transposed (column-major: a lane's MFMA
-// fragment, EPL consecutive k of one column, is then one 16-byte read), with
-// the next step's rows loaded to registers while this one multiplies.
+// jobs) over its K range; dense jobs split K into `ksplit` ranges whose
+// partial tiles k_bwd_wsum adds in order, so every element is written once.
+// Each step stages 32 rows of A and of B in LDS transposed (column-major: a
+// lane's MFMA fragment, EPL consecutive k of one column, is then one 16-byte
+// read).  A lane loads two rows' 16-byte chunks and stores each column's
+// pair of values with one LDS write.  One LDS buffer (30 KiB: four
+// workgroups per CU hide each other's load latency); loads run two steps
+// ahead in two register sets, row indices three (two index sets, each fetched
+// before the data loads that precede its use: vector loads retire in issue
+// order, so a wait for an index never waits for data requested after it).
 struct WArgs {
   int M, N, K;                // C shape; K = rows of a dense job (per expert: the expert's count)
   int per_expert;             // 1: one C per expert over its token list
@@ -304,70 +312,142 @@ struct WArgs {
   size_t c_estride;           // per-expert stride of the outputs (elements)
   const float* add;           // optional: C += add_scale * add[m][n] (ld N)
   float add_scale;
+  int ksplit;                 // dense jobs: K ranges (1: none); > 1 writes partial tiles to `part`
+  float* part;                // [ksplit][M][N] partial sums
   const int* ecnt;
   const int* list_tok;
   const int* slot_list;
   int Tcap;
 };
 
-template <class DT, bool SA, bool SB>
-__global__ void __launch_bounds__(256) k_bwd_wgrad(WArgs a) {
+constexpr int WG_KS = 32;   // rows per step
+
+template <class DT>
+struct WShape {
   using elem = typename DT::elem;
-  constexpr int ES = (int)sizeof(elem);
-  constexpr int EPL = DT::EPL, KB = DT::KB;
-  constexpr int KS = 32;                  // rows per step
-  constexpr int PITCH = KS + 16 / ES;     // LDS elements per column (a 16-byte pad)
-  constexpr int EPC = 16 / ES;            // elements per 16-byte chunk
-  constexpr int CPR = 128 / EPC;          // chunks per 128-column row segment
-  constexpr int NLD = KS * CPR / 256;     // chunks per thread per operand and step
-  static_assert(KS % KB == 0 && (KS * CPR) % 256 == 0, "step shape");
-  constexpr int NA = SA ? 2 : 1, NB = SB ? 2 : 1;   // planes: value (high part), low part
-  __shared__ elem sA[2][NA][128 * PITCH];
-  __shared__ elem sB[2][NB][128 * PITCH];
+  static constexpr int ES = (int)sizeof(elem);
+  static constexpr int PITCH = WG_KS + 16 / ES;   // LDS elements per column (a 16-byte pad)
+  static constexpr int PLANE = 128 * PITCH;       // elements per plane
+  static constexpr int MAX_PLANES = ES == 2 ? 3 : 2;   // operand planes (value, low part) per buffer
+  static constexpr int LDS_BYTES = MAX_PLANES * PLANE * ES;
+};
+
+template <class DT, bool SA, bool SB>
+__device__ __forceinline__ void wgrad_tile(const WArgs& a, int bid, char* lds_raw) {
+  using elem = typename DT::elem;
+  using WS = WShape<DT>;
+  constexpr int ES = WS::ES, EPL = DT::EPL, KB = DT::KB, KS = WG_KS;
+  constexpr int PITCH = WS::PITCH, PLANE = WS::PLANE;
+  constexpr int EPC = 16 / ES;                // elements per 16-byte chunk
+  constexpr int CPR = 128 / EPC;              // chunks per 128-column row segment
+  constexpr int TPL = 2;                      // rows per lane task
+  constexpr int NKP = KS / TPL;               // row pairs per step
+  constexpr int NLD = NKP * CPR / 256;        // lane tasks per plane and step
+  static_assert((NKP * CPR) % 256 == 0 && KS % KB == 0, "step shape");
+  constexpr int NA = SA ? 2 : 1, NB = SB ? 2 : 1;
+  static_assert(NA + NB <= WS::MAX_PLANES, "LDS planes");
+  elem* sA = reinterpret_cast<elem*>(lds_raw);   // [NA][PLANE]
+  elem* sB = sA + NA * PLANE;                    // [NB][PLANE]
   const int tid = threadIdx.x, w = tid >> 6, wm = w >> 1, wn = w & 1, l = tid & 63, g = l >> 4, c = l & 15;
   const int per = a.tm * a.tn;
-  const int e = a.per_expert ? (int)blockIdx.x / per : 0;
-  const int tile = (int)blockIdx.x % per;
+  const int e = a.per_expert ? bid / per : 0;   // expert, or K range of a split dense job
+  const int tile = bid % per;
   const int m0 = (tile / a.tn) * 128, n0 = (tile % a.tn) * 128;
-  const int K = a.per_expert ? a.ecnt[e] : a.K;
+  // rows k0 .. k0 + K - 1 of the job
+  int k0 = 0, K = a.per_expert ? a.ecnt[e] : a.K;
+  if (!a.per_expert && a.ksplit > 1) {
+    const int len = ((a.K + a.ksplit - 1) / a.ksplit + KS - 1) / KS * KS;
+    const int kb = bid / per;
+    k0 = kb * len;
+    K = a.K - k0 < len ? a.K - k0 : len;
+    if (K < 0) K = 0;
+  }
   const int nsteps = (K + KS - 1) / KS;
   const elem* Ap[2] = {(const elem*)a.A, (const elem*)a.A2};
   const elem* Bp[2] = {(const elem*)a.B, (const elem*)a.B2};
-  auto row_index = [&](int k, int by_slot) -> size_t {
-    if (!a.per_expert) return (size_t)k;
-    const int* lst = by_slot ? a.slot_list : a.list_tok;
-    return (size_t)lst[(size_t)e * a.Tcap + k];
+  // this thread's rows of a step: 2 kp and 2 kp + 1; its chunks tid / NKP + (256 / NKP) u
+  const int kp = tid % NKP;
+  // Row of step s.  Ranks past K read the last real row (finite data at a
+  // valid address): their B values are zeroed when staged, and nothing else
+  // is masked, since out-of-range columns only reach outputs that are
+  // dropped.  No load sits under a branch and no loaded value is touched
+  // before it is staged (either would make the compiler wait for the
+  // prefetch right after issuing it).
+  const int* lst_a = a.a_slot ? a.slot_list : a.list_tok;
+  const int* lst_b = a.b_slot ? a.slot_list : a.list_tok;
+  const int eoff = a.per_expert ? e : 0;
+  auto idx = [&](int s, int t, const int* lst) -> int {
+    const int k = s * KS + TPL * kp + t;
+    const int kc = k < K ? k : K - 1;
+    const int r = lst[(size_t)eoff * a.Tcap + kc];   // read by dense jobs too (kc < T <= Tcap): no branch
+    return a.per_expert ? r : k0 + kc;
   };
-  i32x4_t ra[NA][NLD], rb[NB][NLD];
-  auto load = [&](int s) {
+  struct Regs {
+    i32x4_t va[NA][NLD][TPL];
+    i32x4_t vb[NB][NLD][TPL];
+  };
+  Regs R0, R1;
+  struct Idx {
+    int ia[TPL], ib[TPL];
+  };
+  Idx X0, X1;
+  auto fetch_idx = [&](Idx& X, int s) {
 #pragma unroll
-    for (int u = 0; u < NLD; ++u) {
-      const int q = tid + 256 * u, kk = q / CPR, ch = q % CPR, k = s * KS + kk;
-      const int ca = m0 + ch * EPC, cb = n0 + ch * EPC;
-      const bool oka = k < K && ca < a.M, okb = k < K && cb < a.N;
-      const size_t ia = oka ? row_index(k, a.a_slot) * a.lda + ca : 0;
-      const size_t ib = okb ? row_index(k, a.b_slot) * a.ldb + cb : 0;
-#pragma unroll
-      for (int h = 0; h < NA; ++h) ra[h][u] = oka ? ld16(Ap[h] + ia) : zero16();
-#pragma unroll
-      for (int h = 0; h < NB; ++h) rb[h][u] = okb ? ld16(Bp[h] + ib) : zero16();
+    for (int t = 0; t < TPL; ++t) {
+      X.ia[t] = idx(s, t, lst_a);
+      X.ib[t] = idx(s, t, lst_b);
     }
   };
-  auto stage = [&](int buf) {
+  auto load = [&](Regs& R, const Idx& X) {
+    const int* ia = X.ia;
+    const int* ib = X.ib;
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
-      const int q = tid + 256 * u, kk = q / CPR, ch = q % CPR;
+      const int ch = tid / NKP + (256 / NKP) * u;
+      const int ca = m0 + ch * EPC, cb = n0 + ch * EPC;
 #pragma unroll
-      for (int h = 0; h < NA; ++h) {
-        const elem* va = reinterpret_cast<const elem*>(&ra[h][u]);
+      for (int t = 0; t < TPL; ++t) {
+        const size_t oa = (size_t)ia[t] * a.lda + (ca < a.M ? ca : 0);
+        const size_t ob = (size_t)ib[t] * a.ldb + (cb < a.N ? cb : 0);
 #pragma unroll
-        for (int j = 0; j < EPC; ++j) sA[buf][h][(ch * EPC + j) * PITCH + kk] = va[j];
+        for (int h = 0; h < NA; ++h) R.va[h][u][t] = ld16(Ap[h] + oa);
+#pragma unroll
+        for (int h = 0; h < NB; ++h) R.vb[h][u][t] = ld16(Bp[h] + ob);
       }
+    }
+  };
+  // column col of a plane gets the two rows' values at k = 2 kp, 2 kp + 1 in one store
+  auto put = [&](elem* plane, int col, const i32x4_t& r0, const i32x4_t& r1, int j) {
+    const elem* e0 = reinterpret_cast<const elem*>(&r0);
+    const elem* e1 = reinterpret_cast<const elem*>(&r1);
+    elem* dst = plane + col * PITCH + TPL * kp;
+    if constexpr (ES == 2) {
+      *reinterpret_cast<uint32_t*>(dst) = (uint32_t)e0[j] | ((uint32_t)e1[j] << 16);
+    } else {
+      *reinterpret_cast<float2*>(dst) = make_float2(e0[j], e1[j]);
+    }
+  };
+  auto stage = [&](Regs& R, int s) {
+    // B rows past K contribute nothing
 #pragma unroll
-      for (int h = 0; h < NB; ++h) {
-        const elem* vb = reinterpret_cast<const elem*>(&rb[h][u]);
+    for (int t = 0; t < TPL; ++t) {
+      const int mk = s * KS + TPL * kp + t < K ? -1 : 0;
 #pragma unroll
-        for (int j = 0; j < EPC; ++j) sB[buf][h][(ch * EPC + j) * PITCH + kk] = vb[j];
+      for (int h = 0; h < NB; ++h)
+#pragma unroll
+        for (int u = 0; u < NLD; ++u)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) R.vb[h][u][t][q] &= mk;
+    }
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int ch = tid / NKP + (256 / NKP) * u;
+#pragma unroll
+      for (int j = 0; j < EPC; ++j) {
+#pragma unroll
+        for (int h = 0; h < NA; ++h) put(sA + h * PLANE, ch * EPC + j, R.va[h][u][0], R.va[h][u][1], j);
+#pragma unroll
+        for (int h = 0; h < NB; ++h) put(sB + h * PLANE, ch * EPC + j, R.vb[h][u][0], R.vb[h][u][1], j);
       }
     }
   };
@@ -376,31 +456,24 @@ __global__ void __launch_bounds__(256) k_bwd_wgrad(WArgs a) {
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  if (nsteps > 0) {
-    load(0);
-    stage(0);
-  }
-  __syncthreads();
-  for (int s = 0; s < nsteps; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < nsteps) load(s + 1);
+  auto frag = [&](const elem* plane, int col, int kb) {
+    return *reinterpret_cast<const i32x4_t*>(plane + col * PITCH + kb * KB + EPL * g);
+  };
+  auto compute = [&]() {
 #pragma unroll
     for (int kb = 0; kb < KS / KB; ++kb) {
       i32x4_t af[4], bf[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const i32x4_t*>(&sA[buf][0][(wm * 64 + 16 * i + c) * PITCH + kb * KB + EPL * g]);
+      for (int i = 0; i < 4; ++i) af[i] = frag(sA, wm * 64 + 16 * i + c, kb);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bf[j] = *reinterpret_cast<const i32x4_t*>(&sB[buf][0][(wn * 64 + 16 * j + c) * PITCH + kb * KB + EPL * g]);
+      for (int j = 0; j < 4; ++j) bf[j] = frag(sB, wn * 64 + 16 * j + c, kb);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) DT::mma(acc[i][j], af[i], bf[j]);
       if constexpr (SA) {   // + A_lo^T B
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          af[i] = *reinterpret_cast<const i32x4_t*>(&sA[buf][1][(wm * 64 + 16 * i + c) * PITCH + kb * KB + EPL * g]);
+        for (int i = 0; i < 4; ++i) af[i] = frag(sA + PLANE, wm * 64 + 16 * i + c, kb);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -408,21 +481,58 @@ __global__ void __launch_bounds__(256) k_bwd_wgrad(WArgs a) {
       }
       if constexpr (SB) {   // + A^T B_lo
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          af[i] = *reinterpret_cast<const i32x4_t*>(&sA[buf][0][(wm * 64 + 16 * i + c) * PITCH + kb * KB + EPL * g]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          bf[j] = *reinterpret_cast<const i32x4_t*>(&sB[buf][1][(wn * 64 + 16 * j + c) * PITCH + kb * KB + EPL * g]);
+        for (int j = 0; j < 4; ++j) bf[j] = frag(sB + PLANE, wn * 64 + 16 * j + c, kb);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j) DT::mma(acc[i][j], af[i], bf[j]);
       }
     }
-    if (s + 1 < nsteps) stage(buf ^ 1);   // the other buffer: read in step s - 1, released by its barrier
-    __syncthreads();
+  };
+  // steps s, s+1 alternate register sets R0 / R1 and index sets X0 / X1.
+  // Loads and stages run unconditionally (past the last step they read
+  // clamped rows): with no load under a branch the compiler's waits cover
+  // exactly the rows being staged.
+  if (nsteps > 0) {
+    fetch_idx(X0, 0);
+    fetch_idx(X1, 1);
+    load(R0, X0);
+    fetch_idx(X0, 2);
+    load(R1, X1);
+  }
+  for (int s = 0; s < nsteps; s += 2) {
+    // R0 holds step s, R1 step s + 1; X0 holds step s + 2
+    stage(R0, s);
+    lds_barrier();   // LDS only: the prefetched rows stay in flight
+    fetch_idx(X1, s + 3);
+    load(R0, X0);
+    compute();
+    lds_barrier();   // the buffer is read by every wave before the next stage
+    if (s + 1 >= nsteps) break;
+    // R1 holds step s + 1, R0 step s + 2; X1 holds step s + 3
+    stage(R1, s + 1);
+    lds_barrier();
+    fetch_idx(X0, s + 4);
+    load(R1, X1);
+    compute();
+    lds_barrier();
   }
   // lane (c, g) of acc[i][j]: rows m0 + wm*64 + 16 i + 4 g + ii, column n0 + wn*64 + 16 j + c
+  if (!a.per_expert && a.ksplit > 1) {
+    float* pt = a.part + (size_t)(bid / per) * a.M * a.N;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + wn * 64 + 16 * j + c;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int m = m0 + wm * 64 + 16 * i + 4 * g + ii;
+          if (m < a.M && n < a.N) pt[(size_t)m * a.N + n] = acc[i][j][ii];
+        }
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int n = n0 + wn * 64 + 16 * j + c;
@@ -443,6 +553,34 @@ __global__ void __launch_bounds__(256) k_bwd_wgrad(WArgs a) {
           out[(size_t)m * a.sld[sec]] = v;
         }
       }
+  }
+}
+
+template <class DT, bool SA, bool SB>
+__global__ void __launch_bounds__(256, 3) k_bwd_wgrad(WArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds_raw[WShape<DT>::LDS_BYTES];
+  wgrad_tile<DT, SA, SB>(a, blockIdx.x, lds_raw);
+}
+
+// C = sum of a split dense job's partial tiles in K order, stored through the
+// job's column sections (4 consecutive columns per thread)
+__global__ void __launch_bounds__(256) k_bwd_wsum(WArgs a) {
+  const long long idx = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (idx >= (long long)a.M * a.N) return;
+  const int m = (int)(idx / a.N), n = (int)(idx % a.N);
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int q = 0; q < a.ksplit; ++q) {
+    const float4 p = *reinterpret_cast<const float4*>(a.part + (size_t)q * a.M * a.N + idx);
+    v.x += p.x;
+    v.y += p.y;
+    v.z += p.z;
+    v.w += p.w;
+  }
+  const float vv[4] = {v.x, v.y, v.z, v.w};
+  for (int u = 0; u < 4; ++u) {
+    const int nn = n + u;
+    for (int q = 0; q < a.nsec; ++q)
+      if (nn >= a.sc0[q] && nn < a.sc0[q] + a.scnt[q]) a.sptr[q][(size_t)m * a.sld[q] + (nn - a.sc0[q])] = vv[u];
   }
 }
 
@@ -592,20 +730,34 @@ hipError_t backward(const deco_moe_layer* L, const void* x, const void* dout, in
   w4.c_estride = (size_t)d * F;
   w4.add = L->gbuf;
   w4.add_scale = 1.0f / (float)E;
-  for (WArgs* wp : {&w3, &w4}) {
+  for (WArgs* wp : {&w1, &w2, &w3, &w4}) {   // dense jobs read the lists too (branch-free index loads)
     wp->ecnt = L->ecnt;
     wp->list_tok = L->list_tok;
     wp->slot_list = L->slot_list;
     wp->Tcap = Tcap;
   }
-  for (const WArgs* wp : {&w1, &w2, &w3, &w4}) {
+  // the dense jobs (K = T) in K ranges of at least 512 rows, four at most,
+  // reduced in order afterwards
+  const int ks = T >= 2048 ? 4 : (T >= 1024 ? 2 : 1);
+  for (WArgs* wp : {&w1, &w2}) {
+    wp->ksplit = ks;
+    wp->part = L->wpart;
+  }
+  // dW_up (w4) last: its epilogue adds G / E from w1
+  for (WArgs* wp : {&w1, &w2, &w3, &w4}) {
     if (err != hipSuccess) break;
-    const unsigned grid = (unsigned)(wp->tm * wp->tn * (wp->per_expert ? E : 1));
-    // the low-part passes exist for bf16 layers only
-    const bool sa = sizeof(typename DT::elem) == 2 && wp->A2, sb = sizeof(typename DT::elem) == 2 && wp->B2;
-    void (*kw)(WArgs) = sa ? k_bwd_wgrad<DT, true, false> : sb ? k_bwd_wgrad<DT, false, true>
-                                                                : k_bwd_wgrad<DT, false, false>;
+    const unsigned grid = (unsigned)(wp->tm * wp->tn * (wp->per_expert ? E : wp->ksplit > 1 ? wp->ksplit : 1));
+    void (*kw)(WArgs) = k_bwd_wgrad<DT, false, false>;
+    if constexpr (sizeof(typename DT::elem) == 2) {   // the low-part passes exist for bf16 layers only
+      if (wp->A2) kw = k_bwd_wgrad<DT, true, false>;
+      else if (wp->B2) kw = k_bwd_wgrad<DT, false, true>;
+    } else {
+      wp->A2 = wp->B2 = nullptr;
+    }
     err = launch(deco_host::KS_BWD_WGRAD, kw, dim3(grid), dim3(256), s, *wp);
+    if (err == hipSuccess && !wp->per_expert && wp->ksplit > 1)   // the partials buffer is reused by the next job
+      err = launch(deco_host::KS_BWD_WGRAD, k_bwd_wsum, dim3((unsigned)(((long long)wp->M * wp->N / 4 + 255) / 256)),
+                   dim3(256), s, *wp);
   }
   if (err != hipSuccess) return err;
   return hipGetLastError();

@@ -4,6 +4,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <new>
 #include <vector>
 
@@ -245,6 +246,8 @@ static int load_layer(const deco_moe_config* cfg, const void* W_r, const float* 
   size_t o_dl = bwd ? k.take(sizeof(float) * Tcap * E) : 0;
   size_t o_gb = bwd ? k.take(sizeof(float) * (size_t)L->d * L->F) : 0;
   size_t o_cp = bwd ? k.take(sizeof(float) * 2 * ((Tcap + 63) / 64) * E) : 0;
+  const size_t wpart_n = std::max((size_t)L->d * (L->Fp + L->Ep + L->Fsp), (size_t)L->Fs * L->d);
+  size_t o_wp = bwd ? k.take(sizeof(float) * 4 * wpart_n) : 0;
   const bool split = bwd && L->esz == 2;   // low parts of the backward's bf16 operands
   size_t o_dhl = split ? k.take((size_t)L->esz * n_slots * L->F) : 0;
   size_t o_agl = split ? k.take((size_t)L->esz * n_slots * L->F) : 0;
@@ -306,6 +309,7 @@ static int load_layer(const deco_moe_config* cfg, const void* W_r, const float* 
     L->dlz = (float*)(L->ws + o_dl);
     L->gbuf = (float*)(L->ws + o_gb);
     L->colpart = (float*)(L->ws + o_cp);
+    L->wpart = (float*)(L->ws + o_wp);
     L->sb_hi = L->ws + o_sbh;
     if (split) {
       L->dhbuf_lo = L->ws + o_dhl;
