@@ -189,8 +189,9 @@ def sweep():
         Fl = backward_flops(L, r["P"], T)
         row = dict(cfg=f"c{cfg}", T=T, pass_="backward", ratio=round(r["ratio"], 4), pairs=r["P"],
                    us_per_call=round(t * 1e6, 2), tokens_per_s=round(T / t, 1),
-                   mfma_frac=round(Fl / t / (BF16_PEAK_TFLOPS * 1e12), 4),
-                   kernels_us={k: round(v * 1e3, 2) for k, v in r["kernels"].items()})
+                   tflops=round(Fl / t / 1e12, 1), mfma_frac=round(Fl / t / (BF16_PEAK_TFLOPS * 1e12), 4),
+                   kernels_us={k: round(v * 1e3, 2) for k, v in r["kernels"].items()},
+                   cpu_oracle=cpu_backward_baseline(L))
         log(json.dumps(row))
         rows.append(row)
     print(json.dumps({"sweep": rows}), flush=True)
@@ -305,6 +306,26 @@ def cpu_baseline(L, budget_s: float = 12.0):
     return dict(value=n * L.T / el, unit="tokens/s", cores=int(threads), kind="oracle",
                 sample=f"{n} full forward passes of the same workload ({L.T} tokens each), "
                        f"{el:.1f} s wall, numpy float64 + BLAS")
+
+
+def cpu_backward_baseline(L, n_tokens: int = 256, budget_s: float = 10.0):
+    """fp64 backward oracle on the host cores, on the first `n_tokens` tokens
+    of the workload (a bounded sample), repeated for ~budget_s."""
+    import oracle
+    from synthetic import make_dout
+    Ls = L.with_x(L.x[:n_tokens])
+    w = Ls.weights()
+    dout = make_dout(Ls)
+    oracle.backward(Ls.x, **w, dout=dout, eps=Ls.eps)   # warm-up
+    n, t0 = 0, time.perf_counter()
+    while True:
+        oracle.backward(Ls.x, **w, dout=dout, eps=Ls.eps)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 1000:
+            break
+    return dict(value=round(n * Ls.T / el, 1), unit="tokens/s", kind="oracle",
+                sample=f"{n} backward passes of the first {Ls.T} tokens, {el:.1f} s wall")
 
 
 def write_profile_summary(db: str, out: str, command: str):
