@@ -38,6 +38,14 @@ Readings taken where the text is silent:
     its RMS over the gate row) and multiplies the up projection elementwise:
     a = NormSiLU(x.W_gate[e]) * (x.W_up[e]), y = a.W_down[e]; the shared
     expert is unchanged;
+  * ablation switches ([W-CN] 二 reports the two NormSiLU steps removed one
+    at a time and a scalar router scale in place of the per-expert one; the
+    pages give no further detail): `normsilu_mean=False` drops step 1 (no
+    mean term), `normsilu_rms=False` drops step 2 (r = 1, eps unused), both
+    off give vanilla SiLU experts; `scalar_lambda=True` uses lambda[0] for
+    every expert; `shared_rms=True` gives the shared expert an RMS-only
+    NormSiLU (RMS over its Fs entries, eps inside the root, no mean term:
+    there is one shared expert);
   * TopK variant (top_k = k > 0): the same router projection; each token keeps
     the k experts with the largest logits, ties going to the lower expert
     index; gates are the softmax of the kept logits (conventional TopK
@@ -120,30 +128,36 @@ def mean_up(W_up) -> np.ndarray:
     return W_up.sum(axis=0) / W_up.shape[0]
 
 
-def normsilu(h, m, eps):
+def normsilu(h, m, eps, use_mean: bool = True, use_rms: bool = True):
     """NormSiLU on up-projection rows.
 
     [W-CN] Sec. 二 and [P-DECO] Sec. 1/2: first subtract the inter-expert mean
     term m = x . Wbar from the expert's intermediate activation h, then
     normalise the scale inside the expert (RMS over the F entries of the row),
-    then apply SiLU.  h, m: [n, F].
+    then apply SiLU.  h, m: [n, F].  use_mean / use_rms = False drop step 1 /
+    step 2 (the ablations of [W-CN] 二).
     """
-    ht = np.asarray(h, np.float64) - np.asarray(m, np.float64)
+    ht = np.asarray(h, np.float64)
+    if use_mean:
+        ht = ht - np.asarray(m, np.float64)
+    if not use_rms:
+        return silu(ht)
     r = np.sqrt(np.mean(ht * ht, axis=-1, keepdims=True) + eps)
     return silu(ht / r)
 
 
-def expert_mlp(x_rows, m_rows, W_up_e, W_down_e, eps):
+def expert_mlp(x_rows, m_rows, W_up_e, W_down_e, eps, use_mean: bool = True, use_rms: bool = True):
     """One non-gated routed expert: up-projection -> NormSiLU -> down-projection.
 
     [W-CN] Sec. 二 (non-gated MLP experts: two matrices, no gate matrix);
     [P-DECO] Sec. 2 "Expert design".  x_rows [n,d], m_rows [n,F] -> [n,d].
     """
     h = np.asarray(x_rows, np.float64) @ np.asarray(W_up_e, np.float64)
-    return normsilu(h, m_rows, eps) @ np.asarray(W_down_e, np.float64)
+    return normsilu(h, m_rows, eps, use_mean, use_rms) @ np.asarray(W_down_e, np.float64)
 
 
-def expert_mlp_gated(x_rows, m_rows, W_gate_e, W_up_e, W_down_e, eps):
+def expert_mlp_gated(x_rows, m_rows, W_gate_e, W_up_e, W_down_e, eps, use_mean: bool = True,
+                     use_rms: bool = True):
     """One gated routed expert ("DECO (gated)"): NormSiLU of the gate
     projection times the up projection, then the down-projection.
 
@@ -154,16 +168,20 @@ def expert_mlp_gated(x_rows, m_rows, W_gate_e, W_up_e, W_down_e, eps):
     x_rows = np.asarray(x_rows, np.float64)
     hg = x_rows @ np.asarray(W_gate_e, np.float64)
     u = x_rows @ np.asarray(W_up_e, np.float64)
-    return (normsilu(hg, m_rows, eps) * u) @ np.asarray(W_down_e, np.float64)
+    return (normsilu(hg, m_rows, eps, use_mean, use_rms) * u) @ np.asarray(W_down_e, np.float64)
 
 
-def shared_expert(x, Ws_up, Ws_down):
+def shared_expert(x, Ws_up, Ws_down, rms: bool = False, eps: float = 1e-6):
     """Always-on shared expert: non-gated MLP with plain SiLU, weight 1.
 
     [W-CN] Sec. 二 (a shared expert takes part for every token);
-    [P-DECO] Sec. 1.  x [T,d] -> [T,d].
+    [P-DECO] Sec. 1.  x [T,d] -> [T,d].  rms=True: the RMS-only NormSiLU
+    ablation (u / sqrt(mean_j u_j^2 + eps) before the SiLU).
     """
-    return silu(np.asarray(x, np.float64) @ np.asarray(Ws_up, np.float64)) @ np.asarray(Ws_down, np.float64)
+    u = np.asarray(x, np.float64) @ np.asarray(Ws_up, np.float64)
+    if rms:
+        u = u / np.sqrt(np.mean(u * u, axis=-1, keepdims=True) + eps)
+    return silu(u) @ np.asarray(Ws_down, np.float64)
 
 
 @dataclasses.dataclass
@@ -177,7 +195,8 @@ class OracleResult:
 
 
 def forward(x, W_r, b_r, lam, W_up, W_down, Ws_up, Ws_down, eps=1e-6, top_k: int = 0,
-            W_gate=None) -> OracleResult:
+            W_gate=None, normsilu_mean: bool = True, normsilu_rms: bool = True,
+            scalar_lambda: bool = False, shared_rms: bool = False) -> OracleResult:
     """Sparse evaluation of one DECO layer, expert by expert.
 
     Steps: router (the ReLU router, or with top_k > 0 the TopK variant);
@@ -187,11 +206,14 @@ def forward(x, W_r, b_r, lam, W_up, W_down, Ws_up, Ws_down, eps=1e-6, top_k: int
     "Router design": the router assigns a weight to each expert); finally the
     shared expert is added.  With W_gate [E,d,F] the routed experts are the
     gated variant (`expert_mlp_gated`) and the mean term comes from W_gate.
+    The last four switches are the ablations described in the module notes.
     """
     x = np.asarray(x, np.float64)
     T, d = x.shape
     W_up = np.asarray(W_up, np.float64)
     E = W_up.shape[0]
+    if scalar_lambda:
+        lam = np.full(E, np.asarray(lam, np.float64)[0])
     z, active, g = router_topk(x, W_r, b_r, top_k) if top_k > 0 else router(x, W_r, b_r, lam)
     m = x @ mean_up(W_up if W_gate is None else W_gate)
     routed = np.zeros((T, d))
@@ -200,11 +222,12 @@ def forward(x, W_r, b_r, lam, W_up, W_down, Ws_up, Ws_down, eps=1e-6, top_k: int
         if S.size == 0:
             continue
         if W_gate is None:
-            y = expert_mlp(x[S], m[S], W_up[e], W_down[e], eps)
+            y = expert_mlp(x[S], m[S], W_up[e], W_down[e], eps, normsilu_mean, normsilu_rms)
         else:
-            y = expert_mlp_gated(x[S], m[S], np.asarray(W_gate, np.float64)[e], W_up[e], W_down[e], eps)
+            y = expert_mlp_gated(x[S], m[S], np.asarray(W_gate, np.float64)[e], W_up[e], W_down[e], eps,
+                                 normsilu_mean, normsilu_rms)
         routed[S] += g[S, e][:, None] * y
-    shared = shared_expert(x, Ws_up, Ws_down)
+    shared = shared_expert(x, Ws_up, Ws_down, shared_rms, eps)
     return OracleResult(out=routed + shared, z=z, active=active, g=g, routed=routed, shared=shared)
 
 
@@ -226,7 +249,9 @@ def _topk_gates_by_subsets(z_row: np.ndarray, k: int) -> np.ndarray:
 
 
 def forward_dense_bruteforce(x, W_r, b_r, lam, W_up, W_down, Ws_up, Ws_down, eps=1e-6,
-                             top_k: int = 0, W_gate=None) -> np.ndarray:
+                             top_k: int = 0, W_gate=None, normsilu_mean: bool = True,
+                             normsilu_rms: bool = True, scalar_lambda: bool = False,
+                             shared_rms: bool = False) -> np.ndarray:
     """Dense brute force for small inputs: every expert for every token.
 
     Ignores the mask: each (token, expert) pair is evaluated one at a time,
@@ -245,18 +270,22 @@ def forward_dense_bruteforce(x, W_r, b_r, lam, W_up, W_down, Ws_up, Ws_down, eps
         zz = x @ np.asarray(W_r, np.float64) + np.asarray(b_r, np.float64)
         g = np.stack([_topk_gates_by_subsets(zz[t], top_k) for t in range(T)])
     else:
-        _, _, g = router(x, W_r, b_r, lam)
+        lam_e = np.asarray(lam, np.float64)
+        _, _, g = router(x, W_r, b_r, np.array([lam_e[0] if scalar_lambda else lam_e[e] for e in range(E)]))
     out = np.zeros((T, d))
     Wn = W_up if W_gate is None else np.asarray(W_gate, np.float64)   # NormSiLU input
     for t in range(T):
         h_all = np.stack([x[t] @ Wn[e] for e in range(E)])      # [E, F]
         m_t = h_all.sum(axis=0) / E
         for e in range(E):
-            ht = h_all[e] - m_t
-            r = np.sqrt(np.mean(ht * ht) + eps)
+            ht = h_all[e] - m_t if normsilu_mean else h_all[e]
+            r = np.sqrt(np.mean(ht * ht) + eps) if normsilu_rms else 1.0
             a = silu(ht / r)
             if W_gate is not None:
                 a = a * (x[t] @ W_up[e])
             out[t] += g[t, e] * (a @ W_down[e])
-        out[t] += silu(x[t] @ np.asarray(Ws_up, np.float64)) @ np.asarray(Ws_down, np.float64)
+        us = x[t] @ np.asarray(Ws_up, np.float64)
+        if shared_rms:
+            us = us / np.sqrt(np.mean(us * us) + eps)
+        out[t] += silu(us) @ np.asarray(Ws_down, np.float64)
     return out

@@ -388,3 +388,82 @@ def test_gated_mean_term_is_the_mean_gate_projection():
     a = oracle.forward(L.x, **L.weights(), eps=L.eps)
     b = oracle.forward(L.x, **dict(L.weights(), W_gate=L.W_gate + shift[None]), eps=L.eps)
     assert np.max(np.abs(a.out - b.out)) <= 1e-10 * _rms(a.out)
+
+
+# ablation switches ------------------------------------------------------------
+ABL = [dict(normsilu_mean=False), dict(normsilu_rms=False), dict(normsilu_mean=False, normsilu_rms=False),
+       dict(scalar_lambda=True), dict(shared_rms=True)]
+
+
+@pytest.mark.parametrize("flags", ABL)
+def test_ablation_sparse_forward_equals_dense_bruteforce(flags):
+    L = make_custom(96, 7, 64, 80, 10, "f32", seed=31, ratio=0.35)
+    r = oracle.forward(L.x, **L.weights(), eps=L.eps, **flags)
+    bf = oracle.forward_dense_bruteforce(L.x, **L.weights(), eps=L.eps, **flags)
+    assert r.active.any() and not r.active.all()
+    assert np.max(np.abs(r.out - bf)) <= 1e-12 * _rms(bf)
+    # each switch changes the result
+    base = oracle.forward(L.x, **L.weights(), eps=L.eps)
+    assert np.max(np.abs(r.out - base.out)) > 1e-3 * _rms(base.out)
+
+
+def test_ablation_without_both_steps_is_a_vanilla_silu_mlp():
+    # library check: torch's SiLU MLP per expert, gate-weighted, plus the shared expert
+    L = make_custom(64, 5, 32, 48, 9, "f32", seed=32, ratio=0.4)
+    r = oracle.forward(L.x, **L.weights(), eps=L.eps, normsilu_mean=False, normsilu_rms=False)
+    x = torch.tensor(L.x)
+    out = torch.nn.functional.silu(x @ torch.tensor(L.Ws_up)) @ torch.tensor(L.Ws_down)
+    g = torch.tensor(r.g)
+    for e in range(L.E):
+        y = torch.nn.functional.silu(x @ torch.tensor(L.W_up[e])) @ torch.tensor(L.W_down[e])
+        out = out + g[:, e:e + 1] * y
+    assert np.max(np.abs(r.out - out.numpy())) <= 1e-12 * _rms(r.out)
+
+
+def test_ablation_no_rms_equals_full_on_unit_rms_rows():
+    # one token, two experts, F = 2: h~ = (1, -1) and (-1, 1) have RMS 1, so
+    # with eps = 0 dropping step 2 changes nothing; scaling W_up by 3 then
+    # changes the no-RMS layer only
+    x = np.array([[1.0]])
+    W_up = np.array([[[2.0, 0.0]], [[0.0, 2.0]]])
+    W_down = np.array([[[0.5], [-1.5]], [[2.0], [0.25]]])
+    kw = dict(W_r=np.array([[1.0, 1.0]]), b_r=np.zeros(2), lam=np.array([0.7, 1.3]), W_down=W_down,
+              Ws_up=np.array([[0.3]]), Ws_down=np.array([[1.1]]), eps=0.0)
+    full = oracle.forward(x, W_up=W_up, **kw).out
+    norms = oracle.forward(x, W_up=W_up, **kw, normsilu_rms=False).out
+    assert np.allclose(full, norms, rtol=0, atol=1e-15)
+    full3 = oracle.forward(x, W_up=3 * W_up, **kw).out
+    norms3 = oracle.forward(x, W_up=3 * W_up, **kw, normsilu_rms=False).out
+    assert np.allclose(full3, full, rtol=0, atol=1e-15)          # RMS step: scale invariant
+    assert np.max(np.abs(norms3 - full)) > 1e-2
+
+
+def test_ablation_no_mean_equals_full_on_zero_mean_experts():
+    L = make_custom(64, 6, 32, 48, 9, "f32", seed=33, ratio=0.4)
+    W0 = L.W_up - L.W_up.mean(axis=0, keepdims=True)     # the experts' mean is zero
+    w = dict(L.weights(), W_up=W0)
+    a = oracle.forward(L.x, **w, eps=L.eps).out
+    b = oracle.forward(L.x, **w, eps=L.eps, normsilu_mean=False).out
+    assert np.max(np.abs(a - b)) <= 1e-12 * _rms(a)
+
+
+def test_ablation_shared_rms_is_scale_invariant_and_plain_on_unit_rms():
+    L = make_custom(64, 4, 32, 2, 1, "f32", seed=34)
+    L.b_r = np.full_like(L.b_r, -1e3)                    # shared expert only
+    x = np.zeros((1, 64))
+    x[0, 0] = 1.0
+    Ws_up = np.zeros((64, 2))
+    Ws_up[0] = [1.0, -1.0]                               # u = (1, -1): RMS 1
+    w = dict(L.weights(), Ws_up=Ws_up)
+    plain = oracle.forward(x, **w, eps=0.0).out
+    rmsv = oracle.forward(x, **w, eps=0.0, shared_rms=True).out
+    assert np.allclose(plain, rmsv, rtol=0, atol=1e-15)
+    rms5 = oracle.forward(x, **dict(w, Ws_up=5 * Ws_up), eps=0.0, shared_rms=True).out
+    assert np.allclose(rms5, rmsv, rtol=0, atol=1e-15)
+
+
+def test_ablation_scalar_lambda_is_lambda0_everywhere():
+    L = make_custom(64, 6, 32, 48, 9, "f32", seed=35, ratio=0.4)
+    a = oracle.forward(L.x, **L.weights(), eps=L.eps, scalar_lambda=True)
+    b = oracle.forward(L.x, **dict(L.weights(), lam=np.full_like(L.lam, L.lam[0])), eps=L.eps)
+    assert np.array_equal(a.out, b.out) and np.array_equal(a.g, b.g)
