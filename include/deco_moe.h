@@ -76,12 +76,25 @@ typedef struct {
   int32_t backward;     /* 0: inference only.  1: also keep the transposed      */
                         /* weight copies and the workspace deco_moe_backward    */
                         /* needs (non-gated experts only)                       */
+  /* Ablation switches (the qidianchuan.cn write-up, section 二, reports the   */
+  /* NormSiLU steps removed one at a time and a scalar router scale in place   */
+  /* of the per-expert one).  All 0 is the DECO layer; backward needs all 0.   */
+  int32_t normsilu;     /* bit DECO_NORMSILU_NO_MEAN: no mean term (step 1);    */
+                        /* bit DECO_NORMSILU_NO_RMS: no RMS step (r = 1); both: */
+                        /* vanilla SiLU experts                                 */
+  int32_t scalar_lambda;/* 1: lambda[0] scales every expert                     */
+  int32_t shared_rms;   /* 1: the shared expert's SiLU input is divided by its  */
+                        /* RMS over the Fs entries (eps inside the root)        */
 } deco_moe_config;
+
+#define DECO_NORMSILU_NO_MEAN 1
+#define DECO_NORMSILU_NO_RMS 2
 
 /* Check a configuration without touching the GPU.  Returns DECO_OK,
  * DECO_ERR_INVALID_ARG (null, non-positive sizes, negative eps, top_k outside
- * 0..n_experts, backward not 0 or 1) or DECO_ERR_UNSUPPORTED (shape outside
- * the set documented in the struct). */
+ * 0..n_experts, a flag outside its range) or DECO_ERR_UNSUPPORTED (shape
+ * outside the set documented in the struct, or backward = 1 with an ablation
+ * switch on). */
 int deco_moe_check_config(const deco_moe_config* cfg);
 
 /* Copy, pack and preprocess one layer's weights into library-owned device

@@ -30,6 +30,8 @@ DECO_PATH_AUTO = 0
 DECO_PATH_DECODE = 1
 DECO_PATH_PREFILL = 2
 DECODE_MAX_T = 16
+DECO_NORMSILU_NO_MEAN = 1
+DECO_NORMSILU_NO_RMS = 2
 
 EXPORTS = ("deco_moe_check_config", "deco_moe_load_weights", "deco_moe_load_weights_gated", "deco_moe_forward",
            "deco_moe_forward_path", "deco_moe_copy_routing", "deco_moe_copy_mean_up",
@@ -42,7 +44,8 @@ class DecoConfig(ctypes.Structure):
     _fields_ = [("d_model", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("d_ff", ctypes.c_int32), ("d_ff_shared", ctypes.c_int32),
                 ("max_tokens", ctypes.c_int32), ("dtype", ctypes.c_int),
-                ("rms_eps", ctypes.c_float), ("top_k", ctypes.c_int32), ("backward", ctypes.c_int32)]
+                ("rms_eps", ctypes.c_float), ("top_k", ctypes.c_int32), ("backward", ctypes.c_int32),
+                ("normsilu", ctypes.c_int32), ("scalar_lambda", ctypes.c_int32), ("shared_rms", ctypes.c_int32)]
 
 
 class DecoGrads(ctypes.Structure):
@@ -111,11 +114,15 @@ def status_string(status: int) -> str:
 
 
 def make_config(d: int, E: int, F: int, Fs: int, max_tokens: int, dtype: str = "bf16",
-                eps: float = 1e-6, top_k: int = 0, backward: bool = False) -> DecoConfig:
+                eps: float = 1e-6, top_k: int = 0, backward: bool = False, *, normsilu_mean: bool = True,
+                normsilu_rms: bool = True, scalar_lambda: bool = False, shared_rms: bool = False) -> DecoConfig:
     """top_k = 0: DECO's ReLU routing; 1..E: the TopK routing variant.
-    backward: keep what deco_moe_backward needs."""
+    backward: keep what deco_moe_backward needs.  The last four are the
+    ablation switches of deco_moe_config."""
     dt = {"bf16": DECO_DT_BF16, "f32": DECO_DT_F32}[dtype]
-    return DecoConfig(d, E, F, Fs, max_tokens, dt, eps, top_k, 1 if backward else 0)
+    ns = (0 if normsilu_mean else DECO_NORMSILU_NO_MEAN) | (0 if normsilu_rms else DECO_NORMSILU_NO_RMS)
+    return DecoConfig(d, E, F, Fs, max_tokens, dt, eps, top_k, 1 if backward else 0, ns,
+                      1 if scalar_lambda else 0, 1 if shared_rms else 0)
 
 
 def sparsity_coef_update(coef: float, active_ratio: float, target_ratio: float, factor: float = 1.002) -> float:
@@ -148,7 +155,9 @@ class Layer:
     """
 
     def __init__(self, W_r, b_r, lam, W_up, W_down, Ws_up, Ws_down, *, max_tokens: int,
-                 eps: float = 1e-6, top_k: int = 0, W_gate=None, backward: bool = False, stream=None):
+                 eps: float = 1e-6, top_k: int = 0, W_gate=None, backward: bool = False,
+                 normsilu_mean: bool = True, normsilu_rms: bool = True, scalar_lambda: bool = False,
+                 shared_rms: bool = False, stream=None):
         lib = load_library()
         dtype = {torch.bfloat16: "bf16", torch.float32: "f32"}.get(W_up.dtype)
         if dtype is None:
@@ -166,7 +175,8 @@ class Layer:
         for name, t in (("b_r", b_r), ("lam", lam)):
             if tuple(t.shape) != (E,) or t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
                 raise ValueError(f"{name}: expected contiguous device float32 ({E},)")
-        self.cfg = make_config(d, E, F, Fs, max_tokens, dtype, eps, top_k, backward)
+        self.cfg = make_config(d, E, F, Fs, max_tokens, dtype, eps, top_k, backward, normsilu_mean=normsilu_mean,
+                               normsilu_rms=normsilu_rms, scalar_lambda=scalar_lambda, shared_rms=shared_rms)
         self.top_k = top_k
         self.gated = W_gate is not None
         self.d, self.E, self.F, self.Fs, self.dtype = d, E, F, Fs, dtype

@@ -87,6 +87,7 @@ struct deco_moe_layer {
   float* gbuf;             // [d][F] x^T dm (gradient of Wbar)
   float* colpart;          // [2][ceil(Tcap / 64)][E] partial column sums (db_r, dlambda)
   float* wpart;            // [4][max(d * (Fp + Ep + Fsp), Fs * d)] partial weight-gradient tiles
+  float* sraw;             // shared_rms: [Tcap][Fs] x . Ws_up before the RMS-only NormSiLU (fp32)
   char* ybuf;              // [Tcap * (E + 1) + 1][d] pair buffer, token-major: per token its
                            // shared-expert output, then gate * expert output for each
                            // active expert in ascending order (fp16 for bf16 layers,

@@ -47,6 +47,8 @@ struct DecArgs {
   int n_shared, wg_per_e;   // up workgroups of the shared expert; per routed expert
   int top_k, pR, W;         // TopK variant (0: ReLU routing); router panels; mask words
   int gated;                // 1: gated experts (up workgroups for W_up[e] follow each expert's own)
+  int no_mean, no_rms;      // NormSiLU ablations: drop the mean term / the RMS step
+  float* sraw;              // RMS-only NormSiLU shared expert: [16][Fs] x . Ws_up (fp32), else null
   const char* Wr_p;
   const char* Wup_p;        // NormSiLU input projection (a gated expert's gate projection)
   const char* Wlin_p;       // gated experts' up-projection
@@ -208,8 +210,11 @@ __global__ void __launch_bounds__(NW * 64) k_dec_up(DecArgs a) {
   const bool lin = rs >= a.wg_per_e;   // W_up slice of a gated expert: no mean term, no RMS
   const int wgi = lin ? rs - a.wg_per_e : rs;
   const int p0 = routed ? wgi * NP : bid * NP;
-  // what the first stream reads: the mean term, or a gated expert's W_up
-  const char* w_first = lin ? a.Wlin_p + (size_t)e * a.up_stride : a.Wbar_p;
+  // what the first stream reads: the mean term, or a gated expert's W_up, or
+  // (no mean term: an ablation) the expert's own slice
+  const char* w_up_e = a.Wup_p + (size_t)e * a.up_stride;
+  const bool mean_pass = !lin && !a.no_mean;   // stream -Wbar, then W_up[e]
+  const char* w_first = lin ? a.Wlin_p + (size_t)e * a.up_stride : (a.no_mean ? w_up_e : a.Wbar_p);
   const int nkb = a.nkb_d;
   const int kb_lo = (w * nkb) / NW, kb_hi = ((w + 1) * nkb) / NW;
   const elem* xrow = (const elem*)a.x + (size_t)c * a.d;
@@ -267,11 +272,11 @@ __global__ void __launch_bounds__(NW * 64) k_dec_up(DecArgs a) {
       return;  // no token keeps expert e: none of its weights are read
     }
     stream(w_first, true, true);
-    if (!lin) {
+    if (mean_pass) {
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int p = 0; p < NP; ++p) acc[p] = -acc[p];
-      stream(a.Wup_p + (size_t)e * a.up_stride, false, x_fits);
+      stream(w_up_e, false, x_fits);
     }
   } else if (routed) {
     // router logits of expert e for the 16 (padded) token rows
@@ -320,12 +325,12 @@ __global__ void __launch_bounds__(NW * 64) k_dec_up(DecArgs a) {
     // acc = -(x . Wbar) + x . W_up[e]: the NormSiLU mean term and the expert
     // in one fp32 accumulator (a gated expert's W_up slice: acc = x . W_up[e])
     stream(w_first, true, true);
-    if (!lin) {
+    if (mean_pass) {
       __builtin_amdgcn_sched_barrier(0);   // keep the two streams' registers apart
 #pragma unroll
       for (int p = 0; p < NP; ++p) acc[p] = -acc[p];
       // (with a single chunk per wave xf still holds it)
-      stream(a.Wup_p + (size_t)e * a.up_stride, false, x_fits);
+      stream(w_up_e, false, x_fits);
     }
   } else {
     stream(a.Wsu_p, false, false);
@@ -345,7 +350,11 @@ __global__ void __launch_bounds__(NW * 64) k_dec_up(DecArgs a) {
   }
   if (!routed) {
     // shared expert: plain SiLU, stored as down-projection operand fragments
-    if (mine) *reinterpret_cast<elem*>(a.sactf + frag_elem_off<DT>(row, col)) = DT::from_f32(silu_f(v));
+    // (RMS-only NormSiLU: the pre-activation, for k_dec_shared_rms)
+    if (mine) {
+      if (a.sraw) a.sraw[(size_t)row * a.Fs + col] = v;
+      else *reinterpret_cast<elem*>(a.sactf + frag_elem_off<DT>(row, col)) = DT::from_f32(silu_f(v));
+    }
     return;
   }
   if (mine && row < a.T) (lin ? a.ubuf : a.hbuf)[((size_t)e * 16 + row) * a.F + col] = v;
@@ -498,7 +507,7 @@ __global__ void __launch_bounds__(NW * 64) k_dec_down(DecArgs a) {
         float ss = 0.f;
 #pragma unroll
         for (int wi = 0; wi < DEC_WGMAX; ++wi) ss += part_ss[wi];
-        rinv = 1.0f / sqrtf(ss * invF + a.eps);
+        rinv = a.no_rms ? 1.0f : 1.0f / sqrtf(ss * invF + a.eps);
         gt = ld_buf(rg, 4u * (unsigned)(t * a.E + e));   // 0 for an inactive pair
       }
       s_rinv[k] = rinv;
@@ -569,6 +578,30 @@ __global__ void __launch_bounds__(NW * 64) k_dec_down(DecArgs a) {
   }
 }
 
+// RMS-only NormSiLU of the shared expert (an ablation switch): one workgroup
+// per padded token row; s = SiLU(u / sqrt(mean_j u_j^2 + eps)) stored as the
+// down-projection operand fragments k_dec_up stores otherwise (rows past T: 0).
+template <class DT>
+__global__ void __launch_bounds__(256) k_dec_shared_rms(DecArgs a) {
+  using elem = typename DT::elem;
+  __shared__ float s_part[4];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const float* u = a.sraw + (size_t)r * a.Fs;
+  float ss = 0.f;
+  if (r < a.T)
+    for (int j = tid; j < a.Fs; j += 256) ss += u[j] * u[j];
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+  if ((tid & 63) == 0) s_part[tid >> 6] = ss;
+  __syncthreads();
+  const float tot = s_part[0] + s_part[1] + s_part[2] + s_part[3];
+  const float rinv = 1.0f / sqrtf(tot / (float)a.Fs + a.eps);
+  for (int j = tid; j < a.Fs; j += 256) {
+    const float v = r < a.T ? silu_f(u[j] * rinv) : 0.f;
+    *reinterpret_cast<elem*>(a.sactf + frag_elem_off<DT>(r, j)) = DT::from_f32(v);
+  }
+}
+
 // out[t][c] = sum over the Q reduction splits of the down kernel's partial
 // products, in split order (deterministic); 4 consecutive columns per thread.
 template <class DT>
@@ -617,6 +650,9 @@ hipError_t decode(const deco_moe_layer* L, const void* x, int T, void* out, hipS
   a.wg_per_e = L->pF / DEC_NP;
   a.top_k = L->cfg.top_k;
   a.gated = L->gated;
+  a.no_mean = (L->cfg.normsilu & DECO_NORMSILU_NO_MEAN) != 0;
+  a.no_rms = (L->cfg.normsilu & DECO_NORMSILU_NO_RMS) != 0;
+  a.sraw = L->cfg.shared_rms ? L->sraw : nullptr;
   a.Wlin_p = L->Wlin_p;
   a.ubuf = L->ubuf;
   a.pR = L->pR;
@@ -649,6 +685,10 @@ hipError_t decode(const deco_moe_layer* L, const void* x, int T, void* out, hipS
   err = deco_host::launch(deco_host::KS_DEC_UP, k_dec_up<DT, DEC_NW, DEC_NP>, dim3(grid_up),
                                      dim3(DEC_NW * 64), s, a);
   if (err != hipSuccess) return err;
+  if (a.sraw) {
+    err = deco_host::launch(deco_host::KS_DEC_UP, k_dec_shared_rms<DT>, dim3(16), dim3(256), s, a);
+    if (err != hipSuccess) return err;
+  }
   const unsigned grid_dn = (unsigned)(L->n_groups * L->dec_q);
   auto down = L->dec_multi ? (a.gated ? k_dec_down<DT, DEC_NW, true, true> : k_dec_down<DT, DEC_NW, true, false>)
                            : (a.gated ? k_dec_down<DT, DEC_NW, false, true> : k_dec_down<DT, DEC_NW, false, false>);

@@ -28,6 +28,10 @@ int validate_cfg(const deco_moe_config* c) {
   if (c->d_ff_shared % 32 != 0 || c->d_ff_shared > 16384) return DECO_ERR_UNSUPPORTED;
   if (c->max_tokens > (1 << 20)) return DECO_ERR_UNSUPPORTED;
   if (c->backward != 0 && c->backward != 1) return DECO_ERR_INVALID_ARG;
+  if (c->normsilu < 0 || c->normsilu > 3 || (c->scalar_lambda != 0 && c->scalar_lambda != 1) ||
+      (c->shared_rms != 0 && c->shared_rms != 1))
+    return DECO_ERR_INVALID_ARG;
+  if (c->backward && (c->normsilu || c->scalar_lambda || c->shared_rms)) return DECO_ERR_UNSUPPORTED;
   return DECO_OK;
 }
 
@@ -237,6 +241,7 @@ static int load_layer(const deco_moe_config* cfg, const void* W_r, const float* 
   // pair buffer plus one scratch row that takes the stores of padding rows
   size_t o_yb = k.take((size_t)L->esz * (Tcap * (E + 1) + 1) * L->d);
   const size_t n_slots = Tcap * (E + 1) + 1;
+  size_t o_sr = L->cfg.shared_rms ? k.take(sizeof(float) * Tcap * L->Fs) : 0;
   size_t o_dg = bwd ? k.take(sizeof(float) * Tcap * E) : 0;
   size_t o_dh = bwd ? k.take((size_t)L->esz * n_slots * L->F) : 0;
   size_t o_ag = bwd ? k.take((size_t)L->esz * n_slots * L->F) : 0;
@@ -299,6 +304,7 @@ static int load_layer(const deco_moe_config* cfg, const void* W_r, const float* 
   L->list_tok = (int*)(L->ws + o_lt);
   L->sbuf = L->ws + o_sb;
   L->ybuf = L->ws + o_yb;
+  L->sraw = L->cfg.shared_rms ? (float*)(L->ws + o_sr) : nullptr;
   if (bwd) {
     L->dgbuf = (float*)(L->ws + o_dg);
     L->dhbuf = L->ws + o_dh;
@@ -325,7 +331,13 @@ static int load_layer(const deco_moe_config* cfg, const void* W_r, const float* 
   size_t zero_end = o_to;
   err = hipMemsetAsync(L->ws, 0, zero_end, s);
   if (err == hipSuccess) err = hipMemcpyAsync(L->b_r, b_r, sizeof(float) * E, hipMemcpyDeviceToDevice, s);
-  if (err == hipSuccess) err = hipMemcpyAsync(L->lam, lambda, sizeof(float) * E, hipMemcpyDeviceToDevice, s);
+  if (err == hipSuccess) {
+    if (L->cfg.scalar_lambda)   // ablation: lambda[0] for every expert
+      for (int e = 0; e < E && err == hipSuccess; ++e)
+        err = hipMemcpyAsync(L->lam + e, lambda, sizeof(float), hipMemcpyDeviceToDevice, s);
+    else
+      err = hipMemcpyAsync(L->lam, lambda, sizeof(float) * E, hipMemcpyDeviceToDevice, s);
+  }
   if (err == hipSuccess) err = deco_host::launch_pack_all(L, W_r, W_norm, W_lin, W_down, Ws_up, Ws_down, s);
   if (err == hipSuccess) err = deco_host::plan_decode(L);
   if (err == hipSuccess) err = deco_host::plan_prefill(L);

@@ -50,6 +50,8 @@ struct PreArgs {
   void* out;
   int T, Tcap, d, E, F, Fs, W;
   int top_k;           // TopK routing variant (0: ReLU routing)
+  int no_mean, no_rms; // NormSiLU ablations: drop the mean term / the RMS step
+  float* sraw;         // RMS-only NormSiLU shared expert: [T][Fs] x . Ws_up (fp32), else null
   int nkb_d, nkb_F, nkb_Fs, pR, pF, pD, pFs;
   int pF4, pFs4;       // panel counts of the mean and shared sections, padded to 4
   int rs_nt;           // 8-panel column tiles of the router/mean/shared GEMM
@@ -248,13 +250,36 @@ __global__ void __launch_bounds__(256, 2) k_pre_router_shared(PreArgs a) {
 #pragma unroll
         for (int i = 0; i < TC::MB; ++i) {
           const int r = m0 + wm * (GM / 2) + 16 * i + c;
-          if (r < a.T)
-            store4<DT>(sb + (size_t)r * a.Fs + c0, silu_f(acc[i][j][0]), silu_f(acc[i][j][1]),
-                       silu_f(acc[i][j][2]), silu_f(acc[i][j][3]));
+          if (r < a.T) {
+            if (a.sraw)   // RMS-only NormSiLU: the row's RMS spans other workgroups' columns
+              *reinterpret_cast<float4*>(a.sraw + (size_t)r * a.Fs + c0) =
+                  make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+            else
+              store4<DT>(sb + (size_t)r * a.Fs + c0, silu_f(acc[i][j][0]), silu_f(acc[i][j][1]),
+                         silu_f(acc[i][j][2]), silu_f(acc[i][j][3]));
+          }
         }
       }
     }
   }
+}
+
+// RMS-only NormSiLU of the shared expert (an ablation switch): one wave per
+// token, s = SiLU(u / sqrt(mean_j u_j^2 + eps)) from the fp32 row u = x . Ws_up.
+template <class DT>
+__global__ void __launch_bounds__(256) k_pre_shared_rms(PreArgs a) {
+  using elem = typename DT::elem;
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + w;
+  if (r >= a.T) return;
+  const float* u = a.sraw + (size_t)r * a.Fs;
+  float ss = 0.f;
+  for (int j = l; j < a.Fs; j += 64) ss += u[j] * u[j];
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+  const float rinv = 1.0f / sqrtf(ss / (float)a.Fs + a.eps);
+  elem* sb = (elem*)a.sbuf + (size_t)r * a.Fs;
+  for (int j = l; j < a.Fs; j += 64) sb[j] = DT::from_f32(silu_f(u[j] * rinv));
 }
 
 // --------------------------------------------------------------------------
@@ -569,14 +594,15 @@ __global__ void __launch_bounds__(256, (ExpertShape<DT, BNP, MODE>::OCC)) k_pre_
       const int R = wm * (BM / 2) + 16 * i + c;
       const int tk = s_tok[R];
       const float* mrow = a.mbuf + (size_t)(tk < 0 ? 0 : tk) * F;
+      const float mk = a.no_mean ? 0.f : 1.f;   // ablation: no mean term
       float ss = 0.f;
 #pragma unroll
       for (int j = 0; j < NBW; ++j) {
         const float4 m = *reinterpret_cast<const float4*>(mrow + 16 * (wn * NBW + j) + 4 * g);
-        acc[i][j][0] -= m.x;
-        acc[i][j][1] -= m.y;
-        acc[i][j][2] -= m.z;
-        acc[i][j][3] -= m.w;
+        acc[i][j][0] -= mk * m.x;
+        acc[i][j][1] -= mk * m.y;
+        acc[i][j][2] -= mk * m.z;
+        acc[i][j][3] -= mk * m.w;
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) ss += acc[i][j][ii] * acc[i][j][ii];
       }
@@ -620,7 +646,7 @@ __global__ void __launch_bounds__(256, (ExpertShape<DT, BNP, MODE>::OCC)) k_pre_
     for (int i = 0; i < MB; ++i) {
       const int R = wm * (BM / 2) + 16 * i + c;
       const bool ok = s_tok[R] >= 0;
-      const float inv_r = ok ? 1.0f / sqrtf((s_ss[0][R] + s_ss[1][R]) * invF + a.eps) : 0.f;
+      const float inv_r = ok ? (a.no_rms ? 1.0f : 1.0f / sqrtf((s_ss[0][R] + s_ss[1][R]) * invF + a.eps)) : 0.f;
       float gr = 0.f, dot_r = 0.f;
       size_t prow = 0;
       if constexpr (MODE == XM_BWD) {
@@ -855,6 +881,9 @@ PreArgs fill_pre_args(const deco_moe_layer* L, const void* x, int T, void* out) 
   a.Fs = L->Fs;
   a.W = L->W;
   a.top_k = L->cfg.top_k;
+  a.no_mean = (L->cfg.normsilu & DECO_NORMSILU_NO_MEAN) != 0;
+  a.no_rms = (L->cfg.normsilu & DECO_NORMSILU_NO_RMS) != 0;
+  a.sraw = L->cfg.shared_rms ? L->sraw : nullptr;
   a.nkb_d = L->nkb_d;
   a.nkb_F = L->nkb_F;
   a.nkb_Fs = L->nkb_Fs;
@@ -902,6 +931,8 @@ hipError_t launch_routing(const deco_moe_layer* L, const PreArgs& a, int T, hipS
       : launch(deco_host::KS_PRE_ROUTER_SHARED, k_pre_router_shared<DT, DECO_PRE_NS>, dim3(rs_grid), dim3(256), s, a);
   if (err == hipSuccess && a.top_k > 0)
     err = launch(deco_host::KS_PRE_TOPK, k_pre_topk, dim3((unsigned)((T + 3) / 4)), dim3(256), s, a);
+  if (err == hipSuccess && a.sraw)
+    err = launch(deco_host::KS_PRE_ROUTER_SHARED, k_pre_shared_rms<DT>, dim3((unsigned)((T + 3) / 4)), dim3(256), s, a);
   if (err == hipSuccess)
     err = launch(deco_host::KS_PRE_DISPATCH, k_pre_dispatch, dim3(L->E + 1), dim3(DISP_NT), s, a);
   return err;

@@ -141,3 +141,14 @@ def test_sparsity_coef_update_matches_the_oracle_rule(lib, ratio, target):
         want = oracle.sparsity_coef_update(np.float32(coef), np.float32(ratio), np.float32(target),
                                            np.float32(1.002))
         assert np.float32(got) == np.float32(want)
+
+
+def test_ablation_switches_are_validated(lib):
+    cfg = dm.make_config(64, 8, 32, 64, 16, "f32", backward=True, shared_rms=True)
+    assert dm.check_config(cfg) == dm.DECO_ERR_UNSUPPORTED   # the backward covers the DECO layer only
+    cfg = dm.make_config(64, 8, 32, 64, 16, "f32", normsilu_mean=False, normsilu_rms=False, scalar_lambda=True)
+    assert dm.check_config(cfg) == dm.DECO_OK and cfg.normsilu == 3
+    for field, bad in (("normsilu", 4), ("normsilu", -1), ("scalar_lambda", 2), ("shared_rms", 7)):
+        c = dm.make_config(64, 8, 32, 64, 16, "f32")
+        setattr(c, field, bad)
+        assert dm.check_config(c) == dm.DECO_ERR_INVALID_ARG, field
