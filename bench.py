@@ -148,9 +148,10 @@ def sweep():
     {1, 16, 256, 2048}, the d=2048 layer at T=1024 over activation ratios
     5..40 % (the d=2048 cases beside the dense-equivalent FFN), the TopK
     routing variant (k = 11 of 56 experts, 20 %) beside the ReLU routing at
-    T = 1, 8 and 4096, the gated-expert variant at T = 1, 8 and 4096, and the
-    backward pass at T = 1024 and 4096 (its MFMA fraction on
-    `backward_flops`):
+    T = 1, 8 and 4096, the gated-expert variant at T = 1, 8 and 4096, the
+    ablation switches (vanilla SiLU experts, RMS-only NormSiLU shared expert)
+    at T = 8 and 4096, and the backward pass at T = 1024 and 4096 (its MFMA
+    fraction on `backward_flops`):
     tokens/s and the fraction of the attainable roofline, max(B/BW, F/MFMA)/t,
     with B the decode byte count (weights touched + x in and out) and F the
     algorithmic flops.  Prints a table; no JSON line."""
@@ -161,21 +162,26 @@ def sweep():
              + [(2, 1, None, 11, False), (2, 8, None, 11, False), (3, 4096, None, 0, False),
                 (3, 4096, None, 11, False)]
              + [(2, 1, None, 0, True), (2, 8, None, 0, True), (3, 4096, None, 0, True)])
-    for cfg, T, ratio, k, gated in cases:
+    cases = [c + ({},) for c in cases]
+    vanilla, srms = dict(normsilu_mean=False, normsilu_rms=False), dict(shared_rms=True)
+    cases += [(2, 8, None, 0, False, vanilla), (3, 4096, None, 0, False, vanilla),
+              (2, 8, None, 0, False, srms), (3, 4096, None, 0, False, srms)]
+    for cfg, T, ratio, k, gated, flags in cases:
         L = make_layer(cfg, T=T, ratio=ratio, gated=gated)
         steps = 400 if T <= 16 else (100 if T <= 256 else 30)
-        r = run_workload(L, steps, max(5, steps // 10), top_k=k)
+        r = run_workload(L, steps, max(5, steps // 10), top_k=k, flags=flags)
         t = r["elapsed"] / steps
         B = decode_bytes(L, r["n_union"], T)
         Bt = sum(B.values()) + T * L.d * (2 if L.dtype == "bf16" else 4)
         Fl = layer_flops(L, r["P"], T)
         fb, ff = Bt / t / (HBM_PEAK_GBS * 1e9), Fl / t / (BF16_PEAK_TFLOPS * 1e12)
         row = dict(cfg=f"c{cfg}", T=T, routing=f"top{k}" if k else "relu",
-                   experts="gated" if gated else "non-gated", ratio=round(r["ratio"], 4), experts_touched=r["n_union"], pairs=r["P"],
+                   experts="gated" if gated else "non-gated",
+                   ablation=",".join(f"{k}={v}" for k, v in flags.items()) or "none", ratio=round(r["ratio"], 4), experts_touched=r["n_union"], pairs=r["P"],
                    us_per_call=round(t * 1e6, 2), tokens_per_s=round(T / t, 1),
                    hbm_frac=round(fb, 4), mfma_frac=round(ff, 4), attainable_frac=round(max(fb, ff), 4),
                    kernels_us={k: round(v * 1e3, 2) for k, v in r["kernels"].items()})
-        if cfg in (2, 5) and k == 0 and not gated:
+        if cfg in (2, 5) and k == 0 and not gated and not flags:
             td = dense_ffn_time(L.d, L.E * L.F + L.Fs, T, steps=200 if T <= 16 else 20)
             row["dense_ffn_us"] = round(td * 1e6, 2)
             row["speedup_vs_dense"] = round(td / t, 3)
@@ -204,7 +210,7 @@ def layer_weight_bytes(L) -> int:
 
 
 # GPU measurement ---------------------------------------------------------------
-def run_workload(L, steps: int, warmup: int, n_layers: int | None = None, top_k: int = 0):
+def run_workload(L, steps: int, warmup: int, n_layers: int | None = None, top_k: int = 0, flags: dict | None = None):
     import numpy as np
     import torch
 
@@ -214,7 +220,7 @@ def run_workload(L, steps: int, warmup: int, n_layers: int | None = None, top_k:
     W = layer_tensors(L)
     if n_layers is None:
         n_layers = max(1, math.ceil(CACHE_DEFEAT_BYTES / layer_weight_bytes(L)))
-    layers = [dm.Layer(**W, max_tokens=L.T, eps=L.eps, top_k=top_k) for _ in range(n_layers)]
+    layers = [dm.Layer(**W, max_tokens=L.T, eps=L.eps, top_k=top_k, **(flags or {})) for _ in range(n_layers)]
     del W
     torch.cuda.synchronize()
     x = x_tensor(L)
