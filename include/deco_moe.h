@@ -75,7 +75,7 @@ typedef struct {
                         /* lambda unused; experts and shared expert unchanged.  */
   int32_t backward;     /* 0: inference only.  1: also keep the transposed      */
                         /* weight copies and the workspace deco_moe_backward    */
-                        /* needs (non-gated experts only)                       */
+                        /* needs (non-gated experts, n_experts >= 2)            */
   /* Ablation switches (the qidianchuan.cn write-up, section 二, reports the   */
   /* NormSiLU steps removed one at a time and a scalar router scale in place   */
   /* of the per-expert one).  All 0 is the DECO layer; backward needs all 0.   */
@@ -94,7 +94,7 @@ typedef struct {
  * DECO_ERR_INVALID_ARG (null, non-positive sizes, negative eps, top_k outside
  * 0..n_experts, a flag outside its range) or DECO_ERR_UNSUPPORTED (shape
  * outside the set documented in the struct, or backward = 1 with an ablation
- * switch on). */
+ * switch on or a single routed expert). */
 int deco_moe_check_config(const deco_moe_config* cfg);
 
 /* Copy, pack and preprocess one layer's weights into library-owned device

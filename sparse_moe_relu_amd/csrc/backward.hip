@@ -49,6 +49,9 @@ struct BwdArgs {
   const char* Wsu_p;
   const char* WsdT_p;
   const char* Bcat_p;
+  const char* WbarLo_p;       // bf16 layers: low part of Wbar (K = d, N = F)
+  float* mbuf;                // [T][F] m = x . Wbar
+  int pF;
   const float* lam;
   const float* z;
   const float* g;
@@ -123,6 +126,51 @@ template <class DT>
 __device__ __forceinline__ void put_split(typename DT::elem* hi, typename DT::elem* lo, size_t i, float v) {
   hi[i] = DT::from_f32(v);
   if constexpr (sizeof(typename DT::elem) == 2) lo[i] = DT::from_f32(v - DT::to_f32(hi[i]));
+}
+
+// m += x . Wbar_lo (bf16 layers): the recomputed mean term then carries
+// Wbar to about 16 significant bits.  A bf16 Wbar alone costs dW_up over 2 %
+// of its RMS when few tokens average the error (T = 1).
+template <class DT>
+__global__ void __launch_bounds__(256) k_bwd_mean_lo(BwdArgs a) {
+  using elem = typename DT::elem;
+  using TD = DenseTile<DT>;
+  __shared__ i32x4_t lds[TD::LDS_V];
+  const int tid = threadIdx.x, w = tid >> 6, wm = w >> 1, wn = w & 1, l = tid & 63, g = l >> 4, c = l & 15;
+  const int nct = (a.pF + GP - 1) / GP;
+  const int m0 = (blockIdx.x / nct) * GM, p0 = (blockIdx.x % nct) * GP;
+  const elem* x = (const elem*)a.x;
+  auto row = [&](int r) -> const elem* {
+    const int rr = m0 + r;
+    return x + (size_t)(rr < a.T ? rr : a.T - 1) * a.d;
+  };
+  auto panel = [&](int p) -> const char* {
+    return a.WbarLo_p + frag_off(p0 + p < a.pF ? p0 + p : a.pF - 1, 0, a.nkb_d);
+  };
+  f32x4_t acc[TD::MB][TD::NBW];
+#pragma unroll
+  for (int i = 0; i < TD::MB; ++i)
+#pragma unroll
+    for (int j = 0; j < TD::NBW; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  tile_gemm<DT, TD, true>(lds, row, panel, a.nkb_d, acc);
+#pragma unroll
+  for (int i = 0; i < TD::MB; ++i) {
+    const int r = m0 + wm * (GM / 2) + 16 * i + c;
+    if (r >= a.T) continue;
+#pragma unroll
+    for (int j = 0; j < TD::NBW; ++j) {
+      const int p = p0 + wn * TD::NBW + j;
+      if (p < a.pF) {
+        float4* mp = reinterpret_cast<float4*>(a.mbuf + (size_t)r * a.F + p * 16 + 4 * g);
+        float4 v = *mp;
+        v.x += acc[i][j][0];
+        v.y += acc[i][j][1];
+        v.z += acc[i][j][2];
+        v.w += acc[i][j][3];
+        *mp = v;
+      }
+    }
+  }
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -641,6 +689,9 @@ hipError_t backward(const deco_moe_layer* L, const void* x, const void* dout, in
   b.Wsu_p = L->Wsu_p;
   b.WsdT_p = L->WsdT_p;
   b.Bcat_p = L->Bcat_p;
+  b.WbarLo_p = L->WbarLo_p;
+  b.mbuf = L->mbuf;
+  b.pF = L->pF;
   b.lam = L->lam;
   b.z = L->z;
   b.g = L->g;
@@ -665,6 +716,8 @@ hipError_t backward(const deco_moe_layer* L, const void* x, const void* dout, in
 
   const unsigned mtiles = (unsigned)((T + GM - 1) / GM);
   hipError_t err = launch_routing<DT>(L, a, T, s);
+  if (err == hipSuccess && L->WbarLo_p)
+    err = launch(deco_host::KS_BWD_SHARED, k_bwd_mean_lo<DT>, dim3(mtiles * ((L->pF + GP - 1) / GP)), dim3(256), s, b);
   if (err == hipSuccess)
     err = launch(deco_host::KS_BWD_SHARED, k_bwd_shared<DT>, dim3(mtiles * ((L->pFs + GP - 1) / GP)), dim3(256), s, b);
   if (err == hipSuccess)

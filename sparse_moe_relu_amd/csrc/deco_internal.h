@@ -50,6 +50,7 @@ struct deco_moe_layer {
   char* WupT_p;            // per expert [pD][nkb_F] frags of W_up[e]^T (K = F, N = d), down operand type
   char* WsdT_p;            // [pFs][nkb_d] frags of Ws_down^T (K = d, N = Fs)
   char* Bcat_p;            // [pD][nkb_cat] frags of [Wbar^T; W_r^T; Ws_up^T] (K = Fp + Ep + Fsp, N = d)
+  char* WbarLo_p;          // bf16 layers: [pF][nkb_d] frags of Wbar - bf16(Wbar)
 
   // workspace (one allocation, sized for max(maxT, 16) tokens)
   char* ws;

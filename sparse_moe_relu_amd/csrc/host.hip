@@ -32,6 +32,9 @@ int validate_cfg(const deco_moe_config* c) {
       (c->shared_rms != 0 && c->shared_rms != 1))
     return DECO_ERR_INVALID_ARG;
   if (c->backward && (c->normsilu || c->scalar_lambda || c->shared_rms)) return DECO_ERR_UNSUPPORTED;
+  // one routed expert: the mean term equals its projection, h~ = 0 and every
+  // routed gradient vanishes (NormSiLU divides 0 by sqrt(eps))
+  if (c->backward && c->n_experts < 2) return DECO_ERR_UNSUPPORTED;
   return DECO_OK;
 }
 
@@ -219,6 +222,7 @@ static int load_layer(const deco_moe_config* cfg, const void* W_r, const float* 
   size_t o_upT = bwd ? w.take(L->dn_stride * E) : 0;
   size_t o_sdT = bwd ? w.take((size_t)L->pFs * L->nkb_d * KBy) : 0;
   size_t o_cat = bwd ? w.take((size_t)L->pD * L->nkb_cat * KBy) : 0;
+  size_t o_wbl = (bwd && L->esz == 2) ? w.take((size_t)L->pF * L->nkb_d * KBy) : 0;
   L->wmem_bytes = w.off;
   // workspace
   const size_t Tcap = (size_t)(L->maxT < 16 ? 16 : L->maxT);
@@ -287,6 +291,7 @@ static int load_layer(const deco_moe_config* cfg, const void* W_r, const float* 
     L->WupT_p = L->wmem + o_upT;
     L->WsdT_p = L->wmem + o_sdT;
     L->Bcat_p = L->wmem + o_cat;
+    L->WbarLo_p = L->esz == 2 ? L->wmem + o_wbl : nullptr;
   }
   L->z = (float*)(L->ws + o_z);
   L->g = (float*)(L->ws + o_g);

@@ -35,7 +35,8 @@ __global__ void __launch_bounds__(256) k_mean_up(const typename DT::elem* __rest
 __device__ __forceinline__ float src_f32(const uint16_t* p, size_t i) { return bf16_to_f32(p[i]); }
 __device__ __forceinline__ float src_f32(const float* p, size_t i) { return p[i]; }
 
-template <class DT, class SRC>
+// LO: pack v - bf16(v), the part of an fp32 value a bf16 copy drops
+template <class DT, class SRC, bool LO = false>
 __global__ void __launch_bounds__(256) k_pack(const SRC* __restrict__ src, size_t src_bstride,
                                               int K, int N, size_t sk, size_t sn, int P, int nkb,
                                               int kb_off, int nkb_tot,
@@ -55,6 +56,7 @@ __global__ void __launch_bounds__(256) k_pack(const SRC* __restrict__ src, size_
   for (int j = 0; j < DT::EPL; ++j) {
     const int k = kb * DT::KB + DT::frag_k(g, j);
     f[j] = (k < K && n < N) ? src_f32(s, (size_t)k * sk + (size_t)n * sn) : 0.f;
+    if constexpr (LO) f[j] -= bf16_to_f32(f32_to_bf16(f[j]));
   }
   st16(dst + (size_t)b * dst_bstride + frag_off(p, kb_off + kb, nkb_tot) + (size_t)l * 16, DT::pack(f));
 }
@@ -118,6 +120,10 @@ hipError_t pack_all(deco_moe_layer* L, const void* W_r, const void* W_up, const 
     pack_tr<DT, float>(L->wbar, 0, F, d, L->pD, L->Fp / KB, 0, L->nkb_cat, L->Bcat_p, 0, 1, s);
     pack_tr<DT, E_t>(W_r, 0, E, d, L->pD, L->Ep / KB, L->Fp / KB, L->nkb_cat, L->Bcat_p, 0, 1, s);
     pack_tr<DT, E_t>(Ws_up, 0, Fs, d, L->pD, L->Fsp / KB, (L->Fp + L->Ep) / KB, L->nkb_cat, L->Bcat_p, 0, 1, s);
+    // the low part of Wbar (K = d, N = F): the backward's mean term is x . (Wbar_bf16 + Wbar_lo)
+    if constexpr (sizeof(E_t) == 2)
+      k_pack<DT, float, true><<<pack_grid(L->pF, L->nkb_d, 1), 256, 0, s>>>(L->wbar, 0, d, F, (size_t)F, 1, L->pF,
+                                                                            L->nkb_d, 0, L->nkb_d, L->WbarLo_p, 0);
   }
   return hipGetLastError();
 }

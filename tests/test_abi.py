@@ -152,3 +152,10 @@ def test_ablation_switches_are_validated(lib):
         c = dm.make_config(64, 8, 32, 64, 16, "f32")
         setattr(c, field, bad)
         assert dm.check_config(c) == dm.DECO_ERR_INVALID_ARG, field
+
+
+def test_backward_needs_two_routed_experts(lib):
+    # with one routed expert the mean term equals its projection (h~ = 0)
+    assert dm.check_config(dm.make_config(64, 1, 32, 64, 16, "bf16", backward=True)) == dm.DECO_ERR_UNSUPPORTED
+    assert dm.check_config(dm.make_config(64, 2, 32, 64, 16, "bf16", backward=True)) == dm.DECO_OK
+    assert dm.check_config(dm.make_config(64, 1, 32, 64, 16, "bf16")) == dm.DECO_OK

@@ -154,3 +154,16 @@ def test_backward_needs_the_flag_and_rejects_bad_calls():
         layer.backward(x_tensor(L), dout, reg_coef=0.5)   # the entropy term is for the ReLU routing
     assert ex.value.status == dm.DECO_ERR_INVALID_ARG
     layer.free()
+
+
+@pytest.mark.parametrize("case", ["T1", "E2", "E256_sparse"])
+def test_backward_edges(case):
+    if case == "T1":
+        L = make_layer(2, T=1)                      # a single token: one-row tiles everywhere
+    elif case == "E2":
+        L = make_custom(64, 2, 32, 32, 9, "bf16", seed=0, ratio=0.5)   # the fewest experts it supports
+    else:
+        L = make_custom(128, 256, 32, 64, 40, "bf16", seed=3, ratio=0.05)   # 4 mask words, many empty experts
+    layer = _layer(L, max(L.T, 16))
+    check(L, layer, label=case, seed=6)
+    layer.free()
