@@ -188,8 +188,13 @@ __global__ void __launch_bounds__(NW * 64) k_dec_topk(DecArgs a) {
   for (int e = tid; e < a.E; e += NW * 64) a.rflag[e] = s_act[e] ? 2u : 1u;
 }
 
-template <class DT, int NW, int NP>
+// VAR: bit 0 gated experts, bit 1 no mean term, bit 2 RMS-only NormSiLU
+// shared expert (the variants are separate instantiations, so the default
+// one carries none of their logic)
+constexpr int DV_GATED = 1, DV_NO_MEAN = 2, DV_SHARED_RMS = 4;
+template <class DT, int NW, int NP, int VAR>
 __global__ void __launch_bounds__(NW * 64) k_dec_up(DecArgs a) {
+  constexpr bool GT = (VAR & DV_GATED) != 0, NM = (VAR & DV_NO_MEAN) != 0, SR = (VAR & DV_SHARED_RMS) != 0;
   using elem = typename DT::elem;
   constexpr int CH = DEC_CH;
   static_assert(NP * 256 <= NW * 64, "one output entry per thread");
@@ -204,17 +209,17 @@ __global__ void __launch_bounds__(NW * 64) k_dec_up(DecArgs a) {
   const int bid = blockIdx.x;
   const bool routed = bid >= a.n_shared;
   const int rb = bid - a.n_shared;
-  const int spe = a.wg_per_e << a.gated;
+  const int spe = GT ? 2 * a.wg_per_e : a.wg_per_e;
   const int e = routed ? rb / spe : 0;
   const int rs = routed ? rb % spe : 0;
-  const bool lin = rs >= a.wg_per_e;   // W_up slice of a gated expert: no mean term, no RMS
+  const bool lin = GT && rs >= a.wg_per_e;   // W_up slice of a gated expert: no mean term, no RMS
   const int wgi = lin ? rs - a.wg_per_e : rs;
   const int p0 = routed ? wgi * NP : bid * NP;
   // what the first stream reads: the mean term, or a gated expert's W_up, or
   // (no mean term: an ablation) the expert's own slice
   const char* w_up_e = a.Wup_p + (size_t)e * a.up_stride;
-  const bool mean_pass = !lin && !a.no_mean;   // stream -Wbar, then W_up[e]
-  const char* w_first = lin ? a.Wlin_p + (size_t)e * a.up_stride : (a.no_mean ? w_up_e : a.Wbar_p);
+  const bool mean_pass = !lin && !NM;   // stream -Wbar, then W_up[e]
+  const char* w_first = lin ? a.Wlin_p + (size_t)e * a.up_stride : (NM ? w_up_e : a.Wbar_p);
   const int nkb = a.nkb_d;
   const int kb_lo = (w * nkb) / NW, kb_hi = ((w + 1) * nkb) / NW;
   const elem* xrow = (const elem*)a.x + (size_t)c * a.d;
@@ -352,7 +357,7 @@ __global__ void __launch_bounds__(NW * 64) k_dec_up(DecArgs a) {
     // shared expert: plain SiLU, stored as down-projection operand fragments
     // (RMS-only NormSiLU: the pre-activation, for k_dec_shared_rms)
     if (mine) {
-      if (a.sraw) a.sraw[(size_t)row * a.Fs + col] = v;
+      if constexpr (SR) a.sraw[(size_t)row * a.Fs + col] = v;
       else *reinterpret_cast<elem*>(a.sactf + frag_elem_off<DT>(row, col)) = DT::from_f32(silu_f(v));
     }
     return;
@@ -376,7 +381,7 @@ __global__ void __launch_bounds__(NW * 64) k_dec_up(DecArgs a) {
   }
 }
 
-template <class DT, int NW, bool MULTI, bool GATED>
+template <class DT, int NW, bool MULTI, bool GATED, bool NO_RMS>
 __global__ void __launch_bounds__(NW * 64) k_dec_down(DecArgs a) {
   using elem = typename DT::elem;
   using DN = typename DT::Down;   // operand type of the routed down-projection
@@ -507,7 +512,7 @@ __global__ void __launch_bounds__(NW * 64) k_dec_down(DecArgs a) {
         float ss = 0.f;
 #pragma unroll
         for (int wi = 0; wi < DEC_WGMAX; ++wi) ss += part_ss[wi];
-        rinv = a.no_rms ? 1.0f : 1.0f / sqrtf(ss * invF + a.eps);
+        rinv = NO_RMS ? 1.0f : 1.0f / sqrtf(ss * invF + a.eps);
         gt = ld_buf(rg, 4u * (unsigned)(t * a.E + e));   // 0 for an inactive pair
       }
       s_rinv[k] = rinv;
@@ -532,9 +537,8 @@ __global__ void __launch_bounds__(NW * 64) k_dec_down(DecArgs a) {
           const float rinv = s_rinv[k], gt = s_gate[k];
 #pragma unroll
           for (int j = 0; j < EPL; ++j) {
-            float v = silu_f(hv[ub][j] * rinv) * gt;
-            if constexpr (GATED) v *= uv[ub][j];
-            hv[ub][j] = gt != 0.f ? v : 0.f;
+            if constexpr (GATED) hv[ub][j] = gt != 0.f ? silu_f(hv[ub][j] * rinv) * gt * uv[ub][j] : 0.f;
+            else hv[ub][j] = gt != 0.f ? silu_f(hv[ub][j] * rinv) * gt : 0.f;
           }
           const i32x4_t af = DN::pack(hv[ub]);
 #pragma unroll
@@ -629,6 +633,30 @@ __global__ void __launch_bounds__(256) k_dec_sum(DecArgs a) {
 }
 
 template <class DT>
+void (*up_kernel(int var))(DecArgs) {
+  switch (var) {
+    case 0: return k_dec_up<DT, DEC_NW, DEC_NP, 0>;
+    case 1: return k_dec_up<DT, DEC_NW, DEC_NP, 1>;
+    case 2: return k_dec_up<DT, DEC_NW, DEC_NP, 2>;
+    case 3: return k_dec_up<DT, DEC_NW, DEC_NP, 3>;
+    case 4: return k_dec_up<DT, DEC_NW, DEC_NP, 4>;
+    case 5: return k_dec_up<DT, DEC_NW, DEC_NP, 5>;
+    case 6: return k_dec_up<DT, DEC_NW, DEC_NP, 6>;
+    default: return k_dec_up<DT, DEC_NW, DEC_NP, 7>;
+  }
+}
+
+template <class DT, bool MULTI>
+void (*down_kernel_m(bool gated, bool no_rms))(DecArgs) {
+  return gated ? (no_rms ? k_dec_down<DT, DEC_NW, MULTI, true, true> : k_dec_down<DT, DEC_NW, MULTI, true, false>)
+               : (no_rms ? k_dec_down<DT, DEC_NW, MULTI, false, true> : k_dec_down<DT, DEC_NW, MULTI, false, false>);
+}
+template <class DT>
+void (*down_kernel(bool multi, bool gated, bool no_rms))(DecArgs) {
+  return multi ? down_kernel_m<DT, true>(gated, no_rms) : down_kernel_m<DT, false>(gated, no_rms);
+}
+
+template <class DT>
 hipError_t decode(const deco_moe_layer* L, const void* x, int T, void* out, hipStream_t s) {
   DecArgs a;
   a.x = x;
@@ -682,7 +710,9 @@ hipError_t decode(const deco_moe_layer* L, const void* x, int T, void* out, hipS
     if (err != hipSuccess) return err;
   }
   const unsigned grid_up = (unsigned)(a.n_shared + L->E * (a.wg_per_e << a.gated));
-  err = deco_host::launch(deco_host::KS_DEC_UP, k_dec_up<DT, DEC_NW, DEC_NP>, dim3(grid_up),
+  const int var = (a.gated ? DV_GATED : 0) | (a.no_mean ? DV_NO_MEAN : 0) | (a.sraw ? DV_SHARED_RMS : 0);
+  void (*up)(DecArgs) = up_kernel<DT>(var);
+  err = deco_host::launch(deco_host::KS_DEC_UP, up, dim3(grid_up),
                                      dim3(DEC_NW * 64), s, a);
   if (err != hipSuccess) return err;
   if (a.sraw) {
@@ -690,8 +720,7 @@ hipError_t decode(const deco_moe_layer* L, const void* x, int T, void* out, hipS
     if (err != hipSuccess) return err;
   }
   const unsigned grid_dn = (unsigned)(L->n_groups * L->dec_q);
-  auto down = L->dec_multi ? (a.gated ? k_dec_down<DT, DEC_NW, true, true> : k_dec_down<DT, DEC_NW, true, false>)
-                           : (a.gated ? k_dec_down<DT, DEC_NW, false, true> : k_dec_down<DT, DEC_NW, false, false>);
+  void (*down)(DecArgs) = down_kernel<DT>(L->dec_multi != 0, a.gated != 0, a.no_rms != 0);
   err = deco_host::launch(deco_host::KS_DEC_DOWN, down, dim3(grid_dn), dim3(DEC_NW * 64), s, a);
   if (err != hipSuccess) return err;
   const unsigned grid_sum = (unsigned)((T * L->d / 4 + 255) / 256);
