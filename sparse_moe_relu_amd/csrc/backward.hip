@@ -279,8 +279,17 @@ __global__ void __launch_bounds__(256) k_bwd_colsum2(BwdArgs a) {
   const int nch = (a.T + CS_ROWS - 1) / CS_ROWS;
   if (q == 0 && e == 0 && a.n_active) a.n_active[0] = a.tok_off[a.T] - a.T;   // slots minus the shared ones
   if (e >= a.E) return;
+  // chunks in order; sixteen loads in flight at a time, added in order
   float v = 0.f;
-  for (int b = 0; b < nch; ++b) v += a.colpart[((size_t)q * nch + b) * a.E + e];
+  int b = 0;
+  for (; b + 16 <= nch; b += 16) {
+    float p[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) p[u] = a.colpart[((size_t)q * nch + b + u) * a.E + e];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v += p[u];
+  }
+  for (; b < nch; ++b) v += a.colpart[((size_t)q * nch + b) * a.E + e];
   (q ? a.dlam : a.db_r)[e] = v;
 }
 
@@ -368,7 +377,11 @@ struct WArgs {
   int Tcap;
 };
 
-constexpr int WG_KS = 32;   // rows per step
+#ifndef DECO_WG_KS
+#define DECO_WG_KS 32
+#endif
+constexpr int WG_KS = DECO_WG_KS;   // rows per step (32 or 64)
+constexpr int WG_OCC = WG_KS == 32 ? 3 : 2;   // workgroups per CU (registers, LDS)
 
 template <class DT>
 struct WShape {
@@ -388,7 +401,7 @@ __device__ __forceinline__ void wgrad_tile(const WArgs& a, int bid, char* lds_ra
   constexpr int PITCH = WS::PITCH, PLANE = WS::PLANE;
   constexpr int EPC = 16 / ES;                // elements per 16-byte chunk
   constexpr int CPR = 128 / EPC;              // chunks per 128-column row segment
-  constexpr int TPL = 2;                      // rows per lane task
+  constexpr int TPL = KS / 16;                // rows per lane task (one LDS store per column)
   constexpr int NKP = KS / TPL;               // row pairs per step
   constexpr int NLD = NKP * CPR / 256;        // lane tasks per plane and step
   static_assert((NKP * CPR) % 256 == 0 && KS % KB == 0, "step shape");
@@ -434,6 +447,7 @@ __device__ __forceinline__ void wgrad_tile(const WArgs& a, int bid, char* lds_ra
     i32x4_t va[NA][NLD][TPL];
     i32x4_t vb[NB][NLD][TPL];
   };
+  static_assert(TPL == 2 || TPL == 4, "rows per lane task");
   Regs R0, R1;
   struct Idx {
     int ia[TPL], ib[TPL];
@@ -464,15 +478,19 @@ __device__ __forceinline__ void wgrad_tile(const WArgs& a, int bid, char* lds_ra
       }
     }
   };
-  // column col of a plane gets the two rows' values at k = 2 kp, 2 kp + 1 in one store
-  auto put = [&](elem* plane, int col, const i32x4_t& r0, const i32x4_t& r1, int j) {
-    const elem* e0 = reinterpret_cast<const elem*>(&r0);
-    const elem* e1 = reinterpret_cast<const elem*>(&r1);
+  // column col of a plane gets the TPL rows' values at k = TPL kp .. in one store
+  auto put = [&](elem* plane, int col, const i32x4_t (&r)[TPL], int j) {
     elem* dst = plane + col * PITCH + TPL * kp;
-    if constexpr (ES == 2) {
-      *reinterpret_cast<uint32_t*>(dst) = (uint32_t)e0[j] | ((uint32_t)e1[j] << 16);
+    auto el = [&](int t) { return reinterpret_cast<const elem*>(&r[t])[j]; };
+    if constexpr (ES == 2 && TPL == 2) {
+      *reinterpret_cast<uint32_t*>(dst) = (uint32_t)el(0) | ((uint32_t)el(1) << 16);
+    } else if constexpr (ES == 2) {
+      *reinterpret_cast<uint2*>(dst) = make_uint2((uint32_t)el(0) | ((uint32_t)el(1) << 16),
+                                                  (uint32_t)el(2) | ((uint32_t)el(3) << 16));
+    } else if constexpr (TPL == 2) {
+      *reinterpret_cast<float2*>(dst) = make_float2(el(0), el(1));
     } else {
-      *reinterpret_cast<float2*>(dst) = make_float2(e0[j], e1[j]);
+      *reinterpret_cast<float4*>(dst) = make_float4(el(0), el(1), el(2), el(3));
     }
   };
   auto stage = [&](Regs& R, int s) {
@@ -493,9 +511,9 @@ __device__ __forceinline__ void wgrad_tile(const WArgs& a, int bid, char* lds_ra
 #pragma unroll
       for (int j = 0; j < EPC; ++j) {
 #pragma unroll
-        for (int h = 0; h < NA; ++h) put(sA + h * PLANE, ch * EPC + j, R.va[h][u][0], R.va[h][u][1], j);
+        for (int h = 0; h < NA; ++h) put(sA + h * PLANE, ch * EPC + j, R.va[h][u], j);
 #pragma unroll
-        for (int h = 0; h < NB; ++h) put(sB + h * PLANE, ch * EPC + j, R.vb[h][u][0], R.vb[h][u][1], j);
+        for (int h = 0; h < NB; ++h) put(sB + h * PLANE, ch * EPC + j, R.vb[h][u], j);
       }
     }
   };
@@ -605,7 +623,7 @@ __device__ __forceinline__ void wgrad_tile(const WArgs& a, int bid, char* lds_ra
 }
 
 template <class DT, bool SA, bool SB>
-__global__ void __launch_bounds__(256, 3) k_bwd_wgrad(WArgs a) {
+__global__ void __launch_bounds__(256, WG_OCC) k_bwd_wgrad(WArgs a) {
   __shared__ __attribute__((aligned(16))) char lds_raw[WShape<DT>::LDS_BYTES];
   wgrad_tile<DT, SA, SB>(a, blockIdx.x, lds_raw);
 }
