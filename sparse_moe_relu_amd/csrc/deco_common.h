@@ -150,35 +150,8 @@ __host__ __device__ __forceinline__ size_t frag_elem_off(int row, int k) {
          (size_t)DT::frag_j(w) * sizeof(typename DT::elem);
 }
 
-// Cross-workgroup hand-off inside one kernel.  Data another workgroup will
-// read is stored with device-scope stores (write-through to the level shared
-// by all XCDs, `sc1`) and read with device-scope loads; the writer waits for
-// its stores to complete before it bumps an arrival counter.  This avoids the
-// agent-scope fences, which write back and invalidate the whole L2 of the
-// XCD and cost microseconds each.
-__device__ __forceinline__ void st_dev(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_dev(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Device-scope (`sc1`) loads through a buffer resource: unlike atomic loads,
-// the compiler issues many of them back to back before it waits.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t dev_rsrc(const void* base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7FFFFFFF, 0x00020000);
-}
-__device__ __forceinline__ float ld_dev_buf(__amdgpu_buffer_rsrc_t r, unsigned byte_off) {
-  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)byte_off, 0, 16));
-}
-__device__ __forceinline__ void st_dev_u32(unsigned* p, unsigned v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 // every memory operation this thread issued has completed
 __device__ __forceinline__ void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0); }
-// returns the counter's previous value
-__device__ __forceinline__ unsigned arrive(unsigned* counter) {
-  return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // TopK selection over one token's logits, by a wave: lane l holds
 // z[j] = logit of expert 64 j + l (-inf past the last expert).  Logits map to
