@@ -207,12 +207,17 @@ class Layer:
 
     def forward(self, x: torch.Tensor, out: torch.Tensor | None = None, *, path: int = DECO_PATH_AUTO,
                 stream=None) -> torch.Tensor:
-        T = x.shape[0]
         if x.dim() != 2 or x.shape[1] != self.d or x.dtype != _TORCH_DT[self.dtype] or not x.is_cuda \
                 or not x.is_contiguous():
             raise ValueError(f"x: expected contiguous device [T,{self.d}] {_TORCH_DT[self.dtype]}")
+        T = x.shape[0]
         if out is None:
             out = torch.empty_like(x)
+        elif (tuple(out.shape) != tuple(x.shape) or out.dtype != x.dtype or out.device != x.device
+              or not out.is_contiguous()):
+            # the library writes T*d elements at out's address: a smaller or
+            # differently typed buffer would be overrun
+            raise ValueError(f"out: expected contiguous {tuple(x.shape)} {x.dtype} on {x.device}")
         st = load_library().deco_moe_forward_path(self.handle, x.data_ptr(), T, out.data_ptr(),
                                                   _stream_handle(stream), int(path))
         if st != DECO_OK:
@@ -225,6 +230,8 @@ class Layer:
         """Gradients of sum(dout * layer(x)) + reg_coef * mean router entropy
         (deco_moe_backward): float32 device tensors dx, dW_r, db_r, dlambda,
         dW_up, dW_down, dWs_up, dWs_down, and n_active_pairs (int32 [1])."""
+        if x.dim() != 2:
+            raise ValueError(f"x: expected contiguous device [T,{self.d}] {_TORCH_DT[self.dtype]}")
         T = x.shape[0]
         for name, t in (("x", x), ("dout", dout)):
             if t.dim() != 2 or tuple(t.shape) != (T, self.d) or t.dtype != _TORCH_DT[self.dtype] or not t.is_cuda \

@@ -271,6 +271,25 @@ def test_invalid_T_rejected_and_out_untouched(c2):
     assert bool((out == 5.0).all())
 
 
+def test_binding_rejects_a_mismatched_out_buffer(c2):
+    # the library writes T*d elements at out's address, so the binding checks
+    # out before any launch: too few rows, another dtype, a strided view
+    L, ref, layer = c2
+    x = x_tensor(L)[:8].contiguous()
+    good = torch.full_like(x, 5.0)
+    bad = [torch.empty((4, L.d), dtype=x.dtype, device="cuda"),
+           torch.empty((8, L.d), dtype=torch.float32, device="cuda"),
+           torch.empty((8, 2 * L.d), dtype=x.dtype, device="cuda")[:, :L.d]]
+    for out in bad:
+        with pytest.raises(ValueError):
+            layer(x, out)
+    torch.cuda.synchronize()
+    assert bool((good == 5.0).all())
+    got = layer(x, good)
+    assert got.data_ptr() == good.data_ptr()
+    assert torch.equal(got, layer(x))
+
+
 def test_max_tokens_boundary():
     L = make_custom(128, 9, 64, 64, 40, "bf16", seed=21)
     ref = oracle.forward(L.x, **L.weights(), eps=L.eps)
