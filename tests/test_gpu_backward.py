@@ -103,6 +103,15 @@ def test_backward_bf16_several_tiles_ragged():
     layer.free()
 
 
+def test_backward_c3_full_size():
+    # the size and launch shapes the bench times (T = 4096, d = 2048, 56 experts);
+    # seed 5: no logit of the 4096 x 56 within 1e-5 of zero (seeds 1-4 have one)
+    L = make_layer(3, seed=5)
+    layer = _layer(L, L.T)
+    check(L, layer, label="c3-4096", seed=2)
+    layer.free()
+
+
 def test_backward_bf16_entropy_term():
     L = make_layer(2, T=200, ratio=0.3)
     layer = _layer(L, 200)
