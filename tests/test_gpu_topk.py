@@ -111,6 +111,15 @@ def test_topk_prefill_several_tiles_ragged():
     layer.free()
 
 
+def test_topk_prefill_full_size():
+    # the size the sweep measures the TopK baseline at (T = 4096, k = 11 of 56)
+    L = make_layer(3)
+    k = 11
+    layer = _layer(L, L.T, k)
+    run_topk(L, k, layer, dm.DECO_PATH_PREFILL, label="c3-4096")
+    layer.free()
+
+
 def test_topk_wide_expert_set_decode():
     # E = 200: four words of mask, router panels past 64 experts
     L = make_custom(256, 200, 32, 64, 12, "bf16", seed=41)
