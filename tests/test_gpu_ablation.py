@@ -82,6 +82,15 @@ def test_ablation_bf16_decode_and_prefill(name):
     layer.free()
 
 
+@pytest.mark.parametrize("name", ["vanilla", "shared_rms"])
+def test_ablation_prefill_full_size(name):
+    # the size the sweep measures the ablations at (c3, T = 4096)
+    L = make_layer(3)
+    layer = dm.Layer(**layer_tensors(L), max_tokens=L.T, eps=L.eps, **FLAGS[name])
+    check(L, layer, PRE, FLAGS[name], label=f"c3-4096-{name}")
+    layer.free()
+
+
 def test_ablation_shapes_and_topk():
     # E not a multiple of 16, Fs not a multiple of 64, TopK routing with the switches
     L = make_custom(192, 70, 64, 96, 77, "bf16", seed=9, ratio=0.3)
