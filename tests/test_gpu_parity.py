@@ -193,6 +193,8 @@ def test_c5_ratio_sweep(ratio):
     (256, 12, 256, 32, "bf16"),   # widest F, narrowest Fs
     (128, 3, 256, 160, "f32"),
     (64, 1, 32, 32, "bf16"),      # E = 1: routed part vanishes
+    (128, 256, 256, 64, "bf16"),  # decode: routed units past one chunk per wave (the reload loop), 4 mask words
+    (4096, 4, 32, 4096, "bf16"),  # decode: 16 shared k-blocks per down workgroup (more than one per wave)
 ])
 @pytest.mark.parametrize("path", ["decode", "prefill"])
 def test_shapes(shape, path):
