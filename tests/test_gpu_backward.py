@@ -112,6 +112,15 @@ def test_backward_c3_full_size():
     layer.free()
 
 
+def test_backward_two_way_split_of_the_dense_weight_gradients():
+    # 1024 <= T < 2048: the dense weight-gradient jobs split their K = T rows in
+    # two ranges (one below, four from 2048); seed 2 keeps every logit off zero
+    L = make_layer(3, seed=2, T=1500)
+    layer = _layer(L, L.T)
+    check(L, layer, label="c3-1500", seed=3)
+    layer.free()
+
+
 def test_backward_bf16_entropy_term():
     L = make_layer(2, T=200, ratio=0.3)
     layer = _layer(L, 200)
