@@ -131,14 +131,19 @@ __device__ __forceinline__ void put_split(typename DT::elem* hi, typename DT::el
 // m += x . Wbar_lo (bf16 layers): the recomputed mean term then carries
 // Wbar to about 16 significant bits.  A bf16 Wbar alone costs dW_up over 2 %
 // of its RMS when few tokens average the error (T = 1).
+// the x . (Wbar - bf16(Wbar)) pass has only F columns: 32-row by 64-column
+// tiles with a four-stage ring, so T = 4096 still spreads over 256 workgroups
+template <class DT>
+using MeanLoTile = Tile<DT, 32, 4, 4>;
+
 template <class DT>
 __global__ void __launch_bounds__(256) k_bwd_mean_lo(BwdArgs a) {
   using elem = typename DT::elem;
-  using TD = DenseTile<DT>;
+  using TD = MeanLoTile<DT>;
   __shared__ i32x4_t lds[TD::LDS_V];
   const int tid = threadIdx.x, w = tid >> 6, wm = w >> 1, wn = w & 1, l = tid & 63, g = l >> 4, c = l & 15;
-  const int nct = (a.pF + GP - 1) / GP;
-  const int m0 = (blockIdx.x / nct) * GM, p0 = (blockIdx.x % nct) * GP;
+  const int nct = (a.pF + TD::BNP - 1) / TD::BNP;
+  const int m0 = (blockIdx.x / nct) * TD::BM, p0 = (blockIdx.x % nct) * TD::BNP;
   const elem* x = (const elem*)a.x;
   auto row = [&](int r) -> const elem* {
     const int rr = m0 + r;
@@ -155,7 +160,7 @@ __global__ void __launch_bounds__(256) k_bwd_mean_lo(BwdArgs a) {
   tile_gemm<DT, TD, true>(lds, row, panel, a.nkb_d, acc);
 #pragma unroll
   for (int i = 0; i < TD::MB; ++i) {
-    const int r = m0 + wm * (GM / 2) + 16 * i + c;
+    const int r = m0 + wm * (TD::BM / 2) + 16 * i + c;
     if (r >= a.T) continue;
 #pragma unroll
     for (int j = 0; j < TD::NBW; ++j) {
@@ -735,7 +740,10 @@ hipError_t backward(const deco_moe_layer* L, const void* x, const void* dout, in
   const unsigned mtiles = (unsigned)((T + GM - 1) / GM);
   hipError_t err = launch_routing<DT>(L, a, T, s);
   if (err == hipSuccess && L->WbarLo_p)
-    err = launch(deco_host::KS_BWD_SHARED, k_bwd_mean_lo<DT>, dim3(mtiles * ((L->pF + GP - 1) / GP)), dim3(256), s, b);
+    err = launch(deco_host::KS_BWD_SHARED, k_bwd_mean_lo<DT>,
+                 dim3((unsigned)((T + MeanLoTile<DT>::BM - 1) / MeanLoTile<DT>::BM) *
+                      ((L->pF + MeanLoTile<DT>::BNP - 1) / MeanLoTile<DT>::BNP)),
+                 dim3(256), s, b);
   if (err == hipSuccess)
     err = launch(deco_host::KS_BWD_SHARED, k_bwd_shared<DT>, dim3(mtiles * ((L->pFs + GP - 1) / GP)), dim3(256), s, b);
   if (err == hipSuccess)
