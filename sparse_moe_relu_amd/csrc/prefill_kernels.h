@@ -161,16 +161,17 @@ __device__ __forceinline__ void store4_pair(PT* p, const f32x4_t& v) {
 
 // --------------------------------------------------------------------------
 // NS pipeline stages in LDS: 2 (64 KiB, two workgroups per CU) when the grid
-// exceeds the CUs, 4 (128 KiB, one per CU, three steps of loads in flight)
-// when it does not, which is the case below a few thousand tokens.
-template <class DT, int NS>
+// exceeds the CUs, 4 (one per CU, three steps of loads in flight) when it
+// does not, which is the case below a few thousand tokens; BMR rows per tile:
+// 128, or 64 when even the four-stage grid of 128-row tiles leaves CUs idle.
+template <class DT, int NS, int BMR = GM>
 __global__ void __launch_bounds__(256, 2) k_pre_router_shared(PreArgs a) {
   using elem = typename DT::elem;
-  using TC = Tile<DT, GM, GP, NS>;
+  using TC = Tile<DT, BMR, GP, NS>;
   __shared__ i32x4_t lds[TC::LDS_V];
   const int tid = threadIdx.x, w = tid >> 6, wm = w >> 1, wn = w & 1, l = tid & 63, g = l >> 4, c = l & 15;
   const int t = xcd_tile(blockIdx.x, gridDim.x);
-  const int m0 = (t / a.rs_nt) * GM, p0 = (t % a.rs_nt) * GP;
+  const int m0 = (t / a.rs_nt) * BMR, p0 = (t % a.rs_nt) * GP;
   const elem* x = (const elem*)a.x;
   // rows past T and padding panels read valid memory; those outputs are dropped
   auto row = [&](int r) -> const elem* {
@@ -206,7 +207,7 @@ __global__ void __launch_bounds__(256, 2) k_pre_router_shared(PreArgs a) {
       }
 #pragma unroll
     for (int i = 0; i < TC::MB; ++i) {
-      const int r = m0 + wm * (GM / 2) + 16 * i + c;
+      const int r = m0 + wm * (BMR / 2) + 16 * i + c;
       uint64_t bits = 0;
 #pragma unroll
       for (int j = 0; j < TC::NBW; ++j)
@@ -233,7 +234,7 @@ __global__ void __launch_bounds__(256, 2) k_pre_router_shared(PreArgs a) {
         const int f0 = (q + j) * 16 + 4 * g;
 #pragma unroll
         for (int i = 0; i < TC::MB; ++i) {
-          const int r = m0 + wm * (GM / 2) + 16 * i + c;
+          const int r = m0 + wm * (BMR / 2) + 16 * i + c;
           if (r < a.T)
             *reinterpret_cast<float4*>(a.mbuf + (size_t)r * a.F + f0) =
                 make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
@@ -249,7 +250,7 @@ __global__ void __launch_bounds__(256, 2) k_pre_router_shared(PreArgs a) {
         const int c0 = (q + j) * 16 + 4 * g;
 #pragma unroll
         for (int i = 0; i < TC::MB; ++i) {
-          const int r = m0 + wm * (GM / 2) + 16 * i + c;
+          const int r = m0 + wm * (BMR / 2) + 16 * i + c;
           if (r < a.T) {
             if (a.sraw)   // RMS-only NormSiLU: the row's RMS spans other workgroups' columns
               *reinterpret_cast<float4*>(a.sraw + (size_t)r * a.Fs + c0) =
@@ -926,9 +927,13 @@ hipError_t launch_routing(const deco_moe_layer* L, const PreArgs& a, int T, hipS
   using deco_host::launch;
   const unsigned mtiles = (unsigned)((T + GM - 1) / GM);
   const unsigned rs_grid = mtiles * a.rs_nt;
-  hipError_t err = rs_grid <= (unsigned)L->n_cu
-      ? launch(deco_host::KS_PRE_ROUTER_SHARED, k_pre_router_shared<DT, 4>, dim3(rs_grid), dim3(256), s, a)
-      : launch(deco_host::KS_PRE_ROUTER_SHARED, k_pre_router_shared<DT, DECO_PRE_NS>, dim3(rs_grid), dim3(256), s, a);
+  const unsigned half_grid = (unsigned)((T + GM / 2 - 1) / (GM / 2)) * a.rs_nt;
+  hipError_t err =
+      2 * rs_grid <= (unsigned)L->n_cu
+          ? launch(deco_host::KS_PRE_ROUTER_SHARED, k_pre_router_shared<DT, 4, GM / 2>, dim3(half_grid), dim3(256), s, a)
+      : rs_grid <= (unsigned)L->n_cu
+          ? launch(deco_host::KS_PRE_ROUTER_SHARED, k_pre_router_shared<DT, 4>, dim3(rs_grid), dim3(256), s, a)
+          : launch(deco_host::KS_PRE_ROUTER_SHARED, k_pre_router_shared<DT, DECO_PRE_NS>, dim3(rs_grid), dim3(256), s, a);
   if (err == hipSuccess && a.top_k > 0)
     err = launch(deco_host::KS_PRE_TOPK, k_pre_topk, dim3((unsigned)((T + 3) / 4)), dim3(256), s, a);
   if (err == hipSuccess && a.sraw)
