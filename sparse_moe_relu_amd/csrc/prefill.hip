@@ -33,15 +33,28 @@
 
 namespace {
 
-template <class DT, int MODE>
+template <class DT, int MODE, bool SMALL>
 void (*expert_kernel_m(int pF))(PreArgs) {
-  return pF == 2 ? k_pre_expert<DT, 2, MODE>
-       : pF == 4 ? k_pre_expert<DT, 4, MODE>
-       : pF == 8 ? k_pre_expert<DT, 8, MODE> : k_pre_expert<DT, 16, MODE>;
+  return pF == 2 ? k_pre_expert<DT, 2, MODE, SMALL>
+       : pF == 4 ? k_pre_expert<DT, 4, MODE, SMALL>
+       : pF == 8 ? k_pre_expert<DT, 8, MODE, SMALL> : k_pre_expert<DT, 16, MODE, SMALL>;
 }
 template <class DT>
-void (*expert_kernel(int pF, bool gated))(PreArgs) {
-  return gated ? expert_kernel_m<DT, XM_GATED>(pF) : expert_kernel_m<DT, XM_FWD>(pF);
+void (*expert_kernel(int pF, bool gated, bool small = false))(PreArgs) {
+  if (gated) return expert_kernel_m<DT, XM_GATED, false>(pF);   // 64-row tiles already
+  return small ? expert_kernel_m<DT, XM_FWD, true>(pF) : expert_kernel_m<DT, XM_FWD, false>(pF);
+}
+
+// 64-row expert tiles when the batch would not fill half the persistent grid
+// with 128-row tiles.  The count is estimated before routing (no host wait):
+// the shared expert's 128 x 128 tiles plus, per expert, the 128-row tiles of
+// a quarter of the tokens (the method's typical activation is about 20 %).
+// Measured (same box): 64-row tiles win up to T = 1024 on the d = 2048 layer
+// and at T = 256 on the d = 4096 one, and lose from T = 2048 on.
+bool small_expert_tiles(const deco_moe_layer* L, int T) {
+  const long long shared_tiles = (long long)((T + GM - 1) / GM) * ((L->pD + GP - 1) / GP);
+  const long long expert_tiles = (long long)L->E * ((T / 4 + GM - 1) / GM);
+  return 2 * (shared_tiles + expert_tiles) < (long long)L->pre_grid;
 }
 
 template <class DT>
@@ -50,7 +63,8 @@ hipError_t prefill(const deco_moe_layer* L, const void* x, int T, void* out, hip
   using deco_host::launch;
   hipError_t err = launch_routing<DT>(L, a, T, s);
   if (err == hipSuccess)
-    err = launch(deco_host::KS_PRE_EXPERT, expert_kernel<DT>(L->pF, L->gated), dim3(L->pre_grid), dim3(256), s, a);
+    err = launch(deco_host::KS_PRE_EXPERT, expert_kernel<DT>(L->pF, L->gated, small_expert_tiles(L, T)),
+                 dim3(L->pre_grid), dim3(256), s, a);
   if (err == hipSuccess)
     err = launch(deco_host::KS_PRE_COMBINE, k_pre_combine<DT>,
                  dim3((unsigned)(((long long)T * (L->d / 8) + 255) / 256)), dim3(256), s, a);

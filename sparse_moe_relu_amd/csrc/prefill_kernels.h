@@ -385,12 +385,13 @@ __global__ void __launch_bounds__(DISP_NT) k_pre_dispatch(PreArgs a) {
 }
 
 // --------------------------------------------------------------------------
-template <class DT, int BNP, int MODE>
+template <class DT, int BNP, int MODE, bool SMALL = false>
 struct ExpertShape {
   using DN = typename DT::Down;                      // down-projection operand type
   // token rows per tile (gated experts and the backward hold a second
-  // K = d accumulator, so their tiles have half the rows)
-  static constexpr int BM = (BNP >= 16 || MODE != XM_FWD) ? 64 : 128;
+  // K = d accumulator, so their tiles have half the rows; SMALL: batches too
+  // small to fill the persistent grid with 128-row tiles use 64)
+  static constexpr int BM = (BNP >= 16 || MODE != XM_FWD || SMALL) ? 64 : 128;
   using TC = Tile<DT, BM, BNP, DECO_PRE_NS>;          // up-projection ring
   static constexpr int F = BNP * 16;
   static constexpr int NKF = F / DN::KB;             // k-blocks of the down-projection
@@ -442,10 +443,10 @@ struct ExpertShape {
 // dg goes to dgbuf, dh~ and g*a to the pair-slot rows of dhbuf and agbuf
 // (operands of the weight gradients), the slot to slot_list, and
 // dh~ . W_up[e]^T (this pair's part of dLoss/dx) to the pair buffer.
-template <class DT, int BNP, int MODE>
-__global__ void __launch_bounds__(256, (ExpertShape<DT, BNP, MODE>::OCC)) k_pre_expert(PreArgs a) {
+template <class DT, int BNP, int MODE, bool SMALL = false>
+__global__ void __launch_bounds__(256, (ExpertShape<DT, BNP, MODE, SMALL>::OCC)) k_pre_expert(PreArgs a) {
   using elem = typename DT::elem;
-  using S = ExpertShape<DT, BNP, MODE>;
+  using S = ExpertShape<DT, BNP, MODE, SMALL>;
   using TC = typename S::TC;
   using DN = typename S::DN;
   using PT = typename DT::pair;
