@@ -398,53 +398,13 @@ __global__ void __launch_bounds__(NW * 64) k_dec_down(DecArgs a) {
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, c = l & 15, g = l >> 4;
   const int grp = blockIdx.x % a.n_groups, q = blockIdx.x / a.n_groups;
 
-  // This workgroup's units (k-blocks of the reduction): its share of the
-  // shared expert's, [sl, sh), known at launch, then its share of the routed
-  // experts', [rl, rh), which needs the list of experts the batch activated.
-  // Wave w < ns takes shared unit sl + w into registers of its own, loaded
-  // before the routing flags are used.  The remaining units, local index
-  // k < ns2 = shared unit sl + NW + k, else routed unit rl + k - ns2, go to
-  // wave w as local units w + NW ub of each chunk.
-  const int S = a.nkb_Fs;
-  const int sl = (int)(((long long)q * S) / a.Q), sh = (int)(((long long)(q + 1) * S) / a.Q);
-  const int ns = sh - sl;
-  const int ns2 = ns > NW ? ns - NW : 0;
-  // the routing flags are read first: waits complete in issue order, so the
-  // list below then does not wait for the shared unit's weights
+  // ascending list of the experts that at least one token activated
   const int nwE = (a.E + 63) >> 6;
   const int e_ = w * 64 + l;
-  const unsigned flag = a.rflag[e_ < a.E ? e_ : a.E - 1];   // no branch: masked where used
-
-  const __amdgpu_buffer_rsrc_t rsd = buf_rsrc(a.Wsd_p), rh = buf_rsrc(a.hbuf), rs = buf_rsrc(a.sactf);
-  const __amdgpu_buffer_rsrc_t ru = buf_rsrc(GATED ? a.ubuf : a.hbuf);
-  // weights of shared unit kb (any = false: reads nothing, zeros)
-  auto load_b_shared = [&](i32x4_t (&b)[DP], int kb, bool any) {
-#pragma unroll
-    for (int p = 0; p < DP; ++p) {
-      int pan = grp * DP + p;
-      pan = pan < a.pD ? pan : a.pD - 1;
-      b[p] = ld16_buf(rsd, any ? 16u * l : OOB, (unsigned)frag_off(pan, kb, a.nkb_Fs));
-    }
-  };
-  // the stored shared activation fragment of unit kb
-  auto load_a_shared = [&](float (&h)[EPL], int kb, bool any) {
-    const i32x4_t r = ld16_buf(rs, any ? (unsigned)(kb * FRAG_BYTES) + 16u * l : OOB, 0u);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) h[j] = __int_as_float(r[j]);
-#pragma unroll
-    for (int j = 4; j < EPL; ++j) h[j] = 0.f;
-  };
-  i32x4_t bsh[DP];
-  float hsh[EPL];
-  load_b_shared(bsh, w < ns ? sl + w : sl, w < ns);
-  load_a_shared(hsh, w < ns ? sl + w : sl, w < ns);
-
-  // ascending list of the experts that at least one token activated (LDS-only
-  // barriers: the shared unit's loads stay in flight)
-  const bool act = w < nwE && e_ < a.E && flag == 2u;
+  const bool act = (w < nwE) && (e_ < a.E) && (a.rflag[e_] == 2u);
   const unsigned long long bal = __ballot(act);
   if (w < nwE && l == 0) s_wcnt[w] = __popcll(bal);
-  lds_barrier();
+  __syncthreads();
   if (act) {
     int base = 0;
     for (int ww = 0; ww < w; ++ww) base += s_wcnt[ww];
@@ -455,61 +415,88 @@ __global__ void __launch_bounds__(NW * 64) k_dec_down(DecArgs a) {
     for (int ww = 0; ww < nwE; ++ww) n += s_wcnt[ww];
     s_nu = n;
   }
-  lds_barrier();
+  __syncthreads();
   const int nu = s_nu;
-  const int R = nu * a.nkb_F;
-  const int rl = (int)(((long long)q * R) / a.Q), rhi = (int)(((long long)(q + 1) * R) / a.Q);
-  const int nk = ns2 + (rhi - rl);   // remaining local units of this workgroup
-  // routed experts with units in [rl, rhi): list entries i0 .. i0 + nx - 1
-  const int i0 = rl < rhi ? rl / a.nkb_F : 0;
-  const int nx = rl < rhi ? (rhi - 1) / a.nkb_F - i0 + 1 : 0;
+  const int n_routed_units = nu * a.nkb_F;
+  const int C = n_routed_units + a.nkb_Fs;
+  const int lo = (int)(((long long)q * C) / a.Q), hi = (int)(((long long)(q + 1) * C) / a.Q);
+  // routed experts with units in [lo, hi): list entries i0 .. i0 + nx - 1
+  const int rhi = hi < n_routed_units ? hi : n_routed_units;
+  const int i0 = lo < rhi ? lo / a.nkb_F : 0;
+  const int nx = lo < rhi ? (rhi - 1) / a.nkb_F - i0 + 1 : 0;
 
-  // Operands of the local units of chunk k0.  For a routed unit (expert e,
-  // k-block kb) lane (c, g) takes h - m of token row c at the EPL columns its
-  // fragment holds (rows past T read nothing: the buffer range check returns
-  // zeros), and for gated experts x . W_up[e] at the same place.  Panels past
-  // the last output column (d not a multiple of NCOL) read the last panel
-  // again and their results are dropped.
+  // weights of one chunk of this wave's units (k-blocks), straight to
+  // registers.  Panels past the last output column (d not a multiple of
+  // NCOL) read the last panel again and their results are dropped.
   i32x4_t bfr[UB][DP];
-  float hv[UB][EPL];
-  float uv[UB][GATED ? EPL : 1];
-  auto load_chunk = [&](int k0) {
+  auto load_b = [&](int u0) {
 #pragma unroll
     for (int ub = 0; ub < UB; ++ub) {
-      const int k = k0 + w + ub * NW;   // wave-uniform
-      if (k < ns2) {
-        load_b_shared(bfr[ub], sl + NW + k, true);
-        load_a_shared(hv[ub], sl + NW + k, true);
-      } else if (k < nk) {
-        const int u = rl + k - ns2;
-        const int e = __builtin_amdgcn_readfirstlane(s_ulist[u / a.nkb_F]);
-        const int kb = u % a.nkb_F;
-        const __amdgpu_buffer_rsrc_t rb = buf_rsrc(a.Wdn_p + (size_t)e * a.dn_stride);
+      const int u = u0 + ub * NW;   // wave-uniform
+      const char* B;
+      int kb, nkb;
+      if (u < rhi) {
+        kb = u % a.nkb_F;
+        nkb = a.nkb_F;
+        B = a.Wdn_p + (size_t)__builtin_amdgcn_readfirstlane(s_ulist[u / a.nkb_F]) * a.dn_stride;
+      } else {
+        kb = u < hi ? u - n_routed_units : 0;
+        nkb = a.nkb_Fs;
+        B = a.Wsd_p;
+      }
+      const __amdgpu_buffer_rsrc_t rb = buf_rsrc(B);
 #pragma unroll
-        for (int p = 0; p < DP; ++p) {
-          int pan = grp * DP + p;
-          pan = pan < a.pD ? pan : a.pD - 1;
-          bfr[ub][p] = ld16_buf(rb, 16u * l, (unsigned)frag_off(pan, kb, a.nkb_F));
-        }
-        i32x4_t r[EPL / 4], r2[EPL / 4];
-        const unsigned off = c < a.T ? 4u * (unsigned)((e * 16 + c) * a.F + kb * DT::KB + EPL * g) : OOB;
-#pragma unroll
-        for (int kk = 0; kk < EPL / 4; ++kk) r[kk] = ld16_buf(rh, off + 16u * kk, 0u);
-        if constexpr (GATED) {
-#pragma unroll
-          for (int kk = 0; kk < EPL / 4; ++kk) r2[kk] = ld16_buf(ru, off + 16u * kk, 0u);
-        }
-#pragma unroll
-        for (int kk = 0; kk < EPL / 4; ++kk)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            hv[ub][4 * kk + j] = __int_as_float(r[kk][j]);
-            if constexpr (GATED) uv[ub][4 * kk + j] = __int_as_float(r2[kk][j]);
-          }
+      for (int p = 0; p < DP; ++p) {
+        int pan = grp * DP + p;
+        pan = pan < a.pD ? pan : a.pD - 1;
+        bfr[ub][p] = u < hi ? ld16_buf(rb, 16u * l, (unsigned)frag_off(pan, kb, nkb)) : zero16();
       }
     }
   };
-  load_chunk(0);
+  // raw activation operands of a chunk: for a routed unit (expert e, k-block
+  // kb) lane (c, g) takes h - m of token row c at the EPL columns its
+  // fragment holds (rows past T read nothing: the buffer range check returns
+  // zeros), and for gated experts x . W_up[e] at the same place; for a
+  // shared unit, the stored fragment
+  const __amdgpu_buffer_rsrc_t rh = buf_rsrc(a.hbuf), rs = buf_rsrc(a.sactf);
+  const __amdgpu_buffer_rsrc_t ru = buf_rsrc(GATED ? a.ubuf : a.hbuf);
+  float hv[UB][EPL];
+  float uv[UB][GATED ? EPL : 1];
+  auto load_a = [&](int u0) {
+#pragma unroll
+    for (int ub = 0; ub < UB; ++ub) {
+      const int u = u0 + ub * NW;
+      i32x4_t r[EPL / 4], r2[EPL / 4];
+      if (u < rhi) {
+        const int e = s_ulist[u / a.nkb_F], kb = u % a.nkb_F;
+        const unsigned off = c < a.T ? 4u * (unsigned)((e * 16 + c) * a.F + kb * DT::KB + EPL * g) : OOB;
+#pragma unroll
+        for (int k = 0; k < EPL / 4; ++k) r[k] = ld16_buf(rh, off + 16u * k, 0u);
+        if constexpr (GATED) {
+#pragma unroll
+          for (int k = 0; k < EPL / 4; ++k) r2[k] = ld16_buf(ru, off + 16u * k, 0u);
+        }
+      } else {   // a shared unit, or past the range (reads nothing)
+        const unsigned off = u < hi ? (unsigned)((u - n_routed_units) * FRAG_BYTES) + 16u * l : OOB;
+        r[0] = ld16_buf(rs, off, 0u);
+#pragma unroll
+        for (int k = 1; k < EPL / 4; ++k) r[k] = zero16();
+        if constexpr (GATED) {
+#pragma unroll
+          for (int k = 0; k < EPL / 4; ++k) r2[k] = zero16();
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < EPL / 4; ++k)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          hv[ub][4 * k + j] = __int_as_float(r[k][j]);
+          if constexpr (GATED) uv[ub][4 * k + j] = __int_as_float(r2[k][j]);
+        }
+    }
+  };
+  load_b(lo + w);
+  load_a(lo + w);
   // 1 / RMS (NormSiLU) and gate of each (expert in range, token row)
   {
     const __amdgpu_buffer_rsrc_t rsp = buf_rsrc(a.sspart), rg = buf_rsrc(a.g);
@@ -537,43 +524,41 @@ __global__ void __launch_bounds__(NW * 64) k_dec_down(DecArgs a) {
   f32x4_t acc[DP];
 #pragma unroll
   for (int p = 0; p < DP; ++p) acc[p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  auto mma_shared = [&](const i32x4_t (&b)[DP], const float (&h)[EPL]) {
-    i32x4_t af;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) af[j] = __float_as_int(h[j]);
-#pragma unroll
-    for (int p = 0; p < DP; ++p) DT::mma(acc[p], af, b[p]);
-  };
-  if (w < ns) mma_shared(bsh, hsh);
-  auto compute = [&](int k0) {
+  auto compute = [&](int u0) {
 #pragma unroll
     for (int ub = 0; ub < UB; ++ub) {
-      const int k = k0 + w + ub * NW;
+      const int u = u0 + ub * NW;
       __builtin_amdgcn_sched_barrier(0);   // one unit's temporaries at a time
-      if (k < ns2) {
-        mma_shared(bfr[ub], hv[ub]);
-      } else if (k < nk) {
-        // NormSiLU times the router gate (and, for gated experts, times
-        // x . W_up[e]), rounded once to the down-projection operand type
-        const int u = rl + k - ns2;
-        const int kk = (u / a.nkb_F - i0) * 16 + c;
-        const float rinv = s_rinv[kk], gt = s_gate[kk];
+      if (u < hi) {
+        if (u < n_routed_units) {
+          // NormSiLU times the router gate (and, for gated experts, times
+          // x . W_up[e]), rounded once to the down-projection operand type
+          const int k = (u / a.nkb_F - i0) * 16 + c;
+          const float rinv = s_rinv[k], gt = s_gate[k];
 #pragma unroll
-        for (int j = 0; j < EPL; ++j) {
-          if constexpr (GATED) hv[ub][j] = gt != 0.f ? silu_f(hv[ub][j] * rinv) * gt * uv[ub][j] : 0.f;
-          else hv[ub][j] = gt != 0.f ? silu_f(hv[ub][j] * rinv) * gt : 0.f;
+          for (int j = 0; j < EPL; ++j) {
+            if constexpr (GATED) hv[ub][j] = gt != 0.f ? silu_f(hv[ub][j] * rinv) * gt * uv[ub][j] : 0.f;
+            else hv[ub][j] = gt != 0.f ? silu_f(hv[ub][j] * rinv) * gt : 0.f;
+          }
+          const i32x4_t af = DN::pack(hv[ub]);
+#pragma unroll
+          for (int p = 0; p < DP; ++p) DN::mma(acc[p], af, bfr[ub][p]);
+        } else {
+          i32x4_t af;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) af[j] = __float_as_int(hv[ub][j]);
+#pragma unroll
+          for (int p = 0; p < DP; ++p) DT::mma(acc[p], af, bfr[ub][p]);
         }
-        const i32x4_t af = DN::pack(hv[ub]);
-#pragma unroll
-        for (int p = 0; p < DP; ++p) DN::mma(acc[p], af, bfr[ub][p]);
       }
     }
   };
-  compute(0);
+  compute(lo + w);
   if constexpr (MULTI) {
-    for (int k0 = NW * UB; k0 < nk; k0 += NW * UB) {
-      load_chunk(k0);
-      compute(k0);
+    for (int u0 = lo + w + NW * UB; u0 < hi; u0 += NW * UB) {
+      load_b(u0);
+      load_a(u0);
+      compute(u0);
     }
   }
   // sum the waves' partial products, 4 panels at a time through LDS
@@ -756,20 +741,15 @@ namespace deco_host {
 hipError_t plan_decode(deco_moe_layer* L) {
   int q = (DECO_DEC_DOWN_WG + L->n_groups - 1) / L->n_groups;
   q = q < 1 ? 1 : (q > DEC_QMAX ? DEC_QMAX : q);
-  // With every expert active the routed experts have R units and the shared
-  // expert S.  A down workgroup takes at most ceil(S / q) + ceil(R / q) of
-  // them, one shared unit per wave aside: one chunk of DEC_UB units per wave
-  // when the rest fits (the kernel
-  // without a reload loop, which needs fewer registers), and at most
-  // DEC_XMAX experts (1/RMS and gates in LDS; a range of n routed units spans
+  // With every expert active the reduction has C units.  A down workgroup
+  // takes ceil(C / q) of them: one chunk of DEC_UB units per wave when that
+  // fits (the kernel without a reload loop, which needs fewer registers), and
+  // at most DEC_XMAX experts (1/RMS and gates in LDS; a range of n units spans
   // at most n / nkb_F + 2 experts).
-  const int R = L->E * L->nkb_F, S = L->nkb_Fs;
-  auto span = [&](int qq) {   // units past the one shared unit per wave
-    const int s2 = (S + qq - 1) / qq - DEC_NW;
-    return (s2 > 0 ? s2 : 0) + (R + qq - 1) / qq;
-  };
+  const int C = L->E * L->nkb_F + L->nkb_Fs;
+  auto span = [&](int qq) { return (C + qq - 1) / qq; };
   auto xmax = [&](int qq) {
-    const int x = ((R + qq - 1) / qq) / L->nkb_F + 2;
+    const int x = span(qq) / L->nkb_F + 2;
     return x < L->E ? x : L->E;
   };
   while (q < DEC_QMAX && (span(q) > DEC_NW * DEC_UB || xmax(q) > DEC_XMAX)) ++q;
