@@ -150,6 +150,38 @@ def test_c2_decode_and_prefill_agree_and_repeat_bitwise(c2):
     assert float(gap.max()) <= 2e-2 * rms
 
 
+def test_decode_and_prefill_replay_from_a_hip_graph(c2):
+    """Both forward paths are kernel launches only (no allocation, copy,
+    memset or host wait per call), so a serving loop can capture them in a
+    HIP graph.  Every replay must equal the eager result bitwise, also with
+    eager calls on other inputs between the replays (they rewrite the
+    layer's workspace)."""
+    L, ref, layer = c2
+    x = x_tensor(L)
+    x_other = torch.flip(x, dims=[0]).contiguous()
+    want_dec = layer(x, path=dm.DECO_PATH_DECODE).clone()
+    want_pre = layer(x, path=dm.DECO_PATH_PREFILL).clone()
+    out_dec, out_pre = torch.empty_like(x), torch.empty_like(x)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer(x, out_dec, path=dm.DECO_PATH_DECODE)
+        layer(x, out_pre, path=dm.DECO_PATH_PREFILL)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        other = layer(x_other, path=dm.DECO_PATH_DECODE if rep % 2 else dm.DECO_PATH_PREFILL).clone()
+        out_dec.zero_()
+        out_pre.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_dec, want_dec), f"decode replay {rep} differs from the eager call"
+        assert torch.equal(out_pre, want_pre), f"prefill replay {rep} differs from the eager call"
+        assert not torch.equal(other, want_dec)
+    del g
+    torch.cuda.synchronize()
+
+
 def test_c3_prefill_full_size():
     L = _workload(3)
     ref = oracle.forward(L.x, **L.weights(), eps=L.eps)
