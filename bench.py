@@ -441,7 +441,7 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build measures the layer on one GPU only (tokens shard across GPUs with "
+        print("bench.py: the benchmark measures the layer on one GPU only (tokens shard across GPUs with "
               "no exchange step). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
