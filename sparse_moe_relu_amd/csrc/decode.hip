@@ -608,10 +608,16 @@ __global__ void __launch_bounds__(256) k_dec_shared_rms(DecArgs a) {
 
 // out[t][c] = sum over the Q reduction splits of the down kernel's partial
 // products, in split order (deterministic); 4 consecutive columns per thread.
+#ifndef DECO_DEC_SUM_NT
+#define DECO_DEC_SUM_NT 64
+#endif
+// threads per k_dec_sum workgroup: one wave, so T = 8 spreads its 4096
+// threads over 64 CUs (same-box A/B, c2: 0.3 us per step faster than 256)
+constexpr int DEC_SUM_NT = DECO_DEC_SUM_NT;
 template <class DT>
-__global__ void __launch_bounds__(256) k_dec_sum(DecArgs a) {
+__global__ void __launch_bounds__(DEC_SUM_NT) k_dec_sum(DecArgs a) {
   constexpr int NCOL = DEC_DP * 16;
-  const int idx = blockIdx.x * 256 + threadIdx.x;
+  const int idx = blockIdx.x * DEC_SUM_NT + threadIdx.x;
   if (idx * 4 >= a.T * a.d) return;
   const int row = (idx * 4) / a.d, col = (idx * 4) % a.d;
   const int grp = col / NCOL, cin = col % NCOL;
@@ -723,8 +729,8 @@ hipError_t decode(const deco_moe_layer* L, const void* x, int T, void* out, hipS
   void (*down)(DecArgs) = down_kernel<DT>(L->dec_multi != 0, a.gated != 0, a.no_rms != 0);
   err = deco_host::launch(deco_host::KS_DEC_DOWN, down, dim3(grid_dn), dim3(DEC_NW * 64), s, a);
   if (err != hipSuccess) return err;
-  const unsigned grid_sum = (unsigned)((T * L->d / 4 + 255) / 256);
-  err = deco_host::launch(deco_host::KS_DEC_SUM, k_dec_sum<DT>, dim3(grid_sum), dim3(256), s, a);
+  const unsigned grid_sum = (unsigned)((T * L->d / 4 + DEC_SUM_NT - 1) / DEC_SUM_NT);
+  err = deco_host::launch(deco_host::KS_DEC_SUM, k_dec_sum<DT>, dim3(grid_sum), dim3(DEC_SUM_NT), s, a);
   if (err != hipSuccess) return err;
   return hipGetLastError();
 }
