@@ -921,6 +921,15 @@ PreArgs fill_pre_args(const deco_moe_layer* L, const void* x, int T, void* out) 
   return a;
 }
 
+// rows per router tile once the batch makes more 128-row tiles than CUs.
+// 64 (twice the tiles, the two-stage ring) balances the tiles over the CUs
+// better than 128 (same-box A/B: 40.4 -> 36.6 us at T = 4096 on the
+// d = 2048 layer, 76.0 -> 66.7 us at T = 2048 on the d = 4096 one).
+#ifndef DECO_PRE_RS_LARGE_BM
+#define DECO_PRE_RS_LARGE_BM 64
+#endif
+static_assert(DECO_PRE_RS_LARGE_BM == GM || DECO_PRE_RS_LARGE_BM == GM / 2, "router tile rows");
+
 // the routing steps shared by the forward and backward launchers: router
 // (and the mean and shared up-projection), TopK selection, dispatch
 template <class DT>
@@ -929,12 +938,14 @@ hipError_t launch_routing(const deco_moe_layer* L, const PreArgs& a, int T, hipS
   const unsigned mtiles = (unsigned)((T + GM - 1) / GM);
   const unsigned rs_grid = mtiles * a.rs_nt;
   const unsigned half_grid = (unsigned)((T + GM / 2 - 1) / (GM / 2)) * a.rs_nt;
+  const unsigned large_grid = DECO_PRE_RS_LARGE_BM == GM ? rs_grid : half_grid;
   hipError_t err =
       2 * rs_grid <= (unsigned)L->n_cu
           ? launch(deco_host::KS_PRE_ROUTER_SHARED, k_pre_router_shared<DT, 4, GM / 2>, dim3(half_grid), dim3(256), s, a)
       : rs_grid <= (unsigned)L->n_cu
           ? launch(deco_host::KS_PRE_ROUTER_SHARED, k_pre_router_shared<DT, 4>, dim3(rs_grid), dim3(256), s, a)
-          : launch(deco_host::KS_PRE_ROUTER_SHARED, k_pre_router_shared<DT, DECO_PRE_NS>, dim3(rs_grid), dim3(256), s, a);
+          : launch(deco_host::KS_PRE_ROUTER_SHARED, k_pre_router_shared<DT, DECO_PRE_NS, DECO_PRE_RS_LARGE_BM>,
+                   dim3(large_grid), dim3(256), s, a);
   if (err == hipSuccess && a.top_k > 0)
     err = launch(deco_host::KS_PRE_TOPK, k_pre_topk, dim3((unsigned)((T + 3) / 4)), dim3(256), s, a);
   if (err == hipSuccess && a.sraw)
