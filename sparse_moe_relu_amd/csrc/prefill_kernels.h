@@ -921,10 +921,13 @@ PreArgs fill_pre_args(const deco_moe_layer* L, const void* x, int T, void* out) 
   return a;
 }
 
-// rows per router tile once the batch makes more 128-row tiles than CUs.
-// 64 (twice the tiles, the two-stage ring) balances the tiles over the CUs
-// better than 128 (same-box A/B: 40.4 -> 36.6 us at T = 4096 on the
-// d = 2048 layer, 76.0 -> 66.7 us at T = 2048 on the d = 4096 one).
+// Router tile shape: 64-row tiles, with the four-stage ring while the batch
+// makes at most half as many 128-row tiles as CUs, else with the two-stage
+// ring (three workgroups per CU).  Twice the tiles balance better over the
+// CUs than 128-row ones (same-box A/B on the d = 2048 layer: T = 2048 32.0 ->
+// 29.4 us, T = 4096 40.4 -> 36.6 us; d = 4096 layer at T = 2048: 76.0 ->
+// 66.7 us).  DECO_PRE_RS_LARGE_BM = 128 restores 128-row tiles for the
+// larger batches.
 #ifndef DECO_PRE_RS_LARGE_BM
 #define DECO_PRE_RS_LARGE_BM 64
 #endif
@@ -942,8 +945,6 @@ hipError_t launch_routing(const deco_moe_layer* L, const PreArgs& a, int T, hipS
   hipError_t err =
       2 * rs_grid <= (unsigned)L->n_cu
           ? launch(deco_host::KS_PRE_ROUTER_SHARED, k_pre_router_shared<DT, 4, GM / 2>, dim3(half_grid), dim3(256), s, a)
-      : rs_grid <= (unsigned)L->n_cu
-          ? launch(deco_host::KS_PRE_ROUTER_SHARED, k_pre_router_shared<DT, 4>, dim3(rs_grid), dim3(256), s, a)
           : launch(deco_host::KS_PRE_ROUTER_SHARED, k_pre_router_shared<DT, DECO_PRE_NS, DECO_PRE_RS_LARGE_BM>,
                    dim3(large_grid), dim3(256), s, a);
   if (err == hipSuccess && a.top_k > 0)
