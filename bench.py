@@ -42,7 +42,6 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "k_dec_up": "sparse_moe_relu_amd/csrc/decode.hip",
     "k_dec_down": "sparse_moe_relu_amd/csrc/decode.hip",
-    "k_dec_sum": "sparse_moe_relu_amd/csrc/decode.hip",
     "k_pre_router_shared": "sparse_moe_relu_amd/csrc/prefill_kernels.h",
     "k_pre_dispatch": "sparse_moe_relu_amd/csrc/prefill_kernels.h",
     "k_pre_expert": "sparse_moe_relu_amd/csrc/prefill_kernels.h",
@@ -90,7 +89,7 @@ def decode_bytes(L, n_union: int, T: int) -> dict:
     n_up = 2 if L.W_gate is not None else 1
     up = L.d * L.E * s + 8 * L.E + n_up * n_union * L.d * L.F * s + L.d * L.Fs * s + T * L.d * s
     down = n_union * L.F * L.d * s + L.Fs * L.d * s
-    return {"k_dec_up": up, "k_dec_down": down, "k_dec_sum": T * L.d * s}
+    return {"k_dec_up": up, "k_dec_down": down}
 
 
 def prefill_flops(L, P: int, T: int) -> dict:

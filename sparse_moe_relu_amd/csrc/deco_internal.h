@@ -18,10 +18,16 @@ struct deco_moe_layer {
   int pR;                  // router panels (E padded to a multiple of 64, /16)
   int pF, pD, pFs;         // 16-column panels of F, d, Fs
   int W;                   // mask words per token = ceil(E/64)
-  int n_groups;            // ceil(d / 128) output column groups (decode down kernel)
-  int dec_q;               // reduction split of the decode down kernel
-  int dec_multi;           // decode down kernel needs more than one chunk of units per wave
+  // decode launch plan (plan_decode_sizes, plan_decode)
+  int dec_np;              // 16-column panels per up-kernel slice
+  int dec_S;               // column slices per routed expert
+  int dec_n_mean;          // mean-term workgroups (one per routed slice position; 0 without the mean term)
+  int dec_n_shs, dec_nsub, dec_n_sh;   // shared slices, slices per shared workgroup, shared workgroups
+  int dec_grid_up;
+  int dec_Fp, dec_Fsp;     // F, Fs padded to whole column-pair fragments (2 k-blocks)
+  int dec_kpe, dec_kps;    // column-pair fragments per routed expert / of the shared expert, per 8 columns
   int dec_ok;              // the decode path is available for this layer
+  int last_path;           // path of the most recent forward (DECO_PATH_DECODE or _PREFILL)
   int pre_grid;            // persistent grid of the prefill expert kernel
   int n_cu;                // compute units of the device
   int bwd_grid;            // persistent grid of the backward expert kernel
@@ -39,7 +45,10 @@ struct deco_moe_layer {
   char* Wdn16_p;           // bf16 layers: W_down again, in fp16 (prefill); fp32 layers: = Wdn_p
   char* Wsu_p;             // [pFs][nkb_d]
   char* Wsd_p;             // [pD][nkb_Fs]
+  char* Wdn8_p;            // per expert [d/8][dec_kpe] column-pair frags of W_down[e] (down operand type)
+  char* Wsd8_p;            // [d/8][dec_kps] column-pair frags of Ws_down (layer dtype)
   size_t up_stride, dn_stride;   // bytes per expert
+  size_t dn8_stride;       // bytes per expert of Wdn8_p
   float* b_r;
   float* lam;
   float* wbar;             // [d][F] fp32
@@ -59,14 +68,15 @@ struct deco_moe_layer {
   float* g;                // [Tcap][E] gates
   uint64_t* mask;          // [Tcap][W]
   // decode
-  float* mbuf;             // [Tcap][F]    x . Wbar (NormSiLU mean term)
-  float* hbuf;             // [E][16][F]   h - m rows of each routed expert (decode)
-  float* ubuf;             // [E][16][F]   gated experts: x . W_up[e] rows (decode); else null
-  float* sspart;           // [E][16][16]  per-slice sums of squares of h - m (decode)
-  char* sactf;             // [nkb_Fs] frags      shared SiLU output
+  float* mbuf;             // [Tcap][F]    x . Wbar (NormSiLU mean term; decode: rows 0..15)
   unsigned* rflag;         // [E] routing of the last decode call (1 no token, 2 some token routed to e)
-  unsigned* dec_err;       // [1] device-side error flags
-  float* part;             // [dec_q][n_groups][16][128] partial outputs of the decode down kernel
+  unsigned* dec_err;       // [1] device-side error flags (bit 0: a decode hand-off wait timed out)
+  unsigned char* act8;     // [16][E] routing decisions of the last decode call
+  void* hwords;            // [n_hwords] 64-bit decode hand-off words (epoch | value)
+  int n_hwords;
+  unsigned* dec_ctr;       // [dec_grid_up] epoch counters of the decode up kernel's workgroups
+  char* arow;              // [E][16][dec_Fp] routed activations (down operand type)
+  char* srow;              // [16][dec_Fsp] shared activations (layer dtype)
   // prefill
   int* tok_off;            // [Tcap + 1]
   int* ecnt;               // [E]
@@ -116,8 +126,6 @@ enum {
   KS_PACK = 0,
   KS_DEC_UP,
   KS_DEC_DOWN,
-  KS_DEC_SUM,
-  KS_DEC_TOPK,
   KS_PRE_TOPK,
   KS_PRE_ROUTER_SHARED,
   KS_PRE_DISPATCH,
@@ -139,12 +147,13 @@ const char* kernel_slot_name(int slot);
 // experts); W_lin: gated experts' W_up (null otherwise)
 hipError_t launch_pack_all(deco_moe_layer* L, const void* W_r, const void* W_norm, const void* W_lin,
                            const void* W_down, const void* Ws_up, const void* Ws_down, hipStream_t s);
-hipError_t plan_decode(deco_moe_layer* L);   // decode launch shape (load time)
+void plan_decode_sizes(deco_moe_layer* L, int n_cu);   // decode slices and buffer sizes (load time)
+hipError_t plan_decode(deco_moe_layer* L);   // decode residency check (load time, after plan_prefill)
 hipError_t plan_prefill(deco_moe_layer* L);  // prefill launch shape (load time)
 hipError_t plan_backward(deco_moe_layer* L); // backward launch shape (load time, after plan_prefill)
 hipError_t launch_decode(const deco_moe_layer* L, const void* x, int T, void* out, hipStream_t s);
 hipError_t launch_prefill(const deco_moe_layer* L, const void* x, int T, void* out, hipStream_t s);
-hipError_t launch_copy_mask(const deco_moe_layer* L, int T, uint64_t* mask, hipStream_t s);
+hipError_t launch_dec_mask(const deco_moe_layer* L, int T, uint64_t* mask, hipStream_t s);
 hipError_t launch_backward(const deco_moe_layer* L, const void* x, const void* dout, int T, float reg_coef,
                            const deco_moe_grads* gr, hipStream_t s);
 

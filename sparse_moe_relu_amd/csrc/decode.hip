@@ -5,666 +5,638 @@
 // point of ReLU routing with sparse experts is that inactive routed experts
 // cost nothing: the DECO paper (Sec. 1 and the Sec. 4 acceleration paragraph
 // with Table 4) attributes its speedup to skipping the memory traffic of
-// inactive experts.  Three kernels, no workgroup waiting on another:
+// inactive experts.  Two kernels:
 //
-//   k_dec_up   one workgroup per 32 columns of the shared expert, and per
-//              (routed expert, 32 columns of F).  A routed workgroup computes
-//              its expert's router logits for the batch (router: linear
-//              projection + bias, ReLU, per-expert scale; DECO paper Sec. 2
-//              "Router design") while its slice of the inter-expert mean Wbar
-//              loads (one matrix shared by all experts, so it stays in L2),
-//              and exits without reading any expert weight when no token
-//              activated the expert.  Otherwise it streams its slice of
-//              W_up[e] through v_mfma 16x16 products (tokens padded to 16 rows)
-//              into the accumulator that already holds -x.Wbar: h - m, the
-//              mean-subtracted pre-activation of NormSiLU (qidianchuan.cn
-//              write-up, section 二: subtract the mean term, RMS inside the
-//              expert, then SiLU).  It stores h - m and the per-row sums of
-//              squares of its slice; the expert's first slice also stores the
-//              logits, the gates and the expert's routing flag.  Shared-expert
-//              workgroups store SiLU(x.Ws_up) as down-projection operands.
-//   k_dec_down one workgroup per (128 output columns, 1/Q of the reduction).
-//              It lists the experts at least one token activated, loads its
-//              share of their down-projection weights (and of the shared
-//              expert's), completes each row's RMS from the slices' sums of
-//              squares, applies SiLU and the gate while building the MFMA
-//              operands, multiplies, and stores its partial product.
-//   k_dec_sum  adds the Q partial products of each output in split order
-//              (deterministic) and writes out.
+//   k_dec_up    one workgroup per column slice of the inter-expert mean
+//               term (x.Wbar), per group of column slices of the shared
+//               expert's up-projection, and per (routed expert, column
+//               slice).  A routed workgroup computes its expert's router
+//               logits for the batch (router: linear projection + bias, ReLU,
+//               per-expert scale; DECO paper Sec. 2 "Router design") and
+//               exits without reading any expert weight when no token
+//               activated the expert.  Otherwise it streams its slice of
+//               W_up[e] through v_mfma 16x16 products (tokens padded to 16
+//               rows), subtracts the mean term (published by the mean
+//               workgroups), takes the row's RMS over all F columns (the
+//               per-row sums of squares of the other slices of the same
+//               expert are exchanged through device memory), applies SiLU and
+//               the gate, and stores the activations as the down-projection
+//               operand (NormSiLU: qidianchuan.cn write-up, section 二:
+//               subtract the mean term, RMS inside the expert, then SiLU).
+//   k_dec_down  one workgroup per 8 output columns.  It lists the experts
+//               the batch touched and multiplies their down-projection rows
+//               for its 8 columns (and the shared expert's) with the
+//               activations: the whole reduction over the shared expert and
+//               every touched expert happens inside the workgroup, so each
+//               output is written once, with no partial sums.
+//
+// Hand-offs inside k_dec_up (mean term, sums of squares, TopK logits) are
+// 64-bit words written and read with agent-scope relaxed atomics: the high
+// half is the call's epoch and the low half the value, so a reader needs no
+// separate flag and no fence, and a word left from an earlier call is never
+// taken for this call's.  Each workgroup takes the epoch from an atomic
+// increment of its own counter word (every call increments every counter
+// once, so they stay equal and no two workgroups contend).  Waiting workgroups only
+// depend on the mean-term workgroups (launched first) and on the other slices
+// of their own expert (consecutive workgroups); every wait is bounded (a
+// timeout sets the layer's error flag).
+#include <string.h>
+
 #include "deco_common.h"
 #include "deco_internal.h"
-#include "gemm_tile.h"
 
 using namespace deco;
 
 namespace {
 
+constexpr int DNW = 8;            // waves per workgroup (both kernels)
+constexpr int DNT = DNW * 64;
+constexpr int SPIN_LIMIT = 1 << 20;
+constexpr int NSUB_MAX = 4;       // shared-expert slices per workgroup
+typedef unsigned long long u64;
+
 struct DecArgs {
   const void* x;
   void* out;
-  int T, d, E, F, Fs;
-  int nkb_d, nkb_F, nkb_Fs, pF, pFs, pD, n_groups, Q;
-  int n_shared, wg_per_e;   // up workgroups of the shared expert; per routed expert
-  int top_k, pR, W;         // TopK variant (0: ReLU routing); router panels; mask words
-  int gated;                // 1: gated experts (up workgroups for W_up[e] follow each expert's own)
-  int no_mean, no_rms;      // NormSiLU ablations: drop the mean term / the RMS step
-  float* sraw;              // RMS-only NormSiLU shared expert: [16][Fs] x . Ws_up (fp32), else null
+  int T, d, E, F, Fs, W;
+  int nkb_d;                // k-blocks of d
+  int S;                    // column slices per routed expert
+  int n_mean, n_sh, nsub;   // mean-term workgroups, shared workgroups, shared slices per workgroup
+  int n_shs;                // shared slices
+  int pF, pFs;              // 16-column panels of F and Fs
+  int top_k;                // TopK routing variant (0: ReLU routing)
+  int no_rms;               // NormSiLU ablation: no RMS step
+  float eps;
   const char* Wr_p;
   const char* Wup_p;        // NormSiLU input projection (a gated expert's gate projection)
   const char* Wlin_p;       // gated experts' up-projection
   const char* Wbar_p;
-  const char* Wdn_p;        // W_down in the operand type of the routed down-projection
   const char* Wsu_p;
-  const char* Wsd_p;
-  size_t up_stride, dn_stride;
+  const char* Wdn8_p;       // W_down[e] in column-pair fragments, down operand type
+  const char* Wsd8_p;       // Ws_down in column-pair fragments, layer dtype
+  size_t up_stride, dn8_stride;
   const float* b_r;
   const float* lam;
-  float eps;
-  float* z;
-  float* g;
-  float* hbuf;              // [E][16][F] h - m of each token row
-  float* ubuf;              // [E][16][F] gated experts: x . W_up[e] of each token row
-  float* sspart;            // [E][wg_per_e][16] sums of squares of h - m over each slice
-  char* sactf;              // shared-expert activations as down-projection operand fragments
-  unsigned* rflag;          // [E] 1 no token routed to e, 2 some token did
-  uint64_t* mask;           // [T][W] routing masks (stored by the TopK router)
-  float* part;
+  float* z;                 // [T][E] logits
+  float* g;                 // [T][E] gates
+  unsigned char* act8;      // [16][E] routing decisions
+  unsigned* rflag;          // [E] 1: no token routed to e, 2: some token was
+  u64* hw;                  // hand-off words: [16][F] mean term | [E * S][16] sums of squares |
+                            // [E][16] logits (TopK) | [n_sh][16] shared sums of squares
+  unsigned* ctr;            // [grid] epoch counters, one per up-kernel workgroup
+  void* arow;               // [E][16][Fp] routed activations, down operand type
+  void* srow;               // [16][Fsp] shared activations, layer dtype
+  int Fp, Fsp;              // F, Fs padded to whole column-pair fragments
+  int kpe, kps;             // column-pair fragments per routed expert / of the shared expert
+  unsigned* err;
 };
 
-#ifndef DECO_DEC_NW
-#define DECO_DEC_NW 8
-#endif
-#ifndef DECO_DEC_NP
-#define DECO_DEC_NP 2
-#endif
-#ifndef DECO_DEC_CH
-#define DECO_DEC_CH 8
-#endif
-constexpr int DEC_NW = DECO_DEC_NW;   // waves per workgroup
-constexpr int DEC_NP = DECO_DEC_NP;   // 16-column panels per up workgroup
-constexpr int DEC_CH = DECO_DEC_CH;   // k-blocks held in registers per wave at a time
-constexpr int DEC_QMAX = 64;          // largest K-split of the down kernel (host clamps dec_q)
-constexpr int DEC_WGMAX = 8;          // largest number of up slices per routed expert
-constexpr int DEC_UB = 2;             // down-kernel units (k-blocks) in flight per wave
-constexpr int DEC_DP = 8;             // 16-column output panels per down workgroup
-constexpr int DEC_XMAX = 64;          // routed experts one down workgroup may touch (host plan)
-// A buffer-load offset past the resource's range: the load returns zeros
-// without touching memory (used to mask loads without branching).
-constexpr unsigned OOB = 0xFFFFFF00u;
+__device__ __forceinline__ u64* hw_m(const DecArgs& a) { return a.hw; }
+__device__ __forceinline__ u64* hw_ss(const DecArgs& a) { return a.hw + (size_t)16 * a.F; }
+__device__ __forceinline__ u64* hw_z(const DecArgs& a) { return hw_ss(a) + (size_t)a.E * a.S * 16; }
+__device__ __forceinline__ u64* hw_sh(const DecArgs& a) { return hw_z(a) + (size_t)a.E * 16; }
 
-// 16 bytes through a buffer resource: `soff` is wave-uniform (an SGPR), so a
-// run of such loads needs one VGPR for all its addresses
+__device__ __forceinline__ void put_word(u64* p, unsigned ep, float v) {
+  __hip_atomic_store(p, ((u64)ep << 32) | __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ u64 get_word(const u64* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool word_ok(u64 v, unsigned ep) { return (unsigned)(v >> 32) == ep; }
+__device__ __forceinline__ float word_val(u64 v) { return __uint_as_float((unsigned)v); }
+
+// Block-wide wait: every thread holds N words (already loaded from p[i];
+// need marks those that matter); returns once all carry epoch ep, reloading the
+// invalid ones.  Bounded: a timeout sets bit 0 of *err and the bit `which`
+// naming the hand-off (2 mean term, 4 sums of squares, 8 TopK logits, 16
+// shared sums of squares).
+template <int N>
+__device__ __forceinline__ void wait_words(u64 (&v)[N], const u64* const (&p)[N], const bool (&need)[N],
+                                           unsigned ep, unsigned* err, unsigned which) {
+  for (int it = 0;; ++it) {
+    bool ok = true;
+#pragma unroll
+    for (int k = 0; k < N; ++k) ok = ok && (!need[k] || word_ok(v[k], ep));
+    if (__syncthreads_and(ok)) return;
+    if (it > SPIN_LIMIT) {
+      if (threadIdx.x == 0) atomicOr(err, 1u | which);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+    for (int k = 0; k < N; ++k)
+      if (need[k] && !word_ok(v[k], ep)) v[k] = get_word(p[k]);
+  }
+}
+
+// 16 bytes through a buffer resource; loads whose vector offset is past
+// num_records return zeros without touching memory
 __device__ __forceinline__ i32x4_t ld16_buf(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
   return __builtin_bit_cast(i32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
 }
-__device__ __forceinline__ float ld_buf(__amdgpu_buffer_rsrc_t r, unsigned voff) {
-  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, 0));
-}
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7FFFFFFF, 0x00020000);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, unsigned bytes = 0x7FFFFFFFu) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }
 
-// TopK routing variant (the baseline of the DECO paper's Sec. 4 acceleration
-// experiment, Table 4): one workgroup computes the logits of all experts for
-// the batch (MFMA, 16 padded rows; the waves split d, then add their
-// products in a fixed order), keeps each token's top_k experts (ties to the
-// lower index), stores logits, gates (softmax of the kept logits) and masks,
-// and publishes each expert's flag for the up and down kernels.
-template <class DT, int NW>
-__global__ void __launch_bounds__(NW * 64) k_dec_topk(DecArgs a) {
+// acc[p] += x[16 rows][k-blocks kb_lo .. kb_hi) . W[..][panels p0 + p] for p < NP
+// (panels at or past pmax read panel pmax - 1; their results are dropped by
+// the caller).  Loads go in batches of 8 k-blocks x NP panels (up to 32
+// fragments) issued together.  x rows past T read zeros (buffer range).
+template <class DT, int NP>
+__device__ __forceinline__ void up_stream(__amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rw, int p0, int pmax,
+                                          int nkb, int kb_lo, int kb_hi, int d, f32x4_t (&acc)[NP],
+                                          bool x_loaded, const i32x4_t* x0) {
   using elem = typename DT::elem;
-  constexpr int CH = 4, PG = 4;   // k-blocks and router panels per load batch
-  constexpr int PMAX = 16;        // router panels (E <= 256)
-  __shared__ f32x4_t s_red[NW][PG][64];
-  __shared__ float s_z[16][PMAX * 16];
-  __shared__ int s_act[PMAX * 16];
-  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 4, c = l & 15;
-  const int nkb = a.nkb_d;
-  const int kb_lo = (w * nkb) / NW, kb_hi = ((w + 1) * nkb) / NW;
-  const elem* xrow = (const elem*)a.x + (size_t)c * a.d;
-  const bool row_ok = c < a.T;
-  const __amdgpu_buffer_rsrc_t rw = buf_rsrc(a.Wr_p);
-  for (int e = tid; e < PMAX * 16; e += NW * 64) s_act[e] = 0;
-  for (int pg = 0; pg < a.pR; pg += PG) {
-    f32x4_t acc[PG];
+  constexpr int U = 8;
+  const int l = threadIdx.x & 63, c = l & 15, g = l >> 4;
+  const unsigned xoff = (unsigned)(((size_t)c * d + (size_t)DT::EPL * g) * sizeof(elem));
+  for (int kb0 = kb_lo; kb0 < kb_hi; kb0 += U) {
+    i32x4_t xf[U], wf[U][NP];
 #pragma unroll
-    for (int p = 0; p < PG; ++p) acc[p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int kb0 = kb_lo; kb0 < kb_hi; kb0 += CH) {
-      i32x4_t xf[CH], wf[CH][PG];
+    for (int u = 0; u < U; ++u) {
+      int kb = kb0 + u;
+      kb = kb < kb_hi ? kb : kb_hi - 1;   // past the range: a valid block, its products are skipped
+      if (x_loaded && kb0 == kb_lo) xf[u] = x0[u];
+      else xf[u] = ld16_buf(rx, xoff, (unsigned)(kb * DT::KB * sizeof(elem)));
 #pragma unroll
-      for (int u = 0; u < CH; ++u) {
-        const int kb = kb0 + u;
-        xf[u] = (kb < kb_hi && row_ok) ? load_row_frag<DT>(xrow, kb, g) : zero16();
-#pragma unroll
-        for (int p = 0; p < PG; ++p)
-          wf[u][p] = (kb < kb_hi && pg + p < a.pR) ? ld16_buf(rw, 16u * l, (unsigned)frag_off(pg + p, kb, nkb)) : zero16();
+      for (int p = 0; p < NP; ++p) {
+        const int pp = p0 + p < pmax ? p0 + p : pmax - 1;
+        wf[u][p] = ld16_buf(rw, 16u * l, (unsigned)frag_off(pp, kb, nkb));
       }
-#pragma unroll
-      for (int u = 0; u < CH; ++u)
-        if (kb0 + u < kb_hi) {
-#pragma unroll
-          for (int p = 0; p < PG; ++p) DT::mma(acc[p], xf[u], wf[u][p]);
-        }
     }
 #pragma unroll
-    for (int p = 0; p < PG; ++p) s_red[w][p][l] = acc[p];
-    __syncthreads();
-    // lane (c, g) of panel p holds rows 4 g + i of expert 16 p + c
-    for (int idx = tid; idx < PG * 256; idx += NW * 64) {
-      const int p = idx >> 8, ll = (idx >> 2) & 63, i = idx & 3;
-      float v = 0.f;
-#pragma unroll
-      for (int ww = 0; ww < NW; ++ww) v += s_red[ww][p][ll][i];
-      const int e = (pg + p) * 16 + (ll & 15);
-      s_z[4 * (ll >> 4) + i][e] = v + (e < a.E ? a.b_r[e] : 0.f);
-    }
-    __syncthreads();
-  }
-  // one wave per token: keep the top_k logits
-  if (w < a.T) {
-    const int t = w;
-    float zv[4];
-    bool sel[4];
-    float gate[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = 64 * j + l;
-      zv[j] = e < a.E ? s_z[t][e] : -__builtin_inff();
-    }
-    topk_wave<4>(zv, a.top_k, sel, gate);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = 64 * j + l;
-      if (e < a.E) {
-        a.z[(size_t)t * a.E + e] = zv[j];
-        a.g[(size_t)t * a.E + e] = gate[j];
-        if (sel[j]) s_act[e] = 1;
-      }
-      const unsigned long long word = __ballot(sel[j]);
-      if (l == 0 && j < a.W) a.mask[(size_t)t * a.W + j] = word;
-    }
-  }
-  __syncthreads();
-  for (int e = tid; e < a.E; e += NW * 64) a.rflag[e] = s_act[e] ? 2u : 1u;
-}
-
-// VAR: bit 0 gated experts, bit 1 no mean term, bit 2 RMS-only NormSiLU
-// shared expert (the variants are separate instantiations, so the default
-// one carries none of their logic)
-constexpr int DV_GATED = 1, DV_NO_MEAN = 2, DV_SHARED_RMS = 4;
-template <class DT, int NW, int NP, int VAR>
-__global__ void __launch_bounds__(NW * 64) k_dec_up(DecArgs a) {
-  constexpr bool GT = (VAR & DV_GATED) != 0, NM = (VAR & DV_NO_MEAN) != 0, SR = (VAR & DV_SHARED_RMS) != 0;
-  using elem = typename DT::elem;
-  constexpr int CH = DEC_CH;
-  static_assert(NP * 256 <= NW * 64, "one output entry per thread");
-  static_assert(NP <= 4, "s_red holds 4 panels per wave");
-  __shared__ float s_zred[NW][16];
-  __shared__ float s_ss[NP][16];
-  __shared__ f32x4_t s_red[NW][4][64];
-  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 4, c = l & 15;
-  // grid order: shared-expert slices (they need no router result, so they
-  // stream from the start), then (routed expert, slice); a gated expert's
-  // slices of its NormSiLU input come first, then those of its W_up
-  const int bid = blockIdx.x;
-  const bool routed = bid >= a.n_shared;
-  const int rb = bid - a.n_shared;
-  const int spe = GT ? 2 * a.wg_per_e : a.wg_per_e;
-  const int e = routed ? rb / spe : 0;
-  const int rs = routed ? rb % spe : 0;
-  const bool lin = GT && rs >= a.wg_per_e;   // W_up slice of a gated expert: no mean term, no RMS
-  const int wgi = lin ? rs - a.wg_per_e : rs;
-  const int p0 = routed ? wgi * NP : bid * NP;
-  // what the first stream reads: the mean term, or a gated expert's W_up, or
-  // (no mean term: an ablation) the expert's own slice
-  const char* w_up_e = a.Wup_p + (size_t)e * a.up_stride;
-  const bool mean_pass = !lin && !NM;   // stream -Wbar, then W_up[e]
-  const char* w_first = lin ? a.Wlin_p + (size_t)e * a.up_stride : (NM ? w_up_e : a.Wbar_p);
-  const int nkb = a.nkb_d;
-  const int kb_lo = (w * nkb) / NW, kb_hi = ((w + 1) * nkb) / NW;
-  const elem* xrow = (const elem*)a.x + (size_t)c * a.d;
-  const bool row_ok = c < a.T;
-  const bool x_fits = kb_hi - kb_lo <= CH;   // the wave's x fragments fit in registers at once
-
-  i32x4_t xf[CH];
-  i32x4_t wf[CH][NP];
-  auto load_x = [&](int kb0) {
-#pragma unroll
-    for (int u = 0; u < CH; ++u) {
-      const int kb = kb0 + u;
-      xf[u] = (kb < kb_hi && row_ok) ? load_row_frag<DT>(xrow, kb, g) : zero16();
-    }
-  };
-  auto load_w = [&](const char* wbase, int kb0) {
-    const __amdgpu_buffer_rsrc_t rw = buf_rsrc(wbase);
-#pragma unroll
-    for (int u = 0; u < CH; ++u) {
-      const int kb = kb0 + u;
-#pragma unroll
-      for (int p = 0; p < NP; ++p)
-        wf[u][p] = kb < kb_hi ? ld16_buf(rw, 16u * l, (unsigned)frag_off(p0 + p, kb, nkb)) : zero16();
-    }
-  };
-  f32x4_t acc[NP];
-#pragma unroll
-  for (int p = 0; p < NP; ++p) acc[p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  auto mma_chunk = [&](int kb0) {
-#pragma unroll
-    for (int u = 0; u < CH; ++u) {
+    for (int u = 0; u < U; ++u)
       if (kb0 + u < kb_hi) {
 #pragma unroll
         for (int p = 0; p < NP; ++p) DT::mma(acc[p], xf[u], wf[u][p]);
       }
-    }
-  };
-  // acc += x . (the NP panels at p0 of wbase) over this wave's k-range; xf
-  // and wf may already hold the first chunk's operands
-  auto stream = [&](const char* wbase, bool w0_loaded, bool x0_loaded) {
-    for (int kb0 = kb_lo; kb0 < kb_hi; kb0 += CH) {
-      if (!(x0_loaded && kb0 == kb_lo)) load_x(kb0);
-      if (!(w0_loaded && kb0 == kb_lo)) load_w(wbase, kb0);
-      mma_chunk(kb0);
-    }
-  };
-
-  if (routed && a.top_k > 0) {
-    // TopK variant: k_dec_topk has routed the batch; x and the first
-    // weights load while the expert's flag is read
-    load_x(kb_lo);
-    load_w(w_first, kb_lo);
-    if (a.rflag[e] != 2u) {
-      wait_all_mem();
-      return;  // no token keeps expert e: none of its weights are read
-    }
-    stream(w_first, true, true);
-    if (mean_pass) {
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int p = 0; p < NP; ++p) acc[p] = -acc[p];
-      stream(w_up_e, false, x_fits);
-    }
-  } else if (routed) {
-    // router logits of expert e for the 16 (padded) token rows
-    const float lam_e = a.lam[e];
-    const float b_e = a.b_r[e];
-    float zp = 0.f;
-    const char* wr = a.Wr_p + frag_off(e >> 4, 0, nkb) + (size_t)((e & 15) + 16 * g) * 16;
-    for (int kb0 = kb_lo; kb0 < kb_hi; kb0 += CH) {
-      load_x(kb0);
-      i32x4_t wv[CH];
-#pragma unroll
-      for (int u = 0; u < CH; ++u) wv[u] = kb0 + u < kb_hi ? ld16(wr + (size_t)(kb0 + u) * FRAG_BYTES) : zero16();
-#pragma unroll
-      for (int u = 0; u < CH; ++u) {
-#pragma unroll
-        for (int j = 0; j < DT::EPL; ++j) zp += DT::lane_elem(xf[u], j) * DT::lane_elem(wv[u], j);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);   // keep the router's registers apart from the weights'
-    if (!x_fits) load_x(kb_lo);
-    // the first weights load while the waves combine their logits
-    load_w(w_first, kb_lo);
-    zp += __shfl_xor(zp, 16);
-    zp += __shfl_xor(zp, 32);
-    if (g == 0) s_zred[w][c] = zp;
-    lds_barrier();   // LDS only: the weight loads stay in flight
-    // every wave forms the logits itself (lane: token row c, same order
-    // everywhere), so the activity decision needs no further barrier
-    float zz = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < NW; ++ww) zz += s_zred[ww][c];
-    zz += b_e;
-    const bool act = c < a.T && zz > 0.f && lam_e != 0.f;
-    const bool any = __ballot(act) != 0ull;
-    if (rs == 0 && w == 0) {
-      if (l == 0) a.rflag[e] = any ? 2u : 1u;
-      if (l < a.T) {
-        a.z[(size_t)l * a.E + e] = zz;
-        a.g[(size_t)l * a.E + e] = act ? lam_e * zz : 0.f;
-      }
-    }
-    if (!any) {
-      wait_all_mem();
-      return;  // inactive expert: none of its weights are read
-    }
-    // acc = -(x . Wbar) + x . W_up[e]: the NormSiLU mean term and the expert
-    // in one fp32 accumulator (a gated expert's W_up slice: acc = x . W_up[e])
-    stream(w_first, true, true);
-    if (mean_pass) {
-      __builtin_amdgcn_sched_barrier(0);   // keep the two streams' registers apart
-#pragma unroll
-      for (int p = 0; p < NP; ++p) acc[p] = -acc[p];
-      // (with a single chunk per wave xf still holds it)
-      stream(w_up_e, false, x_fits);
-    }
-  } else {
-    stream(a.Wsu_p, false, false);
   }
+}
 
-  // sum the waves' partial products: one (row, column) entry per thread
+// sum the waves' accumulators into dst[row][col] (16 rows x 16 NP columns)
+template <int NP, int LD>
+__device__ __forceinline__ void reduce_waves(f32x4_t (&s_red)[DNW][NP][64], const f32x4_t (&acc)[NP],
+                                             float (*dst)[LD]) {
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
 #pragma unroll
   for (int p = 0; p < NP; ++p) s_red[w][p][l] = acc[p];
   __syncthreads();
-  const bool mine = tid < NP * 256;
-  const int pp = tid >> 8, ll = (tid >> 2) & 63, i = tid & 3;
-  const int row = 4 * (ll >> 4) + i, col = (p0 + pp) * 16 + (ll & 15);
-  float v = 0.f;
-  if (mine) {
+  for (int o = tid; o < 256 * NP; o += DNT) {
+    const int p = o >> 8, ll = (o >> 2) & 63, i = o & 3;
+    float v = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < NW; ++ww) v += s_red[ww][pp][ll][i];
+    for (int ww = 0; ww < DNW; ++ww) v += s_red[ww][p][ll][i];
+    dst[4 * (ll >> 4) + i][16 * p + (ll & 15)] = v;
   }
-  if (!routed) {
-    // shared expert: plain SiLU, stored as down-projection operand fragments
-    // (RMS-only NormSiLU: the pre-activation, for k_dec_shared_rms)
-    if (mine) {
-      if constexpr (SR) a.sraw[(size_t)row * a.Fs + col] = v;
-      else *reinterpret_cast<elem*>(a.sactf + frag_elem_off<DT>(row, col)) = DT::from_f32(silu_f(v));
+  __syncthreads();
+}
+
+// VAR bits of the up kernel (separate instantiations, so the default one
+// carries none of the variants' logic)
+constexpr int DV_GATED = 1, DV_NO_MEAN = 2, DV_SHARED_RMS = 4;
+
+template <class DT, int NP, int VAR>
+__global__ void __launch_bounds__(DNT) k_dec_up(DecArgs a) {
+  constexpr bool GT = (VAR & DV_GATED) != 0, NM = (VAR & DV_NO_MEAN) != 0, SR = (VAR & DV_SHARED_RMS) != 0;
+  using elem = typename DT::elem;
+  using DN = typename DT::Down;
+  constexpr int U = 8;             // k-blocks per load batch
+  constexpr int NCOL = 16 * NP;    // columns of a slice
+  constexpr int CPT = NCOL / 32;   // columns per thread in the row phase (32 threads per row)
+  __shared__ f32x4_t s_red[DNW][NP][64];
+  __shared__ float s_h[SR ? NSUB_MAX : 1][16][NCOL + 1];
+  __shared__ float s_u[GT ? 16 : 1][GT ? NCOL + 1 : 1];
+  __shared__ float s_zr[DNW][16];
+  __shared__ float s_gate[16], s_ssx[16][33];
+  __shared__ int s_act[16];
+  __shared__ float s_zall[16][257];   // TopK: every expert's logits
+  __shared__ unsigned s_ep;
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, c = l & 15, g = l >> 4;
+  const int b = blockIdx.x;
+  // this call's epoch: 1 + the number of earlier calls (the atomic returns
+  // the coherent value of this workgroup's counter and advances it)
+  if (tid == 0) s_ep = __hip_atomic_fetch_add(a.ctr + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+  const int kind = b < a.n_mean ? 0 : (b < a.n_mean + a.n_sh ? 1 : 2);   // mean, shared, routed
+  const int rb = b - a.n_mean - a.n_sh;
+  const int e = kind == 2 ? rb / a.S : 0;
+  const int slice = kind == 0 ? b : (kind == 1 ? b - a.n_mean : rb % a.S);
+  const int nkb = a.nkb_d;
+  const int kb_lo = (w * nkb) / DNW, kb_hi = ((w + 1) * nkb) / DNW;
+  const __amdgpu_buffer_rsrc_t rx = buf_rsrc(a.x, (unsigned)((size_t)a.T * a.d * sizeof(elem)));
+  // row phase: 32 threads per token row, CPT consecutive columns each
+  const int row = tid >> 5, cq = tid & 31;
+  const int col0 = CPT * cq;
+
+  f32x4_t acc[NP], accu[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) acc[p] = accu[p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  i32x4_t x0[U];
+  bool x_loaded = false;
+
+  if (kind == 1) {
+    // ---- shared expert: slices slice * nsub .. (+ nsub), SiLU(x . Ws_up) as
+    // the down-projection operand (RMS-only variant: the row's RMS spans all
+    // slices, exchanged between the shared workgroups)
+    float ss = 0.f;
+    for (int j = 0; j < a.nsub; ++j) {
+      const int q = slice * a.nsub + j;
+      if (q >= a.n_shs) break;
+#pragma unroll
+      for (int p = 0; p < NP; ++p) acc[p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      up_stream<DT, NP>(rx, buf_rsrc(a.Wsu_p), q * NP, a.pFs, nkb, kb_lo, kb_hi, a.d, acc, false, x0);
+      reduce_waves<NP, NCOL + 1>(s_red, acc, s_h[SR ? j : 0]);
+      const int gcol0 = q * NCOL + col0;
+      const bool col_ok = gcol0 < a.Fs;   // a partial last slice: CPT divides 32, so all or none
+      if constexpr (SR) {
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) ss += col_ok ? s_h[j][row][col0 + k] * s_h[j][row][col0 + k] : 0.f;
+      } else if (row < a.T && col_ok) {
+        elem* srow = (elem*)a.srow + (size_t)row * a.Fsp + gcol0;
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) srow[k] = DT::from_f32(silu_f(s_h[0][row][col0 + k]));
+      }
+    }
+    if constexpr (SR) {
+#pragma unroll
+      for (int o = 16; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+      const unsigned ep = s_ep;
+      if (cq == 0) put_word(hw_sh(a) + (size_t)slice * 16 + row, ep, ss);
+      // every shared workgroup's sums (32 at a time, one per thread of the
+      // row), then the row's 1 / RMS
+      float tot = 0.f;
+      for (int q0 = 0; q0 < a.n_sh; q0 += 32) {
+        u64 v[1];
+        const bool need[1] = {q0 + cq < a.n_sh};
+        const u64* const p[1] = {hw_sh(a) + (size_t)(need[0] ? q0 + cq : 0) * 16 + row};
+        v[0] = need[0] ? get_word(p[0]) : 0ull;
+        wait_words<1>(v, p, need, ep, a.err, 16u);
+        s_ssx[row][cq] = need[0] ? word_val(v[0]) : 0.f;
+        __syncthreads();
+        for (int q = 0; q < 32 && q0 + q < a.n_sh; ++q) tot += s_ssx[row][q];   // workgroup order
+        __syncthreads();
+      }
+      const float rinv = 1.0f / sqrtf(tot / (float)a.Fs + a.eps);
+      for (int j = 0; j < a.nsub; ++j) {
+        const int q = slice * a.nsub + j;
+        const int gcol0 = q * NCOL + col0;
+        if (q < a.n_shs && row < a.T && gcol0 < a.Fs) {
+          elem* srow = (elem*)a.srow + (size_t)row * a.Fsp + gcol0;
+#pragma unroll
+          for (int k = 0; k < CPT; ++k) srow[k] = DT::from_f32(silu_f(s_h[j][row][col0 + k] * rinv));
+        }
+      }
     }
     return;
   }
-  if (mine && row < a.T) (lin ? a.ubuf : a.hbuf)[((size_t)e * 16 + row) * a.F + col] = v;
-  if (lin) return;
-  // per-row sum of squares over this slice: lanes with equal l & 3 of a wave
-  // hold one row (4 (w & 3) + (l & 3)) of panel w >> 2, columns l >> 2
-  float sq = v * v;
-  sq += __shfl_xor(sq, 4);
-  sq += __shfl_xor(sq, 8);
-  sq += __shfl_xor(sq, 16);
-  sq += __shfl_xor(sq, 32);
-  if (mine && l < 4) s_ss[pp][row] = sq;
-  __syncthreads();
-  if (tid < a.T) {
-    float ss = 0.f;
-#pragma unroll
-    for (int p = 0; p < NP; ++p) ss += s_ss[p][tid];
-    a.sspart[((size_t)e * a.wg_per_e + wgi) * 16 + tid] = ss;
-  }
-}
 
-template <class DT, int NW, bool MULTI, bool GATED, bool NO_RMS>
-__global__ void __launch_bounds__(NW * 64) k_dec_down(DecArgs a) {
-  using elem = typename DT::elem;
-  using DN = typename DT::Down;   // operand type of the routed down-projection
-  constexpr int UB = DEC_UB;
-  constexpr int DP = DEC_DP;
-  constexpr int EPL = DT::EPL;
-  constexpr int NCOL = DP * 16;
-  __shared__ int s_ulist[256];
-  __shared__ int s_wcnt[4];
-  __shared__ int s_nu;
-  __shared__ float s_rinv[DEC_XMAX * 16];
-  __shared__ float s_gate[DEC_XMAX * 16];
-  __shared__ f32x4_t s_red[NW][4][64];
-  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, c = l & 15, g = l >> 4;
-  const int grp = blockIdx.x % a.n_groups, q = blockIdx.x / a.n_groups;
-
-  // ascending list of the experts that at least one token activated
-  const int nwE = (a.E + 63) >> 6;
-  const int e_ = w * 64 + l;
-  const bool act = (w < nwE) && (e_ < a.E) && (a.rflag[e_] == 2u);
-  const unsigned long long bal = __ballot(act);
-  if (w < nwE && l == 0) s_wcnt[w] = __popcll(bal);
-  __syncthreads();
-  if (act) {
-    int base = 0;
-    for (int ww = 0; ww < w; ++ww) base += s_wcnt[ww];
-    s_ulist[base + __popcll(bal & ((1ull << l) - 1ull))] = e_;
-  }
-  if (tid == 0) {
-    int n = 0;
-    for (int ww = 0; ww < nwE; ++ww) n += s_wcnt[ww];
-    s_nu = n;
-  }
-  __syncthreads();
-  const int nu = s_nu;
-  const int n_routed_units = nu * a.nkb_F;
-  const int C = n_routed_units + a.nkb_Fs;
-  const int lo = (int)(((long long)q * C) / a.Q), hi = (int)(((long long)(q + 1) * C) / a.Q);
-  // routed experts with units in [lo, hi): list entries i0 .. i0 + nx - 1
-  const int rhi = hi < n_routed_units ? hi : n_routed_units;
-  const int i0 = lo < rhi ? lo / a.nkb_F : 0;
-  const int nx = lo < rhi ? (rhi - 1) / a.nkb_F - i0 + 1 : 0;
-
-  // weights of one chunk of this wave's units (k-blocks), straight to
-  // registers.  Panels past the last output column (d not a multiple of
-  // NCOL) read the last panel again and their results are dropped.
-  i32x4_t bfr[UB][DP];
-  auto load_b = [&](int u0) {
+  if (kind == 0) {
+    // ---- mean term slice: m[row][cols] = x . Wbar, published as words
+    up_stream<DT, NP>(rx, buf_rsrc(a.Wbar_p), slice * NP, a.pF, nkb, kb_lo, kb_hi, a.d, acc, false, x0);
+    reduce_waves<NP, NCOL + 1>(s_red, acc, s_h[0]);
+    if (row < a.T) {
 #pragma unroll
-    for (int ub = 0; ub < UB; ++ub) {
-      const int u = u0 + ub * NW;   // wave-uniform
-      const char* B;
-      int kb, nkb;
-      if (u < rhi) {
-        kb = u % a.nkb_F;
-        nkb = a.nkb_F;
-        B = a.Wdn_p + (size_t)__builtin_amdgcn_readfirstlane(s_ulist[u / a.nkb_F]) * a.dn_stride;
-      } else {
-        kb = u < hi ? u - n_routed_units : 0;
-        nkb = a.nkb_Fs;
-        B = a.Wsd_p;
-      }
-      const __amdgpu_buffer_rsrc_t rb = buf_rsrc(B);
-#pragma unroll
-      for (int p = 0; p < DP; ++p) {
-        int pan = grp * DP + p;
-        pan = pan < a.pD ? pan : a.pD - 1;
-        bfr[ub][p] = u < hi ? ld16_buf(rb, 16u * l, (unsigned)frag_off(pan, kb, nkb)) : zero16();
-      }
+      for (int k = 0; k < CPT; ++k)
+        put_word(hw_m(a) + (size_t)row * a.F + slice * NCOL + col0 + k, s_ep, s_h[0][row][col0 + k]);
     }
-  };
-  // raw activation operands of a chunk: for a routed unit (expert e, k-block
-  // kb) lane (c, g) takes h - m of token row c at the EPL columns its
-  // fragment holds (rows past T read nothing: the buffer range check returns
-  // zeros), and for gated experts x . W_up[e] at the same place; for a
-  // shared unit, the stored fragment
-  const __amdgpu_buffer_rsrc_t rh = buf_rsrc(a.hbuf), rs = buf_rsrc(a.sactf);
-  const __amdgpu_buffer_rsrc_t ru = buf_rsrc(GATED ? a.ubuf : a.hbuf);
-  float hv[UB][EPL];
-  float uv[UB][GATED ? EPL : 1];
-  auto load_a = [&](int u0) {
-#pragma unroll
-    for (int ub = 0; ub < UB; ++ub) {
-      const int u = u0 + ub * NW;
-      i32x4_t r[EPL / 4], r2[EPL / 4];
-      if (u < rhi) {
-        const int e = s_ulist[u / a.nkb_F], kb = u % a.nkb_F;
-        const unsigned off = c < a.T ? 4u * (unsigned)((e * 16 + c) * a.F + kb * DT::KB + EPL * g) : OOB;
-#pragma unroll
-        for (int k = 0; k < EPL / 4; ++k) r[k] = ld16_buf(rh, off + 16u * k, 0u);
-        if constexpr (GATED) {
-#pragma unroll
-          for (int k = 0; k < EPL / 4; ++k) r2[k] = ld16_buf(ru, off + 16u * k, 0u);
-        }
-      } else {   // a shared unit, or past the range (reads nothing)
-        const unsigned off = u < hi ? (unsigned)((u - n_routed_units) * FRAG_BYTES) + 16u * l : OOB;
-        r[0] = ld16_buf(rs, off, 0u);
-#pragma unroll
-        for (int k = 1; k < EPL / 4; ++k) r[k] = zero16();
-        if constexpr (GATED) {
-#pragma unroll
-          for (int k = 0; k < EPL / 4; ++k) r2[k] = zero16();
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < EPL / 4; ++k)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          hv[ub][4 * k + j] = __int_as_float(r[k][j]);
-          if constexpr (GATED) uv[ub][4 * k + j] = __int_as_float(r2[k][j]);
-        }
-    }
-  };
-  load_b(lo + w);
-  load_a(lo + w);
-  // 1 / RMS (NormSiLU) and gate of each (expert in range, token row)
+    return;
+  }
+
+  // ---- routed: router logits of expert e for the 16 (padded) token rows;
+  // each lane sums x[c][k] W_r[k][e] over its fragment entries, waves over d
+  const float lam_e = a.lam[e], b_e = a.b_r[e];
   {
-    const __amdgpu_buffer_rsrc_t rsp = buf_rsrc(a.sspart), rg = buf_rsrc(a.g);
-    const float invF = 1.0f / (float)a.F;
-    for (int k = tid; k < nx * 16; k += NW * 64) {
-      const int e = s_ulist[i0 + (k >> 4)], t = k & 15;
-      float rinv = 0.f, gt = 0.f;
-      if (t < a.T) {
-        float part_ss[DEC_WGMAX];
+    const char* wr = a.Wr_p + frag_off(e >> 4, 0, nkb) + (size_t)((e & 15) + 16 * g) * 16;
+    const unsigned xoff = (unsigned)(((size_t)c * a.d + (size_t)DT::EPL * g) * sizeof(elem));
+    float zp = 0.f;
+    x_loaded = kb_hi - kb_lo <= U;
+    for (int kb0 = kb_lo; kb0 < kb_hi; kb0 += U) {
+      i32x4_t xv[U], wv[U];
 #pragma unroll
-        for (int wi = 0; wi < DEC_WGMAX; ++wi)   // issued together; slices past wg_per_e read 0
-          part_ss[wi] = ld_buf(rsp, wi < a.wg_per_e ? 4u * (unsigned)((e * a.wg_per_e + wi) * 16 + t) : OOB);
-        float ss = 0.f;
-#pragma unroll
-        for (int wi = 0; wi < DEC_WGMAX; ++wi) ss += part_ss[wi];
-        rinv = NO_RMS ? 1.0f : 1.0f / sqrtf(ss * invF + a.eps);
-        gt = ld_buf(rg, 4u * (unsigned)(t * a.E + e));   // 0 for an inactive pair
+      for (int u = 0; u < U; ++u) {
+        const int kb = kb0 + u < kb_hi ? kb0 + u : kb_hi - 1;
+        xv[u] = ld16_buf(rx, xoff, (unsigned)(kb * DT::KB * sizeof(elem)));
+        wv[u] = ld16(wr + (size_t)kb * FRAG_BYTES);
       }
-      s_rinv[k] = rinv;
-      s_gate[k] = gt;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (kb0 + u < kb_hi) {
+#pragma unroll
+          for (int j = 0; j < DT::EPL; ++j) zp += DT::lane_elem(xv[u], j) * DT::lane_elem(wv[u], j);
+        }
+        x0[u] = xv[u];
+      }
     }
+    zp += __shfl_xor(zp, 16);
+    zp += __shfl_xor(zp, 32);
+    if (g == 0) s_zr[w][c] = zp;
   }
   __syncthreads();
+  const unsigned ep = s_ep;
+  if (tid < 16) {
+    float zz = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < DNW; ++ww) zz += s_zr[ww][tid];
+    zz += b_e;
+    s_zr[0][tid] = zz;   // read below by row tid only
+    const bool act = tid < a.T && zz > 0.f && lam_e != 0.f;
+    s_act[tid] = act;
+    s_gate[tid] = act ? lam_e * zz : 0.f;
+  }
+  if (a.top_k > 0) {
+    // TopK: every expert's logits are needed before any expert can be
+    // skipped.  The expert's first slice publishes its logits; all routed
+    // workgroups read every expert's, and one wave per token selects.
+    __syncthreads();
+    if (slice == 0 && tid < 16) put_word(hw_z(a) + (size_t)e * 16 + tid, ep, s_zr[0][tid]);
+    constexpr int ZPT = 16 * 256 / DNT;   // words per thread (T x E <= 16 x 256)
+    u64 v[ZPT];
+    bool need[ZPT];
+    const u64* p[ZPT];
+#pragma unroll
+    for (int k = 0; k < ZPT; ++k) {
+      const int i = tid + DNT * k;
+      need[k] = i < a.T * a.E;
+      const int t = need[k] ? i / a.E : 0, ee = need[k] ? i % a.E : 0;
+      p[k] = hw_z(a) + (size_t)ee * 16 + t;
+      v[k] = need[k] ? get_word(p[k]) : 0ull;
+    }
+    wait_words<ZPT>(v, p, need, ep, a.err, 8u);
+#pragma unroll
+    for (int k = 0; k < ZPT; ++k) {
+      const int i = tid + DNT * k;
+      if (need[k]) s_zall[i / a.E][i % a.E] = word_val(v[k]);
+    }
+    __syncthreads();
+    for (int t = w; t < a.T; t += DNW) {
+      float zv[4];
+      bool sel[4];
+      float gate[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int ee = 64 * j + l;
+        zv[j] = ee < a.E ? s_zall[t][ee] : -__builtin_inff();
+      }
+      topk_wave<4>(zv, a.top_k, sel, gate);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (64 * j + l == e) {
+          s_act[t] = sel[j];
+          s_gate[t] = gate[j];
+        }
+    }
+  }
+  const bool any = __syncthreads_or(tid < 16 && s_act[tid] != 0) != 0;
+  if (slice == 0) {
+    if (tid < a.T) {
+      a.z[(size_t)tid * a.E + e] = s_zr[0][tid];
+      a.g[(size_t)tid * a.E + e] = s_gate[tid];
+      a.act8[(size_t)tid * a.E + e] = (unsigned char)(s_act[tid] != 0);
+    }
+    if (tid == 0) a.rflag[e] = any ? 2u : 1u;
+  }
+  if (!any) return;   // no token activated expert e: none of its weights are read
 
-  f32x4_t acc[DP];
+  const int gcol0 = slice * NCOL + col0;   // in F
+  // the mean term of this thread's entries, requested before the weights
+  u64 mv[CPT];
+  bool mneed[CPT];
+  const u64* mp[CPT];
 #pragma unroll
-  for (int p = 0; p < DP; ++p) acc[p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](int u0) {
+  for (int k = 0; k < CPT; ++k) {
+    mneed[k] = !NM && row < a.T;
+    mp[k] = hw_m(a) + (size_t)(row < a.T ? row : 0) * a.F + gcol0 + k;
+    mv[k] = mneed[k] ? get_word(mp[k]) : 0ull;
+  }
+  // the slice's up-projection (gated: the linear projection first, then the
+  // NormSiLU input)
+  const int p0 = slice * NP;
+  if constexpr (GT) {
+    up_stream<DT, NP>(rx, buf_rsrc(a.Wlin_p + (size_t)e * a.up_stride), p0, a.pF, nkb, kb_lo, kb_hi, a.d, accu,
+                      x_loaded, x0);
+    reduce_waves<NP, GT ? NCOL + 1 : 1>(s_red, accu, s_u);
+  }
+  up_stream<DT, NP>(rx, buf_rsrc(a.Wup_p + (size_t)e * a.up_stride), p0, a.pF, nkb, kb_lo, kb_hi, a.d, acc,
+                    x_loaded, x0);
+  reduce_waves<NP, NCOL + 1>(s_red, acc, s_h[0]);
+
+  // h - m, then the row's sum of squares over this slice
+  float hv[CPT];
+  if constexpr (!NM) wait_words<CPT>(mv, mp, mneed, ep, a.err, 2u);
 #pragma unroll
-    for (int ub = 0; ub < UB; ++ub) {
-      const int u = u0 + ub * NW;
-      __builtin_amdgcn_sched_barrier(0);   // one unit's temporaries at a time
-      if (u < hi) {
-        if (u < n_routed_units) {
-          // NormSiLU times the router gate (and, for gated experts, times
-          // x . W_up[e]), rounded once to the down-projection operand type
-          const int k = (u / a.nkb_F - i0) * 16 + c;
-          const float rinv = s_rinv[k], gt = s_gate[k];
+  for (int k = 0; k < CPT; ++k) hv[k] = s_h[0][row][col0 + k] - (mneed[k] ? word_val(mv[k]) : 0.f);
+  float ss = 0.f;
 #pragma unroll
-          for (int j = 0; j < EPL; ++j) {
-            if constexpr (GATED) hv[ub][j] = gt != 0.f ? silu_f(hv[ub][j] * rinv) * gt * uv[ub][j] : 0.f;
-            else hv[ub][j] = gt != 0.f ? silu_f(hv[ub][j] * rinv) * gt : 0.f;
+  for (int k = 0; k < CPT; ++k) ss += hv[k] * hv[k];
+#pragma unroll
+  for (int o = 16; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+  if (a.S > 1) {
+    // the other slices' sums of squares of the same rows, added in slice order
+    if (cq == 0) put_word(hw_ss(a) + ((size_t)e * a.S + slice) * 16 + row, ep, ss);
+    u64 v[1];
+    const bool need[1] = {cq < a.S};
+    const u64* const p[1] = {hw_ss(a) + ((size_t)e * a.S + (cq < a.S ? cq : 0)) * 16 + row};
+    v[0] = need[0] ? get_word(p[0]) : 0ull;
+    wait_words<1>(v, p, need, ep, a.err, 4u);
+    if (cq < a.S) s_ssx[row][cq] = word_val(v[0]);
+    __syncthreads();
+    ss = 0.f;
+    for (int q = 0; q < a.S; ++q) ss += s_ssx[row][q];
+  }
+  const float rinv = a.no_rms ? 1.0f : 1.0f / sqrtf(ss / (float)a.F + a.eps);
+  const float gt = s_gate[row];
+  if (row < a.T) {
+    float av[CPT];
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      av[k] = gt != 0.f ? silu_f(hv[k] * rinv) * gt : 0.f;
+      if constexpr (GT) av[k] *= s_u[row][col0 + k];
+    }
+    using DE = typename DN::elem;
+    DE* ar = (DE*)a.arow + ((size_t)e * 16 + row) * a.Fp + gcol0;
+    if constexpr (sizeof(DE) == 2) {
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) ar[k] = (DE)DN::bits(av[k]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) ar[k] = av[k];
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// Down-projection, one workgroup per 8 output columns.  Its reduction runs
+// over the shared expert's rows and the rows of every expert the batch
+// touched, in "column-pair" fragments: a 1 KiB fragment holds two k-blocks of
+// the 8 columns (columns 0-7 of the MFMA tile take the first k-block,
+// columns 8-15 the second), and the token operand holds the same two k-blocks
+// in its rows 0-7 and 8-15, so one 16x16 product covers both k-blocks and
+// the result's diagonal quadrants are the two halves of the sum.  TH token
+// halves of 8 rows (T <= 8: one; T <= 16: two).  Fragment ("slot") order:
+// the shared expert's, then each touched expert's in ascending expert order;
+// wave w takes slots w, w + 8, ...; the first two of each wave are issued
+// before the routing flags are read.
+template <class DT, int TH>
+__global__ void __launch_bounds__(DNT) k_dec_down(DecArgs a) {
+  using elem = typename DT::elem;
+  using DN = typename DT::Down;
+  using DE = typename DN::elem;
+  constexpr int SPW = 12;           // slots per wave per batch after the first two
+  __shared__ f32x4_t s_red[DNW * TH * 64];
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
+  const int r16 = l & 15, g = l >> 4, half = r16 >> 3;
+  const int cg = blockIdx.x;   // 8 output columns 8 cg .. 8 cg + 7
+  const int kps = a.kps, kpe = a.kpe;
+
+  // routing flags (first, so the shared slots' loads queue behind them)
+  unsigned rf[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = 64 * j + l;
+    rf[j] = a.rflag[e < a.E ? e : a.E - 1];
+  }
+  const __amdgpu_buffer_rsrc_t rs = buf_rsrc(a.srow, (unsigned)((size_t)a.T * a.Fsp * sizeof(elem)));
+  const unsigned tok_s = (unsigned)(((r16 & 7) * (size_t)a.Fsp + (size_t)DT::EPL * g) * sizeof(elem));
+  const unsigned tok_r = (unsigned)(((r16 & 7) * (size_t)a.Fp + (size_t)DN::EPL * g) * sizeof(DE));
+  auto load_shared = [&](int gi, i32x4_t& wv, i32x4_t (&av)[TH]) {
+    wv = ld16(a.Wsd8_p + ((size_t)cg * kps + gi) * FRAG_BYTES + (size_t)l * 16);
+    const unsigned ko = (unsigned)((2 * gi + half) * DT::KB * sizeof(elem));
+#pragma unroll
+    for (int th = 0; th < TH; ++th)
+      av[th] = ld16_buf(rs, tok_s + (unsigned)(8 * th * (size_t)a.Fsp * sizeof(elem)), ko);
+  };
+  i32x4_t wv0[2], av0[2][TH];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int gi = w + DNW * k;
+    load_shared(gi < kps ? gi : kps - 1, wv0[k], av0[k]);   // past the shared slots: a duplicate, not used
+  }
+  // the experts the batch touched, as bit words (every wave the same)
+  unsigned long long mk[4];
+  int n_act = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    mk[j] = __ballot(j < a.W && 64 * j + l < a.E && rf[j] == 2u);
+    n_act += __popcll(mk[j]);
+  }
+  // the r-th touched expert (ascending)
+  auto nth = [&](int r) -> int {
+    int base = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int pc = __popcll(mk[j]);
+      if (r < pc) {
+        unsigned long long m = mk[j];
+        int bit = 0;
+#pragma unroll
+        for (int s = 32; s >= 1; s >>= 1) {   // binary search of the r-th set bit
+          const unsigned long long lo = m & ((1ull << s) - 1ull);
+          const int plo = __popcll(lo);
+          if (r >= plo) {
+            r -= plo;
+            m >>= s;
+            bit += s;
+          } else {
+            m = lo;
           }
-          const i32x4_t af = DN::pack(hv[ub]);
+        }
+        return base + bit;
+      }
+      r -= pc;
+      base += 64;
+    }
+    return 0;
+  };
+  const int extra_shared = kps > 2 * DNW ? kps - 2 * DNW : 0;   // shared slots after the first 16
+  const int n_rest = extra_shared + n_act * kpe;
+
+  f32x4_t acc[TH];
 #pragma unroll
-          for (int p = 0; p < DP; ++p) DN::mma(acc[p], af, bfr[ub][p]);
+  for (int th = 0; th < TH; ++th) acc[th] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+    if (w + DNW * k < kps) {
+#pragma unroll
+      for (int th = 0; th < TH; ++th) DT::mma(acc[th], av0[k][th], wv0[k]);
+    }
+  for (int base = 0; base < n_rest; base += DNW * SPW) {
+    i32x4_t wv[SPW], av[SPW][TH];
+#pragma unroll
+    for (int k = 0; k < SPW; ++k) {
+      const int r = base + w + DNW * k;
+      if (r < n_rest) {
+        if (r < extra_shared) {
+          load_shared(2 * DNW + r, wv[k], av[k]);
         } else {
-          i32x4_t af;
+          const int q = r - extra_shared, kp = q % kpe;
+          const int e = nth(q / kpe);
+          wv[k] = ld16(a.Wdn8_p + (size_t)e * a.dn8_stride + ((size_t)cg * kpe + kp) * FRAG_BYTES + (size_t)l * 16);
+          const __amdgpu_buffer_rsrc_t ra =
+              buf_rsrc((const DE*)a.arow + (size_t)e * 16 * a.Fp, (unsigned)((size_t)a.T * a.Fp * sizeof(DE)));
+          const unsigned ko = (unsigned)((2 * kp + half) * DN::KB * sizeof(DE));
 #pragma unroll
-          for (int j = 0; j < 4; ++j) af[j] = __float_as_int(hv[ub][j]);
-#pragma unroll
-          for (int p = 0; p < DP; ++p) DT::mma(acc[p], af, bfr[ub][p]);
+          for (int th = 0; th < TH; ++th)
+            av[k][th] = ld16_buf(ra, tok_r + (unsigned)(8 * th * (size_t)a.Fp * sizeof(DE)), ko);
         }
       }
     }
-  };
-  compute(lo + w);
-  if constexpr (MULTI) {
-    for (int u0 = lo + w + NW * UB; u0 < hi; u0 += NW * UB) {
-      load_b(u0);
-      load_a(u0);
-      compute(u0);
-    }
-  }
-  // sum the waves' partial products, 4 panels at a time through LDS
-  float* mypart = a.part + ((size_t)q * a.n_groups + grp) * (16 * NCOL);
 #pragma unroll
-  for (int h = 0; h < DP / 4; ++h) {
+    for (int k = 0; k < SPW; ++k) {
+      const int r = base + w + DNW * k;
+      if (r < n_rest) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) s_red[w][p][l] = acc[4 * h + p];
-    __syncthreads();
-    for (int idx = tid; idx < 1024; idx += NW * 64) {
-      const int p = idx >> 8, ll = (idx >> 2) & 63, i = idx & 3;
-      const int row = 4 * (ll >> 4) + i, col = (4 * h + p) * 16 + (ll & 15);
-      if (row < a.T) {
-        float v = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) v += s_red[ww][p][ll][i];
-        mypart[row * NCOL + col] = v;
+        for (int th = 0; th < TH; ++th) {
+          if (r < extra_shared) DT::mma(acc[th], av[k][th], wv[k]);
+          else DN::mma(acc[th], av[k][th], wv[k]);
+        }
       }
     }
-    __syncthreads();
   }
-}
-
-// RMS-only NormSiLU of the shared expert (an ablation switch): one workgroup
-// per padded token row; s = SiLU(u / sqrt(mean_j u_j^2 + eps)) stored as the
-// down-projection operand fragments k_dec_up stores otherwise (rows past T: 0).
-template <class DT>
-__global__ void __launch_bounds__(256) k_dec_shared_rms(DecArgs a) {
-  using elem = typename DT::elem;
-  __shared__ float s_part[4];
-  const int r = blockIdx.x, tid = threadIdx.x;
-  const float* u = a.sraw + (size_t)r * a.Fs;
-  float ss = 0.f;
-  if (r < a.T)
-    for (int j = tid; j < a.Fs; j += 256) ss += u[j] * u[j];
+  // sum the waves' products, then the two diagonal quadrants: lane
+  // (col cc, group g < 2) holds C[4 g + i][cc] (first k-block of each
+  // pair), lane (cc + 8, g + 2) holds C[8 + 4 g + i][cc + 8] (second)
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
-  if ((tid & 63) == 0) s_part[tid >> 6] = ss;
+  for (int th = 0; th < TH; ++th) s_red[(w * TH + th) * 64 + l] = acc[th];
   __syncthreads();
-  const float tot = s_part[0] + s_part[1] + s_part[2] + s_part[3];
-  const float rinv = 1.0f / sqrtf(tot / (float)a.Fs + a.eps);
-  for (int j = tid; j < a.Fs; j += 256) {
-    const float v = r < a.T ? silu_f(u[j] * rinv) : 0.f;
-    *reinterpret_cast<elem*>(a.sactf + frag_elem_off<DT>(r, j)) = DT::from_f32(v);
+  for (int q = tid; q < 64 * TH; q += DNT) {
+    const int th = q >> 6, rem = q & 63, g2 = rem >> 5, cc = (rem >> 2) & 7, i = rem & 3;
+    const int t = 8 * th + 4 * g2 + i;
+    float v = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < DNW; ++ww) {
+      const f32x4_t p1 = s_red[(ww * TH + th) * 64 + cc + 16 * g2];
+      const f32x4_t p2 = s_red[(ww * TH + th) * 64 + cc + 8 + 16 * (g2 + 2)];
+      v += p1[i] + p2[i];
+    }
+    if (t < a.T) ((elem*)a.out)[(size_t)t * a.d + 8 * cg + cc] = DT::from_f32(v);
   }
 }
 
-// out[t][c] = sum over the Q reduction splits of the down kernel's partial
-// products, in split order (deterministic); 4 consecutive columns per thread.
-#ifndef DECO_DEC_SUM_NT
-#define DECO_DEC_SUM_NT 64
-#endif
-// threads per k_dec_sum workgroup: one wave, so T = 8 spreads its 4096
-// threads over 64 CUs (same-box A/B, c2: 0.3 us per step faster than 256)
-constexpr int DEC_SUM_NT = DECO_DEC_SUM_NT;
-template <class DT>
-__global__ void __launch_bounds__(DEC_SUM_NT) k_dec_sum(DecArgs a) {
-  constexpr int NCOL = DEC_DP * 16;
-  const int idx = blockIdx.x * DEC_SUM_NT + threadIdx.x;
-  if (idx * 4 >= a.T * a.d) return;
-  const int row = (idx * 4) / a.d, col = (idx * 4) % a.d;
-  const int grp = col / NCOL, cin = col % NCOL;
-  f32x4_t v = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int q0 = 0; q0 < a.Q; q0 += 16) {
-    f32x4_t pv[16];
-#pragma unroll
-    for (int qq = 0; qq < 16; ++qq)   // issued together
-      pv[qq] = q0 + qq < a.Q
-                   ? *reinterpret_cast<const f32x4_t*>(
-                         a.part + ((((size_t)(q0 + qq) * a.n_groups + grp) * 16 + row) * NCOL + cin))
-                   : f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int qq = 0; qq < 16; ++qq) v += pv[qq];
-  }
-  typename DT::elem* o = (typename DT::elem*)a.out + (size_t)row * a.d + col;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) o[j] = DT::from_f32(v[j]);
-}
-
-template <class DT>
-void (*up_kernel(int var))(DecArgs) {
+template <class DT, int NP>
+void (*up_kernel_np(int var))(DecArgs) {
   switch (var) {
-    case 0: return k_dec_up<DT, DEC_NW, DEC_NP, 0>;
-    case 1: return k_dec_up<DT, DEC_NW, DEC_NP, 1>;
-    case 2: return k_dec_up<DT, DEC_NW, DEC_NP, 2>;
-    case 3: return k_dec_up<DT, DEC_NW, DEC_NP, 3>;
-    case 4: return k_dec_up<DT, DEC_NW, DEC_NP, 4>;
-    case 5: return k_dec_up<DT, DEC_NW, DEC_NP, 5>;
-    case 6: return k_dec_up<DT, DEC_NW, DEC_NP, 6>;
-    default: return k_dec_up<DT, DEC_NW, DEC_NP, 7>;
+    case 0: return k_dec_up<DT, NP, 0>;
+    case 1: return k_dec_up<DT, NP, 1>;
+    case 2: return k_dec_up<DT, NP, 2>;
+    case 3: return k_dec_up<DT, NP, 3>;
+    case 4: return k_dec_up<DT, NP, 4>;
+    case 5: return k_dec_up<DT, NP, 5>;
+    case 6: return k_dec_up<DT, NP, 6>;
+    default: return k_dec_up<DT, NP, 7>;
   }
 }
-
-template <class DT, bool MULTI>
-void (*down_kernel_m(bool gated, bool no_rms))(DecArgs) {
-  return gated ? (no_rms ? k_dec_down<DT, DEC_NW, MULTI, true, true> : k_dec_down<DT, DEC_NW, MULTI, true, false>)
-               : (no_rms ? k_dec_down<DT, DEC_NW, MULTI, false, true> : k_dec_down<DT, DEC_NW, MULTI, false, false>);
-}
 template <class DT>
-void (*down_kernel(bool multi, bool gated, bool no_rms))(DecArgs) {
-  return multi ? down_kernel_m<DT, true>(gated, no_rms) : down_kernel_m<DT, false>(gated, no_rms);
+void (*up_kernel(int np, int var))(DecArgs) {
+  return np == 4 ? up_kernel_np<DT, 4>(var) : up_kernel_np<DT, 2>(var);
 }
 
-template <class DT>
-hipError_t decode(const deco_moe_layer* L, const void* x, int T, void* out, hipStream_t s) {
+int dec_variant(const deco_moe_layer* L) {
+  return (L->gated ? DV_GATED : 0) | ((L->cfg.normsilu & DECO_NORMSILU_NO_MEAN) ? DV_NO_MEAN : 0) |
+         (L->cfg.shared_rms ? DV_SHARED_RMS : 0);
+}
+
+DecArgs dec_args(const deco_moe_layer* L, const void* x, int T, void* out) {
   DecArgs a;
+  memset(&a, 0, sizeof(a));
   a.x = x;
   a.out = out;
   a.T = T;
@@ -672,103 +644,132 @@ hipError_t decode(const deco_moe_layer* L, const void* x, int T, void* out, hipS
   a.E = L->E;
   a.F = L->F;
   a.Fs = L->Fs;
+  a.W = L->W;
   a.nkb_d = L->nkb_d;
-  a.nkb_F = L->nkb_F;
-  a.nkb_Fs = L->nkb_Fs;
+  a.S = L->dec_S;
+  a.n_mean = L->dec_n_mean;
+  a.n_sh = L->dec_n_sh;
+  a.nsub = L->dec_nsub;
+  a.n_shs = L->dec_n_shs;
   a.pF = L->pF;
   a.pFs = L->pFs;
-  a.pD = L->pD;
-  a.n_groups = L->n_groups;
-  a.Q = L->dec_q;
-  a.n_shared = L->pFs / DEC_NP;
-  a.wg_per_e = L->pF / DEC_NP;
   a.top_k = L->cfg.top_k;
-  a.gated = L->gated;
-  a.no_mean = (L->cfg.normsilu & DECO_NORMSILU_NO_MEAN) != 0;
   a.no_rms = (L->cfg.normsilu & DECO_NORMSILU_NO_RMS) != 0;
-  a.sraw = L->cfg.shared_rms ? L->sraw : nullptr;
-  a.Wlin_p = L->Wlin_p;
-  a.ubuf = L->ubuf;
-  a.pR = L->pR;
-  a.W = L->W;
-  a.mask = L->mask;
+  a.eps = L->cfg.rms_eps;
   a.Wr_p = L->Wr_p;
   a.Wup_p = L->Wup_p;
+  a.Wlin_p = L->Wlin_p;
   a.Wbar_p = L->Wbar_p;
-  a.Wdn_p = L->Wdn16_p;   // fp16 copy for bf16 layers, W_down itself for fp32 layers
   a.Wsu_p = L->Wsu_p;
-  a.Wsd_p = L->Wsd_p;
+  a.Wdn8_p = L->Wdn8_p;
+  a.Wsd8_p = L->Wsd8_p;
   a.up_stride = L->up_stride;
-  a.dn_stride = L->dn_stride;
+  a.dn8_stride = L->dn8_stride;
   a.b_r = L->b_r;
   a.lam = L->lam;
-  a.eps = L->cfg.rms_eps;
   a.z = L->z;
   a.g = L->g;
-  a.hbuf = L->hbuf;
-  a.sspart = L->sspart;
-  a.sactf = L->sactf;
+  a.act8 = L->act8;
   a.rflag = L->rflag;
-  a.part = L->part;
-  hipError_t err = hipSuccess;
-  if (a.top_k > 0) {
-    err = deco_host::launch(deco_host::KS_DEC_TOPK, k_dec_topk<DT, 16>, dim3(1), dim3(16 * 64), s, a);
-    if (err != hipSuccess) return err;
-  }
-  const unsigned grid_up = (unsigned)(a.n_shared + L->E * (a.wg_per_e << a.gated));
-  const int var = (a.gated ? DV_GATED : 0) | (a.no_mean ? DV_NO_MEAN : 0) | (a.sraw ? DV_SHARED_RMS : 0);
-  void (*up)(DecArgs) = up_kernel<DT>(var);
-  err = deco_host::launch(deco_host::KS_DEC_UP, up, dim3(grid_up),
-                                     dim3(DEC_NW * 64), s, a);
+  a.hw = (u64*)L->hwords;
+  a.ctr = L->dec_ctr;
+  a.arow = L->arow;
+  a.srow = L->srow;
+  a.Fp = L->dec_Fp;
+  a.Fsp = L->dec_Fsp;
+  a.kpe = L->dec_kpe;
+  a.kps = L->dec_kps;
+  a.err = L->dec_err;
+  return a;
+}
+
+template <class DT>
+hipError_t decode(const deco_moe_layer* L, const void* x, int T, void* out, hipStream_t s) {
+  const DecArgs a = dec_args(L, x, T, out);
+  hipError_t err = deco_host::launch(deco_host::KS_DEC_UP, up_kernel<DT>(L->dec_np, dec_variant(L)),
+                                     dim3((unsigned)L->dec_grid_up), dim3(DNT), s, a);
   if (err != hipSuccess) return err;
-  if (a.sraw) {
-    err = deco_host::launch(deco_host::KS_DEC_UP, k_dec_shared_rms<DT>, dim3(16), dim3(256), s, a);
-    if (err != hipSuccess) return err;
-  }
-  const unsigned grid_dn = (unsigned)(L->n_groups * L->dec_q);
-  void (*down)(DecArgs) = down_kernel<DT>(L->dec_multi != 0, a.gated != 0, a.no_rms != 0);
-  err = deco_host::launch(deco_host::KS_DEC_DOWN, down, dim3(grid_dn), dim3(DEC_NW * 64), s, a);
-  if (err != hipSuccess) return err;
-  const unsigned grid_sum = (unsigned)((T * L->d / 4 + DEC_SUM_NT - 1) / DEC_SUM_NT);
-  err = deco_host::launch(deco_host::KS_DEC_SUM, k_dec_sum<DT>, dim3(grid_sum), dim3(DEC_SUM_NT), s, a);
+  void (*down)(DecArgs) = T <= 8 ? k_dec_down<DT, 1> : k_dec_down<DT, 2>;
+  err = deco_host::launch(deco_host::KS_DEC_DOWN, down, dim3((unsigned)(L->d / 8)), dim3(DNT), s, a);
   if (err != hipSuccess) return err;
   return hipGetLastError();
+}
+
+// the routing masks of the last decode call, as bit words
+__global__ void __launch_bounds__(256) k_dec_mask(const unsigned char* __restrict__ act8, int T, int E, int W,
+                                                  uint64_t* __restrict__ mask) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= T * W) return;
+  const int t = idx / W, wi = idx % W;
+  uint64_t word = 0;
+  for (int b = 0; b < 64; ++b) {
+    const int e = wi * 64 + b;
+    if (e < E && act8[(size_t)t * E + e]) word |= 1ull << b;
+  }
+  mask[idx] = word;
 }
 
 }  // namespace
 
 namespace deco_host {
 
-// Decode launch shape: the down kernel splits its reduction Q ways so that
-// about DECO_DEC_DOWN_WG workgroups stream the down-projection weights.
-#ifndef DECO_DEC_DOWN_WG
-#define DECO_DEC_DOWN_WG 256
-#endif
+// Decode launch shape, chosen at load (sizes before the workspace is carved,
+// the residency check once the kernels' occupancy is known).  Routed experts
+// are cut into column slices of 32 columns (S = F / 32) when every routed
+// slice, mean-term slice and group of shared slices fits on the device at
+// once (one workgroup per CU), else of 64 columns; the mean term is cut like
+// the routed experts (one mean workgroup per routed slice position) and the
+// shared expert into slices of the same width, nsub of them per workgroup
+// (the smallest nsub <= 4 that lets the whole grid fit).  The waits of the up
+// kernel need every group of workgroups that wait on each other (an
+// expert's slices; with the RMS-only shared expert, all shared workgroups;
+// with TopK routing, the whole grid) to fit on the device at once.
+static void dec_sizes(deco_moe_layer* L, int np, int cap) {
+  const int ncol = 16 * np;
+  L->dec_np = np;
+  L->dec_S = L->F / ncol;
+  L->dec_n_mean = (L->cfg.normsilu & DECO_NORMSILU_NO_MEAN) ? 0 : L->dec_S;
+  L->dec_n_shs = (L->Fs + ncol - 1) / ncol;
+  int nsub = 1;
+  while (nsub < NSUB_MAX && L->dec_n_mean + (L->dec_n_shs + nsub - 1) / nsub + L->E * L->dec_S > cap) nsub *= 2;
+  L->dec_nsub = nsub;
+  L->dec_n_sh = (L->dec_n_shs + nsub - 1) / nsub;
+  L->dec_grid_up = L->dec_n_mean + L->dec_n_sh + L->E * L->dec_S;
+}
+
+void plan_decode_sizes(deco_moe_layer* L, int n_cu) {
+  dec_sizes(L, 2, n_cu);
+  if (L->F >= 64 && L->dec_grid_up > n_cu) dec_sizes(L, 4, n_cu);
+  const int kp_rows = 2 * L->KB;   // rows of one column-pair fragment
+  L->dec_Fp = (L->F + kp_rows - 1) / kp_rows * kp_rows;
+  L->dec_Fsp = (L->Fs + kp_rows - 1) / kp_rows * kp_rows;
+  L->dec_kpe = L->dec_Fp / kp_rows;
+  L->dec_kps = L->dec_Fsp / kp_rows;
+  L->n_hwords = 16 * L->F + L->E * L->dec_S * 16 + L->E * 16 + L->dec_n_sh * 16;
+}
+
 hipError_t plan_decode(deco_moe_layer* L) {
-  int q = (DECO_DEC_DOWN_WG + L->n_groups - 1) / L->n_groups;
-  q = q < 1 ? 1 : (q > DEC_QMAX ? DEC_QMAX : q);
-  // With every expert active the reduction has C units.  A down workgroup
-  // takes ceil(C / q) of them: one chunk of DEC_UB units per wave when that
-  // fits (the kernel without a reload loop, which needs fewer registers), and
-  // at most DEC_XMAX experts (1/RMS and gates in LDS; a range of n units spans
-  // at most n / nkb_F + 2 experts).
-  const int C = L->E * L->nkb_F + L->nkb_Fs;
-  auto span = [&](int qq) { return (C + qq - 1) / qq; };
-  auto xmax = [&](int qq) {
-    const int x = span(qq) / L->nkb_F + 2;
-    return x < L->E ? x : L->E;
-  };
-  while (q < DEC_QMAX && (span(q) > DEC_NW * DEC_UB || xmax(q) > DEC_XMAX)) ++q;
-  if (xmax(q) > DEC_XMAX || L->pF / DEC_NP > DEC_WGMAX) return hipErrorInvalidValue;
-  L->dec_q = q;
-  L->dec_multi = span(q) > DEC_NW * DEC_UB;
-  L->dec_ok = 1;
+  void (*up)(DecArgs) = L->cfg.dtype == DECO_DT_BF16 ? up_kernel<BF16>(L->dec_np, dec_variant(L))
+                                                     : up_kernel<F32>(L->dec_np, dec_variant(L));
+  int occ = 0;
+  hipError_t err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, up, DNT, 0);
+  if (err != hipSuccess) return err;
+  const long long cap = (long long)(occ < 1 ? 0 : occ) * L->n_cu;
+  bool ok = cap >= L->dec_S && cap >= L->dec_n_mean + (L->cfg.shared_rms ? L->dec_n_sh : 0);
+  if (L->cfg.top_k > 0) ok = ok && cap >= L->dec_grid_up;
+  L->dec_ok = ok ? 1 : 0;
   return hipSuccess;
 }
 
 hipError_t launch_decode(const deco_moe_layer* L, const void* x, int T, void* out, hipStream_t s) {
   if (L->cfg.dtype == DECO_DT_BF16) return decode<BF16>(L, x, T, out, s);
   return decode<F32>(L, x, T, out, s);
+}
+
+hipError_t launch_dec_mask(const deco_moe_layer* L, int T, uint64_t* mask, hipStream_t s) {
+  const int n = T * L->W;
+  k_dec_mask<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(L->act8, T, L->E, L->W, mask);
+  return hipGetLastError();
 }
 
 }  // namespace deco_host

@@ -27,6 +27,13 @@ int validate_cfg(const deco_moe_config* c) {
   if (c->d_ff != 32 && c->d_ff != 64 && c->d_ff != 128 && c->d_ff != 256) return DECO_ERR_UNSUPPORTED;
   if (c->d_ff_shared % 32 != 0 || c->d_ff_shared > 16384) return DECO_ERR_UNSUPPORTED;
   if (c->max_tokens > (1 << 20)) return DECO_ERR_UNSUPPORTED;
+  // every packed matrix stays below 2 GiB (32-bit buffer offsets)
+  {
+    const size_t esz = c->dtype == DECO_DT_BF16 ? 2 : 4;
+    const size_t lim = (size_t)1 << 31;
+    if ((size_t)c->d_model * c->d_ff_shared * esz >= lim || (size_t)c->d_model * c->d_ff * esz >= lim)
+      return DECO_ERR_UNSUPPORTED;
+  }
   if (c->backward != 0 && c->backward != 1) return DECO_ERR_INVALID_ARG;
   if (c->normsilu < 0 || c->normsilu > 3 || (c->scalar_lambda != 0 && c->scalar_lambda != 1) ||
       (c->shared_rms != 0 && c->shared_rms != 1))
@@ -56,8 +63,6 @@ void derive(deco_moe_layer* L) {
   L->pD = L->d / 16;
   L->pFs = L->Fs / 16;
   L->W = (L->E + 63) / 64;
-  L->n_groups = (L->pD + 7) / 8;   // 128-column groups of the decode down role
-  L->dec_q = 64;   // upper bound for the workspace; the decode plan picks the value at load
   L->pre_grid = 1024;
   auto r64 = [](int v) { return (v + 63) / 64 * 64; };
   L->Fp = r64(L->F);
@@ -119,8 +124,6 @@ const char* kernel_slot_name(int slot) {
     case KS_PACK: return "load_pack";
     case KS_DEC_UP: return "k_dec_up";
     case KS_DEC_DOWN: return "k_dec_down";
-    case KS_DEC_SUM: return "k_dec_sum";
-    case KS_DEC_TOPK: return "k_dec_topk";
     case KS_PRE_TOPK: return "k_pre_topk";
     case KS_PRE_ROUTER_SHARED: return "k_pre_router_shared";
     case KS_PRE_DISPATCH: return "k_pre_dispatch";
@@ -196,10 +199,13 @@ static int load_layer(const deco_moe_config* cfg, const void* W_r, const float* 
   L->cfg = *cfg;
   L->gated = gated;
   derive(L);
-  if (hipGetDevice(&L->device) != hipSuccess) {
+  int n_cu = 0;
+  if (hipGetDevice(&L->device) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, L->device) != hipSuccess) {
     delete L;
     return DECO_ERR_HIP;
   }
+  deco_host::plan_decode_sizes(L, n_cu < 1 ? 1 : n_cu);
   const size_t KBy = 1024;
   const int E = L->E;
   // packed weights
@@ -214,6 +220,9 @@ static int load_layer(const deco_moe_config* cfg, const void* W_r, const float* 
   size_t o_dn16 = L->cfg.dtype == DECO_DT_BF16 ? w.take(L->dn_stride * E) : o_dn;
   size_t o_su = w.take((size_t)L->pFs * L->nkb_d * KBy);
   size_t o_sd = w.take((size_t)L->pD * L->nkb_Fs * KBy);
+  L->dn8_stride = (size_t)(L->d / 8) * L->dec_kpe * KBy;
+  size_t o_dn8 = w.take(L->dn8_stride * E);
+  size_t o_sd8 = w.take((size_t)(L->d / 8) * L->dec_kps * KBy);
   size_t o_b = w.take(sizeof(float) * E);
   size_t o_l = w.take(sizeof(float) * E);
   size_t o_wb = w.take(sizeof(float) * (size_t)L->d * L->F);
@@ -231,13 +240,16 @@ static int load_layer(const deco_moe_config* cfg, const void* W_r, const float* 
   size_t o_g = k.take(sizeof(float) * Tcap * E);
   size_t o_m = k.take(sizeof(uint64_t) * Tcap * L->W);
   size_t o_mb = k.take(sizeof(float) * Tcap * L->F);
-  size_t o_h = k.take(sizeof(float) * (size_t)E * 16 * L->F);
-  size_t o_u = L->gated ? k.take(sizeof(float) * (size_t)E * 16 * L->F) : 0;
-  size_t o_ss = k.take(sizeof(float) * (size_t)E * 16 * 16);
-  size_t o_sf = k.take((size_t)L->nkb_Fs * KBy);
+  // decode hand-offs and activations (zeroed at load: flags start clear, and
+  // the activation rows' padding columns must read as zero)
   size_t o_rf = k.take(sizeof(unsigned) * E);
   size_t o_er = k.take(sizeof(unsigned));
-  size_t o_pt = k.take(sizeof(float) * (size_t)L->dec_q * L->n_groups * 16 * 128);
+  size_t o_a8 = k.take((size_t)16 * E);
+  size_t o_hw = k.take(sizeof(uint64_t) * (size_t)L->n_hwords);
+  size_t o_ct = k.take(sizeof(unsigned) * (size_t)L->dec_grid_up);
+  const size_t dn_esz = L->esz == 2 ? 2 : 4;   // fp16 operands for bf16 layers
+  size_t o_ar = k.take(dn_esz * (size_t)E * 16 * L->dec_Fp);
+  size_t o_sr2 = k.take((size_t)L->esz * 16 * L->dec_Fsp);
   size_t o_to = k.take(sizeof(int) * (Tcap + 1));
   size_t o_ec = k.take(sizeof(int) * E);
   size_t o_lt = k.take(sizeof(int) * (size_t)E * Tcap);
@@ -283,6 +295,8 @@ static int load_layer(const deco_moe_config* cfg, const void* W_r, const float* 
   L->Wdn16_p = L->wmem + o_dn16;
   L->Wsu_p = L->wmem + o_su;
   L->Wsd_p = L->wmem + o_sd;
+  L->Wdn8_p = L->wmem + o_dn8;
+  L->Wsd8_p = L->wmem + o_sd8;
   L->b_r = (float*)(L->wmem + o_b);
   L->lam = (float*)(L->wmem + o_l);
   L->wbar = (float*)(L->wmem + o_wb);
@@ -297,13 +311,13 @@ static int load_layer(const deco_moe_config* cfg, const void* W_r, const float* 
   L->g = (float*)(L->ws + o_g);
   L->mask = (uint64_t*)(L->ws + o_m);
   L->mbuf = (float*)(L->ws + o_mb);
-  L->hbuf = (float*)(L->ws + o_h);
-  L->ubuf = L->gated ? (float*)(L->ws + o_u) : nullptr;
-  L->sspart = (float*)(L->ws + o_ss);
-  L->sactf = L->ws + o_sf;
   L->rflag = (unsigned*)(L->ws + o_rf);
   L->dec_err = (unsigned*)(L->ws + o_er);
-  L->part = (float*)(L->ws + o_pt);
+  L->act8 = (unsigned char*)(L->ws + o_a8);
+  L->hwords = L->ws + o_hw;
+  L->dec_ctr = (unsigned*)(L->ws + o_ct);
+  L->arow = L->ws + o_ar;
+  L->srow = L->ws + o_sr2;
   L->tok_off = (int*)(L->ws + o_to);
   L->ecnt = (int*)(L->ws + o_ec);
   L->list_tok = (int*)(L->ws + o_lt);
@@ -344,8 +358,8 @@ static int load_layer(const deco_moe_config* cfg, const void* W_r, const float* 
       err = hipMemcpyAsync(L->lam, lambda, sizeof(float) * E, hipMemcpyDeviceToDevice, s);
   }
   if (err == hipSuccess) err = deco_host::launch_pack_all(L, W_r, W_norm, W_lin, W_down, Ws_up, Ws_down, s);
+  if (err == hipSuccess) err = deco_host::plan_prefill(L);   // also reads the CU count
   if (err == hipSuccess) err = deco_host::plan_decode(L);
-  if (err == hipSuccess) err = deco_host::plan_prefill(L);
   if (err == hipSuccess && bwd) err = deco_host::plan_backward(L);
   if (err == hipSuccess) err = hipStreamSynchronize(s);
   if (err != hipSuccess) {
@@ -389,6 +403,8 @@ int deco_moe_forward_path(const deco_moe_layer* L, const void* x, int64_t T, voi
   hipStream_t s = (hipStream_t)stream;
   hipError_t err = path == DECO_PATH_DECODE ? deco_host::launch_decode(L, x, (int)T, out, s)
                                             : deco_host::launch_prefill(L, x, (int)T, out, s);
+  // which path's routing state deco_moe_copy_routing returns
+  const_cast<deco_moe_layer*>(L)->last_path = path;
   return err == hipSuccess ? DECO_OK : DECO_ERR_HIP;
 }
 
@@ -400,11 +416,12 @@ int deco_moe_copy_routing(const deco_moe_layer* L, int64_t T, uint64_t* mask, fl
   if (!L || T < 0 || T > L->maxT || !mask) return DECO_ERR_INVALID_ARG;
   if (T == 0) return DECO_OK;
   hipStream_t s = (hipStream_t)stream;
-  // ReLU routing: the mask follows from the logits and lambda; TopK: the
-  // routing kernels stored it
-  hipError_t err = L->cfg.top_k > 0
-      ? hipMemcpyAsync(mask, L->mask, sizeof(uint64_t) * (size_t)T * L->W, hipMemcpyDeviceToDevice, s)
-      : deco_host::launch_copy_mask(L, (int)T, mask, s);
+  // the decisions the kernels of the last call used: the decode up kernel's
+  // per-expert decisions (packed into words here), or the mask words the
+  // prefill dispatch read
+  hipError_t err = L->last_path == DECO_PATH_DECODE
+      ? deco_host::launch_dec_mask(L, (int)T, mask, s)
+      : hipMemcpyAsync(mask, L->mask, sizeof(uint64_t) * (size_t)T * L->W, hipMemcpyDeviceToDevice, s);
   if (err == hipSuccess && logits)
     err = hipMemcpyAsync(logits, L->z, sizeof(float) * (size_t)T * L->E, hipMemcpyDeviceToDevice, s);
   return err == hipSuccess ? DECO_OK : DECO_ERR_HIP;

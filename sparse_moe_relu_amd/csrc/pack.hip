@@ -61,6 +61,33 @@ __global__ void __launch_bounds__(256) k_pack(const SRC* __restrict__ src, size_
   st16(dst + (size_t)b * dst_bstride + frag_off(p, kb_off + kb, nkb_tot) + (size_t)l * 16, DT::pack(f));
 }
 
+// Column-pair packing of the K x N row-major matrix src (`batch` matrices
+// `src_bstride` elements apart) for the decode down-projection: fragment
+// (column group cg of 8 columns, k-pair kp) holds, in lane l (c = l & 15,
+// g = l >> 4), rows (2 kp + c / 8) * KB + frag_k(g, j) of column 8 cg + c % 8,
+// so MFMA tile columns 0-7 take the first k-block of the pair and columns
+// 8-15 the second.  Layout [cg][kp], entries outside K x N zero.
+template <class DT, class SRC>
+__global__ void __launch_bounds__(256) k_pack_pair(const SRC* __restrict__ src, size_t src_bstride, int K, int N,
+                                                   int ncg, int nkp, char* __restrict__ dst, size_t dst_bstride) {
+  const int b = blockIdx.y;
+  const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= (size_t)ncg * nkp * WAVE) return;
+  const int l = (int)(t % WAVE);
+  const int kp = (int)((t / WAVE) % nkp);
+  const int cg = (int)(t / ((size_t)WAVE * nkp));
+  const int g = l >> 4, c = l & 15;
+  const int n = 8 * cg + (c & 7);
+  const SRC* s = src + (size_t)b * src_bstride;
+  float f[DT::EPL];
+#pragma unroll
+  for (int j = 0; j < DT::EPL; ++j) {
+    const int k = (2 * kp + (c >> 3)) * DT::KB + DT::frag_k(g, j);
+    f[j] = (k < K && n < N) ? src_f32(s, (size_t)k * N + n) : 0.f;
+  }
+  st16(dst + (size_t)b * dst_bstride + ((size_t)cg * nkp + kp) * FRAG_BYTES + (size_t)l * 16, DT::pack(f));
+}
+
 dim3 pack_grid(int P, int nkb, int batch) {
   size_t thr = (size_t)P * nkb * WAVE;
   return dim3((unsigned)((thr + 255) / 256), (unsigned)batch);
@@ -108,6 +135,16 @@ hipError_t pack_all(deco_moe_layer* L, const void* W_r, const void* W_up, const 
   // shared up: K = d, N = Fs; shared down: K = Fs, N = d
   pack_rm<DT, E_t>(Ws_up, 0, d, Fs, L->pFs, L->nkb_d, L->Wsu_p, 0, 1, s);
   pack_rm<DT, E_t>(Ws_down, 0, Fs, d, L->pD, L->nkb_Fs, L->Wsd_p, 0, 1, s);
+  // the decode down-projection's column-pair copies: routed W_down in the
+  // down operand type, Ws_down in the layer dtype
+  {
+    const int ncg = d / 8;
+    const size_t thr_r = (size_t)ncg * L->dec_kpe * WAVE, thr_s = (size_t)ncg * L->dec_kps * WAVE;
+    k_pack_pair<DN, E_t><<<dim3((unsigned)((thr_r + 255) / 256), (unsigned)E), 256, 0, s>>>(
+        (const E_t*)W_down, dF, F, d, ncg, L->dec_kpe, L->Wdn8_p, L->dn8_stride);
+    k_pack_pair<DT, E_t><<<dim3((unsigned)((thr_s + 255) / 256), 1u), 256, 0, s>>>(
+        (const E_t*)Ws_down, 0, Fs, d, ncg, L->dec_kps, L->Wsd8_p, 0);
+  }
   if (L->cfg.backward) {
     // W_down[e]^T: K = d, N = F (the ungated output gradient times W_down^T)
     pack_tr<DT, E_t>(W_down, dF, d, F, L->pF, L->nkb_d, 0, L->nkb_d, L->WdnT_p, L->up_stride, E, s);

@@ -97,10 +97,4 @@ hipError_t plan_prefill(deco_moe_layer* L) {
   return hipSuccess;
 }
 
-hipError_t launch_copy_mask(const deco_moe_layer* L, int T, uint64_t* mask, hipStream_t s) {
-  const int n = T * L->W;
-  k_copy_mask<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(L->z, L->lam, T, L->E, L->W, mask);
-  return hipGetLastError();
-}
-
 }  // namespace deco_host

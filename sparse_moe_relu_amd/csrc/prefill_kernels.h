@@ -853,20 +853,6 @@ __global__ void __launch_bounds__(256) k_pre_combine(PreArgs a) {
   }
 }
 
-// --------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) k_copy_mask(const float* __restrict__ z, const float* __restrict__ lam,
-                                                   int T, int E, int W, uint64_t* __restrict__ mask) {
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= T * W) return;
-  const int t = idx / W, wi = idx % W;
-  uint64_t word = 0;
-  for (int b = 0; b < 64; ++b) {
-    const int e = wi * 64 + b;
-    if (e < E && z[(size_t)t * E + e] > 0.f && lam[e] != 0.f) word |= 1ull << b;
-  }
-  mask[idx] = word;
-}
-
 int round4(int v) { return (v + 3) / 4 * 4; }
 
 // launch arguments shared by the forward and backward launchers
