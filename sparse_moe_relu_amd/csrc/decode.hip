@@ -464,150 +464,179 @@ __global__ void __launch_bounds__(DNT) k_dec_up(DecArgs a) {
 }
 
 // --------------------------------------------------------------------------
-// Down-projection, one workgroup per 8 output columns.  Its reduction runs
-// over the shared expert's rows and the rows of every expert the batch
-// touched, in "column-pair" fragments: a 1 KiB fragment holds two k-blocks of
-// the 8 columns (columns 0-7 of the MFMA tile take the first k-block,
+// Down-projection, one workgroup per CG groups of 8 output columns.  Its
+// reduction runs over the shared expert's rows and the rows of every expert
+// the batch touched, in "column-pair" fragments: a 1 KiB fragment holds two
+// k-blocks of 8 columns (columns 0-7 of the MFMA tile take the first k-block,
 // columns 8-15 the second), and the token operand holds the same two k-blocks
-// in its rows 0-7 and 8-15, so one 16x16 product covers both k-blocks and
-// the result's diagonal quadrants are the two halves of the sum.  TH token
-// halves of 8 rows (T <= 8: one; T <= 16: two).  Fragment ("slot") order:
-// the shared expert's, then each touched expert's in ascending expert order;
-// wave w takes slots w, w + 8, ...; the first two of each wave are issued
-// before the routing flags are read.
-template <class DT, int TH>
+// in its rows 0-7 and 8-15, so one 16x16 product covers both k-blocks and the
+// result's diagonal quadrants are the two halves of the sum.  TH token halves
+// of 8 rows (T <= 8: one; T <= 16: two); the CG column groups share each
+// token fragment.  Fragment ("slot") order: the shared expert's, then each
+// touched expert's in ascending expert order; wave w takes slots w, w + 8, ...
+// Every batch of loads is issued without a branch: a slot past the end gets
+// a vector offset past its buffer's range, which loads zeros without a memory
+// access, so its product adds nothing.
+template <class DT, int TH, int CG>
 __global__ void __launch_bounds__(DNT) k_dec_down(DecArgs a) {
   using elem = typename DT::elem;
   using DN = typename DT::Down;
   using DE = typename DN::elem;
-  constexpr int SPW = 12;           // slots per wave per batch after the first two
-  __shared__ f32x4_t s_red[DNW * TH * 64];
+  constexpr int SB = 4;                                   // shared slots per wave, issued first
+  constexpr int SPW = (TH == 2 && CG == 2) ? 8 : 12;      // expert slots per wave per batch
+  constexpr unsigned OOR = 0x40000000u;                   // past every buffer range used here
+  __shared__ f32x4_t s_red[DNW][CG][TH][64];
+  __shared__ int s_list[DNW][256];
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
   const int r16 = l & 15, g = l >> 4, half = r16 >> 3;
-  const int cg = blockIdx.x;   // 8 output columns 8 cg .. 8 cg + 7
+  const int cg0 = blockIdx.x * CG;   // first of the workgroup's column groups
   const int kps = a.kps, kpe = a.kpe;
 
-  // routing flags (first, so the shared slots' loads queue behind them)
+  // routing flags first, so the shared slots' loads queue behind them
   unsigned rf[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int e = 64 * j + l;
     rf[j] = a.rflag[e < a.E ? e : a.E - 1];
   }
+  // the lane's token row (r16 & 7) and k offset; rows 8-15 of the tile take
+  // the second k-block of the pair (in the vector offset, so the scalar
+  // offset stays uniform)
+  const unsigned tok_s = (unsigned)(((r16 & 7) * (size_t)a.Fsp + (size_t)half * DT::KB + (size_t)DT::EPL * g) *
+                                    sizeof(elem));
+  const unsigned tok_r = (unsigned)(((r16 & 7) * (size_t)a.Fp + (size_t)half * DN::KB + (size_t)DN::EPL * g) *
+                                    sizeof(DE));
+  const unsigned th_s = (unsigned)(8 * (size_t)a.Fsp * sizeof(elem));
+  const unsigned th_r = (unsigned)(8 * (size_t)a.Fp * sizeof(DE));
   const __amdgpu_buffer_rsrc_t rs = buf_rsrc(a.srow, (unsigned)((size_t)a.T * a.Fsp * sizeof(elem)));
-  const unsigned tok_s = (unsigned)(((r16 & 7) * (size_t)a.Fsp + (size_t)DT::EPL * g) * sizeof(elem));
-  const unsigned tok_r = (unsigned)(((r16 & 7) * (size_t)a.Fp + (size_t)DN::EPL * g) * sizeof(DE));
-  auto load_shared = [&](int gi, i32x4_t& wv, i32x4_t (&av)[TH]) {
-    wv = ld16(a.Wsd8_p + ((size_t)cg * kps + gi) * FRAG_BYTES + (size_t)l * 16);
-    const unsigned ko = (unsigned)((2 * gi + half) * DT::KB * sizeof(elem));
+  const __amdgpu_buffer_rsrc_t rws =
+      buf_rsrc(a.Wsd8_p + (size_t)cg0 * kps * FRAG_BYTES, (unsigned)((size_t)CG * kps * FRAG_BYTES));
+  auto load_sh = [&](int gi, i32x4_t (&wv)[CG], i32x4_t (&av)[TH]) {
+    const bool ok = gi < kps;
+    const int gc = ok ? gi : 0;
+    const unsigned vo = ok ? 0u : OOR;
+#pragma unroll
+    for (int c = 0; c < CG; ++c) wv[c] = ld16_buf(rws, 16u * l + vo, (unsigned)(((size_t)c * kps + gc) * FRAG_BYTES));
 #pragma unroll
     for (int th = 0; th < TH; ++th)
-      av[th] = ld16_buf(rs, tok_s + (unsigned)(8 * th * (size_t)a.Fsp * sizeof(elem)), ko);
+      av[th] = ld16_buf(rs, tok_s + th * th_s + vo, (unsigned)(2 * gc * DT::KB * sizeof(elem)));
   };
-  i32x4_t wv0[2], av0[2][TH];
+  i32x4_t sw[SB][CG], sa[SB][TH];
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int gi = w + DNW * k;
-    load_shared(gi < kps ? gi : kps - 1, wv0[k], av0[k]);   // past the shared slots: a duplicate, not used
-  }
-  // the experts the batch touched, as bit words (every wave the same)
+  for (int k = 0; k < SB; ++k) load_sh(w + DNW * k, sw[k], sa[k]);
+
+  // the touched experts in ascending order, as a list in this wave's LDS row
   unsigned long long mk[4];
   int n_act = 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    mk[j] = __ballot(j < a.W && 64 * j + l < a.E && rf[j] == 2u);
+    // (bitwise, so every flag load stays unconditional and ahead of the
+    // shared loads: a load sunk into a branch would be waited for with them)
+    mk[j] = __ballot((j < a.W) & (64 * j + l < a.E) & (rf[j] == 2u));
+    if ((mk[j] >> l) & 1ull) s_list[w][n_act + __popcll(mk[j] & ((1ull << l) - 1ull))] = 64 * j + l;
     n_act += __popcll(mk[j]);
   }
-  // the r-th touched expert (ascending)
-  auto nth = [&](int r) -> int {
-    int base = 0;
+  __builtin_amdgcn_wave_barrier();
+  const int n_exp = n_act * kpe;
+  const int ksh = __builtin_ctz(kpe);   // kpe is a power of two (F is)
+  // a batch of expert slots q = base + w + 8 k: the experts from the list
+  // first (one LDS round trip for the batch), then the loads.  Past the end
+  // the list entry is stale or unset; it is clamped to a valid expert and the
+  // slot reads zeros.
+  auto load_ex = [&](int base, auto& wv, auto& av) {
+    constexpr int NS = sizeof(wv) / sizeof(wv[0]);
+    int ev[NS];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int pc = __popcll(mk[j]);
-      if (r < pc) {
-        unsigned long long m = mk[j];
-        int bit = 0;
-#pragma unroll
-        for (int s = 32; s >= 1; s >>= 1) {   // binary search of the r-th set bit
-          const unsigned long long lo = m & ((1ull << s) - 1ull);
-          const int plo = __popcll(lo);
-          if (r >= plo) {
-            r -= plo;
-            m >>= s;
-            bit += s;
-          } else {
-            m = lo;
-          }
-        }
-        return base + bit;
-      }
-      r -= pc;
-      base += 64;
+    for (int k = 0; k < NS; ++k) {
+      const int q = base + w + DNW * k;
+      ev[k] = s_list[w][(q < n_exp ? q : 0) >> ksh];
     }
-    return 0;
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+      const int q = base + w + DNW * k;
+      const bool ok = q < n_exp;
+      const int kp = (ok ? q : 0) & (kpe - 1);
+      int e = __builtin_amdgcn_readfirstlane(ev[k]);
+      e = e < 0 ? 0 : (e >= a.E ? a.E - 1 : e);
+      const unsigned vo = ok ? 0u : OOR;
+      const __amdgpu_buffer_rsrc_t rw = buf_rsrc(a.Wdn8_p + (size_t)e * a.dn8_stride + (size_t)cg0 * kpe * FRAG_BYTES,
+                                                 (unsigned)((size_t)CG * kpe * FRAG_BYTES));
+#pragma unroll
+      for (int c = 0; c < CG; ++c)
+        wv[k][c] = ld16_buf(rw, 16u * l + vo, (unsigned)(((size_t)c * kpe + kp) * FRAG_BYTES));
+      const __amdgpu_buffer_rsrc_t ra =
+          buf_rsrc((const DE*)a.arow + (size_t)e * 16 * a.Fp, (unsigned)((size_t)a.T * a.Fp * sizeof(DE)));
+#pragma unroll
+      for (int th = 0; th < TH; ++th)
+        av[k][th] = ld16_buf(ra, tok_r + th * th_r + vo, (unsigned)(2 * kp * DN::KB * sizeof(DE)));
+    }
   };
-  const int extra_shared = kps > 2 * DNW ? kps - 2 * DNW : 0;   // shared slots after the first 16
-  const int n_rest = extra_shared + n_act * kpe;
 
-  f32x4_t acc[TH];
+  f32x4_t acc[CG][TH];
 #pragma unroll
-  for (int th = 0; th < TH; ++th) acc[th] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < CG; ++c)
 #pragma unroll
-  for (int k = 0; k < 2; ++k)
-    if (w + DNW * k < kps) {
+    for (int th = 0; th < TH; ++th) acc[c][th] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  {
+    // first expert batch, then the shared products (their loads are older)
+    i32x4_t wv[SPW][CG], av[SPW][TH];
+    load_ex(0, wv, av);
+    __builtin_amdgcn_sched_barrier(0);   // every load of the batch before the first product
 #pragma unroll
-      for (int th = 0; th < TH; ++th) DT::mma(acc[th], av0[k][th], wv0[k]);
-    }
-  for (int base = 0; base < n_rest; base += DNW * SPW) {
-    i32x4_t wv[SPW], av[SPW][TH];
+    for (int k = 0; k < SB; ++k)
 #pragma unroll
-    for (int k = 0; k < SPW; ++k) {
-      const int r = base + w + DNW * k;
-      if (r < n_rest) {
-        if (r < extra_shared) {
-          load_shared(2 * DNW + r, wv[k], av[k]);
-        } else {
-          const int q = r - extra_shared, kp = q % kpe;
-          const int e = nth(q / kpe);
-          wv[k] = ld16(a.Wdn8_p + (size_t)e * a.dn8_stride + ((size_t)cg * kpe + kp) * FRAG_BYTES + (size_t)l * 16);
-          const __amdgpu_buffer_rsrc_t ra =
-              buf_rsrc((const DE*)a.arow + (size_t)e * 16 * a.Fp, (unsigned)((size_t)a.T * a.Fp * sizeof(DE)));
-          const unsigned ko = (unsigned)((2 * kp + half) * DN::KB * sizeof(DE));
+      for (int c = 0; c < CG; ++c)
 #pragma unroll
-          for (int th = 0; th < TH; ++th)
-            av[k][th] = ld16_buf(ra, tok_r + (unsigned)(8 * th * (size_t)a.Fp * sizeof(DE)), ko);
-        }
-      }
-    }
+        for (int th = 0; th < TH; ++th) DT::mma(acc[c][th], sa[k][th], sw[k][c]);
 #pragma unroll
-    for (int k = 0; k < SPW; ++k) {
-      const int r = base + w + DNW * k;
-      if (r < n_rest) {
+    for (int k = 0; k < SPW; ++k)
 #pragma unroll
-        for (int th = 0; th < TH; ++th) {
-          if (r < extra_shared) DT::mma(acc[th], av[k][th], wv[k]);
-          else DN::mma(acc[th], av[k][th], wv[k]);
-        }
-      }
-    }
+      for (int c = 0; c < CG; ++c)
+#pragma unroll
+        for (int th = 0; th < TH; ++th) DN::mma(acc[c][th], av[k][th], wv[k][c]);
+  }
+  for (int base = DNW * SPW; base < n_exp; base += DNW * SPW) {
+    i32x4_t wv[SPW][CG], av[SPW][TH];
+    load_ex(base, wv, av);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < SPW; ++k)
+#pragma unroll
+      for (int c = 0; c < CG; ++c)
+#pragma unroll
+        for (int th = 0; th < TH; ++th) DN::mma(acc[c][th], av[k][th], wv[k][c]);
+  }
+  for (int s0 = DNW * SB; s0 < kps; s0 += DNW * SB) {   // shared slots past the first batch
+    i32x4_t wv[SB][CG], av[SB][TH];
+#pragma unroll
+    for (int k = 0; k < SB; ++k) load_sh(s0 + w + DNW * k, wv[k], av[k]);
+#pragma unroll
+    for (int k = 0; k < SB; ++k)
+#pragma unroll
+      for (int c = 0; c < CG; ++c)
+#pragma unroll
+        for (int th = 0; th < TH; ++th) DT::mma(acc[c][th], av[k][th], wv[k][c]);
   }
   // sum the waves' products, then the two diagonal quadrants: lane
   // (col cc, group g < 2) holds C[4 g + i][cc] (first k-block of each
   // pair), lane (cc + 8, g + 2) holds C[8 + 4 g + i][cc + 8] (second)
 #pragma unroll
-  for (int th = 0; th < TH; ++th) s_red[(w * TH + th) * 64 + l] = acc[th];
+  for (int c = 0; c < CG; ++c)
+#pragma unroll
+    for (int th = 0; th < TH; ++th) s_red[w][c][th][l] = acc[c][th];
   __syncthreads();
-  for (int q = tid; q < 64 * TH; q += DNT) {
-    const int th = q >> 6, rem = q & 63, g2 = rem >> 5, cc = (rem >> 2) & 7, i = rem & 3;
+  for (int q = tid; q < CG * TH * 64; q += DNT) {
+    const int c = q / (TH * 64), th = (q >> 6) % TH, rem = q & 63;
+    const int g2 = rem >> 5, cc = (rem >> 2) & 7, i = rem & 3;
     const int t = 8 * th + 4 * g2 + i;
     float v = 0.f;
 #pragma unroll
     for (int ww = 0; ww < DNW; ++ww) {
-      const f32x4_t p1 = s_red[(ww * TH + th) * 64 + cc + 16 * g2];
-      const f32x4_t p2 = s_red[(ww * TH + th) * 64 + cc + 8 + 16 * (g2 + 2)];
+      const f32x4_t p1 = s_red[ww][c][th][cc + 16 * g2];
+      const f32x4_t p2 = s_red[ww][c][th][cc + 8 + 16 * (g2 + 2)];
       v += p1[i] + p2[i];
     }
-    if (t < a.T) ((elem*)a.out)[(size_t)t * a.d + 8 * cg + cc] = DT::from_f32(v);
+    if (t < a.T) ((elem*)a.out)[(size_t)t * a.d + 8 * (cg0 + c) + cc] = DT::from_f32(v);
   }
 }
 
@@ -689,8 +718,11 @@ hipError_t decode(const deco_moe_layer* L, const void* x, int T, void* out, hipS
   hipError_t err = deco_host::launch(deco_host::KS_DEC_UP, up_kernel<DT>(L->dec_np, dec_variant(L)),
                                      dim3((unsigned)L->dec_grid_up), dim3(DNT), s, a);
   if (err != hipSuccess) return err;
-  void (*down)(DecArgs) = T <= 8 ? k_dec_down<DT, 1> : k_dec_down<DT, 2>;
-  err = deco_host::launch(deco_host::KS_DEC_DOWN, down, dim3((unsigned)(L->d / 8)), dim3(DNT), s, a);
+  // two column groups per workgroup once one per group would exceed the CU count
+  const int cgw = L->d / 8 > L->n_cu ? 2 : 1;
+  void (*down)(DecArgs) = T <= 8 ? (cgw == 2 ? k_dec_down<DT, 1, 2> : k_dec_down<DT, 1, 1>)
+                                 : (cgw == 2 ? k_dec_down<DT, 2, 2> : k_dec_down<DT, 2, 1>);
+  err = deco_host::launch(deco_host::KS_DEC_DOWN, down, dim3((unsigned)(L->d / (8 * cgw))), dim3(DNT), s, a);
   if (err != hipSuccess) return err;
   return hipGetLastError();
 }
