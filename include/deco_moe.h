@@ -213,9 +213,12 @@ float deco_moe_sparsity_coef_update(float coef, float active_ratio, float target
 
 /* Health flags of L's device-side work, read synchronously (waits for all
  * work on the device) and cleared by the read.  Bit 0: an in-kernel
- * hand-off between workgroups timed out (the output of that call is not
- * valid).  The current kernels never wait on other workgroups, so the flags
- * stay 0.  Returns DECO_ERR_INVALID_ARG on NULL arguments. */
+ * hand-off between workgroups of the decode path timed out (the output of
+ * that call is not valid); the bit naming the hand-off is set with it:
+ * 2 the mean term x.Wbar, 4 an expert's per-row sums of squares (NormSiLU's
+ * RMS across column slices), 8 the TopK logits, 16 the shared expert's sums
+ * of squares (shared_rms layers).  The prefill and backward kernels never
+ * wait on other workgroups.  Returns DECO_ERR_INVALID_ARG on NULL arguments. */
 int deco_moe_read_error_flags(const deco_moe_layer* L, uint32_t* flags);
 
 /* Release every device buffer of L (NULL is a no-op).  The caller must make

@@ -384,6 +384,9 @@ __global__ void __launch_bounds__(DNT) k_dec_up(DecArgs a) {
           s_gate[t] = gate[j];
         }
     }
+    // every wave's decisions are in before they are read (the predicate
+    // below is evaluated before its barrier)
+    __syncthreads();
   }
   const bool any = __syncthreads_or(tid < 16 && s_act[tid] != 0) != 0;
   if (slice == 0) {
