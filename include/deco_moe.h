@@ -154,6 +154,28 @@ int deco_moe_forward(const deco_moe_layer* L, const void* x, int64_t T, void* ou
 int deco_moe_forward_path(const deco_moe_layer* L, const void* x, int64_t T, void* out,
                           void* stream, int path);
 
+/* Allocation-free decode, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same result as deco_moe_forward_path(..., DECO_PATH_DECODE),
+ * bit for bit (same kernels), with the scratch those kernels hand to each
+ * other (hand-off words, epoch counters, routing flags, decisions, logits and
+ * gates, activation rows: deco_moe_decode_noalloc_bytes(L) bytes) in one
+ * static device array of 4 MiB per device instead of L's workspace.
+ * Allocates nothing; asynchronous on `stream`.  T in 0..min(max_tokens,
+ * DECO_DECODE_MAX_T), else DECO_ERR_INVALID_ARG; DECO_ERR_UNSUPPORTED when
+ * the layer's scratch exceeds 4 MiB or its decode path is unavailable.  The
+ * array is cleared at the start of every call and keeps the last call's
+ * contents; all calls on one device share that device's array, so calls that
+ * overlap on a device (another stream, another thread) race.  L's routing
+ * state is left as it was (deco_moe_copy_routing describes the last regular
+ * forward); timeouts still set L's error flags. */
+int deco_moe_forward_decode_noalloc(const deco_moe_layer* L, const void* x, int64_t T, void* out,
+                                    void* stream);
+
+/* Scratch bytes deco_moe_forward_decode_noalloc needs for L (at most 4 MiB
+ * is accepted); DECO_ERR_INVALID_ARG for NULL. */
+int64_t deco_moe_decode_noalloc_bytes(const deco_moe_layer* L);
+
 /* Routing state of the most recent forward on L, for the same T:
  *   mask   [T, ceil(E/64)] uint64 (device): bit e%64 of word e/64 of row t is
  *          set iff expert e was active for token t (z > 0 and lambda_e != 0;

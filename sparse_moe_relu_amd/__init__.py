@@ -35,7 +35,8 @@ DECO_NORMSILU_NO_MEAN = 1
 DECO_NORMSILU_NO_RMS = 2
 
 EXPORTS = ("deco_moe_check_config", "deco_moe_load_weights", "deco_moe_load_weights_gated", "deco_moe_forward",
-           "deco_moe_forward_path", "deco_moe_copy_routing", "deco_moe_copy_mean_up",
+           "deco_moe_forward_path", "deco_moe_forward_decode_noalloc", "deco_moe_decode_noalloc_bytes",
+           "deco_moe_copy_routing", "deco_moe_copy_mean_up",
            "deco_moe_free", "deco_moe_status_string", "deco_moe_read_error_flags", "deco_moe_timing_enable",
            "deco_moe_timing_reset", "deco_moe_timing_read", "deco_moe_backward",
            "deco_moe_sparsity_coef_update")
@@ -85,6 +86,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.deco_moe_forward.restype = i32
     lib.deco_moe_forward_path.argtypes = [vp, vp, i64, vp, vp, i32]
     lib.deco_moe_forward_path.restype = i32
+    lib.deco_moe_forward_decode_noalloc.argtypes = [vp, vp, i64, vp, vp]
+    lib.deco_moe_forward_decode_noalloc.restype = i32
+    lib.deco_moe_decode_noalloc_bytes.argtypes = [vp]
+    lib.deco_moe_decode_noalloc_bytes.restype = i64
     lib.deco_moe_copy_routing.argtypes = [vp, i64, vp, vp, vp]
     lib.deco_moe_copy_routing.restype = i32
     lib.deco_moe_copy_mean_up.argtypes = [vp, vp, vp]
@@ -226,6 +231,25 @@ class Layer:
         return out
 
     __call__ = forward
+
+    def forward_decode_noalloc(self, x: torch.Tensor, out: torch.Tensor, *, stream=None) -> torch.Tensor:
+        """deco_moe_forward_decode_noalloc: the decode path with its scratch in
+        the library's static device array (allocates nothing; `out` is
+        required)."""
+        if x.dim() != 2 or x.shape[1] != self.d or x.dtype != _TORCH_DT[self.dtype] or not x.is_cuda \
+                or not x.is_contiguous():
+            raise ValueError(f"x: expected contiguous device [T,{self.d}] {_TORCH_DT[self.dtype]}")
+        if (tuple(out.shape) != tuple(x.shape) or out.dtype != x.dtype or out.device != x.device
+                or not out.is_contiguous()):
+            raise ValueError(f"out: expected contiguous {tuple(x.shape)} {x.dtype} on {x.device}")
+        st = load_library().deco_moe_forward_decode_noalloc(self.handle, x.data_ptr(), x.shape[0],
+                                                            out.data_ptr(), _stream_handle(stream))
+        if st != DECO_OK:
+            raise DecoError(st, "deco_moe_forward_decode_noalloc")
+        return out
+
+    def decode_noalloc_bytes(self) -> int:
+        return int(load_library().deco_moe_decode_noalloc_bytes(self.handle))
 
     def backward(self, x: torch.Tensor, dout: torch.Tensor, *, reg_coef: float = 0.0, stream=None) -> dict:
         """Gradients of sum(dout * layer(x)) + reg_coef * mean router entropy

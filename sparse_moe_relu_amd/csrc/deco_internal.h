@@ -154,6 +154,10 @@ hipError_t plan_backward(deco_moe_layer* L); // backward launch shape (load time
 hipError_t launch_decode(const deco_moe_layer* L, const void* x, int T, void* out, hipStream_t s);
 hipError_t launch_prefill(const deco_moe_layer* L, const void* x, int T, void* out, hipStream_t s);
 hipError_t launch_dec_mask(const deco_moe_layer* L, int T, uint64_t* mask, hipStream_t s);
+// allocation-free decode (static device array as scratch)
+size_t decode_scratch_bytes(const deco_moe_layer* L);
+size_t decode_scratch_limit();
+hipError_t launch_decode_scratch(const deco_moe_layer* L, const void* x, int T, void* out, hipStream_t s);
 hipError_t launch_backward(const deco_moe_layer* L, const void* x, const void* dout, int T, float reg_coef,
                            const deco_moe_grads* gr, hipStream_t s);
 

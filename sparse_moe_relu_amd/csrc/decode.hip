@@ -42,6 +42,10 @@
 // timeout sets the layer's error flag).
 #include <string.h>
 
+#include <algorithm>
+#include <map>
+#include <mutex>
+
 #include "deco_common.h"
 #include "deco_internal.h"
 
@@ -716,17 +720,116 @@ DecArgs dec_args(const deco_moe_layer* L, const void* x, int T, void* out) {
 }
 
 template <class DT>
+void (*down_kernel(const deco_moe_layer* L, int T, int* grid))(DecArgs) {
+  // two column groups per workgroup once one per group would exceed the CU count
+  const int cgw = L->d / 8 > L->n_cu ? 2 : 1;
+  *grid = L->d / (8 * cgw);
+  return T <= 8 ? (cgw == 2 ? k_dec_down<DT, 1, 2> : k_dec_down<DT, 1, 1>)
+                : (cgw == 2 ? k_dec_down<DT, 2, 2> : k_dec_down<DT, 2, 1>);
+}
+
+template <class DT>
 hipError_t decode(const deco_moe_layer* L, const void* x, int T, void* out, hipStream_t s) {
   const DecArgs a = dec_args(L, x, T, out);
   hipError_t err = deco_host::launch(deco_host::KS_DEC_UP, up_kernel<DT>(L->dec_np, dec_variant(L)),
                                      dim3((unsigned)L->dec_grid_up), dim3(DNT), s, a);
   if (err != hipSuccess) return err;
-  // two column groups per workgroup once one per group would exceed the CU count
-  const int cgw = L->d / 8 > L->n_cu ? 2 : 1;
-  void (*down)(DecArgs) = T <= 8 ? (cgw == 2 ? k_dec_down<DT, 1, 2> : k_dec_down<DT, 1, 1>)
-                                 : (cgw == 2 ? k_dec_down<DT, 2, 2> : k_dec_down<DT, 2, 1>);
-  err = deco_host::launch(deco_host::KS_DEC_DOWN, down, dim3((unsigned)(L->d / (8 * cgw))), dim3(DNT), s, a);
+  int grid = 0;
+  void (*down)(DecArgs) = down_kernel<DT>(L, T, &grid);
+  err = deco_host::launch(deco_host::KS_DEC_DOWN, down, dim3((unsigned)grid), dim3(DNT), s, a);
   if (err != hipSuccess) return err;
+  return hipGetLastError();
+}
+
+// --------------------------------------------------------------------------
+// Allocation-free decode.  The same two kernels, with everything they hand to
+// each other (hand-off words, epoch counters, routing flags, decisions,
+// logits and gates, activation rows) in one file-scope device array instead
+// of the layer's workspace; a fill kernel clears it at the start of every
+// call, so each call runs with epoch 1.  Only the error flags go to the layer.
+// Every call on a device shares that device's array: calls that overlap on
+// one device race.
+constexpr size_t SCRATCH_BYTES = (size_t)4 << 20;
+static __device__ __align__(256) unsigned char scratch[SCRATCH_BYTES];
+
+// device-scope stores of zero (the hand-off words are read with device-scope
+// atomics by workgroups on every XCD)
+__global__ void __launch_bounds__(256) k_scratch_clear(unsigned* __restrict__ p, unsigned n) {
+  for (unsigned i = blockIdx.x * 256u + threadIdx.x; i < n; i += gridDim.x * 256u)
+    __hip_atomic_store(p + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+struct ScratchPlan {
+  size_t o_hw, o_ct, o_rf, o_a8, o_z, o_g, o_ar, o_sr, bytes;
+};
+size_t al256(size_t v) { return (v + 255) / 256 * 256; }
+ScratchPlan scratch_plan(const deco_moe_layer* L) {
+  ScratchPlan p;
+  size_t o = 0;
+  p.o_hw = o;
+  o += al256(sizeof(u64) * (size_t)L->n_hwords);
+  p.o_ct = o;
+  o += al256(sizeof(unsigned) * (size_t)L->dec_grid_up);
+  p.o_rf = o;
+  o += al256(sizeof(unsigned) * (size_t)L->E);
+  p.o_a8 = o;
+  o += al256((size_t)16 * L->E);
+  p.o_z = o;
+  o += al256(sizeof(float) * 16 * L->E);
+  p.o_g = o;
+  o += al256(sizeof(float) * 16 * L->E);
+  p.o_ar = o;
+  o += al256((size_t)(L->esz == 2 ? 2 : 4) * L->E * 16 * L->dec_Fp);
+  p.o_sr = o;
+  o += al256((size_t)L->esz * 16 * L->dec_Fsp);
+  p.bytes = o;
+  return p;
+}
+
+// the address of `scratch` on each device, taken once per device with that
+// device current (each device holds its own copy of the array)
+std::mutex g_scr_mu;
+std::map<int, char*> g_scr_ptr;
+hipError_t scratch_base(char** out) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  std::lock_guard<std::mutex> lk(g_scr_mu);
+  auto it = g_scr_ptr.find(dev);
+  if (it != g_scr_ptr.end()) {
+    *out = it->second;
+    return hipSuccess;
+  }
+  void* p = nullptr;
+  err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (err != hipSuccess) return err;
+  g_scr_ptr[dev] = (char*)p;
+  *out = (char*)p;
+  return hipSuccess;
+}
+
+template <class DT>
+hipError_t decode_scratch(const deco_moe_layer* L, const void* x, int T, void* out, char* base,
+                          const ScratchPlan& sp, hipStream_t s) {
+  DecArgs a = dec_args(L, x, T, out);
+  a.hw = (u64*)(base + sp.o_hw);
+  a.ctr = (unsigned*)(base + sp.o_ct);
+  a.rflag = (unsigned*)(base + sp.o_rf);
+  a.act8 = (unsigned char*)(base + sp.o_a8);
+  a.z = (float*)(base + sp.o_z);
+  a.g = (float*)(base + sp.o_g);
+  a.arow = base + sp.o_ar;
+  a.srow = base + sp.o_sr;
+  const unsigned nw = (unsigned)(sp.bytes / 4);
+  hipLaunchKernelGGL(k_scratch_clear, dim3(std::min(1024u, (nw + 255) / 256)), dim3(256), 0, s, (unsigned*)base, nw);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(up_kernel<DT>(L->dec_np, dec_variant(L)), dim3((unsigned)L->dec_grid_up), dim3(DNT), 0, s, a);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  int grid = 0;
+  void (*down)(DecArgs) = down_kernel<DT>(L, T, &grid);
+  hipLaunchKernelGGL(down, dim3((unsigned)grid), dim3(DNT), 0, s, a);
   return hipGetLastError();
 }
 
@@ -799,6 +902,19 @@ hipError_t plan_decode(deco_moe_layer* L) {
 hipError_t launch_decode(const deco_moe_layer* L, const void* x, int T, void* out, hipStream_t s) {
   if (L->cfg.dtype == DECO_DT_BF16) return decode<BF16>(L, x, T, out, s);
   return decode<F32>(L, x, T, out, s);
+}
+
+size_t decode_scratch_bytes(const deco_moe_layer* L) { return scratch_plan(L).bytes; }
+size_t decode_scratch_limit() { return SCRATCH_BYTES; }
+
+hipError_t launch_decode_scratch(const deco_moe_layer* L, const void* x, int T, void* out, hipStream_t s) {
+  const ScratchPlan sp = scratch_plan(L);
+  if (sp.bytes > SCRATCH_BYTES) return hipErrorInvalidValue;   // the caller checks the size first
+  char* base = nullptr;
+  hipError_t err = scratch_base(&base);
+  if (err != hipSuccess) return err;
+  if (L->cfg.dtype == DECO_DT_BF16) return decode_scratch<BF16>(L, x, T, out, base, sp, s);
+  return decode_scratch<F32>(L, x, T, out, base, sp, s);
 }
 
 hipError_t launch_dec_mask(const deco_moe_layer* L, int T, uint64_t* mask, hipStream_t s) {

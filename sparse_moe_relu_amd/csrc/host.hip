@@ -412,6 +412,26 @@ int deco_moe_forward(const deco_moe_layer* L, const void* x, int64_t T, void* ou
   return deco_moe_forward_path(L, x, T, out, stream, DECO_PATH_AUTO);
 }
 
+int deco_moe_forward_decode_noalloc(const deco_moe_layer* L, const void* x, int64_t T, void* out, void* stream) {
+  if (!L || T < 0 || T > L->maxT || T > DECO_DECODE_MAX_T) return DECO_ERR_INVALID_ARG;
+  if (T == 0) return DECO_OK;
+  if (!x || !out) return DECO_ERR_INVALID_ARG;
+  if (((uintptr_t)x % 16) != 0 || ((uintptr_t)out % 16) != 0) return DECO_ERR_INVALID_ARG;
+  const size_t bytes = (size_t)T * L->d * L->esz;
+  const char* xb = (const char*)x;
+  const char* ob = (const char*)out;
+  if (xb < ob + bytes && ob < xb + bytes) return DECO_ERR_INVALID_ARG;
+  if (!L->dec_ok) return DECO_ERR_UNSUPPORTED;
+  if (deco_host::decode_scratch_bytes(L) > deco_host::decode_scratch_limit()) return DECO_ERR_UNSUPPORTED;
+  const hipError_t err = deco_host::launch_decode_scratch(L, x, (int)T, out, (hipStream_t)stream);
+  return err == hipSuccess ? DECO_OK : DECO_ERR_HIP;
+}
+
+int64_t deco_moe_decode_noalloc_bytes(const deco_moe_layer* L) {
+  if (!L) return DECO_ERR_INVALID_ARG;
+  return (int64_t)deco_host::decode_scratch_bytes(L);
+}
+
 int deco_moe_copy_routing(const deco_moe_layer* L, int64_t T, uint64_t* mask, float* logits, void* stream) {
   if (!L || T < 0 || T > L->maxT || !mask) return DECO_ERR_INVALID_ARG;
   if (T == 0) return DECO_OK;
