@@ -114,7 +114,12 @@ int deco_moe_check_config(const deco_moe_config* cfg);
  * `stream` and synchronizes it
  * before returning, so the sources may be freed afterwards.  On success
  * *out_layer receives the new layer; on failure it is set to NULL and nothing
- * stays allocated. */
+ * stays allocated.  bf16 layers run the routed down-projection on fp16
+ * operands (W_down and the gated activations; the paths' fp32 accumulation
+ * is unchanged): a W_down entry whose magnitude exceeds the fp16 range
+ * (65504), or a NaN, gets DECO_ERR_UNSUPPORTED.  Activations or pair rows
+ * that leave the fp16 range at run time (very large gates) set error bit 5
+ * (see deco_moe_read_error_flags). */
 int deco_moe_load_weights(const deco_moe_config* cfg,
                           const void* W_r, const float* b_r, const float* lambda,
                           const void* W_up, const void* W_down,
@@ -240,7 +245,10 @@ float deco_moe_sparsity_coef_update(float coef, float active_ratio, float target
  * 2 the mean term x.Wbar, 4 an expert's per-row sums of squares (NormSiLU's
  * RMS across column slices), 8 the TopK logits, 16 the shared expert's sums
  * of squares (shared_rms layers).  The prefill and backward kernels never
- * wait on other workgroups.  Returns DECO_ERR_INVALID_ARG on NULL arguments. */
+ * wait on other workgroups.  Bit 5 (32), any path of a bf16 layer: a value
+ * of the down-projection's fp16 operands or of the fp16 pair rows left the
+ * fp16 range (a gate too large for it); that call's output is not valid.
+ * Returns DECO_ERR_INVALID_ARG on NULL arguments. */
 int deco_moe_read_error_flags(const deco_moe_layer* L, uint32_t* flags);
 
 /* Release every device buffer of L (NULL is a no-op).  The caller must make

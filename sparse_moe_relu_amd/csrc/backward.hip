@@ -43,6 +43,7 @@ namespace {
 struct BwdArgs {
   const void* x;
   const void* dout;
+  unsigned* err;              // device error flags (bit 5: a value outside the fp16 range)
   int T, d, E, F, Fs, W, top_k;
   int Fp, Ep, Fsp, Kc;        // dcat row: dm [Fp] | dz [Ep] | du_s [Fsp]
   int nkb_d, nkb_cat, pFs, pD;
@@ -331,6 +332,7 @@ __global__ void __launch_bounds__(256) k_bwd_dense_dx(BwdArgs a) {
     tile_gemm<DT, TD, true>(lds, row_lo, panel, a.nkb_cat, acc);
   }
   PT* yb = (PT*)a.ybuf;
+  bool bad = false;
 #pragma unroll
   for (int i = 0; i < TD::MB; ++i) {
     const int r = m0 + wm * (GM / 2) + 16 * i + c;
@@ -339,9 +341,10 @@ __global__ void __launch_bounds__(256) k_bwd_dense_dx(BwdArgs a) {
 #pragma unroll
     for (int j = 0; j < TD::NBW; ++j) {
       const int p = p0 + wn * TD::NBW + j;
-      if (p < a.pD) store4_pair(yb + base + p * 16 + 4 * g, acc[i][j]);
+      if (p < a.pD) store4_pair(yb + base + p * 16 + 4 * g, acc[i][j], bad);
     }
   }
+  if (bad) atomicOr(a.err, 32u);
 }
 
 // ---------------------------------------------------------------------------
@@ -694,6 +697,7 @@ hipError_t backward(const deco_moe_layer* L, const void* x, const void* dout, in
   memset(&b, 0, sizeof(b));
   b.x = x;
   b.dout = dout;
+  b.err = L->dec_err;
   b.T = T;
   b.d = L->d;
   b.E = L->E;

@@ -145,6 +145,7 @@ const char* kernel_slot_name(int slot);
 // launchers (return hipSuccess or the launch error)
 // W_norm: the projection NormSiLU acts on (W_up, or W_gate for gated
 // experts); W_lin: gated experts' W_up (null otherwise)
+hipError_t check_down_range(deco_moe_layer* L, const void* W_down, hipStream_t s, bool* ok);
 hipError_t launch_pack_all(deco_moe_layer* L, const void* W_r, const void* W_norm, const void* W_lin,
                            const void* W_down, const void* Ws_up, const void* Ws_down, hipStream_t s);
 void plan_decode_sizes(deco_moe_layer* L, int n_cu);   // decode slices and buffer sizes (load time)

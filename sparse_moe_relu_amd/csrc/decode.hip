@@ -461,8 +461,15 @@ __global__ void __launch_bounds__(DNT) k_dec_up(DecArgs a) {
     using DE = typename DN::elem;
     DE* ar = (DE*)a.arow + ((size_t)e * 16 + row) * a.Fp + gcol0;
     if constexpr (sizeof(DE) == 2) {
+      // fp16 operand of the down-projection: a value past its range would be
+      // stored as inf; report it (bit 5) instead of returning a silent inf
+      bool bad = false;
 #pragma unroll
-      for (int k = 0; k < CPT; ++k) ar[k] = (DE)DN::bits(av[k]);
+      for (int k = 0; k < CPT; ++k) {
+        bad |= !(fabsf(av[k]) <= 65504.f);
+        ar[k] = (DE)DN::bits(av[k]);
+      }
+      if (bad) atomicOr(a.err, 32u);
     } else {
 #pragma unroll
       for (int k = 0; k < CPT; ++k) ar[k] = av[k];

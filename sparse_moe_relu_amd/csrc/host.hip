@@ -357,6 +357,14 @@ static int load_layer(const deco_moe_config* cfg, const void* W_r, const float* 
     else
       err = hipMemcpyAsync(L->lam, lambda, sizeof(float) * E, hipMemcpyDeviceToDevice, s);
   }
+  bool down_ok = true;
+  if (err == hipSuccess) err = deco_host::check_down_range(L, W_down, s, &down_ok);
+  if (err == hipSuccess && !down_ok) {
+    // bf16 layers run the down-projection on fp16 operands: a W_down entry
+    // past the fp16 range is refused rather than turned into inf
+    deco_moe_free(L);
+    return DECO_ERR_UNSUPPORTED;
+  }
   if (err == hipSuccess) err = deco_host::launch_pack_all(L, W_r, W_norm, W_lin, W_down, Ws_up, Ws_down, s);
   if (err == hipSuccess) err = deco_host::plan_prefill(L);   // also reads the CU count
   if (err == hipSuccess) err = deco_host::plan_decode(L);

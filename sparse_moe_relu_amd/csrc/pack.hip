@@ -8,6 +8,8 @@
 // once per token and subtract it from every expert's up-projection.  (Folding
 // Wbar into each expert's packed weights would save that product but rounds
 // W_up[e] - Wbar to the dtype, which costs about 1 % of RMS(out) in bf16.)
+#include <string.h>
+
 #include "deco_common.h"
 #include "deco_internal.h"
 
@@ -86,6 +88,24 @@ __global__ void __launch_bounds__(256) k_pack_pair(const SRC* __restrict__ src, 
     f[j] = (k < K && n < N) ? src_f32(s, (size_t)k * N + n) : 0.f;
   }
   st16(dst + (size_t)b * dst_bstride + ((size_t)cg * nkp + kp) * FRAG_BYTES + (size_t)l * 16, DT::pack(f));
+}
+
+// Largest |W_down| of a bf16 layer, as fp32 bits (non-negative floats order
+// like their bit patterns; NaN patterns sort above inf, so they count as out
+// of range): bf16 layers feed W_down to the down-projection in fp16.
+__global__ void __launch_bounds__(256) k_absmax_bf16(const uint16_t* __restrict__ w, size_t n,
+                                                     unsigned* __restrict__ out) {
+  unsigned m = 0;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    const unsigned b = ((unsigned)w[i] << 16) & 0x7FFFFFFFu;
+    m = b > m ? b : m;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const unsigned y = (unsigned)__shfl_xor((int)m, o);
+    m = y > m ? y : m;
+  }
+  if ((threadIdx.x & 63) == 0) atomicMax(out, m);
 }
 
 dim3 pack_grid(int P, int nkb, int batch) {
@@ -168,6 +188,28 @@ hipError_t pack_all(deco_moe_layer* L, const void* W_r, const void* W_up, const 
 }  // namespace
 
 namespace deco_host {
+
+// bf16 layers: is every |W_down| within the fp16 range (the down-projection's
+// operand type)?  Synchronous (load time); uses the layer's mbuf as scratch.
+hipError_t check_down_range(deco_moe_layer* L, const void* W_down, hipStream_t s, bool* ok) {
+  *ok = true;
+  if (L->cfg.dtype != DECO_DT_BF16) return hipSuccess;
+  unsigned* word = (unsigned*)L->mbuf;
+  hipError_t err = hipMemsetAsync(word, 0, sizeof(unsigned), s);
+  if (err != hipSuccess) return err;
+  const size_t n = (size_t)L->E * L->F * L->d;
+  k_absmax_bf16<<<1024, 256, 0, s>>>((const uint16_t*)W_down, n, word);
+  err = hipGetLastError();
+  unsigned bits = 0;
+  if (err == hipSuccess) err = hipMemcpyAsync(&bits, word, sizeof(bits), hipMemcpyDeviceToHost, s);
+  if (err == hipSuccess) err = hipStreamSynchronize(s);
+  if (err != hipSuccess) return err;
+  const float fp16_max = 65504.f;
+  unsigned lim = 0;
+  memcpy(&lim, &fp16_max, sizeof(lim));
+  *ok = bits <= lim;
+  return hipSuccess;
+}
 
 hipError_t launch_pack_all(deco_moe_layer* L, const void* W_r, const void* W_norm, const void* W_lin,
                            const void* W_down, const void* Ws_up, const void* Ws_down, hipStream_t s) {

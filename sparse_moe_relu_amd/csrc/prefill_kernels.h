@@ -48,6 +48,7 @@ namespace {
 struct PreArgs {
   const void* x;
   void* out;
+  unsigned* err;       // device error flags (bit 5: a value outside the fp16 range)
   int T, Tcap, d, E, F, Fs, W;
   int top_k;           // TopK routing variant (0: ReLU routing)
   int no_mean, no_rms; // NormSiLU ablations: drop the mean term / the RMS step
@@ -148,9 +149,14 @@ __device__ __forceinline__ void store4_split(typename DT::elem* hi, typename DT:
   }
 }
 
+// fp16 pair rows: `bad` is raised for a value outside the fp16 range (the
+// caller reports it), which would otherwise be stored as inf
+constexpr float FP16_MAX = 65504.f;
 template <class PT>
-__device__ __forceinline__ void store4_pair(PT* p, const f32x4_t& v) {
+__device__ __forceinline__ void store4_pair(PT* p, const f32x4_t& v, bool& bad) {
   if constexpr (sizeof(PT) == 2) {
+    bad |= !(fabsf(v[0]) <= FP16_MAX && fabsf(v[1]) <= FP16_MAX && fabsf(v[2]) <= FP16_MAX &&
+             fabsf(v[3]) <= FP16_MAX);
     typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 h4;
     h4 h = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
     *reinterpret_cast<h4*>(p) = h;
@@ -509,13 +515,15 @@ __global__ void __launch_bounds__(256, (ExpertShape<DT, BNP, MODE, SMALL>::OCC))
       tile_gemm<DT, TD, true>(lds, row, panel, a.nkb_Fs, acc);
       // stage the tile (pair type) in LDS, then store whole rows
       constexpr int SP = S::SPITCH_V;
+      bool bad = false;
 #pragma unroll
       for (int i = 0; i < TD::MB; ++i) {
         const int R = wm * (GM / 2) + 16 * i + c;
 #pragma unroll
         for (int j = 0; j < TD::NBW; ++j)
-          store4_pair(reinterpret_cast<PT*>(lds + R * SP) + (wn * TD::NBW + j) * 16 + 4 * g, acc[i][j]);
+          store4_pair(reinterpret_cast<PT*>(lds + R * SP) + (wn * TD::NBW + j) * 16 + 4 * g, acc[i][j], bad);
       }
+      if (bad) atomicOr(a.err, 32u);
       lds_barrier();
       constexpr int CPR = GP * 16 * (int)sizeof(PT) / 16;   // 16-byte chunks per row
       const int ncol_ch = (a.pD - p0 < GP ? a.pD - p0 : GP) * 16 * (int)sizeof(PT) / 16;
@@ -773,6 +781,7 @@ __global__ void __launch_bounds__(256, (ExpertShape<DT, BNP, MODE, SMALL>::OCC))
       }
       lds_barrier();   // flush(st - 1) has read the staging buffer
       // gate, round to the pair type, stage: token R, columns (wn*DP/2 + q)*16 + 4 g ..
+      bool bad = false;
 #pragma unroll
       for (int jt = 0; jt < MB; ++jt) {
         const int R = wm * (BM / 2) + 16 * jt + c;
@@ -786,9 +795,10 @@ __global__ void __launch_bounds__(256, (ExpertShape<DT, BNP, MODE, SMALL>::OCC))
           const int b = ((wn * (DP / 2) + q) * 16 + 4 * g) * (int)sizeof(PT);   // byte in the staged row
           store4_pair(reinterpret_cast<PT*>(reinterpret_cast<char*>(obuf + R * OCH + ((b >> 4) ^ (R & (OCH - 1)))) +
                                             (b & 15)),
-                      v);
+                      v, bad);
         }
       }
+      if (bad) atomicOr(a.err, 32u);
     }
     lds_barrier();
     if (nds > 0) flush(nds - 1);
@@ -904,6 +914,7 @@ PreArgs fill_pre_args(const deco_moe_layer* L, const void* x, int T, void* out) 
   a.Wdn16_p = L->Wdn16_p;
   a.sbuf = L->sbuf;
   a.ybuf = L->ybuf;
+  a.err = L->dec_err;
   return a;
 }
 
