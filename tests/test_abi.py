@@ -65,6 +65,10 @@ def test_status_strings(lib):
     (dict(top_k=8), dm.DECO_OK),
     (dict(top_k=9), dm.DECO_ERR_INVALID_ARG),
     (dict(top_k=-1), dm.DECO_ERR_INVALID_ARG),
+    # every packed matrix stays below 2 GiB (32-bit buffer offsets)
+    (dict(d=32768, Fs=16384, dtype="bf16"), dm.DECO_OK),              # 1 GiB
+    (dict(d=32768, Fs=16352), dm.DECO_OK),                            # fp32, 2 GiB - 4 MiB
+    (dict(d=32768, Fs=16384), dm.DECO_ERR_UNSUPPORTED),               # fp32, exactly 2 GiB
 ])
 def test_check_config(lib, kw, expect):
     a = dict(d=64, E=8, F=32, Fs=64, T=16, dtype="f32", eps=1e-6, top_k=0)
