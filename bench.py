@@ -202,6 +202,164 @@ def sweep():
     print(json.dumps({"sweep": rows}), flush=True)
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_timing(L, budget_s: float = 1.5):
+    """The fp64 oracle as it stands on the host: one warm-up, then the median
+    of 5 timed runs, on the first S tokens with S chosen so that one run takes
+    about budget_s (all tokens when that is fast enough); then one run limited
+    to a single BLAS thread."""
+    import statistics
+    import oracle
+    from threadpoolctl import threadpool_info, threadpool_limits
+    threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+                  or [os.cpu_count() or 1])
+    w = L.weights()
+    S = L.T
+    t0 = time.perf_counter()
+    oracle.forward(L.x[:S], **w, eps=L.eps)   # warm-up, also sizes the sample
+    el = time.perf_counter() - t0
+    if el > budget_s and L.T > 16:
+        S = max(16, int(L.T * budget_s / el))
+    times = []
+    for _ in range(5):
+        t0 = time.perf_counter()
+        oracle.forward(L.x[:S], **w, eps=L.eps)
+        times.append(time.perf_counter() - t0)
+    med = statistics.median(times)
+    with threadpool_limits(limits=1, user_api="blas"):
+        t0 = time.perf_counter()
+        oracle.forward(L.x[:S], **w, eps=L.eps)
+        one = time.perf_counter() - t0
+    return dict(tokens_per_s=round(S / med, 1), threads=int(threads), sample_tokens=S,
+                median_s=round(med, 4), runs_s=[round(t, 4) for t in times],
+                single_thread_tokens_per_s=round(S / one, 1), cpu=_cpu_model())
+
+
+def _parity_figures(L, top_k: int = 0):
+    """One GPU call on a fresh layer against the oracle on the same rows:
+    literal max|err|/RMS, the excess over the output's half ulp /RMS, routing
+    masks (mismatches inside and outside the |z| < 1e-5 band) and the
+    near-zero logit count, the logits' max error."""
+    import numpy as np
+    import torch
+    import oracle
+    import sparse_moe_relu_amd as dm
+    from synthetic.device import layer_tensors, x_tensor
+    ref = oracle.forward(L.x, **L.weights(), eps=L.eps, top_k=top_k)
+    layer = dm.Layer(**layer_tensors(L), max_tokens=L.T, eps=L.eps, top_k=top_k)
+    layer.error_flags()
+    out = layer(x_tensor(L)).float().cpu().numpy().astype(np.float64)
+    torch.cuda.synchronize()
+    rms = float(np.sqrt(np.mean(ref.out ** 2)))
+    _, ex = np.frexp(np.abs(out))
+    bits = 8 if L.dtype == "bf16" else 24
+    half = np.where(out == 0, 0.0, np.ldexp(1.0, ex - 1 - bits))
+    act = layer.active_mask(L.T).numpy()
+    _, logits = layer.routing(L.T)
+    zerr = float(np.max(np.abs(logits.cpu().numpy().astype(np.float64) - ref.z)))
+    near = np.abs(ref.z) < 1e-5
+    mism = act != ref.active
+    flags = layer.error_flags()
+    layer.free()
+    return dict(max_abs_err_over_rms=float(np.max(np.abs(out - ref.out))) / rms,
+                excess_over_half_ulp_over_rms=float(np.max(np.abs(out - ref.out) - half)) / rms,
+                rms_out=rms, mask_mismatch_in_band=int((mism & near).sum()),
+                mask_mismatch_outside_band=int((mism & ~near).sum()), near_zero_logits=int(near.sum()),
+                logit_max_err=zerr, error_flags=int(flags))
+
+
+RECORD_CASES = {1: [(16, None)], 2: [(1, None), (8, None), (16, None)], 3: [(4096, None)],
+                4: [(1, None), (16, None), (256, None), (2048, None)],
+                5: [(1024, r) for r in (0.05, 0.10, 0.20, 0.40)]}
+
+
+def records(only=None):
+    """Per-(workload, T) records, one text file per synthetic workload under
+    profiles/ (records_c<N>.txt): GPU time per call and tokens/s (inputs
+    resident, layer copies cycled past the Infinity Cache), the attainable
+    roofline fraction max(B/HBM, F/MFMA)/t (B: weights touched + x in and
+    out; F: algorithmic flops), the parity figures of one call against the
+    oracle, and the oracle timed on the host."""
+    import torch
+    from synthetic import make_layer
+    gpu = torch.cuda.get_device_name(0)
+    for cfg, cases in RECORD_CASES.items():
+        if only and cfg not in only:
+            continue
+        lines = [f"# DECO layer records, workload c{cfg} (synthetic inputs, seeded)",
+                 f"command: python bench.py --records {cfg}",
+                 f"gpu: {gpu}; host cpu: {_cpu_model()}, {os.cpu_count()} logical cores visible",
+                 "fields: T, ratio target, GPU us/call and tokens/s, attainable roofline fraction (and its HBM and "
+                 "MFMA parts), experts touched, active pairs, parity figures of one call, fp64 oracle on the host "
+                 "(1 warm-up, median of 5 on a sample of the tokens, then one single-BLAS-thread run)"]
+        for T, ratio in cases:
+            L = make_layer(cfg, T=T, ratio=ratio)
+            log(f"records c{cfg} T={T} ratio={ratio}")
+            steps = 400 if T <= 16 else (100 if T <= 256 else 30)
+            r = run_workload(L, steps, max(5, steps // 10))
+            t = r["elapsed"] / steps
+            B = decode_bytes(L, r["n_union"], T)
+            Bt = sum(B.values()) + T * L.d * (2 if L.dtype == "bf16" else 4)
+            Fl = layer_flops(L, r["P"], T)
+            fb, ff = Bt / t / (HBM_PEAK_GBS * 1e9), Fl / t / (BF16_PEAK_TFLOPS * 1e12)
+            rec = dict(workload=f"c{cfg}", T=T, ratio_target=ratio, dtype=L.dtype, d=L.d, E=L.E, F=L.F, Fs=L.Fs,
+                       path="decode" if T <= 16 else "prefill",
+                       us_per_call=round(t * 1e6, 2), tokens_per_s=round(T / t, 1),
+                       attainable_frac=round(max(fb, ff), 4), hbm_frac=round(fb, 4), mfma_frac=round(ff, 4),
+                       bytes_per_call=Bt, flops_per_call=Fl, experts_touched=r["n_union"], active_pairs=r["P"],
+                       active_ratio=round(r["ratio"], 4),
+                       kernels_us={k: round(v * 1e3, 2) for k, v in r["kernels"].items()})
+            rec["parity"] = {k: (round(v, 6) if isinstance(v, float) else v) for k, v in _parity_figures(L).items()}
+            rec["cpu_oracle"] = _oracle_timing(L)
+            rec["gpu_over_cpu"] = round(rec["tokens_per_s"] / rec["cpu_oracle"]["tokens_per_s"], 1)
+            log(json.dumps(rec))
+            lines.append(json.dumps(rec))
+        with open(os.path.join(PROFILE_DIR, f"records_c{cfg}.txt"), "w") as f:
+            f.write("\n".join(lines) + "\n")
+
+
+def crossover():
+    """Decode path against prefill path over T on the d=2048 and d=4096
+    layers: both paths for T <= 16 (the decode path's limit), the prefill path
+    above; writes profiles/crossover_decode_prefill.txt."""
+    import torch
+    from synthetic import make_layer
+    lines = ["# decode vs prefill path over T (us per call, layer copies cycled past the Infinity Cache)",
+             "command: python bench.py --crossover",
+             f"gpu: {torch.cuda.get_device_name(0)}"]
+    for cfg in (2, 4):
+        for T in (1, 2, 4, 8, 12, 16, 24, 32, 48, 64, 128):
+            L = make_layer(cfg, T=T)
+            steps = 200 if T <= 16 else 100
+            row = dict(workload=f"c{cfg}", T=T)
+            for name, path in (("decode", 1), ("prefill", 2)):
+                if name == "decode" and T > 16:
+                    continue
+                r = run_workload(L, steps, 20, path=path)
+                t = r["elapsed"] / steps
+                B = decode_bytes(L, r["n_union"], T)
+                Bt = sum(B.values()) + T * L.d * (2 if L.dtype == "bf16" else 4)
+                Fl = layer_flops(L, r["P"], T)
+                row[name] = dict(us=round(t * 1e6, 2), tokens_per_s=round(T / t, 1),
+                                 attainable_frac=round(max(Bt / t / (HBM_PEAK_GBS * 1e9),
+                                                           Fl / t / (BF16_PEAK_TFLOPS * 1e12)), 4),
+                                 experts_touched=r["n_union"])
+            log(json.dumps(row))
+            lines.append(json.dumps(row))
+    with open(os.path.join(PROFILE_DIR, "crossover_decode_prefill.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def layer_weight_bytes(L) -> int:
     s = 2 if L.dtype == "bf16" else 4
     n_mat = 3 if L.W_gate is not None else 2
@@ -209,7 +367,8 @@ def layer_weight_bytes(L) -> int:
 
 
 # GPU measurement ---------------------------------------------------------------
-def run_workload(L, steps: int, warmup: int, n_layers: int | None = None, top_k: int = 0, flags: dict | None = None):
+def run_workload(L, steps: int, warmup: int, n_layers: int | None = None, top_k: int = 0, flags: dict | None = None,
+                 path: int = 0):
     import numpy as np
     import torch
 
@@ -225,11 +384,11 @@ def run_workload(L, steps: int, warmup: int, n_layers: int | None = None, top_k:
     x = x_tensor(L)
     out = torch.empty_like(x)
     for k in range(warmup):
-        layers[k % n_layers](x, out)
+        layers[k % n_layers](x, out, path=path)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(steps):
-        layers[k % n_layers](x, out)
+        layers[k % n_layers](x, out, path=path)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     elapsed = t1 - t0
@@ -237,7 +396,7 @@ def run_workload(L, steps: int, warmup: int, n_layers: int | None = None, top_k:
     dm.timing_reset()
     dm.timing_enable(True)
     for k in range(steps):
-        layers[k % n_layers](x, out)
+        layers[k % n_layers](x, out, path=path)
     torch.cuda.synchronize()
     kt = dm.timing_read()
     dm.timing_enable(False)
@@ -414,6 +573,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--workload", choices=["decode", "prefill", "backward"], default="decode",
                     help="run only this workload's GPU loop (for profiler runs)")
+    ap.add_argument("--records", nargs="*", type=int, metavar="CFG",
+                    help="write profiles/records_c<N>.txt for the given workloads (all five when none given)")
+    ap.add_argument("--crossover", action="store_true",
+                    help="decode vs prefill path over T on the d=2048 and d=4096 layers")
     ap.add_argument("--sweep", action="store_true",
                     help="T sweep of the d=4096 layer and ratio sweep against the dense FFN (table, no JSON)")
     ap.add_argument("--only-gpu-loop", action="store_true",
@@ -452,6 +615,12 @@ def main():
     import sparse_moe_relu_amd as dm
     dm.load_library()
 
+    if args.crossover:
+        crossover()
+        return
+    if args.records is not None:
+        records(set(args.records) or None)
+        return
     if args.sweep:
         sweep()
         return
