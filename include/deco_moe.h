@@ -85,6 +85,12 @@ typedef struct {
   int32_t scalar_lambda;/* 1: lambda[0] scales every expert                     */
   int32_t shared_rms;   /* 1: the shared expert's SiLU input is divided by its  */
                         /* RMS over the Fs entries (eps inside the root)        */
+  int32_t shared_workspace; /* 0: the layer owns its prefill/backward workspace. */
+                        /* 1: one workspace per device, shared by every layer   */
+                        /* loaded with 1 and sized for the largest of them; the */
+                        /* prefill and backward calls of those layers must not  */
+                        /* overlap on the device (run them on one stream).  The */
+                        /* decode path's state stays per layer either way.      */
 } deco_moe_config;
 
 #define DECO_NORMSILU_NO_MEAN 1
@@ -120,6 +126,15 @@ int deco_moe_check_config(const deco_moe_config* cfg);
  * (65504), or a NaN, gets DECO_ERR_UNSUPPORTED.  Activations or pair rows
  * that leave the fp16 range at run time (very large gates) set error bit 5
  * (see deco_moe_read_error_flags). */
+/* Device memory of a layer, besides its packed weights: a per-layer part of
+ * about max(16, max_tokens) x (8E + 4F) bytes plus the decode path's
+ * hand-off state (under 1 MB at the sizes here), and the prefill/backward
+ * workspace, dominated by the token-major pair buffer of
+ * (max_tokens (E + 1) + 1) x d values of 2 bytes (bf16 layers; 4 for fp32):
+ * every token can activate every expert, so that is the bound the buffer is
+ * sized for (956 MB for d = 2048, E = 56, max_tokens = 4096).  With
+ * cfg.shared_workspace = 1 one such workspace serves every sharing layer on
+ * the device (its size is the largest layer's), instead of one per layer. */
 int deco_moe_load_weights(const deco_moe_config* cfg,
                           const void* W_r, const float* b_r, const float* lambda,
                           const void* W_up, const void* W_down,

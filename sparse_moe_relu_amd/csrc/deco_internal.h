@@ -8,6 +8,11 @@
 
 #include "deco_moe.h"
 
+// offsets (bytes from the prefill/backward workspace's base) of its buffers
+struct PwsOff {
+  size_t to, ec, lt, sb, yb, sr, dg, dh, ag, sl, dc, dz, dl, gb, cp, wp, dhl, agl, dcl, sbh, sbl;
+};
+
 struct deco_moe_layer {
   deco_moe_config cfg;
   int device;
@@ -72,6 +77,10 @@ struct deco_moe_layer {
   unsigned* rflag;         // [E] routing of the last decode call (1 no token, 2 some token routed to e)
   unsigned* dec_err;       // [1] device-side error flags (bit 0: a decode hand-off wait timed out)
   unsigned char* act8;     // [16][E] routing decisions of the last decode call
+  char* pws;               // prefill/backward workspace (its own, or the device's shared one)
+  size_t pws_bytes;
+  int pws_shared;
+  PwsOff pwo;
   void* hwords;            // [n_hwords] 64-bit decode hand-off words (epoch | value)
   int n_hwords;
   unsigned* dec_ctr;       // [dec_grid_up] epoch counters of the decode up kernel's workgroups

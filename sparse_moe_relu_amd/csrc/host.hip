@@ -5,6 +5,8 @@
 #include <string.h>
 
 #include <algorithm>
+#include <map>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -36,7 +38,7 @@ int validate_cfg(const deco_moe_config* c) {
   }
   if (c->backward != 0 && c->backward != 1) return DECO_ERR_INVALID_ARG;
   if (c->normsilu < 0 || c->normsilu > 3 || (c->scalar_lambda != 0 && c->scalar_lambda != 1) ||
-      (c->shared_rms != 0 && c->shared_rms != 1))
+      (c->shared_rms != 0 && c->shared_rms != 1) || (c->shared_workspace != 0 && c->shared_workspace != 1))
     return DECO_ERR_INVALID_ARG;
   if (c->backward && (c->normsilu || c->scalar_lambda || c->shared_rms)) return DECO_ERR_UNSUPPORTED;
   // one routed expert: the mean term equals its projection, h~ = 0 and every
@@ -115,6 +117,79 @@ void drain_pending() {
   g_pending.clear();
 }
 
+// Point L's prefill/backward buffers into the workspace at `base`.
+void bind_pws(deco_moe_layer* L, char* base) {
+  const PwsOff& o = L->pwo;
+  const bool bwd = L->cfg.backward != 0, split = bwd && L->esz == 2;
+  L->pws = base;
+  L->tok_off = (int*)(base + o.to);
+  L->ecnt = (int*)(base + o.ec);
+  L->list_tok = (int*)(base + o.lt);
+  L->sbuf = base + o.sb;
+  L->ybuf = base + o.yb;
+  L->sraw = L->cfg.shared_rms ? (float*)(base + o.sr) : nullptr;
+  if (bwd) {
+    L->dgbuf = (float*)(base + o.dg);
+    L->dhbuf = base + o.dh;
+    L->agbuf = base + o.ag;
+    L->slot_list = (int*)(base + o.sl);
+    L->dcat = base + o.dc;
+    L->dzbuf = (float*)(base + o.dz);
+    L->dlz = (float*)(base + o.dl);
+    L->gbuf = (float*)(base + o.gb);
+    L->colpart = (float*)(base + o.cp);
+    L->wpart = (float*)(base + o.wp);
+    L->sb_hi = base + o.sbh;
+    if (split) {
+      L->dhbuf_lo = base + o.dhl;
+      L->agbuf_lo = base + o.agl;
+      L->dcat_lo = base + o.dcl;
+      L->sb_lo = base + o.sbl;
+    }
+  }
+}
+
+// One prefill/backward workspace per device for the layers that share it,
+// sized for the largest.  Growing it (a larger layer loads) waits for the
+// device, replaces the buffer and points every sharing layer at the new one.
+struct SharedWs {
+  char* p = nullptr;
+  size_t bytes = 0;
+  std::vector<deco_moe_layer*> users;
+};
+std::mutex g_ws_mu;
+std::map<int, SharedWs> g_ws;
+
+hipError_t shared_ws_acquire(deco_moe_layer* L) {
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  SharedWs& a = g_ws[L->device];
+  if (L->pws_bytes > a.bytes) {
+    hipError_t err = hipDeviceSynchronize();
+    char* np = nullptr;
+    if (err == hipSuccess) err = hipMalloc((void**)&np, L->pws_bytes);
+    if (err != hipSuccess) return err;
+    if (a.p) (void)hipFree(a.p);
+    a.p = np;
+    a.bytes = L->pws_bytes;
+    for (deco_moe_layer* u : a.users) bind_pws(u, a.p);
+  }
+  a.users.push_back(L);
+  bind_pws(L, a.p);
+  return hipSuccess;
+}
+
+void shared_ws_release(deco_moe_layer* L) {
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  auto it = g_ws.find(L->device);
+  if (it == g_ws.end()) return;
+  SharedWs& a = it->second;
+  a.users.erase(std::remove(a.users.begin(), a.users.end(), L), a.users.end());
+  if (a.users.empty()) {
+    if (a.p) (void)hipFree(a.p);
+    g_ws.erase(it);
+  }
+}
+
 }  // namespace
 
 namespace deco_host {
@@ -176,6 +251,8 @@ void deco_moe_free(deco_moe_layer* L) {
   if (!L) return;
   if (L->wmem) (void)hipFree(L->wmem);
   if (L->ws) (void)hipFree(L->ws);
+  if (L->pws_shared) shared_ws_release(L);
+  else if (L->pws) (void)hipFree(L->pws);
   delete L;
 }
 
@@ -275,7 +352,16 @@ static int load_layer(const deco_moe_config* cfg, const void* W_r, const float* 
   size_t o_dcl = split ? k.take((size_t)L->esz * Tcap * (L->Fp + L->Ep + L->Fsp)) : 0;
   size_t o_sbh = bwd ? k.take((size_t)L->esz * Tcap * L->Fs) : 0;
   size_t o_sbl = split ? k.take((size_t)L->esz * Tcap * L->Fs) : 0;
-  L->ws_bytes = k.off;
+  // the per-layer part ends where the prefill/backward workspace starts
+  L->ws_bytes = o_to;
+  L->pws_bytes = k.off - o_to;
+  L->pwo = PwsOff{o_to - o_to, o_ec - o_to, o_lt - o_to, o_sb - o_to, o_yb - o_to,
+                  o_sr ? o_sr - o_to : 0, o_dg ? o_dg - o_to : 0, o_dh ? o_dh - o_to : 0,
+                  o_ag ? o_ag - o_to : 0, o_sl ? o_sl - o_to : 0, o_dc ? o_dc - o_to : 0,
+                  o_dz ? o_dz - o_to : 0, o_dl ? o_dl - o_to : 0, o_gb ? o_gb - o_to : 0,
+                  o_cp ? o_cp - o_to : 0, o_wp ? o_wp - o_to : 0, o_dhl ? o_dhl - o_to : 0,
+                  o_agl ? o_agl - o_to : 0, o_dcl ? o_dcl - o_to : 0, o_sbh ? o_sbh - o_to : 0,
+                  o_sbl ? o_sbl - o_to : 0};
 
   if (hipMalloc((void**)&L->wmem, L->wmem_bytes) != hipSuccess) {
     (void)hipGetLastError();
@@ -286,6 +372,22 @@ static int load_layer(const deco_moe_config* cfg, const void* W_r, const float* 
     (void)hipGetLastError();
     deco_moe_free(L);
     return DECO_ERR_OUT_OF_MEMORY;
+  }
+  if (L->cfg.shared_workspace) {
+    if (shared_ws_acquire(L) != hipSuccess) {
+      (void)hipGetLastError();
+      deco_moe_free(L);   // not registered: frees nothing shared
+      return DECO_ERR_OUT_OF_MEMORY;
+    }
+    L->pws_shared = 1;
+  } else {
+    char* p = nullptr;
+    if (hipMalloc((void**)&p, L->pws_bytes) != hipSuccess) {
+      (void)hipGetLastError();
+      deco_moe_free(L);
+      return DECO_ERR_OUT_OF_MEMORY;
+    }
+    bind_pws(L, p);
   }
   L->Wr_p = L->wmem + o_wr;
   L->Wup_p = L->wmem + o_up;
@@ -318,31 +420,6 @@ static int load_layer(const deco_moe_config* cfg, const void* W_r, const float* 
   L->dec_ctr = (unsigned*)(L->ws + o_ct);
   L->arow = L->ws + o_ar;
   L->srow = L->ws + o_sr2;
-  L->tok_off = (int*)(L->ws + o_to);
-  L->ecnt = (int*)(L->ws + o_ec);
-  L->list_tok = (int*)(L->ws + o_lt);
-  L->sbuf = L->ws + o_sb;
-  L->ybuf = L->ws + o_yb;
-  L->sraw = L->cfg.shared_rms ? (float*)(L->ws + o_sr) : nullptr;
-  if (bwd) {
-    L->dgbuf = (float*)(L->ws + o_dg);
-    L->dhbuf = L->ws + o_dh;
-    L->agbuf = L->ws + o_ag;
-    L->slot_list = (int*)(L->ws + o_sl);
-    L->dcat = L->ws + o_dc;
-    L->dzbuf = (float*)(L->ws + o_dz);
-    L->dlz = (float*)(L->ws + o_dl);
-    L->gbuf = (float*)(L->ws + o_gb);
-    L->colpart = (float*)(L->ws + o_cp);
-    L->wpart = (float*)(L->ws + o_wp);
-    L->sb_hi = L->ws + o_sbh;
-    if (split) {
-      L->dhbuf_lo = L->ws + o_dhl;
-      L->agbuf_lo = L->ws + o_agl;
-      L->dcat_lo = L->ws + o_dcl;
-      L->sb_lo = L->ws + o_sbl;
-    }
-  }
 
   hipError_t err = hipSuccess;
   // counters, flags and activation fragments start at zero; the rest of the

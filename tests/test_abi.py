@@ -77,6 +77,13 @@ def test_check_config(lib, kw, expect):
     assert dm.check_config(cfg) == expect
 
 
+def test_shared_workspace_flag_range(lib):
+    cfg = dm.make_config(64, 8, 32, 64, 16, "f32", shared_workspace=True)
+    assert cfg.shared_workspace == 1 and dm.check_config(cfg) == dm.DECO_OK
+    cfg.shared_workspace = 2
+    assert dm.check_config(cfg) == dm.DECO_ERR_INVALID_ARG
+
+
 def test_bad_dtype_is_unsupported(lib):
     cfg = dm.make_config(64, 8, 32, 64, 16, "f32")
     cfg.dtype = 7
