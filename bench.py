@@ -564,6 +564,47 @@ def write_pmc_summary(fetch_csv: str, write_csv: str, workload: str, cmd_fetch: 
         print("\n".join(lines))
 
 
+def write_mfma_summary(csv_path: str, workload: str, cmd: str, n_cu: int = 256, n_xcd: int = 8):
+    """MFMA activity of each library kernel from one rocprofv3 --pmc run of
+    SQ_VALU_MFMA_BUSY_CYCLES, SQ_BUSY_CYCLES and GRBM_GUI_ACTIVE (per
+    dispatch).  GRBM_GUI_ACTIVE comes summed over the XCDs (divided by 8 it
+    matches the kernel's duration times the clock); SQ_VALU_MFMA_BUSY_CYCLES
+    is summed over every SIMD.  Busy fraction = SQ_VALU_MFMA_BUSY_CYCLES /
+    (GRBM_GUI_ACTIVE / XCDs x CUs x 4 SIMDs): the share of SIMD-cycles of the
+    kernel in which the matrix unit was busy.  Writes
+    profiles/<kernel>_<workload>_mfma.txt."""
+    import csv
+    import collections
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            vals[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    for k in KERNEL_SOURCES:
+        rows = {name: cs for name, cs in vals.items() if k in name}
+        if not rows:
+            continue
+        acc = collections.defaultdict(list)
+        for cs in rows.values():
+            for c, v in cs.items():
+                acc[c].extend(v)
+        need = ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+        if any(c not in acc for c in need):
+            continue
+        avg = {c: sum(v) / len(v) for c, v in acc.items()}
+        util = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (avg["GRBM_GUI_ACTIVE"] / n_xcd * n_cu * 4)
+        out = os.path.join(PROFILE_DIR, f"{k}_{workload}_mfma.txt")
+        lines = [f"# rocprofv3 PMC summary: MFMA activity of {k}, {workload} workload",
+                 f"command: {cmd}",
+                 f"dispatches: {len(acc['GRBM_GUI_ACTIVE'])}"]
+        lines += [f"{c}_per_dispatch: {v:.0f}" for c, v in sorted(avg.items())]
+        lines += [f"mfma_busy_frac (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {n_xcd} XCDs x {n_cu} CUs x "
+                  f"4 SIMDs)): {util:.4f}",
+                  f"source_sha256_16: {source_hash(k)}"]
+        with open(out, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -589,6 +630,9 @@ def main():
                     help="profiler mode: run the TopK routing variant with this k")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="profiler mode: first copy this many MiB device to device (PMC calibration)")
+    ap.add_argument("--mfma-summary", nargs=3, metavar=("CSV", "WORKLOAD", "COMMAND"),
+                    help="write profiles/<kernel>_<workload>_mfma.txt from a rocprofv3 --pmc run of "
+                         "SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE")
     ap.add_argument("--pmc-summary", nargs=6,
                     metavar=("FETCH_CSV", "WRITE_CSV", "WORKLOAD", "CMD_FETCH", "CMD_WRITE", "CALIB_MIB"),
                     help="write profiles/<kernel>_<workload>_pmc.txt from two rocprofv3 --pmc runs")
@@ -596,6 +640,9 @@ def main():
 
     if args.profile_summary:
         write_profile_summary(*args.profile_summary)
+        return
+    if args.mfma_summary:
+        write_mfma_summary(*args.mfma_summary)
         return
     if args.pmc_summary:
         fc, wc, wl, cf, cw, mib = args.pmc_summary
