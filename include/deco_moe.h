@@ -54,7 +54,14 @@ typedef enum { DECO_DT_BF16 = 0, DECO_DT_F32 = 1 } deco_dtype;
 typedef enum {
   DECO_PATH_AUTO = 0,     /* decode path for T <= DECO_DECODE_MAX_T, else prefill   */
   DECO_PATH_DECODE = 1,   /* weight-streaming path; requires T <= DECO_DECODE_MAX_T */
-  DECO_PATH_PREFILL = 2   /* bucketed grouped-MFMA path; any T                      */
+  DECO_PATH_PREFILL = 2,  /* bucketed grouped-MFMA path; any T (the _PAIRS variant) */
+  DECO_PATH_PREFILL_PAIRS = 3,  /* prefill, expert-major down-projection into per-pair
+                                 * output rows, then a combine kernel; any layer     */
+  DECO_PATH_PREFILL_TOKEN = 4   /* prefill, token-major down-projection and combine in
+                                 * one kernel (no per-pair rows); slower than _PAIRS
+                                 * on the measured layers; d_ff / k-block <= 4 (bf16:
+                                 * d_ff <= 128, fp32: d_ff <= 64), else
+                                 * DECO_ERR_UNSUPPORTED                              */
 } deco_path;
 
 #define DECO_DECODE_MAX_T 16
@@ -168,9 +175,10 @@ int deco_moe_load_weights_gated(const deco_moe_config* cfg,
  * launches nothing.  Same as deco_moe_forward_path(..., DECO_PATH_AUTO). */
 int deco_moe_forward(const deco_moe_layer* L, const void* x, int64_t T, void* out, void* stream);
 
-/* As deco_moe_forward, with the kernel family chosen explicitly (both give
- * the same result up to fp32 summation order).  DECO_PATH_DECODE with
- * T > DECO_DECODE_MAX_T returns DECO_ERR_INVALID_ARG. */
+/* As deco_moe_forward, with the kernel family chosen explicitly (all give
+ * the same result up to rounding and fp32 summation order).  DECO_PATH_DECODE
+ * with T > DECO_DECODE_MAX_T returns DECO_ERR_INVALID_ARG; an unknown path
+ * DECO_ERR_INVALID_ARG. */
 int deco_moe_forward_path(const deco_moe_layer* L, const void* x, int64_t T, void* out,
                           void* stream, int path);
 

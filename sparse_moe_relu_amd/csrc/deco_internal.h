@@ -147,6 +147,7 @@ enum {
   KS_BWD_DENSE_DX,
   KS_BWD_COMBINE,
   KS_BWD_WGRAD,
+  KS_PRE_DC,
   KS_COUNT
 };
 const char* kernel_slot_name(int slot);
@@ -162,7 +163,9 @@ hipError_t plan_decode(deco_moe_layer* L);   // decode residency check (load tim
 hipError_t plan_prefill(deco_moe_layer* L);  // prefill launch shape (load time)
 hipError_t plan_backward(deco_moe_layer* L); // backward launch shape (load time, after plan_prefill)
 hipError_t launch_decode(const deco_moe_layer* L, const void* x, int T, void* out, hipStream_t s);
-hipError_t launch_prefill(const deco_moe_layer* L, const void* x, int T, void* out, hipStream_t s);
+// path: DECO_PATH_PREFILL (variant chosen here), _PAIRS or _TOKEN
+hipError_t launch_prefill(const deco_moe_layer* L, const void* x, int T, void* out, hipStream_t s, int path);
+bool prefill_token_ok(const deco_moe_layer* L);   // the token-major down-projection fits the layer
 hipError_t launch_dec_mask(const deco_moe_layer* L, int T, uint64_t* mask, hipStream_t s);
 // allocation-free decode (static device array as scratch)
 size_t decode_scratch_bytes(const deco_moe_layer* L);

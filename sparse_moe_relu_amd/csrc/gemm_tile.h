@@ -114,12 +114,14 @@ __device__ __forceinline__ void tile_mma(const i32x4_t* lds_a, const i32x4_t* ld
 // or panels: point them at any valid row or panel and drop those outputs).
 // Wave w = threadIdx.x / 64 computes rows (w / 2) * BM / 2 and panels
 // (w % 2) * BNP / 2 of the tile.  Ends with a barrier, so the caller may
-// reuse the ring at once.
+// reuse the ring at once.  `tid` is the thread's index in its group of 256
+// (a larger workgroup runs one tile per group of four waves, each group with
+// its own ring and the same number of steps, so the barriers line up).
 template <class DT, class TC, bool SWAP, class RowF, class PanelF>
 __device__ __forceinline__ void tile_gemm(i32x4_t* lds, RowF row, PanelF panel, int nkb,
-                                          f32x4_t (&acc)[TC::MB][TC::NBW]) {
+                                          f32x4_t (&acc)[TC::MB][TC::NBW], int tid) {
   using elem = typename DT::elem;
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, wm = w >> 1, wn = w & 1;
+  const int w = tid >> 6, l = tid & 63, wm = w >> 1, wn = w & 1;
   const int nsteps = (nkb + TC::KS - 1) / TC::KS;
   // this wave's loads: A blocks fa = w*NAW + i (rows 8 fa ..; lane l loads
   // row 8 fa + l / 8, chunk ch = (l % 8) ^ (l / 8)), B fragments fb = w*NBL + i
@@ -166,6 +168,12 @@ __device__ __forceinline__ void tile_gemm(i32x4_t* lds, RowF row, PanelF panel, 
     tile_mma<DT, TC, SWAP>(st, st + TC::A_V, acc, wm, wn, nkb - s * TC::KS);
   }
   lds_barrier();
+}
+
+template <class DT, class TC, bool SWAP, class RowF, class PanelF>
+__device__ __forceinline__ void tile_gemm(i32x4_t* lds, RowF row, PanelF panel, int nkb,
+                                          f32x4_t (&acc)[TC::MB][TC::NBW]) {
+  tile_gemm<DT, TC, SWAP>(lds, row, panel, nkb, acc, (int)threadIdx.x);
 }
 
 }  // namespace deco

@@ -204,6 +204,7 @@ const char* kernel_slot_name(int slot) {
     case KS_PRE_DISPATCH: return "k_pre_dispatch";
     case KS_PRE_EXPERT: return "k_pre_expert";
     case KS_PRE_COMBINE: return "k_pre_combine";
+    case KS_PRE_DC: return "k_pre_dc";
     case KS_BWD_SHARED: return "k_bwd_shared";
     case KS_BWD_EXPERT: return "k_bwd_expert";
     case KS_BWD_TOKEN: return "k_bwd_token";
@@ -332,7 +333,9 @@ static int load_layer(const deco_moe_config* cfg, const void* W_r, const float* 
   size_t o_lt = k.take(sizeof(int) * (size_t)E * Tcap);
   size_t o_sb = k.take((size_t)L->esz * Tcap * L->Fs);
   // pair buffer plus one scratch row that takes the stores of padding rows
-  size_t o_yb = k.take((size_t)L->esz * (Tcap * (E + 1) + 1) * L->d);
+  // (large batches: the pair slots' activation rows, F values of the
+  // down-projection operand type, in the same memory)
+  size_t o_yb = k.take(std::max((size_t)L->esz * L->d, dn_esz * L->F) * (Tcap * (E + 1) + 1));
   const size_t n_slots = Tcap * (E + 1) + 1;
   size_t o_sr = L->cfg.shared_rms ? k.take(sizeof(float) * Tcap * L->Fs) : 0;
   size_t o_dg = bwd ? k.take(sizeof(float) * Tcap * E) : 0;
@@ -472,8 +475,8 @@ int deco_moe_load_weights_gated(const deco_moe_config* cfg, const void* W_r, con
 int deco_moe_forward_path(const deco_moe_layer* L, const void* x, int64_t T, void* out, void* stream,
                           int path) {
   if (!L || T < 0 || T > L->maxT) return DECO_ERR_INVALID_ARG;
-  if (path != DECO_PATH_AUTO && path != DECO_PATH_DECODE && path != DECO_PATH_PREFILL)
-    return DECO_ERR_INVALID_ARG;
+  if (path < DECO_PATH_AUTO || path > DECO_PATH_PREFILL_TOKEN) return DECO_ERR_INVALID_ARG;
+  if (path == DECO_PATH_PREFILL_TOKEN && !deco_host::prefill_token_ok(L)) return DECO_ERR_UNSUPPORTED;
   if (T == 0) return DECO_OK;
   if (!x || !out) return DECO_ERR_INVALID_ARG;
   if (((uintptr_t)x % 16) != 0 || ((uintptr_t)out % 16) != 0) return DECO_ERR_INVALID_ARG;
@@ -487,7 +490,7 @@ int deco_moe_forward_path(const deco_moe_layer* L, const void* x, int64_t T, voi
   if (path == DECO_PATH_DECODE && !L->dec_ok) return DECO_ERR_UNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
   hipError_t err = path == DECO_PATH_DECODE ? deco_host::launch_decode(L, x, (int)T, out, s)
-                                            : deco_host::launch_prefill(L, x, (int)T, out, s);
+                                            : deco_host::launch_prefill(L, x, (int)T, out, s, path);
   // which path's routing state deco_moe_copy_routing returns
   const_cast<deco_moe_layer*>(L)->last_path = path;
   return err == hipSuccess ? DECO_OK : DECO_ERR_HIP;

@@ -39,6 +39,16 @@ void (*expert_kernel_m(int pF))(PreArgs) {
        : pF == 4 ? k_pre_expert<DT, 4, MODE, SMALL>
        : pF == 8 ? k_pre_expert<DT, 8, MODE, SMALL> : k_pre_expert<DT, 16, MODE, SMALL>;
 }
+// activation-output variants (the token-major down-projection follows)
+template <class DT, int MODE>
+void (*expert_act_kernel_m(int pF))(PreArgs) {
+  return pF == 2 ? k_pre_expert<DT, 2, MODE, false, true>
+       : pF == 4 ? k_pre_expert<DT, 4, MODE, false, true> : k_pre_expert<DT, 8, MODE, false, true>;
+}
+template <class DT>
+void (*dc_kernel(int nkf))(PreArgs) {
+  return nkf == 1 ? k_pre_dc<DT, 1, 2> : nkf == 2 ? k_pre_dc<DT, 2, 2> : k_pre_dc<DT, 4, 2>;
+}
 template <class DT>
 void (*expert_kernel(int pF, bool gated, bool small = false))(PreArgs) {
   if (gated) return expert_kernel_m<DT, XM_GATED, false>(pF);   // 64-row tiles already
@@ -51,6 +61,22 @@ void (*expert_kernel(int pF, bool gated, bool small = false))(PreArgs) {
 // a quarter of the tokens (the method's typical activation is about 20 %).
 // Measured (same box): 64-row tiles win up to T = 1024 on the d = 2048 layer
 // and at T = 256 on the d = 4096 one, and lose from T = 2048 on.
+// Token-major down-projection (k_pre_dc) instead of per-pair output rows
+// and a combine: only when asked for (DECO_PATH_PREFILL_TOKEN).  Measured on
+// the d = 2048 and d = 4096 layers at T = 128 .. 4096 it is slower than the
+// expert-major tiles at every size (c3 T = 4096: 283-293 against 235 us per
+// call): every (256-token, 128-column) block streams its column slice of all
+// experts' W_down, 1.8 MiB, and one CU pulls 30-60 GB/s from beyond its L2.
+int dc_nkf(const deco_moe_layer* L) { return L->F / L->KB; }
+long long dc_blocks(const deco_moe_layer* L, int T) {
+  return (long long)((T + 2 * GM - 1) / (2 * GM)) * ((L->pD + GP - 1) / GP);
+}
+bool use_dc(const deco_moe_layer* L, int T, int path) {
+  (void)L;
+  (void)T;
+  return path == DECO_PATH_PREFILL_TOKEN;
+}
+
 bool small_expert_tiles(const deco_moe_layer* L, int T) {
   const long long shared_tiles = (long long)((T + GM - 1) / GM) * ((L->pD + GP - 1) / GP);
   const long long expert_tiles = (long long)L->E * ((T / 4 + GM - 1) / GM);
@@ -58,16 +84,25 @@ bool small_expert_tiles(const deco_moe_layer* L, int T) {
 }
 
 template <class DT>
-hipError_t prefill(const deco_moe_layer* L, const void* x, int T, void* out, hipStream_t s) {
+hipError_t prefill(const deco_moe_layer* L, const void* x, int T, void* out, hipStream_t s, int path) {
   const PreArgs a = fill_pre_args(L, x, T, out);
   using deco_host::launch;
   hipError_t err = launch_routing<DT>(L, a, T, s);
-  if (err == hipSuccess)
-    err = launch(deco_host::KS_PRE_EXPERT, expert_kernel<DT>(L->pF, L->gated, small_expert_tiles(L, T)),
-                 dim3(L->pre_grid), dim3(256), s, a);
-  if (err == hipSuccess)
-    err = launch(deco_host::KS_PRE_COMBINE, k_pre_combine<DT>,
-                 dim3((unsigned)(((long long)T * (L->d / 8) + 255) / 256)), dim3(256), s, a);
+  if (use_dc(L, T, path)) {
+    if (err == hipSuccess)
+      err = launch(deco_host::KS_PRE_EXPERT,
+                   L->gated ? expert_act_kernel_m<DT, XM_GATED>(L->pF) : expert_act_kernel_m<DT, XM_FWD>(L->pF),
+                   dim3(L->pre_grid), dim3(256), s, a);
+    if (err == hipSuccess)
+      err = launch(deco_host::KS_PRE_DC, dc_kernel<DT>(dc_nkf(L)), dim3((unsigned)dc_blocks(L, T)), dim3(512), s, a);
+  } else {
+    if (err == hipSuccess)
+      err = launch(deco_host::KS_PRE_EXPERT, expert_kernel<DT>(L->pF, L->gated, small_expert_tiles(L, T)),
+                   dim3(L->pre_grid), dim3(256), s, a);
+    if (err == hipSuccess)
+      err = launch(deco_host::KS_PRE_COMBINE, k_pre_combine<DT>,
+                   dim3((unsigned)(((long long)T * (L->d / 8) + 255) / 256)), dim3(256), s, a);
+  }
   if (err != hipSuccess) return err;
   return hipGetLastError();
 }
@@ -76,10 +111,12 @@ hipError_t prefill(const deco_moe_layer* L, const void* x, int T, void* out, hip
 
 namespace deco_host {
 
-hipError_t launch_prefill(const deco_moe_layer* L, const void* x, int T, void* out, hipStream_t s) {
-  if (L->cfg.dtype == DECO_DT_BF16) return prefill<BF16>(L, x, T, out, s);
-  return prefill<F32>(L, x, T, out, s);
+hipError_t launch_prefill(const deco_moe_layer* L, const void* x, int T, void* out, hipStream_t s, int path) {
+  if (L->cfg.dtype == DECO_DT_BF16) return prefill<BF16>(L, x, T, out, s, path);
+  return prefill<F32>(L, x, T, out, s, path);
 }
+
+bool prefill_token_ok(const deco_moe_layer* L) { return dc_nkf(L) <= 4; }
 
 // Persistent grid of the expert kernel: as many workgroups as fit on the
 // device at once, a multiple of the 8 XCDs.

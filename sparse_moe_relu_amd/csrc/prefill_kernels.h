@@ -165,6 +165,21 @@ __device__ __forceinline__ void store4_pair(PT* p, const f32x4_t& v, bool& bad) 
   }
 }
 
+// 4 consecutive activation values at element `idx` of a row-major buffer of
+// the down-projection operand type (fp16: `bad` is raised for a value
+// outside the fp16 range)
+template <class DN>
+__device__ __forceinline__ void store4_act(void* base, size_t idx, const float* v, bool& bad) {
+  if constexpr (DN::KB == 32) {
+    bad |= !(fabsf(v[0]) <= FP16_MAX && fabsf(v[1]) <= FP16_MAX && fabsf(v[2]) <= FP16_MAX &&
+             fabsf(v[3]) <= FP16_MAX);
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(base) + idx) =
+        make_uint2(DN::bits(v[0]) | (DN::bits(v[1]) << 16), DN::bits(v[2]) | (DN::bits(v[3]) << 16));
+  } else {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(base) + idx) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+}
+
 // --------------------------------------------------------------------------
 // NS pipeline stages in LDS: 2 (64 KiB, two workgroups per CU) when the grid
 // exceeds the CUs, 4 (one per CU, three steps of loads in flight) when it
@@ -449,7 +464,7 @@ struct ExpertShape {
 // dg goes to dgbuf, dh~ and g*a to the pair-slot rows of dhbuf and agbuf
 // (operands of the weight gradients), the slot to slot_list, and
 // dh~ . W_up[e]^T (this pair's part of dLoss/dx) to the pair buffer.
-template <class DT, int BNP, int MODE, bool SMALL = false>
+template <class DT, int BNP, int MODE, bool SMALL = false, bool ACT = false>
 __global__ void __launch_bounds__(256, (ExpertShape<DT, BNP, MODE, SMALL>::OCC)) k_pre_expert(PreArgs a) {
   using elem = typename DT::elem;
   using S = ExpertShape<DT, BNP, MODE, SMALL>;
@@ -482,7 +497,8 @@ __global__ void __launch_bounds__(256, (ExpertShape<DT, BNP, MODE, SMALL>::OCC))
   __syncthreads();
   const int n_et = s_toff[a.E];
   const int nsp = (a.pD + GP - 1) / GP;                      // shared tiles per 128 rows
-  const int n_st = MODE == XM_BWD ? 0 : ((a.T + GM - 1) / GM) * nsp;   // the backward has no shared tiles
+  // the backward and the activation-output mode have no shared tiles
+  const int n_st = (MODE == XM_BWD || ACT) ? 0 : ((a.T + GM - 1) / GM) * nsp;
   const int xg = blockIdx.x % NXCD, lb = blockIdx.x / NXCD;
   const int gx = ((int)gridDim.x - xg + NXCD - 1) / NXCD;    // workgroups on this XCD
   const int e_beg = (int)((long long)n_et * xg / NXCD), e_end = (int)((long long)n_et * (xg + 1) / NXCD);
@@ -593,6 +609,16 @@ __global__ void __launch_bounds__(256, (ExpertShape<DT, BNP, MODE, SMALL>::OCC))
       auto panel_t = [&](int p) -> const char* { return Wt + frag_off(p, 0, a.nkb_d); };
       tile_gemm<DT, TC, true>(lds, row_d, panel_t, a.nkb_d, accu);
     }
+    // the mean-term values of the tile's rows, requested before the K loop so
+    // that they have landed when the NormSiLU needs them
+    float4 mpre[MB][NBW];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      const int tk = s_tok[wm * (BM / 2) + 16 * i + c];
+      const float* mrow = a.mbuf + (size_t)(tk < 0 ? 0 : tk) * F;
+#pragma unroll
+      for (int j = 0; j < NBW; ++j) mpre[i][j] = *reinterpret_cast<const float4*>(mrow + 16 * (wn * NBW + j) + 4 * g);
+    }
     tile_gemm<DT, TC, true>(lds, row, panel, a.nkb_d, acc);
 
     // NormSiLU.  Lane: local row R = wm*BM/2 + 16 i + c, columns
@@ -602,13 +628,11 @@ __global__ void __launch_bounds__(256, (ExpertShape<DT, BNP, MODE, SMALL>::OCC))
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
       const int R = wm * (BM / 2) + 16 * i + c;
-      const int tk = s_tok[R];
-      const float* mrow = a.mbuf + (size_t)(tk < 0 ? 0 : tk) * F;
       const float mk = a.no_mean ? 0.f : 1.f;   // ablation: no mean term
       float ss = 0.f;
 #pragma unroll
       for (int j = 0; j < NBW; ++j) {
-        const float4 m = *reinterpret_cast<const float4*>(mrow + 16 * (wn * NBW + j) + 4 * g);
+        const float4 m = mpre[i][j];
         acc[i][j][0] -= mk * m.x;
         acc[i][j][1] -= mk * m.y;
         acc[i][j][2] -= mk * m.z;
@@ -652,6 +676,7 @@ __global__ void __launch_bounds__(256, (ExpertShape<DT, BNP, MODE, SMALL>::OCC))
     // activations into LDS in the fragment order of the down-projection's
     // token operand (rounded once to the operand type); the backward puts
     // dh~ there and stores its pair rows
+    bool act_bad = false;
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
       const int R = wm * (BM / 2) + 16 * i + c;
@@ -689,7 +714,11 @@ __global__ void __launch_bounds__(256, (ExpertShape<DT, BNP, MODE, SMALL>::OCC))
             if constexpr (MODE == XM_GATED) v[ii] *= accu[i][j][ii];
           }
         }
-        if constexpr (DN::KB == 32) {
+        if constexpr (ACT) {
+          // the pair slot's activation row, ungated, in the down-projection
+          // operand type (row-major, F values)
+          if (ok) store4_act<DN>(a.ybuf, (size_t)s_slot[R] * F + 16 * p + 4 * g, v, act_bad);
+        } else if constexpr (DN::KB == 32) {
           // f = 16 p + 4 g + ii: k-block p / 2, lane group 2 (p % 2) + g / 2,
           // elements 4 (g % 2) + ii of the lane
           const int slot = ((R >> 4) * NKF + (p >> 1)) * 64 + (R & 15) + 16 * (2 * (p & 1) + (g >> 1));
@@ -701,6 +730,10 @@ __global__ void __launch_bounds__(256, (ExpertShape<DT, BNP, MODE, SMALL>::OCC))
               make_float4(v[0], v[1], v[2], v[3]);
         }
       }
+    }
+    if constexpr (ACT) {
+      if (act_bad) atomicOr(a.err, 32u);
+      continue;   // the down-projection runs in k_pre_dc
     }
     lds_barrier();
     // each wave keeps the activations of its token blocks in registers
@@ -866,6 +899,326 @@ __global__ void __launch_bounds__(256) k_pre_combine(PreArgs a) {
 int round4(int v) { return (v + 3) / 4 * 4; }
 
 // launch arguments shared by the forward and backward launchers
+// --------------------------------------------------------------------------
+// Down-projection and combine, token-major (large batches; F <= 4 k-blocks).
+//
+// A workgroup of 256 NG threads owns the output block rows m0 .. m0 + 128 NG
+// and panels p0 .. p0 + 7 (128 columns).  Wave w: rows (w / 2) * 64 + 0..63 of
+// the block, panels (w % 2) * 4 + 0..3; its lane (c, g) accumulates rows
+// 16 i + c (i < 4) of those 64 and columns 4 g .. 4 g + 3 of each panel (the
+// swapped-operand layout of the tile GEMM).
+//   1. acc = S[rows] . Ws_down[:, cols] with S = the shared expert's
+//      activations (one tile GEMM per group of four waves, 128 rows each).
+//   2. For every expert touched by the block's tokens, in ascending order:
+//      W_down[e][:, cols] arrives in a ring of three LDS stages (one expert
+//      per stage, two in flight, shared by all waves).  Each wave lists its
+//      own rows routed to e (a ballot over its 64 rows; the pair slot of row
+//      t is its token's slot base plus the number of lower experts it uses),
+//      loads those rows' activation fragments from the pair-slot buffer one
+//      expert ahead, multiplies them by W_down[e], scales each row by its gate
+//      and adds it to the owning lanes' accumulators through a staging block
+//      of its own in LDS (16 gathered rows at a time, no workgroup barrier).
+//   3. out = acc, rounded once.
+// Every output element gets the shared term first and then its token's
+// experts in ascending order, in fp32, on every call: the result does not
+// depend on scheduling, and no per-pair output rows go through memory.
+// LDS stores issued as inline asm.  While LDS-DMA loads are in flight the
+// compiler cannot tell an ordinary LDS store from one that may overlap their
+// destination and drains every outstanding load before it; these stores go
+// to LDS that no DMA targets, and a wave's LDS accesses are performed in
+// order, so reads later in the same wave see them.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+__device__ __forceinline__ void lds_store16(void* p, float x, float y, float z, float w) {
+  const f32x4_t v = {x, y, z, w};
+  __asm__ volatile("ds_write_b128 %0, %1" ::"v"(lds_addr(p)), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_store4(void* p, uint32_t v) {
+  __asm__ volatile("ds_write_b32 %0, %1" ::"v"(lds_addr(p)), "v"(v) : "memory");
+}
+template <class DT, int NKF, int NG>
+struct DcShape {
+  using TD = Tile<DT, GM, GP, 2>;                       // shared GEMM of one row group
+  static constexpr int NT = 256 * NG, NW = 4 * NG, BT = GM * NG;
+  static constexpr int WSTAGE_V = GP * NKF * 64;        // W_down slots of one expert (8 panels)
+  static constexpr int NWS = 3;                         // W_down ring stages
+  static constexpr int WPW = GP * NKF / NW;             // ring loads per wave per stage
+  static constexpr int SP = 68;                         // floats per staged row (64 + 4 pad)
+  static constexpr int STG_V = 16 * SP / 4;             // one wave's staging block (16-byte slots)
+  static constexpr int PF_RB = 2;                       // row blocks per wave loaded one expert ahead
+  static constexpr int MAXW = 4;                        // mask words (at most 256 experts)
+  static constexpr int RING1_V = NG * TD::LDS_V;
+  static constexpr int P2_V = NWS * WSTAGE_V + NW * STG_V;
+  static constexpr int BIG_V = RING1_V > P2_V ? RING1_V : P2_V;
+  // tables after the big region (bytes): masks, touched experts and their
+  // count, the any-token words, per-wave lists (slot, gate, position) x 2
+  static constexpr int T_MASK = 0;
+  static constexpr int T_ANY = T_MASK + BT * MAXW * 8;
+  static constexpr int T_EX = T_ANY + MAXW * 8;
+  static constexpr int T_WL = T_EX + 260 * 4;
+  static constexpr int T_WG = T_WL + NW * 2 * 64 * 4;
+  static constexpr int T_WP = T_WG + NW * 2 * 64 * 4;
+  static constexpr int T_END = T_WP + NW * 2 * 64 * 4;
+  static constexpr int LDS_V = BIG_V + (T_END + 15) / 16;
+  static_assert(WPW * NW == GP * NKF && WPW >= 1, "ring fragments must divide over the waves");
+  static_assert(PF_RB == 2, "the kernel selects the prefetched row blocks by rb == 0 / 1");
+  static_assert(LDS_V * 16 <= 160 * 1024, "LDS budget");
+};
+
+template <class DT, int NKF, int NG>
+__global__ void __launch_bounds__(256 * NG, 1) k_pre_dc(PreArgs a) {
+  using elem = typename DT::elem;
+  using DN = typename DT::Down;
+  using S = DcShape<DT, NKF, NG>;
+  using TD = typename S::TD;
+  constexpr int NW = S::NW, BT = S::BT, MAXW = S::MAXW, SP = S::SP, PF_RB = S::PF_RB;
+  __shared__ i32x4_t lds[S::LDS_V];
+  char* tab = reinterpret_cast<char*>(lds + S::BIG_V);
+  uint64_t* s_mask = reinterpret_cast<uint64_t*>(tab + S::T_MASK);
+  unsigned long long* s_any = reinterpret_cast<unsigned long long*>(tab + S::T_ANY);
+  int* s_ex = reinterpret_cast<int*>(tab + S::T_EX);             // [256] experts, [256] their count
+  int (*s_wl)[2][64] = reinterpret_cast<int (*)[2][64]>(tab + S::T_WL);
+  float (*s_wg)[2][64] = reinterpret_cast<float (*)[2][64]>(tab + S::T_WG);
+  int (*s_wp)[2][64] = reinterpret_cast<int (*)[2][64]>(tab + S::T_WP);
+
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, g = l >> 4;
+  const int wr = w >> 1, wc = w & 1;
+  const int n_tt = (a.T + BT - 1) / BT;
+  const int t = xcd_tile(blockIdx.x, gridDim.x);   // column-tile major: an XCD keeps few W_down slices
+  const int m0 = (t % n_tt) * BT, p0 = (t / n_tt) * GP;
+  const int nw = a.W;
+
+  // ---- routing masks of the block's rows; experts touched by any of them
+  if (tid < MAXW) s_any[tid] = 0ull;
+  lds_barrier();
+  // row role: lane l of wave w stands for block row wr*64 + l (both waves of
+  // a row pair hold the same rows)
+  const int rloc = wr * 64 + l, rrow = m0 + rloc;
+  const bool rvalid = rrow < a.T;
+  const int rslot0 = rvalid ? a.tok_off[rrow] + 1 : 0;   // slot 0 of a token is its shared expert's
+  if (wc == 0) {
+    for (int ww = 0; ww < nw; ++ww) {
+      const uint64_t v = rvalid ? a.mask[(size_t)rrow * nw + ww] : 0ull;
+      s_mask[rloc * MAXW + ww] = v;
+      if (v) atomicOr(&s_any[ww], (unsigned long long)v);
+    }
+  }
+  lds_barrier();
+  if (w == 0) {
+    int base = 0;
+    for (int q = 0; q < nw; ++q) {
+      const int e = 64 * q + l;
+      const bool bit = e < a.E && ((s_any[q] >> l) & 1ull);
+      const uint64_t bal = __ballot(bit);
+      const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+      if (bit) s_ex[base + pos] = e;
+      base += __popcll(bal);
+    }
+    if (l == 0) s_ex[256] = base;
+  }
+
+  // ---- 1. shared expert: acc = S[rows] . Ws_down[:, cols]
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  {
+    const int grp = w >> 2;
+    const elem* sb = (const elem*)a.sbuf;
+    const int rg0 = m0 + grp * GM;
+    auto row = [&](int r) -> const elem* {
+      const int rr = rg0 + r;   // rows past T read row T - 1; their outputs are dropped
+      return sb + (size_t)(rr < a.T ? rr : a.T - 1) * a.Fs;
+    };
+    auto panel = [&](int p) -> const char* {
+      const int q = p0 + p;
+      return a.Wsd_p + frag_off(q < a.pD ? q : 0, 0, a.nkb_Fs);
+    };
+    tile_gemm<DT, TD, true>(lds + grp * TD::LDS_V, row, panel, a.nkb_Fs, acc, tid & 255);
+  }   // ends with a barrier: s_ex is visible and the LDS ring is free
+
+  // ---- 2. routed experts
+  const int n_ex = s_ex[256];
+  if (n_ex > 0) {
+    i32x4_t* wring = lds;
+    float* stg = reinterpret_cast<float*>(lds + S::NWS * S::WSTAGE_V + w * S::STG_V);
+    const __attribute__((address_space(3))) float* stg3 = (const __attribute__((address_space(3))) float*)stg;
+    const size_t act_row = (size_t)NKF * 64;   // bytes of one activation row (F values)
+    const char* actb = (const char*)a.ybuf;
+    // the touched experts (lane l holds entries l, 64 + l, ..) and this
+    // lane's row mask in registers: no LDS round trip per expert
+    int exr[MAXW];
+    uint64_t rmask[MAXW];
+#pragma unroll
+    for (int q = 0; q < MAXW; ++q) {
+      exr[q] = s_ex[64 * q + l];
+      rmask[q] = q < nw ? s_mask[rloc * MAXW + q] : 0ull;
+    }
+    // (u uniform; the lane is read straight from each register, so the
+    // result does not depend on which lanes are active at the call)
+    auto expert_of = [&](int u) -> int {
+      const int uu = u < n_ex ? u : n_ex - 1;
+      const int q = uu >> 6, ln = uu & 63;
+      const int e0 = __builtin_amdgcn_readlane(exr[0], ln), e1 = __builtin_amdgcn_readlane(exr[1], ln);
+      const int e2 = __builtin_amdgcn_readlane(exr[2], ln), e3 = __builtin_amdgcn_readlane(exr[3], ln);
+      return q == 0 ? e0 : q == 1 ? e1 : q == 2 ? e2 : e3;
+    };
+    // W_down[e][:, cols] of touched expert u into ring stage u % 3 (past the
+    // end: the last expert again, never read)
+    auto issue_w = [&](int u) {
+      const int e = expert_of(u);
+      i32x4_t* st = wring + (u % S::NWS) * S::WSTAGE_V;
+      const char* base = a.Wdn16_p + (size_t)e * a.dn_stride;
+#pragma unroll
+      for (int i = 0; i < S::WPW; ++i) {
+        const int f = w * S::WPW + i;   // panel f / NKF of the block, k-block f % NKF
+        const int q = p0 + f / NKF;
+        load_lds16(base + frag_off(q < a.pD ? q : 0, f % NKF, NKF) + l * 16, st + f * 64);
+      }
+    };
+    // this wave's rows routed to touched expert u: list (parity u & 1), each
+    // row's position in it, and the count
+    int rank = 0;
+    auto build = [&](int u, bool& bit, int& pos) -> int {
+      const int e = expert_of(u);
+      const int q = e >> 6;
+      const uint64_t mw = q == 0 ? rmask[0] : q == 1 ? rmask[1] : q == 2 ? rmask[2] : rmask[3];
+      bit = u < n_ex && ((mw >> (e & 63)) & 1ull);
+      const uint64_t bal = __ballot(bit);
+      pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+      const int b = u & 1;
+      if (bit) lds_store4(&s_wl[w][b][pos], (uint32_t)(rslot0 + rank));
+      lds_store4(&s_wp[w][b][l], (uint32_t)(bit ? pos : -1));
+      rank += bit ? 1 : 0;
+      return (int)__popcll(bal);
+    };
+    // activation fragments of the first PF_RB row blocks of list u, and the
+    // gate of this lane's row
+    auto issue_act = [&](int u, int n, i32x4_t (&av)[PF_RB][NKF], bool bit, float& gate) {
+      const int b = u & 1;
+      int slot[PF_RB];
+#pragma unroll
+      for (int rb = 0; rb < PF_RB; ++rb) {
+        const int p = 16 * rb + c;
+        slot[rb] = p < n ? s_wl[w][b][p] : 0;   // rows past the list: any valid row, unused
+      }
+#pragma unroll
+      for (int rb = 0; rb < PF_RB; ++rb) {
+        if (16 * rb >= n) break;   // no rows in this block (the count is the same for the whole wave)
+        const char* src = actb + (size_t)slot[rb] * act_row + g * 16;
+#pragma unroll
+        for (int kb = 0; kb < NKF; ++kb) av[rb][kb] = ld16(src + kb * 64);
+      }
+      const int e = expert_of(u);
+      gate = a.g[bit ? (size_t)rrow * a.E + e : 0];
+    };
+    // two register sets, used alternately (a copy from one to the other
+    // would wait for the loads just issued)
+    struct Unit {
+      i32x4_t av[PF_RB][NKF];
+      bool bit;
+      int pos, n;
+      float gate;
+    };
+    Unit ua, ub;
+    ua.n = build(0, ua.bit, ua.pos);
+    issue_act(0, ua.n, ua.av, ua.bit, ua.gate);
+    issue_w(0);
+    issue_w(1);
+    auto step = [&](int u, Unit& cu, Unit& nx) {
+      // stage u of W_down (issued two experts ago) and this wave's activation
+      // loads of expert u (issued before the ring loads of u + 1) have landed
+      wait_vmcnt<S::WPW>();
+      if (cu.bit) lds_store4(&s_wg[w][u & 1][cu.pos], __float_as_uint(cu.gate));
+      lds_barrier();   // stage u visible to all waves; stage u - 1 no longer read
+      nx.n = build(u + 1, nx.bit, nx.pos);
+      issue_act(u + 1, nx.n, nx.av, nx.bit, nx.gate);
+      issue_w(u + 2);
+      // expert u on this wave's rows: 16 gathered rows at a time
+      const i32x4_t* st = wring + (u % S::NWS) * S::WSTAGE_V;
+      const int n_c = cu.n, b = u & 1;
+      const int nb = (n_c + 15) >> 4;
+      // positions of the owned rows 16 i + c in the list (-1: not routed)
+      int pos_i[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pos_i[i] = s_wp[w][b][16 * i + c];
+      for (int rb = 0; rb < nb; ++rb) {
+        const int p = 16 * rb + c;
+        const float gt = p < n_c ? s_wg[w][b][p] : 0.f;
+        i32x4_t av[NKF];
+        if (rb < PF_RB) {
+#pragma unroll
+          for (int kb = 0; kb < NKF; ++kb) av[kb] = rb == 0 ? cu.av[0][kb] : cu.av[PF_RB - 1][kb];
+        } else {
+          // more than PF_RB * 16 rows of this wave use the expert: the rest
+          // are loaded here
+          const int slot = p < n_c ? s_wl[w][b][p] : 0;
+          const char* src = actb + (size_t)slot * act_row + g * 16;
+#pragma unroll
+          for (int kb = 0; kb < NKF; ++kb) av[kb] = ld16(src + kb * 64);
+        }
+        f32x4_t y[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) y[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < NKF; ++kb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) DN::mma(y[j], st[((wc * 4 + j) * NKF + kb) * 64 + l], av[kb]);
+        // lane: gathered row 16 rb + c, columns 16 j + 4 g .. of the wave's 64
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          lds_store16(stg + c * SP + 16 * j + 4 * g, y[j][0] * gt, y[j][1] * gt, y[j][2] * gt, y[j][3] * gt);
+        // the staging block is this wave's alone, written before these reads
+        // (a wave's LDS accesses are performed in order): every owned row
+        // reads a staged row (row 0 when it has none in this block) and keeps
+        // it only when it is its own
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          f32x4_t v[2][4];
+          bool own[2];
+#pragma unroll
+          for (int ii = 0; ii < 2; ++ii) {
+            const int pp = pos_i[2 * h + ii] - 16 * rb;
+            own[ii] = pp >= 0 && pp < 16;
+            const int r = own[ii] ? pp : 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              v[ii][j] = *(const __attribute__((address_space(3))) f32x4_t*)(stg3 + r * SP + 16 * j + 4 * g);
+          }
+#pragma unroll
+          for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+              for (int k = 0; k < 4; ++k) acc[2 * h + ii][j][k] += own[ii] ? v[ii][j][k] : 0.f;
+        }
+        // the next block's staging writes come after these reads (in order)
+        __asm__ volatile("" ::: "memory");
+      }
+    };
+    for (int u = 0; u < n_ex; u += 2) {
+      step(u, ua, ub);
+      if (u + 1 < n_ex) step(u + 1, ub, ua);
+    }
+  }
+
+  // ---- 3. out = acc
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = m0 + wr * 64 + 16 * i + c;
+    if (r >= a.T) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int q = p0 + wc * 4 + j;
+      if (q < a.pD)
+        store4<DT>((elem*)a.out + (size_t)r * a.d + 16 * q + 4 * g, acc[i][j][0], acc[i][j][1], acc[i][j][2],
+                   acc[i][j][3]);
+    }
+  }
+}
+
 PreArgs fill_pre_args(const deco_moe_layer* L, const void* x, int T, void* out) {
   PreArgs a;
   memset(&a, 0, sizeof(a));
