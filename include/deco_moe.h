@@ -122,17 +122,23 @@ int deco_moe_check_config(const deco_moe_config* cfg);
  * Computes Wbar = mean over all E routed experts of W_up (the NormSiLU mean
  * term is precomputable because inference weights are fixed: qidianchuan.cn
  * write-up, section 二, expert design) in fp32 and packs it, in the layer
- * dtype, next to the experts' weights; the forward pass forms x.Wbar once per
- * token and subtracts it from every expert's up-projection.  Runs on
+ * dtype, next to the experts' weights; the prefill path forms x.Wbar once per
+ * token and subtracts it from every expert's up-projection.  The decode path
+ * multiplies x by W_up[e] - Wbar instead, packed once more at load (the
+ * difference in fp32, rounded once to fp16 for bf16 layers, fp32 for fp32
+ * layers; not with the mean-term ablation).  Runs on
  * `stream` and synchronizes it
  * before returning, so the sources may be freed afterwards.  On success
  * *out_layer receives the new layer; on failure it is set to NULL and nothing
  * stays allocated.  bf16 layers run the routed down-projection on fp16
  * operands (W_down and the gated activations; the paths' fp32 accumulation
  * is unchanged): a W_down entry whose magnitude exceeds the fp16 range
- * (65504), or a NaN, gets DECO_ERR_UNSUPPORTED.  Activations or pair rows
- * that leave the fp16 range at run time (very large gates) set error bit 5
- * (see deco_moe_read_error_flags). */
+ * (65504), or a NaN, gets DECO_ERR_UNSUPPORTED, and so does, with the mean
+ * term, a W_up entry (the NormSiLU input) beyond 32752, half the fp16 range
+ * (|W_up - Wbar| <= 2 max |W_up|).  Activations or pair rows that leave the
+ * fp16 range at run time (very large gates), or an x value beyond it on the
+ * decode path (x enters the folded product converted to fp16), set error
+ * bit 5 (see deco_moe_read_error_flags). */
 /* Device memory of a layer, besides its packed weights: a per-layer part of
  * about max(16, max_tokens) x (8E + 4F) bytes plus the decode path's
  * hand-off state (under 1 MB at the sizes here), and the prefill/backward
@@ -265,12 +271,15 @@ float deco_moe_sparsity_coef_update(float coef, float active_ratio, float target
  * work on the device) and cleared by the read.  Bit 0: an in-kernel
  * hand-off between workgroups of the decode path timed out (the output of
  * that call is not valid); the bit naming the hand-off is set with it:
- * 2 the mean term x.Wbar, 4 an expert's per-row sums of squares (NormSiLU's
- * RMS across column slices), 8 the TopK logits, 16 the shared expert's sums
- * of squares (shared_rms layers).  The prefill and backward kernels never
+ * 4 an expert's per-row sums of squares (NormSiLU's RMS across column
+ * slices), 8 the TopK logits, 16 the shared expert's sums of squares
+ * (shared_rms layers); bit 1 (2) is no longer used (the mean term is folded
+ * into the decode path's matrices).  The prefill and backward kernels never
  * wait on other workgroups.  Bit 5 (32), any path of a bf16 layer: a value
  * of the down-projection's fp16 operands or of the fp16 pair rows left the
- * fp16 range (a gate too large for it); that call's output is not valid.
+ * fp16 range (a gate too large for it), or, on the decode path, an x value
+ * did (it enters the folded NormSiLU-input product in fp16); that call's
+ * output is not valid.
  * Returns DECO_ERR_INVALID_ARG on NULL arguments. */
 int deco_moe_read_error_flags(const deco_moe_layer* L, uint32_t* flags);
 

@@ -26,7 +26,6 @@ struct deco_moe_layer {
   // decode launch plan (plan_decode_sizes, plan_decode)
   int dec_np;              // 16-column panels per up-kernel slice
   int dec_S;               // column slices per routed expert
-  int dec_n_mean;          // mean-term workgroups (one per routed slice position; 0 without the mean term)
   int dec_n_shs, dec_nsub, dec_n_sh;   // shared slices, slices per shared workgroup, shared workgroups
   int dec_grid_up;
   int dec_Fp, dec_Fsp;     // F, Fs padded to whole column-pair fragments (2 k-blocks)
@@ -45,6 +44,8 @@ struct deco_moe_layer {
   char* Wup_p;             // per expert [pF][nkb_d] frags of the NormSiLU input projection
                            // (W_up[e]; W_gate[e] for gated experts)
   char* Wlin_p;            // gated experts: per expert [pF][nkb_d] frags of W_up[e]; else null
+  char* Wupm_p;            // per expert [pF][nkb_d] frags of Wup - Wbar (the decode path's NormSiLU
+                           // input with the mean term folded in); null with the mean-term ablation
   char* Wbar_p;            // [pF][nkb_d] frags of Wbar, the mean of the Wup_p matrices (layer dtype)
   char* Wdn_p;             // per expert [pD][nkb_F] frags
   char* Wdn16_p;           // bf16 layers: W_down again, in fp16 (prefill); fp32 layers: = Wdn_p
@@ -155,7 +156,10 @@ const char* kernel_slot_name(int slot);
 // launchers (return hipSuccess or the launch error)
 // W_norm: the projection NormSiLU acts on (W_up, or W_gate for gated
 // experts); W_lin: gated experts' W_up (null otherwise)
-hipError_t check_down_range(deco_moe_layer* L, const void* W_down, hipStream_t s, bool* ok);
+// bf16 layers: *ok = W_down fits fp16 (the prefill down-projection operand)
+// and, with the mean term, max |W_norm| <= 32752 (the decode path's folded
+// NormSiLU input W_norm - Wbar in fp16)
+hipError_t check_down_range(deco_moe_layer* L, const void* W_down, const void* W_norm, hipStream_t s, bool* ok);
 hipError_t launch_pack_all(deco_moe_layer* L, const void* W_r, const void* W_norm, const void* W_lin,
                            const void* W_down, const void* Ws_up, const void* Ws_down, hipStream_t s);
 void plan_decode_sizes(deco_moe_layer* L, int n_cu);   // decode slices and buffer sizes (load time)

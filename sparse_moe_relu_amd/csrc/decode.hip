@@ -7,22 +7,24 @@
 // with Table 4) attributes its speedup to skipping the memory traffic of
 // inactive experts.  Two kernels:
 //
-//   k_dec_up    one workgroup per column slice of the inter-expert mean
-//               term (x.Wbar), per group of column slices of the shared
+//   k_dec_up    one workgroup per group of column slices of the shared
 //               expert's up-projection, and per (routed expert, column
 //               slice).  A routed workgroup computes its expert's router
 //               logits for the batch (router: linear projection + bias, ReLU,
 //               per-expert scale; DECO paper Sec. 2 "Router design") and
-//               exits without reading any expert weight when no token
-//               activated the expert.  Otherwise it streams its slice of
-//               W_up[e] through v_mfma 16x16 products (tokens padded to 16
-//               rows), subtracts the mean term (published by the mean
-//               workgroups), takes the row's RMS over all F columns (the
-//               per-row sums of squares of the other slices of the same
-//               expert are exchanged through device memory), applies SiLU and
-//               the gate, and stores the activations as the down-projection
-//               operand (NormSiLU: qidianchuan.cn write-up, section 二:
-//               subtract the mean term, RMS inside the expert, then SiLU).
+//               exits without using any expert weight when no token
+//               activated the expert (from T = 8 on it requests its W_up
+//               slice together with the router operands and drops it then).
+//               Otherwise it streams its slice of W_up[e] - Wbar through
+//               v_mfma 16x16 products (tokens padded to 16 rows): the mean
+//               term is folded into the matrix packed at load, x.(W_up[e] -
+//               Wbar) = x.W_up[e] - x.Wbar.  It takes the row's RMS over all
+//               F columns (the per-row sums of squares of the other slices of
+//               the same expert are exchanged through device memory), applies
+//               SiLU and the gate, and stores the activations as the
+//               down-projection operand (NormSiLU: qidianchuan.cn write-up,
+//               section 二: subtract the mean term, RMS inside the expert,
+//               then SiLU).
 //   k_dec_down  one workgroup per 8 output columns.  It lists the experts
 //               the batch touched and multiplies their down-projection rows
 //               for its 8 columns (and the shared expert's) with the
@@ -30,15 +32,15 @@
 //               every touched expert happens inside the workgroup, so each
 //               output is written once, with no partial sums.
 //
-// Hand-offs inside k_dec_up (mean term, sums of squares, TopK logits) are
+// Hand-offs inside k_dec_up (sums of squares, TopK logits) are
 // 64-bit words written and read with agent-scope relaxed atomics: the high
 // half is the call's epoch and the low half the value, so a reader needs no
 // separate flag and no fence, and a word left from an earlier call is never
 // taken for this call's.  Each workgroup takes the epoch from an atomic
 // increment of its own counter word (every call increments every counter
 // once, so they stay equal and no two workgroups contend).  Waiting workgroups only
-// depend on the mean-term workgroups (launched first) and on the other slices
-// of their own expert (consecutive workgroups); every wait is bounded (a
+// depend on the other slices of their own expert (consecutive workgroups) and,
+// with TopK routing, on every routed workgroup; every wait is bounded (a
 // timeout sets the layer's error flag).
 #include <string.h>
 
@@ -59,17 +61,22 @@ constexpr int SPIN_LIMIT = 1 << 20;
 constexpr int NSUB_MAX = 4;       // shared-expert slices per workgroup
 typedef unsigned long long u64;
 
+#ifndef DEC_SPEC_MIN_T
+#define DEC_SPEC_MIN_T 8
+#endif
+
 struct DecArgs {
   const void* x;
   void* out;
   int T, d, E, F, Fs, W;
   int nkb_d;                // k-blocks of d
   int S;                    // column slices per routed expert
-  int n_mean, n_sh, nsub;   // mean-term workgroups, shared workgroups, shared slices per workgroup
+  int n_sh, nsub;           // shared workgroups, shared slices per workgroup
   int n_shs;                // shared slices
   int pF, pFs;              // 16-column panels of F and Fs
   int top_k;                // TopK routing variant (0: ReLU routing)
   int no_rms;               // NormSiLU ablation: no RMS step
+  int spec;                 // routed workgroups request their W_up slice before the routing decision
   float eps;
   const char* Wr_p;
   const char* Wup_p;        // NormSiLU input projection (a gated expert's gate projection)
@@ -85,7 +92,7 @@ struct DecArgs {
   float* g;                 // [T][E] gates
   unsigned char* act8;      // [16][E] routing decisions
   unsigned* rflag;          // [E] 1: no token routed to e, 2: some token was
-  u64* hw;                  // hand-off words: [16][F] mean term | [E * S][16] sums of squares |
+  u64* hw;                  // hand-off words: [E * S][16] sums of squares |
                             // [E][16] logits (TopK) | [n_sh][16] shared sums of squares
   unsigned* ctr;            // [grid] epoch counters, one per up-kernel workgroup
   void* arow;               // [E][16][Fp] routed activations, down operand type
@@ -95,8 +102,7 @@ struct DecArgs {
   unsigned* err;
 };
 
-__device__ __forceinline__ u64* hw_m(const DecArgs& a) { return a.hw; }
-__device__ __forceinline__ u64* hw_ss(const DecArgs& a) { return a.hw + (size_t)16 * a.F; }
+__device__ __forceinline__ u64* hw_ss(const DecArgs& a) { return a.hw; }
 __device__ __forceinline__ u64* hw_z(const DecArgs& a) { return hw_ss(a) + (size_t)a.E * a.S * 16; }
 __device__ __forceinline__ u64* hw_sh(const DecArgs& a) { return hw_z(a) + (size_t)a.E * 16; }
 
@@ -112,8 +118,8 @@ __device__ __forceinline__ float word_val(u64 v) { return __uint_as_float((unsig
 // Block-wide wait: every thread holds N words (already loaded from p[i];
 // need marks those that matter); returns once all carry epoch ep, reloading the
 // invalid ones.  Bounded: a timeout sets bit 0 of *err and the bit `which`
-// naming the hand-off (2 mean term, 4 sums of squares, 8 TopK logits, 16
-// shared sums of squares).
+// naming the hand-off (4 sums of squares, 8 TopK logits, 16 shared sums of
+// squares).
 template <int N>
 __device__ __forceinline__ void wait_words(u64 (&v)[N], const u64* const (&p)[N], const bool (&need)[N],
                                            unsigned ep, unsigned* err, unsigned which) {
@@ -146,10 +152,26 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uns
 // (panels at or past pmax read panel pmax - 1; their results are dropped by
 // the caller).  Loads go in batches of 8 k-blocks x NP panels (up to 32
 // fragments) issued together.  x rows past T read zeros (buffer range).
-template <class DT, int NP>
+// 8 bf16 values -> 8 fp16 values (exact inside fp16's range); `bad` is
+// raised for a value outside it
+__device__ __forceinline__ i32x4_t bf16x8_to_f16x8(const i32x4_t& v, bool& bad) {
+  i32x4_t r;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t u = (uint32_t)v[q];
+    const float f0 = bf16_to_f32(u & 0xFFFFu), f1 = bf16_to_f32(u >> 16);
+    bad |= !(fabsf(f0) <= 65504.f && fabsf(f1) <= 65504.f);
+    r[q] = (int)(FP16::bits(f0) | (FP16::bits(f1) << 16));
+  }
+  return r;
+}
+
+// XH: the W fragments are fp16 (bf16 layers' folded NormSiLU input) and the
+// x fragments are converted to fp16 for the product
+template <class DT, int NP, bool XH = false>
 __device__ __forceinline__ void up_stream(__amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rw, int p0, int pmax,
                                           int nkb, int kb_lo, int kb_hi, int d, f32x4_t (&acc)[NP],
-                                          bool x_loaded, const i32x4_t* x0) {
+                                          bool x_loaded, const i32x4_t* x0, bool* xbad = nullptr) {
   using elem = typename DT::elem;
   constexpr int U = 8;
   const int l = threadIdx.x & 63, c = l & 15, g = l >> 4;
@@ -171,8 +193,14 @@ __device__ __forceinline__ void up_stream(__amdgpu_buffer_rsrc_t rx, __amdgpu_bu
 #pragma unroll
     for (int u = 0; u < U; ++u)
       if (kb0 + u < kb_hi) {
+        if constexpr (XH) {
+          const i32x4_t xh = bf16x8_to_f16x8(xf[u], *xbad);
 #pragma unroll
-        for (int p = 0; p < NP; ++p) DT::mma(acc[p], xf[u], wf[u][p]);
+          for (int p = 0; p < NP; ++p) FP16::mma(acc[p], xh, wf[u][p]);
+        } else {
+#pragma unroll
+          for (int p = 0; p < NP; ++p) DT::mma(acc[p], xf[u], wf[u][p]);
+        }
       }
   }
 }
@@ -203,6 +231,9 @@ template <class DT, int NP, int VAR>
 __global__ void __launch_bounds__(DNT) k_dec_up(DecArgs a) {
   constexpr bool GT = (VAR & DV_GATED) != 0, NM = (VAR & DV_NO_MEAN) != 0, SR = (VAR & DV_SHARED_RMS) != 0;
   using elem = typename DT::elem;
+  // bf16 layers with the mean term: the NormSiLU input matrix is the folded
+  // W - Wbar in fp16, multiplied by x converted to fp16
+  constexpr bool XH = sizeof(elem) == 2 && !NM;
   using DN = typename DT::Down;
   constexpr int U = 8;             // k-blocks per load batch
   constexpr int NCOL = 16 * NP;    // columns of a slice
@@ -220,10 +251,10 @@ __global__ void __launch_bounds__(DNT) k_dec_up(DecArgs a) {
   // this call's epoch: 1 + the number of earlier calls (the atomic returns
   // the coherent value of this workgroup's counter and advances it)
   if (tid == 0) s_ep = __hip_atomic_fetch_add(a.ctr + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-  const int kind = b < a.n_mean ? 0 : (b < a.n_mean + a.n_sh ? 1 : 2);   // mean, shared, routed
-  const int rb = b - a.n_mean - a.n_sh;
+  const int kind = b < a.n_sh ? 1 : 2;   // shared, routed
+  const int rb = b - a.n_sh;
   const int e = kind == 2 ? rb / a.S : 0;
-  const int slice = kind == 0 ? b : (kind == 1 ? b - a.n_mean : rb % a.S);
+  const int slice = kind == 1 ? b : rb % a.S;
   const int nkb = a.nkb_d;
   const int kb_lo = (w * nkb) / DNW, kb_hi = ((w + 1) * nkb) / DNW;
   const __amdgpu_buffer_rsrc_t rx = buf_rsrc(a.x, (unsigned)((size_t)a.T * a.d * sizeof(elem)));
@@ -293,21 +324,16 @@ __global__ void __launch_bounds__(DNT) k_dec_up(DecArgs a) {
     return;
   }
 
-  if (kind == 0) {
-    // ---- mean term slice: m[row][cols] = x . Wbar, published as words
-    up_stream<DT, NP>(rx, buf_rsrc(a.Wbar_p), slice * NP, a.pF, nkb, kb_lo, kb_hi, a.d, acc, false, x0);
-    reduce_waves<NP, NCOL + 1>(s_red, acc, s_h[0]);
-    if (row < a.T) {
-#pragma unroll
-      for (int k = 0; k < CPT; ++k)
-        put_word(hw_m(a) + (size_t)row * a.F + slice * NCOL + col0 + k, s_ep, s_h[0][row][col0 + k]);
-    }
-    return;
-  }
-
   // ---- routed: router logits of expert e for the 16 (padded) token rows;
-  // each lane sums x[c][k] W_r[k][e] over its fragment entries, waves over d
+  // each lane sums x[c][k] W_r[k][e] over its fragment entries, waves over d.
+  // Speculative mode (non-gated experts, the wave's k range in one batch):
+  // the wave's W_up fragments are requested right after its router loads,
+  // so they stream while the logits are formed; loads complete in issue
+  // order, so the logits do not wait for them.  If no token activates the
+  // expert the fragments are dropped.
   const float lam_e = a.lam[e], b_e = a.b_r[e];
+  const bool spec = !GT && a.spec != 0 && kb_hi - kb_lo <= U;
+  i32x4_t wsp[U][NP];
   {
     const char* wr = a.Wr_p + frag_off(e >> 4, 0, nkb) + (size_t)((e & 15) + 16 * g) * 16;
     const unsigned xoff = (unsigned)(((size_t)c * a.d + (size_t)DT::EPL * g) * sizeof(elem));
@@ -320,6 +346,18 @@ __global__ void __launch_bounds__(DNT) k_dec_up(DecArgs a) {
         const int kb = kb0 + u < kb_hi ? kb0 + u : kb_hi - 1;
         xv[u] = ld16_buf(rx, xoff, (unsigned)(kb * DT::KB * sizeof(elem)));
         wv[u] = ld16(wr + (size_t)kb * FRAG_BYTES);
+      }
+      if (spec) {
+        const __amdgpu_buffer_rsrc_t rw = buf_rsrc(a.Wup_p + (size_t)e * a.up_stride);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int kb = kb_lo + u < kb_hi ? kb_lo + u : kb_hi - 1;
+#pragma unroll
+          for (int p = 0; p < NP; ++p) {
+            const int pp = slice * NP + p < a.pF ? slice * NP + p : a.pF - 1;
+            wsp[u][p] = ld16_buf(rw, 16u * l, (unsigned)frag_off(pp, kb, nkb));
+          }
+        }
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -401,19 +439,14 @@ __global__ void __launch_bounds__(DNT) k_dec_up(DecArgs a) {
     }
     if (tid == 0) a.rflag[e] = any ? 2u : 1u;
   }
-  if (!any) return;   // no token activated expert e: none of its weights are read
+  if (!any) {
+    // no token activated expert e: none of its weights are read (in the
+    // speculative mode, the requested W_up fragments land before the exit)
+    if (spec) __builtin_amdgcn_s_waitcnt(0);
+    return;
+  }
 
   const int gcol0 = slice * NCOL + col0;   // in F
-  // the mean term of this thread's entries, requested before the weights
-  u64 mv[CPT];
-  bool mneed[CPT];
-  const u64* mp[CPT];
-#pragma unroll
-  for (int k = 0; k < CPT; ++k) {
-    mneed[k] = !NM && row < a.T;
-    mp[k] = hw_m(a) + (size_t)(row < a.T ? row : 0) * a.F + gcol0 + k;
-    mv[k] = mneed[k] ? get_word(mp[k]) : 0ull;
-  }
   // the slice's up-projection (gated: the linear projection first, then the
   // NormSiLU input)
   const int p0 = slice * NP;
@@ -422,15 +455,32 @@ __global__ void __launch_bounds__(DNT) k_dec_up(DecArgs a) {
                       x_loaded, x0);
     reduce_waves<NP, GT ? NCOL + 1 : 1>(s_red, accu, s_u);
   }
-  up_stream<DT, NP>(rx, buf_rsrc(a.Wup_p + (size_t)e * a.up_stride), p0, a.pF, nkb, kb_lo, kb_hi, a.d, acc,
-                    x_loaded, x0);
+  bool xbad = false;
+  if (spec) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (kb_lo + u < kb_hi) {
+        if constexpr (XH) {
+          const i32x4_t xh = bf16x8_to_f16x8(x0[u], xbad);
+#pragma unroll
+          for (int p = 0; p < NP; ++p) FP16::mma(acc[p], xh, wsp[u][p]);
+        } else {
+#pragma unroll
+          for (int p = 0; p < NP; ++p) DT::mma(acc[p], x0[u], wsp[u][p]);
+        }
+      }
+  } else {
+    up_stream<DT, NP, XH>(rx, buf_rsrc(a.Wup_p + (size_t)e * a.up_stride), p0, a.pF, nkb, kb_lo, kb_hi, a.d, acc,
+                          x_loaded, x0, &xbad);
+  }
+  if (xbad) atomicOr(a.err, 32u);   // an x value outside the fp16 range
   reduce_waves<NP, NCOL + 1>(s_red, acc, s_h[0]);
 
-  // h - m, then the row's sum of squares over this slice
+  // h~ = x . (W_up[e] - Wbar) (the mean term is folded into the packed
+  // matrix), then the row's sum of squares over this slice
   float hv[CPT];
-  if constexpr (!NM) wait_words<CPT>(mv, mp, mneed, ep, a.err, 2u);
 #pragma unroll
-  for (int k = 0; k < CPT; ++k) hv[k] = s_h[0][row][col0 + k] - (mneed[k] ? word_val(mv[k]) : 0.f);
+  for (int k = 0; k < CPT; ++k) hv[k] = s_h[0][row][col0 + k];
   float ss = 0.f;
 #pragma unroll
   for (int k = 0; k < CPT; ++k) ss += hv[k] * hv[k];
@@ -690,7 +740,6 @@ DecArgs dec_args(const deco_moe_layer* L, const void* x, int T, void* out) {
   a.W = L->W;
   a.nkb_d = L->nkb_d;
   a.S = L->dec_S;
-  a.n_mean = L->dec_n_mean;
   a.n_sh = L->dec_n_sh;
   a.nsub = L->dec_nsub;
   a.n_shs = L->dec_n_shs;
@@ -698,9 +747,15 @@ DecArgs dec_args(const deco_moe_layer* L, const void* x, int T, void* out) {
   a.pFs = L->pFs;
   a.top_k = L->cfg.top_k;
   a.no_rms = (L->cfg.normsilu & DECO_NORMSILU_NO_RMS) != 0;
+  // speculative W_up requests from T = 8 on, where most experts are touched
+  // (at 20 % activation, 1 - 0.8^T of them: 83 % at T = 8); below, the
+  // bytes of untouched experts cost more than the earlier start saves
+  a.spec = T >= DEC_SPEC_MIN_T ? 1 : 0;
   a.eps = L->cfg.rms_eps;
   a.Wr_p = L->Wr_p;
-  a.Wup_p = L->Wup_p;
+  // the mean term folded into the experts' matrices (x . (W_up[e] - Wbar)),
+  // or plain W_up with the mean-term ablation
+  a.Wup_p = L->Wupm_p ? L->Wupm_p : L->Wup_p;
   a.Wlin_p = L->Wlin_p;
   a.Wbar_p = L->Wbar_p;
   a.Wsu_p = L->Wsu_p;
@@ -861,10 +916,9 @@ namespace deco_host {
 // Decode launch shape, chosen at load (sizes before the workspace is carved,
 // the residency check once the kernels' occupancy is known).  Routed experts
 // are cut into column slices of 32 columns (S = F / 32) when every routed
-// slice, mean-term slice and group of shared slices fits on the device at
-// once (one workgroup per CU), else of 64 columns; the mean term is cut like
-// the routed experts (one mean workgroup per routed slice position) and the
-// shared expert into slices of the same width, nsub of them per workgroup
+// slice and group of shared slices fits on the device at once (one
+// workgroup per CU), else of 64 columns; the shared expert is cut into
+// slices of the same width, nsub of them per workgroup
 // (the smallest nsub <= 4 that lets the whole grid fit).  The waits of the up
 // kernel need every group of workgroups that wait on each other (an
 // expert's slices; with the RMS-only shared expert, all shared workgroups;
@@ -873,13 +927,12 @@ static void dec_sizes(deco_moe_layer* L, int np, int cap) {
   const int ncol = 16 * np;
   L->dec_np = np;
   L->dec_S = L->F / ncol;
-  L->dec_n_mean = (L->cfg.normsilu & DECO_NORMSILU_NO_MEAN) ? 0 : L->dec_S;
   L->dec_n_shs = (L->Fs + ncol - 1) / ncol;
   int nsub = 1;
-  while (nsub < NSUB_MAX && L->dec_n_mean + (L->dec_n_shs + nsub - 1) / nsub + L->E * L->dec_S > cap) nsub *= 2;
+  while (nsub < NSUB_MAX && (L->dec_n_shs + nsub - 1) / nsub + L->E * L->dec_S > cap) nsub *= 2;
   L->dec_nsub = nsub;
   L->dec_n_sh = (L->dec_n_shs + nsub - 1) / nsub;
-  L->dec_grid_up = L->dec_n_mean + L->dec_n_sh + L->E * L->dec_S;
+  L->dec_grid_up = L->dec_n_sh + L->E * L->dec_S;
 }
 
 void plan_decode_sizes(deco_moe_layer* L, int n_cu) {
@@ -890,7 +943,7 @@ void plan_decode_sizes(deco_moe_layer* L, int n_cu) {
   L->dec_Fsp = (L->Fs + kp_rows - 1) / kp_rows * kp_rows;
   L->dec_kpe = L->dec_Fp / kp_rows;
   L->dec_kps = L->dec_Fsp / kp_rows;
-  L->n_hwords = 16 * L->F + L->E * L->dec_S * 16 + L->E * 16 + L->dec_n_sh * 16;
+  L->n_hwords = L->E * L->dec_S * 16 + L->E * 16 + L->dec_n_sh * 16;
 }
 
 hipError_t plan_decode(deco_moe_layer* L) {
@@ -900,7 +953,7 @@ hipError_t plan_decode(deco_moe_layer* L) {
   hipError_t err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, up, DNT, 0);
   if (err != hipSuccess) return err;
   const long long cap = (long long)(occ < 1 ? 0 : occ) * L->n_cu;
-  bool ok = cap >= L->dec_S && cap >= L->dec_n_mean + (L->cfg.shared_rms ? L->dec_n_sh : 0);
+  bool ok = cap >= L->dec_S && cap >= (L->cfg.shared_rms ? L->dec_n_sh : 0);
   if (L->cfg.top_k > 0) ok = ok && cap >= L->dec_grid_up;
   L->dec_ok = ok ? 1 : 0;
   return hipSuccess;

@@ -293,6 +293,10 @@ static int load_layer(const deco_moe_config* cfg, const void* W_r, const float* 
   L->dn_stride = (size_t)L->pD * L->nkb_F * KBy;
   size_t o_up = w.take(L->up_stride * E);
   size_t o_lin = L->gated ? w.take(L->up_stride * E) : 0;
+  // the decode path's NormSiLU input with the mean term folded in,
+  // W_up[e] - Wbar (not with the mean-term ablation)
+  const bool fold = (L->cfg.normsilu & DECO_NORMSILU_NO_MEAN) == 0;
+  size_t o_upm = fold ? w.take(L->up_stride * E) : 0;
   size_t o_wbp = w.take((size_t)L->pF * L->nkb_d * KBy);
   size_t o_dn = w.take(L->dn_stride * E);
   size_t o_dn16 = L->cfg.dtype == DECO_DT_BF16 ? w.take(L->dn_stride * E) : o_dn;
@@ -395,6 +399,7 @@ static int load_layer(const deco_moe_config* cfg, const void* W_r, const float* 
   L->Wr_p = L->wmem + o_wr;
   L->Wup_p = L->wmem + o_up;
   L->Wlin_p = L->gated ? L->wmem + o_lin : nullptr;
+  L->Wupm_p = fold ? L->wmem + o_upm : nullptr;
   L->Wbar_p = L->wmem + o_wbp;
   L->Wdn_p = L->wmem + o_dn;
   L->Wdn16_p = L->wmem + o_dn16;
@@ -438,10 +443,11 @@ static int load_layer(const deco_moe_config* cfg, const void* W_r, const float* 
       err = hipMemcpyAsync(L->lam, lambda, sizeof(float) * E, hipMemcpyDeviceToDevice, s);
   }
   bool down_ok = true;
-  if (err == hipSuccess) err = deco_host::check_down_range(L, W_down, s, &down_ok);
+  if (err == hipSuccess) err = deco_host::check_down_range(L, W_down, W_norm, s, &down_ok);
   if (err == hipSuccess && !down_ok) {
-    // bf16 layers run the down-projection on fp16 operands: a W_down entry
-    // past the fp16 range is refused rather than turned into inf
+    // bf16 layers run the down-projection and the decode path's folded
+    // NormSiLU input on fp16 operands: an entry past their range is refused
+    // rather than turned into inf
     deco_moe_free(L);
     return DECO_ERR_UNSUPPORTED;
   }

@@ -28,6 +28,35 @@ __global__ void __launch_bounds__(256) k_mean_up(const typename DT::elem* __rest
   wbar[i] = s / (float)E;
 }
 
+// Fragments of W_up[e] - Wbar (row-major [d][F] sources, `batch` experts):
+// the difference in fp32 (W_up values are exact in fp32, Wbar is fp32),
+// rounded once to OUT (fp16 for bf16 layers: 11 significant bits instead of
+// bf16's 8 keep the folded matrix about as accurate as subtracting a
+// separately formed mean term).
+template <class DT, class OUT>
+__global__ void __launch_bounds__(256) k_pack_minus_mean(const typename DT::elem* __restrict__ src, size_t src_bstride,
+                                                         const float* __restrict__ wbar, int K, int N, int P, int nkb,
+                                                         char* __restrict__ dst, size_t dst_bstride) {
+  const int b = blockIdx.y;
+  const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t total = (size_t)P * nkb * WAVE;
+  if (t >= total) return;
+  const int l = (int)(t % WAVE);
+  const int kb = (int)((t / WAVE) % nkb);
+  const int p = (int)(t / ((size_t)WAVE * nkb));
+  const int g = l >> 4, c = l & 15;
+  const int n = p * 16 + c;
+  const typename DT::elem* s = src + (size_t)b * src_bstride;
+  float f[DT::EPL];
+#pragma unroll
+  for (int j = 0; j < DT::EPL; ++j) {
+    const int k = kb * DT::KB + DT::frag_k(g, j);
+    const size_t i = (size_t)k * N + n;
+    f[j] = (k < K && n < N) ? DT::to_f32(s[i]) - wbar[i] : 0.f;
+  }
+  st16(dst + (size_t)b * dst_bstride + frag_off(p, kb, nkb) + (size_t)l * 16, OUT::pack(f));
+}
+
 // Pack the K x N matrix src(k, n) = src[k*sk + n*sn] (`batch` matrices
 // `src_bstride` elements apart; sk = ld, sn = 1 for a row-major [K][N]
 // matrix, sk = 1, sn = ld for the transpose of a row-major [N][K] one) into
@@ -144,6 +173,9 @@ hipError_t pack_all(deco_moe_layer* L, const void* W_r, const void* W_up, const 
   pack_rm<DT, E_t>(W_r, 0, d, E, L->pR, L->nkb_d, L->Wr_p, 0, 1, s);
   // routed up: K = d, N = F
   pack_rm<DT, E_t>(W_up, dF, d, F, L->pF, L->nkb_d, L->Wup_p, L->up_stride, E, s);
+  if (L->Wupm_p)
+    k_pack_minus_mean<DT, DN><<<pack_grid(L->pF, L->nkb_d, E), 256, 0, s>>>((const E_t*)W_up, dF, L->wbar, d, F,
+                                                                           L->pF, L->nkb_d, L->Wupm_p, L->up_stride);
   if (W_lin) pack_rm<DT, E_t>(W_lin, dF, d, F, L->pF, L->nkb_d, L->Wlin_p, L->up_stride, E, s);
   // inter-expert mean, in the layer dtype: K = d, N = F
   pack_rm<DT, float>(L->wbar, 0, d, F, L->pF, L->nkb_d, L->Wbar_p, 0, 1, s);
@@ -191,24 +223,33 @@ namespace deco_host {
 
 // bf16 layers: is every |W_down| within the fp16 range (the down-projection's
 // operand type)?  Synchronous (load time); uses the layer's mbuf as scratch.
-hipError_t check_down_range(deco_moe_layer* L, const void* W_down, hipStream_t s, bool* ok) {
-  *ok = true;
-  if (L->cfg.dtype != DECO_DT_BF16) return hipSuccess;
+// *ok = every |w[i]| <= limit, for n bf16 values on the device
+static hipError_t check_abs_below(deco_moe_layer* L, const void* w, size_t n, float limit, hipStream_t s, bool* ok) {
   unsigned* word = (unsigned*)L->mbuf;
   hipError_t err = hipMemsetAsync(word, 0, sizeof(unsigned), s);
   if (err != hipSuccess) return err;
-  const size_t n = (size_t)L->E * L->F * L->d;
-  k_absmax_bf16<<<1024, 256, 0, s>>>((const uint16_t*)W_down, n, word);
+  k_absmax_bf16<<<1024, 256, 0, s>>>((const uint16_t*)w, n, word);
   err = hipGetLastError();
   unsigned bits = 0;
   if (err == hipSuccess) err = hipMemcpyAsync(&bits, word, sizeof(bits), hipMemcpyDeviceToHost, s);
   if (err == hipSuccess) err = hipStreamSynchronize(s);
   if (err != hipSuccess) return err;
-  const float fp16_max = 65504.f;
   unsigned lim = 0;
-  memcpy(&lim, &fp16_max, sizeof(lim));
+  memcpy(&lim, &limit, sizeof(lim));
   *ok = bits <= lim;
   return hipSuccess;
+}
+
+hipError_t check_down_range(deco_moe_layer* L, const void* W_down, const void* W_norm, hipStream_t s, bool* ok) {
+  *ok = true;
+  if (L->cfg.dtype != DECO_DT_BF16) return hipSuccess;
+  const size_t n = (size_t)L->E * L->F * L->d;
+  hipError_t err = check_abs_below(L, W_down, n, 65504.f, s, ok);
+  // the decode path's folded NormSiLU input W - Wbar in fp16: |W - Wbar| <=
+  // 2 max |W| stays in range below half the fp16 maximum
+  if (err == hipSuccess && *ok && (L->cfg.normsilu & DECO_NORMSILU_NO_MEAN) == 0)
+    err = check_abs_below(L, W_norm, n, 32752.f, s, ok);
+  return err;
 }
 
 hipError_t launch_pack_all(deco_moe_layer* L, const void* W_r, const void* W_norm, const void* W_lin,

@@ -94,3 +94,49 @@ def test_w_down_past_fp16_range_refused_for_bf16_only():
     W[3, 5, 7] = 1.0e5
     f = dm.Layer(**layer_tensors(dataclasses.replace(Lf, W_down=W)), max_tokens=16, eps=Lf.eps)
     f.free()
+
+
+def test_norm_input_past_half_fp16_range_refused_with_the_mean_term():
+    """The decode path multiplies x by the folded NormSiLU input W_up[e] - Wbar
+    in fp16: |W_up - Wbar| <= 2 max |W_up|, so bf16 layers with the mean term
+    refuse max |W_up| > 32752; the mean-term ablation (plain W_up) and fp32
+    layers accept it."""
+    L = make_custom(128, 8, 32, 64, 4, "bf16", seed=3)
+    W = L.W_up.copy()
+    W[2, 9, 4] = 4.0e4   # bf16-representable, past 32752
+    big = dataclasses.replace(L, W_up=W)
+    with pytest.raises(dm.DecoError) as ei:
+        dm.Layer(**layer_tensors(big), max_tokens=16, eps=L.eps)
+    assert ei.value.status == dm.DECO_ERR_UNSUPPORTED
+    W = L.W_up.copy()
+    W[2, 9, 4] = 32640.0   # the largest bf16 value within the limit
+    ok = dm.Layer(**layer_tensors(dataclasses.replace(L, W_up=W)), max_tokens=16, eps=L.eps)
+    ok.free()
+    nm = dm.Layer(**layer_tensors(big), max_tokens=16, eps=L.eps, normsilu_mean=False)
+    nm.free()
+    Lf = make_custom(128, 8, 32, 64, 4, "f32", seed=3)
+    W = Lf.W_up.copy()
+    W[2, 9, 4] = 4.0e4
+    f = dm.Layer(**layer_tensors(dataclasses.replace(Lf, W_up=W)), max_tokens=16, eps=Lf.eps)
+    f.free()
+
+
+def test_x_past_fp16_range_raises_the_flag_on_the_decode_path():
+    """x enters the decode path's NormSiLU-input product converted to fp16: a
+    token value past 65504 raises error bit 5 instead of an inf product."""
+    L = make_layer(2, T=8)
+    x = L.x.copy()
+    x[3, 100] = 1.0e5
+    big = L.with_x(x)
+    layer = dm.Layer(**layer_tensors(big), max_tokens=16, eps=L.eps)
+    layer.error_flags()
+    layer(x_tensor(big), path=DEC)
+    torch.cuda.synchronize()
+    flags = layer.error_flags()
+    _say(f"x = 1e5 decode: flags {flags}")
+    assert flags & RANGE_BIT
+    # in range: no flag, and the result matches the oracle
+    layer(x_tensor(L), path=DEC)
+    torch.cuda.synchronize()
+    assert layer.error_flags() == 0
+    layer.free()
