@@ -12,10 +12,9 @@
 //               slice).  A routed workgroup computes its expert's router
 //               logits for the batch (router: linear projection + bias, ReLU,
 //               per-expert scale; DECO paper Sec. 2 "Router design") and
-//               exits without using any expert weight when no token
-//               activated the expert (from T = 8 on it requests its W_up
-//               slice together with the router operands and drops it then).
-//               Otherwise it streams its slice of W_up[e] - Wbar through
+//               exits without reading any expert weight when no token
+//               activated the expert.  Otherwise it streams its slice of
+//               W_up[e] - Wbar through
 //               v_mfma 16x16 products (tokens padded to 16 rows): the mean
 //               term is folded into the matrix packed at load, x.(W_up[e] -
 //               Wbar) = x.W_up[e] - x.Wbar.  It takes the row's RMS over all
@@ -61,10 +60,6 @@ constexpr int SPIN_LIMIT = 1 << 20;
 constexpr int NSUB_MAX = 4;       // shared-expert slices per workgroup
 typedef unsigned long long u64;
 
-#ifndef DEC_SPEC_MIN_T
-#define DEC_SPEC_MIN_T 8
-#endif
-
 struct DecArgs {
   const void* x;
   void* out;
@@ -76,7 +71,6 @@ struct DecArgs {
   int pF, pFs;              // 16-column panels of F and Fs
   int top_k;                // TopK routing variant (0: ReLU routing)
   int no_rms;               // NormSiLU ablation: no RMS step
-  int spec;                 // routed workgroups request their W_up slice before the routing decision
   float eps;
   const char* Wr_p;
   const char* Wup_p;        // NormSiLU input projection (a gated expert's gate projection)
@@ -325,15 +319,8 @@ __global__ void __launch_bounds__(DNT) k_dec_up(DecArgs a) {
   }
 
   // ---- routed: router logits of expert e for the 16 (padded) token rows;
-  // each lane sums x[c][k] W_r[k][e] over its fragment entries, waves over d.
-  // Speculative mode (non-gated experts, the wave's k range in one batch):
-  // the wave's W_up fragments are requested right after its router loads,
-  // so they stream while the logits are formed; loads complete in issue
-  // order, so the logits do not wait for them.  If no token activates the
-  // expert the fragments are dropped.
+  // each lane sums x[c][k] W_r[k][e] over its fragment entries, waves over d
   const float lam_e = a.lam[e], b_e = a.b_r[e];
-  const bool spec = !GT && a.spec != 0 && kb_hi - kb_lo <= U;
-  i32x4_t wsp[U][NP];
   {
     const char* wr = a.Wr_p + frag_off(e >> 4, 0, nkb) + (size_t)((e & 15) + 16 * g) * 16;
     const unsigned xoff = (unsigned)(((size_t)c * a.d + (size_t)DT::EPL * g) * sizeof(elem));
@@ -346,18 +333,6 @@ __global__ void __launch_bounds__(DNT) k_dec_up(DecArgs a) {
         const int kb = kb0 + u < kb_hi ? kb0 + u : kb_hi - 1;
         xv[u] = ld16_buf(rx, xoff, (unsigned)(kb * DT::KB * sizeof(elem)));
         wv[u] = ld16(wr + (size_t)kb * FRAG_BYTES);
-      }
-      if (spec) {
-        const __amdgpu_buffer_rsrc_t rw = buf_rsrc(a.Wup_p + (size_t)e * a.up_stride);
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int kb = kb_lo + u < kb_hi ? kb_lo + u : kb_hi - 1;
-#pragma unroll
-          for (int p = 0; p < NP; ++p) {
-            const int pp = slice * NP + p < a.pF ? slice * NP + p : a.pF - 1;
-            wsp[u][p] = ld16_buf(rw, 16u * l, (unsigned)frag_off(pp, kb, nkb));
-          }
-        }
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -439,12 +414,7 @@ __global__ void __launch_bounds__(DNT) k_dec_up(DecArgs a) {
     }
     if (tid == 0) a.rflag[e] = any ? 2u : 1u;
   }
-  if (!any) {
-    // no token activated expert e: none of its weights are read (in the
-    // speculative mode, the requested W_up fragments land before the exit)
-    if (spec) __builtin_amdgcn_s_waitcnt(0);
-    return;
-  }
+  if (!any) return;   // no token activated expert e: none of its weights are read
 
   const int gcol0 = slice * NCOL + col0;   // in F
   // the slice's up-projection (gated: the linear projection first, then the
@@ -456,23 +426,8 @@ __global__ void __launch_bounds__(DNT) k_dec_up(DecArgs a) {
     reduce_waves<NP, GT ? NCOL + 1 : 1>(s_red, accu, s_u);
   }
   bool xbad = false;
-  if (spec) {
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (kb_lo + u < kb_hi) {
-        if constexpr (XH) {
-          const i32x4_t xh = bf16x8_to_f16x8(x0[u], xbad);
-#pragma unroll
-          for (int p = 0; p < NP; ++p) FP16::mma(acc[p], xh, wsp[u][p]);
-        } else {
-#pragma unroll
-          for (int p = 0; p < NP; ++p) DT::mma(acc[p], x0[u], wsp[u][p]);
-        }
-      }
-  } else {
-    up_stream<DT, NP, XH>(rx, buf_rsrc(a.Wup_p + (size_t)e * a.up_stride), p0, a.pF, nkb, kb_lo, kb_hi, a.d, acc,
-                          x_loaded, x0, &xbad);
-  }
+  up_stream<DT, NP, XH>(rx, buf_rsrc(a.Wup_p + (size_t)e * a.up_stride), p0, a.pF, nkb, kb_lo, kb_hi, a.d, acc,
+                        x_loaded, x0, &xbad);
   if (xbad) atomicOr(a.err, 32u);   // an x value outside the fp16 range
   reduce_waves<NP, NCOL + 1>(s_red, acc, s_h[0]);
 
@@ -747,10 +702,6 @@ DecArgs dec_args(const deco_moe_layer* L, const void* x, int T, void* out) {
   a.pFs = L->pFs;
   a.top_k = L->cfg.top_k;
   a.no_rms = (L->cfg.normsilu & DECO_NORMSILU_NO_RMS) != 0;
-  // speculative W_up requests from T = 8 on, where most experts are touched
-  // (at 20 % activation, 1 - 0.8^T of them: 83 % at T = 8); below, the
-  // bytes of untouched experts cost more than the earlier start saves
-  a.spec = T >= DEC_SPEC_MIN_T ? 1 : 0;
   a.eps = L->cfg.rms_eps;
   a.Wr_p = L->Wr_p;
   // the mean term folded into the experts' matrices (x . (W_up[e] - Wbar)),
