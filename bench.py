@@ -283,7 +283,7 @@ RECORD_CASES = {1: [(16, None)], 2: [(1, None), (8, None), (16, None)], 3: [(409
                 5: [(1024, r) for r in (0.05, 0.10, 0.20, 0.40)]}
 
 
-def records(only=None):
+def records(only=None, out_dir=PROFILE_DIR):
     """Per-(workload, T) records, one text file per synthetic workload under
     profiles/ (records_c<N>.txt): GPU time per call and tokens/s (inputs
     resident, layer copies cycled past the Infinity Cache), the attainable
@@ -324,11 +324,11 @@ def records(only=None):
             rec["gpu_over_cpu"] = round(rec["tokens_per_s"] / rec["cpu_oracle"]["tokens_per_s"], 1)
             log(json.dumps(rec))
             lines.append(json.dumps(rec))
-        with open(os.path.join(PROFILE_DIR, f"records_c{cfg}.txt"), "w") as f:
+        with open(os.path.join(out_dir, f"records_c{cfg}.txt"), "w") as f:
             f.write("\n".join(lines) + "\n")
 
 
-def crossover():
+def crossover(out_dir=PROFILE_DIR):
     """Decode path against prefill path over T on the d=2048 and d=4096
     layers: both paths for T <= 16 (the decode path's limit), the prefill path
     above; writes profiles/crossover_decode_prefill.txt."""
@@ -356,7 +356,7 @@ def crossover():
                                  experts_touched=r["n_union"])
             log(json.dumps(row))
             lines.append(json.dumps(row))
-    with open(os.path.join(PROFILE_DIR, "crossover_decode_prefill.txt"), "w") as f:
+    with open(os.path.join(out_dir, "crossover_decode_prefill.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
 
@@ -616,6 +616,8 @@ def main():
                     help="run only this workload's GPU loop (for profiler runs)")
     ap.add_argument("--records", nargs="*", type=int, metavar="CFG",
                     help="write profiles/records_c<N>.txt for the given workloads (all five when none given)")
+    ap.add_argument("--out-dir", default=PROFILE_DIR,
+                    help="folder for the --records and --crossover files (default: profiles/)")
     ap.add_argument("--crossover", action="store_true",
                     help="decode vs prefill path over T on the d=2048 and d=4096 layers")
     ap.add_argument("--sweep", action="store_true",
@@ -663,10 +665,12 @@ def main():
     dm.load_library()
 
     if args.crossover:
-        crossover()
+        os.makedirs(args.out_dir, exist_ok=True)
+        crossover(args.out_dir)
         return
     if args.records is not None:
-        records(set(args.records) or None)
+        os.makedirs(args.out_dir, exist_ok=True)
+        records(set(args.records) or None, args.out_dir)
         return
     if args.sweep:
         sweep()
