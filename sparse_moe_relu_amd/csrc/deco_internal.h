@@ -10,7 +10,7 @@
 
 // offsets (bytes from the prefill/backward workspace's base) of its buffers
 struct PwsOff {
-  size_t to, ec, lt, sb, yb, sr, dg, dh, ag, sl, dc, dz, dl, gb, cp, wp, dhl, agl, dcl, sbh, sbl;
+  size_t to, ec, lt, sb, yb, sr, dg, dh, ag, sl, dc, dz, dl, gb, cp, wp, dhl, agl, dcl, sbh, sbl, hp;
 };
 
 struct deco_moe_layer {
@@ -109,6 +109,9 @@ struct deco_moe_layer {
   float* colpart;          // [2][ceil(Tcap / 64)][E] partial column sums (db_r, dlambda)
   float* wpart;            // [4][max(d * (Fp + Ep + Fsp), Fs * d)] partial weight-gradient tiles
   float* sraw;             // shared_rms: [Tcap][Fs] x . Ws_up before the RMS-only NormSiLU (fp32)
+  float* hpart;            // [SPLIT_NKS][split_maxT * (E + 1)][F] K-part sums of x . W_up[e] per
+                           // pair slot (small-batch prefill), or null
+  int split_maxT;          // largest batch the small-batch prefill split is sized for (0: none)
   char* ybuf;              // [Tcap * (E + 1) + 1][d] pair buffer, token-major: per token its
                            // shared-expert output, then gate * expert output for each
                            // active expert in ascending order (fp16 for bf16 layers,
@@ -149,6 +152,7 @@ enum {
   KS_BWD_COMBINE,
   KS_BWD_WGRAD,
   KS_PRE_DC,
+  KS_PRE_UP_PART,
   KS_COUNT
 };
 const char* kernel_slot_name(int slot);
@@ -170,6 +174,8 @@ hipError_t launch_decode(const deco_moe_layer* L, const void* x, int T, void* ou
 // path: DECO_PATH_PREFILL (variant chosen here), _PAIRS or _TOKEN
 hipError_t launch_prefill(const deco_moe_layer* L, const void* x, int T, void* out, hipStream_t s, int path);
 bool prefill_token_ok(const deco_moe_layer* L);   // the token-major down-projection fits the layer
+int split_max_tokens(const deco_moe_layer* L, long long grid);   // small-batch split: largest batch (load time)
+constexpr int SPLIT_NKS_MAX = 4;                 // k parts of the small-batch split, at most
 hipError_t launch_dec_mask(const deco_moe_layer* L, int T, uint64_t* mask, hipStream_t s);
 // allocation-free decode (static device array as scratch)
 size_t decode_scratch_bytes(const deco_moe_layer* L);

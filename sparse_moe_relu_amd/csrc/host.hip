@@ -128,6 +128,7 @@ void bind_pws(deco_moe_layer* L, char* base) {
   L->sbuf = base + o.sb;
   L->ybuf = base + o.yb;
   L->sraw = L->cfg.shared_rms ? (float*)(base + o.sr) : nullptr;
+  L->hpart = o.hp ? (float*)(base + o.hp) : nullptr;
   if (bwd) {
     L->dgbuf = (float*)(base + o.dg);
     L->dhbuf = base + o.dh;
@@ -205,6 +206,7 @@ const char* kernel_slot_name(int slot) {
     case KS_PRE_EXPERT: return "k_pre_expert";
     case KS_PRE_COMBINE: return "k_pre_combine";
     case KS_PRE_DC: return "k_pre_dc";
+    case KS_PRE_UP_PART: return "k_pre_expert_kpart";
     case KS_BWD_SHARED: return "k_bwd_shared";
     case KS_BWD_EXPERT: return "k_bwd_expert";
     case KS_BWD_TOKEN: return "k_bwd_token";
@@ -359,6 +361,13 @@ static int load_layer(const deco_moe_config* cfg, const void* W_r, const float* 
   size_t o_dcl = split ? k.take((size_t)L->esz * Tcap * (L->Fp + L->Ep + L->Fsp)) : 0;
   size_t o_sbh = bwd ? k.take((size_t)L->esz * Tcap * L->Fs) : 0;
   size_t o_sbl = split ? k.take((size_t)L->esz * Tcap * L->Fs) : 0;
+  // small-batch prefill split: fp32 k-part sums of x . W_up[e] per pair slot,
+  // for batches up to split_maxT (estimated here on the grid the expert
+  // kernel's occupancy gives; a larger real grid only lowers the split's use)
+  L->split_maxT = deco_host::split_max_tokens(L, (long long)(n_cu < 1 ? 1 : n_cu) * (L->esz == 2 ? 2 : 1));
+  size_t o_hp = L->split_maxT
+                    ? k.take(sizeof(float) * deco_host::SPLIT_NKS_MAX * (size_t)L->split_maxT * (E + 1) * L->F)
+                    : 0;
   // the per-layer part ends where the prefill/backward workspace starts
   L->ws_bytes = o_to;
   L->pws_bytes = k.off - o_to;
@@ -368,7 +377,7 @@ static int load_layer(const deco_moe_config* cfg, const void* W_r, const float* 
                   o_dz ? o_dz - o_to : 0, o_dl ? o_dl - o_to : 0, o_gb ? o_gb - o_to : 0,
                   o_cp ? o_cp - o_to : 0, o_wp ? o_wp - o_to : 0, o_dhl ? o_dhl - o_to : 0,
                   o_agl ? o_agl - o_to : 0, o_dcl ? o_dcl - o_to : 0, o_sbh ? o_sbh - o_to : 0,
-                  o_sbl ? o_sbl - o_to : 0};
+                  o_sbl ? o_sbl - o_to : 0, o_hp ? o_hp - o_to : 0};
 
   if (hipMalloc((void**)&L->wmem, L->wmem_bytes) != hipSuccess) {
     (void)hipGetLastError();

@@ -29,6 +29,8 @@
 // so an accumulator lane holds 4 consecutive columns of one row.  Pair values
 // are fp16 (11-bit significand): a bf16 pair buffer costs up to 4 % of
 // RMS(out) on heavy-tailed gates.
+#include <algorithm>
+
 #include "prefill_kernels.h"
 
 namespace {
@@ -77,10 +79,67 @@ bool use_dc(const deco_moe_layer* L, int T, int path) {
   return path == DECO_PATH_PREFILL_TOKEN;
 }
 
-bool small_expert_tiles(const deco_moe_layer* L, int T) {
-  const long long shared_tiles = (long long)((T + GM - 1) / GM) * ((L->pD + GP - 1) / GP);
-  const long long expert_tiles = (long long)L->E * ((T / 4 + GM - 1) / GM);
-  return 2 * (shared_tiles + expert_tiles) < (long long)L->pre_grid;
+long long est_shared_tiles(const deco_moe_layer* L, int T) {
+  return (long long)((T + GM - 1) / GM) * ((L->pD + GP - 1) / GP);
+}
+long long est_expert_tiles(const deco_moe_layer* L, int T, int bm) { return (long long)L->E * ((T / 4 + bm - 1) / bm); }
+bool small_tiles_at(const deco_moe_layer* L, int T, long long grid) {
+  return 2 * (est_shared_tiles(L, T) + est_expert_tiles(L, T, GM)) < grid;
+}
+bool small_expert_tiles(const deco_moe_layer* L, int T) { return small_tiles_at(L, T, L->pre_grid); }
+
+// Small batches of a non-gated layer split each 64-row expert tile over nks
+// k parts of the up-projection and ncb column blocks of the down-projection
+// (k_pre_expert, PART): at T = 256 on the d = 4096 layer the 64-row tiles
+// leave one thin tile per expert, and one CU streams 2 d F of weights for
+// it.  nks: the k-blocks of d in 4 (or 2) parts of at least 8; ncb: the
+// largest power of two up to 4 whose units, with the shared tiles, stay
+// within one per workgroup of the persistent grid.
+#ifndef DECO_SPLIT_NKS
+#define DECO_SPLIT_NKS 0   // 0: chosen from the shape
+#endif
+#ifndef DECO_SPLIT_NCB
+#define DECO_SPLIT_NCB 0
+#endif
+int split_nks(const deco_moe_layer* L);
+bool use_split(const deco_moe_layer* L, int T) {
+#ifdef DECO_NO_SPLIT
+  return false;   // measurement builds: the unsplit 64-row tiles
+#endif
+  // and only while the k-part units fit the grid in one pass: with more
+  // 64-row tiles per expert the unsplit tiles already spread the weights
+  // (same-box A/B, us per call: d = 4096 layer T = 64 / 256 / 512: 141.7 /
+  // 151.3 / 175.2 unsplit, 98.7 / 126.9 / 181.9 split; d = 2048 layer
+  // T = 32 / 128 / 512: 78.0 / 80.4 / 84.8 against 51.1 / 57.6 / 76.3, and
+  // T = 1024: 96.0 against 109.3)
+  return L->hpart && !L->gated && T <= L->split_maxT && small_expert_tiles(L, T) &&
+         est_expert_tiles(L, T, GM / 2) * split_nks(L) <= (long long)L->pre_grid;
+}
+int split_nks(const deco_moe_layer* L) {
+  static_assert(DECO_SPLIT_NKS <= deco_host::SPLIT_NKS_MAX, "k parts beyond the buffer");
+  if (DECO_SPLIT_NKS && L->nkb_d % DECO_SPLIT_NKS == 0) return DECO_SPLIT_NKS;
+  for (int q : {deco_host::SPLIT_NKS_MAX, 2})
+    if (L->nkb_d % q == 0 && L->nkb_d / q >= 8) return q;
+  return 1;
+}
+int split_ncb(const deco_moe_layer* L, int T, int dp) {
+  const int nds = L->pD / dp;
+  if (DECO_SPLIT_NCB) return nds % DECO_SPLIT_NCB == 0 ? DECO_SPLIT_NCB : 1;
+  const long long units = est_expert_tiles(L, T, GM / 2);
+  const long long shared = (long long)((T + GM - 1) / GM) * ((L->pD + DECO_SPLIT_SGP - 1) / DECO_SPLIT_SGP);
+  int ncb = 1;
+  while (ncb < 4 && nds % (2 * ncb) == 0 && shared + units * 2 * ncb <= (long long)L->pre_grid) ncb *= 2;
+  return ncb;
+}
+template <class DT>
+void (*split_kernel(int pF, int part))(PreArgs) {
+  if (part == 1)
+    return pF == 2 ? k_pre_expert<DT, 2, XM_FWD, true, false, 1>
+         : pF == 4 ? k_pre_expert<DT, 4, XM_FWD, true, false, 1>
+         : pF == 8 ? k_pre_expert<DT, 8, XM_FWD, true, false, 1> : k_pre_expert<DT, 16, XM_FWD, true, false, 1>;
+  return pF == 2 ? k_pre_expert<DT, 2, XM_FWD, true, false, 2>
+       : pF == 4 ? k_pre_expert<DT, 4, XM_FWD, true, false, 2>
+       : pF == 8 ? k_pre_expert<DT, 8, XM_FWD, true, false, 2> : k_pre_expert<DT, 16, XM_FWD, true, false, 2>;
 }
 
 template <class DT>
@@ -95,6 +154,17 @@ hipError_t prefill(const deco_moe_layer* L, const void* x, int T, void* out, hip
                    dim3(L->pre_grid), dim3(256), s, a);
     if (err == hipSuccess)
       err = launch(deco_host::KS_PRE_DC, dc_kernel<DT>(dc_nkf(L)), dim3((unsigned)dc_blocks(L, T)), dim3(512), s, a);
+  } else if (use_split(L, T)) {
+    PreArgs b = a;
+    b.nks = split_nks(L);
+    b.ncb = split_ncb(L, T, (L->F / (L->cfg.dtype == DECO_DT_BF16 ? FP16::KB : F32::KB)) >= 8 ? 2 : 4);
+    if (err == hipSuccess)
+      err = launch(deco_host::KS_PRE_UP_PART, split_kernel<DT>(L->pF, 1), dim3(L->pre_grid), dim3(256), s, b);
+    if (err == hipSuccess)
+      err = launch(deco_host::KS_PRE_EXPERT, split_kernel<DT>(L->pF, 2), dim3(L->pre_grid), dim3(256), s, b);
+    if (err == hipSuccess)
+      err = launch(deco_host::KS_PRE_COMBINE, k_pre_combine<DT>,
+                   dim3((unsigned)(((long long)T * (L->d / 8) + 255) / 256)), dim3(256), s, a);
   } else {
     if (err == hipSuccess)
       err = launch(deco_host::KS_PRE_EXPERT, expert_kernel<DT>(L->pF, L->gated, small_expert_tiles(L, T)),
@@ -117,6 +187,18 @@ hipError_t launch_prefill(const deco_moe_layer* L, const void* x, int T, void* o
 }
 
 bool prefill_token_ok(const deco_moe_layer* L) { return dc_nkf(L) <= 4; }
+
+// Largest batch the small-batch split can take on a grid of `grid`
+// workgroups (0 for gated layers, which keep their own tiles); the K-part
+// buffer is sized for it at load.
+int split_max_tokens(const deco_moe_layer* L, long long grid) {
+  if (L->gated) return 0;
+  const int tcap = std::min(L->maxT < 16 ? 16 : L->maxT, 2048);
+  int best = 0;
+  for (int T = 1; T <= tcap; ++T)
+    if (small_tiles_at(L, T, grid) && est_expert_tiles(L, T, GM / 2) * split_nks(L) <= grid) best = T;
+  return best;
+}
 
 // Persistent grid of the expert kernel: as many workgroups as fit on the
 // device at once, a multiple of the 8 XCDs.

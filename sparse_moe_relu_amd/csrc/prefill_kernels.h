@@ -87,6 +87,10 @@ struct PreArgs {
   void* dhbuf_lo;          // bf16 layers: the low parts (value - high part, rounded), else null
   void* agbuf_lo;
   int* slot_list;          // [E][Tcap] pair slot of each list entry
+  // small-batch split of the expert tiles (see k_pre_expert, PART)
+  float* hpart;            // [nks][pcap][F] K-part sums of x . W_up[e] per pair slot
+  size_t pcap;             // pair-slot rows of one K part
+  int nks, ncb;            // K parts of the up-projection, column blocks of the down-projection
 };
 
 // what an expert tile computes
@@ -108,6 +112,9 @@ constexpr int GM = 128;   // rows of the dense GEMM tiles
 constexpr int GP = 8;     // 16-column panels of the dense GEMM tiles
 template <class DT>
 using DenseTile = Tile<DT, GM, GP, DECO_PRE_NS>;
+#ifndef DECO_SPLIT_SGP
+#define DECO_SPLIT_SGP 4   // panels per shared tile beside the split's column-block units
+#endif
 
 // Workgroups are handed to the 8 XCDs round-robin (workgroup b runs on XCD
 // b % 8).  Renumber them so each XCD works on one contiguous range of tiles:
@@ -185,14 +192,21 @@ __device__ __forceinline__ void store4_act(void* base, size_t idx, const float* 
 // exceeds the CUs, 4 (one per CU, three steps of loads in flight) when it
 // does not, which is the case below a few thousand tokens; BMR rows per tile:
 // 128, or 64 when even the four-stage grid of 128-row tiles leaves CUs idle.
-template <class DT, int NS, int BMR = GM>
+// BNP 16-column panels per tile: 8, or 4 or 2 for small batches, where 8-panel
+// tiles leave most CUs without work and each busy CU streams 1 MiB of weights
+// at one CU's rate.  Narrow tiles go column-tile major (the row tiles of one
+// column tile on one XCD, which then reads those weight panels once).
+template <class DT, int NS, int BMR = GM, int BNP = GP>
 __global__ void __launch_bounds__(256, 2) k_pre_router_shared(PreArgs a) {
   using elem = typename DT::elem;
-  using TC = Tile<DT, BMR, GP, NS>;
+  using TC = Tile<DT, BMR, BNP, NS>;
+  static_assert(BNP == 2 || BNP == 4 || BNP == 8, "a wave's panels must lie in one 4-panel section");
   __shared__ i32x4_t lds[TC::LDS_V];
   const int tid = threadIdx.x, w = tid >> 6, wm = w >> 1, wn = w & 1, l = tid & 63, g = l >> 4, c = l & 15;
   const int t = xcd_tile(blockIdx.x, gridDim.x);
-  const int m0 = (t / a.rs_nt) * BMR, p0 = (t % a.rs_nt) * GP;
+  const int n_mt = (a.T + BMR - 1) / BMR;
+  const int m0 = BNP == GP ? (t / a.rs_nt) * BMR : (t % n_mt) * BMR;
+  const int p0 = BNP == GP ? (t % a.rs_nt) * GP : (t / n_mt) * BNP;
   const elem* x = (const elem*)a.x;
   // rows past T and padding panels read valid memory; those outputs are dropped
   auto row = [&](int r) -> const elem* {
@@ -214,8 +228,8 @@ __global__ void __launch_bounds__(256, 2) k_pre_router_shared(PreArgs a) {
     for (int j = 0; j < TC::NBW; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   tile_gemm<DT, TC, true>(lds, row, panel, a.nkb_d, acc);
 
-  // lane: row m0 + wm*64 + 16 i + c, columns 16 (q0 + j) + 4 g + ii
-  const int q0 = p0 + wn * TC::NBW;   // a multiple of 4: one section per wave
+  // lane: row m0 + wm*BMR/2 + 16 i + c, columns 16 (q0 + j) + 4 g + ii
+  const int q0 = p0 + wn * TC::NBW;   // a multiple of NBW: one section per wave
   if (q0 < a.pR) {
     float be[TC::NBW][4], le[TC::NBW][4];
 #pragma unroll
@@ -245,7 +259,14 @@ __global__ void __launch_bounds__(256, 2) k_pre_router_shared(PreArgs a) {
         }
       bits |= shfl_xor_u64(bits, 16);
       bits |= shfl_xor_u64(bits, 32);
-      if (g == 0 && r < a.T) a.mask[(size_t)r * a.W + q0 / 4] = bits;
+      // the wave's 16 NBW experts are bits 16 (q0 % 4) .. of mask word q0 / 4
+      // (little-endian: bytes 2 (q0 % 4) ..); narrower tiles store their part
+      if (g == 0 && r < a.T) {
+        uint64_t* mw = a.mask + (size_t)r * a.W + q0 / 4;
+        if constexpr (TC::NBW == 4) *mw = bits;
+        else if constexpr (TC::NBW == 2) reinterpret_cast<uint32_t*>(mw)[(q0 & 3) >> 1] = (uint32_t)bits;
+        else reinterpret_cast<uint16_t*>(mw)[q0 & 3] = (uint16_t)bits;
+      }
     }
   } else if (q0 - a.pR < a.pF4) {
     const int q = q0 - a.pR;
@@ -436,6 +457,7 @@ struct ExpertShape {
   static constexpr int cmax(int x, int y) { return x > y ? x : y; }
   // shared tiles stage their 128 x 128 output the same way
   static constexpr int SPITCH_V = GP * 16 * (int)sizeof(PT) / 16 + 1;
+  static constexpr int GM_SPITCH_V = GM * SPITCH_V;
   static constexpr int LDS_V = cmax(cmax(TC::LDS_V, ACT_V),
                                     cmax(DNS * DSTAGE_V + OBUF_V,
                                          cmax(DenseTile<DT>::LDS_V, GM * SPITCH_V)));
@@ -464,8 +486,18 @@ struct ExpertShape {
 // dg goes to dgbuf, dh~ and g*a to the pair-slot rows of dhbuf and agbuf
 // (operands of the weight gradients), the slot to slot_list, and
 // dh~ . W_up[e]^T (this pair's part of dLoss/dx) to the pair buffer.
-template <class DT, int BNP, int MODE, bool SMALL = false, bool ACT = false>
+//
+// PART (small batches, XM_FWD): the expert tiles split over more workgroups,
+// in two launches.  PART = 1: unit (expert tile, k part q) computes the
+// tile's x . W_up[e] over k-blocks q nkb/nks .. (q + 1) nkb/nks - 1 and stores
+// it in fp32 to hpart[q][pair slot]; no shared tiles.  PART = 2: unit (expert
+// tile, column block b) adds the nks parts in order, applies NormSiLU and
+// multiplies by column block b (pD/ncb panels) of W_down[e]; shared tiles as
+// usual.  A thin expert then costs a few hundred KiB of weights per workgroup
+// instead of its whole 2 d F, spread over nks + ncb workgroups.
+template <class DT, int BNP, int MODE, bool SMALL = false, bool ACT = false, int PART = 0>
 __global__ void __launch_bounds__(256, (ExpertShape<DT, BNP, MODE, SMALL>::OCC)) k_pre_expert(PreArgs a) {
+  static_assert(PART == 0 || (MODE == XM_FWD && SMALL && !ACT), "the split runs the forward's 64-row tiles");
   using elem = typename DT::elem;
   using S = ExpertShape<DT, BNP, MODE, SMALL>;
   using TC = typename S::TC;
@@ -495,12 +527,17 @@ __global__ void __launch_bounds__(256, (ExpertShape<DT, BNP, MODE, SMALL>::OCC))
     if (tid == 0) s_toff[a.E] = tot;
   }
   __syncthreads();
-  const int n_et = s_toff[a.E];
-  const int nsp = (a.pD + GP - 1) / GP;                      // shared tiles per 128 rows
-  // the backward and the activation-output mode have no shared tiles
-  const int n_st = (MODE == XM_BWD || ACT) ? 0 : ((a.T + GM - 1) / GM) * nsp;
+  const int nsub = PART == 1 ? a.nks : PART == 2 ? a.ncb : 1;   // units per expert tile
+  const int n_et = s_toff[a.E] * nsub;                       // expert units
+  // shared tiles: 128 rows x SGP panels (the split's column-block units are
+  // small, and 8-panel shared tiles would be the few long ones among them)
+  constexpr int SGP = PART == 2 ? DECO_SPLIT_SGP : GP;
+  const int nsp = (a.pD + SGP - 1) / SGP;                    // shared tiles per 128 rows
+  // the backward, the activation-output mode and the K-part units have no shared tiles
+  const int n_st = (MODE == XM_BWD || ACT || PART == 1) ? 0 : ((a.T + GM - 1) / GM) * nsp;
   const int xg = blockIdx.x % NXCD, lb = blockIdx.x / NXCD;
   const int gx = ((int)gridDim.x - xg + NXCD - 1) / NXCD;    // workgroups on this XCD
+  // consecutive units (of one tile: they share its rows) stay on one XCD
   const int e_beg = (int)((long long)n_et * xg / NXCD), e_end = (int)((long long)n_et * (xg + 1) / NXCD);
   const int s_beg = (int)((long long)n_st * xg / NXCD), s_end = (int)((long long)n_st * (xg + 1) / NXCD);
   const int n_mine = (e_end - e_beg) + (s_end - s_beg);
@@ -512,9 +549,9 @@ __global__ void __launch_bounds__(256, (ExpertShape<DT, BNP, MODE, SMALL>::OCC))
     lds_barrier();   // the previous tile no longer reads LDS
     if (k >= e_end - e_beg) {
       // ---- shared tile: rows m0.., panels p0.. of SiLU(x Ws_up) . Ws_down
-      using TD = DenseTile<DT>;
+      using TD = Tile<DT, GM, SGP, DECO_PRE_NS>;
       const int ts = s_beg + k - (e_end - e_beg);
-      const int m0 = (ts / nsp) * GM, p0 = (ts % nsp) * GP;
+      const int m0 = (ts / nsp) * GM, p0 = (ts % nsp) * SGP;
       const elem* sbuf = (const elem*)a.sbuf;
       auto row = [&](int r) -> const elem* {
         const int rr = m0 + r;
@@ -530,29 +567,31 @@ __global__ void __launch_bounds__(256, (ExpertShape<DT, BNP, MODE, SMALL>::OCC))
         for (int j = 0; j < TD::NBW; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       tile_gemm<DT, TD, true>(lds, row, panel, a.nkb_Fs, acc);
       // stage the tile (pair type) in LDS, then store whole rows
-      constexpr int SP = S::SPITCH_V;
+      constexpr int CPR = SGP * 16 * (int)sizeof(PT) / 16;   // 16-byte chunks per row
+      constexpr int SPI = CPR + 1;                            // staged row pitch (16-byte slots)
+      static_assert(GM * SPI <= S::GM_SPITCH_V, "shared staging fits the LDS");
       bool bad = false;
 #pragma unroll
       for (int i = 0; i < TD::MB; ++i) {
         const int R = wm * (GM / 2) + 16 * i + c;
 #pragma unroll
         for (int j = 0; j < TD::NBW; ++j)
-          store4_pair(reinterpret_cast<PT*>(lds + R * SP) + (wn * TD::NBW + j) * 16 + 4 * g, acc[i][j], bad);
+          store4_pair(reinterpret_cast<PT*>(lds + R * SPI) + (wn * TD::NBW + j) * 16 + 4 * g, acc[i][j], bad);
       }
       if (bad) atomicOr(a.err, 32u);
       lds_barrier();
-      constexpr int CPR = GP * 16 * (int)sizeof(PT) / 16;   // 16-byte chunks per row
-      const int ncol_ch = (a.pD - p0 < GP ? a.pD - p0 : GP) * 16 * (int)sizeof(PT) / 16;
+      const int ncol_ch = (a.pD - p0 < SGP ? a.pD - p0 : SGP) * 16 * (int)sizeof(PT) / 16;
       for (int idx = tid; idx < GM * CPR; idx += 256) {
         const int R = idx / CPR, q = idx % CPR, r = m0 + R;
         if (r < a.T && q < ncol_ch)
-          st16(reinterpret_cast<char*>(yb + (size_t)a.tok_off[r] * a.d + p0 * 16) + q * 16, lds[R * SP + q]);
+          st16(reinterpret_cast<char*>(yb + (size_t)a.tok_off[r] * a.d + p0 * 16) + q * 16, lds[R * SPI + q]);
       }
       continue;
     }
 
-    // ---- expert tile
-    const int tile = e_beg + k;
+    // ---- expert tile (one unit of it)
+    const int unit = e_beg + k;
+    const int tile = unit / nsub, sub = unit - tile * nsub;
     int lo = 0, hi = a.E;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
@@ -583,6 +622,33 @@ __global__ void __launch_bounds__(256, (ExpertShape<DT, BNP, MODE, SMALL>::OCC))
 
     // up-projection of the gathered rows, all F columns
     const char* Wu = a.Wup_p + (size_t)e * a.up_stride;
+    if constexpr (PART == 1) {
+      // k part `sub`: its k-blocks of every row and panel, stored as fp32 sums
+      const int nkq = a.nkb_d / a.nks, kb0 = sub * nkq;
+      auto row_q = [&](int r) -> const elem* {
+        const int tk = s_tok[r];
+        return x + (size_t)(tk >= 0 ? tk : 0) * a.d + (size_t)kb0 * DT::KB;
+      };
+      auto panel_q = [&](int p) -> const char* { return Wu + frag_off(p, kb0, a.nkb_d); };
+      f32x4_t accq[MB][NBW];
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) accq[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      tile_gemm<DT, TC, true>(lds, row_q, panel_q, nkq, accq);
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        const int R = wm * (BM / 2) + 16 * i + c;
+        if (s_tok[R] >= 0) {
+          float* hp = a.hpart + ((size_t)sub * a.pcap + s_slot[R]) * F + 4 * g;
+#pragma unroll
+          for (int j = 0; j < NBW; ++j)
+            *reinterpret_cast<float4*>(hp + 16 * (wn * NBW + j)) =
+                make_float4(accq[i][j][0], accq[i][j][1], accq[i][j][2], accq[i][j][3]);
+        }
+      }
+      continue;
+    }
     auto row = [&](int r) -> const elem* {
       const int tk = s_tok[r];   // padding rows read token 0; their outputs are dropped
       return x + (size_t)(tk >= 0 ? tk : 0) * a.d;
@@ -619,7 +685,28 @@ __global__ void __launch_bounds__(256, (ExpertShape<DT, BNP, MODE, SMALL>::OCC))
 #pragma unroll
       for (int j = 0; j < NBW; ++j) mpre[i][j] = *reinterpret_cast<const float4*>(mrow + 16 * (wn * NBW + j) + 4 * g);
     }
-    tile_gemm<DT, TC, true>(lds, row, panel, a.nkb_d, acc);
+    if constexpr (PART == 2) {
+      // the nks k-part sums of the tile's rows, added in part order
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        const int R = wm * (BM / 2) + 16 * i + c;
+        if (s_tok[R] >= 0) {
+          for (int q = 0; q < a.nks; ++q) {
+            const float* hp = a.hpart + ((size_t)q * a.pcap + s_slot[R]) * F + 4 * g;
+#pragma unroll
+            for (int j = 0; j < NBW; ++j) {
+              const float4 v = *reinterpret_cast<const float4*>(hp + 16 * (wn * NBW + j));
+              acc[i][j][0] += v.x;
+              acc[i][j][1] += v.y;
+              acc[i][j][2] += v.z;
+              acc[i][j][3] += v.w;
+            }
+          }
+        }
+      }
+    } else {
+      tile_gemm<DT, TC, true>(lds, row, panel, a.nkb_d, acc);
+    }
 
     // NormSiLU.  Lane: local row R = wm*BM/2 + 16 i + c, columns
     // f = 16 (wn*NBW + j) + 4 g + ii.  Subtract the mean term, then the sum
@@ -752,7 +839,9 @@ __global__ void __launch_bounds__(256, (ExpertShape<DT, BNP, MODE, SMALL>::OCC))
     // panels wn*DP/2 .. of each stage.  Operands swapped (W_down as the row
     // operand): a lane holds 4 consecutive output columns of one token.
     const char* Wd = (MODE == XM_BWD ? a.WupT_p : a.Wdn16_p) + (size_t)e * a.dn_stride;
-    const int nds = a.pD / DP;
+    // stages of this unit: all pD / DP, or (PART = 2) column block `sub` of them
+    const int nds = PART == 2 ? a.pD / DP / a.ncb : a.pD / DP;
+    const int st0 = PART == 2 ? sub * nds : 0;
     i32x4_t* obuf = lds + S::DNS * S::DSTAGE_V;   // staging buffer after the ring
     constexpr int OCH = S::OCH;
     auto issue = [&](int st) {
@@ -760,7 +849,7 @@ __global__ void __launch_bounds__(256, (ExpertShape<DT, BNP, MODE, SMALL>::OCC))
 #pragma unroll
       for (int i = 0; i < S::DLPW; ++i) {
         const int f = w * S::DLPW + i;   // panel f / NKF of the stage, k-block f % NKF
-        load_lds16(Wd + frag_off(st * DP + f / NKF, f % NKF, NKF) + l * 16, ring + f * 64);
+        load_lds16(Wd + frag_off((st0 + st) * DP + f / NKF, f % NKF, NKF) + l * 16, ring + f * 64);
       }
     };
     // copy the staged stage `st` (BM rows x OROW bytes) to the tokens' pair
@@ -772,7 +861,7 @@ __global__ void __launch_bounds__(256, (ExpertShape<DT, BNP, MODE, SMALL>::OCC))
 #pragma unroll
       for (int u = 0; u < S::FPT; ++u) {
         const int idx = tid + 256 * u, R = idx / OCH, q = idx % OCH, slot = s_slot[R];
-        st16(reinterpret_cast<char*>(yb + (slot >= 0 ? (size_t)slot : trash) * a.d + st * DP * 16) + q * 16,
+        st16(reinterpret_cast<char*>(yb + (slot >= 0 ? (size_t)slot : trash) * a.d + (st0 + st) * DP * 16) + q * 16,
              obuf[R * OCH + (q ^ (R & (OCH - 1)))]);
       }
     };
@@ -1268,6 +1357,9 @@ PreArgs fill_pre_args(const deco_moe_layer* L, const void* x, int T, void* out) 
   a.sbuf = L->sbuf;
   a.ybuf = L->ybuf;
   a.err = L->dec_err;
+  a.hpart = L->hpart;
+  a.pcap = (size_t)L->split_maxT * (L->E + 1);
+  a.nks = a.ncb = 1;
   return a;
 }
 
@@ -1282,6 +1374,9 @@ PreArgs fill_pre_args(const deco_moe_layer* L, const void* x, int T, void* out) 
 #define DECO_PRE_RS_LARGE_BM 64
 #endif
 static_assert(DECO_PRE_RS_LARGE_BM == GM || DECO_PRE_RS_LARGE_BM == GM / 2, "router tile rows");
+#ifndef DECO_PRE_RS_NARROW
+#define DECO_PRE_RS_NARROW 1   // 0: 8-panel router tiles at every batch size (measurement builds)
+#endif
 
 // the routing steps shared by the forward and backward launchers: router
 // (and the mean and shared up-projection), TopK selection, dispatch
@@ -1290,13 +1385,25 @@ hipError_t launch_routing(const deco_moe_layer* L, const PreArgs& a, int T, hipS
   using deco_host::launch;
   const unsigned mtiles = (unsigned)((T + GM - 1) / GM);
   const unsigned rs_grid = mtiles * a.rs_nt;
-  const unsigned half_grid = (unsigned)((T + GM / 2 - 1) / (GM / 2)) * a.rs_nt;
+  const unsigned mt64 = (unsigned)((T + GM / 2 - 1) / (GM / 2));
+  const unsigned half_grid = mt64 * a.rs_nt;
   const unsigned large_grid = DECO_PRE_RS_LARGE_BM == GM ? rs_grid : half_grid;
-  hipError_t err =
-      2 * rs_grid <= (unsigned)L->n_cu
-          ? launch(deco_host::KS_PRE_ROUTER_SHARED, k_pre_router_shared<DT, 4, GM / 2>, dim3(half_grid), dim3(256), s, a)
-          : launch(deco_host::KS_PRE_ROUTER_SHARED, k_pre_router_shared<DT, DECO_PRE_NS, DECO_PRE_RS_LARGE_BM>,
-                   dim3(large_grid), dim3(256), s, a);
+  // small batches: the widest of 8, 4, 2-panel tiles whose grid covers the
+  // CUs (2 if none does); the sections are whole multiples of 4 panels
+  const unsigned n_pan = (unsigned)(a.pR + a.pF4 + a.pFs4), cus = (unsigned)L->n_cu;
+  const int bnp = (!DECO_PRE_RS_NARROW || half_grid >= cus) ? 8 : mt64 * (n_pan / 4) >= cus ? 4 : 2;
+  hipError_t err;
+  if (2 * rs_grid > cus)
+    err = launch(deco_host::KS_PRE_ROUTER_SHARED, k_pre_router_shared<DT, DECO_PRE_NS, DECO_PRE_RS_LARGE_BM>,
+                 dim3(large_grid), dim3(256), s, a);
+  else if (bnp == 8)
+    err = launch(deco_host::KS_PRE_ROUTER_SHARED, k_pre_router_shared<DT, 4, GM / 2>, dim3(half_grid), dim3(256), s, a);
+  else if (bnp == 4)
+    err = launch(deco_host::KS_PRE_ROUTER_SHARED, k_pre_router_shared<DT, 4, GM / 2, 4>, dim3(mt64 * (n_pan / 4)),
+                 dim3(256), s, a);
+  else
+    err = launch(deco_host::KS_PRE_ROUTER_SHARED, k_pre_router_shared<DT, 4, GM / 2, 2>, dim3(mt64 * (n_pan / 2)),
+                 dim3(256), s, a);
   if (err == hipSuccess && a.top_k > 0)
     err = launch(deco_host::KS_PRE_TOPK, k_pre_topk, dim3((unsigned)((T + 3) / 4)), dim3(256), s, a);
   if (err == hipSuccess && a.sraw)
