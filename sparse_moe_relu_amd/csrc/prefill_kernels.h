@@ -427,14 +427,17 @@ __global__ void __launch_bounds__(DISP_NT) k_pre_dispatch(PreArgs a) {
 }
 
 // --------------------------------------------------------------------------
-template <class DT, int BNP, int MODE, bool SMALL = false>
+#ifndef DECO_SPLIT_NS
+#define DECO_SPLIT_NS 3   // up-projection ring stages of the split's k-part units
+#endif
+template <class DT, int BNP, int MODE, bool SMALL = false, int NSU = DECO_PRE_NS>
 struct ExpertShape {
   using DN = typename DT::Down;                      // down-projection operand type
   // token rows per tile (gated experts and the backward hold a second
   // K = d accumulator, so their tiles have half the rows; SMALL: batches too
   // small to fill the persistent grid with 128-row tiles use 64)
   static constexpr int BM = (BNP >= 16 || MODE != XM_FWD || SMALL) ? 64 : 128;
-  using TC = Tile<DT, BM, BNP, DECO_PRE_NS>;          // up-projection ring
+  using TC = Tile<DT, BM, BNP, NSU>;                  // up-projection ring
   static constexpr int F = BNP * 16;
   static constexpr int NKF = F / DN::KB;             // k-blocks of the down-projection
   static constexpr int RB = BM / 16;                 // 16-row blocks of the tile
@@ -499,7 +502,7 @@ template <class DT, int BNP, int MODE, bool SMALL = false, bool ACT = false, int
 __global__ void __launch_bounds__(256, (ExpertShape<DT, BNP, MODE, SMALL>::OCC)) k_pre_expert(PreArgs a) {
   static_assert(PART == 0 || (MODE == XM_FWD && SMALL && !ACT), "the split runs the forward's 64-row tiles");
   using elem = typename DT::elem;
-  using S = ExpertShape<DT, BNP, MODE, SMALL>;
+  using S = ExpertShape<DT, BNP, MODE, SMALL, PART == 1 ? DECO_SPLIT_NS : DECO_PRE_NS>;
   using TC = typename S::TC;
   using DN = typename S::DN;
   using PT = typename DT::pair;
@@ -1377,6 +1380,9 @@ static_assert(DECO_PRE_RS_LARGE_BM == GM || DECO_PRE_RS_LARGE_BM == GM / 2, "rou
 #ifndef DECO_PRE_RS_NARROW
 #define DECO_PRE_RS_NARROW 1   // 0: 8-panel router tiles at every batch size (measurement builds)
 #endif
+#ifndef DECO_PRE_RS_NARROW_NS
+#define DECO_PRE_RS_NARROW_NS 4   // ring stages of the narrow router tiles
+#endif
 
 // the routing steps shared by the forward and backward launchers: router
 // (and the mean and shared up-projection), TopK selection, dispatch
@@ -1399,10 +1405,10 @@ hipError_t launch_routing(const deco_moe_layer* L, const PreArgs& a, int T, hipS
   else if (bnp == 8)
     err = launch(deco_host::KS_PRE_ROUTER_SHARED, k_pre_router_shared<DT, 4, GM / 2>, dim3(half_grid), dim3(256), s, a);
   else if (bnp == 4)
-    err = launch(deco_host::KS_PRE_ROUTER_SHARED, k_pre_router_shared<DT, 4, GM / 2, 4>, dim3(mt64 * (n_pan / 4)),
+    err = launch(deco_host::KS_PRE_ROUTER_SHARED, k_pre_router_shared<DT, DECO_PRE_RS_NARROW_NS, GM / 2, 4>, dim3(mt64 * (n_pan / 4)),
                  dim3(256), s, a);
   else
-    err = launch(deco_host::KS_PRE_ROUTER_SHARED, k_pre_router_shared<DT, 4, GM / 2, 2>, dim3(mt64 * (n_pan / 2)),
+    err = launch(deco_host::KS_PRE_ROUTER_SHARED, k_pre_router_shared<DT, DECO_PRE_RS_NARROW_NS, GM / 2, 2>, dim3(mt64 * (n_pan / 2)),
                  dim3(256), s, a);
   if (err == hipSuccess && a.top_k > 0)
     err = launch(deco_host::KS_PRE_TOPK, k_pre_topk, dim3((unsigned)((T + 3) / 4)), dim3(256), s, a);
