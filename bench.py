@@ -626,6 +626,10 @@ def main():
                     help="profiler mode: GPU loop of --workload only, no JSON")
     ap.add_argument("--profile-summary", nargs=3, metavar=("DB", "OUT", "COMMAND"),
                     help="write a text summary of a rocprofv3 kernel-trace database (no GPU needed)")
+    ap.add_argument("--cfg", type=int, default=0, metavar="N",
+                    help="with --only-gpu-loop: synthetic workload N (default: 2 for decode, 3 otherwise)")
+    ap.add_argument("--tokens", type=int, default=None, metavar="T",
+                    help="with --only-gpu-loop: batch size (default: the workload's own)")
     ap.add_argument("--gated", action="store_true",
                     help="with --only-gpu-loop: the gated-expert variant (for profiler runs)")
     ap.add_argument("--top-k", type=int, default=0,
@@ -684,7 +688,8 @@ def main():
                 dst.copy_(src)
             torch.cuda.synchronize()
             del src, dst
-        L = make_layer(2, gated=args.gated) if args.workload == "decode" else make_layer(3, gated=args.gated)
+        cfg = args.cfg or (2 if args.workload == "decode" else 3)
+        L = make_layer(cfg, T=args.tokens, gated=args.gated)
         if args.workload == "backward":
             r = run_backward(L, args.steps, args.warmup)
             Fl = backward_flops(L, r["P"], L.T)

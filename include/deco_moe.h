@@ -145,7 +145,10 @@ int deco_moe_check_config(const deco_moe_config* cfg);
  * workspace, dominated by the token-major pair buffer of
  * (max_tokens (E + 1) + 1) x d values of 2 bytes (bf16 layers; 4 for fp32):
  * every token can activate every expert, so that is the bound the buffer is
- * sized for (956 MB for d = 2048, E = 56, max_tokens = 4096).  With
+ * sized for (956 MB for d = 2048, E = 56, max_tokens = 4096).  Non-gated
+ * layers add 16 F (E + 1) bytes per token of the largest batch whose prefill
+ * splits its expert tiles (fp32 partial sums; at most a few hundred tokens on
+ * a 256-CU device: about 60 MB at d = 2048 and at d = 4096).  With
  * cfg.shared_workspace = 1 one such workspace serves every sharing layer on
  * the device (its size is the largest layer's), instead of one per layer. */
 int deco_moe_load_weights(const deco_moe_config* cfg,
