@@ -57,11 +57,16 @@ typedef enum {
   DECO_PATH_PREFILL = 2,  /* bucketed grouped-MFMA path; any T (the _PAIRS variant) */
   DECO_PATH_PREFILL_PAIRS = 3,  /* prefill, expert-major down-projection into per-pair
                                  * output rows, then a combine kernel; any layer     */
-  DECO_PATH_PREFILL_TOKEN = 4   /* prefill, token-major down-projection and combine in
+  DECO_PATH_PREFILL_TOKEN = 4,  /* prefill, token-major down-projection and combine in
                                  * one kernel (no per-pair rows); slower than _PAIRS
                                  * on the measured layers; d_ff / k-block <= 4 (bf16:
                                  * d_ff <= 128, fp32: d_ff <= 64), else
                                  * DECO_ERR_UNSUPPORTED                              */
+  DECO_PATH_PREFILL_FUSED = 5   /* prefill as _PAIRS, with the combine fused with the
+                                 * shared expert's down-projection (one kernel forms
+                                 * the shared term on MFMA and adds the pair rows);
+                                 * slower than _PAIRS on the measured layers; any
+                                 * layer                                             */
 } deco_path;
 
 #define DECO_DECODE_MAX_T 16

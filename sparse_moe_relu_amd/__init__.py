@@ -32,6 +32,7 @@ DECO_PATH_DECODE = 1
 DECO_PATH_PREFILL = 2
 DECO_PATH_PREFILL_PAIRS = 3
 DECO_PATH_PREFILL_TOKEN = 4
+DECO_PATH_PREFILL_FUSED = 5
 DECODE_MAX_T = 16
 DECO_NORMSILU_NO_MEAN = 1
 DECO_NORMSILU_NO_RMS = 2

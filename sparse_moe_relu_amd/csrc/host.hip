@@ -490,7 +490,7 @@ int deco_moe_load_weights_gated(const deco_moe_config* cfg, const void* W_r, con
 int deco_moe_forward_path(const deco_moe_layer* L, const void* x, int64_t T, void* out, void* stream,
                           int path) {
   if (!L || T < 0 || T > L->maxT) return DECO_ERR_INVALID_ARG;
-  if (path < DECO_PATH_AUTO || path > DECO_PATH_PREFILL_TOKEN) return DECO_ERR_INVALID_ARG;
+  if (path < DECO_PATH_AUTO || path > DECO_PATH_PREFILL_FUSED) return DECO_ERR_INVALID_ARG;
   if (path == DECO_PATH_PREFILL_TOKEN && !deco_host::prefill_token_ok(L)) return DECO_ERR_UNSUPPORTED;
   if (T == 0) return DECO_OK;
   if (!x || !out) return DECO_ERR_INVALID_ARG;

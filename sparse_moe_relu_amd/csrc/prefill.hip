@@ -24,6 +24,12 @@
 //                        Ws_down into slot 0.
 //   k_pre_combine        out[t] = sum of token t's pair rows in slot order, in
 //                        fp32, rounded once to the dtype.
+//   k_pre_shared_combine (DECO_PATH_PREFILL_FUSED, in place of the shared
+//                        tiles and k_pre_combine) the shared expert's
+//                        down-projection per 128-token tile on MFMA plus each
+//                        token's pair rows (slots 1..) in slot order, in
+//                        fp32, rounded once: the combine fused with the
+//                        shared expert.
 //
 // All GEMMs run on the LDS-staged tile of gemm_tile.h with swapped operands,
 // so an accumulator lane holds 4 consecutive columns of one row.  Pair values
@@ -122,11 +128,12 @@ int split_nks(const deco_moe_layer* L) {
     if (L->nkb_d % q == 0 && L->nkb_d / q >= 8) return q;
   return 1;
 }
-int split_ncb(const deco_moe_layer* L, int T, int dp) {
+int split_ncb(const deco_moe_layer* L, int T, int dp, bool fused) {
   const int nds = L->pD / dp;
   if (DECO_SPLIT_NCB) return nds % DECO_SPLIT_NCB == 0 ? DECO_SPLIT_NCB : 1;
   const long long units = est_expert_tiles(L, T, GM / 2);
-  const long long shared = (long long)((T + GM - 1) / GM) * ((L->pD + DECO_SPLIT_SGP - 1) / DECO_SPLIT_SGP);
+  const long long shared =
+      fused ? 0 : (long long)((T + GM - 1) / GM) * ((L->pD + DECO_SPLIT_SGP - 1) / DECO_SPLIT_SGP);
   int ncb = 1;
   while (ncb < 4 && nds % (2 * ncb) == 0 && shared + units * 2 * ncb <= (long long)L->pre_grid) ncb *= 2;
   return ncb;
@@ -142,9 +149,31 @@ void (*split_kernel(int pF, int part))(PreArgs) {
        : pF == 8 ? k_pre_expert<DT, 8, XM_FWD, true, false, 2> : k_pre_expert<DT, 16, XM_FWD, true, false, 2>;
 }
 
+// The combine fused with the shared expert's down-projection
+// (k_pre_shared_combine, DECO_PATH_PREFILL_FUSED): 128-token tiles 8 panels
+// wide, or 4 or 2 when the batch makes fewer 8-panel tiles than CUs.  Only
+// when asked for: same-box A/B, us per call, fused against the shared tiles
+// inside k_pre_expert plus k_pre_combine: d = 2048 layer T = 4096 256.0 /
+// 241.9, T = 128 70.6 / 55.9; d = 4096 layer T = 256 145.0 / 126.5, T = 2048
+// 431.2 / 429.0.  The fused kernel's workgroups run the shared GEMM's K loop
+// and then stream their tokens' pair rows, one after the other (76 us at
+// T = 4096 against 38 us of combine and ~18 us of shared tiles that ran
+// beside the expert tiles).
+int shared_combine_sgp(const deco_moe_layer* L, int T) {
+  const long long mt = (T + GM - 1) / GM;
+  if (mt * ((L->pD + 7) / 8) >= L->n_cu) return 8;
+  if (mt * ((L->pD + 3) / 4) >= L->n_cu) return 4;
+  return 2;
+}
+template <class DT>
+void (*shared_combine_kernel(int sgp))(PreArgs) {
+  return sgp == 8 ? k_pre_shared_combine<DT, 8> : sgp == 4 ? k_pre_shared_combine<DT, 4> : k_pre_shared_combine<DT, 2>;
+}
+
 template <class DT>
 hipError_t prefill(const deco_moe_layer* L, const void* x, int T, void* out, hipStream_t s, int path) {
-  const PreArgs a = fill_pre_args(L, x, T, out);
+  PreArgs a = fill_pre_args(L, x, T, out);
+  a.fuse_shared = path == DECO_PATH_PREFILL_FUSED ? 1 : 0;
   using deco_host::launch;
   hipError_t err = launch_routing<DT>(L, a, T, s);
   if (use_dc(L, T, path)) {
@@ -157,21 +186,25 @@ hipError_t prefill(const deco_moe_layer* L, const void* x, int T, void* out, hip
   } else if (use_split(L, T)) {
     PreArgs b = a;
     b.nks = split_nks(L);
-    b.ncb = split_ncb(L, T, (L->F / (L->cfg.dtype == DECO_DT_BF16 ? FP16::KB : F32::KB)) >= 8 ? 2 : 4);
+    b.ncb = split_ncb(L, T, (L->F / (L->cfg.dtype == DECO_DT_BF16 ? FP16::KB : F32::KB)) >= 8 ? 2 : 4, a.fuse_shared);
     if (err == hipSuccess)
       err = launch(deco_host::KS_PRE_UP_PART, split_kernel<DT>(L->pF, 1), dim3(L->pre_grid), dim3(256), s, b);
     if (err == hipSuccess)
       err = launch(deco_host::KS_PRE_EXPERT, split_kernel<DT>(L->pF, 2), dim3(L->pre_grid), dim3(256), s, b);
-    if (err == hipSuccess)
-      err = launch(deco_host::KS_PRE_COMBINE, k_pre_combine<DT>,
-                   dim3((unsigned)(((long long)T * (L->d / 8) + 255) / 256)), dim3(256), s, a);
   } else {
     if (err == hipSuccess)
       err = launch(deco_host::KS_PRE_EXPERT, expert_kernel<DT>(L->pF, L->gated, small_expert_tiles(L, T)),
                    dim3(L->pre_grid), dim3(256), s, a);
-    if (err == hipSuccess)
+  }
+  if (!use_dc(L, T, path) && err == hipSuccess) {
+    if (a.fuse_shared) {
+      const int sgp = shared_combine_sgp(L, T);
+      const unsigned grid = (unsigned)(((T + GM - 1) / GM) * ((L->pD + sgp - 1) / sgp));
+      err = launch(deco_host::KS_PRE_COMBINE, shared_combine_kernel<DT>(sgp), dim3(grid), dim3(256), s, a);
+    } else {
       err = launch(deco_host::KS_PRE_COMBINE, k_pre_combine<DT>,
                    dim3((unsigned)(((long long)T * (L->d / 8) + 255) / 256)), dim3(256), s, a);
+    }
   }
   if (err != hipSuccess) return err;
   return hipGetLastError();

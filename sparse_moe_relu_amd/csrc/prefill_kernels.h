@@ -51,6 +51,8 @@ struct PreArgs {
   unsigned* err;       // device error flags (bit 5: a value outside the fp16 range)
   int T, Tcap, d, E, F, Fs, W;
   int top_k;           // TopK routing variant (0: ReLU routing)
+  int fuse_shared;     // the shared expert's down-projection runs in k_pre_shared_combine, not as
+                       // shared tiles of k_pre_expert (slot 0 of the pair rows stays unused)
   int no_mean, no_rms; // NormSiLU ablations: drop the mean term / the RMS step
   float* sraw;         // RMS-only NormSiLU shared expert: [T][Fs] x . Ws_up (fp32), else null
   int nkb_d, nkb_F, nkb_Fs, pR, pF, pD, pFs;
@@ -537,7 +539,7 @@ __global__ void __launch_bounds__(256, (ExpertShape<DT, BNP, MODE, SMALL>::OCC))
   constexpr int SGP = PART == 2 ? DECO_SPLIT_SGP : GP;
   const int nsp = (a.pD + SGP - 1) / SGP;                    // shared tiles per 128 rows
   // the backward, the activation-output mode and the K-part units have no shared tiles
-  const int n_st = (MODE == XM_BWD || ACT || PART == 1) ? 0 : ((a.T + GM - 1) / GM) * nsp;
+  const int n_st = (MODE == XM_BWD || ACT || PART == 1 || a.fuse_shared) ? 0 : ((a.T + GM - 1) / GM) * nsp;
   const int xg = blockIdx.x % NXCD, lb = blockIdx.x / NXCD;
   const int gx = ((int)gridDim.x - xg + NXCD - 1) / NXCD;    // workgroups on this XCD
   // consecutive units (of one tile: they share its rows) stay on one XCD
@@ -927,6 +929,101 @@ __global__ void __launch_bounds__(256, (ExpertShape<DT, BNP, MODE, SMALL>::OCC))
     }
     lds_barrier();
     if (nds > 0) flush(nds - 1);
+  }
+}
+
+// --------------------------------------------------------------------------
+// The gate-weighted combine fused with the shared expert (DECO paper Sec. 2:
+// the shared expert is always active and its output is added to the routed
+// experts' weighted sum).  One workgroup per 128 tokens x 16 SGP columns:
+// s . Ws_down for its tile on the LDS-staged MFMA tile (s = SiLU(x Ws_up)
+// from the router GEMM), the fp32 result staged in LDS; then per (token,
+// 8 columns) the shared value plus the token's pair rows (slots 1.. of its
+// pair range, ascending expert order) in fp32, rounded once to the dtype.
+// The shared term never passes through the fp16 pair buffer.
+template <class DT, int SGP>
+__global__ void __launch_bounds__(256, 2) k_pre_shared_combine(PreArgs a) {
+  using elem = typename DT::elem;
+  using PT = typename DT::pair;
+  using TD = Tile<DT, GM, SGP, DECO_PRE_NS>;
+  constexpr int NCOL = 16 * SGP;
+  constexpr int SPF = NCOL + 4;                    // staged row pitch, floats
+  constexpr int STAGE_V = GM * SPF / 4;            // 16-byte LDS slots of the stage
+  constexpr int LDS_V = TD::LDS_V > STAGE_V ? TD::LDS_V : STAGE_V;
+  __shared__ i32x4_t lds[LDS_V];
+  const int tid = threadIdx.x, w = tid >> 6, wm = w >> 1, wn = w & 1, l = tid & 63, g = l >> 4, c = l & 15;
+  const int nsp = (a.pD + SGP - 1) / SGP;
+  // consecutive tiles (one XCD) are the column tiles of one row tile
+  const int t = xcd_tile(blockIdx.x, gridDim.x);
+  const int m0 = (t / nsp) * GM, p0 = (t % nsp) * SGP;
+  const elem* sbuf = (const elem*)a.sbuf;
+  auto row = [&](int r) -> const elem* {
+    const int rr = m0 + r;
+    return sbuf + (size_t)(rr < a.T ? rr : a.T - 1) * a.Fs;
+  };
+  auto panel = [&](int p) -> const char* { return a.Wsd_p + frag_off(p0 + p < a.pD ? p0 + p : 0, 0, a.nkb_Fs); };
+  f32x4_t acc[TD::MB][TD::NBW];
+#pragma unroll
+  for (int i = 0; i < TD::MB; ++i)
+#pragma unroll
+    for (int j = 0; j < TD::NBW; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  tile_gemm<DT, TD, true>(lds, row, panel, a.nkb_Fs, acc);   // ends with a barrier: the ring is free
+  float* st = reinterpret_cast<float*>(lds);
+#pragma unroll
+  for (int i = 0; i < TD::MB; ++i) {
+    const int R = wm * (GM / 2) + 16 * i + c;
+#pragma unroll
+    for (int j = 0; j < TD::NBW; ++j)
+      *reinterpret_cast<float4*>(st + R * SPF + 16 * (wn * TD::NBW + j) + 4 * g) =
+          make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+  }
+  lds_barrier();
+  constexpr int CH = NCOL / 8;                     // 8-column chunks per row
+  const int ncol = (a.pD - p0 < SGP ? a.pD - p0 : SGP) * 16;
+  for (int it = tid; it < GM * CH; it += 256) {
+    const int R = it / CH, col = 8 * (it % CH), r = m0 + R;
+    if (r >= a.T || col >= ncol) continue;
+    float v[8];
+    {
+      const float4 u0 = *reinterpret_cast<const float4*>(st + R * SPF + col);
+      const float4 u1 = *reinterpret_cast<const float4*>(st + R * SPF + col + 4);
+      v[0] = u0.x; v[1] = u0.y; v[2] = u0.z; v[3] = u0.w;
+      v[4] = u1.x; v[5] = u1.y; v[6] = u1.z; v[7] = u1.w;
+    }
+    const int s1 = a.tok_off[r + 1];
+    int s = a.tok_off[r] + 1;   // slot 0 (the unfused shared row) is not used
+    const PT* yb = (const PT*)a.ybuf + p0 * 16 + col;
+    auto add = [&](const PT* p) {
+      if constexpr (sizeof(PT) == 2) {
+        const f16x8_t y = *reinterpret_cast<const f16x8_t*>(p);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] += (float)y[k];
+      } else {
+        const float4 y0 = *reinterpret_cast<const float4*>(p);
+        const float4 y1 = *reinterpret_cast<const float4*>(p + 4);
+        v[0] += y0.x; v[1] += y0.y; v[2] += y0.z; v[3] += y0.w;
+        v[4] += y1.x; v[5] += y1.y; v[6] += y1.z; v[7] += y1.w;
+      }
+    };
+    for (; s + 4 <= s1; s += 4) {
+      // four independent loads in flight, added in slot order
+      if constexpr (sizeof(PT) == 2) {
+        f16x8_t y[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) y[u] = *reinterpret_cast<const f16x8_t*>(yb + (size_t)(s + u) * a.d);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int k = 0; k < 8; ++k) v[k] += (float)y[u][k];
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) add(yb + (size_t)(s + u) * a.d);
+      }
+    }
+    for (; s < s1; ++s) add(yb + (size_t)s * a.d);
+    elem* orow = (elem*)a.out + (size_t)r * a.d + p0 * 16 + col;
+    store4<DT>(orow, v[0], v[1], v[2], v[3]);
+    store4<DT>(orow + 4, v[4], v[5], v[6], v[7]);
   }
 }
 

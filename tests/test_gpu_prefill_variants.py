@@ -10,6 +10,10 @@ blocks, a wave with more than 32 rows on one expert (the rows past the
 prefetched blocks), no active expert at all, one expert, gated experts, and a
 bitwise repeat.  DECO_PATH_PREFILL_PAIRS: the per-pair output rows and the
 combine kernel, at full size (what DECO_PATH_PREFILL runs).
+DECO_PATH_PREFILL_FUSED: the shared expert's down-projection and the combine
+in one kernel (8-, 4- and 2-panel tiles by batch size), on the same shapes,
+with the split expert tiles of small batches, gated experts, no active
+expert, and at full size.
 """
 import numpy as np
 import pytest
@@ -24,7 +28,7 @@ pytestmark = pytest.mark.gpu
 
 import sparse_moe_relu_amd as dm
 
-TOKEN, PAIRS = dm.DECO_PATH_PREFILL_TOKEN, dm.DECO_PATH_PREFILL_PAIRS
+TOKEN, PAIRS, FUSED = dm.DECO_PATH_PREFILL_TOKEN, dm.DECO_PATH_PREFILL_PAIRS, dm.DECO_PATH_PREFILL_FUSED
 
 
 def test_token_variant_c1_fp32():
@@ -81,20 +85,62 @@ def test_token_variant_needs_at_most_four_k_blocks():
     lib = dm.load_library()
     st = lib.deco_moe_forward_path(layer.handle, x.data_ptr(), L.T, out.data_ptr(), None, TOKEN)
     assert st == dm.DECO_ERR_UNSUPPORTED
-    assert lib.deco_moe_forward_path(layer.handle, x.data_ptr(), L.T, out.data_ptr(), None, 5) == \
+    assert lib.deco_moe_forward_path(layer.handle, x.data_ptr(), L.T, out.data_ptr(), None, 6) == \
         dm.DECO_ERR_INVALID_ARG
     layer.free()
 
 
-def test_both_variants_full_size_c3():
+def test_all_variants_full_size_c3():
     L = make_layer(3)
     ref = oracle.forward(L.x, **L.weights(), eps=L.eps)
     layer = _layer_obj(L, L.T)
     a = check(L, ref, layer, PAIRS, label="c3-pairs")
-    b = check(L, ref, layer, TOKEN, label="c3-token")
+    check(L, ref, layer, TOKEN, label="c3-token")
+    check(L, ref, layer, FUSED, label="c3-fused")
     c = check(L, ref, layer, dm.DECO_PATH_PREFILL, label="c3-prefill")
     assert np.array_equal(a, c), "DECO_PATH_PREFILL runs the pairs variant"
     for T in (257, 4001):
         check(L, _subset(ref, T), layer, PAIRS, T=T, label="c3-pairs-ragged")
         check(L, _subset(ref, T), layer, TOKEN, T=T, label="c3-token-ragged")
+        check(L, _subset(ref, T), layer, FUSED, T=T, label="c3-fused-ragged")
+    layer.free()
+
+
+def test_fused_variant_c1_fp32():
+    L = make_layer(1)
+    ref = oracle.forward(L.x, **L.weights(), eps=L.eps)
+    layer = _layer_obj(L, 64)
+    check(L, ref, layer, FUSED, label="c1-fused")
+    layer.free()
+
+
+@pytest.mark.parametrize("shape", [
+    (256, 24, 128, 128, "bf16", 0.2),
+    (192, 70, 64, 96, "bf16", 0.3),     # a partial 8-, 4- and 2-panel column tile (d = 12 panels)
+    (1024, 40, 32, 64, "bf16", 0.3),
+    (128, 3, 64, 160, "f32", 0.3),
+])
+@pytest.mark.parametrize("T", [1, 77, 300, 1100])
+def test_fused_variant_shapes(shape, T):
+    d, E, F, Fs, dt, ratio = shape
+    L = make_custom(d, E, F, Fs, T, dt, seed=7, ratio=ratio)
+    ref = oracle.forward(L.x, **L.weights(), eps=L.eps)
+    layer = _layer_obj(L, 1100)
+    got = check(L, ref, layer, FUSED, label=f"fused{shape}")
+    again = layer(x_tensor(L), path=FUSED).float().cpu().numpy().astype(np.float64)
+    assert np.array_equal(got, again), "the fused prefill is not repeatable bitwise"
+    layer.free()
+
+
+def test_fused_variant_no_active_expert_and_gated():
+    L = make_custom(256, 24, 128, 128, 300, "bf16", seed=4)
+    L.b_r = np.full_like(L.b_r, -1e4)
+    ref = oracle.forward(L.x, **L.weights(), eps=L.eps)
+    layer = _layer_obj(L, 300)
+    check(L, ref, layer, FUSED, label="fused-none-active")
+    layer.free()
+    L = make_custom(256, 24, 128, 128, 300, "bf16", seed=6, ratio=0.3, gated=True)
+    ref = oracle.forward(L.x, **L.weights(), eps=L.eps)
+    layer = dm.Layer(**layer_tensors(L), max_tokens=300, eps=L.eps)
+    check(L, ref, layer, FUSED, label="fused-gated")
     layer.free()
