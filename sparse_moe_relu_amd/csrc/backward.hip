@@ -389,7 +389,10 @@ struct WArgs {
 #define DECO_WG_KS 32
 #endif
 constexpr int WG_KS = DECO_WG_KS;   // rows per step (32 or 64)
-constexpr int WG_OCC = WG_KS == 32 ? 3 : 2;   // workgroups per CU (registers, LDS)
+#ifndef DECO_WG_OCC
+#define DECO_WG_OCC (WG_KS == 32 ? 3 : 2)
+#endif
+constexpr int WG_OCC = DECO_WG_OCC;   // workgroups per CU (registers, LDS)
 
 template <class DT>
 struct WShape {
@@ -742,27 +745,6 @@ hipError_t backward(const deco_moe_layer* L, const void* x, const void* dout, in
   b.n_active = gr->n_active_pairs;
 
   const unsigned mtiles = (unsigned)((T + GM - 1) / GM);
-  hipError_t err = launch_routing<DT>(L, a, T, s);
-  if (err == hipSuccess && L->WbarLo_p)
-    err = launch(deco_host::KS_BWD_SHARED, k_bwd_mean_lo<DT>,
-                 dim3((unsigned)((T + MeanLoTile<DT>::BM - 1) / MeanLoTile<DT>::BM) *
-                      ((L->pF + MeanLoTile<DT>::BNP - 1) / MeanLoTile<DT>::BNP)),
-                 dim3(256), s, b);
-  if (err == hipSuccess)
-    err = launch(deco_host::KS_BWD_SHARED, k_bwd_shared<DT>, dim3(mtiles * ((L->pFs + GP - 1) / GP)), dim3(256), s, b);
-  if (err == hipSuccess)
-    err = launch(deco_host::KS_BWD_EXPERT, expert_kernel_bwd<DT>(L->pF), dim3(L->bwd_grid), dim3(256), s, a);
-  if (err == hipSuccess)
-    err = launch(deco_host::KS_BWD_TOKEN, k_bwd_token<DT>, dim3((unsigned)((T + 3) / 4)), dim3(256), s, b);
-  const unsigned nch = (unsigned)((T + CS_ROWS - 1) / CS_ROWS);
-  if (err == hipSuccess) err = launch(deco_host::KS_BWD_COLSUM, k_bwd_colsum1, dim3(nch, 2), dim3(256), s, b);
-  if (err == hipSuccess) err = launch(deco_host::KS_BWD_COLSUM, k_bwd_colsum2, dim3(1, 2), dim3(256), s, b);
-  if (err == hipSuccess)
-    err = launch(deco_host::KS_BWD_DENSE_DX, k_bwd_dense_dx<DT>, dim3(mtiles * ((L->pD + GP - 1) / GP)), dim3(256),
-                 s, b);
-  if (err == hipSuccess)
-    err = launch(deco_host::KS_BWD_COMBINE, k_pre_combine<DT, true>,
-                 dim3((unsigned)(((long long)T * (L->d / 8) + 255) / 256)), dim3(256), s, a);
   // weight gradients
   const int d = L->d, E = L->E, F = L->F, Fs = L->Fs, Kc = b.Kc;
   const int Tcap = L->maxT < 16 ? 16 : L->maxT;
@@ -822,26 +804,79 @@ hipError_t backward(const deco_moe_layer* L, const void* x, const void* dout, in
   // the dense jobs (K = T) in K ranges of at least 512 rows, four at most,
   // reduced in order afterwards
   const int ks = T >= 2048 ? 4 : (T >= 1024 ? 2 : 1);
-  for (WArgs* wp : {&w1, &w2}) {
-    wp->ksplit = ks;
-    wp->part = L->wpart;
-  }
-  // dW_up (w4) last: its epilogue adds G / E from w1
-  for (WArgs* wp : {&w1, &w2, &w3, &w4}) {
-    if (err != hipSuccess) break;
-    const unsigned grid = (unsigned)(wp->tm * wp->tn * (wp->per_expert ? E : wp->ksplit > 1 ? wp->ksplit : 1));
+  w1.ksplit = w2.ksplit = ks;
+  w1.part = L->wpart;
+  w2.part = L->wpart2;   // w1 and w2 run on different streams
+  auto run_job = [&](WArgs& wj, hipStream_t st) -> hipError_t {
+    const unsigned grid = (unsigned)(wj.tm * wj.tn * (wj.per_expert ? E : wj.ksplit > 1 ? wj.ksplit : 1));
     void (*kw)(WArgs) = k_bwd_wgrad<DT, false, false>;
     if constexpr (sizeof(typename DT::elem) == 2) {   // the low-part passes exist for bf16 layers only
-      if (wp->A2) kw = k_bwd_wgrad<DT, true, false>;
-      else if (wp->B2) kw = k_bwd_wgrad<DT, false, true>;
+      if (wj.A2) kw = k_bwd_wgrad<DT, true, false>;
+      else if (wj.B2) kw = k_bwd_wgrad<DT, false, true>;
     } else {
-      wp->A2 = wp->B2 = nullptr;
+      wj.A2 = wj.B2 = nullptr;
     }
-    err = launch(deco_host::KS_BWD_WGRAD, kw, dim3(grid), dim3(256), s, *wp);
-    if (err == hipSuccess && !wp->per_expert && wp->ksplit > 1)   // the partials buffer is reused by the next job
-      err = launch(deco_host::KS_BWD_WGRAD, k_bwd_wsum, dim3((unsigned)(((long long)wp->M * wp->N / 4 + 255) / 256)),
-                   dim3(256), s, *wp);
+    hipError_t e = launch(deco_host::KS_BWD_WGRAD, kw, dim3(grid), dim3(256), st, wj);
+    if (e == hipSuccess && !wj.per_expert && wj.ksplit > 1)
+      e = launch(deco_host::KS_BWD_WGRAD, k_bwd_wsum, dim3((unsigned)(((long long)wj.M * wj.N / 4 + 255) / 256)),
+                 dim3(256), st, wj);
+    return e;
+  };
+
+  // Two streams (fork and join through events, so the call stays ordered
+  // on the caller's stream as a whole).  DECO_BWD_FORK = 1: the side stream
+  // starts at once with what does not wait on the expert kernel: the shared
+  // expert's gradient rows and s (k_bwd_shared reads only x, dout and the
+  // weights), s^T dout (dWs_down), then (g a)^T dout (dW_down) once the
+  // expert kernel is done.  DECO_BWD_FORK = 2: the shared rows run before the
+  // expert kernel on the caller's stream, and the side stream takes dW_down
+  // and dWs_down beside the token, dx and the other weight-gradient kernels.
+#ifndef DECO_BWD_FORK
+#define DECO_BWD_FORK 2
+#endif
+  hipStream_t s2 = L->bwd_side;
+  hipEvent_t ev_fork = L->bwd_ev[0], ev_shared = L->bwd_ev[1], ev_expert = L->bwd_ev[2], ev_join = L->bwd_ev[3];
+  const unsigned shared_grid = mtiles * ((L->pFs + GP - 1) / GP);
+  hipError_t err = hipSuccess;
+  if (DECO_BWD_FORK == 1) {
+    err = hipEventRecord(ev_fork, s);
+    if (err == hipSuccess) err = hipStreamWaitEvent(s2, ev_fork, 0);
+    if (err == hipSuccess) err = launch(deco_host::KS_BWD_SHARED, k_bwd_shared<DT>, dim3(shared_grid), dim3(256), s2, b);
+    if (err == hipSuccess) err = hipEventRecord(ev_shared, s2);
+    if (err == hipSuccess) err = run_job(w2, s2);
   }
+  if (err == hipSuccess) err = launch_routing<DT>(L, a, T, s);
+  if (err == hipSuccess && L->WbarLo_p)
+    err = launch(deco_host::KS_BWD_SHARED, k_bwd_mean_lo<DT>,
+                 dim3((unsigned)((T + MeanLoTile<DT>::BM - 1) / MeanLoTile<DT>::BM) *
+                      ((L->pF + MeanLoTile<DT>::BNP - 1) / MeanLoTile<DT>::BNP)),
+                 dim3(256), s, b);
+  if (DECO_BWD_FORK != 1 && err == hipSuccess)
+    err = launch(deco_host::KS_BWD_SHARED, k_bwd_shared<DT>, dim3(shared_grid), dim3(256), s, b);
+  if (err == hipSuccess)
+    err = launch(deco_host::KS_BWD_EXPERT, expert_kernel_bwd<DT>(L->pF), dim3(L->bwd_grid), dim3(256), s, a);
+  if (err == hipSuccess) err = hipEventRecord(ev_expert, s);
+  if (err == hipSuccess) err = hipStreamWaitEvent(s2, ev_expert, 0);
+  if (err == hipSuccess) err = run_job(w3, s2);
+  if (DECO_BWD_FORK != 1 && err == hipSuccess) err = run_job(w2, s2);
+  if (err == hipSuccess) err = hipEventRecord(ev_join, s2);
+
+  if (DECO_BWD_FORK == 1 && err == hipSuccess) err = hipStreamWaitEvent(s, ev_shared, 0);
+  if (err == hipSuccess)
+    err = launch(deco_host::KS_BWD_TOKEN, k_bwd_token<DT>, dim3((unsigned)((T + 3) / 4)), dim3(256), s, b);
+  const unsigned nch = (unsigned)((T + CS_ROWS - 1) / CS_ROWS);
+  if (err == hipSuccess) err = launch(deco_host::KS_BWD_COLSUM, k_bwd_colsum1, dim3(nch, 2), dim3(256), s, b);
+  if (err == hipSuccess) err = launch(deco_host::KS_BWD_COLSUM, k_bwd_colsum2, dim3(1, 2), dim3(256), s, b);
+  if (err == hipSuccess)
+    err = launch(deco_host::KS_BWD_DENSE_DX, k_bwd_dense_dx<DT>, dim3(mtiles * ((L->pD + GP - 1) / GP)), dim3(256),
+                 s, b);
+  if (err == hipSuccess)
+    err = launch(deco_host::KS_BWD_COMBINE, k_pre_combine<DT, true>,
+                 dim3((unsigned)(((long long)T * (L->d / 8) + 255) / 256)), dim3(256), s, a);
+  // dW_up (w4) after w1: its epilogue adds G / E from w1
+  if (err == hipSuccess) err = run_job(w1, s);
+  if (err == hipSuccess) err = run_job(w4, s);
+  if (err == hipSuccess) err = hipStreamWaitEvent(s, ev_join, 0);
   if (err != hipSuccess) return err;
   return hipGetLastError();
 }
@@ -864,7 +899,10 @@ hipError_t plan_backward(deco_moe_layer* L) {
   if (err != hipSuccess) return err;
   int grid = (occ < 1 ? 1 : occ) * (L->n_cu < 1 ? 1 : L->n_cu);
   L->bwd_grid = (grid + NXCD - 1) / NXCD * NXCD;
-  return hipSuccess;
+  // the side stream (default priority) and its fork/join events
+  err = hipStreamCreateWithFlags(&L->bwd_side, hipStreamNonBlocking);
+  for (int i = 0; i < 4 && err == hipSuccess; ++i) err = hipEventCreateWithFlags(&L->bwd_ev[i], hipEventDisableTiming);
+  return err;
 }
 
 }  // namespace deco_host

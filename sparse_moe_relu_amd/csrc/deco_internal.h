@@ -10,7 +10,7 @@
 
 // offsets (bytes from the prefill/backward workspace's base) of its buffers
 struct PwsOff {
-  size_t to, ec, lt, sb, yb, sr, dg, dh, ag, sl, dc, dz, dl, gb, cp, wp, dhl, agl, dcl, sbh, sbl, hp;
+  size_t to, ec, lt, sb, yb, sr, dg, dh, ag, sl, dc, dz, dl, gb, cp, wp, dhl, agl, dcl, sbh, sbl, hp, wp2;
 };
 
 struct deco_moe_layer {
@@ -35,6 +35,9 @@ struct deco_moe_layer {
   int pre_grid;            // persistent grid of the prefill expert kernel
   int n_cu;                // compute units of the device
   int bwd_grid;            // persistent grid of the backward expert kernel
+  hipStream_t bwd_side;    // backward: a second stream for the branches that do not wait on the
+                           // expert kernel (default priority), and its fork/join events
+  hipEvent_t bwd_ev[4];
   int gated;               // gated routed experts: NormSiLU(x.W_gate[e]) * (x.W_up[e])
 
   // packed weights (one allocation)
@@ -107,7 +110,8 @@ struct deco_moe_layer {
   float* dlz;              // [Tcap][E] ReLU(z) * dLoss/dg
   float* gbuf;             // [d][F] x^T dm (gradient of Wbar)
   float* colpart;          // [2][ceil(Tcap / 64)][E] partial column sums (db_r, dlambda)
-  float* wpart;            // [4][max(d * (Fp + Ep + Fsp), Fs * d)] partial weight-gradient tiles
+  float* wpart;            // [4][d * (Fp + Ep + Fsp)] partial weight-gradient tiles of x^T [dm | dz | du_s]
+  float* wpart2;           // [4][Fs * d] those of s^T dout (the two jobs run on different streams)
   float* sraw;             // shared_rms: [Tcap][Fs] x . Ws_up before the RMS-only NormSiLU (fp32)
   float* hpart;            // [SPLIT_NKS][split_maxT * (E + 1)][F] K-part sums of x . W_up[e] per
                            // pair slot (small-batch prefill), or null

@@ -140,6 +140,7 @@ void bind_pws(deco_moe_layer* L, char* base) {
     L->gbuf = (float*)(base + o.gb);
     L->colpart = (float*)(base + o.cp);
     L->wpart = (float*)(base + o.wp);
+    L->wpart2 = (float*)(base + o.wp2);
     L->sb_hi = base + o.sbh;
     if (split) {
       L->dhbuf_lo = base + o.dhl;
@@ -256,6 +257,9 @@ void deco_moe_free(deco_moe_layer* L) {
   if (L->ws) (void)hipFree(L->ws);
   if (L->pws_shared) shared_ws_release(L);
   else if (L->pws) (void)hipFree(L->pws);
+  for (hipEvent_t& e : L->bwd_ev)
+    if (e) (void)hipEventDestroy(e);
+  if (L->bwd_side) (void)hipStreamDestroy(L->bwd_side);
   delete L;
 }
 
@@ -353,8 +357,8 @@ static int load_layer(const deco_moe_config* cfg, const void* W_r, const float* 
   size_t o_dl = bwd ? k.take(sizeof(float) * Tcap * E) : 0;
   size_t o_gb = bwd ? k.take(sizeof(float) * (size_t)L->d * L->F) : 0;
   size_t o_cp = bwd ? k.take(sizeof(float) * 2 * ((Tcap + 63) / 64) * E) : 0;
-  const size_t wpart_n = std::max((size_t)L->d * (L->Fp + L->Ep + L->Fsp), (size_t)L->Fs * L->d);
-  size_t o_wp = bwd ? k.take(sizeof(float) * 4 * wpart_n) : 0;
+  size_t o_wp = bwd ? k.take(sizeof(float) * 4 * (size_t)L->d * (L->Fp + L->Ep + L->Fsp)) : 0;
+  size_t o_wp2 = bwd ? k.take(sizeof(float) * 4 * (size_t)L->Fs * L->d) : 0;
   const bool split = bwd && L->esz == 2;   // low parts of the backward's bf16 operands
   size_t o_dhl = split ? k.take((size_t)L->esz * n_slots * L->F) : 0;
   size_t o_agl = split ? k.take((size_t)L->esz * n_slots * L->F) : 0;
@@ -377,7 +381,7 @@ static int load_layer(const deco_moe_config* cfg, const void* W_r, const float* 
                   o_dz ? o_dz - o_to : 0, o_dl ? o_dl - o_to : 0, o_gb ? o_gb - o_to : 0,
                   o_cp ? o_cp - o_to : 0, o_wp ? o_wp - o_to : 0, o_dhl ? o_dhl - o_to : 0,
                   o_agl ? o_agl - o_to : 0, o_dcl ? o_dcl - o_to : 0, o_sbh ? o_sbh - o_to : 0,
-                  o_sbl ? o_sbl - o_to : 0, o_hp ? o_hp - o_to : 0};
+                  o_sbl ? o_sbl - o_to : 0, o_hp ? o_hp - o_to : 0, o_wp2 ? o_wp2 - o_to : 0};
 
   if (hipMalloc((void**)&L->wmem, L->wmem_bytes) != hipSuccess) {
     (void)hipGetLastError();
