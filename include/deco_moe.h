@@ -264,9 +264,9 @@ typedef struct {
  * previous forward call is needed.  Requires a layer loaded with
  * cfg.backward = 1 and non-gated experts (else DECO_ERR_UNSUPPORTED); T in
  * 1..max_tokens; asynchronous on `stream`; allocates nothing.  Part of the
- * work runs on a second stream the layer creates at load (default priority),
- * forked from `stream` and joined back into it by events, so the call is
- * ordered on `stream` as a whole.  Overwrites the layer's routing state
+ * work runs on two more streams the layer creates at load (default
+ * priority), forked from `stream` and joined back into it by events, so the
+ * call is ordered on `stream` as a whole.  Overwrites the layer's routing state
  * (deco_moe_copy_routing then describes x). */
 int deco_moe_backward(const deco_moe_layer* L, const void* x, const void* dout, int64_t T,
                       float reg_coef, const deco_moe_grads* grads, void* stream);

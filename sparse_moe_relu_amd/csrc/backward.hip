@@ -823,60 +823,48 @@ hipError_t backward(const deco_moe_layer* L, const void* x, const void* dout, in
     return e;
   };
 
-  // Two streams (fork and join through events, so the call stays ordered
-  // on the caller's stream as a whole).  DECO_BWD_FORK = 1: the side stream
-  // starts at once with what does not wait on the expert kernel: the shared
-  // expert's gradient rows and s (k_bwd_shared reads only x, dout and the
-  // weights), s^T dout (dWs_down), then (g a)^T dout (dW_down) once the
-  // expert kernel is done.  DECO_BWD_FORK = 2: the shared rows run before the
-  // expert kernel on the caller's stream, and the side stream takes dW_down
-  // and dWs_down beside the token, dx and the other weight-gradient kernels.
-#ifndef DECO_BWD_FORK
-#define DECO_BWD_FORK 2
-#endif
-  hipStream_t s2 = L->bwd_side;
-  hipEvent_t ev_fork = L->bwd_ev[0], ev_shared = L->bwd_ev[1], ev_expert = L->bwd_ev[2], ev_join = L->bwd_ev[3];
-  const unsigned shared_grid = mtiles * ((L->pFs + GP - 1) / GP);
-  hipError_t err = hipSuccess;
-  if (DECO_BWD_FORK == 1) {
-    err = hipEventRecord(ev_fork, s);
-    if (err == hipSuccess) err = hipStreamWaitEvent(s2, ev_fork, 0);
-    if (err == hipSuccess) err = launch(deco_host::KS_BWD_SHARED, k_bwd_shared<DT>, dim3(shared_grid), dim3(256), s2, b);
-    if (err == hipSuccess) err = hipEventRecord(ev_shared, s2);
-    if (err == hipSuccess) err = run_job(w2, s2);
-  }
-  if (err == hipSuccess) err = launch_routing<DT>(L, a, T, s);
+  // Three streams, forked from the caller's stream and joined back into it
+  // through events, so the call stays ordered on the caller's stream as a
+  // whole.  The caller's stream runs routing, the shared rows, the expert
+  // kernel, the token kernel, G and dW_up; once the expert kernel is done a
+  // side stream runs dW_down and dWs_down, and once the token kernel is done
+  // another runs the column sums, dense dx and the dx combine.
+  hipStream_t s2 = L->bwd_side[0], s3 = L->bwd_side[1];
+  hipEvent_t ev_expert = L->bwd_ev[0], ev_join2 = L->bwd_ev[1], ev_token = L->bwd_ev[2], ev_join3 = L->bwd_ev[3];
+  hipError_t err = launch_routing<DT>(L, a, T, s);
   if (err == hipSuccess && L->WbarLo_p)
     err = launch(deco_host::KS_BWD_SHARED, k_bwd_mean_lo<DT>,
                  dim3((unsigned)((T + MeanLoTile<DT>::BM - 1) / MeanLoTile<DT>::BM) *
                       ((L->pF + MeanLoTile<DT>::BNP - 1) / MeanLoTile<DT>::BNP)),
                  dim3(256), s, b);
-  if (DECO_BWD_FORK != 1 && err == hipSuccess)
-    err = launch(deco_host::KS_BWD_SHARED, k_bwd_shared<DT>, dim3(shared_grid), dim3(256), s, b);
+  if (err == hipSuccess)
+    err = launch(deco_host::KS_BWD_SHARED, k_bwd_shared<DT>, dim3(mtiles * ((L->pFs + GP - 1) / GP)), dim3(256), s, b);
   if (err == hipSuccess)
     err = launch(deco_host::KS_BWD_EXPERT, expert_kernel_bwd<DT>(L->pF), dim3(L->bwd_grid), dim3(256), s, a);
   if (err == hipSuccess) err = hipEventRecord(ev_expert, s);
   if (err == hipSuccess) err = hipStreamWaitEvent(s2, ev_expert, 0);
   if (err == hipSuccess) err = run_job(w3, s2);
-  if (DECO_BWD_FORK != 1 && err == hipSuccess) err = run_job(w2, s2);
-  if (err == hipSuccess) err = hipEventRecord(ev_join, s2);
-
-  if (DECO_BWD_FORK == 1 && err == hipSuccess) err = hipStreamWaitEvent(s, ev_shared, 0);
+  if (err == hipSuccess) err = run_job(w2, s2);
+  if (err == hipSuccess) err = hipEventRecord(ev_join2, s2);
   if (err == hipSuccess)
     err = launch(deco_host::KS_BWD_TOKEN, k_bwd_token<DT>, dim3((unsigned)((T + 3) / 4)), dim3(256), s, b);
+  if (err == hipSuccess) err = hipEventRecord(ev_token, s);
+  if (err == hipSuccess) err = hipStreamWaitEvent(s3, ev_token, 0);
   const unsigned nch = (unsigned)((T + CS_ROWS - 1) / CS_ROWS);
-  if (err == hipSuccess) err = launch(deco_host::KS_BWD_COLSUM, k_bwd_colsum1, dim3(nch, 2), dim3(256), s, b);
-  if (err == hipSuccess) err = launch(deco_host::KS_BWD_COLSUM, k_bwd_colsum2, dim3(1, 2), dim3(256), s, b);
+  if (err == hipSuccess) err = launch(deco_host::KS_BWD_COLSUM, k_bwd_colsum1, dim3(nch, 2), dim3(256), s3, b);
+  if (err == hipSuccess) err = launch(deco_host::KS_BWD_COLSUM, k_bwd_colsum2, dim3(1, 2), dim3(256), s3, b);
   if (err == hipSuccess)
     err = launch(deco_host::KS_BWD_DENSE_DX, k_bwd_dense_dx<DT>, dim3(mtiles * ((L->pD + GP - 1) / GP)), dim3(256),
-                 s, b);
+                 s3, b);
   if (err == hipSuccess)
     err = launch(deco_host::KS_BWD_COMBINE, k_pre_combine<DT, true>,
-                 dim3((unsigned)(((long long)T * (L->d / 8) + 255) / 256)), dim3(256), s, a);
+                 dim3((unsigned)(((long long)T * (L->d / 8) + 255) / 256)), dim3(256), s3, a);
+  if (err == hipSuccess) err = hipEventRecord(ev_join3, s3);
   // dW_up (w4) after w1: its epilogue adds G / E from w1
   if (err == hipSuccess) err = run_job(w1, s);
   if (err == hipSuccess) err = run_job(w4, s);
-  if (err == hipSuccess) err = hipStreamWaitEvent(s, ev_join, 0);
+  if (err == hipSuccess) err = hipStreamWaitEvent(s, ev_join3, 0);
+  if (err == hipSuccess) err = hipStreamWaitEvent(s, ev_join2, 0);
   if (err != hipSuccess) return err;
   return hipGetLastError();
 }
@@ -900,8 +888,8 @@ hipError_t plan_backward(deco_moe_layer* L) {
   int grid = (occ < 1 ? 1 : occ) * (L->n_cu < 1 ? 1 : L->n_cu);
   L->bwd_grid = (grid + NXCD - 1) / NXCD * NXCD;
   // the side stream (default priority) and its fork/join events
-  err = hipStreamCreateWithFlags(&L->bwd_side, hipStreamNonBlocking);
-  for (int i = 0; i < 4 && err == hipSuccess; ++i) err = hipEventCreateWithFlags(&L->bwd_ev[i], hipEventDisableTiming);
+  for (int i = 0; i < 2 && err == hipSuccess; ++i) err = hipStreamCreateWithFlags(&L->bwd_side[i], hipStreamNonBlocking);
+  for (int i = 0; i < 6 && err == hipSuccess; ++i) err = hipEventCreateWithFlags(&L->bwd_ev[i], hipEventDisableTiming);
   return err;
 }
 

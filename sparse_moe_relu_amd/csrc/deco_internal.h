@@ -35,9 +35,9 @@ struct deco_moe_layer {
   int pre_grid;            // persistent grid of the prefill expert kernel
   int n_cu;                // compute units of the device
   int bwd_grid;            // persistent grid of the backward expert kernel
-  hipStream_t bwd_side;    // backward: a second stream for the branches that do not wait on the
-                           // expert kernel (default priority), and its fork/join events
-  hipEvent_t bwd_ev[4];
+  hipStream_t bwd_side[2]; // backward: two more streams for branches that run beside the caller's
+                           // stream (default priority), and their fork/join events
+  hipEvent_t bwd_ev[6];
   int gated;               // gated routed experts: NormSiLU(x.W_gate[e]) * (x.W_up[e])
 
   // packed weights (one allocation)

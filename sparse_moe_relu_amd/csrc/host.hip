@@ -259,7 +259,8 @@ void deco_moe_free(deco_moe_layer* L) {
   else if (L->pws) (void)hipFree(L->pws);
   for (hipEvent_t& e : L->bwd_ev)
     if (e) (void)hipEventDestroy(e);
-  if (L->bwd_side) (void)hipStreamDestroy(L->bwd_side);
+  for (hipStream_t& st : L->bwd_side)
+    if (st) (void)hipStreamDestroy(st);
   delete L;
 }
 
