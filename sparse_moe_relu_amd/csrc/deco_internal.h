@@ -87,7 +87,7 @@ struct deco_moe_layer {
   PwsOff pwo;
   void* hwords;            // [n_hwords] 64-bit decode hand-off words (epoch | value)
   int n_hwords;
-  unsigned* dec_ctr;       // [dec_grid_up] epoch counters of the decode up kernel's workgroups
+  unsigned* dec_ctr;       // decode call counter (the up kernel's epoch is 1 + its value)
   char* arow;              // [E][16][dec_Fp] routed activations (down operand type)
   char* srow;              // [16][dec_Fsp] shared activations (layer dtype)
   // prefill

@@ -35,9 +35,10 @@
 // 64-bit words written and read with agent-scope relaxed atomics: the high
 // half is the call's epoch and the low half the value, so a reader needs no
 // separate flag and no fence, and a word left from an earlier call is never
-// taken for this call's.  Each workgroup takes the epoch from an atomic
-// increment of its own counter word (every call increments every counter
-// once, so they stay equal and no two workgroups contend).  Waiting workgroups only
+// taken for this call's.  The epoch is 1 + a call counter that the down
+// kernel advances once per call, read by every up workgroup with a plain
+// load (the kernel boundary orders the increment before the next call's
+// reads).  Waiting workgroups only
 // depend on the other slices of their own expert (consecutive workgroups) and,
 // with TopK routing, on every routed workgroup; every wait is bounded (a
 // timeout sets the layer's error flag).
@@ -88,7 +89,7 @@ struct DecArgs {
   unsigned* rflag;          // [E] 1: no token routed to e, 2: some token was
   u64* hw;                  // hand-off words: [E * S][16] sums of squares |
                             // [E][16] logits (TopK) | [n_sh][16] shared sums of squares
-  unsigned* ctr;            // [grid] epoch counters, one per up-kernel workgroup
+  unsigned* ctr;            // call counter: the up kernel's epoch is 1 + its value
   void* arow;               // [E][16][Fp] routed activations, down operand type
   void* srow;               // [16][Fsp] shared activations, layer dtype
   int Fp, Fsp;              // F, Fs padded to whole column-pair fragments
@@ -141,6 +142,12 @@ __device__ __forceinline__ i32x4_t ld16_buf(__amdgpu_buffer_rsrc_t r, unsigned v
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, unsigned bytes = 0x7FFFFFFFu) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }
+// one 32-bit word p[i] as a vector-memory load: a uniform load written as
+// p[i] becomes a scalar load, and the scalar loads' wait (shared with the
+// kernel-argument loads) would come before the router's first vector load
+__device__ __forceinline__ unsigned ld_word(const void* p, int i) {
+  return (unsigned)__builtin_amdgcn_raw_buffer_load_b32(buf_rsrc(p), 4 * i, 0, 0);
+}
 
 // acc[p] += x[16 rows][k-blocks kb_lo .. kb_hi) . W[..][panels p0 + p] for p < NP
 // (panels at or past pmax read panel pmax - 1; their results are dropped by
@@ -184,6 +191,7 @@ __device__ __forceinline__ void up_stream(__amdgpu_buffer_rsrc_t rx, __amdgpu_bu
         wf[u][p] = ld16_buf(rw, 16u * l, (unsigned)frag_off(pp, kb, nkb));
       }
     }
+    __builtin_amdgcn_sched_barrier(0);   // the whole batch in flight before its first product
 #pragma unroll
     for (int u = 0; u < U; ++u)
       if (kb0 + u < kb_hi) {
@@ -239,12 +247,13 @@ __global__ void __launch_bounds__(DNT) k_dec_up(DecArgs a) {
   __shared__ float s_gate[16], s_ssx[16][33];
   __shared__ int s_act[16];
   __shared__ float s_zall[16][257];   // TopK: every expert's logits
-  __shared__ unsigned s_ep;
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, c = l & 15, g = l >> 4;
   const int b = blockIdx.x;
-  // this call's epoch: 1 + the number of earlier calls (the atomic returns
-  // the coherent value of this workgroup's counter and advances it)
-  if (tid == 0) s_ep = __hip_atomic_fetch_add(a.ctr + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+  // this call's epoch (ep below): 1 + the number of earlier calls.  The down
+  // kernel of each call advances the counter once; the kernel boundary
+  // between that launch and this one makes the new value visible, so a plain
+  // load issued behind the first loads reads it (no atomic round trip in
+  // front of them)
   const int kind = b < a.n_sh ? 1 : 2;   // shared, routed
   const int rb = b - a.n_sh;
   const int e = kind == 2 ? rb / a.S : 0;
@@ -288,7 +297,7 @@ __global__ void __launch_bounds__(DNT) k_dec_up(DecArgs a) {
     if constexpr (SR) {
 #pragma unroll
       for (int o = 16; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
-      const unsigned ep = s_ep;
+      const unsigned ep = ld_word(a.ctr, 0) + 1u;
       if (cq == 0) put_word(hw_sh(a) + (size_t)slice * 16 + row, ep, ss);
       // every shared workgroup's sums (32 at a time, one per thread of the
       // row), then the row's 1 / RMS
@@ -320,20 +329,26 @@ __global__ void __launch_bounds__(DNT) k_dec_up(DecArgs a) {
 
   // ---- routed: router logits of expert e for the 16 (padded) token rows;
   // each lane sums x[c][k] W_r[k][e] over its fragment entries, waves over d
-  const float lam_e = a.lam[e], b_e = a.b_r[e];
+  float lam_e, b_e;
+  unsigned ep;
   {
     const char* wr = a.Wr_p + frag_off(e >> 4, 0, nkb) + (size_t)((e & 15) + 16 * g) * 16;
     const unsigned xoff = (unsigned)(((size_t)c * a.d + (size_t)DT::EPL * g) * sizeof(elem));
     float zp = 0.f;
     x_loaded = kb_hi - kb_lo <= U;
-    for (int kb0 = kb_lo; kb0 < kb_hi; kb0 += U) {
-      i32x4_t xv[U], wv[U];
+    i32x4_t xv[U], wv[U];
+    auto loads = [&](int kb0) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int kb = kb0 + u < kb_hi ? kb0 + u : kb_hi - 1;
+        // past the wave's range: a valid block (k-block 0 for a wave with
+        // none), whose products are skipped
+        int kb = kb0 + u < kb_hi ? kb0 + u : kb_hi - 1;
+        kb = kb < 0 ? 0 : kb;
         xv[u] = ld16_buf(rx, xoff, (unsigned)(kb * DT::KB * sizeof(elem)));
         wv[u] = ld16(wr + (size_t)kb * FRAG_BYTES);
       }
+    };
+    auto products = [&](int kb0) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (kb0 + u < kb_hi) {
@@ -342,13 +357,28 @@ __global__ void __launch_bounds__(DNT) k_dec_up(DecArgs a) {
         }
         x0[u] = xv[u];
       }
+    };
+    // the first batch in straight-line code: in a loop, a register reused
+    // across the back edge puts a wait for older loads in front of it
+    loads(kb_lo);
+    // the call's epoch and the expert's router scalars, behind the batch
+    ep = ld_word(a.ctr, 0) + 1u;
+    lam_e = __uint_as_float(ld_word(a.lam, e));
+    b_e = __uint_as_float(ld_word(a.b_r, e));
+    // every load of the batch before the first product (the scheduler
+    // otherwise sinks some below the first FMAs, a second round trip)
+    __builtin_amdgcn_sched_barrier(0);
+    products(kb_lo);
+    for (int kb0 = kb_lo + U; kb0 < kb_hi; kb0 += U) {
+      loads(kb0);
+      __builtin_amdgcn_sched_barrier(0);
+      products(kb0);
     }
     zp += __shfl_xor(zp, 16);
     zp += __shfl_xor(zp, 32);
     if (g == 0) s_zr[w][c] = zp;
   }
   __syncthreads();
-  const unsigned ep = s_ep;
   if (tid < 16) {
     float zz = 0.f;
 #pragma unroll
@@ -510,6 +540,9 @@ __global__ void __launch_bounds__(DNT) k_dec_down(DecArgs a) {
   const int r16 = l & 15, g = l >> 4, half = r16 >> 3;
   const int cg0 = blockIdx.x * CG;   // first of the workgroup's column groups
   const int kps = a.kps, kpe = a.kpe;
+  // the call counter the next call's up kernel takes its epoch from (this
+  // call's up kernel has read it; nothing waits for the result)
+  if (blockIdx.x == 0 && tid == 0) __hip_atomic_fetch_add(a.ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // routing flags first, so the shared slots' loads queue behind them
   unsigned rf[4];
@@ -782,7 +815,7 @@ ScratchPlan scratch_plan(const deco_moe_layer* L) {
   p.o_hw = o;
   o += al256(sizeof(u64) * (size_t)L->n_hwords);
   p.o_ct = o;
-  o += al256(sizeof(unsigned) * (size_t)L->dec_grid_up);
+  o += al256(sizeof(unsigned));
   p.o_rf = o;
   o += al256(sizeof(unsigned) * (size_t)L->E);
   p.o_a8 = o;

@@ -335,7 +335,7 @@ static int load_layer(const deco_moe_config* cfg, const void* W_r, const float* 
   size_t o_er = k.take(sizeof(unsigned));
   size_t o_a8 = k.take((size_t)16 * E);
   size_t o_hw = k.take(sizeof(uint64_t) * (size_t)L->n_hwords);
-  size_t o_ct = k.take(sizeof(unsigned) * (size_t)L->dec_grid_up);
+  size_t o_ct = k.take(sizeof(unsigned));   // the decode call counter
   const size_t dn_esz = L->esz == 2 ? 2 : 4;   // fp16 operands for bf16 layers
   size_t o_ar = k.take(dn_esz * (size_t)E * 16 * L->dec_Fp);
   size_t o_sr2 = k.take((size_t)L->esz * 16 * L->dec_Fsp);
