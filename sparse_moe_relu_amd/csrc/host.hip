@@ -23,7 +23,12 @@ int validate_cfg(const deco_moe_config* c) {
     return DECO_ERR_INVALID_ARG;
   if (!(c->rms_eps >= 0.0f) || !isfinite(c->rms_eps)) return DECO_ERR_INVALID_ARG;
   if (c->top_k < 0 || c->top_k > c->n_experts) return DECO_ERR_INVALID_ARG;
-  if (c->dtype != DECO_DT_BF16 && c->dtype != DECO_DT_F32) return DECO_ERR_UNSUPPORTED;
+  // the dtype field as the integer a C caller stored (a C++ load of an enum
+  // outside its listed values is undefined)
+  static_assert(sizeof(deco_dtype) == sizeof(int32_t), "deco_dtype is stored as a 32-bit int");
+  int32_t dt = 0;
+  memcpy(&dt, &c->dtype, sizeof(dt));
+  if (dt != DECO_DT_BF16 && dt != DECO_DT_F32) return DECO_ERR_UNSUPPORTED;
   if (c->d_model % 64 != 0 || c->d_model > 32768) return DECO_ERR_UNSUPPORTED;
   if (c->n_experts > 256) return DECO_ERR_UNSUPPORTED;
   if (c->d_ff != 32 && c->d_ff != 64 && c->d_ff != 128 && c->d_ff != 256) return DECO_ERR_UNSUPPORTED;
