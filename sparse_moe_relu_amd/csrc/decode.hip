@@ -168,30 +168,26 @@ __device__ __forceinline__ i32x4_t bf16x8_to_f16x8(const i32x4_t& v, bool& bad) 
 }
 
 // XH: the W fragments are fp16 (bf16 layers' folded NormSiLU input) and the
-// x fragments are converted to fp16 for the product
-template <class DT, int NP, bool XH = false>
+// x fragments are converted to fp16 for the product.  XPRE: x0 holds the
+// first batch's x fragments (loaded by the router).  WPRE: w0 holds the first
+// batch's W fragments (requested before the routing decision).  The first
+// batch is straight-line code (no wait inherited from a loop's back edge).
+template <class DT, int NP, bool XH = false, bool XPRE = false, bool WPRE = false>
 __device__ __forceinline__ void up_stream(__amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rw, int p0, int pmax,
                                           int nkb, int kb_lo, int kb_hi, int d, f32x4_t (&acc)[NP],
-                                          bool x_loaded, const i32x4_t* x0, bool* xbad = nullptr) {
+                                          const i32x4_t* x0, bool* xbad = nullptr,
+                                          const i32x4_t (*w0)[NP] = nullptr) {
   using elem = typename DT::elem;
   constexpr int U = 8;
   const int l = threadIdx.x & 63, c = l & 15, g = l >> 4;
   const unsigned xoff = (unsigned)(((size_t)c * d + (size_t)DT::EPL * g) * sizeof(elem));
-  for (int kb0 = kb_lo; kb0 < kb_hi; kb0 += U) {
-    i32x4_t xf[U], wf[U][NP];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      int kb = kb0 + u;
-      kb = kb < kb_hi ? kb : kb_hi - 1;   // past the range: a valid block, its products are skipped
-      if (x_loaded && kb0 == kb_lo) xf[u] = x0[u];
-      else xf[u] = ld16_buf(rx, xoff, (unsigned)(kb * DT::KB * sizeof(elem)));
-#pragma unroll
-      for (int p = 0; p < NP; ++p) {
-        const int pp = p0 + p < pmax ? p0 + p : pmax - 1;
-        wf[u][p] = ld16_buf(rw, 16u * l, (unsigned)frag_off(pp, kb, nkb));
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);   // the whole batch in flight before its first product
+  // past the wave's range: a valid block (k-block 0 for a wave with none),
+  // whose products are skipped
+  auto blk = [&](int kb) {
+    kb = kb < kb_hi ? kb : kb_hi - 1;
+    return kb < 0 ? 0 : kb;
+  };
+  auto products = [&](int kb0, const i32x4_t (&xf)[U], const i32x4_t (&wf)[U][NP]) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
       if (kb0 + u < kb_hi) {
@@ -204,6 +200,38 @@ __device__ __forceinline__ void up_stream(__amdgpu_buffer_rsrc_t rx, __amdgpu_bu
           for (int p = 0; p < NP; ++p) DT::mma(acc[p], xf[u], wf[u][p]);
         }
       }
+  };
+  {
+    i32x4_t xf[U], wf[U][NP];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kb = blk(kb_lo + u);
+      if constexpr (XPRE) xf[u] = x0[u];
+      else xf[u] = ld16_buf(rx, xoff, (unsigned)(kb * DT::KB * sizeof(elem)));
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const int pp = p0 + p < pmax ? p0 + p : pmax - 1;
+        if constexpr (WPRE) wf[u][p] = w0[u][p];
+        else wf[u][p] = ld16_buf(rw, 16u * l, (unsigned)frag_off(pp, kb, nkb));
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);   // the whole batch in flight before its first product
+    products(kb_lo, xf, wf);
+  }
+  for (int kb0 = kb_lo + U; kb0 < kb_hi; kb0 += U) {
+    i32x4_t xf[U], wf[U][NP];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kb = blk(kb0 + u);
+      xf[u] = ld16_buf(rx, xoff, (unsigned)(kb * DT::KB * sizeof(elem)));
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const int pp = p0 + p < pmax ? p0 + p : pmax - 1;
+        wf[u][p] = ld16_buf(rw, 16u * l, (unsigned)frag_off(pp, kb, nkb));
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    products(kb0, xf, wf);
   }
 }
 
@@ -229,7 +257,9 @@ __device__ __forceinline__ void reduce_waves(f32x4_t (&s_red)[DNW][NP][64], cons
 // carries none of the variants' logic)
 constexpr int DV_GATED = 1, DV_NO_MEAN = 2, DV_SHARED_RMS = 4;
 
-template <class DT, int NP, int VAR>
+// SPEC: the routed slice's first batch of W_up requested with the router's
+// loads, before the routing decision (for batches that touch most experts)
+template <class DT, int NP, int VAR, bool SPEC = false>
 __global__ void __launch_bounds__(DNT) k_dec_up(DecArgs a) {
   constexpr bool GT = (VAR & DV_GATED) != 0, NM = (VAR & DV_NO_MEAN) != 0, SR = (VAR & DV_SHARED_RMS) != 0;
   using elem = typename DT::elem;
@@ -268,8 +298,7 @@ __global__ void __launch_bounds__(DNT) k_dec_up(DecArgs a) {
   f32x4_t acc[NP], accu[NP];
 #pragma unroll
   for (int p = 0; p < NP; ++p) acc[p] = accu[p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  i32x4_t x0[U];
-  bool x_loaded = false;
+  i32x4_t x0[U];   // the router's first batch of x fragments
 
   if (kind == 1) {
     // ---- shared expert: slices slice * nsub .. (+ nsub), SiLU(x . Ws_up) as
@@ -281,7 +310,7 @@ __global__ void __launch_bounds__(DNT) k_dec_up(DecArgs a) {
       if (q >= a.n_shs) break;
 #pragma unroll
       for (int p = 0; p < NP; ++p) acc[p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      up_stream<DT, NP>(rx, buf_rsrc(a.Wsu_p), q * NP, a.pFs, nkb, kb_lo, kb_hi, a.d, acc, false, x0);
+      up_stream<DT, NP>(rx, buf_rsrc(a.Wsu_p), q * NP, a.pFs, nkb, kb_lo, kb_hi, a.d, acc, x0);
       reduce_waves<NP, NCOL + 1>(s_red, acc, s_h[SR ? j : 0]);
       const int gcol0 = q * NCOL + col0;
       const bool col_ok = gcol0 < a.Fs;   // a partial last slice: CPT divides 32, so all or none
@@ -331,11 +360,11 @@ __global__ void __launch_bounds__(DNT) k_dec_up(DecArgs a) {
   // each lane sums x[c][k] W_r[k][e] over its fragment entries, waves over d
   float lam_e, b_e;
   unsigned ep;
+  i32x4_t wsp[SPEC ? U : 1][NP];
   {
     const char* wr = a.Wr_p + frag_off(e >> 4, 0, nkb) + (size_t)((e & 15) + 16 * g) * 16;
     const unsigned xoff = (unsigned)(((size_t)c * a.d + (size_t)DT::EPL * g) * sizeof(elem));
     float zp = 0.f;
-    x_loaded = kb_hi - kb_lo <= U;
     i32x4_t xv[U], wv[U];
     auto loads = [&](int kb0) {
 #pragma unroll
@@ -355,12 +384,25 @@ __global__ void __launch_bounds__(DNT) k_dec_up(DecArgs a) {
 #pragma unroll
           for (int j = 0; j < DT::EPL; ++j) zp += DT::lane_elem(xv[u], j) * DT::lane_elem(wv[u], j);
         }
-        x0[u] = xv[u];
       }
     };
     // the first batch in straight-line code: in a loop, a register reused
     // across the back edge puts a wait for older loads in front of it
     loads(kb_lo);
+    if constexpr (SPEC) {
+      const __amdgpu_buffer_rsrc_t rwu = buf_rsrc(a.Wup_p + (size_t)e * a.up_stride);
+      const int p0s = slice * NP;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        int kb = kb_lo + u < kb_hi ? kb_lo + u : kb_hi - 1;
+        kb = kb < 0 ? 0 : kb;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+          const int pp = p0s + p < a.pF ? p0s + p : a.pF - 1;
+          wsp[u][p] = ld16_buf(rwu, 16u * l, (unsigned)frag_off(pp, kb, nkb));
+        }
+      }
+    }
     // the call's epoch and the expert's router scalars, behind the batch
     ep = ld_word(a.ctr, 0) + 1u;
     lam_e = __uint_as_float(ld_word(a.lam, e));
@@ -369,6 +411,8 @@ __global__ void __launch_bounds__(DNT) k_dec_up(DecArgs a) {
     // otherwise sinks some below the first FMAs, a second round trip)
     __builtin_amdgcn_sched_barrier(0);
     products(kb_lo);
+#pragma unroll
+    for (int u = 0; u < U; ++u) x0[u] = xv[u];
     for (int kb0 = kb_lo + U; kb0 < kb_hi; kb0 += U) {
       loads(kb0);
       __builtin_amdgcn_sched_barrier(0);
@@ -451,13 +495,13 @@ __global__ void __launch_bounds__(DNT) k_dec_up(DecArgs a) {
   // NormSiLU input)
   const int p0 = slice * NP;
   if constexpr (GT) {
-    up_stream<DT, NP>(rx, buf_rsrc(a.Wlin_p + (size_t)e * a.up_stride), p0, a.pF, nkb, kb_lo, kb_hi, a.d, accu,
-                      x_loaded, x0);
+    up_stream<DT, NP, false, true>(rx, buf_rsrc(a.Wlin_p + (size_t)e * a.up_stride), p0, a.pF, nkb, kb_lo,
+                                   kb_hi, a.d, accu, x0);
     reduce_waves<NP, GT ? NCOL + 1 : 1>(s_red, accu, s_u);
   }
   bool xbad = false;
-  up_stream<DT, NP, XH>(rx, buf_rsrc(a.Wup_p + (size_t)e * a.up_stride), p0, a.pF, nkb, kb_lo, kb_hi, a.d, acc,
-                        x_loaded, x0, &xbad);
+  up_stream<DT, NP, XH, true, SPEC>(rx, buf_rsrc(a.Wup_p + (size_t)e * a.up_stride), p0, a.pF, nkb, kb_lo,
+                                    kb_hi, a.d, acc, x0, &xbad, wsp);
   if (xbad) atomicOr(a.err, 32u);   // an x value outside the fp16 range
   reduce_waves<NP, NCOL + 1>(s_red, acc, s_h[0]);
 
@@ -706,8 +750,24 @@ void (*up_kernel_np(int var))(DecArgs) {
   }
 }
 template <class DT>
-void (*up_kernel(int np, int var))(DecArgs) {
+void (*up_kernel(int np, int var, bool spec = false))(DecArgs) {
+  if (spec && var == 0) return np == 4 ? k_dec_up<DT, 4, 0, true> : k_dec_up<DT, 2, 0, true>;
   return np == 4 ? up_kernel_np<DT, 4>(var) : up_kernel_np<DT, 2>(var);
+}
+
+// From this batch size on, a routed slice requests its first W_up batch
+// before its expert's routing decision: the batch then touches nearly every
+// expert (about 1 - (1 - p)^T of them at activation ratio p), so the few
+// inactive experts' requests cost less than the router's load trip in front
+// of the stream (on the d = 2048 layer: 0.6 us faster per call at T = 16,
+// even at T = 8, where a fifth of the experts are idle).  Not with TopK routing (its decision waits on every expert's
+// logits), and only when each wave's share of the router is one batch of
+// k-blocks (a second router batch would wait for the speculative requests).
+#ifndef DECO_DEC_SPEC_T
+#define DECO_DEC_SPEC_T 16
+#endif
+bool dec_spec(const deco_moe_layer* L, int T) {
+  return T >= DECO_DEC_SPEC_T && L->cfg.top_k == 0 && (L->nkb_d + DNW - 1) / DNW <= 8;
 }
 
 int dec_variant(const deco_moe_layer* L) {
@@ -777,7 +837,7 @@ void (*down_kernel(const deco_moe_layer* L, int T, int* grid))(DecArgs) {
 template <class DT>
 hipError_t decode(const deco_moe_layer* L, const void* x, int T, void* out, hipStream_t s) {
   const DecArgs a = dec_args(L, x, T, out);
-  hipError_t err = deco_host::launch(deco_host::KS_DEC_UP, up_kernel<DT>(L->dec_np, dec_variant(L)),
+  hipError_t err = deco_host::launch(deco_host::KS_DEC_UP, up_kernel<DT>(L->dec_np, dec_variant(L), dec_spec(L, T)),
                                      dim3((unsigned)L->dec_grid_up), dim3(DNT), s, a);
   if (err != hipSuccess) return err;
   int grid = 0;
@@ -870,7 +930,8 @@ hipError_t decode_scratch(const deco_moe_layer* L, const void* x, int T, void* o
   hipLaunchKernelGGL(k_scratch_clear, dim3(std::min(1024u, (nw + 255) / 256)), dim3(256), 0, s, (unsigned*)base, nw);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(up_kernel<DT>(L->dec_np, dec_variant(L)), dim3((unsigned)L->dec_grid_up), dim3(DNT), 0, s, a);
+  hipLaunchKernelGGL(up_kernel<DT>(L->dec_np, dec_variant(L), dec_spec(L, T)), dim3((unsigned)L->dec_grid_up),
+                     dim3(DNT), 0, s, a);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   int grid = 0;
@@ -936,6 +997,14 @@ hipError_t plan_decode(deco_moe_layer* L) {
   int occ = 0;
   hipError_t err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, up, DNT, 0);
   if (err != hipSuccess) return err;
+  if (dec_variant(L) == 0) {   // the speculative variant runs too: the smaller occupancy
+    void (*sp)(DecArgs) = L->cfg.dtype == DECO_DT_BF16 ? up_kernel<BF16>(L->dec_np, 0, true)
+                                                       : up_kernel<F32>(L->dec_np, 0, true);
+    int occ2 = 0;
+    err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ2, sp, DNT, 0);
+    if (err != hipSuccess) return err;
+    occ = std::min(occ, occ2);
+  }
   const long long cap = (long long)(occ < 1 ? 0 : occ) * L->n_cu;
   bool ok = cap >= L->dec_S && cap >= (L->cfg.shared_rms ? L->dec_n_sh : 0);
   if (L->cfg.top_k > 0) ok = ok && cap >= L->dec_grid_up;
