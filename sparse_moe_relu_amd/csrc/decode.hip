@@ -585,7 +585,10 @@ __global__ void __launch_bounds__(DNT) k_dec_down(DecArgs a) {
   const int cg0 = blockIdx.x * CG;   // first of the workgroup's column groups
   const int kps = a.kps, kpe = a.kpe;
   // the call counter the next call's up kernel takes its epoch from (this
-  // call's up kernel has read it; nothing waits for the result)
+  // call's up kernel has read it; nothing waits for the result).  Every
+  // decode call that launches the up kernel launches this one after it on
+  // the same stream; a call whose second launch failed leaves the counter
+  // behind, and its error is returned to the caller.
   if (blockIdx.x == 0 && tid == 0) __hip_atomic_fetch_add(a.ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // routing flags first, so the shared slots' loads queue behind them

@@ -274,10 +274,13 @@ def test_changing_inputs_between_calls():
     layer.free()
 
 
+# T = 16 also runs the decode up kernel that requests W_up before the routing
+# decision: every expert's slice has loads in flight when it finds no token
+@pytest.mark.parametrize("T", [13, 16])
 @pytest.mark.parametrize("case", ["all_negative", "lambda_zero", "some_lambda_zero"])
 @pytest.mark.parametrize("path", ["decode", "prefill"])
-def test_degenerate_routing(case, path):
-    L = make_custom(256, 24, 128, 128, 13, "bf16", seed=4)
+def test_degenerate_routing(case, path, T):
+    L = make_custom(256, 24, 128, 128, T, "bf16", seed=4)
     b, lam = L.b_r.copy(), L.lam.copy()
     if case == "all_negative":
         b[:] = -1e4
@@ -285,7 +288,7 @@ def test_degenerate_routing(case, path):
         lam[:] = 0.0
     else:
         lam[::3] = 0.0
-    L2 = make_custom(256, 24, 128, 128, 13, "bf16", seed=4)
+    L2 = make_custom(256, 24, 128, 128, T, "bf16", seed=4)
     L2.b_r, L2.lam = b, lam
     ref = oracle.forward(L2.x, **L2.weights(), eps=L2.eps)
     layer = _layer_obj(L2, 32)
