@@ -92,7 +92,13 @@ long long est_expert_tiles(const deco_moe_layer* L, int T, int bm) { return (lon
 bool small_tiles_at(const deco_moe_layer* L, int T, long long grid) {
   return 2 * (est_shared_tiles(L, T) + est_expert_tiles(L, T, GM)) < grid;
 }
-bool small_expert_tiles(const deco_moe_layer* L, int T) { return small_tiles_at(L, T, L->pre_grid); }
+#ifndef DECO_PRE_FORCE_SMALL
+#define DECO_PRE_FORCE_SMALL -1   // measurement builds: 0 / 1 force 128- / 64-row expert tiles
+#endif
+bool small_expert_tiles(const deco_moe_layer* L, int T) {
+  if (DECO_PRE_FORCE_SMALL >= 0) return DECO_PRE_FORCE_SMALL != 0;
+  return small_tiles_at(L, T, L->pre_grid);
+}
 
 // Small batches of a non-gated layer split each 64-row expert tile over nks
 // k parts of the up-projection and ncb column blocks of the down-projection
