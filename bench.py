@@ -146,8 +146,9 @@ def sweep():
     """The decode layer at T in {1, 8}, the d=4096 layer over T in
     {1, 16, 256, 2048}, the d=2048 layer at T=1024 over activation ratios
     5..40 % (the d=2048 cases beside the dense-equivalent FFN), the TopK
-    routing variant (k = 11 of 56 experts, 20 %) beside the ReLU routing at
-    T = 1, 8 and 4096, the gated-expert variant at T = 1, 8 and 4096, the
+    routing variant (k = 11 of 56 experts, 20 %, and k at the ReLU router's
+    realised activation) beside the ReLU routing at T = 1, 8 and 4096, the
+    gated-expert variant at T = 1, 8 and 4096, the
     ablation switches (vanilla SiLU experts, RMS-only NormSiLU shared expert)
     at T = 8 and 4096, and the backward pass at T = 1024 and 4096 (its MFMA
     fraction on `backward_flops`):
@@ -160,6 +161,10 @@ def sweep():
              + [(5, 1024, r, 0, False) for r in (0.05, 0.10, 0.20, 0.40)]
              + [(2, 1, None, 11, False), (2, 8, None, 11, False), (3, 4096, None, 0, False),
                 (3, 4096, None, 11, False)]
+             # TopK at the ReLU router's realised activation (c2 T = 1: 10 of 56
+             # experts per token, T = 8: 12; c3 T = 4096: 12.7, bracketed by 12 and 13)
+             + [(2, 1, None, 10, False), (2, 8, None, 12, False), (3, 4096, None, 12, False),
+                (3, 4096, None, 13, False)]
              + [(2, 1, None, 0, True), (2, 8, None, 0, True), (3, 4096, None, 0, True)])
     cases = [c + ({},) for c in cases]
     vanilla, srms = dict(normsilu_mean=False, normsilu_rms=False), dict(shared_rms=True)
