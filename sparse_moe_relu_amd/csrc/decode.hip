@@ -360,7 +360,27 @@ __global__ void __launch_bounds__(DNT) k_dec_up(DecArgs a) {
   // each lane sums x[c][k] W_r[k][e] over its fragment entries, waves over d
   float lam_e, b_e;
   unsigned ep;
-  i32x4_t wsp[SPEC ? U : 1][NP];
+  // the first batch of the slice's NormSiLU-input stream, requested ahead of
+  // time: before the routing decision (SPEC), or, for gated experts, before
+  // the linear projection's stream, so that both first batches share a trip
+  // (32-column slices: 64 more registers; the 64-column ones would spill)
+  constexpr bool GPRE = GT && NP <= 2;
+  constexpr bool WPRE = SPEC || GPRE;
+  i32x4_t wsp[WPRE ? U : 1][NP];
+  auto preload_wup = [&]() {
+    const __amdgpu_buffer_rsrc_t rwu = buf_rsrc(a.Wup_p + (size_t)e * a.up_stride);
+    const int p0s = slice * NP;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      int kb = kb_lo + u < kb_hi ? kb_lo + u : kb_hi - 1;
+      kb = kb < 0 ? 0 : kb;
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const int pp = p0s + p < a.pF ? p0s + p : a.pF - 1;
+        wsp[WPRE ? u : 0][p] = ld16_buf(rwu, 16u * l, (unsigned)frag_off(pp, kb, nkb));
+      }
+    }
+  };
   {
     const char* wr = a.Wr_p + frag_off(e >> 4, 0, nkb) + (size_t)((e & 15) + 16 * g) * 16;
     const unsigned xoff = (unsigned)(((size_t)c * a.d + (size_t)DT::EPL * g) * sizeof(elem));
@@ -389,20 +409,7 @@ __global__ void __launch_bounds__(DNT) k_dec_up(DecArgs a) {
     // the first batch in straight-line code: in a loop, a register reused
     // across the back edge puts a wait for older loads in front of it
     loads(kb_lo);
-    if constexpr (SPEC) {
-      const __amdgpu_buffer_rsrc_t rwu = buf_rsrc(a.Wup_p + (size_t)e * a.up_stride);
-      const int p0s = slice * NP;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        int kb = kb_lo + u < kb_hi ? kb_lo + u : kb_hi - 1;
-        kb = kb < 0 ? 0 : kb;
-#pragma unroll
-        for (int p = 0; p < NP; ++p) {
-          const int pp = p0s + p < a.pF ? p0s + p : a.pF - 1;
-          wsp[u][p] = ld16_buf(rwu, 16u * l, (unsigned)frag_off(pp, kb, nkb));
-        }
-      }
-    }
+    if constexpr (SPEC) preload_wup();
     // the call's epoch and the expert's router scalars, behind the batch
     ep = ld_word(a.ctr, 0) + 1u;
     lam_e = __uint_as_float(ld_word(a.lam, e));
@@ -495,12 +502,13 @@ __global__ void __launch_bounds__(DNT) k_dec_up(DecArgs a) {
   // NormSiLU input)
   const int p0 = slice * NP;
   if constexpr (GT) {
+    if constexpr (GPRE && !SPEC) preload_wup();
     up_stream<DT, NP, false, true>(rx, buf_rsrc(a.Wlin_p + (size_t)e * a.up_stride), p0, a.pF, nkb, kb_lo,
                                    kb_hi, a.d, accu, x0);
     reduce_waves<NP, GT ? NCOL + 1 : 1>(s_red, accu, s_u);
   }
   bool xbad = false;
-  up_stream<DT, NP, XH, true, SPEC>(rx, buf_rsrc(a.Wup_p + (size_t)e * a.up_stride), p0, a.pF, nkb, kb_lo,
+  up_stream<DT, NP, XH, true, WPRE>(rx, buf_rsrc(a.Wup_p + (size_t)e * a.up_stride), p0, a.pF, nkb, kb_lo,
                                     kb_hi, a.d, acc, x0, &xbad, wsp);
   if (xbad) atomicOr(a.err, 32u);   // an x value outside the fp16 range
   reduce_waves<NP, NCOL + 1>(s_red, acc, s_h[0]);
